@@ -1,0 +1,432 @@
+"""CPU oracle for the forward pass of one mixture-of-experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
+executes this file: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` do.  It shares no code with the HIP
+library; both are fed from the seeded generators in ``moe_synth``.
+
+It is a plain, slow, obviously correct restatement of what the pages define,
+computed in float64 (NumPy) unless the definition itself fixes a precision:
+
+* router logits are float32 values (the router is an fp32 layer): the dot
+  product is formed in float64 and rounded once to float32;
+* expert choice is a decision on those float32 logits;
+* everything else (softmax, expert FFN, combine) stays in float64.
+
+Pages followed (cited by page title and section):
+
+[EP-glossary]  "Expert Parallelism", inferensys.com glossary: the gating
+               network gives each token a probability distribution over the
+               experts and the top-k are selected; capacity limits per expert,
+               overflow is skipped.
+[EP-notes]     "Expert Parallelism", narrativegoldmine.com:
+               section "Components and Architecture" (gating network,
+               dispatch tensor, expert GEMM, combine weighted by the gating
+               probabilities, capacity factor and token dropping) and section
+               "Formal Algorithm: Expert Parallelism Forward Pass" (g_t,
+               p_t = softmax(g_t / tau), e(t) = argmax p_t, w_t = p_{t,e(t)},
+               dispatch, expert computation, combine, residual).
+[EP-infinity]  "Expert Parallelism", theinfinity.ai: the capacity paragraph
+               (C = ceil((B*k/D)*c), overflow = max(0, p*B*k - C)) and the
+               worked-example figure (6 tokens, 8 experts, 4 devices, top-2,
+               capacity 2, two dropped assignments, experts 1 and 8 idle).
+[EP-a2a]       "Expert Parallelism and the All-to-All Bottleneck",
+               ashishsrivastav.com: section "The Mechanism of Expert
+               Parallelism" (routing, dispatch repacks rows per destination
+               expert, expert forward, gather back into the original token
+               order) and section "The All-to-All Communication Pattern"
+               (contiguous expert placement: 64 experts on 8 GPUs, expert 55
+               on GPU 6, expert 5 on GPU 0).
+
+Readings where the pages are silent or disagree (each also listed in the
+design notes of the repository):
+
+* capacity is per expert, ceil((B*k/E)*c) -- the page's per-device formula
+  with E in place of D; it is the only reading that gives the worked example's
+  "capacity of 2" (6*2/8*1.25 = 1.875 -> 2);
+* tau = 1 unless given; selection uses the key (logit descending, expert index
+  ascending), which orders experts exactly as the exact probabilities do and
+  breaks ties toward the lower index;
+* gate weights are the raw softmax probabilities of the chosen experts (not
+  renormalised), as w_t = p_{t,e(t)} in the formal algorithm;
+* assignments claim capacity slot-major: all tokens' first choices in token
+  order, then all second choices, ...; a dropped assignment contributes zero;
+* the packed buffer is compact and expert-major (hence destination-rank
+  major), rows of one expert in claim order;
+* an expert is W2 . act(W1 . x) with exact-erf GELU, or
+  W2 . (silu(W1 . x) * (W3 . x)) for SwiGLU, with no biases;
+* rows owned by experts that do not run on this GPU come back unchanged (the
+  missing collective is the identity).
+
+Pins (what fixes this code other than itself) live in ``tests/test_oracle_*``;
+every function below names the pins that cover it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "capacity", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "gate_logits",
+    "softmax", "route", "assign_slots", "layout", "pack", "gelu", "silu",
+    "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
+]
+
+
+# ----------------------------------------------------------------------------
+# capacity
+# ----------------------------------------------------------------------------
+def capacity(B: int, k: int, E: int, c: float) -> int:
+    """Per-expert capacity C = ceil((B*k/E)*c).
+
+    [EP-infinity] capacity paragraph gives ceil((B*k/D)*c) per device; per
+    expert (E for D) is the reading that reproduces the worked example's
+    capacity of 2.  Evaluated in IEEE double in exactly this operation order.
+    Pins: worked-example capacity 2; the five workload capacities; the
+    overflow identity max(0, n_e - C) on every expert (test_oracle_capacity,
+    test_oracle_worked_example)."""
+    if B == 0:
+        return 0
+    return int(math.ceil((float(B * k) / float(E)) * float(c)))
+
+
+def rank_of_expert(e: int, E: int, D: int) -> int:
+    """Contiguous placement: E/D experts per rank, rank r owns
+    [r*E/D, (r+1)*E/D).  [EP-a2a] "The All-to-All Communication Pattern":
+    with 64 experts on 8 GPUs expert 55 lives on GPU 6 and expert 5 on GPU 0
+    (pinned in test_oracle_special)."""
+    return e // (E // D)
+
+
+# ----------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (the high half of a float32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits_rne(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+
+    Written from the definition: keep the top 16 bits, look at the dropped
+    low 16 bits; round up when they exceed half an ulp, or equal half an ulp
+    and the kept part is odd.  Pins: hand-made tie/non-tie cases in
+    test_oracle_special."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    hi = u >> np.uint64(16)
+    lo = u & np.uint64(0xFFFF)
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & np.uint64(1)) == 1))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+def _x_values(x: np.ndarray) -> np.ndarray:
+    """The defined input values: bf16 bits (uint16) or float32."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# step 1: gate
+# ----------------------------------------------------------------------------
+def gate_logits(x: np.ndarray, Wg: np.ndarray,
+                bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Router logits g_t = x_t . Wg (+ b), float32 [B, E].
+
+    [EP-notes] "Formal Algorithm": g_t in R^E from the routing linear
+    projection; "Components and Architecture": a learned linear map, with an
+    optional bias term on the routing logits.  The sum is formed in float64
+    (each bf16 x fp32 product is exact there) and rounded once to float32.
+    Pins: exact rational dot products (fractions.Fraction) on small inputs in
+    test_oracle_gate."""
+    xv = _x_values(x)
+    l = xv @ np.asarray(Wg, dtype=np.float32).astype(np.float64)
+    if bias is not None:
+        l = l + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    return l.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# step 2: softmax + top-k
+# ----------------------------------------------------------------------------
+def softmax(logits: np.ndarray, tau: float = 1.0) -> np.ndarray:
+    """p_t = softmax(g_t / tau) over the E experts, float64.
+
+    [EP-notes] "Formal Algorithm", gate computation.  Pins: sums to one,
+    equal logits give 1/E, shift invariance, closed-form worked-example
+    weights (test_oracle_route)."""
+    z = np.asarray(logits, dtype=np.float32).astype(np.float64) / float(tau)
+    z = z - z.max(axis=1, keepdims=True)
+    ez = np.exp(z)
+    return ez / ez.sum(axis=1, keepdims=True)
+
+
+def route(logits: np.ndarray, k: int, tau: float = 1.0):
+    """Top-k experts per token and their raw gate probabilities.
+
+    Selection is decided on the float32 logits with the key
+    (logit descending, expert index ascending); j = 0 is the strongest
+    choice.  Because softmax is strictly increasing in the logit this is
+    the exact-probability order, and logit ties are exactly probability
+    ties, broken toward the lower index.  The weight of choice j is the
+    softmax probability of that expert, not renormalised
+    ([EP-notes] "Formal Algorithm": e(t) = argmax p_t, w_t = p_{t,e(t)};
+    [EP-glossary]: top-k of the distribution).
+
+    Returns idx int32 [B, k], w float64 [B, k] (the float32 the GPU
+    reports is compared against it within tolerance).  Pins: k = 1 is
+    argmax; k = E selects everything; brute-force sort with engineered ties;
+    equal logits give 0..k-1 and 1/E (test_oracle_route)."""
+    l32 = np.asarray(logits, dtype=np.float32)
+    B, E = l32.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # stable sort of -logit: descending value, equal values keep index order
+    order = np.argsort(-l32, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    p = softmax(l32, tau)
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    return idx, w
+
+
+# ----------------------------------------------------------------------------
+# step 3: capacity-limited slot assignment
+# ----------------------------------------------------------------------------
+def assign_slots(idx: np.ndarray, E: int, C: int):
+    """Slot of every assignment inside its expert, and which ones are kept.
+
+    Assignment (t, j) has claim priority q = j*B + t (slot-major: every
+    token's first choice in token order, then every second choice, ...).
+    pos[t, j] = number of assignments to the same expert with smaller q;
+    keep = pos < C.  n_e = assignments routed to e; kept_e = min(n_e, C);
+    dropped_e = max(0, n_e - C), the page's overflow with p*B*k = n_e
+    ([EP-infinity] capacity paragraph; [EP-notes] "Components and
+    Architecture", capacity factor and token dropping).
+
+    Uses one library primitive, a stable sort by expert of the assignments
+    listed in q order; the rank inside each run of equal experts is pos.
+    Pins: a sequential pure-Python claim queue (brute force), the worked
+    example fixture, the overflow identity (test_oracle_slots)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    B, k = idx.shape
+    e_q = idx.T.reshape(-1)                     # position q = j*B + t
+    order = np.argsort(e_q, kind="stable")      # by expert, q ascending
+    sorted_e = e_q[order]
+    load = np.bincount(e_q, minlength=E).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(load)[:-1]])
+    pos_q = np.empty(B * k, dtype=np.int64)
+    pos_q[order] = np.arange(B * k) - start[sorted_e]
+    pos = pos_q.reshape(k, B).T.copy()
+    keep = pos < C
+    count = np.minimum(load, C)
+    return pos.astype(np.int32), keep, load.astype(np.int32), count.astype(np.int32)
+
+
+def layout(idx: np.ndarray, pos: np.ndarray, keep: np.ndarray, E: int, D: int,
+           C: int):
+    """Compact, expert-major packed layout (hence grouped by destination rank).
+
+    expert_offset = exclusive prefix sum of kept_e (E+1 entries);
+    rank_offset[r] = expert_offset[r*E/D] (D+1 entries) -- rank r owns the
+    contiguous experts [r*E/D, (r+1)*E/D) ([EP-a2a] "The All-to-All
+    Communication Pattern"; "The Mechanism of Expert Parallelism": rows are
+    repacked per destination expert); dest[t, j] = expert_offset[e] + pos for
+    kept assignments, -1 otherwise; pack_src[dest] = t.
+    Pins: worked-example fixture; bijection/segment invariants
+    (test_oracle_slots)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    load = np.bincount(idx.reshape(-1), minlength=E)
+    kept = np.minimum(load, C)
+    expert_offset = np.zeros(E + 1, dtype=np.int64)
+    expert_offset[1:] = np.cumsum(kept)
+    rank_offset = expert_offset[np.arange(D + 1) * (E // D)]
+    dest = np.where(keep, expert_offset[idx] + pos, -1)
+    K = int(expert_offset[-1])
+    pack_src = np.empty(K, dtype=np.int64)
+    t_of = np.broadcast_to(np.arange(idx.shape[0])[:, None], idx.shape)
+    pack_src[dest[keep]] = t_of[keep]
+    return (expert_offset.astype(np.int32), rank_offset.astype(np.int32),
+            dest.astype(np.int32), pack_src.astype(np.int32))
+
+
+# ----------------------------------------------------------------------------
+# step 4: pack (on-device stand-in for the dispatch all-to-all)
+# ----------------------------------------------------------------------------
+def pack(x: np.ndarray, pack_src: np.ndarray) -> np.ndarray:
+    """packed[r] = bf16(x[pack_src[r]]) as bf16 bits [K, d].
+
+    [EP-a2a] "The Mechanism of Expert Parallelism", dispatch phase: the
+    (tokens, hidden) activations are repacked so that each row is a token
+    bound for one expert.  bf16 inputs are copied bit for bit; float32
+    inputs are rounded to nearest even.  Pins: round trip with ``unpack``
+    and the bf16 rounding cases (test_oracle_special)."""
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x[np.asarray(pack_src, dtype=np.int64)])
+    return f32_to_bf16_bits_rne(np.asarray(x, np.float32)[np.asarray(pack_src, dtype=np.int64)])
+
+
+def unpack(rows: np.ndarray, dest: np.ndarray) -> np.ndarray:
+    """out[t, j] = rows[dest[t, j]] for kept assignments, 0 elsewhere
+    ([EP-a2a] "The Mechanism of Expert Parallelism": results return to the
+    original token order)."""
+    B, k = dest.shape
+    out = np.zeros((B, k, rows.shape[1]), dtype=rows.dtype)
+    m = dest >= 0
+    out[m] = rows[dest[m]]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# step 5: expert FFN
+# ----------------------------------------------------------------------------
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Exact GELU: z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2)), float64.
+    Pins: Phi(1), Phi(-1) and an independent library GELU
+    (test_oracle_ffn)."""
+    from scipy.special import erf
+    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + e^-z), float64 (pinned like ``gelu``)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def _w(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def expert_mlp(xr: np.ndarray, W1: np.ndarray, W2: np.ndarray,
+               W3: Optional[np.ndarray], act: str) -> np.ndarray:
+    """One expert on rows xr [n, d] (float64): W2 . act(W1 . x) per row.
+
+    [EP-notes] "Components and Architecture", Expert GEMM: the expert is a
+    standard transformer MLP.  W1, W3: [f, d]; W2: [d, f] (output-major),
+    bf16 bits or float32.  GELU is exact-erf; SwiGLU is
+    silu(W1 x) * (W3 x); no biases.  Pins: an independent float64 library
+    MLP, E = 1 plain-MLP reduction (test_oracle_ffn)."""
+    w1 = _w(W1)
+    w2 = _w(W2)
+    h = xr @ w1.T
+    if act == "gelu":
+        h = gelu(h)
+    elif act == "swiglu":
+        h = silu(h) * (xr @ _w(W3).T)
+    else:
+        raise ValueError(act)
+    return h @ w2.T
+
+
+def expert_ffn(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
+               e_begin: int, e_end: int, W1, W2, W3, act: str,
+               rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Return buffer ret [K, d] in float64.
+
+    Rows of experts in [e_begin, e_end) get that expert's MLP of the token's
+    defined input x (bf16 values, or the float32 originals for an f32
+    workload); every other row comes back as its packed bf16 value (the
+    missing collective is the identity).  ``rows`` optionally restricts the
+    work to a subset of packed rows (others are NaN) for spot checks at full
+    size.  [EP-notes] "Formal Algorithm", expert computation on received
+    tokens; [EP-a2a] "The Mechanism of Expert Parallelism", phase 3."""
+    pack_src = np.asarray(pack_src, dtype=np.int64)
+    K = pack_src.shape[0]
+    d = x.shape[1]
+    want = np.ones(K, dtype=bool) if rows is None else np.zeros(K, dtype=bool)
+    if rows is not None:
+        want[np.asarray(rows, dtype=np.int64)] = True
+    ret = np.full((K, d), np.nan)
+    xv_rows = lambda r: _x_values(x[pack_src[r]])
+    lo, hi = int(expert_offset[e_begin]), int(expert_offset[e_end])
+    # rows owned by other ranks: identity loopback of the packed bf16 value
+    remote = np.ones(K, dtype=bool)
+    remote[lo:hi] = False
+    rr = np.nonzero(remote & want)[0]
+    if rr.size:
+        ret[rr] = bf16_bits_to_f64(pack(x, pack_src[rr]))
+    for e in range(e_begin, e_end):
+        a, b = int(expert_offset[e]), int(expert_offset[e + 1])
+        r = np.arange(a, b)[want[a:b]]
+        if r.size == 0:
+            continue
+        i = e - e_begin
+        ret[r] = expert_mlp(xv_rows(r), W1[i], W2[i],
+                            None if W3 is None else W3[i], act)
+    return ret
+
+
+# ----------------------------------------------------------------------------
+# step 6: combine
+# ----------------------------------------------------------------------------
+def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
+            x_residual: Optional[np.ndarray] = None,
+            tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[t] = sum_j [kept] w[t, j] * ret[dest[t, j]] (+ x[t]), float64.
+
+    [EP-notes] "Components and Architecture", expert combine: the k outputs
+    of a token are weighted by the gating probabilities and summed, in the
+    original token order ([EP-a2a] gather phase); a dropped assignment
+    contributes nothing, so a token with every choice dropped gets 0 (plus
+    the residual when it is added).  ``w`` is taken at float32 precision,
+    the precision the router reports it in.  ``tokens`` restricts the
+    output rows (others NaN).  Pins: dense soft-mixture equivalence without
+    drops, C = 0 gives 0 (test_oracle_combine)."""
+    B, k = dest.shape
+    tt = np.arange(B) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = np.full((B, ret.shape[1]), np.nan)
+    acc = np.zeros((tt.size, ret.shape[1]))
+    w32 = np.asarray(w, dtype=np.float32).astype(np.float64)
+    for j in range(k):
+        dj = dest[tt, j]
+        m = dj >= 0
+        acc[m] += w32[tt[m], j][:, None] * ret[dj[m]]
+    if x_residual is not None:
+        acc += _x_values(x_residual[tt])
+    y[tt] = acc
+    return y
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
+            n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
+            tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
+            logits: Optional[np.ndarray] = None, ffn_rows=None, tokens=None) -> dict:
+    """All steps in the pages' order ([EP-notes] "Formal Algorithm";
+    [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
+    and slots, pack, expert FFN, unpack + weighted combine (+ residual).
+
+    ``logits`` may be given to skip the gate (routing tests feed the router
+    directly); ``ffn_rows``/``tokens`` restrict the float work to samples."""
+    B = x.shape[0]
+    E = Wg.shape[1] if Wg is not None else logits.shape[1]
+    e_end = E if e_end is None else e_end
+    if logits is None:
+        logits = gate_logits(x, Wg, bias)
+    idx, w = route(logits, k, tau)
+    if C is None:
+        C = capacity(B, k, E, c)
+    pos, keep, load, count = assign_slots(idx, E, C)
+    expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C)
+    packed = pack(x, pack_src)
+    out = dict(logits=logits, idx=idx, w=w, C=C, pos=pos, keep=keep,
+               expert_load=load, expert_count=count, expert_offset=expert_offset,
+               rank_offset=rank_offset, dest=dest, pack_src=pack_src,
+               packed=packed)
+    if W1 is not None:
+        ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3,
+                         act, rows=ffn_rows)
+        out["ret"] = ret
+        if tokens is not None or ffn_rows is None:
+            out["y"] = combine(ret, dest, w, x if add_residual else None,
+                               tokens=tokens)
+    return out
