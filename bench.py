@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE-layer forward on one MI355X.
+
+A step is one moe_forward over the batch: fp32 gate, softmax + top-k,
+capacity-limited slot assignment with drops, pack into per-expert (per-rank)
+segments, grouped expert MLP on bf16 MFMA, weighted combine.  Inputs are
+seeded synthetic tensors of the workload's shape, resident in HBM before the
+timed region.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload uniform] [--cold]
+                  [--no-cpu-baseline] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; expert GEMM % MFMA peak; dispatch % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+# fp32 FMA without packed-math forms: 256 CU x 4 SIMD x 16 lanes x 2 FLOP x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="uniform")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MB buffer before every step (flushes L2 and MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
+    """Bytes / FLOPs the method must move / compute for one forward, per step."""
+    B, d, E, k, f = w.B, w.d, w.E, w.k, w.f
+    sx = 2 if w.x_dtype == "bf16" else 4
+    K = int(eo[-1])
+    lo, hi = int(eo[w.e_begin]), int(eo[w.e_end])
+    Kloc = hi - lo
+    nmat = 3 if w.act == "swiglu" else 2
+    active_local = int(sum(1 for e in range(w.e_begin, w.e_end) if eo[e + 1] > eo[e]))
+    t_act = int(keep.any(axis=1).sum())
+    return dict(
+        gate_flop=2.0 * B * d * E,
+        gate_bytes=B * d * sx + 4.0 * d * E + 4.0 * B * E,
+        route_bytes=B * (4.0 * E + 8.0 * k),
+        slot_bytes=B * k * (4 + 4 + 1 + 4) + 4.0 * K,
+        pack_bytes=t_act * d * sx + 2.0 * d * K,
+        ffn_flop=2.0 * d * f * nmat * Kloc,
+        ffn_bytes=active_local * 2.0 * d * f * nmat + 4.0 * d * Kloc,
+        combine_bytes=2.0 * d * K + B * d * sx + 8.0 * k * B,
+        K=K, Kloc=Kloc, t_act=t_act, active_local=active_local,
+    )
+
+
+def time_calls(fn, n, torch):
+    """Average device time of fn() over n back-to-back calls (HIP events on
+    the current stream, which is the stream the library launches on)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n * 1e-3
+
+
+def cpu_baseline(w, inp, budget_s: float) -> dict:
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    reps, t_tot = 0, 0.0
+    while reps == 0 or (t_tot < budget_s and reps < 20):
+        t0 = time.perf_counter()
+        oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"], k=w.k,
+                       c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end,
+                       tau=w.tau)
+        t_tot += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the whole {w.name} batch ({w.B} tokens), oracle forward run {reps} times "
+                      f"({t_tot:.1f} s), float64 NumPy, input generation excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer has no cross-GPU step in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import expert_token_routing_fp32_amd as moe
+    import moe_synth
+
+    w = moe_synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs")
+    inp = moe_synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    bf16 = w.x_dtype == "bf16"
+    x = d16(inp["x"]) if bf16 else torch.from_numpy(inp["x"]).to(dev)
+    Wg = torch.from_numpy(inp["Wg"]).to(dev)
+    bias = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to(dev)
+    W1 = d16(inp["W1"] if bf16 else inp["W1_bits"])
+    W2 = d16(inp["W2"] if bf16 else inp["W2_bits"])
+    W3 = None
+    if w.act == "swiglu":
+        W3 = d16(inp["W3"] if bf16 else inp["W3_bits"])
+    p = moe.make_problem(B=w.B, d=w.d, E=w.E, k=w.k, c=w.c, f=w.f, act=w.act, x_dtype=w.x_dtype,
+                         n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end, tau=w.tau)
+    ws = torch.empty(moe.workspace_bytes(p, "forward"), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    def step():
+        if flush is not None:
+            flush.fill_(1)
+        moe.forward(p, x, Wg, bias, W1, W3, W2, y=y, ws=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / args.steps
+    log(f"[bench] {sec_per_step * 1e3:.3f} ms/step")
+
+    # per-step breakdown, each API call timed on its own with HIP events
+    _, o = moe.forward(p, x, Wg, bias, W1, W3, W2, outputs=True)
+    torch.cuda.synchronize()
+    keep = o["keep"].cpu().numpy().astype(bool)
+    eo = o["expert_offset"].cpu().numpy()
+    alg = algorithmic(w, keep, eo)
+    n = max(5, min(args.steps, 50))
+    logits = o["logits"]
+    idx, wt = o["topk_idx"], o["topk_w"]
+    disp = moe.dispatch(p, x, idx)
+    packed, eo_d, dest = disp["packed"], disp["expert_offset"], disp["dest"]
+    ws_d = torch.empty(max(moe.workspace_bytes(p, "dispatch"), 1), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(moe.workspace_bytes(p, "ffn"), 1), dtype=torch.uint8, device=dev)
+    t_gate = time_calls(lambda: moe.gate(p, x, Wg, bias, logits=logits), n, torch)
+    t_route = time_calls(lambda: moe.route(p, logits, idx, wt), n, torch)
+    t_disp = time_calls(lambda: moe.dispatch(p, x, idx, ws=ws_d), n, torch)
+    t_ffn = time_calls(lambda: moe.expert_ffn(p, packed, eo_d, W1, W3, W2, ret=packed, ws=ws_f),
+                       n, torch)
+    t_comb = time_calls(lambda: moe.combine(p, packed, dest, wt, y=y), n, torch)
+    log(f"[bench] gate {t_gate*1e6:.1f} us, route {t_route*1e6:.1f} us, dispatch "
+        f"{t_disp*1e6:.1f} us, ffn {t_ffn*1e6:.1f} us, combine {t_comb*1e6:.1f} us")
+
+    ffn_gbs = alg["ffn_bytes"] / t_ffn / 1e9
+    ffn_tflops = alg["ffn_flop"] / t_ffn / 1e12
+    ffn_bound = "hbm" if alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= \
+        alg["ffn_flop"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    if ffn_bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "expert FFN: grouped_gemm_kernel GEMM1 (act) + GEMM2, one moe_expert_ffn call"
+    roof["algorithmic_bytes"] = alg["ffn_bytes"]
+    roof["algorithmic_flop"] = alg["ffn_flop"]
+    roof["avg_launch_us"] = round(t_ffn * 1e6, 2)
+
+    rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]
+    rpc_t = t_route + t_disp + t_comb
+    breakdown = {
+        "gate_us": round(t_gate * 1e6, 2),
+        "gate_alu_frac": round(alg["gate_flop"] / t_gate / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+        "route_us": round(t_route * 1e6, 2),
+        "dispatch_us": round(t_disp * 1e6, 2),
+        "expert_ffn_us": round(t_ffn * 1e6, 2),
+        "combine_us": round(t_comb * 1e6, 2),
+        "expert_gemm_tflops": round(ffn_tflops, 1),
+        "expert_gemm_mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "expert_gemm_hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
+        "route_pack_combine_gbs": round(rpc_bytes / rpc_t / 1e9, 1),
+        "route_pack_combine_hbm_frac": round(rpc_bytes / rpc_t / 1e9 / HBM_PEAK_GBS, 4),
+        "kept": alg["K"], "kept_local": alg["Kloc"], "dropped": int(w.B * w.k - alg["K"]),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.B / sec_per_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} d={w.d} E={w.E} top-{w.k} c={w.c} "
+                               f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
+                               f"local experts [{w.e_begin},{w.e_end})",
+                   "global_batch": w.B, "cache": "cold" if args.cold else "warm"},
+        "roofline": roof,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

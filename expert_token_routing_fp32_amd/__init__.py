@@ -1,0 +1,259 @@
+"""MI355X (gfx950) forward pass of one mixture-of-experts layer.
+
+A thin Python face of the C ABI in include/moe.h (libmoe.so, built from
+csrc/ by ``build.py``).  Tensors are torch tensors on a ROCm device; this
+module only checks shapes and passes pointers and the current HIP stream --
+every step of the layer runs in the library's kernels.  bf16 tensors may be
+``torch.bfloat16`` or raw 16-bit patterns (``torch.int16``).
+
+Steps ("Expert Parallelism", narrativegoldmine.com, "Formal Algorithm";
+"Expert Parallelism and the All-to-All Bottleneck", "The Mechanism of Expert
+Parallelism"): gate -> route -> dispatch (capacity, slots, pack) ->
+expert_ffn -> combine; ``forward`` runs them back to back.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import MoEError, Problem  # noqa: F401
+
+__all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
+           "workspace_bytes", "gate", "route", "dispatch", "expert_ffn", "combine",
+           "unpack", "forward", "MoEError", "Problem", "lib"]
+
+
+def lib():
+    return L.load()
+
+
+def make_problem(B: int, d: int, E: int, k: int, c: float = 1.0, f: int = 8,
+                 act: str = "gelu", x_dtype: str = "bf16", C: int = -1, n_ranks: int = 1,
+                 e_begin: int = 0, e_end: Optional[int] = None, tau: float = 1.0,
+                 add_residual: bool = False) -> Problem:
+    return Problem(B=B, d=d, E=E, k=k, c=c, C=C, n_ranks=n_ranks, e_begin=e_begin,
+                   e_end=E if e_end is None else e_end, f=f,
+                   act={"gelu": L.MOE_GELU, "swiglu": L.MOE_SWIGLU}[act],
+                   x_dtype={"f32": L.MOE_F32, "bf16": L.MOE_BF16}[x_dtype], tau=tau,
+                   add_residual=int(bool(add_residual)))
+
+
+def capacity(B: int, k: int, E: int, c: float) -> int:
+    return lib().moe_capacity(B, k, E, c)
+
+
+def problem_capacity(p: Problem) -> int:
+    return lib().moe_problem_capacity(ctypes.byref(p))
+
+
+def max_kept(p: Problem) -> int:
+    return lib().moe_max_kept(ctypes.byref(p))
+
+
+def validate(p: Problem) -> int:
+    return lib().moe_validate(ctypes.byref(p))
+
+
+def workspace_bytes(p: Problem, op: str = "forward") -> int:
+    o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD}[op]
+    return lib().moe_workspace_bytes(ctypes.byref(p), o)
+
+
+# ---------------------------------------------------------------------------
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], name: str, numel: int, itemsize: int, dev=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != itemsize:
+        raise ValueError(f"{name}: element size {t.element_size()} != {itemsize}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements < {numel}")
+
+
+def _xsize(p: Problem) -> int:
+    return 2 if p.x_dtype == L.MOE_BF16 else 4
+
+
+def _ws(p: Problem, op: str, ws: Optional[torch.Tensor], device) -> torch.Tensor:
+    n = workspace_bytes(p, op)
+    if ws is None:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    _need(ws, "ws", n, 1)
+    return ws
+
+
+def _check(p: Problem):
+    st = validate(p)
+    L.check(st, "problem")
+
+
+def gate(p: Problem, x, Wg, bias=None, logits=None):
+    _check(p)
+    B, d, E = p.B, p.d, p.E
+    _need(x, "x", B * d, _xsize(p))
+    _need(Wg, "Wg", d * E, 4)
+    if bias is not None:
+        _need(bias, "bias", E, 4)
+    if logits is None:
+        logits = torch.empty((B, E), dtype=torch.float32, device=x.device)
+    _need(logits, "logits", B * E, 4)
+    L.check(lib().moe_gate(ctypes.byref(p), _p(x), _p(Wg), _p(bias), _p(logits), _stream()),
+            "moe_gate")
+    return logits
+
+
+def route(p: Problem, logits, topk_idx=None, topk_w=None):
+    _check(p)
+    B, E, k = p.B, p.E, p.k
+    _need(logits, "logits", B * E, 4)
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((B, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", B * k, 4)
+    _need(topk_w, "topk_w", B * k, 4)
+    L.check(lib().moe_route(ctypes.byref(p), _p(logits), _p(topk_idx), _p(topk_w), _stream()),
+            "moe_route")
+    return topk_idx, topk_w
+
+
+def dispatch(p: Problem, x, topk_idx, ws=None) -> dict:
+    """Slots, drops and the pack.  Returns every output as a device tensor;
+    ``packed`` has max_kept(p) rows, of which expert_offset[E] are written."""
+    _check(p)
+    B, d, E, k, D = p.B, p.d, p.E, p.k, p.n_ranks
+    dev = topk_idx.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(topk_idx, "topk_idx", B * k, 4)
+    km = max_kept(p)
+    i32 = dict(dtype=torch.int32, device=dev)
+    o = dict(pos=torch.empty((B, k), **i32), keep=torch.empty((B, k), dtype=torch.uint8, device=dev),
+             dest=torch.empty((B, k), **i32), expert_load=torch.empty(E, **i32),
+             expert_count=torch.empty(E, **i32), expert_offset=torch.empty(E + 1, **i32),
+             rank_offset=torch.empty(D + 1, **i32), pack_src=torch.empty(max(km, 1), **i32),
+             packed=torch.empty((max(km, 1), d), dtype=torch.int16, device=dev))
+    ws = _ws(p, "dispatch", ws, dev)
+    L.check(lib().moe_dispatch(ctypes.byref(p), _p(x), _p(topk_idx), _p(o["pos"]), _p(o["keep"]),
+                               _p(o["dest"]), _p(o["expert_load"]), _p(o["expert_count"]),
+                               _p(o["expert_offset"]), _p(o["rank_offset"]), _p(o["pack_src"]),
+                               _p(o["packed"]), _p(ws), ws.numel(), _stream()), "moe_dispatch")
+    return o
+
+
+def expert_ffn(p: Problem, packed, expert_offset, W1, W3, W2, ret=None, ws=None):
+    """ret = expert MLP of the local experts' rows; other rows copied (or
+    left in place when ``ret is packed``)."""
+    _check(p)
+    d, f, E = p.d, p.f, p.E
+    nl = p.e_end - p.e_begin
+    km = max_kept(p)
+    _need(packed, "packed", km * d, 2)
+    _need(expert_offset, "expert_offset", E + 1, 4)
+    if nl > 0:
+        _need(W1, "W1", nl * f * d, 2)
+        _need(W2, "W2", nl * d * f, 2)
+        if p.act == L.MOE_SWIGLU:
+            _need(W3, "W3", nl * f * d, 2)
+    if ret is None:
+        ret = torch.empty_like(packed)
+    _need(ret, "ret", km * d, 2)
+    ws = _ws(p, "ffn", ws, packed.device)
+    L.check(lib().moe_expert_ffn(ctypes.byref(p), _p(packed), _p(expert_offset), _p(W1),
+                                 _p(W3 if p.act == L.MOE_SWIGLU else None), _p(W2), _p(ret),
+                                 _p(ws), ws.numel(), _stream()), "moe_expert_ffn")
+    return ret
+
+
+def combine(p: Problem, ret, dest, topk_w, x_residual=None, y=None):
+    _check(p)
+    B, d, k = p.B, p.d, p.k
+    _need(ret, "ret", max_kept(p) * d, 2)
+    _need(dest, "dest", B * k, 4)
+    _need(topk_w, "topk_w", B * k, 4)
+    if p.add_residual:
+        _need(x_residual, "x_residual", B * d, _xsize(p))
+    if y is None:
+        y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
+                        device=ret.device)
+    _need(y, "y", B * d, _xsize(p))
+    L.check(lib().moe_combine(ctypes.byref(p), _p(ret), _p(dest), _p(topk_w),
+                              _p(x_residual if p.add_residual else None), _p(y), _stream()),
+            "moe_combine")
+    return y
+
+
+def unpack(p: Problem, ret, dest, out=None):
+    _check(p)
+    B, d, k = p.B, p.d, p.k
+    _need(ret, "ret", max_kept(p) * d, 2)
+    _need(dest, "dest", B * k, 4)
+    if out is None:
+        out = torch.empty((B, k, d), dtype=torch.int16, device=ret.device)
+    _need(out, "out", B * k * d, 2)
+    L.check(lib().moe_unpack(ctypes.byref(p), _p(ret), _p(dest), _p(out), _stream()), "moe_unpack")
+    return out
+
+
+_OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
+               "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")
+
+
+def forward(p: Problem, x, Wg, bias, W1, W3, W2, y=None, outputs: bool = False, ws=None):
+    """The whole layer on the current stream.  With ``outputs`` the
+    intermediate tensors are allocated and returned too (``packed`` then holds
+    the expert outputs of the local rows, in place)."""
+    _check(p)
+    B, d, E, k, f = p.B, p.d, p.E, p.k, p.f
+    nl = p.e_end - p.e_begin
+    dev = x.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(Wg, "Wg", d * E, 4)
+    if bias is not None:
+        _need(bias, "bias", E, 4)
+    if nl > 0:
+        _need(W1, "W1", nl * f * d, 2)
+        _need(W2, "W2", nl * d * f, 2)
+        if p.act == L.MOE_SWIGLU:
+            _need(W3, "W3", nl * f * d, 2)
+    if y is None:
+        y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
+                        device=dev)
+    _need(y, "y", B * d, _xsize(p))
+    o = None
+    outp = None
+    if outputs:
+        km = max(max_kept(p), 1)
+        i32 = dict(dtype=torch.int32, device=dev)
+        o = dict(logits=torch.empty((B, E), dtype=torch.float32, device=dev),
+                 topk_idx=torch.empty((B, k), **i32),
+                 topk_w=torch.empty((B, k), dtype=torch.float32, device=dev),
+                 pos=torch.empty((B, k), **i32), keep=torch.empty((B, k), dtype=torch.uint8, device=dev),
+                 dest=torch.empty((B, k), **i32), expert_load=torch.empty(E, **i32),
+                 expert_count=torch.empty(E, **i32), expert_offset=torch.empty(E + 1, **i32),
+                 rank_offset=torch.empty(p.n_ranks + 1, **i32), pack_src=torch.empty(km, **i32),
+                 packed=torch.empty((km, d), dtype=torch.int16, device=dev))
+        outp = L.ForwardOut(**{n: o[n].data_ptr() for n in _OUT_FIELDS})
+    n = workspace_bytes(p, "forward")
+    if ws is None:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", 1, 1)
+    L.check(lib().moe_forward(ctypes.byref(p), _p(x), _p(Wg), _p(bias), _p(W1),
+                              _p(W3 if p.act == L.MOE_SWIGLU else None), _p(W2), _p(y),
+                              ctypes.byref(outp) if outp is not None else None, _p(ws),
+                              ws.numel(), _stream()), "moe_forward")
+    return (y, o) if outputs else y

@@ -1,0 +1,95 @@
+"""ctypes view of include/moe.h: the struct, the status codes and the
+function prototypes.  Argument marshalling only; every step of the layer runs
+in the HIP library.  Loading fails loudly when the library is not built."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_GELU, MOE_SWIGLU = 0, 1
+MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD = 0, 1, 2
+
+
+class Problem(ctypes.Structure):
+    """moe_problem_t."""
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("c", ctypes.c_double),
+        ("C", ctypes.c_int32),
+        ("n_ranks", ctypes.c_int32),
+        ("e_begin", ctypes.c_int32),
+        ("e_end", ctypes.c_int32),
+        ("f", ctypes.c_int32),
+        ("act", ctypes.c_int32),
+        ("x_dtype", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+        ("add_residual", ctypes.c_int32),
+    ]
+
+
+class ForwardOut(ctypes.Structure):
+    """moe_forward_out_t (every field a device pointer or NULL)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
+        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.moe_status_str(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg} (status {code})")
+
+
+_P = ctypes.POINTER(Problem)
+_V = ctypes.c_void_p
+_SIGS = {
+    "moe_capacity": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double]),
+    "moe_problem_capacity": (ctypes.c_int32, [_P]),
+    "moe_max_kept": (ctypes.c_int64, [_P]),
+    "moe_validate": (ctypes.c_int, [_P]),
+    "moe_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int]),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_gate": (ctypes.c_int, [_P, _V, _V, _V, _V, _V]),
+    "moe_route": (ctypes.c_int, [_P, _V, _V, _V, _V]),
+    "moe_dispatch": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                    ctypes.c_size_t, _V]),
+    "moe_expert_ffn": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "moe_combine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
+    "moe_unpack": (ctypes.c_int, [_P, _V, _V, _V, _V]),
+    "moe_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.POINTER(ForwardOut),
+                                   _V, ctypes.c_size_t, _V]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m expert_token_routing_fp32_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(code: int, where: str) -> None:
+    if code != MOE_OK:
+        raise MoEError(code, where)

@@ -1,0 +1,154 @@
+// Gate-weighted combine back into token order, its unpack helper, and the
+// identity return of rows whose experts run elsewhere.
+//
+// "Expert Parallelism" (narrativegoldmine.com), "Components and
+// Architecture", expert combine: a token's k expert outputs are weighted by
+// their gating probabilities and summed before the residual addition;
+// "Formal Algorithm", expert combine and residual addition.  "Expert
+// Parallelism and the All-to-All Bottleneck", "The Mechanism of Expert
+// Parallelism": the gathered rows return to (tokens, hidden) in the original
+// token order.  On one GPU the return all-to-all is the identity, so the
+// combine reads the packed rows in place (a gather by dest; no atomics, fixed
+// j order, fp32 accumulation).
+//
+// All three kernels are row copies/gathers bound by HBM: one thread moves a
+// 16-byte chunk (8 bf16), consecutive threads walk a row.
+#include "moe_kernels.h"
+
+namespace moek {
+namespace {
+
+unsigned grid_for(int64_t work, int threads) {
+  int64_t g = (work + threads - 1) / threads;
+  if (g > (1 << 20)) g = 1 << 20;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+template <bool XBF16, bool RES>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const uint16_t* __restrict__ ret, const int32_t* __restrict__ dest,
+    const float* __restrict__ w, const void* __restrict__ xres, void* __restrict__ y, int64_t B,
+    int k, int d, int64_t kmax) {
+  const int cpr = d / 8;
+  const int64_t total = B * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / cpr;
+    const int c = (int)(i - t * cpr);
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int r = dest[t * k + j];
+      if (r >= 0 && r < kmax) {
+        const float wj = w[t * k + j];
+        const u32x4 v = *(const u32x4*)(ret + (int64_t)r * d + c * 8);
+        float f[8];
+        unpack8(v, f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
+      }
+    }
+    if (RES) {
+      float xr[8];
+      if (XBF16) {
+        unpack8(*(const u32x4*)((const uint16_t*)xres + t * d + c * 8), xr);
+      } else {
+        const float* xf = (const float*)xres + t * d + c * 8;
+        const f32x4 a = *(const f32x4*)xf;
+        const f32x4 b = *(const f32x4*)(xf + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { xr[u] = a[u]; xr[u + 4] = b[u]; }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += xr[u];
+    }
+    if (XBF16) {
+      *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
+    } else {
+      float* yf = (float*)y + t * d + c * 8;
+      *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const uint16_t* __restrict__ ret,
+                                                     const int32_t* __restrict__ dest, int64_t B,
+                                                     int k, int d, int64_t kmax,
+                                                     uint16_t* __restrict__ out) {
+  const int cpr = d / 8;
+  const int64_t total = B * k * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t tj = i / cpr;
+    const int c = (int)(i - tj * cpr);
+    const int r = dest[tj];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r >= 0 && r < kmax) v = *(const u32x4*)(ret + (int64_t)r * d + c * 8);
+    *(u32x4*)(out + tj * d + c * 8) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_remote_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst,
+                                                          const int32_t* __restrict__ eo, int E,
+                                                          int e_begin, int e_end, int64_t kmax,
+                                                          int d) {
+  const int64_t K = eo[E];
+  const int64_t lo = eo[e_begin], hi = eo[e_end];
+  const int cpr = d / 8;
+  const int64_t total = (K < kmax ? K : kmax) * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cpr;
+    if (r >= lo && r < hi) continue;
+    const int c = (int)(i - r * cpr);
+    *(u32x4*)(dst + r * d + c * 8) = *(const u32x4*)(src + r * d + c * 8);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
+                          const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
+                          int64_t kmax, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const unsigned g = grid_for(B * (d / 8), 256);
+  if (x_bf16) {
+    if (x_res)
+      hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,
+                         x_res, y, B, k, d, kmax);
+    else
+      hipLaunchKernelGGL((combine_kernel<true, false>), dim3(g), dim3(256), 0, s, ret, dest, w,
+                         x_res, y, B, k, d, kmax);
+  } else {
+    if (x_res)
+      hipLaunchKernelGGL((combine_kernel<false, true>), dim3(g), dim3(256), 0, s, ret, dest, w,
+                         x_res, y, B, k, d, kmax);
+    else
+      hipLaunchKernelGGL((combine_kernel<false, false>), dim3(g), dim3(256), 0, s, ret, dest, w,
+                         x_res, y, B, k, d, kmax);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint16_t* ret, const int32_t* dest, int64_t B, int k, int d,
+                         int64_t kmax, uint16_t* out, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const unsigned g = grid_for(B * k * (d / 8), 256);
+  hipLaunchKernelGGL(unpack_kernel, dim3(g), dim3(256), 0, s, ret, dest, B, k, d, kmax, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_remote(const uint16_t* src, uint16_t* dst, const int32_t* expert_offset,
+                              int E, int e_begin, int e_end, int64_t kmax, int d, hipStream_t s) {
+  if (kmax <= 0) return hipSuccess;
+  const unsigned g = grid_for(kmax * (d / 8), 256);
+  hipLaunchKernelGGL(copy_remote_kernel, dim3(g), dim3(256), 0, s, src, dst, expert_offset, E,
+                     e_begin, e_end, kmax, d);
+  return hipGetLastError();
+}
+
+}  // namespace moek

@@ -1,0 +1,271 @@
+// Capacity-limited slot assignment and the pack that replaces the dispatch
+// all-to-all on one GPU.
+//
+// "Expert Parallelism" (theinfinity.ai), capacity paragraph: every expert
+// takes at most C = ceil((B*k/E)*c) assignments and the overflow,
+// max(0, n_e - C), is dropped.  "Expert Parallelism and the All-to-All
+// Bottleneck", "The Mechanism of Expert Parallelism": the (tokens, hidden)
+// activations are repacked so that each row is a token bound for one expert,
+// and rows for one destination rank are contiguous ("The All-to-All
+// Communication Pattern": experts are placed contiguously, E/D per rank).
+//
+// Claim order is q = j*B + t.  The q range is cut into tiles; three kernels
+// give every assignment its slot without any order-dependent atomic:
+//   slot_hist  per-tile expert histogram (LDS atomics only count)
+//   slot_scan  per expert, exclusive prefix over tiles -> tile bases; n_e,
+//              min(n_e, C), expert_offset (prefix over experts), rank_offset
+//   slot_rank  inside a tile: 64-lane ballot match gives each lane its rank
+//              among equal experts in its wavefront; per-wavefront counts and
+//              bases in LDS carry the order across the four wavefronts and
+//              across chunks.  Writes pos, keep, dest, pack_src.
+// pack then moves each token row once from x into its kept packed rows.
+#include "moe_kernels.h"
+
+namespace moek {
+namespace {
+
+constexpr int kSlotThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// lanes of this wavefront holding the same (valid) expert id
+__device__ __forceinline__ unsigned long long match_expert(int e, int nbits) {
+  unsigned long long m = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const unsigned long long bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__device__ __forceinline__ int load_expert(const int32_t* idx, int64_t q, int64_t B, int k,
+                                           int E) {
+  const int64_t j = q / B;
+  const int64_t t = q - j * B;
+  const int e = idx[t * k + j];
+  return ((unsigned)e < (unsigned)E) ? e : -1;
+}
+
+__global__ __launch_bounds__(kSlotThreads) void slot_hist_kernel(const int32_t* __restrict__ idx,
+                                                                int64_t B, int k, int E,
+                                                                int64_t BK, int tile,
+                                                                int32_t* __restrict__ hist) {
+  extern __shared__ int h[];
+  for (int e = threadIdx.x; e < E; e += kSlotThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t q0 = (int64_t)blockIdx.x * tile;
+  const int64_t q1 = q0 + tile < BK ? q0 + tile : BK;
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += kSlotThreads) {
+    const int e = load_expert(idx, q, B, k, E);
+    if (e >= 0) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSlotThreads) hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block.  Thread (g, e) of G = 1024/Epad groups walks a contiguous range
+// of tiles for expert e.
+__global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
+    int32_t* __restrict__ hist, int n_tiles, int E, int Epad, int C, int D,
+    int32_t* __restrict__ expert_load, int32_t* __restrict__ expert_count,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
+  __shared__ int gsum[kScanThreads];
+  __shared__ int sc[kScanThreads];
+  const int tid = threadIdx.x;
+  const int G = kScanThreads / Epad;
+  const int g = tid / Epad, e = tid % Epad;
+  const bool live = g < G && e < E;
+  const int tpg = (n_tiles + G - 1) / (G > 0 ? G : 1);
+  const int tb = g * tpg;
+  const int te = tb + tpg < n_tiles ? tb + tpg : n_tiles;
+
+  int sum = 0;
+  if (live)
+    for (int t = tb; t < te; ++t) sum += hist[(int64_t)t * E + e];
+  gsum[tid] = sum;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  if (live) {
+    for (int g2 = 0; g2 < G; ++g2) {
+      const int v = gsum[g2 * Epad + e];
+      if (g2 < g) pre += v;
+      tot += v;
+    }
+    int run = pre;
+    for (int t = tb; t < te; ++t) {
+      const int v = hist[(int64_t)t * E + e];
+      hist[(int64_t)t * E + e] = run;
+      run += v;
+    }
+  }
+  int kept = 0;
+  if (g == 0 && e < E) {
+    kept = tot < C ? tot : C;
+    if (expert_load) expert_load[e] = tot;
+    expert_count[e] = kept;
+  }
+  sc[tid] = (g == 0) ? kept : 0;
+  __syncthreads();
+  for (int off = 1; off < Epad; off <<= 1) {
+    const int v = (tid < Epad && tid >= off) ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  // sc[i] is now the inclusive prefix over experts 0..i
+  for (int i = tid; i <= E; i += kScanThreads) expert_offset[i] = i == 0 ? 0 : sc[i - 1];
+  for (int r = tid; r <= D; r += kScanThreads) {
+    const int i = r * (E / D);
+    rank_offset[r] = i == 0 ? 0 : sc[i - 1];
+  }
+}
+
+__global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
+    const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C, int64_t BK,
+    int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ pos, uint8_t* __restrict__ keep, int32_t* __restrict__ dest,
+    int32_t* __restrict__ pack_src) {
+  extern __shared__ int sm[];
+  int* ebuf = sm;         // [tile] experts in claim order
+  int* wb = sm + tile;    // [4][E] per-wavefront counts, then running bases
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t q0 = (int64_t)blockIdx.x * tile;
+  const int64_t n = BK - q0 < tile ? BK - q0 : tile;
+  for (int i = tid; i < tile; i += kSlotThreads) ebuf[i] = i < n ? load_expert(idx, q0 + i, B, k, E) : -1;
+  for (int i = tid; i < 4 * E; i += kSlotThreads) wb[i] = 0;
+  __syncthreads();
+
+  const int S = tile / 4;  // contiguous share of each wavefront (multiple of 64)
+  const unsigned long long lt = lanemask_lt(lane);
+  int* mycnt = wb + wave * E;
+  for (int c = 0; c < S; c += 64) {
+    const int e = ebuf[wave * S + c + lane];
+    const unsigned long long m = match_expert(e, nbits);
+    if (e >= 0 && (m & lt) == 0) mycnt[e] += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kSlotThreads) {
+    int b = base[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int cnt = wb[w * E + e];
+      wb[w * E + e] = b;
+      b += cnt;
+    }
+  }
+  __syncthreads();
+  for (int c = 0; c < S; c += 64) {
+    const int i = wave * S + c + lane;
+    const int e = ebuf[i];
+    const unsigned long long m = match_expert(e, nbits);
+    const int rank = __popcll(m & lt);
+    int p = -1;
+    if (e >= 0) p = mycnt[e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && rank == 0) mycnt[e] = p + __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+    if (i < n) {
+      const int64_t q = q0 + i;
+      const int64_t j = q / B;
+      const int64_t t = q - j * B;
+      const int64_t o = t * k + j;
+      const bool kp = e >= 0 && p < C;
+      const int dr = kp ? expert_offset[e] + p : -1;
+      pos[o] = p;
+      keep[o] = kp ? 1 : 0;
+      dest[o] = dr;
+      if (kp) pack_src[dr] = (int32_t)t;
+    }
+  }
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
+                                                   const int32_t* __restrict__ dest, int64_t B,
+                                                   int k, int d, uint16_t* __restrict__ packed) {
+  const int cpr = d / 8;
+  const int64_t total = B * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / cpr;
+    const int c = (int)(i - t * cpr);
+    u32x4 v;
+    if (XBF16) {
+      v = *(const u32x4*)((const uint16_t*)x + t * d + c * 8);
+    } else {
+      const float* xf = (const float*)x + t * d + c * 8;
+      const f32x4 a = *(const f32x4*)xf;
+      const f32x4 b = *(const f32x4*)(xf + 4);
+      const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      v = pack8(f);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = dest[t * k + j];
+      if (r >= 0) *(u32x4*)(packed + (int64_t)r * d + c * 8) = v;
+    }
+  }
+}
+
+unsigned grid_for(int64_t work, int threads) {
+  int64_t g = (work + threads - 1) / threads;
+  if (g > (1 << 20)) g = 1 << 20;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+SlotPlan slot_plan(int64_t B, int k) {
+  SlotPlan p;
+  p.BK = B * k;
+  p.tile = 2048;
+  p.n_tiles = (int)((p.BK + p.tile - 1) / p.tile);
+  return p;
+}
+
+size_t slot_ws_bytes(int64_t B, int k, int E) {
+  const SlotPlan p = slot_plan(B, k);
+  return (size_t)(p.n_tiles > 0 ? p.n_tiles : 1) * E * sizeof(int32_t);
+}
+
+hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int D, int32_t* pos,
+                        uint8_t* keep, int32_t* dest, int32_t* expert_load, int32_t* expert_count,
+                        int32_t* expert_offset, int32_t* rank_offset, int32_t* pack_src,
+                        int32_t* ws_hist, hipStream_t s) {
+  const SlotPlan p = slot_plan(B, k);
+  int Epad = 1;
+  while (Epad < E) Epad <<= 1;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (p.n_tiles > 0) {
+    hipLaunchKernelGGL(slot_hist_kernel, dim3(p.n_tiles), dim3(kSlotThreads), E * sizeof(int), s,
+                       idx, B, k, E, p.BK, p.tile, ws_hist);
+  }
+  hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
+                     Epad, C, D, expert_load, expert_count, expert_offset, rank_offset);
+  if (p.n_tiles > 0) {
+    const size_t lds = (size_t)(p.tile + 4 * E) * sizeof(int);
+    hipLaunchKernelGGL(slot_rank_kernel, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx, B, k,
+                       E, nbits, C, p.BK, p.tile, ws_hist, expert_offset, pos, keep, dest,
+                       pack_src);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
+                       uint16_t* packed, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const unsigned g = grid_for(B * (d / 8), 256);
+  if (x_bf16)
+    hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
+  return hipGetLastError();
+}
+
+}  // namespace moek

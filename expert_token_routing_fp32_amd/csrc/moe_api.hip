@@ -1,0 +1,299 @@
+// C ABI of the MoE layer forward: host-side checks, capacity, workspace
+// layout and the launch order of the kernels.  Declared in include/moe.h.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+constexpr int32_t kMaxE = 1024;
+constexpr int32_t kMaxK = 16;
+constexpr int32_t kMaxDim = 1 << 16;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int32_t capacity_of(const moe_problem_t* p) {
+  if (p->C >= 0) return p->C;
+  return moe_capacity(p->B, p->k, p->E, p->c);
+}
+
+// rows one expert can hold: min(C, B) (a token picks an expert at most once)
+int64_t rows_per_expert(const moe_problem_t* p) {
+  const int64_t C = capacity_of(p);
+  return C < p->B ? C : p->B;
+}
+
+int64_t kmax_of(const moe_problem_t* p) {
+  const int64_t bk = p->B * p->k;
+  const int64_t ec = (int64_t)p->E * rows_per_expert(p);
+  return bk < ec ? bk : ec;
+}
+
+int64_t kloc_of(const moe_problem_t* p) {
+  const int64_t bk = p->B * p->k;
+  const int64_t ec = (int64_t)(p->e_end - p->e_begin) * rows_per_expert(p);
+  return bk < ec ? bk : ec;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+size_t ffn_ws(const moe_problem_t* p) { return align_up((size_t)kloc_of(p) * p->f * 2); }
+size_t dispatch_ws(const moe_problem_t* p) {
+  return align_up(moek::slot_ws_bytes(p->B, p->k, p->E));
+}
+
+// Workspace carving for moe_forward: fields the caller did not supply.
+struct Carve {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename T>
+  T* take(T* given, size_t bytes) {
+    if (given) return given;
+    T* r = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return r;
+  }
+};
+
+struct FwdBufs {
+  float* logits;
+  int32_t* idx;
+  float* w;
+  int32_t *pos, *dest;
+  uint8_t* keep;
+  int32_t *load, *count, *eo, *ro, *pack_src;
+  uint16_t* packed;
+  int32_t* hist;
+  uint16_t* H;
+};
+
+size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* ws, FwdBufs* b) {
+  moe_forward_out_t none;
+  std::memset(&none, 0, sizeof(none));
+  if (!o) o = &none;
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  const size_t BE = (size_t)p->B * p->E, BKn = (size_t)p->B * p->k;
+  const size_t km = (size_t)kmax_of(p);
+  FwdBufs t;
+  t.logits = c.take(o->logits, BE * 4);
+  t.idx = c.take(o->topk_idx, BKn * 4);
+  t.w = c.take(o->topk_w, BKn * 4);
+  t.pos = c.take(o->pos, BKn * 4);
+  t.keep = c.take(o->keep, BKn);
+  t.dest = c.take(o->dest, BKn * 4);
+  t.load = c.take(o->expert_load, (size_t)p->E * 4);
+  t.count = c.take(o->expert_count, (size_t)p->E * 4);
+  t.eo = c.take(o->expert_offset, (size_t)(p->E + 1) * 4);
+  t.ro = c.take(o->rank_offset, (size_t)(p->n_ranks + 1) * 4);
+  t.pack_src = c.take(o->pack_src, km * 4);
+  t.packed = c.take(reinterpret_cast<uint16_t*>(o->packed), km * p->d * 2);
+  t.hist = c.take<int32_t>(nullptr, dispatch_ws(p));
+  t.H = c.take<uint16_t>(nullptr, ffn_ws(p));
+  if (b) *b = t;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int64_t B, int32_t k, int32_t E, double c) {
+  if (B < 0 || k < 1 || E < 1 || !(c > 0.0) || !std::isfinite(c)) return -1;
+  if (B == 0) return 0;
+  const double v = std::ceil(((double)(B * k) / (double)E) * c);
+  if (!(v <= 2147483647.0)) return -1;
+  return (int32_t)v;
+}
+
+int32_t moe_problem_capacity(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return -1;
+  return capacity_of(p);
+}
+
+int64_t moe_max_kept(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return -1;
+  return kmax_of(p);
+}
+
+moe_status_t moe_validate(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID;
+  if (p->B < 0 || p->d < 8 || p->d % 8 || p->E < 1 || p->k < 1 || p->k > p->E)
+    return MOE_ERR_INVALID;
+  if (p->C < 0 && !(p->c > 0.0 && std::isfinite(p->c))) return MOE_ERR_INVALID;
+  if (p->n_ranks < 1 || p->E % p->n_ranks) return MOE_ERR_INVALID;
+  if (p->e_begin < 0 || p->e_end > p->E || p->e_begin > p->e_end) return MOE_ERR_INVALID;
+  if (p->f < 8 || p->f % 8) return MOE_ERR_INVALID;
+  if (p->act != MOE_GELU && p->act != MOE_SWIGLU) return MOE_ERR_INVALID;
+  if (p->x_dtype != MOE_F32 && p->x_dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (!(p->tau > 0.0f) || !std::isfinite(p->tau)) return MOE_ERR_INVALID;
+  if (p->add_residual != 0 && p->add_residual != 1) return MOE_ERR_INVALID;
+  if (p->E > kMaxE || p->k > kMaxK || p->d > kMaxDim || p->f > kMaxDim)
+    return MOE_ERR_UNSUPPORTED;
+  if (p->B > (int64_t)INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
+  if (p->C < 0 && moe_capacity(p->B, p->k, p->E, p->c) < 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op) {
+  if (moe_validate(p) != MOE_OK) return SIZE_MAX;
+  switch (op) {
+    case MOE_OP_DISPATCH:
+      return dispatch_ws(p);
+    case MOE_OP_FFN:
+      return ffn_ws(p);
+    case MOE_OP_FORWARD:
+      return carve_forward(p, nullptr, nullptr, nullptr);
+  }
+  return SIZE_MAX;
+}
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK:
+      return "ok";
+    case MOE_ERR_INVALID:
+      return "invalid argument";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported size";
+    case MOE_ERR_WORKSPACE:
+      return "workspace too small";
+    case MOE_ERR_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_gate(const moe_problem_t* p, const void* x, const float* Wg, const float* bias,
+                      float* logits, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!x || !Wg || !logits)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a4(Wg) || !a4(logits) || (bias && !a4(bias))))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_gate(x, p->x_dtype == MOE_BF16, Wg, bias, logits, p->B, p->d,
+                                      p->E, stream));
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* topk_idx,
+                       float* topk_w, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a4(logits) || !a4(topk_idx) || !a4(topk_w))) return MOE_ERR_INVALID;
+  return hip_status(moek::launch_route(logits, p->B, p->E, p->k, p->tau, topk_idx, topk_w, stream));
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                          int32_t* pos, uint8_t* keep, int32_t* dest, int32_t* expert_load,
+                          int32_t* expert_count, int32_t* expert_offset, int32_t* rank_offset,
+                          int32_t* pack_src, moe_bf16_t* packed, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!expert_count || !expert_offset || !rank_offset) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!x || !topk_idx || !pos || !keep || !dest || !pack_src || !packed))
+    return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a16(packed))) return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < dispatch_ws(p)) return MOE_ERR_WORKSPACE;
+  const int C = capacity_of(p);
+  hipError_t e = moek::launch_slots(topk_idx, p->B, p->k, p->E, C, p->n_ranks, pos, keep, dest,
+                                    expert_load, expert_count, expert_offset, rank_offset,
+                                    pack_src, static_cast<int32_t*>(ws), stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(
+      moek::launch_pack(x, p->x_dtype == MOE_BF16, dest, p->B, p->k, p->d, packed, stream));
+}
+
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
+                            const int32_t* expert_offset, const moe_bf16_t* W1,
+                            const moe_bf16_t* W3, const moe_bf16_t* W2, moe_bf16_t* ret,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool swiglu = p->act == MOE_SWIGLU;
+  const int n_local = p->e_end - p->e_begin;
+  if (!expert_offset || (p->B > 0 && (!packed || !ret))) return MOE_ERR_INVALID;
+  if (n_local > 0 && (!W1 || !W2 || (swiglu && !W3))) return MOE_ERR_INVALID;
+  if ((packed && !a16(packed)) || (ret && !a16(ret)) || (W1 && !a16(W1)) || (W2 && !a16(W2)) ||
+      (swiglu && W3 && !a16(W3)))
+    return MOE_ERR_INVALID;
+  const size_t need = ffn_ws(p);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (p->B == 0) return MOE_OK;
+  if (ret != packed) {
+    hipError_t e = moek::launch_copy_remote(packed, ret, expert_offset, p->E, p->e_begin,
+                                            p->e_end, kmax_of(p), p->d, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return hip_status(moek::launch_expert_ffn(
+      packed, expert_offset, p->e_begin, n_local, (int)rows_per_expert(p), p->d, p->f, swiglu,
+      W1, swiglu ? W3 : nullptr, W2, static_cast<uint16_t*>(ws), ret, stream));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const moe_bf16_t* ret, const int32_t* dest,
+                         const float* topk_w, const void* x_residual, void* y,
+                         hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!ret || !dest || !topk_w || !y)) return MOE_ERR_INVALID;
+  if (p->B > 0 && p->add_residual && !x_residual) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(ret) || !a16(y) || (p->add_residual && !a16(x_residual))))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_combine(ret, dest, topk_w, p->add_residual ? x_residual : nullptr,
+                                         p->x_dtype == MOE_BF16, y, p->B, p->k, p->d,
+                                         kmax_of(p), stream));
+}
+
+moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret, const int32_t* dest,
+                        moe_bf16_t* out, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!ret || !dest || !out)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(ret) || !a16(out))) return MOE_ERR_INVALID;
+  return hip_status(moek::launch_unpack(ret, dest, p->B, p->k, p->d, kmax_of(p), out, stream));
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg, const float* bias,
+                         const moe_bf16_t* W1, const moe_bf16_t* W3, const moe_bf16_t* W2,
+                         void* y, moe_forward_out_t* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool swiglu = p->act == MOE_SWIGLU;
+  const int n_local = p->e_end - p->e_begin;
+  if (p->B > 0 && (!x || !Wg || !y)) return MOE_ERR_INVALID;
+  if (n_local > 0 && (!W1 || !W2 || (swiglu && !W3))) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a16(y) || !a4(Wg) || (bias && !a4(bias)))) return MOE_ERR_INVALID;
+  if ((W1 && !a16(W1)) || (W2 && !a16(W2)) || (swiglu && W3 && !a16(W3))) return MOE_ERR_INVALID;
+  if (out && out->packed && !a16(out->packed)) return MOE_ERR_INVALID;
+  const size_t need = carve_forward(p, out, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  FwdBufs b;
+  carve_forward(p, out, ws, &b);
+  const bool xb = p->x_dtype == MOE_BF16;
+  const int C = capacity_of(p);
+  hipError_t e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, stream);
+  if (e == hipSuccess)
+    e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
+  if (e == hipSuccess)
+    e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->n_ranks, b.pos, b.keep, b.dest, b.load,
+                           b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
+  if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
+  if (e == hipSuccess && p->B > 0)
+    e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
+                                p->d, p->f, swiglu, W1, swiglu ? W3 : nullptr, W2, b.H, b.packed,
+                                stream);
+  if (e == hipSuccess)
+    e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
+                             p->k, p->d, kmax_of(p), stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

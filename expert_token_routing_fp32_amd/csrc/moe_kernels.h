@@ -1,0 +1,86 @@
+// Internal interface between the C ABI (moe_api.hip) and the gfx950 kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moek {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 helpers (raw 16-bit patterns, finite values) --------------------
+__device__ __forceinline__ float bf16_lo(unsigned int v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest, ties to even
+__device__ __forceinline__ unsigned int f32_to_bf16(float f) {
+  unsigned int u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+__device__ __forceinline__ void unpack8(u32x4 v, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = bf16_lo(v[i]);
+    o[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return r;
+}
+
+// ---- launchers --------------------------------------------------------------
+hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
+                       float* logits, int64_t B, int d, int E, hipStream_t s);
+
+hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,
+                        int32_t* idx, float* w, hipStream_t s);
+
+// slot assignment: tile geometry shared by the three kernels
+struct SlotPlan {
+  int64_t BK;      // B*k assignments
+  int tile;        // assignments per tile (multiple of 256)
+  int n_tiles;
+};
+SlotPlan slot_plan(int64_t B, int k);
+size_t slot_ws_bytes(int64_t B, int k, int E);
+
+hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int D,
+                        int32_t* pos, uint8_t* keep, int32_t* dest, int32_t* expert_load,
+                        int32_t* expert_count, int32_t* expert_offset, int32_t* rank_offset,
+                        int32_t* pack_src, int32_t* ws_hist, hipStream_t s);
+
+hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k,
+                       int d, uint16_t* packed, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
+                          const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
+                          int64_t kmax, hipStream_t s);
+
+hipError_t launch_unpack(const uint16_t* ret, const int32_t* dest, int64_t B, int k, int d,
+                         int64_t kmax, uint16_t* out, hipStream_t s);
+
+// rows of [0, expert_offset[E]) outside [expert_offset[e_begin], expert_offset[e_end])
+hipError_t launch_copy_remote(const uint16_t* src, uint16_t* dst, const int32_t* expert_offset,
+                              int E, int e_begin, int e_end, int64_t kmax, int d,
+                              hipStream_t s);
+
+// grouped expert MLP: H = act(X W1^T [, X W3^T]) then Out = H W2^T
+hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
+                             int n_local, int rows_max, int d, int f, bool swiglu,
+                             const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                             uint16_t* H, uint16_t* ret, hipStream_t s);
+
+}  // namespace moek

@@ -1,0 +1,112 @@
+// Softmax over E and top-k selection, one token per group of L lanes.
+//
+// "Expert Parallelism" (narrativegoldmine.com), "Formal Algorithm":
+// p_t = softmax(g_t / tau), e(t) = argmax p_t and w_t = p_{t,e(t)};
+// "Components and Architecture": the top-k experts of that distribution are
+// selected.  Experts are ranked by (logit descending, index ascending): the
+// order of the exact probabilities, since softmax is strictly increasing, with
+// ties to the lower index.  Ranking on the logits rather than on rounded fp32
+// probabilities keeps the choice exact.  The weights are the raw
+// probabilities of the chosen experts.
+//
+// A token's E logits are spread over L = min(64, pow2 >= E) lanes, V per lane.
+// Max, sum and each of the k arg-max rounds are butterfly reductions inside
+// the L-lane segment of the 64-wide wavefront.
+#include <climits>
+
+#include "moe_kernels.h"
+
+namespace moek {
+namespace {
+
+constexpr int kRouteThreads = 256;
+
+template <int L, int V>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const float* __restrict__ logits, int64_t B, int E, int k, float inv_tau,
+    int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int tid = threadIdx.x;
+  const int64_t t = ((int64_t)blockIdx.x * kRouteThreads + tid) / L;
+  const int li = tid % L;
+  const bool tok = t < B;
+
+  float v[V];
+  bool ok[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int e = li + u * L;
+    ok[u] = tok && e < E;
+    v[u] = ok[u] ? logits[t * E + e] : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (ok[u]) m = fmaxf(m, v[u]);
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (ok[u]) s += expf((v[u] - m) * inv_tau);
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
+
+  unsigned taken = 0u;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int e = li + u * L;
+      if (ok[u] && !((taken >> u) & 1u) && (v[u] > bv || (v[u] == bv && e < bi))) {
+        bv = v[u];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, L);
+      const int oi = __shfl_xor(bi, off, L);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi != INT_MAX && bi % L == li) taken |= 1u << (bi / L);
+    if (li == 0 && tok) {
+      idx[t * k + j] = bi;
+      w[t * k + j] = expf((bv - m) * inv_tau) / s;
+    }
+  }
+}
+
+template <int L, int V>
+hipError_t go(const float* logits, int64_t B, int E, int k, float tau, int32_t* idx, float* w,
+              hipStream_t s) {
+  const int64_t threads = B * L;
+  dim3 grid((unsigned)((threads + kRouteThreads - 1) / kRouteThreads));
+  hipLaunchKernelGGL((route_kernel<L, V>), grid, dim3(kRouteThreads), 0, s, logits, B, E, k,
+                     1.0f / tau, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau, int32_t* idx,
+                        float* w, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (E <= 1) return go<1, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 2) return go<2, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 4) return go<4, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 8) return go<8, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 16) return go<16, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 32) return go<32, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 64) return go<64, 1>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 128) return go<64, 2>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 256) return go<64, 4>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 512) return go<64, 8>(logits, B, E, k, tau, idx, w, s);
+  return go<64, 16>(logits, B, E, k, tau, idx, w, s);
+}
+
+}  // namespace moek

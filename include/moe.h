@@ -1,0 +1,244 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts layer forward.
+ *
+ * One MoE layer on one GPU's share of tokens, in the steps the pages give
+ * ("Expert Parallelism", narrativegoldmine.com, section "Formal Algorithm:
+ * Expert Parallelism Forward Pass"; "Expert Parallelism and the All-to-All
+ * Bottleneck", ashishsrivastav.com, section "The Mechanism of Expert
+ * Parallelism"):
+ *
+ *   moe_gate       router logits  g = x . Wg (+ b)                 (fp32)
+ *   moe_route      softmax over E, top-k choice and gate weights
+ *   moe_dispatch   per-expert capacity, slot assignment with drops, and the
+ *                  pack that stands in for the dispatch all-to-all
+ *   moe_expert_ffn grouped expert MLP on the packed rows (bf16 MFMA)
+ *   moe_combine    gate-weighted sum back into token order (the return
+ *                  all-to-all becomes the identity on one GPU)
+ *   moe_forward    all of the above, enqueued back to back
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is DEVICE memory unless stated otherwise; the
+ *   caller allocates every buffer (and the workspace) and keeps ownership.
+ *   The library allocates nothing and keeps no state between calls.
+ * - Every call only enqueues work on `stream` and returns; results are valid
+ *   once the stream reaches that point.  Nothing synchronizes the host.
+ * - All arguments are checked on the host before anything is enqueued; a
+ *   failed check returns an error code and enqueues nothing.  After the
+ *   launches, a launch failure reported by the HIP runtime returns
+ *   MOE_ERR_HIP.  Kernels have no device-side error path: integer inputs
+ *   that come from the caller (topk_idx, dest) are treated as "dropped" when
+ *   out of range rather than read out of bounds; float inputs are assumed
+ *   finite.
+ * - Row-major everywhere.  bf16 tensors are passed as raw 16-bit patterns
+ *   (moe_bf16_t).  Pointers used with 16-byte vector accesses (x, packed,
+ *   weights, y, ret, out) must be 16-byte aligned; d and f must be multiples
+ *   of 8.
+ * - Sizes: Kmax = min(B*k, E*C) bounds the number of kept assignments K; the
+ *   exact K is expert_offset[E], known only on the device.
+ * - Expert weights are stored output-major, one matrix per expert: W1 and W3
+ *   are [n_local][f][d] and W2 is [n_local][d][f], where
+ *   n_local = e_end - e_begin; expert e computes W2 . act(W1 . x) (GELU) or
+ *   W2 . (silu(W1 . x) * (W3 . x)) (SwiGLU), with no biases.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16_t; /* raw bf16 bits */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* a null required pointer, a bad size or field */
+  MOE_ERR_UNSUPPORTED = 2, /* valid, but outside the sizes the kernels handle */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act_t;
+
+/* Which call a workspace is sized for (moe_workspace_bytes). */
+typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_FFN = 1, MOE_OP_FORWARD = 2 } moe_op_t;
+
+/* The problem statement: B tokens of hidden size d, E experts, top-k routing
+ * with capacity factor c and per-expert capacity C = ceil((B*k/E)*c)
+ * ("Expert Parallelism", theinfinity.ai, capacity paragraph, read per
+ * expert); experts spread contiguously over n_ranks ranks, E/n_ranks each
+ * ("Expert Parallelism and the All-to-All Bottleneck", section "The
+ * All-to-All Communication Pattern"). */
+typedef struct {
+  int64_t B;          /* tokens (>= 0; 0 is an empty batch)                  */
+  int32_t d;          /* hidden size, multiple of 8                          */
+  int32_t E;          /* experts, 1..1024                                    */
+  int32_t k;          /* experts per token, 1..min(E, 16)                    */
+  double c;           /* capacity factor (> 0 when C < 0)                    */
+  int32_t C;          /* < 0: computed as ceil((B*k/E)*c); >= 0: used as is */
+  int32_t n_ranks;    /* D >= 1, E % D == 0; rank r owns [r*E/D, (r+1)*E/D) */
+  int32_t e_begin;    /* experts whose FFN runs on this GPU: [e_begin, e_end) */
+  int32_t e_end;
+  int32_t f;          /* expert FFN inner size, multiple of 8                */
+  int32_t act;        /* moe_act_t                                           */
+  int32_t x_dtype;    /* moe_dtype_t of x and y                              */
+  float tau;          /* softmax temperature (> 0), 1 by default             */
+  int32_t add_residual; /* 1: y = x + combine; 0: y = combine              */
+} moe_problem_t;
+
+/* ---- host-only helpers (no GPU work) ---------------------------------- */
+
+/* ceil((B*k/E)*c) in IEEE double, in that order; 0 when B == 0; -1 on bad
+ * arguments ("Expert Parallelism", theinfinity.ai, capacity paragraph). */
+int32_t moe_capacity(int64_t B, int32_t k, int32_t E, double c);
+
+/* The capacity the problem uses (C if C >= 0, else moe_capacity), or -1. */
+int32_t moe_problem_capacity(const moe_problem_t* p);
+
+/* min(B*k, E*C): rows the packed buffer must hold; -1 on a bad problem. */
+int64_t moe_max_kept(const moe_problem_t* p);
+
+/* Checks every field; MOE_OK or the error code a call would return. */
+moe_status_t moe_validate(const moe_problem_t* p);
+
+/* Workspace bytes `op` needs for problem p (0 if none; SIZE_MAX if p is
+ * invalid).  The workspace is scratch owned by the caller; its contents on
+ * entry do not matter. */
+size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op);
+
+/* Static description of a status code. */
+const char* moe_status_str(moe_status_t s);
+
+/* ---- the path --------------------------------------------------------- */
+
+/* Router logits ("Expert Parallelism", narrativegoldmine.com, "Formal
+ * Algorithm", gate computation; "Components and Architecture": a learned
+ * linear map with an optional bias on the logits).
+ *   x      [B][d]  float32 (x_dtype F32) or bf16 (BF16)
+ *   Wg     [d][E]  float32
+ *   bias   [E]     float32, or NULL for none
+ *   logits [B][E]  float32, out
+ * Computed in fp32 on the vector ALUs with blocked accumulation. */
+moe_status_t moe_gate(const moe_problem_t* p, const void* x, const float* Wg,
+                      const float* bias, float* logits, hipStream_t stream);
+
+/* Softmax over E and top-k ("Formal Algorithm": p_t = softmax(g_t / tau),
+ * e(t) = argmax p_t, w_t = p_{t,e(t)}; "Components and Architecture": the
+ * top-k experts are selected).  Experts are ranked by (logit descending,
+ * index ascending): the exact-probability order with ties to the lower
+ * index.  topk_w holds the raw (not renormalised) probabilities; choice j = 0
+ * is the strongest.
+ *   logits   [B][E] float32, in
+ *   topk_idx [B][k] int32, out
+ *   topk_w   [B][k] float32, out */
+moe_status_t moe_route(const moe_problem_t* p, const float* logits,
+                       int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Capacity-limited slot assignment and pack ("Expert Parallelism",
+ * theinfinity.ai, capacity paragraph: tokens past C are dropped, overflow
+ * max(0, n_e - C); "Expert Parallelism and the All-to-All Bottleneck", "The
+ * Mechanism of Expert Parallelism": rows repacked per destination expert).
+ * Assignment (t, j) claims its expert's next slot in the order q = j*B + t;
+ * pos is its slot, keep = pos < C.  Kept rows are packed compactly,
+ * expert-major (so rank-major), in claim order.
+ *   x             [B][d]   f32 or bf16 (f32 is rounded to nearest-even bf16)
+ *   topk_idx      [B][k]   int32 in [0, E) (others count as dropped)
+ *   pos           [B][k]   int32 out (slot; -1 for an out-of-range index)
+ *   keep          [B][k]   uint8 out
+ *   dest          [B][k]   int32 out: packed row, or -1 when dropped
+ *   expert_load   [E]      int32 out n_e (assignments routed), may be NULL
+ *   expert_count  [E]      int32 out min(n_e, C)
+ *   expert_offset [E+1]    int32 out exclusive prefix sum of expert_count
+ *   rank_offset   [D+1]    int32 out expert_offset[r*E/D]
+ *   pack_src      [Kmax]   int32 out token of each packed row
+ *   packed        [Kmax][d] bf16 out
+ *   ws / ws_bytes          workspace, >= moe_workspace_bytes(p, MOE_OP_DISPATCH)
+ * Deterministic: no result depends on the order of atomic operations. */
+moe_status_t moe_dispatch(const moe_problem_t* p, const void* x,
+                          const int32_t* topk_idx, int32_t* pos, uint8_t* keep,
+                          int32_t* dest, int32_t* expert_load,
+                          int32_t* expert_count, int32_t* expert_offset,
+                          int32_t* rank_offset, int32_t* pack_src,
+                          moe_bf16_t* packed, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Grouped expert MLP ("Expert Parallelism", narrativegoldmine.com,
+ * "Components and Architecture", Expert GEMM; "Formal Algorithm", expert
+ * computation on the received tokens).  For every expert e in
+ * [e_begin, e_end) and its packed rows [expert_offset[e], expert_offset[e+1]):
+ * ret = W2 . act(W1 . x), with bf16 operands, fp32 accumulation and the
+ * hidden activation stored as bf16 in the workspace.  Rows of other experts
+ * come back unchanged (the missing collective is the identity): with
+ * ret == packed nothing is copied, otherwise they are copied to ret.
+ *   packed        [Kmax][d] bf16 in
+ *   expert_offset [E+1]     int32 in (as written by moe_dispatch)
+ *   W1, W3        [n_local][f][d] bf16 (W3 only for SwiGLU, else NULL)
+ *   W2            [n_local][d][f] bf16
+ *   ret           [Kmax][d] bf16 out; may alias packed
+ *   ws / ws_bytes workspace, >= moe_workspace_bytes(p, MOE_OP_FFN) */
+moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
+                            const int32_t* expert_offset, const moe_bf16_t* W1,
+                            const moe_bf16_t* W3, const moe_bf16_t* W2,
+                            moe_bf16_t* ret, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Gate-weighted combine back into token order ("Components and
+ * Architecture", expert combine; "Formal Algorithm", residual addition):
+ * y[t] = sum_{j<k, dest[t,j]>=0} topk_w[t,j] * ret[dest[t,j]]  (+ x[t]),
+ * accumulated in fp32 in j order.  A token whose choices were all dropped
+ * gets 0 (or x[t] with the residual).
+ *   ret        [Kmax][d] bf16
+ *   dest       [B][k] int32 (as written by moe_dispatch)
+ *   topk_w     [B][k] float32
+ *   x_residual [B][d] x_dtype, required iff add_residual, else ignored
+ *   y          [B][d] x_dtype out */
+moe_status_t moe_combine(const moe_problem_t* p, const moe_bf16_t* ret,
+                         const int32_t* dest, const float* topk_w,
+                         const void* x_residual, void* y, hipStream_t stream);
+
+/* Inverse of the pack: out[t][j] = ret[dest[t][j]], zeros where dropped
+ * ("The Mechanism of Expert Parallelism": rows return to the original token
+ * order).  A checking aid; out is [B][k][d] bf16. */
+moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret,
+                        const int32_t* dest, moe_bf16_t* out,
+                        hipStream_t stream);
+
+/* Optional outputs of moe_forward; any NULL field lives in the workspace. */
+typedef struct {
+  float* logits;          /* [B][E]   */
+  int32_t* topk_idx;      /* [B][k]   */
+  float* topk_w;          /* [B][k]   */
+  int32_t* pos;           /* [B][k]   */
+  uint8_t* keep;          /* [B][k]   */
+  int32_t* dest;          /* [B][k]   */
+  int32_t* expert_load;   /* [E]      */
+  int32_t* expert_count;  /* [E]      */
+  int32_t* expert_offset; /* [E+1]    */
+  int32_t* rank_offset;   /* [D+1]    */
+  int32_t* pack_src;      /* [Kmax]   */
+  moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
+                             outputs overwrite the local rows in place) */
+} moe_forward_out_t;
+
+/* The whole layer, enqueued on one stream with no host synchronisation:
+ * gate, route, dispatch, expert FFN (in place on the packed rows), combine.
+ *   x [B][d] x_dtype; Wg [d][E] f32; bias [E] f32 or NULL;
+ *   W1/W3/W2 as in moe_expert_ffn; y [B][d] x_dtype out;
+ *   out may be NULL; ws >= moe_workspace_bytes(p, MOE_OP_FORWARD). */
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
+                         const float* bias, const moe_bf16_t* W1,
+                         const moe_bf16_t* W3, const moe_bf16_t* W2, void* y,
+                         moe_forward_out_t* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -160,6 +160,8 @@ def softmax(logits: np.ndarray, tau: float = 1.0) -> np.ndarray:
     equal logits give 1/E, shift invariance, closed-form worked-example
     weights (test_oracle_route)."""
     z = np.asarray(logits, dtype=np.float32).astype(np.float64) / float(tau)
+    if z.shape[0] == 0:
+        return z
     z = z - z.max(axis=1, keepdims=True)
     ez = np.exp(z)
     return ez / ez.sum(axis=1, keepdims=True)
@@ -328,38 +330,32 @@ def expert_mlp(xr: np.ndarray, W1: np.ndarray, W2: np.ndarray,
 def expert_ffn(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
                e_begin: int, e_end: int, W1, W2, W3, act: str,
                rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Return buffer ret [K, d] in float64.
+    """Return buffer ret in float64: [K, d], or [len(rows), d] for the packed
+    rows listed in ``rows`` (spot checks at full size).
 
     Rows of experts in [e_begin, e_end) get that expert's MLP of the token's
     defined input x (bf16 values, or the float32 originals for an f32
     workload); every other row comes back as its packed bf16 value (the
-    missing collective is the identity).  ``rows`` optionally restricts the
-    work to a subset of packed rows (others are NaN) for spot checks at full
-    size.  [EP-notes] "Formal Algorithm", expert computation on received
-    tokens; [EP-a2a] "The Mechanism of Expert Parallelism", phase 3."""
+    missing collective is the identity).  [EP-notes] "Formal Algorithm",
+    expert computation on received tokens; [EP-a2a] "The Mechanism of
+    Expert Parallelism", phase 3."""
     pack_src = np.asarray(pack_src, dtype=np.int64)
     K = pack_src.shape[0]
-    d = x.shape[1]
-    want = np.ones(K, dtype=bool) if rows is None else np.zeros(K, dtype=bool)
-    if rows is not None:
-        want[np.asarray(rows, dtype=np.int64)] = True
-    ret = np.full((K, d), np.nan)
-    xv_rows = lambda r: _x_values(x[pack_src[r]])
+    r_all = np.arange(K) if rows is None else np.asarray(rows, dtype=np.int64)
+    ret = np.empty((r_all.size, x.shape[1]))
     lo, hi = int(expert_offset[e_begin]), int(expert_offset[e_end])
     # rows owned by other ranks: identity loopback of the packed bf16 value
-    remote = np.ones(K, dtype=bool)
-    remote[lo:hi] = False
-    rr = np.nonzero(remote & want)[0]
-    if rr.size:
-        ret[rr] = bf16_bits_to_f64(pack(x, pack_src[rr]))
+    remote = (r_all < lo) | (r_all >= hi)
+    if remote.any():
+        ret[remote] = bf16_bits_to_f64(pack(x, pack_src[r_all[remote]]))
     for e in range(e_begin, e_end):
         a, b = int(expert_offset[e]), int(expert_offset[e + 1])
-        r = np.arange(a, b)[want[a:b]]
-        if r.size == 0:
+        sel = np.nonzero((r_all >= a) & (r_all < b))[0]
+        if sel.size == 0:
             continue
         i = e - e_begin
-        ret[r] = expert_mlp(xv_rows(r), W1[i], W2[i],
-                            None if W3 is None else W3[i], act)
+        ret[sel] = expert_mlp(_x_values(x[pack_src[r_all[sel]]]), W1[i], W2[i],
+                              None if W3 is None else W3[i], act)
     return ret
 
 
@@ -368,7 +364,8 @@ def expert_ffn(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
 # ----------------------------------------------------------------------------
 def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
             x_residual: Optional[np.ndarray] = None,
-            tokens: Optional[np.ndarray] = None) -> np.ndarray:
+            tokens: Optional[np.ndarray] = None,
+            ret_rows: Optional[np.ndarray] = None) -> np.ndarray:
     """y[t] = sum_j [kept] w[t, j] * ret[dest[t, j]] (+ x[t]), float64.
 
     [EP-notes] "Components and Architecture", expert combine: the k outputs
@@ -376,22 +373,24 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
     original token order ([EP-a2a] gather phase); a dropped assignment
     contributes nothing, so a token with every choice dropped gets 0 (plus
     the residual when it is added).  ``w`` is taken at float32 precision,
-    the precision the router reports it in.  ``tokens`` restricts the
-    output rows (others NaN).  Pins: dense soft-mixture equivalence without
-    drops, C = 0 gives 0 (test_oracle_combine)."""
+    the precision the router reports it in.
+
+    ``tokens`` restricts the output to those tokens ([len(tokens), d]);
+    ``ret_rows`` says which packed rows ``ret`` holds (sorted), when it holds
+    only some.  Pins: dense soft-mixture equivalence without drops, C = 0
+    gives 0 (test_oracle_combine_special)."""
     B, k = dest.shape
     tt = np.arange(B) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    y = np.full((B, ret.shape[1]), np.nan)
     acc = np.zeros((tt.size, ret.shape[1]))
     w32 = np.asarray(w, dtype=np.float32).astype(np.float64)
     for j in range(k):
-        dj = dest[tt, j]
+        dj = dest[tt, j].astype(np.int64)
         m = dj >= 0
-        acc[m] += w32[tt[m], j][:, None] * ret[dj[m]]
+        r = dj[m] if ret_rows is None else np.searchsorted(ret_rows, dj[m])
+        acc[m] += w32[tt[m], j][:, None] * ret[r]
     if x_residual is not None:
         acc += _x_values(x_residual[tt])
-    y[tt] = acc
-    return y
+    return acc
 
 
 # ----------------------------------------------------------------------------
@@ -400,13 +399,14 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
 def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
             n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
             tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
-            logits: Optional[np.ndarray] = None, ffn_rows=None, tokens=None) -> dict:
+            logits: Optional[np.ndarray] = None) -> dict:
     """All steps in the pages' order ([EP-notes] "Formal Algorithm";
     [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
     and slots, pack, expert FFN, unpack + weighted combine (+ residual).
 
     ``logits`` may be given to skip the gate (routing tests feed the router
-    directly); ``ffn_rows``/``tokens`` restrict the float work to samples."""
+    directly); without expert weights only the integer steps and the pack
+    run."""
     B = x.shape[0]
     E = Wg.shape[1] if Wg is not None else logits.shape[1]
     e_end = E if e_end is None else e_end
@@ -423,10 +423,7 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
                rank_offset=rank_offset, dest=dest, pack_src=pack_src,
                packed=packed)
     if W1 is not None:
-        ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3,
-                         act, rows=ffn_rows)
+        ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3, act)
         out["ret"] = ret
-        if tokens is not None or ffn_rows is None:
-            out["y"] = combine(ret, dest, w, x if add_residual else None,
-                               tokens=tokens)
+        out["y"] = combine(ret, dest, w, x if add_residual else None)
     return out

@@ -1,0 +1,140 @@
+"""The C ABI, checked without a GPU: the library loads, exports every function
+include/moe.h declares, the ctypes struct matches the C layout, and the
+host-only helpers agree with the oracle's capacity and reject bad problems."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from expert_token_routing_fp32_amd import _lib
+    return _lib
+
+
+@pytest.fixture(scope="module")
+def lib(L):
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "moe_forward" in names and "moe_dispatch" in names and len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_ctypes_layout_matches_c(L, tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    fields = [f for f, _ in L.Problem._fields_]
+    ofields = [f for f, _ in L.ForwardOut._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){",
+             'printf("%zu\\n", sizeof(moe_problem_t));']
+    lines += [f'printf("%zu\\n", offsetof(moe_problem_t, {f}));' for f in fields]
+    lines += ['printf("%zu\\n", sizeof(moe_forward_out_t));']
+    lines += [f'printf("%zu\\n", offsetof(moe_forward_out_t, {f}));' for f in ofields]
+    lines += ["return 0;}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    r = subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(c), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("cannot compile against the HIP headers: " + r.stderr[-300:])
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(L.Problem)] + [getattr(L.Problem, f).offset for f in fields]
+    want += [ctypes.sizeof(L.ForwardOut)] + [getattr(L.ForwardOut, f).offset for f in ofields]
+    assert vals == want
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(0, 1 << 20), st.integers(1, 16), st.integers(1, 1024),
+       st.sampled_from([0.5, 1.0, 1.1, 1.25, 1.5, 2.0, 0.3, 3.7]))
+def test_capacity_matches_oracle(B, k, E, c):
+    from expert_token_routing_fp32_amd import _lib
+    lib = _lib.load()
+    assert lib.moe_capacity(B, k, E, c) == oracle.capacity(B, k, E, c)
+
+
+def _prob(L, **kw):
+    base = dict(B=64, d=32, E=8, k=2, c=1.25, C=-1, n_ranks=2, e_begin=0, e_end=8, f=48,
+                act=L.MOE_GELU, x_dtype=L.MOE_BF16, tau=1.0, add_residual=0)
+    base.update(kw)
+    return L.Problem(**base)
+
+
+@pytest.mark.parametrize("change,code", [
+    ({}, 0),
+    ({"B": 0}, 0),
+    ({"B": -1}, 1), ({"d": 12}, 1), ({"d": 0}, 1), ({"E": 0}, 1), ({"k": 0}, 1), ({"k": 9}, 1),
+    ({"c": 0.0}, 1), ({"c": 0.0, "C": 5}, 0), ({"n_ranks": 3}, 1), ({"n_ranks": 0}, 1),
+    ({"e_begin": 3, "e_end": 2}, 1), ({"e_end": 9}, 1), ({"f": 4}, 1), ({"act": 7}, 1),
+    ({"x_dtype": 5}, 1), ({"tau": 0.0}, 1), ({"add_residual": 2}, 1),
+    ({"E": 2048, "e_end": 2048, "n_ranks": 1}, 2), ({"k": 17, "E": 32, "e_end": 32}, 2),
+    ({"B": 1 << 30, "k": 4}, 2),
+])
+def test_validate_codes(L, lib, change, code):
+    p = _prob(L, **change)
+    assert lib.moe_validate(ctypes.byref(p)) == code
+    if code:
+        assert lib.moe_workspace_bytes(ctypes.byref(p), L.MOE_OP_FORWARD) == ctypes.c_size_t(-1).value
+        assert lib.moe_max_kept(ctypes.byref(p)) == -1
+
+
+def test_max_kept_and_workspace(L, lib):
+    p = _prob(L)
+    C = oracle.capacity(64, 2, 8, 1.25)
+    assert lib.moe_problem_capacity(ctypes.byref(p)) == C
+    assert lib.moe_max_kept(ctypes.byref(p)) == min(64 * 2, 8 * min(C, 64))
+    p2 = _prob(L, C=3)
+    assert lib.moe_max_kept(ctypes.byref(p2)) == 8 * 3
+    for op in (L.MOE_OP_DISPATCH, L.MOE_OP_FFN, L.MOE_OP_FORWARD):
+        assert 0 < lib.moe_workspace_bytes(ctypes.byref(p), op) < 1 << 30
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.moe_status_str(code)
+
+
+def test_calls_reject_before_launch(L, lib):
+    """Invalid problems and missing buffers are refused on the host; no GPU
+    is touched (this runs without one)."""
+    bad = _prob(L, E=0)
+    nul = None
+    assert lib.moe_route(ctypes.byref(bad), nul, nul, nul, nul) == L.MOE_ERR_INVALID
+    p = _prob(L)
+    assert lib.moe_route(ctypes.byref(p), nul, nul, nul, nul) == L.MOE_ERR_INVALID
+    assert lib.moe_gate(ctypes.byref(p), nul, nul, nul, nul, nul) == L.MOE_ERR_INVALID
+    assert lib.moe_combine(ctypes.byref(p), nul, nul, nul, nul, nul, nul) == L.MOE_ERR_INVALID
+    assert lib.moe_unpack(ctypes.byref(p), nul, nul, nul, nul) == L.MOE_ERR_INVALID
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: the workspace check fails first
+    r = lib.moe_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                         fake, fake, None, 0, None)
+    assert r == L.MOE_ERR_WORKSPACE
+    r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, None, fake, fake, None, None, 0,
+                        None)
+    assert r == L.MOE_ERR_WORKSPACE
+    unaligned = ctypes.c_void_p((1 << 20) + 2)
+    r = lib.moe_gate(ctypes.byref(p), unaligned, fake, None, fake, None)
+    assert r == L.MOE_ERR_INVALID

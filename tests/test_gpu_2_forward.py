@@ -1,0 +1,97 @@
+"""End-to-end moe_forward against the oracle, with the launch configuration
+bench.py times (one stream, in-place expert outputs, workspace outputs).
+
+The GPU computes the router logits in fp32 and the oracle rounds an exact
+float64 sum, so a token whose top-(k+1) logits are closer than the logit
+tolerance may legitimately be routed differently.  Such tokens are found from
+the oracle's logits alone ("undecided"); every other token must be routed
+identically.  When all tokens agree, every integer output must match bit for
+bit.  Outputs y are compared on tokens whose choices and drop flags agree
+(all of them, normally) -- y of a token depends only on its own choices,
+weights and drop flags."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_synth import ORDER
+from _helpers import (TOL_F32, assert_bf16_close, assert_f32_close, problem_for, say, to_dev,
+                      to_np, weights_for_gpu, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def undecided_tokens(logits: np.ndarray, k: int, tol: float = TOL_F32) -> np.ndarray:
+    """Tokens whose ordered top-(k+1) logits have a gap within twice the
+    tolerance (so the fp32 gate may order them either way)."""
+    l = np.sort(logits.astype(np.float64), axis=1)[:, ::-1]
+    m = min(k + 1, l.shape[1])
+    top = l[:, :m]
+    gaps = top[:, :-1] - top[:, 1:]
+    band = 2 * tol * np.maximum(1.0, np.abs(top[:, :-1]))
+    return np.nonzero((gaps <= band).any(axis=1))[0] if m > 1 else np.zeros(0, dtype=np.int64)
+
+
+def run_forward(w, inp, ref, name, n_sample=48):
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    W1, W3, W2 = weights_for_gpu(inp)
+    p = problem_for(w)
+    x = to_dev(inp["x"])
+    y, o = moe.forward(p, x, to_dev(inp["Wg"]), None if inp["bias"] is None else to_dev(inp["bias"]),
+                       to_dev(W1), None if W3 is None else to_dev(W3), to_dev(W2), outputs=True)
+    torch.cuda.synchronize()
+    assert_f32_close(to_np(o["logits"]), ref["logits"], what=f"{name} logits")
+    und = undecided_tokens(ref["logits"], w.k)
+    gi = to_np(o["topk_idx"])
+    diff = np.nonzero((gi != ref["idx"]).any(axis=1))[0]
+    say(f"  {name}: undecided tokens {und.size}, tokens routed differently {diff.size}")
+    assert np.isin(diff, und).all(), "a decided token was routed differently"
+    assert_f32_close(to_np(o["topk_w"])[np.setdiff1d(np.arange(w.B), diff)],
+                     ref["w"][np.setdiff1d(np.arange(w.B), diff)], what=f"{name} topk_w")
+    gkeep = to_np(o["keep"]).astype(bool)
+    if diff.size == 0:
+        for key in ("pos", "dest", "expert_load", "expert_count", "expert_offset",
+                    "rank_offset"):
+            np.testing.assert_array_equal(to_np(o[key]), ref[key], err_msg=key)
+        np.testing.assert_array_equal(gkeep, ref["keep"])
+        K = int(ref["expert_offset"][-1])
+        np.testing.assert_array_equal(to_np(o["pack_src"])[:K], ref["pack_src"])
+    # a moved choice shifts at most one keep decision in each of two experts
+    kdiff = np.nonzero((gkeep != ref["keep"]).any(axis=1) | (gi != ref["idx"]).any(axis=1))[0]
+    assert kdiff.size <= 3 * diff.size
+    agree = np.setdiff1d(np.arange(w.B), kdiff)
+    # y on sampled agreeing tokens (all of them for the small workloads)
+    if w.B * w.f <= 4096 * 4096:
+        tokens = agree
+    else:
+        rng = np.random.default_rng(2)
+        tokens = np.sort(rng.choice(agree, size=min(n_sample, agree.size), replace=False))
+    dsub = ref["dest"][tokens]
+    rows = np.unique(dsub[dsub >= 0])
+    ret = oracle.expert_ffn(inp["x"], ref["pack_src"], ref["expert_offset"], w.e_begin, w.e_end,
+                            inp["W1"], inp["W2"], inp["W3"], w.act, rows=rows)
+    exp = oracle.combine(ret, ref["dest"], ref["w"], tokens=tokens, ret_rows=rows)
+    yg = to_np(y[torch.from_numpy(tokens).to(y.device)])
+    got = oracle.bf16_bits_to_f64(yg) if yg.dtype == np.uint16 else yg.astype(np.float64)
+    assert_bf16_close(got, exp, what=f"{name} y ({tokens.size} tokens)")
+    return y, o
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_forward(name):
+    say(f"[forward {name}]")
+    w, inp, ref = workload(name)
+    run_forward(w, inp, ref, name)
+
+
+def test_forward_is_deterministic():
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    w, inp, ref = workload("uniform")
+    W1, W3, W2 = weights_for_gpu(inp)
+    p = problem_for(w)
+    args = (to_dev(inp["x"]), to_dev(inp["Wg"]), None, to_dev(W1), None, to_dev(W2))
+    y1 = moe.forward(p, *args)
+    y2 = moe.forward(p, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
