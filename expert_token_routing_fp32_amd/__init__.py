@@ -22,8 +22,8 @@ from . import _lib as L
 from ._lib import MoEError, Problem  # noqa: F401
 
 __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
-           "workspace_bytes", "gate", "route", "dispatch", "expert_ffn", "combine",
-           "unpack", "forward", "MoEError", "Problem", "lib"]
+           "workspace_bytes", "weights_bytes", "pack_weights", "gate", "route", "dispatch",
+           "expert_ffn", "combine", "unpack", "forward", "MoEError", "Problem", "lib"]
 
 
 def lib():
@@ -60,6 +60,10 @@ def validate(p: Problem) -> int:
 def workspace_bytes(p: Problem, op: str = "forward") -> int:
     o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD}[op]
     return lib().moe_workspace_bytes(ctypes.byref(p), o)
+
+
+def weights_bytes(p: Problem) -> int:
+    return lib().moe_weights_bytes(ctypes.byref(p))
 
 
 # ---------------------------------------------------------------------------
@@ -155,27 +159,43 @@ def dispatch(p: Problem, x, topk_idx, ws=None) -> dict:
     return o
 
 
-def expert_ffn(p: Problem, packed, expert_offset, W1, W3, W2, ret=None, ws=None):
-    """ret = expert MLP of the local experts' rows; other rows copied (or
-    left in place when ``ret is packed``)."""
+def pack_weights(p: Problem, W1, W3, W2, out=None):
+    """The local experts' weights (W1, W3: [n_local, f, d]; W2: [n_local, d, f],
+    bf16) in the blocked layout the expert GEMM streams; done once per model."""
     _check(p)
-    d, f, E = p.d, p.f, p.E
+    d, f = p.d, p.f
     nl = p.e_end - p.e_begin
-    km = max_kept(p)
-    _need(packed, "packed", km * d, 2)
-    _need(expert_offset, "expert_offset", E + 1, 4)
+    n = weights_bytes(p)
+    dev = W2.device if W2 is not None else torch.device("cuda")
+    if out is None:
+        out = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    _need(out, "wpacked", n, 1)
     if nl > 0:
         _need(W1, "W1", nl * f * d, 2)
         _need(W2, "W2", nl * d * f, 2)
         if p.act == L.MOE_SWIGLU:
             _need(W3, "W3", nl * f * d, 2)
+    L.check(lib().moe_pack_weights(ctypes.byref(p), _p(W1), _p(W3 if p.act == L.MOE_SWIGLU else None),
+                                   _p(W2), _p(out), out.numel(), _stream()), "moe_pack_weights")
+    return out
+
+
+def expert_ffn(p: Problem, packed, expert_offset, wpacked, ret=None, ws=None):
+    """ret = expert MLP of the local experts' rows; other rows copied (or
+    left in place when ``ret is packed``).  ``wpacked`` from pack_weights."""
+    _check(p)
+    d, E = p.d, p.E
+    km = max_kept(p)
+    _need(packed, "packed", km * d, 2)
+    _need(expert_offset, "expert_offset", E + 1, 4)
+    if p.e_end > p.e_begin:
+        _need(wpacked, "wpacked", weights_bytes(p), 1)
     if ret is None:
         ret = torch.empty_like(packed)
     _need(ret, "ret", km * d, 2)
     ws = _ws(p, "ffn", ws, packed.device)
-    L.check(lib().moe_expert_ffn(ctypes.byref(p), _p(packed), _p(expert_offset), _p(W1),
-                                 _p(W3 if p.act == L.MOE_SWIGLU else None), _p(W2), _p(ret),
-                                 _p(ws), ws.numel(), _stream()), "moe_expert_ffn")
+    L.check(lib().moe_expert_ffn(ctypes.byref(p), _p(packed), _p(expert_offset), _p(wpacked),
+                                 _p(ret), _p(ws), ws.numel(), _stream()), "moe_expert_ffn")
     return ret
 
 
@@ -213,23 +233,19 @@ _OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_lo
                "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")
 
 
-def forward(p: Problem, x, Wg, bias, W1, W3, W2, y=None, outputs: bool = False, ws=None):
-    """The whole layer on the current stream.  With ``outputs`` the
-    intermediate tensors are allocated and returned too (``packed`` then holds
-    the expert outputs of the local rows, in place)."""
+def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None):
+    """The whole layer on the current stream (``wpacked`` from pack_weights).
+    With ``outputs`` the intermediate tensors are allocated and returned too
+    (``packed`` then holds the expert outputs of the local rows, in place)."""
     _check(p)
-    B, d, E, k, f = p.B, p.d, p.E, p.k, p.f
-    nl = p.e_end - p.e_begin
+    B, d, E, k = p.B, p.d, p.E, p.k
     dev = x.device
     _need(x, "x", B * d, _xsize(p))
     _need(Wg, "Wg", d * E, 4)
     if bias is not None:
         _need(bias, "bias", E, 4)
-    if nl > 0:
-        _need(W1, "W1", nl * f * d, 2)
-        _need(W2, "W2", nl * d * f, 2)
-        if p.act == L.MOE_SWIGLU:
-            _need(W3, "W3", nl * f * d, 2)
+    if p.e_end > p.e_begin:
+        _need(wpacked, "wpacked", weights_bytes(p), 1)
     if y is None:
         y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
                         device=dev)
@@ -252,8 +268,7 @@ def forward(p: Problem, x, Wg, bias, W1, W3, W2, y=None, outputs: bool = False, 
     if ws is None:
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     _need(ws, "ws", 1, 1)
-    L.check(lib().moe_forward(ctypes.byref(p), _p(x), _p(Wg), _p(bias), _p(W1),
-                              _p(W3 if p.act == L.MOE_SWIGLU else None), _p(W2), _p(y),
+    L.check(lib().moe_forward(ctypes.byref(p), _p(x), _p(Wg), _p(bias), _p(wpacked), _p(y),
                               ctypes.byref(outp) if outp is not None else None, _p(ws),
                               ws.numel(), _stream()), "moe_forward")
     return (y, o) if outputs else y

@@ -62,11 +62,13 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_P, _V, _V, _V, _V]),
     "moe_dispatch": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),
-    "moe_expert_ffn": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "moe_weights_bytes": (ctypes.c_size_t, [_P]),
+    "moe_pack_weights": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "moe_expert_ffn": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "moe_combine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "moe_unpack": (ctypes.c_int, [_P, _V, _V, _V, _V]),
-    "moe_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.POINTER(ForwardOut),
-                                   _V, ctypes.c_size_t, _V]),
+    "moe_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.POINTER(ForwardOut), _V,
+                                   ctypes.c_size_t, _V]),
 }
 
 _lib = None

@@ -8,30 +8,34 @@
 //
 // Two launches per call, each a grouped GEMM over the experts' contiguous
 // packed segments (rows [expert_offset[e], expert_offset[e+1])):
-//   GEMM1  H   = act(X . W1^T)              (GELU)   or
-//          H   = silu(X . W1^T) * (X . W3^T) (SwiGLU, both products in one tile)
+//   GEMM1  H   = act(X . W1^T)               (GELU)   or
+//          H   = silu(X . W1^T) * (X . W3^T)  (SwiGLU, both products in one tile)
 //   GEMM2  Out = H . W2^T
-// with W stored output-major ([N][K], the contraction index contiguous), so
-// both operands of every MFMA are read along K.
 //
-// Tile: 256 rows x 256 output columns (128 for SwiGLU), K stages of 64.
-//  * The rows of one expert are usually <= 256 (C is 160 / 256 / 1280 / 2048 in
-//    the workloads), so one tile row covers the whole segment and every weight
-//    byte is fetched from HBM once.  Only the 32-row blocks that hold rows run
-//    MFMAs; the rest are skipped with a wavefront-uniform branch.
-//  * The activation tile (256 x 64 bf16 = 32 KB) is shared by the four
-//    wavefronts through LDS, double buffered, 16-byte chunks XOR-swizzled by
-//    row so that the 32 lanes reading one MFMA operand hit distinct banks.
-//  * Each wavefront owns 64 output columns (two 32-column MFMA blocks) and
-//    reads its weight fragments straight from global memory into registers in
-//    the MFMA operand layout (lane = column, 8 contiguous k): nothing else
-//    reads them, so LDS would only add a copy.  The next stage is in flight
-//    while the current one computes.
-//  * Accumulators: 2 column blocks x 8 row blocks x 16 fp32 = 256 per lane,
-//    one wavefront per SIMD; latency is hidden by the explicit prefetch.
+// Weight streaming.  With ~100-2000 rows per expert the GEMMs of the smaller
+// workloads are bound by reading the weights from HBM once.  Weights are
+// therefore kept in a blocked layout (moe_pack_weights, once per model): for
+// every expert, 256-row output tile and 64-wide K stage, one contiguous 32 KB
+// block holding the 256 rows' 128-byte K slices in exactly the order (and
+// bank swizzle) the tile uses in LDS.  A workgroup streams its tile's blocks
+// front to back, so every weight byte is read once, as whole 1 KB DMA
+// requests, from consecutive addresses.  Tails (N or K not a multiple of
+// 256 / 64) are zero in the blocks, so the MFMAs need no masking.
+//
+// Tile: 256 rows x 256 output columns (128 for SwiGLU), K stages of 64,
+// 8 wavefronts = 2 (rows) x 4 (columns).
+//  * One tile row usually covers a whole expert segment (C is 160 / 256 in
+//    the HBM-bound workloads); only the 32-row blocks that hold rows run
+//    MFMAs (the block count is a template parameter chosen per tile).
+//  * Operands move global -> LDS by DMA (global_load_lds_dwordx4, no register
+//    staging), NST - 1 stages ahead of the MFMAs, with NST as large as the
+//    160 KB LDS allows (2..4).
+//  * Each wavefront owns 64 output columns and half of the row blocks:
+//    accumulators <= 128 registers, so two wavefronts share each SIMD and hide
+//    each other's LDS and barrier latency.
 //  * Tiles are numbered so that those sharing an expert's activations land
 //    on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so
-//    the activation rows are read once per L2.
+//    the activation rows are read from HBM once per expert.
 #include "moe_kernels.h"
 
 namespace moek {
@@ -39,11 +43,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kThreads = 256;
-constexpr int BM = 256;
-constexpr int BK = 64;
-constexpr int MSUB = BM / 32;
+constexpr int kThreads = 512;
+constexpr int BM = 256;                   // rows per tile
+constexpr int BK = 64;                    // K per stage
+constexpr int kRowBytes = BK * 2;         // one K slice of a row: 128 B
+constexpr int kTileRows = 256;            // weight rows per tile
+constexpr int kBStage = kTileRows * kRowBytes;  // 32 KB weight block per stage
+constexpr int kLdsBytes = 160 * 1024;
 constexpr int kXcd = 8;
 
 enum { MODE_GELU = 0, MODE_SWIGLU = 1, MODE_PLAIN = 2 };
@@ -51,13 +60,12 @@ enum { MODE_GELU = 0, MODE_SWIGLU = 1, MODE_PLAIN = 2 };
 struct GemmArgs {
   const uint16_t* A;         // rows of length K
   const int32_t* eo;         // expert_offset [E+1]
-  const uint16_t* W0;        // [n_exp][Nw][K]
-  const uint16_t* W1;        // [n_exp][Nw][K] (SwiGLU second matrix) or null
+  const uint16_t* Wp;        // blocked weights of this GEMM
   uint16_t* Out;             // rows of length Nout
   int a_local, o_local;      // row index relative to expert_offset[e_begin]
   int e_begin;
-  int K, Nw, Nout;
-  int n_tiles_n, m_tiles, total;
+  int K, Nout;
+  int n_tiles_n, m_tiles, nk, total;
 };
 
 __device__ __forceinline__ float gelu_erf(float z) {
@@ -67,139 +75,156 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// One tile with NS active 32-row blocks (NS = ceil(rows / 32), 1..8).  All
-// loops are static, so the accumulators stay in AGPRs without copies.
-template <int MODE, int NS>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint16_t* __restrict__ As, int el,
-                                          int n_t, int64_t a_row0, int64_t o_row0, int rows) {
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; lds must be wavefront-uniform).
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// wait until at most N vector-memory operations of this wavefront are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Byte offset of 16-byte chunk `ch` of row `r` in a tile of 128-byte rows.
+// Chunks are XOR-swizzled by row, so the 32 lanes that read one MFMA operand
+// (32 rows, same chunk) hit distinct banks.
+__device__ __forceinline__ int swz(int r, int ch) { return r * kRowBytes + ((ch ^ (r & 7)) << 4); }
+
+// LDS ring for a tile of NS row blocks: each stage holds the activation
+// slice (rounded up to whole 64-row DMA rounds) and the 32 KB weight block;
+// as many stages as fit in 160 KB, at most 4.
+template <int NS>
+struct Ring {
+  static constexpr int A_ROUNDS = (NS + 1) / 2;
+  static constexpr int A_BYTES = A_ROUNDS * 64 * kRowBytes;
+  static constexpr int STAGE = A_BYTES + kBStage;
+  static constexpr int NST = kLdsBytes / STAGE > 4 ? 4 : kLdsBytes / STAGE;
+  static constexpr int LOADS = A_ROUNDS + 4;  // DMA instructions per thread per stage
+};
+
+// The tile with NS active 32-row blocks, as seen by one wavefront that
+// multiplies MI of them starting at row block FIRST.  Every wavefront runs
+// the same loop (same barriers); MI may be 0.
+template <int MODE, int NS, int MI>
+__device__ __forceinline__ void gemm_part(const GemmArgs& a, char* __restrict__ smem, int el,
+                                          int n_t, int64_t a_row0, int64_t o_row0, int rows,
+                                          int first) {
+  using R = Ring<NS>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, lg = lane >> 5;
+  const int wn = wave & 3;
   const int K = a.K;
 
-  // weight rows (output columns) this lane feeds, one per 32-column block
-  int ncol0, ncol1;
-  const uint16_t* wsrc0 = a.W0 + (size_t)el * a.Nw * K;
-  const uint16_t* wsrc1;
-  if (MODE == MODE_SWIGLU) {
-    ncol0 = ncol1 = n_t * 128 + wave * 32 + l32;
-    wsrc1 = a.W1 + (size_t)el * a.Nw * K;
-  } else {
-    ncol0 = n_t * 256 + wave * 64 + l32;
-    ncol1 = ncol0 + 32;
-    wsrc1 = wsrc0;
-  }
-  // Loads are unconditional from clamped (always valid) addresses; lanes
-  // outside the matrix then select zero.  A branch around a load would force
-  // a wait for it before the join.
-  const bool bok0 = ncol0 < a.Nw, bok1 = ncol1 < a.Nw;
-  const uint16_t* bp0 = wsrc0 + (size_t)(bok0 ? ncol0 : a.Nw - 1) * K + 8 * lg;
-  const uint16_t* bp1 = wsrc1 + (size_t)(bok1 ? ncol1 : a.Nw - 1) * K + 8 * lg;
-
-  // activation loader: thread owns 16-byte chunk ac of rows ar + 32 i
-  const int ac = tid & 7, ar = tid >> 3;
-  const uint16_t* ap = a.A + a_row0 * K + 8 * ac;
-  int aoff[NS];
-  bool aok[NS];
+  // DMA lane geometry: in round i the block fills rows 64 i + 8 wave + lane/8,
+  // LDS chunk lane % 8, which holds K chunk (lane % 8) ^ (lane / 8).
+  const int drow = 8 * wave + (lane >> 3);
+  const int dchunk = (lane & 7) ^ (lane >> 3);
+  const uint16_t* ap = a.A + a_row0 * K + 8 * dchunk;
+  int aoff[R::A_ROUNDS];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int r = ar + 32 * i;
-    aok[i] = r < rows;
-    aoff[i] = (aok[i] ? r : rows - 1);
+  for (int i = 0; i < R::A_ROUNDS; ++i) {
+    const int r = 64 * i + drow;
+    aoff[i] = r < rows ? r : rows - 1;  // rows past the segment: any valid row
   }
+  const char* wblk = reinterpret_cast<const char*>(a.Wp) +
+                     (size_t)(el * a.n_tiles_n + n_t) * a.nk * kBStage + drow * kRowBytes +
+                     16 * (lane & 7);
+  // weight-tile rows of this lane's two MFMA column blocks
+  const int jb0 = MODE == MODE_SWIGLU ? wn * 32 + l32 : wn * 64 + l32;
+  const int jb1 = MODE == MODE_SWIGLU ? 128 + wn * 32 + l32 : wn * 64 + 32 + l32;
 
-  f32x16 acc0[NS], acc1[NS];
+  f32x16 acc0[MI > 0 ? MI : 1], acc1[MI > 0 ? MI : 1];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       acc0[i][r] = 0.f;
       acc1[i][r] = 0.f;
     }
   }
-  u32x4 bA[4][2], bB[4][2], av[NS];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-#define LOAD_B(BUF, K0)                                                   \
-  _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                     \
-    const int kk_ = (K0) + 16 * s_ + 8 * lg;                              \
-    const int ko_ = kk_ < K ? (K0) + 16 * s_ : K - 8 - 8 * lg;            \
-    const u32x4 t0_ = *(const u32x4*)(bp0 + ko_);                         \
-    const u32x4 t1_ = *(const u32x4*)(bp1 + ko_);                         \
-    BUF[s_][0] = (bok0 && kk_ < K) ? t0_ : zero;                          \
-    BUF[s_][1] = (bok1 && kk_ < K) ? t1_ : zero;                          \
-  }
-#define LOAD_A(K0)                                                        \
-  {                                                                       \
-    const bool kin_ = (K0) + 8 * ac < K;                                  \
-    const int ko_ = kin_ ? (K0) : K - 8 - 8 * ac;                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_) {                   \
-      const u32x4 t_ = *(const u32x4*)(ap + (int64_t)aoff[i_] * K + ko_); \
-      av[i_] = (aok[i_] && kin_) ? t_ : zero;                             \
-    }                                                                     \
-  }
-#define STORE_A(BUFI)                                                     \
-  _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_) {                     \
-    const int r_ = ar + 32 * i_;                                          \
-    *(u32x4*)&As[(BUFI) * (BM * BK) + r_ * BK + ((ac ^ (r_ & 7)) << 3)] = av[i_]; \
-  }
-#define COMPUTE(BUFI, BUF)                                                \
-  _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                     \
-    const bf16x8 b0_ = as_bf16x8(BUF[s_][0]);                             \
-    const bf16x8 b1_ = as_bf16x8(BUF[s_][1]);                             \
-    const int ch_ = 2 * s_ + lg;                                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_) {                   \
-      const int r_ = 32 * i_ + l32;                                       \
-      const bf16x8 af_ = as_bf16x8(                                       \
-          *(const u32x4*)&As[(BUFI) * (BM * BK) + r_ * BK + ((ch_ ^ (r_ & 7)) << 3)]); \
-      acc0[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_, b0_, acc0[i_], 0, 0, 0); \
-      acc1[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_, b1_, acc1[i_], 0, 0, 0); \
-    }                                                                     \
+  // K chunks past K hold zeros in the weight blocks, so the activation side
+  // may load anything finite there: clamp the offset into the row.
+#define ISSUE(KT, SLOT)                                                            \
+  {                                                                                \
+    char* st_ = smem + (SLOT) * R::STAGE;                                          \
+    const int k0_ = (KT) * BK;                                                     \
+    const int ko_ = k0_ + 8 * dchunk < K ? k0_ : K - 8 - 8 * dchunk;               \
+    _Pragma("unroll") for (int i_ = 0; i_ < R::A_ROUNDS; ++i_)                     \
+      dma16(ap + (int64_t)aoff[i_] * K + ko_, st_ + (64 * i_ + 8 * wave) * kRowBytes); \
+    const char* wb_ = wblk + (size_t)(KT) * kBStage;                               \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                               \
+      dma16(wb_ + i_ * 64 * kRowBytes, st_ + R::A_BYTES + (64 * i_ + 8 * wave) * kRowBytes); \
   }
 
-  // Two stages per iteration so that the two register sets of weight
-  // fragments swap statically.  Prefetches past the last stage reload the
-  // last stage (in bounds, never consumed), which keeps the loop free of
-  // branches around loads.
-  const int nk = (K + BK - 1) / BK;
-  LOAD_A(0);
-  LOAD_B(bA, 0);
-  STORE_A(0);
+  const int nk = a.nk;
+#pragma unroll
+  for (int p = 0; p < R::NST - 1; ++p) ISSUE(p < nk ? p : nk - 1, p);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<(R::NST - 2) * R::LOADS>();  // this wavefront's part of stage kt landed
+    __syncthreads();                         // everyone's part landed; stage kt-1 consumed
+    {
+      // refill the slot of stage kt-1; past the end, reload the last stage
+      // (in bounds, never read) so every iteration issues the same count
+      const int kn = kt + R::NST - 1;
+      ISSUE(kn < nk ? kn : nk - 1, kn % R::NST);
+    }
+    if (MI > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      const char* sa = smem + (kt % R::NST) * R::STAGE;
+      const char* sbt = sa + R::A_BYTES;
+      // operand fragments double buffered in registers: the reads for step
+      // s + 1 are issued before the MFMAs of step s
+      u32x4 fa[2][MI > 0 ? MI : 1], fb[2][2];
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_) {
+        const int cur = s_ & 1;
+        if (s_ == 0) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) fa[0][i] = *(const u32x4*)(sa + swz(32 * (first + i) + l32, lg));
+          fb[0][0] = *(const u32x4*)(sbt + swz(jb0, lg));
+          fb[0][1] = *(const u32x4*)(sbt + swz(jb1, lg));
+        }
+        if (s_ < 3) {
+          const int ch = 2 * (s_ + 1) + lg;
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            fa[cur ^ 1][i] = *(const u32x4*)(sa + swz(32 * (first + i) + l32, ch));
+          fb[cur ^ 1][0] = *(const u32x4*)(sbt + swz(jb0, ch));
+          fb[cur ^ 1][1] = *(const u32x4*)(sbt + swz(jb1, ch));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 b0 = as_bf16x8(fb[cur][0]);
+        const bf16x8 b1 = as_bf16x8(fb[cur][1]);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const bf16x8 af = as_bf16x8(fa[cur][i]);
+          acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0[i], 0, 0, 0);
+          acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1[i], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+#undef ISSUE
+  wait_vmcnt<0>();
   __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    const int k1 = (kt + 1) * BK;
-    LOAD_A(k1);
-    LOAD_B(bB, k1);
-    COMPUTE(0, bA);
-    STORE_A(1);
-    __syncthreads();
-    const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
-    LOAD_A(k2);
-    LOAD_B(bA, k2);
-    COMPUTE(1, bB);
-    STORE_A(0);
-    __syncthreads();
-  }
-  if (kt < nk) {
-    COMPUTE(0, bA);
-    __syncthreads();
-  }
-#undef LOAD_B
-#undef LOAD_A
-#undef STORE_A
-#undef COMPUTE
 
   // Epilogue, one 32-row block at a time: the wavefront parks its fp32
-  // accumulators in LDS (acc[i][r] is row 8 (r / 4) + 4 lg + r % 4 of block
-  // i, column l32 of its 32-column block), then reads them back row-wise,
-  // applies the activation and writes 16-byte bf16 chunks.  The A buffers are
-  // free: every wavefront has passed the last barrier of the main loop.
+  // accumulators in its own LDS scratch (acc[i][r] is row 8 (r / 4) + 4 lg +
+  // r % 4 of the block, column l32 of its 32-column block), then reads them
+  // back row-wise, applies the activation and writes 16-byte bf16 chunks.
   constexpr int LD = 68;  // padded row of 64 fp32
-  float* scr = reinterpret_cast<float*>(As) + wave * (32 * LD);
-  const int n_base = MODE == MODE_SWIGLU ? n_t * 128 + wave * 32 : n_t * 256 + wave * 64;
+  float* scr = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+  const int n_base = MODE == MODE_SWIGLU ? n_t * 128 + wn * 32 : n_t * 256 + wn * 64;
   uint16_t* out = a.Out + o_row0 * a.Nout;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
+  for (int i = 0; i < MI; ++i) {
+    const int blk = first + i;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * lg + (r & 3);
@@ -220,7 +245,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint16_t* __restric
           h[q] = silu_f(g0[q]) * u0[q];
           h[q + 4] = silu_f(g1[q]) * u1[q];
         }
-        const int grow = 32 * i + row, gcol = n_base + 8 * c;
+        const int grow = 32 * blk + row, gcol = n_base + 8 * c;
         if (grow < rows && gcol < a.Nout) *(u32x4*)(out + (int64_t)grow * a.Nout + gcol) = pack8(h);
       }
     } else {
@@ -235,7 +260,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint16_t* __restric
           h[q] = MODE == MODE_GELU ? gelu_erf(v0[q]) : v0[q];
           h[q + 4] = MODE == MODE_GELU ? gelu_erf(v1[q]) : v1[q];
         }
-        const int grow = 32 * i + row, gcol = n_base + 8 * c;
+        const int grow = 32 * blk + row, gcol = n_base + 8 * c;
         if (grow < rows && gcol < a.Nout) *(u32x4*)(out + (int64_t)grow * a.Nout + gcol) = pack8(h);
       }
     }
@@ -243,9 +268,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint16_t* __restric
   }
 }
 
+// Row blocks are split between the two wavefront rows: the first takes
+// ceil(NS / 2) blocks, the second the rest.
+template <int MODE, int NS>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, int el, int n_t,
+                                          int64_t a_row0, int64_t o_row0, int rows) {
+  if ((threadIdx.x >> 8) == 0)
+    gemm_part<MODE, NS, (NS + 1) / 2>(a, smem, el, n_t, a_row0, o_row0, rows, 0);
+  else
+    gemm_part<MODE, NS, NS / 2>(a, smem, el, n_t, a_row0, o_row0, rows, (NS + 1) / 2);
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2 * BM * BK];
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
 
   // tile id: consecutive ids (same expert, neighbouring column tiles) share an XCD
   const int bid = blockIdx.x;
@@ -265,45 +301,113 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
   const int rows = M - m0 < BM ? M - m0 : BM;
   switch ((rows + 31) >> 5) {
-    case 1: gemm_tile<MODE, 1>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 2: gemm_tile<MODE, 2>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 3: gemm_tile<MODE, 3>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 4: gemm_tile<MODE, 4>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 5: gemm_tile<MODE, 5>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 6: gemm_tile<MODE, 6>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    case 7: gemm_tile<MODE, 7>(a, As, el, n_t, a_row0, o_row0, rows); break;
-    default: gemm_tile<MODE, 8>(a, As, el, n_t, a_row0, o_row0, rows); break;
+    case 1: gemm_tile<MODE, 1>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 2: gemm_tile<MODE, 2>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 3: gemm_tile<MODE, 3>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 4: gemm_tile<MODE, 4>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 5: gemm_tile<MODE, 5>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 6: gemm_tile<MODE, 6>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    case 7: gemm_tile<MODE, 7>(a, smem, el, n_t, a_row0, o_row0, rows); break;
+    default: gemm_tile<MODE, 8>(a, smem, el, n_t, a_row0, o_row0, rows); break;
   }
 }
 
 template <int MODE>
-hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.total <= 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_kernel<MODE>, dim3(g.total), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
+// Blocked weight layout: for expert e, output tile nt, stage kt, one 32 KB
+// block of 256 rows x 8 chunks of 16 B; chunk p of row j holds K chunk
+// p ^ (j & 7) of the row's weight-matrix row (zeros past N or K).  Row j is
+// weight row nt*256 + j (GELU, plain), or W1 row nt*128 + j for j < 128 and
+// W3 row nt*128 + j - 128 otherwise (SwiGLU).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W0,
+                                                           const uint16_t* __restrict__ W1,
+                                                           int n_exp, int Nw, int K, int n_tiles,
+                                                           int nk, int swiglu,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t total = (int64_t)n_exp * n_tiles * nk * kTileRows * 8;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int p = (int)(q & 7);
+    const int j = (int)((q >> 3) & (kTileRows - 1));
+    int64_t rest = q >> 11;
+    const int kt = (int)(rest % nk);
+    rest /= nk;
+    const int nt = (int)(rest % n_tiles);
+    const int e = (int)(rest / n_tiles);
+    const int k = kt * BK + 8 * (p ^ (j & 7));
+    int n;
+    const uint16_t* src;
+    if (swiglu) {
+      n = nt * 128 + (j & 127);
+      src = j < 128 ? W0 : W1;
+    } else {
+      n = nt * 256 + j;
+      src = W0;
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < Nw && k < K) v = *(const u32x4*)(src + ((int64_t)e * Nw + n) * K + k);
+    *(u32x4*)(out + q * 8) = v;
+  }
+}
+
+struct Geo {
+  int n_tiles, nk;
+  size_t bytes;
+};
+Geo geo(int n_local, int N, int K, bool swiglu) {
+  Geo g;
+  g.n_tiles = swiglu ? (N + 127) / 128 : (N + 255) / 256;
+  g.nk = (K + BK - 1) / BK;
+  g.bytes = (size_t)n_local * g.n_tiles * g.nk * kBStage;
+  return g;
+}
+
 }  // namespace
 
+size_t packed_weights_bytes(int n_local, int d, int f, bool swiglu) {
+  return geo(n_local, f, d, swiglu).bytes + geo(n_local, d, f, false).bytes;
+}
+
+hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                               int n_local, int d, int f, bool swiglu, void* wp, hipStream_t s) {
+  if (n_local <= 0) return hipSuccess;
+  const Geo g1 = geo(n_local, f, d, swiglu), g2 = geo(n_local, d, f, false);
+  uint16_t* o1 = static_cast<uint16_t*>(wp);
+  uint16_t* o2 = reinterpret_cast<uint16_t*>(static_cast<char*>(wp) + g1.bytes);
+  auto blocks = [](size_t bytes) {
+    int64_t g = (int64_t)(bytes / 16 + 255) / 256;
+    return (unsigned)(g > (1 << 20) ? (1 << 20) : g);
+  };
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks(g1.bytes)), dim3(256), 0, s, W1,
+                     swiglu ? W3 : nullptr, n_local, f, d, g1.n_tiles, g1.nk, swiglu ? 1 : 0, o1);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(blocks(g2.bytes)), dim3(256), 0, s, W2, nullptr,
+                     n_local, d, f, g2.n_tiles, g2.nk, 0, o2);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
-                             int n_local, int rows_max, int d, int f, bool swiglu,
-                             const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                             int n_local, int rows_max, int d, int f, bool swiglu, const void* wp,
                              uint16_t* H, uint16_t* ret, hipStream_t s) {
   if (n_local <= 0 || rows_max <= 0) return hipSuccess;
   const int m_tiles = (rows_max + BM - 1) / BM;
+  const Geo geo1 = geo(n_local, f, d, swiglu), geo2 = geo(n_local, d, f, false);
   GemmArgs g1{};
   g1.A = packed;
   g1.eo = expert_offset;
-  g1.W0 = W1;
-  g1.W1 = swiglu ? W3 : nullptr;
+  g1.Wp = static_cast<const uint16_t*>(wp);
   g1.Out = H;
   g1.a_local = 0;
   g1.o_local = 1;
   g1.e_begin = e_begin;
   g1.K = d;
-  g1.Nw = f;
   g1.Nout = f;
-  g1.n_tiles_n = swiglu ? (f + 127) / 128 : (f + 255) / 256;
+  g1.n_tiles_n = geo1.n_tiles;
+  g1.nk = geo1.nk;
   g1.m_tiles = m_tiles;
   g1.total = n_local * m_tiles * g1.n_tiles_n;
   hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, s) : launch_gemm<MODE_GELU>(g1, s);
@@ -312,16 +416,15 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   GemmArgs g2{};
   g2.A = H;
   g2.eo = expert_offset;
-  g2.W0 = W2;
-  g2.W1 = nullptr;
+  g2.Wp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(wp) + geo1.bytes);
   g2.Out = ret;
   g2.a_local = 1;
   g2.o_local = 0;
   g2.e_begin = e_begin;
   g2.K = f;
-  g2.Nw = d;
   g2.Nout = d;
-  g2.n_tiles_n = (d + 255) / 256;
+  g2.n_tiles_n = geo2.n_tiles;
+  g2.nk = geo2.nk;
   g2.m_tiles = m_tiles;
   g2.total = n_local * m_tiles * g2.n_tiles_n;
   return launch_gemm<MODE_PLAIN>(g2, s);

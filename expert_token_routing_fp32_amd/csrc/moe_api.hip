@@ -211,18 +211,37 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
       moek::launch_pack(x, p->x_dtype == MOE_BF16, dest, p->B, p->k, p->d, packed, stream));
 }
 
+size_t moe_weights_bytes(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return SIZE_MAX;
+  return moek::packed_weights_bytes(p->e_end - p->e_begin, p->d, p->f, p->act == MOE_SWIGLU);
+}
+
+moe_status_t moe_pack_weights(const moe_problem_t* p, const moe_bf16_t* W1, const moe_bf16_t* W3,
+                              const moe_bf16_t* W2, void* wpacked, size_t wpacked_bytes,
+                              hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool swiglu = p->act == MOE_SWIGLU;
+  const int n_local = p->e_end - p->e_begin;
+  if (n_local == 0) return MOE_OK;
+  if (!W1 || !W2 || (swiglu && !W3) || !wpacked) return MOE_ERR_INVALID;
+  if (!a16(W1) || !a16(W2) || (swiglu && !a16(W3)) || !a16(wpacked)) return MOE_ERR_INVALID;
+  if (wpacked_bytes < moek::packed_weights_bytes(n_local, p->d, p->f, swiglu))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moek::launch_pack_weights(W1, swiglu ? W3 : nullptr, W2, n_local, p->d, p->f,
+                                              swiglu, wpacked, stream));
+}
+
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
-                            const int32_t* expert_offset, const moe_bf16_t* W1,
-                            const moe_bf16_t* W3, const moe_bf16_t* W2, moe_bf16_t* ret,
+                            const int32_t* expert_offset, const void* wpacked, moe_bf16_t* ret,
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = moe_validate(p);
   if (st != MOE_OK) return st;
   const bool swiglu = p->act == MOE_SWIGLU;
   const int n_local = p->e_end - p->e_begin;
   if (!expert_offset || (p->B > 0 && (!packed || !ret))) return MOE_ERR_INVALID;
-  if (n_local > 0 && (!W1 || !W2 || (swiglu && !W3))) return MOE_ERR_INVALID;
-  if ((packed && !a16(packed)) || (ret && !a16(ret)) || (W1 && !a16(W1)) || (W2 && !a16(W2)) ||
-      (swiglu && W3 && !a16(W3)))
+  if (n_local > 0 && !wpacked) return MOE_ERR_INVALID;
+  if ((packed && !a16(packed)) || (ret && !a16(ret)) || (wpacked && !a16(wpacked)))
     return MOE_ERR_INVALID;
   const size_t need = ffn_ws(p);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
@@ -232,9 +251,9 @@ moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
                                             p->e_end, kmax_of(p), p->d, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  return hip_status(moek::launch_expert_ffn(
-      packed, expert_offset, p->e_begin, n_local, (int)rows_per_expert(p), p->d, p->f, swiglu,
-      W1, swiglu ? W3 : nullptr, W2, static_cast<uint16_t*>(ws), ret, stream));
+  return hip_status(moek::launch_expert_ffn(packed, expert_offset, p->e_begin, n_local,
+                                            (int)rows_per_expert(p), p->d, p->f, swiglu, wpacked,
+                                            static_cast<uint16_t*>(ws), ret, stream));
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const moe_bf16_t* ret, const int32_t* dest,
@@ -261,17 +280,16 @@ moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret, const int
 }
 
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg, const float* bias,
-                         const moe_bf16_t* W1, const moe_bf16_t* W3, const moe_bf16_t* W2,
-                         void* y, moe_forward_out_t* out, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         const void* wpacked, void* y, moe_forward_out_t* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = moe_validate(p);
   if (st != MOE_OK) return st;
   const bool swiglu = p->act == MOE_SWIGLU;
   const int n_local = p->e_end - p->e_begin;
   if (p->B > 0 && (!x || !Wg || !y)) return MOE_ERR_INVALID;
-  if (n_local > 0 && (!W1 || !W2 || (swiglu && !W3))) return MOE_ERR_INVALID;
+  if (n_local > 0 && !wpacked) return MOE_ERR_INVALID;
   if (p->B > 0 && (!a16(x) || !a16(y) || !a4(Wg) || (bias && !a4(bias)))) return MOE_ERR_INVALID;
-  if ((W1 && !a16(W1)) || (W2 && !a16(W2)) || (swiglu && W3 && !a16(W3))) return MOE_ERR_INVALID;
+  if (wpacked && !a16(wpacked)) return MOE_ERR_INVALID;
   if (out && out->packed && !a16(out->packed)) return MOE_ERR_INVALID;
   const size_t need = carve_forward(p, out, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
@@ -288,8 +306,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
   if (e == hipSuccess && p->B > 0)
     e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
-                                p->d, p->f, swiglu, W1, swiglu ? W3 : nullptr, W2, b.H, b.packed,
-                                stream);
+                                p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
                              p->k, p->d, kmax_of(p), stream);

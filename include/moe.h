@@ -36,10 +36,12 @@
  *   of 8.
  * - Sizes: Kmax = min(B*k, E*C) bounds the number of kept assignments K; the
  *   exact K is expert_offset[E], known only on the device.
- * - Expert weights are stored output-major, one matrix per expert: W1 and W3
+ * - Expert weights are given output-major, one matrix per expert: W1 and W3
  *   are [n_local][f][d] and W2 is [n_local][d][f], where
  *   n_local = e_end - e_begin; expert e computes W2 . act(W1 . x) (GELU) or
- *   W2 . (silu(W1 . x) * (W3 . x)) (SwiGLU), with no biases.
+ *   W2 . (silu(W1 . x) * (W3 . x)) (SwiGLU), with no biases.  The expert GEMM
+ *   streams them from a blocked copy made once by moe_pack_weights (see
+ *   there); moe_expert_ffn and moe_forward take that copy.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -168,6 +170,25 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x,
                           moe_bf16_t* packed, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Bytes of the blocked expert-weight copy for problem p (SIZE_MAX if p is
+ * invalid). */
+size_t moe_weights_bytes(const moe_problem_t* p);
+
+/* Rearranges the local experts' weights into the blocked layout the expert
+ * GEMM streams: per expert, per output tile (256 rows of W1 or W2, or 128
+ * rows of W1 plus the same 128 rows of W3 for SwiGLU) and per 64-wide K
+ * slice, one contiguous 32 KB block whose rows and 16-byte chunks are in the
+ * order the GEMM keeps them in LDS; padding past f or d is zero.  A one-time
+ * format conversion (weights are parameters), not part of the layer; the
+ * caller does it when the weights are loaded and owns the copy.
+ *   W1, W3  [n_local][f][d] bf16 (W3 only for SwiGLU, else NULL)
+ *   W2      [n_local][d][f] bf16
+ *   wpacked moe_weights_bytes(p) bytes, 16-byte aligned, out */
+moe_status_t moe_pack_weights(const moe_problem_t* p, const moe_bf16_t* W1,
+                              const moe_bf16_t* W3, const moe_bf16_t* W2,
+                              void* wpacked, size_t wpacked_bytes,
+                              hipStream_t stream);
+
 /* Grouped expert MLP ("Expert Parallelism", narrativegoldmine.com,
  * "Components and Architecture", Expert GEMM; "Formal Algorithm", expert
  * computation on the received tokens).  For every expert e in
@@ -178,13 +199,11 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x,
  * ret == packed nothing is copied, otherwise they are copied to ret.
  *   packed        [Kmax][d] bf16 in
  *   expert_offset [E+1]     int32 in (as written by moe_dispatch)
- *   W1, W3        [n_local][f][d] bf16 (W3 only for SwiGLU, else NULL)
- *   W2            [n_local][d][f] bf16
+ *   wpacked       the local experts' weights as written by moe_pack_weights
  *   ret           [Kmax][d] bf16 out; may alias packed
  *   ws / ws_bytes workspace, >= moe_workspace_bytes(p, MOE_OP_FFN) */
 moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
-                            const int32_t* expert_offset, const moe_bf16_t* W1,
-                            const moe_bf16_t* W3, const moe_bf16_t* W2,
+                            const int32_t* expert_offset, const void* wpacked,
                             moe_bf16_t* ret, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
@@ -229,11 +248,10 @@ typedef struct {
 /* The whole layer, enqueued on one stream with no host synchronisation:
  * gate, route, dispatch, expert FFN (in place on the packed rows), combine.
  *   x [B][d] x_dtype; Wg [d][E] f32; bias [E] f32 or NULL;
- *   W1/W3/W2 as in moe_expert_ffn; y [B][d] x_dtype out;
+ *   wpacked as in moe_expert_ffn; y [B][d] x_dtype out;
  *   out may be NULL; ws >= moe_workspace_bytes(p, MOE_OP_FORWARD). */
 moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
-                         const float* bias, const moe_bf16_t* W1,
-                         const moe_bf16_t* W3, const moe_bf16_t* W2, void* y,
+                         const float* bias, const void* wpacked, void* y,
                          moe_forward_out_t* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 

@@ -92,6 +92,14 @@ def weights_for_gpu(inp: dict):
     return inp["W1_bits"], inp["W3_bits"], inp["W2_bits"]
 
 
+def packed_weights_for_gpu(p, inp: dict):
+    """Upload the bf16 expert weights and put them in the library's blocked
+    layout (moe_pack_weights), as a model would once at load time."""
+    import expert_token_routing_fp32_amd as moe
+    W1, W3, W2 = weights_for_gpu(inp)
+    return moe.pack_weights(p, to_dev(W1), None if W3 is None else to_dev(W3), to_dev(W2))
+
+
 @functools.lru_cache(maxsize=2)
 def workload(name: str, **scale):
     """Inputs plus the oracle's routing/dispatch results (no FFN)."""

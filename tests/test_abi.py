@@ -132,8 +132,7 @@ def test_calls_reject_before_launch(L, lib):
     r = lib.moe_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                          fake, fake, None, 0, None)
     assert r == L.MOE_ERR_WORKSPACE
-    r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, None, fake, fake, None, None, 0,
-                        None)
+    r = lib.moe_forward(ctypes.byref(p), fake, fake, None, fake, fake, None, None, 0, None)
     assert r == L.MOE_ERR_WORKSPACE
     unaligned = ctypes.c_void_p((1 << 20) + 2)
     r = lib.moe_gate(ctypes.byref(p), unaligned, fake, None, fake, None)

@@ -16,7 +16,7 @@ import pytest
 import oracle
 from moe_synth import ORDER
 from _helpers import (assert_bf16_close, assert_f32_close, problem_for, sample_rows, say,
-                      to_dev, to_np, weights_for_gpu, workload)
+                      to_dev, to_np, packed_weights_for_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +27,9 @@ def wl(request):
     name = request.param
     say(f"[workload {name}] generating inputs + oracle routing")
     w, inp, ref = workload(name)
-    W1, W3, W2 = weights_for_gpu(inp)
     d = dict(x=to_dev(inp["x"]), Wg=to_dev(inp["Wg"]),
              bias=None if inp["bias"] is None else to_dev(inp["bias"]),
-             W1=to_dev(W1), W3=None if W3 is None else to_dev(W3), W2=to_dev(W2))
+             wp=packed_weights_for_gpu(problem_for(w), inp))
     torch.cuda.synchronize()
     say(f"[workload {name}] B={w.B} d={w.d} E={w.E} k={w.k} C={ref['C']} "
         f"kept={int(ref['expert_offset'][-1])}")
@@ -98,7 +97,7 @@ def test_expert_ffn(wl):
     packed_d[:K] = to_dev(ref["packed"])
     keep_copy = packed_d.clone()
     eo_d = to_dev(eo)
-    ret = moe.expert_ffn(p, packed_d, eo_d, d["W1"], d["W3"], d["W2"])
+    ret = moe.expert_ffn(p, packed_d, eo_d, d["wp"])
     full = w.B * w.f <= 4096 * 4096
     rows = np.arange(int(eo[w.e_begin]), int(eo[w.e_end])) if full else \
         sample_rows(eo, w.e_begin, w.e_end, 96)
@@ -116,7 +115,7 @@ def test_expert_ffn(wl):
         assert torch.equal(ret[hi:K], keep_copy[hi:K])
         say(f"  {name}: {K - hi + lo} remote rows returned unchanged")
     # in place (ret aliases packed) gives the same rows
-    moe.expert_ffn(p, packed_d, eo_d, d["W1"], d["W3"], d["W2"], ret=packed_d)
+    moe.expert_ffn(p, packed_d, eo_d, d["wp"], ret=packed_d)
     np.testing.assert_array_equal(to_np(packed_d[rows_t]), got_bits)
 
 

@@ -15,7 +15,7 @@ import pytest
 import oracle
 from moe_synth import ORDER
 from _helpers import (TOL_F32, assert_bf16_close, assert_f32_close, problem_for, say, to_dev,
-                      to_np, weights_for_gpu, workload)
+                      to_np, packed_weights_for_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +34,11 @@ def undecided_tokens(logits: np.ndarray, k: int, tol: float = TOL_F32) -> np.nda
 def run_forward(w, inp, ref, name, n_sample=48):
     import torch
     import expert_token_routing_fp32_amd as moe
-    W1, W3, W2 = weights_for_gpu(inp)
     p = problem_for(w)
     x = to_dev(inp["x"])
+    wp = packed_weights_for_gpu(p, inp)
     y, o = moe.forward(p, x, to_dev(inp["Wg"]), None if inp["bias"] is None else to_dev(inp["bias"]),
-                       to_dev(W1), None if W3 is None else to_dev(W3), to_dev(W2), outputs=True)
+                       wp, outputs=True)
     torch.cuda.synchronize()
     assert_f32_close(to_np(o["logits"]), ref["logits"], what=f"{name} logits")
     und = undecided_tokens(ref["logits"], w.k)
@@ -88,9 +88,8 @@ def test_forward_is_deterministic():
     import torch
     import expert_token_routing_fp32_amd as moe
     w, inp, ref = workload("uniform")
-    W1, W3, W2 = weights_for_gpu(inp)
     p = problem_for(w)
-    args = (to_dev(inp["x"]), to_dev(inp["Wg"]), None, to_dev(W1), None, to_dev(W2))
+    args = (to_dev(inp["x"]), to_dev(inp["Wg"]), None, packed_weights_for_gpu(p, inp))
     y1 = moe.forward(p, *args)
     y2 = moe.forward(p, *args)
     torch.cuda.synchronize()

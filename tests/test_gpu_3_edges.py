@@ -9,8 +9,8 @@ from hypothesis import HealthCheck, given, settings, strategies as st
 
 import moe_synth
 import oracle
-from _helpers import (assert_bf16_close, assert_f32_close, problem_for, say, to_dev, to_np,
-                      weights_for_gpu)
+from _helpers import (assert_bf16_close, assert_f32_close, packed_weights_for_gpu, problem_for,
+                      say, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,13 +61,12 @@ def check_stages(w, C=None, residual=False, ffn=True):
     if not ffn or w.B == 0:
         return
     # expert ffn on the oracle's packed rows
-    W1, W3, W2 = weights_for_gpu(inp)
+    wp = packed_weights_for_gpu(p, inp)
     km = moe.max_kept(p)
     pk = torch.zeros((max(km, 1), w.d), dtype=torch.int16, device="cuda")
     if K:
         pk[:K] = to_dev(ref["packed"])
-    ret = moe.expert_ffn(p, pk, to_dev(ref["expert_offset"]), to_dev(W1),
-                         None if W3 is None else to_dev(W3), to_dev(W2))
+    ret = moe.expert_ffn(p, pk, to_dev(ref["expert_offset"]), wp)
     exp = oracle.expert_ffn(inp["x"], ref["pack_src"], ref["expert_offset"], w.e_begin, w.e_end,
                             inp["W1"], inp["W2"], inp["W3"], w.act)
     if K:
@@ -89,7 +88,7 @@ def check_stages(w, C=None, residual=False, ffn=True):
         assert (got[~ref["keep"].any(axis=1)] == 0).all()
     # and the whole layer
     yf = moe.forward(p, x, to_dev(inp["Wg"]), None if inp["bias"] is None else to_dev(inp["bias"]),
-                     to_dev(W1), None if W3 is None else to_dev(W3), to_dev(W2))
+                     wp)
     yfe = oracle.combine(exp, ref["dest"], ref["w"], x_residual=inp["x"] if residual else None)
     yfg = to_np(yf)
     gotf = oracle.bf16_bits_to_f64(yfg) if yfg.dtype == np.uint16 else yfg.astype(np.float64)
