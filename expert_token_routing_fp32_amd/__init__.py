@@ -233,10 +233,13 @@ _OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_lo
                "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")
 
 
-def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None):
+def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None,
+            ffn_events=None):
     """The whole layer on the current stream (``wpacked`` from pack_weights).
     With ``outputs`` the intermediate tensors are allocated and returned too
-    (``packed`` then holds the expert outputs of the local rows, in place)."""
+    (``packed`` then holds the expert outputs of the local rows, in place).
+    ``ffn_events``: optional pair of timing-enabled ``torch.cuda.Event`` that
+    the library records around the expert FFN."""
     _check(p)
     B, d, E, k = p.B, p.d, p.E, p.k
     dev = x.device
@@ -264,6 +267,13 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
                  rank_offset=torch.empty(p.n_ranks + 1, **i32), pack_src=torch.empty(km, **i32),
                  packed=torch.empty((km, d), dtype=torch.int16, device=dev))
         outp = L.ForwardOut(**{n: o[n].data_ptr() for n in _OUT_FIELDS})
+    if ffn_events is not None:
+        if outp is None:
+            outp = L.ForwardOut()
+        for ev, name in zip(ffn_events, ("ffn_begin", "ffn_end")):
+            if ev.cuda_event == 0:  # torch creates the HIP event on first record
+                ev.record()
+            setattr(outp, name, ev.cuda_event)
     n = workspace_bytes(p, "forward")
     if ws is None:
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)

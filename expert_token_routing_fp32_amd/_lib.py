@@ -36,10 +36,12 @@ class Problem(ctypes.Structure):
 
 
 class ForwardOut(ctypes.Structure):
-    """moe_forward_out_t (every field a device pointer or NULL)."""
+    """moe_forward_out_t: device pointers or NULL, then two hipEvent_t
+    handles (or NULL) recorded around the expert FFN."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
-        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")]
+        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed",
+        "ffn_begin", "ffn_end")]
 
 
 class MoEError(RuntimeError):

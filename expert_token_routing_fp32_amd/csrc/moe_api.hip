@@ -304,9 +304,12 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
     e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->n_ranks, b.pos, b.keep, b.dest, b.load,
                            b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
+  const bool timed = out && out->ffn_begin && out->ffn_end;
+  if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_begin, stream);
   if (e == hipSuccess && p->B > 0)
     e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                 p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
+  if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_end, stream);
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
                              p->k, p->d, kmax_of(p), stream);

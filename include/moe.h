@@ -243,6 +243,12 @@ typedef struct {
   int32_t* pack_src;      /* [Kmax]   */
   moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
                              outputs overwrite the local rows in place) */
+  /* Optional timing: when both are non-NULL they are recorded on the call's
+   * stream right before and right after the expert-FFN launches, so a caller
+   * can time that stage inside a running sequence of forwards.  The caller
+   * owns the events (created with timing enabled). */
+  hipEvent_t ffn_begin;
+  hipEvent_t ffn_end;
 } moe_forward_out_t;
 
 /* The whole layer, enqueued on one stream with no host synchronisation:
