@@ -15,27 +15,28 @@
 // Weight streaming.  With ~100-2000 rows per expert the GEMMs of the smaller
 // workloads are bound by reading the weights from HBM once.  Weights are
 // therefore kept in a blocked layout (moe_pack_weights, once per model): for
-// every expert, 256-row output tile and 64-wide K stage, one contiguous 32 KB
-// block holding the 256 rows' 128-byte K slices in exactly the order (and
-// bank swizzle) the tile uses in LDS.  A workgroup streams its tile's blocks
-// front to back, so every weight byte is read once, as whole 1 KB DMA
-// requests, from consecutive addresses.  Tails (N or K not a multiple of
-// 256 / 64) are zero in the blocks, so the MFMAs need no masking.
+// every expert, 256-column output tile and 64-wide K stage, one contiguous
+// 32 KB block holding, in order, each wavefront's MFMA operand fragments
+// (1 KB per fragment: 64 lanes x 16 bytes).  A wavefront loads its fragments
+// straight into registers, front to back, as whole 1 KB requests from
+// consecutive addresses; every weight byte is read once.  Tails (N or K not
+// a multiple of 256 / 64, and K padded to a whole pipeline group) are zero
+// in the blocks, so the MFMAs need no masking.
 //
-// Tile: 256 rows x 256 output columns (128 for SwiGLU), K stages of 64,
-// 8 wavefronts = 2 (rows) x 4 (columns).
-//  * One tile row usually covers a whole expert segment (C is 160 / 256 in
-//    the HBM-bound workloads); only the 32-row blocks that hold rows run
-//    MFMAs (the block count is a template parameter chosen per tile).
-//  * Operands move global -> LDS by DMA (global_load_lds_dwordx4, no register
-//    staging), NST - 1 stages ahead of the MFMAs, with NST as large as the
-//    160 KB LDS allows (2..4).
-//  * Each wavefront owns 64 output columns and half of the row blocks:
-//    accumulators <= 128 registers, so two wavefronts share each SIMD and hide
-//    each other's LDS and barrier latency.
-//  * Tiles are numbered so that those sharing an expert's activations land
-//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so
-//    the activation rows are read from HBM once per expert.
+// Tile: up to 256 rows x 256 output columns (128 hidden units of W1 and W3
+// for SwiGLU), K stages of 64; 4 wavefronts, one per SIMD, each owning 64
+// weight columns and all row blocks (accumulators in the AGPRs, up to 256).
+//  * One tile usually covers a whole expert segment (C is 160 / 256 in the
+//    HBM-bound workloads); only the 32-row blocks that hold rows run MFMAs
+//    (the block count is a template parameter chosen per tile).
+//  * Weights: global -> registers, kP - 1 stages ahead (8 KB per wavefront
+//    per stage).  Activations: global -> LDS by DMA (global_load_lds_dwordx4,
+//    no register staging) into a kP-slot ring, bank-swizzled; every
+//    activation fragment read from LDS feeds two MFMAs.
+//  * Persistent: each workgroup runs a contiguous range of tiles; tiles of
+//    one expert that share its activation rows sit on the same XCD
+//    (workgroups are dealt round-robin over the 8 XCDs), so the activation
+//    rows are read from HBM about once per expert and then from L2.
 #include "moe_kernels.h"
 
 namespace moek {
@@ -46,12 +47,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int BM = 256;                   // rows per tile
 constexpr int BK = 64;                    // K per stage
 constexpr int kRowBytes = BK * 2;         // one K slice of a row: 128 B
 constexpr int kTileRows = 256;            // weight rows per tile
-constexpr int kBStage = kTileRows * kRowBytes;  // 32 KB weight block per stage
+constexpr int kWStage = kTileRows * kRowBytes;  // 32 KB of weights per tile and stage
+constexpr int kP = 4;                     // pipeline depth (stages in flight + 1)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kXcd = 8;
 
@@ -73,25 +75,31 @@ struct GemmArgs {
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
 // evaluated with Abramowitz & Stegun, Handbook of Mathematical Functions,
 // formula 7.1.26 (absolute error <= 1.5e-7, far below the bf16 rounding of
-// the stored activation): erf(x) = 1 - (a1 t + ... + a5 t^5) e^{-x^2},
-// t = 1 / (1 + p x) for x >= 0, odd symmetry for x < 0.  A dozen VALU
-// operations instead of a general-purpose erff: the epilogue evaluates it
-// once per hidden activation.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __frcp_rn(fmaf(0.3275911f, ax, 1.0f));
+// the stored activation): for x >= 0, erf(x) = 1 - q with
+// q = (a1 t + a2 t^2 + ... + a5 t^5) e^{-x^2}, t = 1 / (1 + p x), and erf is
+// odd.  With x = |z| / sqrt 2 this gives GELU(z) = z - z q / 2 for z >= 0
+// and z q / 2 for z < 0.  The constants p / sqrt 2 and log2(e) / 2 are
+// folded in, and the reciprocal and exponential are single hardware
+// instructions (v_rcp_f32, v_exp_f32: about 1 ulp), once per hidden
+// activation in the epilogue.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188f, az, 1.0f));  // p / sqrt 2
   float p = fmaf(1.061405429f, t, -1.453152027f);
   p = fmaf(p, t, 1.421413741f);
   p = fmaf(p, t, -0.284496736f);
   p = fmaf(p, t, 0.254829592f);
   p *= t;
-  const float y = 1.0f - p * __expf(-ax * ax);
-  return copysignf(y, x);
+  // e^{-z^2 / 2} = 2^{-(log2 e / 2) z^2}
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752f);
+  const float r = 0.5f * z * (p * e);
+  return z >= 0.0f ? z - r : r;
 }
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erf_as7126(z * 0.7071067811865475f));
+// silu(z) = z / (1 + e^{-z}), with e^{-z} = 2^{-z log2 e} and a hardware
+// reciprocal
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504f));
 }
-__device__ __forceinline__ float silu_f(float z) { return z * __frcp_rn(1.0f + __expf(-z)); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -99,6 +107,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // (global_load_lds_dwordx4; lds must be wavefront-uniform).
 __device__ __forceinline__ void dma16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// The same with the non-temporal hint (cache-policy bit NT): for the weight
+// stream, which is read once, so that it does not push the activation rows
+// that the other tiles of the expert re-read out of L2.
+__device__ __forceinline__ void dma16nt(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 2);
+}
+
+// One accumulator element, read out of the accumulation registers where it
+// is used (left alone, the compiler copies every accumulator of the tile to
+// ordinary registers at the start of the epilogue).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+// value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2])
+__device__ __forceinline__ float swap_adjacent(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 // wait until at most N vector-memory operations of this wavefront are in flight
@@ -119,216 +148,201 @@ __device__ __forceinline__ int swz(int r, int ch) {
   return r * kRowBytes + ((ch ^ swz_key(r)) << 4);
 }
 
-// LDS ring for a tile of NS row blocks: each stage holds the activation
-// slice (rounded up to whole 64-row DMA rounds) and the 32 KB weight block;
-// as many stages as fit in 160 KB, at most 4.
+// Activation ring for a tile of NS row blocks: kP slots, each the tile's
+// 64-wide K slice of its 32 NS rows (one 32-row DMA round per block).
 template <int NS>
 struct Ring {
-  static constexpr int A_ROUNDS = (NS + 1) / 2;
-  static constexpr int A_BYTES = A_ROUNDS * 64 * kRowBytes;
-  static constexpr int STAGE = A_BYTES + kBStage;
-  static constexpr int NST = kLdsBytes / STAGE > 4 ? 4 : kLdsBytes / STAGE;
-  static constexpr int LOADS = A_ROUNDS + 4;  // DMA instructions per thread per stage
+  static constexpr int A_BYTES = NS * 32 * kRowBytes;
+  static constexpr int LOADS = NS + 8;  // vector-memory loads per thread per stage
 };
+static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
+static_assert((kP - 2) * Ring<8>::LOADS < 64, "vmcnt range");
 
-// A run of `ntile` consecutive output tiles (columns n0 .. n0+ntile-1) of one
-// expert and one 256-row slice with NS active 32-row blocks, as seen by one
-// wavefront that multiplies MI of the row blocks starting at block FIRST.
-// Every wavefront runs the same loop (same barriers); MI may be 0.
+__device__ __forceinline__ u32x4 load_nt(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// A run of `ntile` consecutive output tiles (n0 .. n0+ntile-1) of one expert
+// and one row slice of `rows` <= 32 NS rows.  Wavefront w (one per SIMD)
+// owns the 64 weight rows 64w .. 64w+63 of each tile -- two 32-column MFMA
+// blocks -- and all NS row blocks: 2 NS accumulators of 16 registers.
 //
-// The run is one continuous pipeline over ntile * nk stages: the prefetch
-// for the next tile's first stages is in flight while a tile's last stages
-// and its epilogue run, so the weight stream does not stop between tiles.
-// The epilogue stores straight from the accumulators (no LDS), pairing
-// neighbouring columns across lanes into 4-byte stores.
-template <int MODE, int NS, int MI>
+// The run is one pipeline over ntile * nk stages of 64 K; nk is a multiple
+// of kP, so tile ends fall on the last step of the unrolled group and the
+// register set and ring slot of a stage are compile-time constants.  Stage
+// g + kP - 1 is issued while stage g is multiplied:
+//   weights     global -> registers, the wavefront's own 8 KB (eight 1 KB
+//               fragment loads, non-temporal), set (g + kP - 1) % kP;
+//   activations global -> LDS by DMA, slot (g + kP - 1) % kP.
+// Vector-memory loads complete in issue order, so waiting until at most
+// (kP - 2) stages' loads are outstanding means stage g has landed.  After an
+// epilogue the counter also holds stores, which are not ordered with the
+// loads: then wait for everything.
+template <int MODE, int NS>
 __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ smem, int el,
                                          int n0, int ntile, int64_t a_row0, int64_t o_row0,
-                                         int rows, int first) {
+                                         int rows) {
   using R = Ring<NS>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  // wavefront-uniform, so that every address below that depends only on it
+  // lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lg = lane >> 5;
-  const int wn = wave & 3;
   const int K = a.K;
   const int nk = a.nk;
   const int nstage = ntile * nk;
 
-  // DMA lane geometry: in round i the block fills rows 64 i + 8 wave + lane/8,
-  // LDS chunk lane % 8, which holds K chunk (lane % 8) ^ swz_key(row) (the
-  // key depends only on drow, as 64 i is a multiple of 16).
+  // DMA lane geometry: round i fills rows 32 i + 8 wave + lane/8, LDS chunk
+  // lane % 8, which holds K chunk (lane % 8) ^ swz_key(row) (the key depends
+  // only on drow, as 32 i is a multiple of 16).  Global addresses are a
+  // scalar base plus a 32-bit per-lane byte offset (a row slice is far below
+  // 4 GB).
   const int drow = 8 * wave + (lane >> 3);
-  const int dchunk = (lane & 7) ^ swz_key(drow);
-  const uint16_t* ap = a.A + a_row0 * K + 8 * dchunk;
-  int aoff[R::A_ROUNDS];
+  const int dcol = 8 * ((lane & 7) ^ swz_key(drow));  // K offset of the lane's chunk
+  const char* abase = reinterpret_cast<const char*>(a.A + a_row0 * K);
+  uint32_t arow[NS];
 #pragma unroll
-  for (int i = 0; i < R::A_ROUNDS; ++i) {
-    const int r = 64 * i + drow;
-    aoff[i] = r < rows ? r : rows - 1;  // rows past the segment: any valid row
+  for (int i = 0; i < NS; ++i) {
+    const int r = 32 * i + drow;
+    arow[i] = 2u * (uint32_t)(r < rows ? r : rows - 1) * (uint32_t)K;  // past the segment: any valid row
   }
-  // weight blocks of tile n are (el * n_tiles + n) * nk + kt: consecutive
-  // tiles of the run are one contiguous stream
-  const char* wblk = reinterpret_cast<const char*>(a.Wp) +
-                     (size_t)(el * a.n_tiles_n + n0) * nk * kBStage + drow * kRowBytes +
-                     16 * (lane & 7);
-  // weight-tile rows of this lane's two MFMA column blocks
-  const int jb0 = MODE == MODE_SWIGLU ? wn * 32 + l32 : wn * 64 + l32;
-  const int jb1 = MODE == MODE_SWIGLU ? 128 + wn * 32 + l32 : wn * 64 + 32 + l32;
+  // this wavefront's weight fragments: stage G of the run at G * kWStage
+  const char* wbase = reinterpret_cast<const char*>(a.Wp) +
+                      (size_t)(el * a.n_tiles_n + n0) * nk * kWStage + wave * 8192;
+  const uint32_t wlane = 16u * lane;
 
-  f32x16 acc0[MI > 0 ? MI : 1], acc1[MI > 0 ? MI : 1];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc0[i][r] = 0.f;
-      acc1[i][r] = 0.f;
-    }
-  }
+  u32x4 bw[kP][8];
 
-  // K chunks past K hold zeros in the weight blocks, so the activation side
-  // may load anything finite there: clamp the offset into the row.
-#define ISSUE(G, SLOT)                                                             \
+  // Issue state, all scalar: the next stage to issue is K stage iss_k of the
+  // weight block at iss_w; once the last stage is issued the pointers stop
+  // and further issues reload it (in bounds, never read), so every step
+  // issues the same number of loads.
+  int iss_k = 0, iss_left = nstage;
+  // this wavefront's rows of ring slot 0; made opaque once per stage below,
+  // so that the per-slot, per-round LDS addresses are recomputed where they
+  // are used instead of all being hoisted into scalar registers
+  char* lds_w = smem + 8 * wave * kRowBytes;
+  const char* iss_w = wbase;
+  // K chunks past K (and whole padding stages) have zero weights, so the
+  // activation side may load anything finite there: clamp into the row.
+#define ISSUE(SLOT)                                                                \
   {                                                                                \
-    char* st_ = smem + (SLOT) * R::STAGE;                                          \
-    const int k0_ = ((G) % nk) * BK;                                               \
-    const int ko_ = k0_ + 8 * dchunk < K ? k0_ : K - 8 - 8 * dchunk;               \
-    _Pragma("unroll") for (int i_ = 0; i_ < R::A_ROUNDS; ++i_)                     \
-      dma16(ap + (int64_t)aoff[i_] * K + ko_, st_ + (64 * i_ + 8 * wave) * kRowBytes); \
-    const char* wb_ = wblk + (size_t)(G) * kBStage;                                \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                               \
-      dma16(wb_ + i_ * 64 * kRowBytes, st_ + R::A_BYTES + (64 * i_ + 8 * wave) * kRowBytes); \
+    char* st_ = lds_w + (SLOT) * R::A_BYTES;                                       \
+    const int kc_ = iss_k * BK + dcol;                                             \
+    const uint32_t cb_ = 2u * (uint32_t)(kc_ < K ? kc_ : K - 8);                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_)                              \
+      dma16(abase + (arow[i_] + cb_), st_ + 32 * i_ * kRowBytes);                  \
+    const char* wb_ = iss_w + wlane;                                               \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) bw[SLOT][j_] = load_nt(wb_ + 1024 * j_); \
+    if (iss_left > 1) {                                                            \
+      --iss_left;                                                                  \
+      iss_w += kWStage;                                                            \
+      iss_k = iss_k + 1 == nk ? 0 : iss_k + 1;                                     \
+    }                                                                              \
   }
 
 #pragma unroll
-  for (int p = 0; p < R::NST - 1; ++p) ISSUE(p < nstage ? p : nstage - 1, p);
+  for (int p = 0; p < kP - 1; ++p) ISSUE(p);
 
-  bool drained = false;  // the previous iteration ended a tile with stores
-  for (int g = 0; g < nstage; ++g) {
-    // This wavefront's part of stage g has landed.  After an epilogue the
-    // vector-memory counter also holds its stores, so wait for everything.
-    if (drained)
-      wait_vmcnt<0>();
-    else
-      wait_vmcnt<(R::NST - 2) * R::LOADS>();
-    // Everyone's part landed and stage g-1 is consumed (its LDS reads fed
-    // MFMAs, so they completed).  A bare s_barrier: __syncthreads() would add
-    // a release fence, i.e. wait for *all* outstanding loads -- including the
-    // stages prefetched ahead -- and serialize the pipeline.
-    __builtin_amdgcn_s_barrier();
-    {
-      // refill the slot of stage g-1; past the end, reload the last stage
-      // (in bounds, never read) so every iteration issues the same count
-      const int gn = g + R::NST - 1;
-      ISSUE(gn < nstage ? gn : nstage - 1, gn % R::NST);
-    }
-    drained = false;
-    if (MI > 0) {
-      __builtin_amdgcn_sched_barrier(0);
-      const char* sa = smem + (g % R::NST) * R::STAGE;
-      const char* sbt = sa + R::A_BYTES;
-      // Operand fragments: each activation fragment is re-read for step s + 1
-      // right after the two MFMAs of step s that consume it, and the two
-      // weight fragments of step s + 1 at the start of step s, so every LDS
-      // read has a whole step of MFMAs to land while only one set of
-      // activation fragments is live (the accumulators need the registers).
-      u32x4 fa[MI > 0 ? MI : 1], fb[2][2];
+  for (int tile = n0; tile < n0 + ntile; ++tile) {
+  // accumulators live only inside one tile (carried across the tile loop
+  // they would be kept in a second copy)
+  f32x16 acc[2][NS];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = *(const u32x4*)(sa + swz(32 * (first + i) + l32, lg));
-      fb[0][0] = *(const u32x4*)(sbt + swz(jb0, lg));
-      fb[0][1] = *(const u32x4*)(sbt + swz(jb1, lg));
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][i][r] = 0.f;
+  for (int kk = 0; kk < nk; kk += kP) {
+#pragma unroll
+    for (int u = 0; u < kP; ++u) {
+      wait_vmcnt<(kP - 2) * R::LOADS>();
+      // every wavefront's part of slot u has landed and slot u - 1 is
+      // consumed (its LDS reads fed MFMAs).  A bare s_barrier: a
+      // __syncthreads() fence would wait for the whole prefetch.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" : "+s"(lds_w));
+      ISSUE((u + kP - 1) % kP);
+      __builtin_amdgcn_sched_barrier(0);
+      const char* sa = smem + u * R::A_BYTES;
+      // Activation fragments are re-read for step s + 1 right after the two
+      // MFMAs of step s that consume them.
+      u32x4 fa[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, lg));
 #pragma unroll
       for (int s_ = 0; s_ < 4; ++s_) {
-        const int cur = s_ & 1;
+        const bf16x8 b0 = as_bf16x8(bw[u][2 * s_]);
+        const bf16x8 b1 = as_bf16x8(bw[u][2 * s_ + 1]);
         const int chn = 2 * (s_ + 1) + lg;
-        if (s_ < 3) {
-          fb[cur ^ 1][0] = *(const u32x4*)(sbt + swz(jb0, chn));
-          fb[cur ^ 1][1] = *(const u32x4*)(sbt + swz(jb1, chn));
-        }
-        const bf16x8 b0 = as_bf16x8(fb[cur][0]);
-        const bf16x8 b1 = as_bf16x8(fb[cur][1]);
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < NS; ++i) {
           const bf16x8 af = as_bf16x8(fa[i]);
-          acc0[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0[i], 0, 0, 0);
-          acc1[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1[i], 0, 0, 0);
-          if (s_ < 3) fa[i] = *(const u32x4*)(sa + swz(32 * (first + i) + l32, chn));
+          acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc[0][i], 0, 0, 0);
+          acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc[1][i], 0, 0, 0);
+          if (s_ < 3) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, chn));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if ((g % nk) == nk - 1) {
-        // Epilogue of tile n0 + g / nk.  acc[i][r] is row 8 (r / 4) + 4 lg +
-        // r % 4 of row block first + i, column l32 of its 32-column block.
-        // Rows r and r + 1 (r even) are adjacent: lanes 2j and 2j + 1 swap
-        // one value so that the even lane writes columns (2j, 2j+1) of row r
-        // and the odd lane the same columns of row r + 1, 4 bytes each.
-        const int nt = n0 + g / nk;
-        const int n_base = MODE == MODE_SWIGLU ? nt * 128 + wn * 32 : nt * 256 + wn * 64;
+    }
+  }
+  {
+        // Epilogue of tile `tile`.  acc[c][i][r] is row 8 (r / 4) +
+        // 4 lg + r % 4 of row block i, column l32 of the wavefront's weight
+        // block c.  Rows r and r + 1 (r even) are adjacent: lanes 2j and
+        // 2j + 1 swap one value so that the even lane writes columns
+        // (2j, 2j+1) of row r and the odd lane the same columns of row r + 1,
+        // 4 bytes each.
+        const int nt = tile;
         const bool odd = lane & 1;
-        const int col = n_base + (l32 & ~1);
         // Opaque copy of the row length: without it the compiler hoists every
         // row address of the epilogue out of the tile loop and spills them.
         int nout = a.Nout;
         asm volatile("" : "+s"(nout));
         uint16_t* out = a.Out + o_row0 * nout;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+        for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
+          // SwiGLU: block 0 holds the W1 products and block 1 the W3 products
+          // of hidden units 32 wave + l32, in the same lanes
+          const int col = MODE == MODE_SWIGLU ? nt * 128 + 32 * wave + (l32 & ~1)
+                                              : nt * 256 + 64 * wave + 32 * c + (l32 & ~1);
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const int row = 32 * (first + i) + 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+          for (int i = 0; i < NS; ++i) {
 #pragma unroll
-            for (int cb = 0; cb < (MODE == MODE_SWIGLU ? 1 : 2); ++cb) {
+            for (int r = 0; r < 16; r += 2) {
               float v0, v1;
               if (MODE == MODE_SWIGLU) {
-                v0 = silu_f(acc0[i][r]) * acc1[i][r];
-                v1 = silu_f(acc0[i][r + 1]) * acc1[i][r + 1];
+                v0 = silu_f(acc_read(acc[0][i][r])) * acc_read(acc[1][i][r]);
+                v1 = silu_f(acc_read(acc[0][i][r + 1])) * acc_read(acc[1][i][r + 1]);
               } else {
-                v0 = cb == 0 ? acc0[i][r] : acc1[i][r];
-                v1 = cb == 0 ? acc0[i][r + 1] : acc1[i][r + 1];
+                v0 = acc_read(acc[c][i][r]);
+                v1 = acc_read(acc[c][i][r + 1]);
                 if (MODE == MODE_GELU) {
                   v0 = gelu_erf(v0);
                   v1 = gelu_erf(v1);
                 }
               }
-              const float send = odd ? v0 : v1;
-              const float got = __shfl_xor(send, 1);
+              const float got = swap_adjacent(odd ? v0 : v1);
               const float lo = odd ? got : v0;  // column col
               const float hi = odd ? v1 : got;  // column col + 1
-              const int c = col + 32 * cb;
-              if (row < rows && c < nout)
-                *(unsigned int*)(out + (row * nout + c)) = pack_bf16x2(lo, hi);
+              const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+              if (row < rows && col < nout)
+                *(unsigned int*)(out + (row * nout + col)) = pack_bf16x2(lo, hi);
               // one pair at a time: keeps the epilogue's temporaries from
               // piling up next to the live accumulators
               __builtin_amdgcn_sched_barrier(0);
             }
           }
         }
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc0[i][r] = 0.f;
-            acc1[i][r] = 0.f;
-          }
-        }
-        drained = true;
-      }
-    } else if ((g % nk) == nk - 1) {
-      drained = true;
-    }
+    // the counter now also holds stores, which are not ordered with the
+    // loads: wait for everything before the next tile's first stage
+    wait_vmcnt<0>();
+  }
   }
 #undef ISSUE
   wait_vmcnt<0>();
   __syncthreads();
-}
-
-// Row blocks are split between the two wavefront rows: the first takes
-// ceil(NS / 2) blocks, the second the rest.
-template <int MODE, int NS>
-__device__ __forceinline__ void gemm_tiles(const GemmArgs& a, char* smem, int el, int n0,
-                                           int ntile, int64_t a_row0, int64_t o_row0, int rows) {
-  if ((threadIdx.x >> 8) == 0)
-    gemm_run<MODE, NS, (NS + 1) / 2>(a, smem, el, n0, ntile, a_row0, o_row0, rows, 0);
-  else
-    gemm_run<MODE, NS, NS / 2>(a, smem, el, n0, ntile, a_row0, o_row0, rows, (NS + 1) / 2);
 }
 
 // Persistent over a contiguous range of tiles (expert-major, then row slice,
@@ -346,7 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     t0 = bid < per * kXcd ? (bid % kXcd) * per + bid / kXcd : bid;
     t1 = t0 + 1;
   } else {
-    t0 = blockIdx.x * a.per_wg;
+    // a contiguous range per workgroup, the ranges of neighbouring logical
+    // ids (mostly one expert) placed on the same XCD: workgroups are dealt
+    // round-robin over the XCDs, so block b runs on XCD b % 8
+    const int nper = gridDim.x / kXcd, b = blockIdx.x;
+    const int L = b < nper * kXcd ? (b % kXcd) * nper + b / kXcd : b;
+    t0 = L * a.per_wg;
     t1 = t0 + a.per_wg < a.total ? t0 + a.per_wg : a.total;
   }
   const int loc = a.eo[a.e_begin];
@@ -366,14 +385,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
     const int rows = M - m0 < BM ? M - m0 : BM;
     switch ((rows + 31) >> 5) {
-      case 1: gemm_tiles<MODE, 1>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 2: gemm_tiles<MODE, 2>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 3: gemm_tiles<MODE, 3>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 4: gemm_tiles<MODE, 4>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 5: gemm_tiles<MODE, 5>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 6: gemm_tiles<MODE, 6>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 7: gemm_tiles<MODE, 7>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      default: gemm_tiles<MODE, 8>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 1: gemm_run<MODE, 1>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 2: gemm_run<MODE, 2>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 3: gemm_run<MODE, 3>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 4: gemm_run<MODE, 4>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 5: gemm_run<MODE, 5>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 6: gemm_run<MODE, 6>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 7: gemm_run<MODE, 7>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      default: gemm_run<MODE, 8>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
     }
   }
 }
@@ -392,8 +411,8 @@ int device_cus() {
 }
 
 // One workgroup per CU (the LDS ring takes all 160 KB).  A launch with no
-// more tiles than CUs gives each workgroup one tile and groups an expert's
-// tiles on one XCD; a larger one hands each workgroup a contiguous range.
+// more tiles than CUs gives each workgroup one tile, a larger one hands each
+// workgroup a contiguous range; either way an expert's tiles share an XCD.
 template <int MODE>
 hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
   if (g.total <= 0) return hipSuccess;
@@ -412,34 +431,40 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Blocked weight layout: for expert e, output tile nt, stage kt, one 32 KB
-// block of 256 rows x 8 chunks of 16 B; chunk p of row j holds K chunk
-// p ^ swz_key(j) of the row's weight-matrix row (zeros past N or K).  Row j is
-// weight row nt*256 + j (GELU, plain), or W1 row nt*128 + j for j < 128 and
-// W3 row nt*128 + j - 128 otherwise (SwiGLU).
+// Blocked weight layout, in the order the wavefronts load it: for expert e,
+// output tile nt and stage kt (nk stages, padded to a multiple of kP), one
+// 32 KB block; inside it wavefront w's 8 KB, then MFMA step s's 2 KB, then
+// column block cb's 1 KB, then lane l's 16 bytes = K values
+// kt*64 + 16 s + 8 (l / 32) .. +7 of weight-tile row j = 64 w + 32 cb + l % 32
+// (zeros past N or K).  Tile row j is weight row nt*256 + j (GELU, plain);
+// for SwiGLU, block cb = 0 of wavefront w is W1 rows nt*128 + 32 w .. +31
+// and block cb = 1 the W3 rows of the same hidden units, so both products
+// of a hidden unit land in the same lane.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W0,
                                                            const uint16_t* __restrict__ W1,
                                                            int n_exp, int Nw, int K, int n_tiles,
                                                            int nk, int swiglu,
                                                            uint16_t* __restrict__ out) {
-  const int64_t total = (int64_t)n_exp * n_tiles * nk * kTileRows * 8;
+  const int64_t total = (int64_t)n_exp * n_tiles * nk * (kWStage / 16);
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
        q += (int64_t)gridDim.x * 256) {
-    const int p = (int)(q & 7);
-    const int j = (int)((q >> 3) & (kTileRows - 1));
+    const int l = (int)(q & 63);
+    const int cb = (int)((q >> 6) & 1);
+    const int s = (int)((q >> 7) & 3);
+    const int w = (int)((q >> 9) & 3);
     int64_t rest = q >> 11;
     const int kt = (int)(rest % nk);
     rest /= nk;
     const int nt = (int)(rest % n_tiles);
     const int e = (int)(rest / n_tiles);
-    const int k = kt * BK + 8 * (p ^ swz_key(j));
+    const int k = kt * BK + 16 * s + 8 * (l >> 5);
     int n;
     const uint16_t* src;
     if (swiglu) {
-      n = nt * 128 + (j & 127);
-      src = j < 128 ? W0 : W1;
+      n = nt * 128 + 32 * w + (l & 31);
+      src = cb == 0 ? W0 : W1;
     } else {
-      n = nt * 256 + j;
+      n = nt * 256 + 64 * w + 32 * cb + (l & 31);
       src = W0;
     }
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -455,8 +480,9 @@ struct Geo {
 Geo geo(int n_local, int N, int K, bool swiglu) {
   Geo g;
   g.n_tiles = swiglu ? (N + 127) / 128 : (N + 255) / 256;
-  g.nk = (K + BK - 1) / BK;
-  g.bytes = (size_t)n_local * g.n_tiles * g.nk * kBStage;
+  const int nk = (K + BK - 1) / BK;
+  g.nk = (nk + kP - 1) / kP * kP;
+  g.bytes = (size_t)n_local * g.n_tiles * g.nk * kWStage;
   return g;
 }
 

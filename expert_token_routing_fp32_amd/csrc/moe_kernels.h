@@ -24,8 +24,13 @@ __device__ __forceinline__ unsigned int f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// gfx950's v_cvt_pk_bf16_f32 (same result as f32_to_bf16 on finite values)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ void unpack8(u32x4 v, float* o) {
 #pragma unroll
