@@ -67,9 +67,8 @@ struct GemmArgs {
   int a_local, o_local;      // row index relative to expert_offset[e_begin]
   int e_begin;
   int K, Nout;
-  int n_tiles_n, m_tiles, nk, total;
-  int per_wg;                // consecutive tiles per workgroup
-  int remap;                 // one tile per workgroup, same-expert tiles on one XCD
+  int n_tiles_n, nk;
+  int n_local;               // experts e_begin .. e_begin + n_local - 1
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -345,42 +344,76 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   __syncthreads();
 }
 
-// Persistent over a contiguous range of tiles (expert-major, then row slice,
-// then output tile).  Consecutive tiles of one expert and row slice are one
-// pipelined run; the weight blocks of a run are contiguous in memory.
+// Persistent over an equal share of the active tiles.  Expert el has
+// ceil(M_el / BM) row slices of its M_el rows, each with n_tiles_n output
+// tiles; tiles are ordered (expert, row slice, output tile), so consecutive
+// tiles of one expert and row slice form a pipelined run over contiguous
+// weight blocks.  Every workgroup counts the active tiles itself from
+// expert_offset (a scan of one value per expert in LDS), so experts with no
+// rows cost nothing and skewed routing does not idle workgroups.
+constexpr int kRingBytes = kP * Ring<8>::A_BYTES;
+static_assert(kRingBytes + 4 * 1029 <= kLdsBytes, "LDS budget");
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  int t0, t1;
-  if (a.remap) {
-    // one tile each: consecutive tiles (same expert) on the same XCD, which
-    // then reads that expert's activation rows from HBM once
-    const int bid = blockIdx.x;
-    const int per = a.total / kXcd;
-    t0 = bid < per * kXcd ? (bid % kXcd) * per + bid / kXcd : bid;
-    t1 = t0 + 1;
-  } else {
-    // a contiguous range per workgroup, the ranges of neighbouring logical
-    // ids (mostly one expert) placed on the same XCD: workgroups are dealt
-    // round-robin over the XCDs, so block b runs on XCD b % 8
-    const int nper = gridDim.x / kXcd, b = blockIdx.x;
-    const int L = b < nper * kXcd ? (b % kXcd) * nper + b / kXcd : b;
-    t0 = L * a.per_wg;
-    t1 = t0 + a.per_wg < a.total ? t0 + a.per_wg : a.total;
+  // pre[el] = active (expert, row slice) pairs of the experts before el
+  int* pre = reinterpret_cast<int*>(smem + kRingBytes);
+  int* wsum = pre + 1025;  // per-wavefront totals (4)
+  const int nl = a.n_local;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    // thread tid scans experts [4 tid, 4 tid + 4) (n_local <= 1024)
+    int cnt[4], run_ = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int el = 4 * tid + j;
+      int m = 0;
+      if (el < nl) {
+        const int M = a.eo[a.e_begin + el + 1] - a.eo[a.e_begin + el];
+        m = (M + BM - 1) / BM;
+      }
+      cnt[j] = run_;
+      run_ += m;
+    }
+    // inclusive scan of the per-thread totals inside the wavefront
+    int incl = run_;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = incl - run_;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * tid + j < nl) pre[4 * tid + j] = base + cnt[j];
+    if (tid == kThreads - 1) pre[nl] = base + run_;
+    __syncthreads();
   }
+  const int64_t total = (int64_t)pre[nl] * a.n_tiles_n;
+  // neighbouring logical ids (mostly one expert's tiles) on the same XCD:
+  // workgroups are dealt round-robin over the XCDs, block b runs on XCD b % 8
+  const int G = gridDim.x, b = blockIdx.x;
+  const int nper = G / kXcd;
+  const int L = b < nper * kXcd ? (b % kXcd) * nper + b / kXcd : b;
+  const int64_t t0 = total * L / G, t1 = total * (L + 1) / G;
+  if (t0 >= t1) return;
   const int loc = a.eo[a.e_begin];
-  for (int t = t0; t < t1;) {
-    const int n_t = t % a.n_tiles_n;
-    const int em = t / a.n_tiles_n;  // expert and row slice
-    const int m_t = em % a.m_tiles;
-    const int el = em / a.m_tiles;
-    const int run = (t1 - t < a.n_tiles_n - n_t) ? t1 - t : a.n_tiles_n - n_t;
+  int el = 0;  // expert of the current pair (pairs only grow along the range)
+  for (int64_t t = t0; t < t1;) {
+    const int p = (int)(t / a.n_tiles_n);
+    const int n_t = (int)(t - (int64_t)p * a.n_tiles_n);
+    while (pre[el + 1] <= p) ++el;
+    const int m_t = p - pre[el];
+    const int run = (int)(t1 - t < a.n_tiles_n - n_t ? t1 - t : a.n_tiles_n - n_t);
     t += run;
     const int e = a.e_begin + el;
     const int rb = a.eo[e];
     const int M = a.eo[e + 1] - rb;
     const int m0 = m_t * BM;
-    if (m0 >= M) continue;
     const int64_t a_row0 = (int64_t)(rb - (a.a_local ? loc : 0) + m0);
     const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
     const int rows = M - m0 < BM ? M - m0 : BM;
@@ -410,23 +443,14 @@ int device_cus() {
   return cus;
 }
 
-// One workgroup per CU (the LDS ring takes all 160 KB).  A launch with no
-// more tiles than CUs gives each workgroup one tile, a larger one hands each
-// workgroup a contiguous range; either way an expert's tiles share an XCD.
+// One workgroup per CU (the LDS ring takes most of the 160 KB), no more
+// workgroups than there could be tiles.
 template <int MODE>
-hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
-  if (g.total <= 0) return hipSuccess;
+hipError_t launch_gemm(GemmArgs g, int m_tiles, hipStream_t s) {
+  const int64_t bound = (int64_t)g.n_local * m_tiles * g.n_tiles_n;
+  if (bound <= 0) return hipSuccess;
   const int cus = device_cus();
-  int grid;
-  if (g.total <= cus) {
-    g.remap = 1;
-    g.per_wg = 1;
-    grid = g.total;
-  } else {
-    g.remap = 0;
-    g.per_wg = (g.total + cus - 1) / cus;
-    grid = (g.total + g.per_wg - 1) / g.per_wg;
-  }
+  const int grid = bound < cus ? (int)bound : cus;
   hipLaunchKernelGGL(grouped_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
@@ -527,9 +551,9 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g1.Nout = f;
   g1.n_tiles_n = geo1.n_tiles;
   g1.nk = geo1.nk;
-  g1.m_tiles = m_tiles;
-  g1.total = n_local * m_tiles * g1.n_tiles_n;
-  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, s) : launch_gemm<MODE_GELU>(g1, s);
+  g1.n_local = n_local;
+  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, s)
+                          : launch_gemm<MODE_GELU>(g1, m_tiles, s);
   if (err != hipSuccess) return err;
 
   GemmArgs g2{};
@@ -544,9 +568,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g2.Nout = d;
   g2.n_tiles_n = geo2.n_tiles;
   g2.nk = geo2.nk;
-  g2.m_tiles = m_tiles;
-  g2.total = n_local * m_tiles * g2.n_tiles_n;
-  return launch_gemm<MODE_PLAIN>(g2, s);
+  g2.n_local = n_local;
+  return launch_gemm<MODE_PLAIN>(g2, m_tiles, s);
 }
 
 }  // namespace moek
