@@ -25,52 +25,52 @@ unsigned grid_for(int64_t work, int threads) {
   return (unsigned)g;
 }
 
+// One wavefront per token row, one lane per 16-byte chunk: block (4 tokens)
+// x (64 chunks), grid (ceil(B / 4), ceil(d / 512)).  The token index is
+// wavefront-uniform, so dest and the weights come through scalar loads.
 template <bool XBF16, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t* __restrict__ ret, const int32_t* __restrict__ dest,
     const float* __restrict__ w, const void* __restrict__ xres, void* __restrict__ y, int64_t B,
     int k, int d, int64_t kmax) {
   const int cpr = d / 8;
-  const int64_t total = B * cpr;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t t = i / cpr;
-    const int c = (int)(i - t * cpr);
-    float acc[8];
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.y * 64 + (threadIdx.x & 63);
+  if (t >= B || c >= cpr) return;
+  float acc[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = dest[t * k + j];
-      if (r >= 0 && r < kmax) {
-        const float wj = w[t * k + j];
-        const u32x4 v = *(const u32x4*)(ret + (int64_t)r * d + c * 8);
-        float f[8];
-        unpack8(v, f);
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int r = dest[t * k + j];
+    if (r >= 0 && r < kmax) {
+      const float wj = w[t * k + j];
+      const u32x4 v = *(const u32x4*)(ret + (int64_t)r * d + c * 8);
+      float f[8];
+      unpack8(v, f);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
-      }
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
     }
-    if (RES) {
-      float xr[8];
-      if (XBF16) {
-        unpack8(*(const u32x4*)((const uint16_t*)xres + t * d + c * 8), xr);
-      } else {
-        const float* xf = (const float*)xres + t * d + c * 8;
-        const f32x4 a = *(const f32x4*)xf;
-        const f32x4 b = *(const f32x4*)(xf + 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) { xr[u] = a[u]; xr[u + 4] = b[u]; }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += xr[u];
-    }
+  }
+  if (RES) {
+    float xr[8];
     if (XBF16) {
-      *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
+      unpack8(*(const u32x4*)((const uint16_t*)xres + t * d + c * 8), xr);
     } else {
-      float* yf = (float*)y + t * d + c * 8;
-      *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      const float* xf = (const float*)xres + t * d + c * 8;
+      const f32x4 a = *(const f32x4*)xf;
+      const f32x4 b = *(const f32x4*)(xf + 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { xr[u] = a[u]; xr[u + 4] = b[u]; }
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += xr[u];
+  }
+  if (XBF16) {
+    *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
+  } else {
+    float* yf = (float*)y + t * d + c * 8;
+    *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -115,7 +115,7 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
                           int64_t kmax, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const unsigned g = grid_for(B * (d / 8), 256);
+  const dim3 g((unsigned)((B + 3) / 4), (unsigned)((d / 8 + 63) / 64));
   if (x_bf16) {
     if (x_res)
       hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,

@@ -184,30 +184,31 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   }
 }
 
+// One wavefront per token row, one lane per 16-byte chunk (block: 4 tokens x
+// 64 chunks): the row is read once and written to each of its kept packed
+// rows; the token index is wavefront-uniform, so dest comes through scalar
+// loads.
 template <bool XBF16>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
                                                    const int32_t* __restrict__ dest, int64_t B,
                                                    int k, int d, uint16_t* __restrict__ packed) {
   const int cpr = d / 8;
-  const int64_t total = B * cpr;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t t = i / cpr;
-    const int c = (int)(i - t * cpr);
-    u32x4 v;
-    if (XBF16) {
-      v = *(const u32x4*)((const uint16_t*)x + t * d + c * 8);
-    } else {
-      const float* xf = (const float*)x + t * d + c * 8;
-      const f32x4 a = *(const f32x4*)xf;
-      const f32x4 b = *(const f32x4*)(xf + 4);
-      const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      v = pack8(f);
-    }
-    for (int j = 0; j < k; ++j) {
-      const int r = dest[t * k + j];
-      if (r >= 0) *(u32x4*)(packed + (int64_t)r * d + c * 8) = v;
-    }
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.y * 64 + (threadIdx.x & 63);
+  if (t >= B || c >= cpr) return;
+  u32x4 v;
+  if (XBF16) {
+    v = *(const u32x4*)((const uint16_t*)x + t * d + c * 8);
+  } else {
+    const float* xf = (const float*)x + t * d + c * 8;
+    const f32x4 a = *(const f32x4*)xf;
+    const f32x4 b = *(const f32x4*)(xf + 4);
+    const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    v = pack8(f);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int r = dest[t * k + j];
+    if (r >= 0) *(u32x4*)(packed + (int64_t)r * d + c * 8) = v;
   }
 }
 
@@ -220,10 +221,14 @@ unsigned grid_for(int64_t work, int threads) {
 
 }  // namespace
 
+// Claim-order tiles of 256 .. 2048 assignments: small enough that the
+// histogram and rank passes run on many workgroups, large enough that the
+// single-workgroup scan over (tile, expert) stays short (<= ~256 tiles).
 SlotPlan slot_plan(int64_t B, int k) {
   SlotPlan p;
   p.BK = B * k;
-  p.tile = 2048;
+  p.tile = 256;
+  while (p.tile < 2048 && p.BK > (int64_t)p.tile * 256) p.tile <<= 1;
   p.n_tiles = (int)((p.BK + p.tile - 1) / p.tile);
   return p;
 }
@@ -260,7 +265,7 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
                        uint16_t* packed, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const unsigned g = grid_for(B * (d / 8), 256);
+  const dim3 g((unsigned)((B + 3) / 4), (unsigned)((d / 8 + 63) / 64));
   if (x_bf16)
     hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
   else
