@@ -352,7 +352,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 // expert_offset (a scan of one value per expert in LDS), so experts with no
 // rows cost nothing and skewed routing does not idle workgroups.
 constexpr int kRingBytes = kP * Ring<8>::A_BYTES;
-static_assert(kRingBytes + 4 * 1029 <= kLdsBytes, "LDS budget");
+static_assert(kRingBytes + 4 * (1029 + 1025) <= kLdsBytes, "LDS budget");
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
@@ -360,6 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   // pre[el] = active (expert, row slice) pairs of the experts before el
   int* pre = reinterpret_cast<int*>(smem + kRingBytes);
   int* wsum = pre + 1025;  // per-wavefront totals (4)
+  int* eos = wsum + 4;     // expert_offset[e_begin .. e_begin + n_local]
   const int nl = a.n_local;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   {
@@ -370,8 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int el = 4 * tid + j;
       int m = 0;
       if (el < nl) {
-        const int M = a.eo[a.e_begin + el + 1] - a.eo[a.e_begin + el];
-        m = (M + BM - 1) / BM;
+        const int lo = a.eo[a.e_begin + el], hi = a.eo[a.e_begin + el + 1];
+        eos[el] = lo;
+        if (el == nl - 1) eos[nl] = hi;
+        m = (hi - lo + BM - 1) / BM;
       }
       cnt[j] = run_;
       run_ += m;
@@ -401,8 +404,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int L = b < nper * kXcd ? (b % kXcd) * nper + b / kXcd : b;
   const int64_t t0 = total * L / G, t1 = total * (L + 1) / G;
   if (t0 >= t1) return;
-  const int loc = a.eo[a.e_begin];
-  int el = 0;  // expert of the current pair (pairs only grow along the range)
+  const int loc = eos[0];
+  // expert of the first pair: the last el with pre[el] <= p (binary search;
+  // experts without rows share their pre value with the next one)
+  int el = 0;
+  {
+    const int p = (int)(t0 / a.n_tiles_n);
+    int lo = 0, hi = nl - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    el = lo;
+  }
   for (int64_t t = t0; t < t1;) {
     const int p = (int)(t / a.n_tiles_n);
     const int n_t = (int)(t - (int64_t)p * a.n_tiles_n);
@@ -410,9 +424,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int m_t = p - pre[el];
     const int run = (int)(t1 - t < a.n_tiles_n - n_t ? t1 - t : a.n_tiles_n - n_t);
     t += run;
-    const int e = a.e_begin + el;
-    const int rb = a.eo[e];
-    const int M = a.eo[e + 1] - rb;
+    const int rb = eos[el];
+    const int M = eos[el + 1] - rb;
     const int m0 = m_t * BM;
     const int64_t a_row0 = (int64_t)(rb - (a.a_local ? loc : 0) + m0);
     const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
