@@ -262,7 +262,16 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       // __syncthreads() fence would wait for the whole prefetch.
       __builtin_amdgcn_s_barrier();
       asm volatile("" : "+s"(lds_w));
-      ISSUE((u + kP - 1) % kP);
+      // Stage g + kP - 1 is issued spread between this stage's MFMAs, not as
+      // one burst: part q (NS activation rounds, then 8 weight fragments)
+      // follows MFMA pair q * 4NS / NL.  With one wavefront per SIMD, a load
+      // whose issue stalls (memory queues full) stalls the matrix core too;
+      // spread out, the stalls fall in the gaps between MFMAs.
+      constexpr int NL = NS + 8;
+      char* ist_ = lds_w + ((u + kP - 1) % kP) * R::A_BYTES;
+      const int ikc_ = iss_k * BK + dcol;
+      const uint32_t icb_ = 2u * (uint32_t)(ikc_ < K ? ikc_ : K - 8);
+      const char* iwb_ = iss_w + wlane;
       __builtin_amdgcn_sched_barrier(0);
       const char* sa = smem + u * R::A_BYTES;
       // Activation fragments are re-read for step s + 1 right after the two
@@ -281,8 +290,22 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc[0][i], 0, 0, 0);
           acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc[1][i], 0, 0, 0);
           if (s_ < 3) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, chn));
+#pragma unroll
+          for (int q = 0; q < NL; ++q) {
+            if (q * 4 * NS / NL == s_ * NS + i) {
+              if (q < NS)
+                dma16(abase + (arow[q < NS ? q : 0] + icb_), ist_ + 32 * q * kRowBytes);
+              else
+                bw[(u + kP - 1) % kP][q - NS] = load_nt(iwb_ + 1024 * (q - NS));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (iss_left > 1) {
+        --iss_left;
+        iss_w += kWStage;
+        iss_k = iss_k + 1 == nk ? 0 : iss_k + 1;
       }
     }
   }
