@@ -69,6 +69,7 @@ struct GemmArgs {
   int K, Nout;
   int n_tiles_n, nk;
   int n_local;               // experts e_begin .. e_begin + n_local - 1
+  int xcd_sched;             // 1: per-XCD blocks of (expert, tile, row slice), dealt round-robin
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -420,14 +421,56 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     __syncthreads();
   }
   const int64_t total = (int64_t)pre[nl] * a.n_tiles_n;
-  // neighbouring logical ids (mostly one expert's tiles) on the same XCD:
-  // workgroups are dealt round-robin over the XCDs, block b runs on XCD b % 8
   const int G = gridDim.x, b = blockIdx.x;
+  const int loc0 = eos[0];
+  if (a.xcd_sched) {
+    // Matrix-core-bound launches (hundreds of rows per expert): XCD x (the
+    // workgroups b with b % 8 == x; workgroups are dealt round-robin over
+    // the 8 XCDs) owns the x-th eighth of the tiles, ordered (expert,
+    // output tile, row slice), and deals them round-robin to its
+    // workgroups.  At any moment an XCD then works on a compact patch of
+    // one expert -- few row slices x few output tiles -- so the activation
+    // slices and weight tiles it streams are shared through its L2.
+    const int x = b % kXcd, j = b / kXcd;
+    const int nx = (G - x + kXcd - 1) / kXcd;  // workgroups on this XCD (G >= 8)
+    const int64_t xb = total * x / kXcd, xe = total * (x + 1) / kXcd;
+    for (int64_t t = xb + j; t < xe; t += nx) {
+      const int p = (int)(t / a.n_tiles_n);
+      int lo = 0, hi = nl - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      const int el = lo;
+      const int mel = pre[el + 1] - pre[el];  // row slices of this expert
+      const int64_t loc_t = t - (int64_t)pre[el] * a.n_tiles_n;
+      const int n_t = (int)(loc_t / mel), m_t = (int)(loc_t - (int64_t)n_t * mel);
+      const int rb = eos[el];
+      const int M = eos[el + 1] - rb;
+      const int m0 = m_t * BM;
+      const int64_t a_row0 = (int64_t)(rb - (a.a_local ? loc0 : 0) + m0);
+      const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc0 : 0) + m0);
+      const int rows = M - m0 < BM ? M - m0 : BM;
+      switch ((rows + 31) >> 5) {
+        case 1: gemm_run<MODE, 1>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 2: gemm_run<MODE, 2>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 3: gemm_run<MODE, 3>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 4: gemm_run<MODE, 4>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 5: gemm_run<MODE, 5>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 6: gemm_run<MODE, 6>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 7: gemm_run<MODE, 7>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        default: gemm_run<MODE, 8>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+      }
+    }
+    return;
+  }
+  // Weight-streaming launches: a contiguous range per workgroup, the ranges
+  // of neighbouring logical ids (mostly one expert's tiles) on the same XCD.
   const int nper = G / kXcd;
   const int L = b < nper * kXcd ? (b % kXcd) * nper + b / kXcd : b;
   const int64_t t0 = total * L / G, t1 = total * (L + 1) / G;
   if (t0 >= t1) return;
-  const int loc = eos[0];
+  const int loc = loc0;
   // expert of the first pair: the last el with pre[el] <= p (binary search;
   // experts without rows share their pre value with the next one)
   int el = 0;
@@ -482,11 +525,12 @@ int device_cus() {
 // One workgroup per CU (the LDS ring takes most of the 160 KB), no more
 // workgroups than there could be tiles.
 template <int MODE>
-hipError_t launch_gemm(GemmArgs g, int m_tiles, hipStream_t s) {
+hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s) {
   const int64_t bound = (int64_t)g.n_local * m_tiles * g.n_tiles_n;
   if (bound <= 0) return hipSuccess;
   const int cus = device_cus();
   const int grid = bound < cus ? (int)bound : cus;
+  g.xcd_sched = mfma_bound && grid >= kXcd ? 1 : 0;
   hipLaunchKernelGGL(grouped_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
@@ -570,9 +614,13 @@ hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uin
 }
 
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
-                             int n_local, int rows_max, int d, int f, bool swiglu, const void* wp,
-                             uint16_t* H, uint16_t* ret, hipStream_t s) {
+                             int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s) {
   if (n_local <= 0 || rows_max <= 0) return hipSuccess;
+  // a 256-column tile does 2 * rows FLOP per weight byte; above ~384 rows per
+  // expert the matrix cores, not the weight stream, set the pace (the
+  // MI355X bf16 / HBM ridge is ~310 FLOP per byte)
+  const bool mfma_bound = rows_hint >= 384;
   const int m_tiles = (rows_max + BM - 1) / BM;
   const Geo geo1 = geo(n_local, f, d, swiglu), geo2 = geo(n_local, d, f, false);
   GemmArgs g1{};
@@ -588,8 +636,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g1.n_tiles_n = geo1.n_tiles;
   g1.nk = geo1.nk;
   g1.n_local = n_local;
-  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, s)
-                          : launch_gemm<MODE_GELU>(g1, m_tiles, s);
+  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s)
+                          : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s);
   if (err != hipSuccess) return err;
 
   GemmArgs g2{};
@@ -605,7 +653,7 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g2.n_tiles_n = geo2.n_tiles;
   g2.nk = geo2.nk;
   g2.n_local = n_local;
-  return launch_gemm<MODE_PLAIN>(g2, m_tiles, s);
+  return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s);
 }
 
 }  // namespace moek

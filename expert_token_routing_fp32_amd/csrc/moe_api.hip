@@ -29,6 +29,13 @@ int64_t rows_per_expert(const moe_problem_t* p) {
   return C < p->B ? C : p->B;
 }
 
+// expected rows per expert with even routing, B k / E, at most the row cap
+int rows_hint(const moe_problem_t* p) {
+  const int64_t even = ((int64_t)p->B * p->k + p->E - 1) / p->E;
+  const int64_t cap = rows_per_expert(p);
+  return (int)(even < cap ? even : cap);
+}
+
 int64_t kmax_of(const moe_problem_t* p) {
   const int64_t bk = p->B * p->k;
   const int64_t ec = (int64_t)p->E * rows_per_expert(p);
@@ -252,7 +259,8 @@ moe_status_t moe_expert_ffn(const moe_problem_t* p, const moe_bf16_t* packed,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(moek::launch_expert_ffn(packed, expert_offset, p->e_begin, n_local,
-                                            (int)rows_per_expert(p), p->d, p->f, swiglu, wpacked,
+                                            (int)rows_per_expert(p), rows_hint(p), p->d, p->f,
+                                            swiglu, wpacked,
                                             static_cast<uint16_t*>(ws), ret, stream));
 }
 
@@ -308,7 +316,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
   if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_begin, stream);
   if (e == hipSuccess && p->B > 0)
     e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
-                                p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
+                                rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
   if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_end, stream);
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,

@@ -87,8 +87,9 @@ hipError_t launch_copy_remote(const uint16_t* src, uint16_t* dst, const int32_t*
 size_t packed_weights_bytes(int n_local, int d, int f, bool swiglu);
 hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
                                int n_local, int d, int f, bool swiglu, void* wp, hipStream_t s);
+// rows_hint: expected rows per local expert (chooses the tile schedule only)
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
-                             int n_local, int rows_max, int d, int f, bool swiglu, const void* wp,
-                             uint16_t* H, uint16_t* ret, hipStream_t s);
+                             int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s);
 
 }  // namespace moek

@@ -114,6 +114,10 @@ CASES = {
     "max_E_k": dict(w=dict(E=1024, k=16, e_end=1024, B=2048, d=64, f=16), ffn=False),
     "E_not_pow2_many": dict(w=dict(E=300, k=5, e_end=300, B=1500, d=48, f=32)),
     "drop_heavy": dict(w=dict(E=16, e_end=16, B=512, c=0.25, zipf_bias=True)),
+    # >= 384 rows per expert: the matrix-core tile schedule (per-XCD blocks)
+    "rows_1024_gelu": dict(w=dict(B=2048, d=72, E=4, e_end=4, k=2, c=1.0, f=520)),
+    "rows_1024_swiglu": dict(w=dict(B=2048, d=136, E=4, e_end=4, k=2, c=1.25, f=264,
+                                    act="swiglu")),
 }
 
 
