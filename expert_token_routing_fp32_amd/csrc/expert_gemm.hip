@@ -69,7 +69,6 @@ struct GemmArgs {
   int K, Nout;
   int n_tiles_n, nk;
   int n_local;               // experts e_begin .. e_begin + n_local - 1
-  int xcd_sched;             // 1: per-XCD blocks of (expert, tile, row slice), dealt round-robin
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -107,13 +106,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // (global_load_lds_dwordx4; lds must be wavefront-uniform).
 __device__ __forceinline__ void dma16(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
-}
-
-// The same with the non-temporal hint (cache-policy bit NT): for the weight
-// stream, which is read once, so that it does not push the activation rows
-// that the other tiles of the expert re-read out of L2.
-__device__ __forceinline__ void dma16nt(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 2);
 }
 
 // One accumulator element, read out of the accumulation registers where it
@@ -158,8 +150,14 @@ struct Ring {
 static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
 static_assert((kP - 2) * Ring<8>::LOADS < 64, "vmcnt range");
 
-__device__ __forceinline__ u32x4 load_nt(const char* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Weight fragment load.  Streaming launches (each weight byte used by one
+// tile) mark it non-temporal so it does not push the activation rows out of
+// L2; matrix-core-bound launches share weight tiles between row slices
+// through L2, so there it is an ordinary load.
+template <bool NT>
+__device__ __forceinline__ u32x4 load_w(const char* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // A run of `ntile` consecutive output tiles (n0 .. n0+ntile-1) of one expert
@@ -178,7 +176,7 @@ __device__ __forceinline__ u32x4 load_nt(const char* p) {
 // (kP - 2) stages' loads are outstanding means stage g has landed.  After an
 // epilogue the counter also holds stores, which are not ordered with the
 // loads: then wait for everything.
-template <int MODE, int NS>
+template <int MODE, int NS, bool NT>
 __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ smem, int el,
                                          int n0, int ntile, int64_t a_row0, int64_t o_row0,
                                          int rows) {
@@ -233,7 +231,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
     _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_)                              \
       dma16(abase + (arow[i_] + cb_), st_ + 32 * i_ * kRowBytes);                  \
     const char* wb_ = iss_w + wlane;                                               \
-    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) bw[SLOT][j_] = load_nt(wb_ + 1024 * j_); \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) bw[SLOT][j_] = load_w<NT>(wb_ + 1024 * j_); \
     if (iss_left > 1) {                                                            \
       --iss_left;                                                                  \
       iss_w += kWStage;                                                            \
@@ -297,7 +295,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
               if (q < NS)
                 dma16(abase + (arow[q < NS ? q : 0] + icb_), ist_ + 32 * q * kRowBytes);
               else
-                bw[(u + kP - 1) % kP][q - NS] = load_nt(iwb_ + 1024 * (q - NS));
+                bw[(u + kP - 1) % kP][q - NS] = load_w<NT>(iwb_ + 1024 * (q - NS));
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -378,7 +376,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 constexpr int kRingBytes = kP * Ring<8>::A_BYTES;
 static_assert(kRingBytes + 4 * (1029 + 1025) <= kLdsBytes, "LDS budget");
 
-template <int MODE>
+template <int MODE, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   // pre[el] = active (expert, row slice) pairs of the experts before el
@@ -423,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t total = (int64_t)pre[nl] * a.n_tiles_n;
   const int G = gridDim.x, b = blockIdx.x;
   const int loc0 = eos[0];
-  if (a.xcd_sched) {
+  if (XS) {
     // Matrix-core-bound launches (hundreds of rows per expert): XCD x (the
     // workgroups b with b % 8 == x; workgroups are dealt round-robin over
     // the 8 XCDs) owns the x-th eighth of the tiles, ordered (expert,
@@ -452,14 +450,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc0 : 0) + m0);
       const int rows = M - m0 < BM ? M - m0 : BM;
       switch ((rows + 31) >> 5) {
-        case 1: gemm_run<MODE, 1>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 2: gemm_run<MODE, 2>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 3: gemm_run<MODE, 3>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 4: gemm_run<MODE, 4>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 5: gemm_run<MODE, 5>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 6: gemm_run<MODE, 6>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        case 7: gemm_run<MODE, 7>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
-        default: gemm_run<MODE, 8>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 1: gemm_run<MODE, 1, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 2: gemm_run<MODE, 2, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 3: gemm_run<MODE, 3, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 4: gemm_run<MODE, 4, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 5: gemm_run<MODE, 5, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 6: gemm_run<MODE, 6, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        case 7: gemm_run<MODE, 7, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
+        default: gemm_run<MODE, 8, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
       }
     }
     return;
@@ -497,14 +495,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
     const int rows = M - m0 < BM ? M - m0 : BM;
     switch ((rows + 31) >> 5) {
-      case 1: gemm_run<MODE, 1>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 2: gemm_run<MODE, 2>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 3: gemm_run<MODE, 3>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 4: gemm_run<MODE, 4>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 5: gemm_run<MODE, 5>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 6: gemm_run<MODE, 6>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      case 7: gemm_run<MODE, 7>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
-      default: gemm_run<MODE, 8>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 1: gemm_run<MODE, 1, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 2: gemm_run<MODE, 2, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 3: gemm_run<MODE, 3, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 4: gemm_run<MODE, 4, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 5: gemm_run<MODE, 5, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 6: gemm_run<MODE, 6, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      case 7: gemm_run<MODE, 7, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
+      default: gemm_run<MODE, 8, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
     }
   }
 }
@@ -530,8 +528,10 @@ hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s) 
   if (bound <= 0) return hipSuccess;
   const int cus = device_cus();
   const int grid = bound < cus ? (int)bound : cus;
-  g.xcd_sched = mfma_bound && grid >= kXcd ? 1 : 0;
-  hipLaunchKernelGGL(grouped_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, g);
+  if (mfma_bound && grid >= kXcd)
+    hipLaunchKernelGGL((grouped_gemm_kernel<MODE, true>), dim3(grid), dim3(kThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<MODE, false>), dim3(grid), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
