@@ -46,6 +46,64 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return r;
 }
 
+// ---- routing of one token ---------------------------------------------------
+// The token's E logits row[0..E) are spread over L lanes (li = lane within
+// the group), V per lane.  Softmax with temperature (inv_tau), then k rounds
+// of arg-max by (logit descending, index ascending); lane li == 0 writes
+// idx_t[j] and the raw probability w_t[j].  Lanes past E hold nothing, so
+// the butterfly trees combine the same values in the same order for any L.
+template <int L, int V>
+__device__ __forceinline__ void route_token(const float* row, int E, int k, float inv_tau,
+                                            int li, bool tok, int32_t* idx_t, float* w_t) {
+  float v[V];
+  bool ok[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int e = li + u * L;
+    ok[u] = tok && e < E;
+    v[u] = ok[u] ? row[e] : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (ok[u]) m = fmaxf(m, v[u]);
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (ok[u]) s += expf((v[u] - m) * inv_tau);
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
+  unsigned taken = 0u;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int e = li + u * L;
+      if (ok[u] && !((taken >> u) & 1u) && (v[u] > bv || (v[u] == bv && e < bi))) {
+        bv = v[u];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, L);
+      const int oi = __shfl_xor(bi, off, L);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi != 0x7fffffff && bi % L == li) taken |= 1u << (bi / L);
+    if (li == 0 && tok) {
+      idx_t[j] = bi;
+      w_t[j] = expf((bv - m) * inv_tau) / s;
+    }
+  }
+}
+
 // ---- launchers --------------------------------------------------------------
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
                        float* logits, int64_t B, int d, int E, hipStream_t s);

@@ -12,8 +12,6 @@
 // A token's E logits are spread over L = min(64, pow2 >= E) lanes, V per lane.
 // Max, sum and each of the k arg-max rounds are butterfly reductions inside
 // the L-lane segment of the 64-wide wavefront.
-#include <climits>
-
 #include "moe_kernels.h"
 
 namespace moek {
@@ -29,56 +27,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int64_t t = ((int64_t)blockIdx.x * kRouteThreads + tid) / L;
   const int li = tid % L;
   const bool tok = t < B;
-
-  float v[V];
-  bool ok[V];
-#pragma unroll
-  for (int u = 0; u < V; ++u) {
-    const int e = li + u * L;
-    ok[u] = tok && e < E;
-    v[u] = ok[u] ? logits[t * E + e] : -INFINITY;
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < V; ++u)
-    if (ok[u]) m = fmaxf(m, v[u]);
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, L));
-
-  float s = 0.f;
-#pragma unroll
-  for (int u = 0; u < V; ++u)
-    if (ok[u]) s += expf((v[u] - m) * inv_tau);
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, L);
-
-  unsigned taken = 0u;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int u = 0; u < V; ++u) {
-      const int e = li + u * L;
-      if (ok[u] && !((taken >> u) & 1u) && (v[u] > bv || (v[u] == bv && e < bi))) {
-        bv = v[u];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, L);
-      const int oi = __shfl_xor(bi, off, L);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi != INT_MAX && bi % L == li) taken |= 1u << (bi / L);
-    if (li == 0 && tok) {
-      idx[t * k + j] = bi;
-      w[t * k + j] = expf((bv - m) * inv_tau) / s;
-    }
-  }
+  route_token<L, V>(logits + (tok ? t : 0) * E, E, k, inv_tau, li, tok, idx + t * k, w + t * k);
 }
 
 template <int L, int V>

@@ -8,7 +8,8 @@ the oracle's logits alone ("undecided"); every other token must be routed
 identically.  When all tokens agree, every integer output must match bit for
 bit.  Outputs y are compared on tokens whose choices and drop flags agree
 (all of them, normally) -- y of a token depends only on its own choices,
-weights and drop flags."""
+weights and drop flags.  The forward's choices and weights must also equal,
+bit for bit, what moe_route makes of the forward's own logits."""
 import numpy as np
 import pytest
 
@@ -41,8 +42,12 @@ def run_forward(w, inp, ref, name, n_sample=48):
                        wp, outputs=True)
     torch.cuda.synchronize()
     assert_f32_close(to_np(o["logits"]), ref["logits"], what=f"{name} logits")
-    und = undecided_tokens(ref["logits"], w.k)
     gi = to_np(o["topk_idx"])
+    # the forward's routing is the route kernel's on the forward's own logits
+    idx2, w2 = moe.route(p, o["logits"])
+    np.testing.assert_array_equal(to_np(idx2), gi)
+    np.testing.assert_array_equal(to_np(w2).view(np.uint32), to_np(o["topk_w"]).view(np.uint32))
+    und = undecided_tokens(ref["logits"], w.k)
     diff = np.nonzero((gi != ref["idx"]).any(axis=1))[0]
     say(f"  {name}: undecided tokens {und.size}, tokens routed differently {diff.size}")
     assert np.isin(diff, und).all(), "a decided token was routed differently"
