@@ -18,10 +18,9 @@
 //   block    = EB expert blocks x KS K ranges; the KS partial sums are added
 //              in a fixed order through LDS, so results do not depend on
 //              scheduling
-//   operands = straight from global memory into registers (x rows: 16 bytes
-//              per lane; weights: the lane's expert column, 8 k values per
-//              step), one group of steps prefetched ahead; the EB waves of a
-//              block read the same x rows, which the caches serve
+//   operands = x rows staged in LDS by DMA, shared by the EB waves of a K
+//              range; weights straight from global memory into registers
+//              (the lane's expert column, 8 k per step), split there
 //
 // fp32 activations: the vector ALUs (a block owns BT tokens x BE experts;
 // four waves split each 128-wide slice of d; blocked accumulation keeps the
@@ -174,29 +173,53 @@ __device__ __forceinline__ void split3(const float* v, u32x4& hi, u32x4& mid, u3
   }
 }
 
-template <int MI, int G, int EB, int KS>
-__global__ __launch_bounds__(64 * EB * KS) void gate_mfma_kernel(
+// The token rows are staged once per block in LDS, shared by the EB waves
+// of one K range.  Stages of 64 k; a 3-slot ring filled by DMA
+// (global_load_lds_dwordx4, rows bank-swizzled) two stages ahead; the
+// lane's weight column (8 k per MFMA step) prefetched two stages ahead in
+// registers and split there.
+typedef __attribute__((address_space(3))) void g_lds_void_t;
+typedef __attribute__((address_space(1))) const void g_gbl_void_t;
+
+template <int N>
+__device__ __forceinline__ void g_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ int g_swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
+
+template <int MI, int EB, int KS>
+__global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bias,
     float* __restrict__ logits, int64_t B, int d, int E) {
-  extern __shared__ float red[];  // [EB][KS-1][MI*16][64]
+  extern __shared__ __attribute__((aligned(16))) char gsm[];
+  constexpr int SLOT = 32 * MI * 128;  // one stage (64 k) of the block's rows
+  constexpr int NSL = 3;
+  constexpr int ND = 4 * MI / EB;      // DMA instructions per wave per stage
+  static_assert(ND >= 1 && ND * EB == 4 * MI, "rows split evenly over the expert waves");
+  constexpr int LOADS = 32 + ND;       // vector-memory loads per wave per stage
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int eb = w % EB, kq = w / EB;
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t t0 = (int64_t)blockIdx.x * (32 * MI);
   const int e0 = (blockIdx.y * EB + eb) * 32;
-  const int kspan = (d + 16 * KS - 1) / (16 * KS) * 16;
+  const int kspan = (d + 64 * KS - 1) / (64 * KS) * 64;
   const int kb = kq * kspan;
   const int ke = kb + kspan < d ? kb + kspan : d;
-  const int nsteps = ke > kb ? (ke - kb + 15) / 16 : 0;
+  const int nst = kspan / 64;  // the same for every wave (barriers)
 
-  // rows / column past the edge read a valid neighbour; their results are
-  // never stored
-  const uint16_t* xr[MI];
+  // DMA: instruction q covers rows 8 (eb + EB q) .. +7; lane -> row + lane / 8,
+  // LDS chunk lane % 8 holding K chunk (lane % 8) ^ key(row)
+  const uint16_t* xrow[ND];
+  int dcol[ND], dofs[ND];
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int64_t t = t0 + 32 * i + l32;
-    xr[i] = x + (t < B ? t : B - 1) * d + 8 * h;
+  for (int q = 0; q < ND; ++q) {
+    const int row = 8 * (eb + EB * q) + (lane >> 3);
+    const int64_t t = t0 + row < B ? t0 + row : B - 1;  // past B: any valid row, never stored
+    xrow[q] = x + t * d;
+    dcol[q] = 8 * ((lane & 7) ^ ((row >> 1) & 7));
+    dofs[q] = kq * SLOT + 8 * (eb + EB * q) * 128;
   }
   const float* wc = Wg + (e0 + l32 < E ? e0 + l32 : E - 1);
 
@@ -205,55 +228,64 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_mfma_kernel(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  float wv[NSL][4][8];
 
-  u32x4 xa[2][G][MI];
-  float wv[2][G][8];
-  // step s covers k = kb + 16 s .. +15; this lane's half is k + 8 h .. +7,
-  // which lies wholly inside or outside [kb, ke) (d is a multiple of 8)
-#define GATE_LOAD(BUF, S0)                                                        \
-  _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) {                              \
-    const int k_ = kb + 16 * ((S0) + g_) + 8 * h;                                  \
-    const bool ok_ = k_ < ke;                                                      \
-    /* outside: the row's first chunk (xr already points 8 h into the row) */     \
-    const int kc_ = ok_ ? k_ - 8 * h : -8 * h;                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_)                              \
-      xa[BUF][g_][i_] = *(const u32x4*)(xr[i_] + kc_);                             \
-    const float* wp_ = wc + (int64_t)(ok_ ? k_ : 0) * E;                           \
-    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) {                             \
-      const float v_ = wp_[(int64_t)j_ * E];                                       \
-      wv[BUF][g_][j_] = ok_ ? v_ : 0.f;                                            \
-    }                                                                              \
+  // stage s (clamped to the last one): weights, then rows.  K chunks past
+  // the end of the row read the row's last chunk; their weights are zero.
+#define GL_ISSUE(S, B_)                                                              \
+  {                                                                                  \
+    const int sc_ = (S) < nst ? (S) : nst - 1;                                       \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                               \
+      const int k_ = kb + 64 * sc_ + 16 * j_ + 8 * h;                                \
+      const bool ok_ = k_ < ke;                                                      \
+      const float* wp_ = wc + (int64_t)(ok_ ? k_ : 0) * E;                           \
+      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                             \
+        const float v_ = wp_[(int64_t)i_ * E];                                       \
+        wv[B_][j_][i_] = ok_ ? v_ : 0.f;                                             \
+      }                                                                              \
+    }                                                                                \
+    const int kx_ = kb + 64 * sc_;                                                   \
+    char* sl_ = gsm + ((S) % NSL) * KS * SLOT;                                       \
+    _Pragma("unroll") for (int q_ = 0; q_ < ND; ++q_) {                              \
+      const int kk_ = kx_ + dcol[q_];                                                \
+      __builtin_amdgcn_global_load_lds((g_gbl_void_t*)(xrow[q_] + (kk_ < d ? kk_ : d - 8)), \
+                                       (g_lds_void_t*)(sl_ + dofs[q_]), 16, 0, 0);   \
+    }                                                                                \
   }
-#define GATE_COMPUTE(BUF)                                                         \
-  _Pragma("unroll") for (int g_ = 0; g_ < G; ++g_) {                              \
-    u32x4 hi_, mid_, lo_;                                                          \
-    split3(wv[BUF][g_], hi_, mid_, lo_);                                           \
-    _Pragma("unroll") for (int i_ = 0; i_ < MI; ++i_) {                            \
-      const g_bf16x8 a_ = __builtin_bit_cast(g_bf16x8, xa[BUF][g_][i_]);           \
-      acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                          \
-          a_, __builtin_bit_cast(g_bf16x8, lo_), acc[i_], 0, 0, 0);                \
-      acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                          \
-          a_, __builtin_bit_cast(g_bf16x8, mid_), acc[i_], 0, 0, 0);               \
-      acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                          \
-          a_, __builtin_bit_cast(g_bf16x8, hi_), acc[i_], 0, 0, 0);                \
-    }                                                                              \
-  }
-
-  if (nsteps > 0) {
-    GATE_LOAD(0, 0)
-    for (int s0 = 0; s0 < nsteps; s0 += 2 * G) {
-      GATE_LOAD(1, s0 + G)
-      GATE_COMPUTE(0)
-      if (s0 + 2 * G < nsteps) {
-        GATE_LOAD(0, s0 + 2 * G)
+  GL_ISSUE(0, 0)
+  GL_ISSUE(1, 1)
+  for (int s0 = 0; s0 < nst; s0 += NSL) {
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      const int s = s0 + u;
+      if (s < nst) {
+        g_wait_vmcnt<LOADS>();
+        __builtin_amdgcn_s_barrier();
+        GL_ISSUE(s + 2, (u + 2) % NSL)
+        const char* sa = gsm + (s % NSL) * KS * SLOT + kq * SLOT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4 hi, mid, lo;
+          split3(wv[u][j], hi, mid, lo);
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const g_bf16x8 a = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, lo), acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, mid), acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, hi), acc[i], 0, 0, 0);
+          }
+        }
       }
-      GATE_COMPUTE(1)
     }
   }
-#undef GATE_LOAD
-#undef GATE_COMPUTE
+#undef GL_ISSUE
+  g_wait_vmcnt<0>();
+  __syncthreads();
 
-  // acc[i][r] is token t0 + 32 i + 8 (r / 4) + 4 h + r % 4, expert e0 + l32
+  // acc[i][r] is token t0 + 32 i + 8 (r / 4) + 4 h + r % 4, expert e0 + l32;
+  // the K-range partials are added in a fixed order through LDS (the ring's
+  // space, now free)
+  float* red = reinterpret_cast<float*>(gsm);
   if (KS > 1) {
     if (kq > 0) {
       float* dst = red + ((eb * (KS - 1) + kq - 1) * MI * 16) * 64 + lane;
@@ -288,12 +320,12 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_mfma_kernel(
 template <int MI, int EB, int KS>
 hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const float* bias, float* logits,
                               int64_t B, int d, int E, hipStream_t s) {
-  constexpr int G = MI == 4 ? 2 : 4;
   const int neb = (E + 31) / 32;
   dim3 grid((unsigned)((B + 32 * MI - 1) / (32 * MI)), (unsigned)((neb + EB - 1) / EB));
   const size_t lds = (size_t)EB * (KS - 1) * MI * 16 * 64 * sizeof(float);
-  hipLaunchKernelGGL((gate_mfma_kernel<MI, G, EB, KS>), grid, dim3(64 * EB * KS), lds, s, x, Wg,
-                     bias, logits, B, d, E);
+  const size_t ring = (size_t)3 * KS * 32 * MI * 128;
+  hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS>), grid, dim3(64 * EB * KS),
+                     lds > ring ? lds : ring, s, x, Wg, bias, logits, B, d, E);
   return hipGetLastError();
 }
 
@@ -301,8 +333,8 @@ template <int EB, int KS>
 hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const float* bias,
                                float* logits, int64_t B, int d, int E, hipStream_t s) {
   if (mi == 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, bias, logits, B, d, E, s);
-  if (mi == 2) return launch_gate_mfma_t<2, EB, KS>(x, Wg, bias, logits, B, d, E, s);
-  return launch_gate_mfma_t<1, EB, KS>(x, Wg, bias, logits, B, d, E, s);
+  if (mi == 2 || EB >= 8) return launch_gate_mfma_t<2, EB, KS>(x, Wg, bias, logits, B, d, E, s);
+  return launch_gate_mfma_t<EB >= 8 ? 2 : 1, EB, KS>(x, Wg, bias, logits, B, d, E, s);
 }
 
 // Block shape: up to 8 waves; EB expert blocks (up to 256 experts share the
@@ -317,7 +349,9 @@ hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const float* bia
   while (ks > 1 && d / ks < 64) ks /= 2;
   const int64_t gy = (neb + eb - 1) / eb;
   int mi = ks >= 8 ? 1 : ks >= 4 ? 2 : 4;  // keeps the K-split partials in registers
-  while (mi > 1 && ((B + 32 * mi - 1) / (32 * mi)) * gy < 128) mi /= 2;
+  const int mi_min = eb >= 8 ? 2 : 1;        // 4 MI row groups of 8 shared by EB waves
+  if (mi < mi_min) mi = mi_min;
+  while (mi > mi_min && ((B + 32 * mi - 1) / (32 * mi)) * gy < 128) mi /= 2;
   switch (eb * 16 + ks) {
     case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, bias, logits, B, d, E, s);
     case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, bias, logits, B, d, E, s);
