@@ -27,7 +27,8 @@ unsigned grid_for(int64_t work, int threads) {
 
 // One wavefront per token row, one lane per 16-byte chunk: block (4 tokens)
 // x (64 chunks), grid (ceil(B / 4), ceil(d / 512)).  The token index is
-// wavefront-uniform, so dest and the weights come through scalar loads.
+// wavefront-uniform, so dest and the weights come through scalar loads; the
+// expert rows are read once, non-temporally.
 template <bool XBF16, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t* __restrict__ ret, const int32_t* __restrict__ dest,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int r = dest[t * k + j];
     if (r >= 0 && r < kmax) {
       const float wj = w[t * k + j];
-      const u32x4 v = *(const u32x4*)(ret + (int64_t)r * d + c * 8);
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(ret + (int64_t)r * d + c * 8));
       float f[8];
       unpack8(v, f);
 #pragma unroll

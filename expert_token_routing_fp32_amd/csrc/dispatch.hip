@@ -186,8 +186,9 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
 
 // One wavefront per token row, one lane per 16-byte chunk (block: 4 tokens x
 // 64 chunks): the row is read once and written to each of its kept packed
-// rows; the token index is wavefront-uniform, so dest comes through scalar
-// loads.
+// rows (non-temporal stores: each packed row is written once and read back
+// by the expert GEMM long after any cache could hold it); the token index is
+// wavefront-uniform, so dest comes through scalar loads.
 template <bool XBF16>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
                                                    const int32_t* __restrict__ dest, int64_t B,
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
   }
   for (int j = 0; j < k; ++j) {
     const int r = dest[t * k + j];
-    if (r >= 0) *(u32x4*)(packed + (int64_t)r * d + c * 8) = v;
+    if (r >= 0) __builtin_nontemporal_store(v, (u32x4*)(packed + (int64_t)r * d + c * 8));
   }
 }
 
