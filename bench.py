@@ -92,20 +92,6 @@ def measured_traffic(workload: str):
     return rec["expert_ffn_bytes"] if h.hexdigest()[:16] == rec["src_sha256_16"] else None
 
 
-def time_calls(fn, n, torch):
-    """Average device time of fn() over n back-to-back calls (HIP events on
-    the current stream, which is the stream the library launches on)."""
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn()
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(n):
-        fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / n * 1e-3
-
-
 def cpu_baseline(w, inp, budget_s: float) -> dict:
     import oracle
     try:
@@ -175,18 +161,21 @@ def main():
     y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
-    # one pair of HIP events per timed step, recorded by the library on its
-    # stream around the expert-FFN launches inside moe_forward
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        b.record()
+    # HIP events recorded by the library on its stream at the stage
+    # boundaries inside moe_forward (before the gate, after each of gate,
+    # route, dispatch, expert FFN, combine).  The timed steps record only the
+    # two around the expert FFN (each record costs a few microseconds); a
+    # second run of as many steps records all six for the breakdown.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    ffn_only = [[None, None, None, r[3], r[4], None] for r in evs]
 
     def step(ev=None):
         if flush is not None:
             flush.fill_(1)
-        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, ffn_events=ev)
+        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -195,34 +184,25 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(ffn_only[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / args.steps
-    t_ffn_live = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e-3
-    log(f"[bench] {sec_per_step * 1e3:.3f} ms/step, expert FFN {t_ffn_live * 1e6:.1f} us/step")
+    t_ffn_live = sum(r[3].elapsed_time(r[4]) for r in evs) / len(evs) * 1e-3
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_s = {name: sum(r[j].elapsed_time(r[j + 1]) for r in evs) / len(evs) * 1e-3
+               for j, name in enumerate(moe.STAGES)}
+    t_gate, t_route, t_disp, t_comb = (stage_s[k] for k in ("gate", "route", "dispatch", "combine"))
+    log(f"[bench] {sec_per_step * 1e3:.3f} ms/step; " +
+        ", ".join(f"{k} {v * 1e6:.1f} us" for k, v in stage_s.items()))
 
-    # per-step breakdown, each API call timed on its own with HIP events
     _, o = moe.forward(p, x, Wg, bias, wp, outputs=True)
     torch.cuda.synchronize()
     keep = o["keep"].cpu().numpy().astype(bool)
     eo = o["expert_offset"].cpu().numpy()
     alg = algorithmic(w, keep, eo)
-    n = max(5, min(args.steps, 50))
-    logits = o["logits"]
-    idx, wt = o["topk_idx"], o["topk_w"]
-    disp = moe.dispatch(p, x, idx)
-    packed, eo_d, dest = disp["packed"], disp["expert_offset"], disp["dest"]
-    ws_d = torch.empty(max(moe.workspace_bytes(p, "dispatch"), 1), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(max(moe.workspace_bytes(p, "ffn"), 1), dtype=torch.uint8, device=dev)
-    t_gate = time_calls(lambda: moe.gate(p, x, Wg, bias, logits=logits), n, torch)
-    t_route = time_calls(lambda: moe.route(p, logits, idx, wt), n, torch)
-    t_disp = time_calls(lambda: moe.dispatch(p, x, idx, ws=ws_d), n, torch)
-    t_ffn = time_calls(lambda: moe.expert_ffn(p, packed, eo_d, wp, ret=packed, ws=ws_f),
-                       n, torch)
-    t_comb = time_calls(lambda: moe.combine(p, packed, dest, wt, y=y), n, torch)
-    log(f"[bench] gate {t_gate*1e6:.1f} us, route {t_route*1e6:.1f} us, dispatch "
-        f"{t_disp*1e6:.1f} us, ffn {t_ffn*1e6:.1f} us, combine {t_comb*1e6:.1f} us")
 
     ffn_gbs = alg["ffn_bytes"] / t_ffn_live / 1e9
     ffn_tflops = alg["ffn_flop"] / t_ffn_live / 1e12
@@ -245,12 +225,17 @@ def main():
     rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]
     rpc_t = t_route + t_disp + t_comb
     breakdown = {
+        "timing": "moe_forward stage events over a second run of the same number of steps",
+        "expert_ffn_us_breakdown_run": round(stage_s["expert_ffn"] * 1e6, 2),
         "gate_us": round(t_gate * 1e6, 2),
-        "gate_alu_frac": round(alg["gate_flop"] / t_gate / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+        # bf16 activations: three bf16 MFMA products per fp32 multiply-add
+        # (exact split of the fp32 weights); fp32 activations: vector ALUs
+        "gate_frac": round(alg["gate_flop"] * 3 / t_gate / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        if bf16 else round(alg["gate_flop"] / t_gate / 1e12 / VALU_FP32_PEAK_TFLOPS, 4),
+        "gate_peak": "bf16 MFMA x3" if bf16 else "fp32 VALU",
         "route_us": round(t_route * 1e6, 2),
         "dispatch_us": round(t_disp * 1e6, 2),
         "expert_ffn_us": round(t_ffn_live * 1e6, 2),
-        "expert_ffn_alone_us": round(t_ffn * 1e6, 2),
         "combine_us": round(t_comb * 1e6, 2),
         "expert_gemm_tflops": round(ffn_tflops, 1),
         "expert_gemm_mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

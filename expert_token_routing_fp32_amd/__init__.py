@@ -233,13 +233,17 @@ _OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_lo
                "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")
 
 
+STAGES = ("gate", "route", "dispatch", "expert_ffn", "combine")
+
+
 def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None,
-            ffn_events=None):
+            stage_events=None):
     """The whole layer on the current stream (``wpacked`` from pack_weights).
     With ``outputs`` the intermediate tensors are allocated and returned too
     (``packed`` then holds the expert outputs of the local rows, in place).
-    ``ffn_events``: optional pair of timing-enabled ``torch.cuda.Event`` that
-    the library records around the expert FFN."""
+    ``stage_events``: optional six timing-enabled ``torch.cuda.Event`` (or
+    None); the library records them at the boundaries of the STAGES (before
+    the first, after each)."""
     _check(p)
     B, d, E, k = p.B, p.d, p.E, p.k
     dev = x.device
@@ -267,13 +271,17 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
                  rank_offset=torch.empty(p.n_ranks + 1, **i32), pack_src=torch.empty(km, **i32),
                  packed=torch.empty((km, d), dtype=torch.int16, device=dev))
         outp = L.ForwardOut(**{n: o[n].data_ptr() for n in _OUT_FIELDS})
-    if ffn_events is not None:
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
         if outp is None:
             outp = L.ForwardOut()
-        for ev, name in zip(ffn_events, ("ffn_begin", "ffn_end")):
+        for i, ev in enumerate(stage_events):
+            if ev is None:
+                continue
             if ev.cuda_event == 0:  # torch creates the HIP event on first record
                 ev.record()
-            setattr(outp, name, ev.cuda_event)
+            outp.events[i] = ev.cuda_event
     n = workspace_bytes(p, "forward")
     if ws is None:
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)

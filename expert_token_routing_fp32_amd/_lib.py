@@ -36,12 +36,12 @@ class Problem(ctypes.Structure):
 
 
 class ForwardOut(ctypes.Structure):
-    """moe_forward_out_t: device pointers or NULL, then two hipEvent_t
-    handles (or NULL) recorded around the expert FFN."""
+    """moe_forward_out_t: device pointers or NULL, then six hipEvent_t
+    handles (or NULL) recorded at the stage boundaries."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
-        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed",
-        "ffn_begin", "ffn_end")]
+        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")] + [
+        ("events", ctypes.c_void_p * 6)]
 
 
 class MoEError(RuntimeError):

@@ -305,22 +305,29 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
   carve_forward(p, out, ws, &b);
   const bool xb = p->x_dtype == MOE_BF16;
   const int C = capacity_of(p);
-  hipError_t e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, stream);
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (e == hipSuccess && out && out->events[i]) e = hipEventRecord(out->events[i], stream);
+  };
+  mark(0);
+  if (e == hipSuccess) e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, stream);
+  mark(1);
   if (e == hipSuccess)
     e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
+  mark(2);
   if (e == hipSuccess)
     e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->n_ranks, b.pos, b.keep, b.dest, b.load,
                            b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
-  const bool timed = out && out->ffn_begin && out->ffn_end;
-  if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_begin, stream);
+  mark(3);
   if (e == hipSuccess && p->B > 0)
     e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                 rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
-  if (e == hipSuccess && timed) e = hipEventRecord(out->ffn_end, stream);
+  mark(4);
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
                              p->k, p->d, kmax_of(p), stream);
+  mark(5);
   return hip_status(e);
 }
 

@@ -243,12 +243,14 @@ typedef struct {
   int32_t* pack_src;      /* [Kmax]   */
   moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
                              outputs overwrite the local rows in place) */
-  /* Optional timing: when both are non-NULL they are recorded on the call's
-   * stream right before and right after the expert-FFN launches, so a caller
-   * can time that stage inside a running sequence of forwards.  The caller
-   * owns the events (created with timing enabled). */
-  hipEvent_t ffn_begin;
-  hipEvent_t ffn_end;
+  /* Optional timing: each non-NULL events[i] is recorded on the call's
+   * stream at a stage boundary -- 0 before the gate, 1 after the gate, 2
+   * after the route, 3 after the dispatch (slots and pack), 4 after the
+   * expert FFN, 5 after the combine -- so a caller can time stages inside a
+   * running sequence of forwards (each record costs a few microseconds of
+   * stream time).  The caller owns the events (created with timing
+   * enabled). */
+  hipEvent_t events[6];
 } moe_forward_out_t;
 
 /* The whole layer, enqueued on one stream with no host synchronisation:
