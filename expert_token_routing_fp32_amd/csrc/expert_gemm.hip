@@ -148,6 +148,10 @@ struct Ring {
   static constexpr int LOADS = NS + 8;  // vector-memory loads per thread per stage
 };
 static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
+// LDS past the ring: the tile scheduler's scan arrays (4 (1029 + 1025) bytes),
+// then the epilogue's staging area, 32 rows x 64 bf16 columns per wavefront
+constexpr int kStageOff = kP * Ring<8>::A_BYTES + 8448;
+static_assert(kStageOff + (kThreads / 64) * 32 * 128 <= kLdsBytes, "staging area exceeds LDS");
 static_assert((kP - 2) * Ring<8>::LOADS < 64, "vmcnt range");
 
 // Weight fragment load.  Streaming launches (each weight byte used by one
@@ -312,9 +316,13 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
         // Epilogue of tile `tile`.  acc[c][i][r] is row 8 (r / 4) +
         // 4 lg + r % 4 of row block i, column l32 of the wavefront's weight
         // block c.  Rows r and r + 1 (r even) are adjacent: lanes 2j and
-        // 2j + 1 swap one value so that the even lane writes columns
-        // (2j, 2j+1) of row r and the odd lane the same columns of row r + 1,
-        // 4 bytes each.
+        // 2j + 1 swap one value so that the even lane holds columns
+        // (2j, 2j+1) of row r and the odd lane the same columns of row r + 1.
+        // Each 32-row block is staged through LDS (4 KB per wavefront, in a
+        // part of LDS the ring does not use now) and leaves as 16-byte row
+        // segments, so every store writes whole 128-byte lines.  The staging
+        // area is private to the wavefront and lies past the ring, so no
+        // barrier guards it.
         const int nt = tile;
         const bool odd = lane & 1;
         // Opaque copy of the row length: without it the compiler hoists every
@@ -322,14 +330,17 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
         int nout = a.Nout;
         asm volatile("" : "+s"(nout));
         uint16_t* out = a.Out + o_row0 * nout;
+        // output columns of this wavefront: 64 (SwiGLU: 32 hidden units)
+        constexpr int WCOLS = MODE == MODE_SWIGLU ? 32 : 64;
+        constexpr int RB = WCOLS * 2;  // bytes per staged row
+        char* stg = smem + kStageOff + wave * 32 * RB;
+        const int col0 = MODE == MODE_SWIGLU ? nt * 128 + 32 * wave : nt * 256 + 64 * wave;
 #pragma unroll
-        for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
-          // SwiGLU: block 0 holds the W1 products and block 1 the W3 products
-          // of hidden units 32 wave + l32, in the same lanes
-          const int col = MODE == MODE_SWIGLU ? nt * 128 + 32 * wave + (l32 & ~1)
-                                              : nt * 256 + 64 * wave + 32 * c + (l32 & ~1);
+        for (int i = 0; i < NS; ++i) {
 #pragma unroll
-          for (int i = 0; i < NS; ++i) {
+          for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
+            // SwiGLU: block 0 holds the W1 products and block 1 the W3
+            // products of hidden units 32 wave + l32, in the same lanes
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
               float v0, v1;
@@ -345,16 +356,26 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
                 }
               }
               const float got = swap_adjacent(odd ? v0 : v1);
-              const float lo = odd ? got : v0;  // column col
-              const float hi = odd ? v1 : got;  // column col + 1
-              const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
-              if (row < rows && col < nout)
-                *(unsigned int*)(out + (row * nout + col)) = pack_bf16x2(lo, hi);
+              const float lo = odd ? got : v0;  // column (l32 & ~1)
+              const float hi = odd ? v1 : got;  // the next column
+              const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+              *(unsigned int*)(stg + rin * RB + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
               // one pair at a time: keeps the epilogue's temporaries from
               // piling up next to the live accumulators
               __builtin_amdgcn_sched_barrier(0);
             }
           }
+          // block i: 32 rows x WCOLS columns, 16-byte segments
+          constexpr int SPR = WCOLS / 8;  // segments per row
+#pragma unroll
+          for (int q = 0; q < 32 * SPR / 64; ++q) {
+            const int sgi = lane + 64 * q;
+            const int rin = sgi / SPR, sg = sgi % SPR;
+            const u32x4 v = *(const u32x4*)(stg + rin * RB + sg * 16);
+            const int row = 32 * i + rin, col = col0 + 8 * sg;
+            if (row < rows && col < nout) *(u32x4*)(out + (row * nout + col)) = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
     // the counter now also holds stores, which are not ordered with the
     // loads: wait for everything before the next tile's first stage
@@ -374,7 +395,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 // expert_offset (a scan of one value per expert in LDS), so experts with no
 // rows cost nothing and skewed routing does not idle workgroups.
 constexpr int kRingBytes = kP * Ring<8>::A_BYTES;
-static_assert(kRingBytes + 4 * (1029 + 1025) <= kLdsBytes, "LDS budget");
+static_assert(kRingBytes + 4 * (1029 + 1025) <= kStageOff, "LDS budget");
 
 template <int MODE, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
