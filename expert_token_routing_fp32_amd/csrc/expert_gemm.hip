@@ -45,7 +45,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kThreads = 256;
 constexpr int BM = 256;                   // rows per tile
@@ -103,9 +102,14 @@ __device__ __forceinline__ float silu_f(float z) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4; lds must be wavefront-uniform).
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+// (buffer_load_dwordx4 ... lds; lds must be wavefront-uniform), from byte
+// offset off of the buffer rs; offsets past the buffer's size read zeros.
+// The buffer form rather than global_load_lds: the compiler counts a pending
+// global_load_lds against the LDS-read counter as well, and then has to wait
+// for every outstanding LDS read (lgkmcnt(0)) before each MFMA step instead
+// of only the ones that step consumes.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t off, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, off, 0, 0, 0);
 }
 
 // One accumulator element, read out of the accumulation registers where it
@@ -150,6 +154,11 @@ struct Ring {
 static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
 // LDS past the ring: the tile scheduler's scan arrays (4 (1029 + 1025) bytes),
 // then the epilogue's staging area, 32 rows x 64 bf16 columns per wavefront
+// row pairs whose epilogue work is interleaved (1, 2, 4 or 8)
+#ifndef MOE_EPG
+#define MOE_EPG 4
+#endif
+constexpr int kEpg = MOE_EPG;
 constexpr int kStageOff = kP * Ring<8>::A_BYTES + 8448;
 static_assert(kStageOff + (kThreads / 64) * 32 * 128 <= kLdsBytes, "staging area exceeds LDS");
 static_assert((kP - 2) * Ring<8>::LOADS < 64, "vmcnt range");
@@ -202,6 +211,8 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   const int drow = 8 * wave + (lane >> 3);
   const int dcol = 8 * ((lane & 7) ^ swz_key(drow));  // K offset of the lane's chunk
   const char* abase = reinterpret_cast<const char*>(a.A + a_row0 * K);
+  // the row slice as one buffer: rows x K bf16
+  const rsrc_t ars = make_rsrc(abase, 2u * (uint32_t)rows * (uint32_t)K);
   uint32_t arow[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -233,7 +244,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
     const int kc_ = iss_k * BK + dcol;                                             \
     const uint32_t cb_ = 2u * (uint32_t)(kc_ < K ? kc_ : K - 8);                   \
     _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_)                              \
-      dma16(abase + (arow[i_] + cb_), st_ + 32 * i_ * kRowBytes);                  \
+      dma16(ars, arow[i_] + cb_, st_ + 32 * i_ * kRowBytes);                       \
     const char* wb_ = iss_w + wlane;                                               \
     _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) bw[SLOT][j_] = load_w<NT>(wb_ + 1024 * j_); \
     if (iss_left > 1) {                                                            \
@@ -297,7 +308,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           for (int q = 0; q < NL; ++q) {
             if (q * 4 * NS / NL == s_ * NS + i) {
               if (q < NS)
-                dma16(abase + (arow[q < NS ? q : 0] + icb_), ist_ + 32 * q * kRowBytes);
+                dma16(ars, arow[q < NS ? q : 0] + icb_, ist_ + 32 * q * kRowBytes);
               else
                 bw[(u + kP - 1) % kP][q - NS] = load_w<NT>(iwb_ + 1024 * (q - NS));
             }
@@ -341,27 +352,37 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
             // SwiGLU: block 0 holds the W1 products and block 1 the W3
             // products of hidden units 32 wave + l32, in the same lanes
+            // kEpg row pairs at a time: their dependency chains (read-out,
+            // activation with exp2 and reciprocal, conversion, lane swap)
+            // interleave, while the temporaries stay few enough not to
+            // crowd the live accumulators and prefetched weights
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              float v0, v1;
-              if (MODE == MODE_SWIGLU) {
-                v0 = silu_f(acc_read(acc[0][i][r])) * acc_read(acc[1][i][r]);
-                v1 = silu_f(acc_read(acc[0][i][r + 1])) * acc_read(acc[1][i][r + 1]);
-              } else {
-                v0 = acc_read(acc[c][i][r]);
-                v1 = acc_read(acc[c][i][r + 1]);
-                if (MODE == MODE_GELU) {
-                  v0 = gelu_erf(v0);
-                  v1 = gelu_erf(v1);
+            for (int r0 = 0; r0 < 16; r0 += 2 * kEpg) {
+              float v0[kEpg], v1[kEpg];
+#pragma unroll
+              for (int g = 0; g < kEpg; ++g) {
+                const int r = r0 + 2 * g;
+                if (MODE == MODE_SWIGLU) {
+                  v0[g] = silu_f(acc_read(acc[0][i][r])) * acc_read(acc[1][i][r]);
+                  v1[g] = silu_f(acc_read(acc[0][i][r + 1])) * acc_read(acc[1][i][r + 1]);
+                } else {
+                  v0[g] = acc_read(acc[c][i][r]);
+                  v1[g] = acc_read(acc[c][i][r + 1]);
+                  if (MODE == MODE_GELU) {
+                    v0[g] = gelu_erf(v0[g]);
+                    v1[g] = gelu_erf(v1[g]);
+                  }
                 }
               }
-              const float got = swap_adjacent(odd ? v0 : v1);
-              const float lo = odd ? got : v0;  // column (l32 & ~1)
-              const float hi = odd ? v1 : got;  // the next column
-              const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
-              *(unsigned int*)(stg + rin * RB + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
-              // one pair at a time: keeps the epilogue's temporaries from
-              // piling up next to the live accumulators
+#pragma unroll
+              for (int g = 0; g < kEpg; ++g) {
+                const int r = r0 + 2 * g;
+                const float got = swap_adjacent(odd ? v0[g] : v1[g]);
+                const float lo = odd ? got : v0[g];  // column (l32 & ~1)
+                const float hi = odd ? v1[g] : got;  // the next column
+                const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+                *(unsigned int*)(stg + rin * RB + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
           }

@@ -175,16 +175,22 @@ __device__ __forceinline__ void split3(const float* v, u32x4& hi, u32x4& mid, u3
 
 // The token rows are staged once per block in LDS, shared by the EB waves
 // of one K range.  Stages of 64 k; a 3-slot ring filled by DMA
-// (global_load_lds_dwordx4, rows bank-swizzled) two stages ahead; the
+// (buffer_load_dwordx4 ... lds, rows bank-swizzled) two stages ahead; the
 // lane's weight column (8 k per MFMA step) prefetched two stages ahead in
 // registers and split there.
 typedef __attribute__((address_space(3))) void g_lds_void_t;
-typedef __attribute__((address_space(1))) const void g_gbl_void_t;
 
 template <int N>
 __device__ __forceinline__ void g_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// 16 bytes per lane from byte offset off of the buffer [base, base + bytes)
+// into LDS at lds + 16 * lane (buffer_load_dwordx4 ... lds).  The descriptor
+// is built here, not in the kernel body: a kernel with a local of the
+// descriptor type gets no host-side launch stub.
+__device__ __forceinline__ void g_dma16(const void* base, uint32_t bytes, uint32_t off, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (g_lds_void_t*)lds, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ int g_swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
@@ -211,13 +217,17 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 
   // DMA: instruction q covers rows 8 (eb + EB q) .. +7; lane -> row + lane / 8,
   // LDS chunk lane % 8 holding K chunk (lane % 8) ^ key(row)
-  const uint16_t* xrow[ND];
+  // the block's rows as one buffer (byte offsets are 32-bit)
+  const int nrows = B - t0 < 32 * MI ? (int)(B - t0) : 32 * MI;
+  const uint16_t* xblk = x + t0 * d;
+  const uint32_t xbytes = 2u * (uint32_t)nrows * (uint32_t)d;
+  uint32_t xrow[ND];
   int dcol[ND], dofs[ND];
 #pragma unroll
   for (int q = 0; q < ND; ++q) {
     const int row = 8 * (eb + EB * q) + (lane >> 3);
-    const int64_t t = t0 + row < B ? t0 + row : B - 1;  // past B: any valid row, never stored
-    xrow[q] = x + t * d;
+    const int r = row < nrows ? row : nrows - 1;  // past B: any valid row, never stored
+    xrow[q] = 2u * (uint32_t)r * (uint32_t)d;
     dcol[q] = 8 * ((lane & 7) ^ ((row >> 1) & 7));
     dofs[q] = kq * SLOT + 8 * (eb + EB * q) * 128;
   }
@@ -248,8 +258,7 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     char* sl_ = gsm + ((S) % NSL) * KS * SLOT;                                       \
     _Pragma("unroll") for (int q_ = 0; q_ < ND; ++q_) {                              \
       const int kk_ = kx_ + dcol[q_];                                                \
-      __builtin_amdgcn_global_load_lds((g_gbl_void_t*)(xrow[q_] + (kk_ < d ? kk_ : d - 8)), \
-                                       (g_lds_void_t*)(sl_ + dofs[q_]), 16, 0, 0);   \
+      g_dma16(xblk, xbytes, xrow[q_] + 2u * (kk_ < d ? kk_ : d - 8), sl_ + dofs[q_]); \
     }                                                                                \
   }
   GL_ISSUE(0, 0)

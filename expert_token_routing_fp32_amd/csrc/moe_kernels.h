@@ -32,6 +32,22 @@ __device__ __forceinline__ unsigned int pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2_t));
 }
+// Raw buffer descriptor (stride 0) over bytes [base, base + bytes): loads
+// through it take a 32-bit byte offset and read zeros past the end.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// base and bytes must be wavefront-uniform; they are passed through
+// readfirstlane so that the descriptor lives in scalar registers (a
+// descriptor the compiler takes for divergent costs a loop per load).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  // word 3: 32-bit data format, the value the gfx9 family takes for raw
+  // (stride 0) buffers
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
 __device__ __forceinline__ void unpack8(u32x4 v, float* o) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
