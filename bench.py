@@ -47,7 +47,59 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times: the "
                          "kernel of known traffic that HBM byte counters are scaled by")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only time the matrix-core ceiling probe (libmoe_probe.so) with random "
+                         "and with near-constant bf16 operands")
     return ap.parse_args()
+
+
+def mfma_probe(torch) -> dict:
+    """What the matrix cores sustain with the expert GEMM's inner-loop mix and no
+    memory traffic, one workgroup per CU.  After about a second of untimed
+    launches (clocks settle), the two operand cases alternate, 5 launches per
+    round, 3 rounds each; reported per case: mean over the rounds and the
+    slowest and fastest round."""
+    import ctypes
+    here = os.path.dirname(os.path.abspath(__file__))
+    lib = ctypes.CDLL(os.path.join(here, "expert_token_routing_fp32_amd", "libmoe_probe.so"))
+    lib.moe_probe_mfma.restype = ctypes.c_int
+    lib.moe_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.moe_probe_mfma_flop.restype = ctypes.c_double
+    lib.moe_probe_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4000
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def call(rnd):
+        assert lib.moe_probe_mfma(ctypes.c_void_p(out.data_ptr()), grid, iters, rnd,
+                                  ctypes.c_void_p(stream.cuda_stream)) == 0
+
+    for i in range(200):
+        call(i & 1)
+    torch.cuda.synchronize()
+    cases = (("random_bf16", 1), ("constant_bf16", 0))
+    rounds = {name: [] for name, _ in cases}
+    for _ in range(3):
+        for name, rnd in cases:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                call(rnd)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rounds[name].append(e0.elapsed_time(e1) / 5 * 1e-3)
+    flop = lib.moe_probe_mfma_flop(grid, iters)
+    res = {}
+    for name, sec in rounds.items():
+        mean = sum(sec) / len(sec)
+        res[name] = {"us_per_launch": round(mean * 1e6, 1),
+                     "us_rounds": [round(x * 1e6, 1) for x in sec],
+                     "tflops": round(flop / mean / 1e12, 1),
+                     "frac_of_2500": round(flop / mean / 1e12 / 2500.0, 4)}
+    return {"mfma_probe": res, "grid": grid, "iters": iters, "tflop_per_launch": round(flop / 1e12, 3),
+            "warmup_launches": 200, "rounds": 3, "launches_per_round": 5}
 
 
 def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
@@ -129,6 +181,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
+        return
+
+    if args.mfma_probe:
+        print(json.dumps(mfma_probe(torch)))
         return
 
     import expert_token_routing_fp32_amd as moe

@@ -2,7 +2,8 @@
 
 ``python -m expert_token_routing_fp32_amd.build`` or ``build()``; every call
 recompiles.  Each .hip file is compiled on its own (in parallel) and the
-objects are linked into ``expert_token_routing_fp32_amd/libmoe.so``.
+objects are linked into ``expert_token_routing_fp32_amd/libmoe.so``; the
+measurement probe (``probe_mfma.hip``) goes into ``libmoe_probe.so``.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 
 SOURCES = ["moe_api.hip", "gate.hip", "route.hip", "dispatch.hip", "combine.hip",
            "expert_gemm.hip"]
@@ -44,19 +47,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -41,6 +41,22 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_header():
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert names == ["moe_probe_mfma", "moe_probe_mfma_flop"]
+    probe = ctypes.CDLL(os.path.join(ROOT, "expert_token_routing_fp32_amd", "libmoe_probe.so"))
+    for n in names:
+        assert hasattr(probe, n), n
+    probe.moe_probe_mfma_flop.restype = ctypes.c_double
+    probe.moe_probe_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert probe.moe_probe_mfma_flop(256, 10) == 256 * 4 * 10 * 64 * 32768.0
+    # invalid arguments are rejected on the host, before any launch
+    probe.moe_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    assert probe.moe_probe_mfma(None, 256, 10, 1, None) == 1
+
+
 def test_ctypes_layout_matches_c(L, tmp_path):
     gcc = shutil.which("gcc")
     if gcc is None:
