@@ -219,14 +219,19 @@ def main():
 
     # HIP events recorded by the library on its stream at the stage
     # boundaries inside moe_forward (before the gate, after each of gate,
-    # route, dispatch, expert FFN, combine).  The timed steps record only the
-    # two around the expert FFN (each record costs a few microseconds); a
-    # second run of as many steps records all six for the breakdown.
+    # route, dispatch, expert FFN, combine).  Each record costs a few
+    # microseconds of stream time, so the timed steps record only the two
+    # around the expert FFN, and only on every `stride`-th step (at least 10
+    # sampled steps); a second run of as many steps records all six on every
+    # step for the breakdown.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()
-    ffn_only = [[None, None, None, r[3], r[4], None] for r in evs]
+    stride = max(1, args.steps // 10)
+    sampled = list(range(0, args.steps, stride))
+    ffn_only = [[None, None, None, r[3], r[4], None] if i % stride == 0 else None
+                for i, r in enumerate(evs)]
 
     def step(ev=None):
         if flush is not None:
@@ -244,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / args.steps
-    t_ffn_live = sum(r[3].elapsed_time(r[4]) for r in evs) / len(evs) * 1e-3
+    t_ffn_live = sum(evs[i][3].elapsed_time(evs[i][4]) for i in sampled) / len(sampled) * 1e-3
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
@@ -276,7 +281,8 @@ def main():
     roof["algorithmic_flop"] = alg["ffn_flop"]
     roof["avg_launch_us"] = round(t_ffn_live * 1e6, 2)
     roof["timing"] = ("HIP events recorded by moe_forward around the expert FFN on its stream, "
-                      f"averaged over the {args.steps} timed steps")
+                      f"averaged over {len(sampled)} of the {args.steps} timed steps "
+                      f"({'all' if stride == 1 else f'every {stride}th'})")
 
     rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]
     rpc_t = t_route + t_disp + t_comb
