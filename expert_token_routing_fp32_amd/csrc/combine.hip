@@ -35,43 +35,61 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ w, const void* __restrict__ xres, void* __restrict__ y, int64_t B,
     int k, int d, int64_t kmax) {
   const int cpr = d / 8;
-  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.y * 64 + (threadIdx.x & 63);
-  if (t >= B || c >= cpr) return;
-  float acc[8];
+  const int ncb = (cpr + 63) / 64;
+  const int64_t nblk = (B + 3) / 4 * ncb;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t t = (blk / ncb) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = (int)(blk % ncb) * 64 + (threadIdx.x & 63);
+    if (t >= B || c >= cpr) continue;
+    float acc[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int r = dest[t * k + j];
-    if (r >= 0 && r < kmax) {
-      const float wj = w[t * k + j];
-      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(ret + (int64_t)r * d + c * 8));
-      float f[8];
-      unpack8(v, f);
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    // four choices at a time: their row loads are all in flight before the
+    // first is added; the additions stay in j order
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      u32x4 v[4];
+      float wj[4];
+      bool ok[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q;
+        const int r = j < k ? dest[t * k + j] : -1;
+        ok[q] = r >= 0 && r < kmax;
+        wj[q] = ok[q] ? w[t * k + j] : 0.f;
+        v[q] = ok[q] ? __builtin_nontemporal_load((const u32x4*)(ret + (int64_t)r * d + c * 8))
+                     : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (ok[q]) {
+          float f[8];
+          unpack8(v[q], f);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj[q], f[u], acc[u]);
+        }
+      }
     }
-  }
-  if (RES) {
-    float xr[8];
+    if (RES) {
+      float xr[8];
+      if (XBF16) {
+        unpack8(*(const u32x4*)((const uint16_t*)xres + t * d + c * 8), xr);
+      } else {
+        const float* xf = (const float*)xres + t * d + c * 8;
+        const f32x4 a = *(const f32x4*)xf;
+        const f32x4 b = *(const f32x4*)(xf + 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { xr[u] = a[u]; xr[u + 4] = b[u]; }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += xr[u];
+    }
     if (XBF16) {
-      unpack8(*(const u32x4*)((const uint16_t*)xres + t * d + c * 8), xr);
+      *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
     } else {
-      const float* xf = (const float*)xres + t * d + c * 8;
-      const f32x4 a = *(const f32x4*)xf;
-      const f32x4 b = *(const f32x4*)(xf + 4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { xr[u] = a[u]; xr[u + 4] = b[u]; }
+      float* yf = (float*)y + t * d + c * 8;
+      *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] += xr[u];
-  }
-  if (XBF16) {
-    *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
-  } else {
-    float* yf = (float*)y + t * d + c * 8;
-    *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -116,7 +134,9 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
                           int64_t kmax, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const dim3 g((unsigned)((B + 3) / 4), (unsigned)((d / 8 + 63) / 64));
+  // 1-D grid, chunk block fastest (as the pack)
+  const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
+  const dim3 g((unsigned)(nblk < (1 << 24) ? nblk : (1 << 24)));
   if (x_bf16) {
     if (x_res)
       hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,

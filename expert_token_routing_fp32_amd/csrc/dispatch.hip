@@ -188,28 +188,34 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
 // 64 chunks): the row is read once and written to each of its kept packed
 // rows (non-temporal stores: each packed row is written once and read back
 // by the expert GEMM long after any cache could hold it); the token index is
-// wavefront-uniform, so dest comes through scalar loads.
+// wavefront-uniform, so dest comes through scalar loads.  1-D grid with the
+// chunk block fastest: consecutive workgroups cover consecutive pieces of
+// the same rows, not the same piece of consecutive rows.
 template <bool XBF16>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
                                                    const int32_t* __restrict__ dest, int64_t B,
                                                    int k, int d, uint16_t* __restrict__ packed) {
   const int cpr = d / 8;
-  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = blockIdx.y * 64 + (threadIdx.x & 63);
-  if (t >= B || c >= cpr) return;
-  u32x4 v;
-  if (XBF16) {
-    v = *(const u32x4*)((const uint16_t*)x + t * d + c * 8);
-  } else {
-    const float* xf = (const float*)x + t * d + c * 8;
-    const f32x4 a = *(const f32x4*)xf;
-    const f32x4 b = *(const f32x4*)(xf + 4);
-    const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    v = pack8(f);
-  }
-  for (int j = 0; j < k; ++j) {
-    const int r = dest[t * k + j];
-    if (r >= 0) __builtin_nontemporal_store(v, (u32x4*)(packed + (int64_t)r * d + c * 8));
+  const int ncb = (cpr + 63) / 64;
+  const int64_t nblk = (B + 3) / 4 * ncb;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t t = (blk / ncb) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = (int)(blk % ncb) * 64 + (threadIdx.x & 63);
+    if (t >= B || c >= cpr) continue;
+    u32x4 v;
+    if (XBF16) {
+      v = *(const u32x4*)((const uint16_t*)x + t * d + c * 8);
+    } else {
+      const float* xf = (const float*)x + t * d + c * 8;
+      const f32x4 a = *(const f32x4*)xf;
+      const f32x4 b = *(const f32x4*)(xf + 4);
+      const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      v = pack8(f);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = dest[t * k + j];
+      if (r >= 0) __builtin_nontemporal_store(v, (u32x4*)(packed + (int64_t)r * d + c * 8));
+    }
   }
 }
 
@@ -266,7 +272,8 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
                        uint16_t* packed, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const dim3 g((unsigned)((B + 3) / 4), (unsigned)((d / 8 + 63) / 64));
+  const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
+  const dim3 g((unsigned)(nblk < (1 << 24) ? nblk : (1 << 24)));
   if (x_bf16)
     hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
   else
