@@ -124,11 +124,21 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
   }
 }
 
+// FUSED: `base` holds the per-tile counts of slot_hist_kernel (no scan
+// kernel ran), and every block derives what it needs from them itself: its
+// tile's per-expert bases (the counts of the tiles before it), the totals
+// n_e, min(n_e, C) and the expert offsets; block 0 also writes the scan's
+// outputs.  Used when the count table is small (n_tiles x E <= 16384,
+// E % 4 == 0): re-reading it in every block then costs less than the
+// separate single-workgroup scan launch.
+template <bool FUSED>
 __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C, int64_t BK,
-    int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset,
+    int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset_in,
     int32_t* __restrict__ pos, uint8_t* __restrict__ keep, int32_t* __restrict__ dest,
-    int32_t* __restrict__ pack_src) {
+    int32_t* __restrict__ pack_src, int n_tiles, int D, int32_t* __restrict__ expert_load,
+    int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset_out,
+    int32_t* __restrict__ rank_offset) {
   extern __shared__ int sm[];
   int* ebuf = sm;         // [tile] experts in claim order
   int* wb = sm + tile;    // [4][E] per-wavefront counts, then running bases
@@ -137,7 +147,88 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   const int64_t n = BK - q0 < tile ? BK - q0 : tile;
   for (int i = tid; i < tile; i += kSlotThreads) ebuf[i] = i < n ? load_expert(idx, q0 + i, B, k, E) : -1;
   for (int i = tid; i < 4 * E; i += kSlotThreads) wb[i] = 0;
+  // FUSED: sbase [E] bases of this tile, soff [E + 1] expert offsets of the
+  // kept rows, then scratch
+  int* sbase = wb + 4 * E;
+  int* soff = sbase + E;
+  if constexpr (FUSED) {
+    int* pb = soff + E + 1;          // [G][E] partial sums of the earlier tiles
+    int* pt = pb + kSlotThreads * 4;  // [G][E] partial totals
+    int* wsum = pt + kSlotThreads * 4;
+    // thread (g, c): experts 4c .. 4c + 3 (one 16-byte load per tile) over
+    // the g-th of G tile groups
+    const int E4 = E / 4;
+    const int G = kSlotThreads / E4 > 0 ? kSlotThreads / E4 : 1;
+    const int b = blockIdx.x;
+    for (int i = tid; i < G * E4; i += kSlotThreads) {
+      const int g = i / E4, c = i % E4;
+      const int tpg = (n_tiles + G - 1) / G;
+      const int t0 = g * tpg, t1 = t0 + tpg < n_tiles ? t0 + tpg : n_tiles;
+      int sb[4] = {0, 0, 0, 0}, st[4] = {0, 0, 0, 0};
+      for (int t = t0; t < t1; ++t) {
+        const int4 v = *reinterpret_cast<const int4*>(base + (int64_t)t * E + 4 * c);
+        const int vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          st[u] += vv[u];
+          if (t < b) sb[u] += vv[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pb[g * E + 4 * c + u] = sb[u];
+        pt[g * E + 4 * c + u] = st[u];
+      }
+    }
+    __syncthreads();
+    // thread tid: experts 4 tid .. 4 tid + 3 (E <= 1024): bases, totals,
+    // kept counts, then an exclusive scan of the kept counts over experts
+    int kept[4], run = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      kept[u] = 0;
+      if (e < E) {
+        int sb = 0, st = 0;
+        for (int g = 0; g < G; ++g) {
+          sb += pb[g * E + e];
+          st += pt[g * E + e];
+        }
+        sbase[e] = sb;
+        kept[u] = st < C ? st : C;
+        if (b == 0) {
+          if (expert_load) expert_load[e] = st;
+          expert_count[e] = kept[u];
+        }
+      }
+      run += kept[u];
+    }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int pre = incl - run;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      if (e < E) soff[e] = pre;
+      pre += kept[u];
+    }
+    if (tid == kSlotThreads - 1) soff[E] = pre;
+  }
   __syncthreads();
+  if constexpr (FUSED) {
+    if (blockIdx.x == 0) {
+      for (int i = tid; i <= E; i += kSlotThreads) expert_offset_out[i] = soff[i];
+      for (int r = tid; r <= D; r += kSlotThreads) rank_offset[r] = soff[r * (E / D)];
+    }
+  }
+  const int32_t* expert_offset = FUSED ? soff : expert_offset_in;
 
   const int S = tile / 4;  // contiguous share of each wavefront (multiple of 64)
   const unsigned long long lt = lanemask_lt(lane);
@@ -150,7 +241,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += kSlotThreads) {
-    int b = base[(int64_t)blockIdx.x * E + e];
+    int b = FUSED ? sbase[e] : base[(int64_t)blockIdx.x * E + e];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int cnt = wb[w * E + e];
@@ -219,13 +310,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
   }
 }
 
-unsigned grid_for(int64_t work, int threads) {
-  int64_t g = (work + threads - 1) / threads;
-  if (g > (1 << 20)) g = 1 << 20;
-  if (g < 1) g = 1;
-  return (unsigned)g;
-}
-
 }  // namespace
 
 // Claim-order tiles of 256 .. 2048 assignments: small enough that the
@@ -258,13 +342,25 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int 
     hipLaunchKernelGGL(slot_hist_kernel, dim3(p.n_tiles), dim3(kSlotThreads), E * sizeof(int), s,
                        idx, B, k, E, p.BK, p.tile, ws_hist);
   }
-  hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
-                     Epad, C, D, expert_load, expert_count, expert_offset, rank_offset);
+  // small count tables: the rank blocks scan them themselves (no scan launch)
+  const bool fused = p.n_tiles > 0 && E % 4 == 0 && (int64_t)p.n_tiles * E <= 16384 &&
+                     (reinterpret_cast<uintptr_t>(ws_hist) & 15u) == 0;
+  if (!fused)
+    hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
+                       Epad, C, D, expert_load, expert_count, expert_offset, rank_offset);
   if (p.n_tiles > 0) {
-    const size_t lds = (size_t)(p.tile + 4 * E) * sizeof(int);
-    hipLaunchKernelGGL(slot_rank_kernel, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx, B, k,
-                       E, nbits, C, p.BK, p.tile, ws_hist, expert_offset, pos, keep, dest,
-                       pack_src);
+    // ebuf, per-wavefront counts; fused: + bases, offsets, 2 x 1024 partials, 4 wave sums
+    const size_t lds = (size_t)(p.tile + 4 * E + (fused ? 2 * E + 1 + 2 * 4 * kSlotThreads + 4 : 0)) *
+                       sizeof(int);
+    if (fused)
+      hipLaunchKernelGGL(slot_rank_kernel<true>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx,
+                         B, k, E, nbits, C, p.BK, p.tile, ws_hist, nullptr, pos, keep, dest,
+                         pack_src, p.n_tiles, D, expert_load, expert_count, expert_offset,
+                         rank_offset);
+    else
+      hipLaunchKernelGGL(slot_rank_kernel<false>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s,
+                         idx, B, k, E, nbits, C, p.BK, p.tile, ws_hist, expert_offset, pos, keep,
+                         dest, pack_src, p.n_tiles, D, nullptr, nullptr, nullptr, nullptr);
   }
   return hipGetLastError();
 }
