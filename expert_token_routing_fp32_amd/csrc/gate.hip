@@ -349,11 +349,18 @@ hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const
 // Block shape: up to 8 waves; EB expert blocks (up to 256 experts share the
 // x rows), the rest of the 8 waves split K while each wave keeps >= 64 k;
 // token tiles (at most 8 / KS row blocks) shrink until there are >= 128
-// blocks.
+// blocks.  (Token tiles smaller than that would multiply the weight reads,
+// which bound these launches.)
 hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const float* bias, float* logits,
                             int64_t B, int d, int E, hipStream_t s) {
   const int neb = (E + 31) / 32;
-  const int eb = neb >= 8 ? 8 : neb >= 4 ? 4 : neb >= 2 ? 2 : 1;
+  int eb = neb >= 8 ? 8 : neb >= 4 ? 4 : neb >= 2 ? 2 : 1;
+  // Two or three expert blocks and too few token tiles to give every CU a
+  // workgroup (at 32 tokens per tile): one expert block per workgroup, so
+  // the x rows are read once per expert block but the grid doubles and each
+  // wavefront's K range halves (the launch is latency-bound, not bandwidth-
+  // bound, at these sizes).
+  if (eb == 2 && ((B + 31) / 32) * ((neb + 1) / 2) < 256) eb = 1;
   int ks = 8 / eb;
   while (ks > 1 && d / ks < 64) ks /= 2;
   const int64_t gy = (neb + eb - 1) / eb;
