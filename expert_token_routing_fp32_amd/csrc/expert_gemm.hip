@@ -464,17 +464,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int G = gridDim.x, b = blockIdx.x;
   const int loc0 = eos[0];
   if (XS) {
-    // Matrix-core-bound launches (hundreds of rows per expert): XCD x (the
-    // workgroups b with b % 8 == x; workgroups are dealt round-robin over
-    // the 8 XCDs) owns the x-th eighth of the tiles, ordered (expert,
-    // output tile, row slice), and deals them round-robin to its
-    // workgroups.  At any moment an XCD then works on a compact patch of
-    // one expert -- few row slices x few output tiles -- so the activation
-    // slices and weight tiles it streams are shared through its L2.
+    // Matrix-core-bound launches (hundreds of rows per expert): tiles are
+    // ordered (expert, output tile, row slice) and cut into chunks of nx
+    // consecutive tiles, one per workgroup of an XCD (the workgroups b with
+    // b % 8 == x sit on XCD x: workgroups are dealt round-robin over the 8
+    // XCDs); chunk c goes to XCD c % 8.  At any moment an XCD then works on
+    // a compact patch of one expert -- few row slices x few output tiles --
+    // so the activation slices and weight tiles it streams are shared
+    // through its L2, and every XCD gets a share of every expert (experts
+    // differ in rows, so whole experts per XCD would not balance).
     const int x = b % kXcd, j = b / kXcd;
-    const int nx = (G - x + kXcd - 1) / kXcd;  // workgroups on this XCD (G >= 8)
-    const int64_t xb = total * x / kXcd, xe = total * (x + 1) / kXcd;
-    for (int64_t t = xb + j; t < xe; t += nx) {
+    const int nx = G / kXcd;  // workgroups per XCD in the full rounds (G >= 8)
+    if (j >= nx) return;      // the G % 8 extra workgroups have no chunk slot
+    for (int64_t t = (int64_t)x * nx + j; t < total; t += (int64_t)kXcd * nx) {
       const int p = (int)(t / a.n_tiles_n);
       int lo = 0, hi = nl - 1;
       while (lo < hi) {
