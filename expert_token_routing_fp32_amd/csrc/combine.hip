@@ -136,7 +136,9 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
   if (B == 0) return hipSuccess;
   // 1-D grid, chunk block fastest (as the pack)
   const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
-  const dim3 g((unsigned)(nblk < (1 << 24) ? nblk : (1 << 24)));
+  // at most 2^20 workgroups (a grid dimension holds < 2^32 work-items); the
+  // kernel loops over the rest
+  const dim3 g((unsigned)(nblk < (1 << 20) ? nblk : (1 << 20)));
   if (x_bf16) {
     if (x_res)
       hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,

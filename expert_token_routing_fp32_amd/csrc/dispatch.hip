@@ -369,7 +369,9 @@ hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t 
                        uint16_t* packed, hipStream_t s) {
   if (B == 0) return hipSuccess;
   const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
-  const dim3 g((unsigned)(nblk < (1 << 24) ? nblk : (1 << 24)));
+  // at most 2^20 workgroups (a grid dimension holds < 2^32 work-items); the
+  // kernel loops over the rest
+  const dim3 g((unsigned)(nblk < (1 << 20) ? nblk : (1 << 20)));
   if (x_bf16)
     hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
   else

@@ -142,3 +142,28 @@ def test_random_shapes(B, d8, f8, E, data):
             x_dtype=xdt, seed=seed)
     say(f"[random] {w}")
     check_stages(w)
+
+
+def test_pack_combine_past_the_grid_cap():
+    """B = 262147 tokens of d = 8192: the pack and the combine then need more
+    than 2^20 workgroups of 4 rows x 512 columns, so the grid is capped and
+    the kernels loop over the rest.  With one expert, k = 1 and C = B nothing
+    is dropped, every packed row r is token r and its weight is 1, so the
+    packed rows and y must equal x bit for bit (a property at any size; the
+    oracle is not needed)."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    B, d = 262147, 8192
+    p = moe.make_problem(B=B, d=d, E=1, k=1, c=1.0, f=8, act="gelu", x_dtype="bf16")
+    assert moe.problem_capacity(p) == B
+    say(f"[grid cap] B={B} d={d}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(B, d, device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.zeros(B, 1, dtype=torch.int32, device="cuda")
+    o = moe.dispatch(p, x, idx)
+    assert int(o["expert_offset"][1]) == B
+    assert torch.equal(o["dest"].view(-1), torch.arange(B, dtype=torch.int32, device="cuda"))
+    assert torch.equal(o["packed"][:B], x.view(torch.int16))
+    w = torch.ones(B, 1, dtype=torch.float32, device="cuda")
+    y = moe.combine(p, o["packed"], o["dest"], w)
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))
