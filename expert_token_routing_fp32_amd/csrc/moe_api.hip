@@ -12,6 +12,9 @@ namespace {
 constexpr int32_t kMaxE = 1024;
 constexpr int32_t kMaxK = 16;
 constexpr int32_t kMaxDim = 1 << 16;
+// tokens: the router launch has up to 64 lanes per token in one grid
+// dimension, which holds fewer than 2^32 work-items
+constexpr int64_t kMaxB = (int64_t)1 << 25;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -143,7 +146,7 @@ moe_status_t moe_validate(const moe_problem_t* p) {
   if (p->add_residual != 0 && p->add_residual != 1) return MOE_ERR_INVALID;
   if (p->E > kMaxE || p->k > kMaxK || p->d > kMaxDim || p->f > kMaxDim)
     return MOE_ERR_UNSUPPORTED;
-  if (p->B > (int64_t)INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
+  if (p->B > kMaxB || p->B > (int64_t)INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
   if (p->C < 0 && moe_capacity(p->B, p->k, p->E, p->c) < 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

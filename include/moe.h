@@ -78,7 +78,7 @@ typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_FFN = 1, MOE_OP_FORWARD = 2 } moe_op_
  * ("Expert Parallelism and the All-to-All Bottleneck", section "The
  * All-to-All Communication Pattern"). */
 typedef struct {
-  int64_t B;          /* tokens (>= 0; 0 is an empty batch)                  */
+  int64_t B;          /* tokens, 0 .. 2^25 with B*k < 2^31 (0: empty batch)  */
   int32_t d;          /* hidden size, multiple of 8                          */
   int32_t E;          /* experts, 1..1024                                    */
   int32_t k;          /* experts per token, 1..min(E, 16)                    */

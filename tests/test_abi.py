@@ -107,7 +107,7 @@ def _prob(L, **kw):
     ({"e_begin": 3, "e_end": 2}, 1), ({"e_end": 9}, 1), ({"f": 4}, 1), ({"act": 7}, 1),
     ({"x_dtype": 5}, 1), ({"tau": 0.0}, 1), ({"add_residual": 2}, 1),
     ({"E": 2048, "e_end": 2048, "n_ranks": 1}, 2), ({"k": 17, "E": 32, "e_end": 32}, 2),
-    ({"B": 1 << 30, "k": 4}, 2),
+    ({"B": 1 << 30, "k": 4}, 2), ({"B": (1 << 25) + 1, "k": 1}, 2), ({"B": 1 << 25, "k": 1}, 0),
 ])
 def test_validate_codes(L, lib, change, code):
     p = _prob(L, **change)
