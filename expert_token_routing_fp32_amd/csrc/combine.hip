@@ -35,11 +35,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ w, const void* __restrict__ xres, void* __restrict__ y, int64_t B,
     int k, int d, int64_t kmax) {
   const int cpr = d / 8;
-  const int ncb = (cpr + 63) / 64;
-  const int64_t nblk = (B + 3) / 4 * ncb;
-  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int64_t t = (blk / ncb) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = (int)(blk % ncb) * 64 + (threadIdx.x & 63);
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t ntb = (B + 3) / 4;
+  for (int64_t tb = blockIdx.y; tb < ntb; tb += gridDim.y) {
+    const int64_t t = tb * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= B || c >= cpr) continue;
     float acc[8];
 #pragma unroll
@@ -134,11 +133,11 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
                           int64_t kmax, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  // 1-D grid, chunk block fastest (as the pack)
-  const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
-  // at most 2^20 workgroups (a grid dimension holds < 2^32 work-items); the
-  // kernel loops over the rest
-  const dim3 g((unsigned)(nblk < (1 << 20) ? nblk : (1 << 20)));
+  // x: 512-column piece of the rows (fastest in dispatch order, so
+  // consecutive workgroups cover consecutive pieces of the same rows);
+  // y: groups of 4 rows, at most 65535 (the kernel loops over the rest)
+  const int64_t ntb = (B + 3) / 4;
+  const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16) {
     if (x_res)
       hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,

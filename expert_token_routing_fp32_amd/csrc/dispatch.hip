@@ -279,19 +279,19 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
 // 64 chunks): the row is read once and written to each of its kept packed
 // rows (non-temporal stores: each packed row is written once and read back
 // by the expert GEMM long after any cache could hold it); the token index is
-// wavefront-uniform, so dest comes through scalar loads.  1-D grid with the
-// chunk block fastest: consecutive workgroups cover consecutive pieces of
-// the same rows, not the same piece of consecutive rows.
+// wavefront-uniform, so dest comes through scalar loads.  The column piece
+// is the grid's x (fastest in dispatch order): consecutive workgroups cover
+// consecutive pieces of the same rows, not the same piece of consecutive
+// rows.
 template <bool XBF16>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
                                                    const int32_t* __restrict__ dest, int64_t B,
                                                    int k, int d, uint16_t* __restrict__ packed) {
   const int cpr = d / 8;
-  const int ncb = (cpr + 63) / 64;
-  const int64_t nblk = (B + 3) / 4 * ncb;
-  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int64_t t = (blk / ncb) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = (int)(blk % ncb) * 64 + (threadIdx.x & 63);
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int64_t ntb = (B + 3) / 4;
+  for (int64_t tb = blockIdx.y; tb < ntb; tb += gridDim.y) {
+    const int64_t t = tb * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= B || c >= cpr) continue;
     u32x4 v;
     if (XBF16) {
@@ -368,10 +368,11 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
                        uint16_t* packed, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const int64_t nblk = (B + 3) / 4 * ((d / 8 + 63) / 64);
-  // at most 2^20 workgroups (a grid dimension holds < 2^32 work-items); the
-  // kernel loops over the rest
-  const dim3 g((unsigned)(nblk < (1 << 20) ? nblk : (1 << 20)));
+  // x: 512-column piece of the rows (fastest in dispatch order, so
+  // consecutive workgroups cover consecutive pieces of the same rows);
+  // y: groups of 4 rows, at most 65535 (the kernel loops over the rest)
+  const int64_t ntb = (B + 3) / 4;
+  const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16)
     hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
   else

@@ -146,8 +146,8 @@ def test_random_shapes(B, d8, f8, E, data):
 
 def test_pack_combine_past_the_grid_cap():
     """B = 262147 tokens of d = 8192: the pack and the combine then need more
-    than 2^20 workgroups of 4 rows x 512 columns, so the grid is capped and
-    the kernels loop over the rest.  With one expert, k = 1 and C = B nothing
+    than 65535 groups of 4 rows, the grid's y extent is capped and the
+    kernels loop over the rest.  With one expert, k = 1 and C = B nothing
     is dropped, every packed row r is token r and its weight is 1, so the
     packed rows and y must equal x bit for bit (a property at any size; the
     oracle is not needed)."""
