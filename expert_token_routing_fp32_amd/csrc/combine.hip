@@ -43,29 +43,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
     float acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    // four choices at a time: their row loads are all in flight before the
-    // first is added; the additions stay in j order
-    for (int j0 = 0; j0 < k; j0 += 4) {
-      u32x4 v[4];
-      float wj[4];
-      bool ok[4];
+    for (int j = 0; j < k; ++j) {
+      const int r = dest[t * k + j];
+      if (r >= 0 && r < kmax) {
+        const float wj = w[t * k + j];
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(ret + (int64_t)r * d + c * 8));
+        float f[8];
+        unpack8(v, f);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + q;
-        const int r = j < k ? dest[t * k + j] : -1;
-        ok[q] = r >= 0 && r < kmax;
-        wj[q] = ok[q] ? w[t * k + j] : 0.f;
-        v[q] = ok[q] ? __builtin_nontemporal_load((const u32x4*)(ret + (int64_t)r * d + c * 8))
-                     : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (ok[q]) {
-          float f[8];
-          unpack8(v[q], f);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj[q], f[u], acc[u]);
-        }
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
       }
     }
     if (RES) {
