@@ -173,11 +173,39 @@ __device__ __forceinline__ void split3(const float* v, u32x4& hi, u32x4& mid, u3
   }
 }
 
+// Router weights split once per call into the layout the gate's MFMAs read:
+// for expert block eb (32 experts), K step ks (16 k) and part p (0: lo,
+// 1: mid, 2: hi), 64 lanes x 16 bytes; lane l holds the 8 bf16 parts of
+// k = 16 ks + 8 (l / 32) .. +7 of expert 32 eb + l % 32 (zeros past d or E).
+// One thread per (eb, ks, lane).
+__global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict__ Wg, int d,
+                                                         int E, int neb, int nks,
+                                                         u32x4* __restrict__ out) {
+  const int64_t n = (int64_t)neb * nks * 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(i & 63);
+    const int64_t bk = i >> 6;  // eb * nks + ks
+    const int ks = (int)(bk % nks), eb = (int)(bk / nks);
+    const int e = 32 * eb + (lane & 31);
+    const int k0 = 16 * ks + 8 * (lane >> 5);
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (e < E && k0 + q < d) ? Wg[(int64_t)(k0 + q) * E + e] : 0.f;
+    u32x4 hi, mid, lo;
+    split3(v, hi, mid, lo);
+    out[(bk * 3 + 0) * 64 + lane] = lo;
+    out[(bk * 3 + 1) * 64 + lane] = mid;
+    out[(bk * 3 + 2) * 64 + lane] = hi;
+  }
+}
+
 // The token rows are staged once per block in LDS, shared by the EB waves
 // of one K range.  Stages of 64 k; a 3-slot ring filled by DMA
 // (buffer_load_dwordx4 ... lds, rows bank-swizzled) two stages ahead; the
 // lane's weight column (8 k per MFMA step) prefetched two stages ahead in
-// registers and split there.
+// registers and split there, or (PS) its three bf16 parts loaded as they
+// are from the split copy (gate_split_kernel): 3 16-byte loads per step
+// instead of 8 4-byte loads and the split.
 typedef __attribute__((address_space(3))) void g_lds_void_t;
 
 template <int N>
@@ -194,16 +222,16 @@ __device__ __forceinline__ void g_dma16(const void* base, uint32_t bytes, uint32
 }
 __device__ __forceinline__ int g_swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
-template <int MI, int EB, int KS>
+template <int MI, int EB, int KS, bool PS>
 __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ Wg, const float* __restrict__ bias,
-    float* __restrict__ logits, int64_t B, int d, int E) {
+    const uint16_t* __restrict__ x, const float* __restrict__ Wg, const u32x4* __restrict__ Wsp,
+    const float* __restrict__ bias, float* __restrict__ logits, int64_t B, int d, int E) {
   extern __shared__ __attribute__((aligned(16))) char gsm[];
   constexpr int SLOT = 32 * MI * 128;  // one stage (64 k) of the block's rows
   constexpr int NSL = 3;
   constexpr int ND = 4 * MI / EB;      // DMA instructions per wave per stage
   static_assert(ND >= 1 && ND * EB == 4 * MI, "rows split evenly over the expert waves");
-  constexpr int LOADS = 32 + ND;       // vector-memory loads per wave per stage
+  constexpr int LOADS = (PS ? 12 : 32) + ND;  // vector-memory loads per wave per stage
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int eb = w % EB, kq = w / EB;
@@ -238,20 +266,36 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-  float wv[NSL][4][8];
+  float wv[PS ? 1 : NSL][4][8];
+  u32x4 wq[PS ? NSL : 1][4][3];
+  // PS: this wavefront's expert block in the split copy, and its first K step
+  const int nks = (d + 15) / 16;
+  const u32x4* wsb = Wsp + ((int64_t)(blockIdx.y * EB + eb) * nks + kb / 16) * 3 * 64 + lane;
 
   // stage s (clamped to the last one): weights, then rows.  K chunks past
   // the end of the row read the row's last chunk; their weights are zero.
 #define GL_ISSUE(S, B_)                                                              \
   {                                                                                  \
     const int sc_ = (S) < nst ? (S) : nst - 1;                                       \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                               \
-      const int k_ = kb + 64 * sc_ + 16 * j_ + 8 * h;                                \
-      const bool ok_ = k_ < ke;                                                      \
-      const float* wp_ = wc + (int64_t)(ok_ ? k_ : 0) * E;                           \
-      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                             \
-        const float v_ = wp_[(int64_t)i_ * E];                                       \
-        wv[B_][j_][i_] = ok_ ? v_ : 0.f;                                             \
+    if constexpr (PS) {                                                              \
+      /* a K step past this wave's range reads the wave's first step (in the */      \
+      /* copy) and is then zeroed; the copy itself holds zeros past d        */      \
+      _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                             \
+        const bool ok_ = kb + 64 * sc_ + 16 * j_ < ke;                               \
+        const int64_t st_ = ok_ ? (int64_t)(4 * sc_ + j_) * 3 * 64 : 0;              \
+        _Pragma("unroll") for (int p_ = 0; p_ < 3; ++p_)                             \
+          wq[B_][j_][p_] = wsb[st_ + p_ * 64];                                       \
+        if (!ok_) wq[B_][j_][0] = wq[B_][j_][1] = wq[B_][j_][2] = u32x4{0u, 0u, 0u, 0u}; \
+      }                                                                              \
+    } else {                                                                         \
+      _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                             \
+        const int k_ = kb + 64 * sc_ + 16 * j_ + 8 * h;                              \
+        const bool ok_ = k_ < ke;                                                    \
+        const float* wp_ = wc + (int64_t)(ok_ ? k_ : 0) * E;                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                           \
+          const float v_ = wp_[(int64_t)i_ * E];                                     \
+          wv[B_][j_][i_] = ok_ ? v_ : 0.f;                                           \
+        }                                                                            \
       }                                                                              \
     }                                                                                \
     const int kx_ = kb + 64 * sc_;                                                   \
@@ -275,7 +319,13 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           u32x4 hi, mid, lo;
-          split3(wv[u][j], hi, mid, lo);
+          if constexpr (PS) {
+            lo = wq[u][j][0];
+            mid = wq[u][j][1];
+            hi = wq[u][j][2];
+          } else {
+            split3(wv[u][j], hi, mid, lo);
+          }
 #pragma unroll
           for (int i = 0; i < MI; ++i) {
             const g_bf16x8 a = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
@@ -327,23 +377,39 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 }
 
 template <int MI, int EB, int KS>
-hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const float* bias, float* logits,
-                              int64_t B, int d, int E, hipStream_t s) {
+hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* wsp,
+                              const float* bias, float* logits, int64_t B, int d, int E,
+                              hipStream_t s) {
   const int neb = (E + 31) / 32;
   dim3 grid((unsigned)((B + 32 * MI - 1) / (32 * MI)), (unsigned)((neb + EB - 1) / EB));
   const size_t lds = (size_t)EB * (KS - 1) * MI * 16 * 64 * sizeof(float);
   const size_t ring = (size_t)3 * KS * 32 * MI * 128;
-  hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS>), grid, dim3(64 * EB * KS),
-                     lds > ring ? lds : ring, s, x, Wg, bias, logits, B, d, E);
+  if (wsp)
+    hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS, true>), grid, dim3(64 * EB * KS),
+                       lds > ring ? lds : ring, s, x, Wg, wsp, bias, logits, B, d, E);
+  else
+    hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS, false>), grid, dim3(64 * EB * KS),
+                       lds > ring ? lds : ring, s, x, Wg, wsp, bias, logits, B, d, E);
   return hipGetLastError();
 }
 
+// MI as the launcher picks it: at most 8 / KS row blocks of 32 (the K-split
+// partials stay in registers), at least 2 when EB = 8 (4 MI row groups of 8
+// shared by the EB waves); only those shapes are compiled.
 template <int EB, int KS>
-hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const float* bias,
-                               float* logits, int64_t B, int d, int E, hipStream_t s) {
-  if (mi == 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, bias, logits, B, d, E, s);
-  if (mi == 2 || EB >= 8) return launch_gate_mfma_t<2, EB, KS>(x, Wg, bias, logits, B, d, E, s);
-  return launch_gate_mfma_t<EB >= 8 ? 2 : 1, EB, KS>(x, Wg, bias, logits, B, d, E, s);
+hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const u32x4* wsp,
+                               const float* bias, float* logits, int64_t B, int d, int E,
+                               hipStream_t s) {
+  constexpr int MI_MAX = KS >= 8 ? 1 : KS >= 4 ? 2 : 4;
+  constexpr int MI_MIN = EB >= 8 ? 2 : 1;
+  if constexpr (MI_MAX >= 4)
+    if (mi >= 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+  if constexpr (MI_MAX >= 2)
+    if (mi >= 2 || MI_MIN >= 2)
+      return launch_gate_mfma_t<2, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+  if constexpr (MI_MIN <= 1)
+    return launch_gate_mfma_t<1, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+  return hipErrorInvalidValue;
 }
 
 // Block shape: up to 8 waves; EB expert blocks (up to 256 experts share the
@@ -351,34 +417,51 @@ hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const
 // token tiles (at most 8 / KS row blocks) shrink until there are >= 128
 // blocks.  (Token tiles smaller than that would multiply the weight reads,
 // which bound these launches.)
-hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const float* bias, float* logits,
-                            int64_t B, int d, int E, hipStream_t s) {
+struct GatePlan {
+  int eb, ks, mi;
+  int64_t blocks;
+};
+// Workgroup shape (bf16 x); split: the router weights come as the split copy.
+GatePlan gate_plan(int64_t B, int d, int E, bool split) {
   const int neb = (E + 31) / 32;
-  int eb = neb >= 8 ? 8 : neb >= 4 ? 4 : neb >= 2 ? 2 : 1;
+  GatePlan g;
+  g.eb = neb >= 8 ? 8 : neb >= 4 ? 4 : neb >= 2 ? 2 : 1;
   // Two or three expert blocks and too few token tiles to give every CU a
   // workgroup (at 32 tokens per tile): one expert block per workgroup, so
   // the x rows are read once per expert block but the grid doubles and each
   // wavefront's K range halves (the launch is latency-bound, not bandwidth-
   // bound, at these sizes).
-  if (eb == 2 && ((B + 31) / 32) * ((neb + 1) / 2) < 256) eb = 1;
-  int ks = 8 / eb;
-  while (ks > 1 && d / ks < 64) ks /= 2;
-  const int64_t gy = (neb + eb - 1) / eb;
-  int mi = ks >= 8 ? 1 : ks >= 4 ? 2 : 4;  // keeps the K-split partials in registers
-  const int mi_min = eb >= 8 ? 2 : 1;        // 4 MI row groups of 8 shared by EB waves
-  if (mi < mi_min) mi = mi_min;
-  while (mi > mi_min && ((B + 32 * mi - 1) / (32 * mi)) * gy < 128) mi /= 2;
+  if (g.eb == 2 && ((B + 31) / 32) * ((neb + 1) / 2) < 256) g.eb = 1;
+  g.ks = 8 / g.eb;
+  while (g.ks > 1 && d / g.ks < 64) g.ks /= 2;
+  const int64_t gy = (neb + g.eb - 1) / g.eb;
+  g.mi = g.ks >= 8 ? 1 : g.ks >= 4 ? 2 : 4;  // keeps the K-split partials in registers
+  const int mi_min = g.eb >= 8 ? 2 : 1;      // 4 MI row groups of 8 shared by EB waves
+  if (g.mi < mi_min) g.mi = mi_min;
+  // with the split copy the per-workgroup weight work is cheap enough to
+  // give every CU a workgroup
+  const int64_t want = split ? 256 : 128;
+  while (g.mi > mi_min && ((B + 32 * g.mi - 1) / (32 * g.mi)) * gy < want) g.mi /= 2;
+  g.blocks = ((B + 32 * g.mi - 1) / (32 * g.mi)) * gy;
+  return g;
+}
+
+hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const u32x4* wsp,
+                            const float* bias, float* logits, int64_t B, int d, int E,
+                            hipStream_t s) {
+  const GatePlan g = gate_plan(B, d, E, wsp != nullptr);
+  const int eb = g.eb, ks = g.ks, mi = g.mi;
   switch (eb * 16 + ks) {
-    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, bias, logits, B, d, E, s);
-    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, bias, logits, B, d, E, s);
-    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, bias, logits, B, d, E, s);
+    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
   }
 }
 
@@ -398,10 +481,36 @@ hipError_t launch_gate_t(const void* x, bool x_bf16, const float* Wg, const floa
 
 }  // namespace
 
+size_t gate_split_bytes(int d, int E) {
+  return (size_t)((E + 31) / 32) * ((d + 15) / 16) * 3 * 1024;
+}
+
+bool gate_use_split(bool x_bf16, int64_t B, int d, int E) {
+  // The split copy costs a launch and 1.5x the weight bytes per workgroup;
+  // it pays where it lets the grid fill the CUs (smaller token tiles, the
+  // weight split no longer repeated by every workgroup): 16384 tokens x 128
+  // experts, 128 -> 256 workgroups, gate 55 -> 45 us.  Where the grid is
+  // full already it does not (EP share: 374 -> 398 us), nor for small
+  // problems (4096 tokens x 64 experts).
+  if (!x_bf16 || B * E < ((int64_t)1 << 20)) return false;
+  return gate_plan(B, d, E, false).blocks < 256 && gate_plan(B, d, E, true).blocks > 128;
+}
+
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
-                       float* logits, int64_t B, int d, int E, hipStream_t s) {
+                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (x_bf16) return launch_gate_mfma(static_cast<const uint16_t*>(x), Wg, bias, logits, B, d, E, s);
+  if (x_bf16 && wsplit) {
+    const int neb = (E + 31) / 32, nks = (d + 15) / 16;
+    const int64_t n = (int64_t)neb * nks * 64;
+    const int64_t g = (n + 255) / 256;
+    hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0, s,
+                       Wg, d, E, neb, nks, static_cast<u32x4*>(wsplit));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (x_bf16)
+    return launch_gate_mfma(static_cast<const uint16_t*>(x), Wg, static_cast<const u32x4*>(wsplit),
+                            bias, logits, B, d, E, s);
   if (E > 32) return launch_gate_t<64, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s);
   if (E > 16) return launch_gate_t<32, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s);
   if (E > 8) return launch_gate_t<16, 2>(x, x_bf16, Wg, bias, logits, B, d, E, s);

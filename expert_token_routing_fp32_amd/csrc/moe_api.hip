@@ -81,6 +81,7 @@ struct FwdBufs {
   uint16_t* packed;
   int32_t* hist;
   uint16_t* H;
+  void* wsplit;  // split copy of the router weights, or null
 };
 
 size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* ws, FwdBufs* b) {
@@ -106,6 +107,9 @@ size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* w
   t.packed = c.take(reinterpret_cast<uint16_t*>(o->packed), km * p->d * 2);
   t.hist = c.take<int32_t>(nullptr, dispatch_ws(p));
   t.H = c.take<uint16_t>(nullptr, ffn_ws(p));
+  t.wsplit = moek::gate_use_split(p->x_dtype == MOE_BF16, p->B, p->d, p->E)
+                 ? c.take<char>(nullptr, moek::gate_split_bytes(p->d, p->E))
+                 : nullptr;
   if (b) *b = t;
   return c.off;
 }
@@ -188,7 +192,7 @@ moe_status_t moe_gate(const moe_problem_t* p, const void* x, const float* Wg, co
   if (p->B > 0 && (!a16(x) || !a4(Wg) || !a4(logits) || (bias && !a4(bias))))
     return MOE_ERR_INVALID;
   return hip_status(moek::launch_gate(x, p->x_dtype == MOE_BF16, Wg, bias, logits, p->B, p->d,
-                                      p->E, stream));
+                                      p->E, nullptr, stream));
 }
 
 moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* topk_idx,
@@ -313,7 +317,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
     if (e == hipSuccess && out && out->events[i]) e = hipEventRecord(out->events[i], stream);
   };
   mark(0);
-  if (e == hipSuccess) e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, stream);
+  if (e == hipSuccess)
+    e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, b.wsplit, stream);
   mark(1);
   if (e == hipSuccess)
     e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);

@@ -121,8 +121,13 @@ __device__ __forceinline__ void route_token(const float* row, int E, int k, floa
 }
 
 // ---- launchers --------------------------------------------------------------
+// wsplit: device scratch of gate_split_bytes(d, E) for the split copy of the
+// router weights (bf16 x only), or null to split inside the gate kernel;
+// both give bit-identical logits
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
-                       float* logits, int64_t B, int d, int E, hipStream_t s);
+                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s);
+size_t gate_split_bytes(int d, int E);
+bool gate_use_split(bool x_bf16, int64_t B, int d, int E);
 
 hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,
                         int32_t* idx, float* w, hipStream_t s);

@@ -99,3 +99,28 @@ def test_forward_is_deterministic():
     y2 = moe.forward(p, *args)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,d,E", [(8192, 320, 128), (16384, 328, 100), (16384, 512, 256)])
+def test_forward_gate_matches_moe_gate(B, d, E):
+    """Where that fills the CUs (here: every shape) the forward splits the
+    router weights once into a bf16 copy before the gate; moe_gate splits
+    them inside its kernel.
+    The MFMAs see the same three parts in the same order, so the logits must
+    be bit-identical.  Shapes: a K range whose last 64-k stage lies past d
+    (d = 320 over two K ranges), d not a multiple of 16 with E not a multiple
+    of 32, and 256 experts in one workgroup."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    p = moe.make_problem(B=B, d=d, E=E, k=2, c=1.25, f=16, act="gelu", x_dtype="bf16")
+    g = torch.Generator(device="cuda").manual_seed(B + d + E)
+    x = torch.randn(B, d, device="cuda", generator=g).to(torch.bfloat16)
+    Wg = torch.randn(d, E, device="cuda", generator=g) * d ** -0.5
+    W1 = (torch.randn(E, 16, d, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
+    W2 = (torch.randn(E, d, 16, device="cuda", generator=g) * 0.25).to(torch.bfloat16)
+    wp = moe.pack_weights(p, W1, None, W2)
+    say(f"[gate split] B={B} d={d} E={E}")
+    lg = moe.gate(p, x, Wg)
+    _, o = moe.forward(p, x, Wg, None, wp, outputs=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o["logits"].view(torch.int32), lg.view(torch.int32))
