@@ -9,7 +9,8 @@
 // probabilities keeps the choice exact.  The weights are the raw
 // probabilities of the chosen experts.
 //
-// A token's E logits are spread over L = min(64, pow2 >= E) lanes, V per lane.
+// A token's E logits are spread over L lanes, V per lane: L = pow2 >= E up to
+// 16 experts, 16 lanes up to 512 experts, 64 beyond.
 // Max, sum and each of the k arg-max rounds are butterfly reductions inside
 // the L-lane segment of the 64-wide wavefront.
 #include "moe_kernels.h"
@@ -50,11 +51,15 @@ hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,
   if (E <= 4) return go<4, 1>(logits, B, E, k, tau, idx, w, s);
   if (E <= 8) return go<8, 1>(logits, B, E, k, tau, idx, w, s);
   if (E <= 16) return go<16, 1>(logits, B, E, k, tau, idx, w, s);
-  if (E <= 32) return go<32, 1>(logits, B, E, k, tau, idx, w, s);
-  if (E <= 64) return go<64, 1>(logits, B, E, k, tau, idx, w, s);
-  if (E <= 128) return go<64, 2>(logits, B, E, k, tau, idx, w, s);
-  if (E <= 256) return go<64, 4>(logits, B, E, k, tau, idx, w, s);
-  if (E <= 512) return go<64, 8>(logits, B, E, k, tau, idx, w, s);
+  // 16 lanes per token from 32 experts up: each lane walks E / 16 logits
+  // itself and the butterflies take 4 steps instead of 6 (measured: 128
+  // experts 9.9 -> 5.9 us, 256 experts x 32768 tokens 56 -> 35 us); past
+  // 512 experts the per-lane walk costs more than it saves
+  if (E <= 32) return go<16, 2>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 64) return go<16, 4>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 128) return go<16, 8>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 256) return go<16, 16>(logits, B, E, k, tau, idx, w, s);
+  if (E <= 512) return go<16, 32>(logits, B, E, k, tau, idx, w, s);
   return go<64, 16>(logits, B, E, k, tau, idx, w, s);
 }
 
