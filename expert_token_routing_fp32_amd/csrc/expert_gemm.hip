@@ -30,13 +30,17 @@
 //    HBM-bound workloads); only the 32-row blocks that hold rows run MFMAs
 //    (the block count is a template parameter chosen per tile).
 //  * Weights: global -> registers, kP - 1 stages ahead (8 KB per wavefront
-//    per stage).  Activations: global -> LDS by DMA (global_load_lds_dwordx4,
-//    no register staging) into a kP-slot ring, bank-swizzled; every
-//    activation fragment read from LDS feeds two MFMAs.
-//  * Persistent: each workgroup runs a contiguous range of tiles; tiles of
-//    one expert that share its activation rows sit on the same XCD
-//    (workgroups are dealt round-robin over the 8 XCDs), so the activation
-//    rows are read from HBM about once per expert and then from L2.
+//    per stage).  Activations: global -> LDS by buffer loads that write LDS
+//    directly (no register staging) into a kP-slot ring, bank-swizzled;
+//    every activation fragment read from LDS feeds two MFMAs.
+//  * Persistent, two schedules.  Weight-streaming launches: each workgroup
+//    runs a contiguous range of tiles; tiles of one expert that share its
+//    activation rows sit on the same XCD (workgroups are dealt round-robin
+//    over the 8 XCDs), so the activation rows are read from HBM about once
+//    per expert and then from L2.  Matrix-core-bound launches (hundreds of
+//    rows per expert): chunks of consecutive tiles are dealt round-robin
+//    over the XCDs, so each XCD works on a compact patch of one expert at a
+//    time and every XCD gets a share of every expert.
 #include "moe_kernels.h"
 
 namespace moek {
