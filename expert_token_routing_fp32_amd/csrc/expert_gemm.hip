@@ -193,6 +193,14 @@ __device__ __forceinline__ u32x4 load_w(const char* p) {
 // (kP - 2) stages' loads are outstanding means stage g has landed.  After an
 // epilogue the counter also holds stores, which are not ordered with the
 // loads: then wait for everything.
+//
+// Matrix-core-bound launches (NT false) wait one stage further, for stage
+// g + 1 as well, at the start of stage g; each wavefront can then read stage
+// g + 1's first activation fragments right after its last MFMAs of stage g,
+// so the next stage's MFMAs start as soon as the barrier is passed instead
+// of after an LDS round trip.  Their loads hit L2 often enough that two
+// stages of lead suffice; the weight-streaming launches keep the deeper
+// lead, which the loaded HBM latency needs.
 template <int MODE, int NS, bool NT>
 __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ smem, int el,
                                          int n0, int ntile, int64_t a_row0, int64_t o_row0,
@@ -260,6 +268,16 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 
 #pragma unroll
   for (int p = 0; p < kP - 1; ++p) ISSUE(p);
+  // activation fragments of the current MFMA step, one per row block
+  constexpr bool PRE = !NT;
+  u32x4 fa[NS];
+  if (PRE) {
+    // stages 0 and 1 have landed; the first fragments of stage 0
+    wait_vmcnt<(kP - 3) * R::LOADS>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) fa[i] = *(const u32x4*)(smem + swz(32 * i + l32, lg));
+  }
 
   for (int tile = n0; tile < n0 + ntile; ++tile) {
   // accumulators live only inside one tile (carried across the tile loop
@@ -274,9 +292,9 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   for (int kk = 0; kk < nk; kk += kP) {
 #pragma unroll
     for (int u = 0; u < kP; ++u) {
-      wait_vmcnt<(kP - 2) * R::LOADS>();
-      // every wavefront's part of slot u has landed and slot u - 1 is
-      // consumed (its LDS reads fed MFMAs).  A bare s_barrier: a
+      wait_vmcnt<(PRE ? kP - 3 : kP - 2) * R::LOADS>();
+      // every wavefront's part of slot u (PRE: and of slot u + 1) has landed
+      // and slot u - 1 is consumed (its LDS reads fed MFMAs).  A bare s_barrier: a
       // __syncthreads() fence would wait for the whole prefetch.
       __builtin_amdgcn_s_barrier();
       asm volatile("" : "+s"(lds_w));
@@ -293,10 +311,13 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       __builtin_amdgcn_sched_barrier(0);
       const char* sa = smem + u * R::A_BYTES;
       // Activation fragments are re-read for step s + 1 right after the two
-      // MFMAs of step s that consume them.
-      u32x4 fa[NS];
+      // MFMAs of step s that consume them (PRE: after step 3, the next
+      // stage's step 0 from slot u + 1).
+      const char* sn = smem + ((u + 1) % kP) * R::A_BYTES;
+      if (!PRE) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, lg));
+        for (int i = 0; i < NS; ++i) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, lg));
+      }
 #pragma unroll
       for (int s_ = 0; s_ < 4; ++s_) {
         const bf16x8 b0 = as_bf16x8(bw[u][2 * s_]);
@@ -308,6 +329,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc[0][i], 0, 0, 0);
           acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc[1][i], 0, 0, 0);
           if (s_ < 3) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, chn));
+          else if (PRE) fa[i] = *(const u32x4*)(sn + swz(32 * i + l32, lg));
 #pragma unroll
           for (int q = 0; q < NL; ++q) {
             if (q * 4 * NS / NL == s_ * NS + i) {
@@ -422,6 +444,20 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 constexpr int kRingBytes = kP * Ring<8>::A_BYTES;
 static_assert(kRingBytes + 4 * (1029 + 1025) <= kStageOff, "LDS budget");
 
+// Row slice m_t of an expert's M rows, cut into nsl = ceil(M / BM) slices:
+// the ceil(M / 32) row blocks are dealt as evenly as possible (the first
+// nb % nsl slices take one block more), so that no slice is a thin tail
+// whose stages would cost as much as a full slice's.  The slice count is the
+// same as with full slices and a trailing remainder; nsl = ceil(nb / 8), so
+// no slice exceeds 8 blocks.
+__device__ __forceinline__ void row_slice(int M, int nsl, int m_t, int& m0, int& rows) {
+  const int nb = (M + 31) >> 5;
+  const int q = nb / nsl, r = nb - q * nsl;
+  m0 = 32 * (m_t * q + (m_t < r ? m_t : r));
+  const int span = 32 * (q + (m_t < r ? 1 : 0));
+  rows = M - m0 < span ? M - m0 : span;
+}
+
 template <int MODE, bool XS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -492,11 +528,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t loc_t = t - (int64_t)pre[el] * a.n_tiles_n;
       const int n_t = (int)(loc_t / mel), m_t = (int)(loc_t - (int64_t)n_t * mel);
       const int rb = eos[el];
-      const int M = eos[el + 1] - rb;
-      const int m0 = m_t * BM;
+      int m0, rows;
+      row_slice(eos[el + 1] - rb, mel, m_t, m0, rows);
       const int64_t a_row0 = (int64_t)(rb - (a.a_local ? loc0 : 0) + m0);
       const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc0 : 0) + m0);
-      const int rows = M - m0 < BM ? M - m0 : BM;
       switch ((rows + 31) >> 5) {
         case 1: gemm_run<MODE, 1, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
         case 2: gemm_run<MODE, 2, false>(a, smem, el, n_t, 1, a_row0, o_row0, rows); break;
@@ -537,11 +572,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int run = (int)(t1 - t < a.n_tiles_n - n_t ? t1 - t : a.n_tiles_n - n_t);
     t += run;
     const int rb = eos[el];
-    const int M = eos[el + 1] - rb;
-    const int m0 = m_t * BM;
+    int m0, rows;
+    row_slice(eos[el + 1] - rb, pre[el + 1] - pre[el], m_t, m0, rows);
     const int64_t a_row0 = (int64_t)(rb - (a.a_local ? loc : 0) + m0);
     const int64_t o_row0 = (int64_t)(rb - (a.o_local ? loc : 0) + m0);
-    const int rows = M - m0 < BM ? M - m0 : BM;
     switch ((rows + 31) >> 5) {
       case 1: gemm_run<MODE, 1, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;
       case 2: gemm_run<MODE, 2, true>(a, smem, el, n_t, run, a_row0, o_row0, rows); break;

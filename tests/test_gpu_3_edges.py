@@ -118,6 +118,10 @@ CASES = {
     "rows_1024_gelu": dict(w=dict(B=2048, d=72, E=4, e_end=4, k=2, c=1.0, f=520)),
     "rows_1024_swiglu": dict(w=dict(B=2048, d=136, E=4, e_end=4, k=2, c=1.25, f=264,
                                     act="swiglu")),
+    # ~1050 rows per expert: five row slices of 6-7 blocks each, not four full
+    # slices and a thin remainder
+    "rows_1050_five_slices": dict(w=dict(B=2100, d=72, E=4, e_end=4, k=2, c=1.25, f=264,
+                                         act="swiglu")),
 }
 
 
