@@ -158,7 +158,10 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     // thread (g, c): experts 4c .. 4c + 3 (one 16-byte load per tile) over
     // the g-th of G tile groups
     const int E4 = E / 4;
-    const int G = kSlotThreads / E4 > 0 ? kSlotThreads / E4 : 1;
+    // at most 16 groups: the second phase sums G partials per expert in one
+    // thread, so a large G (few experts) would make it the long pole
+    int G = kSlotThreads / E4 > 0 ? kSlotThreads / E4 : 1;
+    if (G > 16) G = 16;
     const int b = blockIdx.x;
     for (int i = tid; i < G * E4; i += kSlotThreads) {
       const int g = i / E4, c = i % E4;
