@@ -420,7 +420,18 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
             const int rin = sgi / SPR, sg = sgi % SPR;
             const u32x4 v = *(const u32x4*)(stg + rin * RB + sg * 16);
             const int row = 32 * i + rin, col = col0 + 8 * sg;
-            if (row < rows && col < nout) *(u32x4*)(out + (row * nout + col)) = v;
+            // The hidden activations H (GELU / SwiGLU launch) are read back
+            // only by the second GEMM, after the whole launch: stored
+            // non-temporally they do not displace the weights and
+            // activation rows the launch is streaming (uniform routing:
+            // FFN 261 -> 240 us).  The FFN output stays a normal store: the
+            // combine reads it next, often still from cache.
+            if (row < rows && col < nout) {
+              if (MODE == MODE_PLAIN)
+                *(u32x4*)(out + (row * nout + col)) = v;
+              else
+                __builtin_nontemporal_store(v, (u32x4*)(out + (row * nout + col)));
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
