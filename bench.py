@@ -219,11 +219,13 @@ def main():
 
     # HIP events recorded by the library on its stream at the stage
     # boundaries inside moe_forward (before the gate, after each of gate,
-    # route, dispatch, expert FFN, combine).  Each record costs a few
-    # microseconds of stream time, so the timed steps record only the two
-    # around the expert FFN, and only on every `stride`-th step (at least 10
-    # sampled steps); a second run of as many steps records all six on every
-    # step for the breakdown.
+    # route, dispatch, expert FFN, combine).  The two around the expert FFN
+    # are taken from its first and last kernel dispatches (start and end
+    # timestamps of the launches, no marker packets); each of the other
+    # records costs a few microseconds of stream time.  The timed steps
+    # record only the FFN pair, and only on every `stride`-th step (at least
+    # 10 sampled steps); a second run of as many steps records all six on
+    # every step for the breakdown.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
@@ -280,7 +282,8 @@ def main():
     roof["algorithmic_bytes"] = alg["ffn_bytes"]
     roof["algorithmic_flop"] = alg["ffn_flop"]
     roof["avg_launch_us"] = round(t_ffn_live * 1e6, 2)
-    roof["timing"] = ("HIP events recorded by moe_forward around the expert FFN on its stream, "
+    roof["timing"] = ("HIP events taken from the start of the expert FFN's first kernel and "
+                      "the end of its last (hipExtLaunchKernelGGL on the forward's stream), "
                       f"averaged over {len(sampled)} of the {args.steps} timed steps "
                       f"({'all' if stride == 1 else f'every {stride}th'})")
 

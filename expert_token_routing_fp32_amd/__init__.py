@@ -243,7 +243,8 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
     (``packed`` then holds the expert outputs of the local rows, in place).
     ``stage_events``: optional six timing-enabled ``torch.cuda.Event`` (or
     None); the library records them at the boundaries of the STAGES (before
-    the first, after each)."""
+    the first, after each); events 3 and 4 come from the expert FFN's first
+    and last kernel dispatches themselves (their start and end timestamps)."""
     _check(p)
     B, d, E, k = p.B, p.d, p.E, p.k
     dev = x.device

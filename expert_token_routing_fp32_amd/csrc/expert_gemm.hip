@@ -41,6 +41,8 @@
 //    rows per expert): chunks of consecutive tiles are dealt round-robin
 //    over the XCDs, so each XCD works on a compact patch of one expert at a
 //    time and every XCD gets a share of every expert.
+#include <hip/hip_ext.h>
+
 #include "moe_kernels.h"
 
 namespace moek {
@@ -614,17 +616,27 @@ int device_cus() {
 }
 
 // One workgroup per CU (the LDS ring takes most of the 160 KB), no more
-// workgroups than there could be tiles.
+// workgroups than there could be tiles.  e0 / e1 (optional) take the
+// dispatch's start / end timestamps; with no tiles they are recorded as
+// markers.
 template <int MODE>
-hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s) {
+hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s,
+                       hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const int64_t bound = (int64_t)g.n_local * m_tiles * g.n_tiles_n;
-  if (bound <= 0) return hipSuccess;
+  if (bound <= 0) {
+    hipError_t e = hipSuccess;
+    if (e0) e = hipEventRecord(e0, s);
+    if (e == hipSuccess && e1) e = hipEventRecord(e1, s);
+    return e;
+  }
   const int cus = device_cus();
   const int grid = bound < cus ? (int)bound : cus;
   if (mfma_bound && grid >= kXcd)
-    hipLaunchKernelGGL((grouped_gemm_kernel<MODE, true>), dim3(grid), dim3(kThreads), 0, s, g);
+    hipExtLaunchKernelGGL((grouped_gemm_kernel<MODE, true>), dim3(grid), dim3(kThreads), 0, s, e0,
+                          e1, 0, g);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<MODE, false>), dim3(grid), dim3(kThreads), 0, s, g);
+    hipExtLaunchKernelGGL((grouped_gemm_kernel<MODE, false>), dim3(grid), dim3(kThreads), 0, s, e0,
+                          e1, 0, g);
   return hipGetLastError();
 }
 
@@ -708,8 +720,14 @@ hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uin
 
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
-                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s) {
-  if (n_local <= 0 || rows_max <= 0) return hipSuccess;
+                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
+                             hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (n_local <= 0 || rows_max <= 0) {
+    hipError_t e = hipSuccess;
+    if (ev_start) e = hipEventRecord(ev_start, s);
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
+    return e;
+  }
   // a 256-column tile does 2 * rows FLOP per weight byte; above ~384 rows per
   // expert the matrix cores, not the weight stream, set the pace (the
   // MI355X bf16 / HBM ridge is ~310 FLOP per byte)
@@ -729,8 +747,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g1.n_tiles_n = geo1.n_tiles;
   g1.nk = geo1.nk;
   g1.n_local = n_local;
-  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s)
-                          : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s);
+  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s, ev_start)
+                          : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s, ev_start);
   if (err != hipSuccess) return err;
 
   GemmArgs g2{};
@@ -746,7 +764,7 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g2.n_tiles_n = geo2.n_tiles;
   g2.nk = geo2.nk;
   g2.n_local = n_local;
-  return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s);
+  return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s, nullptr, ev_stop);
 }
 
 }  // namespace moek

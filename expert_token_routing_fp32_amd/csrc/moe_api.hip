@@ -327,11 +327,18 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
     e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->n_ranks, b.pos, b.keep, b.dest, b.load,
                            b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
-  mark(3);
-  if (e == hipSuccess && p->B > 0)
-    e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
-                                rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed, stream);
-  mark(4);
+  // events 3 and 4: the expert FFN's first dispatch start and last dispatch
+  // end (no marker packets between the launches)
+  if (p->B > 0) {
+    if (e == hipSuccess)
+      e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
+                                  rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
+                                  stream, out ? out->events[3] : nullptr,
+                                  out ? out->events[4] : nullptr);
+  } else {
+    mark(3);
+    mark(4);
+  }
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
                              p->k, p->d, kmax_of(p), stream);

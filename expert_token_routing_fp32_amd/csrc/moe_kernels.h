@@ -167,8 +167,12 @@ size_t packed_weights_bytes(int n_local, int d, int f, bool swiglu);
 hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
                                int n_local, int d, int f, bool swiglu, void* wp, hipStream_t s);
 // rows_hint: expected rows per local expert (chooses the tile schedule only)
+// ev_start / ev_stop (optional): taken by the first launch's start and the
+// last launch's end (HIP fills them from the dispatches' own timestamps, no
+// marker packets); recorded as plain markers if nothing is launched.
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
-                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s);
+                             const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace moek

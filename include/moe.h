@@ -245,11 +245,13 @@ typedef struct {
                              outputs overwrite the local rows in place) */
   /* Optional timing: each non-NULL events[i] is recorded on the call's
    * stream at a stage boundary -- 0 before the gate, 1 after the gate, 2
-   * after the route, 3 after the dispatch (slots and pack), 4 after the
-   * expert FFN, 5 after the combine -- so a caller can time stages inside a
-   * running sequence of forwards (each record costs a few microseconds of
-   * stream time).  The caller owns the events (created with timing
-   * enabled). */
+   * after the route, 3 at the start of the expert FFN's first kernel, 4 at
+   * the end of its last kernel, 5 after the combine -- so a caller can time
+   * stages inside a running sequence of forwards.  Events 3 and 4 are taken
+   * from the FFN dispatches' own start and end timestamps (3 -> 4 is the
+   * FFN's kernel time; the launch gap before it counts in 2 -> 3); the
+   * others are marker records, each costing a few microseconds of stream
+   * time.  The caller owns the events (created with timing enabled). */
   hipEvent_t events[6];
 } moe_forward_out_t;
 
