@@ -72,6 +72,7 @@ __all__ = [
     "capacity", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "gate_logits",
     "softmax", "route", "assign_slots", "layout", "pack", "gelu", "silu",
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
+    "expert_capacities", "routing_stats",
 ]
 
 
@@ -198,16 +199,36 @@ def route(logits: np.ndarray, k: int, tau: float = 1.0):
 # ----------------------------------------------------------------------------
 # step 3: capacity-limited slot assignment
 # ----------------------------------------------------------------------------
-def assign_slots(idx: np.ndarray, E: int, C: int):
+def expert_capacities(E: int, C: int, unavailable=None) -> np.ndarray:
+    """Capacity of each expert: C, or 0 for an expert marked unavailable.
+
+    [EP-glossary] lists an expert that becomes unavailable among the
+    failure modes of routing; [EP-notes] "Components and Architecture":
+    tokens routed to a full expert are dropped.  Reading: an unavailable
+    expert is one whose capacity is zero, so every assignment to it is
+    dropped exactly like overflow.  Pins: masked experts keep nothing,
+    an all-false mask changes nothing, claim-queue brute force with
+    per-expert capacities (test_oracle_health)."""
+    cap = np.full(E, int(C), dtype=np.int64)
+    if unavailable is not None:
+        m = np.asarray(unavailable).astype(bool).reshape(-1)
+        if m.shape[0] != E:
+            raise ValueError("unavailable needs E entries")
+        cap[m] = 0
+    return cap
+
+
+def assign_slots(idx: np.ndarray, E: int, C: int, unavailable=None):
     """Slot of every assignment inside its expert, and which ones are kept.
 
     Assignment (t, j) has claim priority q = j*B + t (slot-major: every
     token's first choice in token order, then every second choice, ...).
     pos[t, j] = number of assignments to the same expert with smaller q;
-    keep = pos < C.  n_e = assignments routed to e; kept_e = min(n_e, C);
-    dropped_e = max(0, n_e - C), the page's overflow with p*B*k = n_e
+    keep = pos < C_e.  n_e = assignments routed to e; kept_e = min(n_e, C_e);
+    dropped_e = max(0, n_e - C_e), the page's overflow with p*B*k = n_e
     ([EP-infinity] capacity paragraph; [EP-notes] "Components and
-    Architecture", capacity factor and token dropping).
+    Architecture", capacity factor and token dropping).  C_e = C, or 0 for
+    experts marked unavailable (``expert_capacities``).
 
     Uses one library primitive, a stable sort by expert of the assignments
     listed in q order; the rank inside each run of equal experts is pos.
@@ -215,6 +236,7 @@ def assign_slots(idx: np.ndarray, E: int, C: int):
     example fixture, the overflow identity (test_oracle_slots)."""
     idx = np.asarray(idx, dtype=np.int64)
     B, k = idx.shape
+    cap = expert_capacities(E, C, unavailable)
     e_q = idx.T.reshape(-1)                     # position q = j*B + t
     order = np.argsort(e_q, kind="stable")      # by expert, q ascending
     sorted_e = e_q[order]
@@ -223,13 +245,13 @@ def assign_slots(idx: np.ndarray, E: int, C: int):
     pos_q = np.empty(B * k, dtype=np.int64)
     pos_q[order] = np.arange(B * k) - start[sorted_e]
     pos = pos_q.reshape(k, B).T.copy()
-    keep = pos < C
-    count = np.minimum(load, C)
+    keep = pos < cap[idx]
+    count = np.minimum(load, cap)
     return pos.astype(np.int32), keep, load.astype(np.int32), count.astype(np.int32)
 
 
 def layout(idx: np.ndarray, pos: np.ndarray, keep: np.ndarray, E: int, D: int,
-           C: int):
+           C: int, unavailable=None):
     """Compact, expert-major packed layout (hence grouped by destination rank).
 
     expert_offset = exclusive prefix sum of kept_e (E+1 entries);
@@ -242,7 +264,7 @@ def layout(idx: np.ndarray, pos: np.ndarray, keep: np.ndarray, E: int, D: int,
     (test_oracle_slots)."""
     idx = np.asarray(idx, dtype=np.int64)
     load = np.bincount(idx.reshape(-1), minlength=E)
-    kept = np.minimum(load, C)
+    kept = np.minimum(load, expert_capacities(E, C, unavailable))
     expert_offset = np.zeros(E + 1, dtype=np.int64)
     expert_offset[1:] = np.cumsum(kept)
     rank_offset = expert_offset[np.arange(D + 1) * (E // D)]
@@ -399,7 +421,7 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
 def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
             n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
             tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
-            logits: Optional[np.ndarray] = None) -> dict:
+            logits: Optional[np.ndarray] = None, unavailable=None) -> dict:
     """All steps in the pages' order ([EP-notes] "Formal Algorithm";
     [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
     and slots, pack, expert FFN, unpack + weighted combine (+ residual).
@@ -415,8 +437,9 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
     idx, w = route(logits, k, tau)
     if C is None:
         C = capacity(B, k, E, c)
-    pos, keep, load, count = assign_slots(idx, E, C)
-    expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C)
+    pos, keep, load, count = assign_slots(idx, E, C, unavailable)
+    expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C,
+                                                        unavailable)
     packed = pack(x, pack_src)
     out = dict(logits=logits, idx=idx, w=w, C=C, pos=pos, keep=keep,
                expert_load=load, expert_count=count, expert_offset=expert_offset,
@@ -427,3 +450,53 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
         out["ret"] = ret
         out["y"] = combine(ret, dest, w, x if add_residual else None)
     return out
+
+
+# ----------------------------------------------------------------------------
+# routing-health signals
+# ----------------------------------------------------------------------------
+def routing_stats(logits: np.ndarray, expert_load: np.ndarray, expert_count: np.ndarray,
+                  C: int, k: int, tau: float = 1.0) -> dict:
+    """Routing-health signals of one batch, float64.
+
+    [EP-glossary] "Practitioner Guidance": expert utilisation and routing
+    entropy are first-class health signals; [EP-infinity] figure text: the
+    bar of an expert is the share of its capacity used, a dashed bar an
+    expert at capacity that drops; [EP-notes] "Components and
+    Architecture", auxiliary load-balancing loss: the Switch loss penalises,
+    per expert, the product of the fraction of tokens routed to it and the
+    fraction of routing probability it receives (the caller applies the
+    coefficient; the page prints no scaling by E).
+
+    Readings (the pages give no formulas):
+      prob_mean[e]  P_e = (1/B) sum_t p_te, p_t = softmax(g_t / tau);
+      token_frac[e] f_e = n_e / B, the share of the B tokens that chose e
+                    (each token counts once per chosen expert; sums to k);
+      aux_loss      sum_e f_e P_e;
+      entropy       routing entropy, the mean over tokens of
+                    -sum_e p_te ln p_te (nats);
+      load_entropy  -sum_e a_e ln a_e with a_e = n_e / (B k), the spread of
+                    the assignments over the experts (nats; 0 ln 0 = 0);
+      utilization[e] kept_e / C (0 when C = 0);
+      dropped[e]    n_e - kept_e.
+    With B = 0 every float is 0.  Pins: equal logits, one-hot logits, a
+    perfectly balanced top-1 batch, a single hot expert, the overflow
+    identity (test_oracle_health)."""
+    l32 = np.asarray(logits, dtype=np.float32)
+    B, E = l32.shape
+    n = np.asarray(expert_load, dtype=np.int64).reshape(E)
+    kept = np.asarray(expert_count, dtype=np.int64).reshape(E)
+    if B == 0:
+        z = np.zeros(E)
+        return dict(prob_mean=z, token_frac=z.copy(), aux_loss=0.0, entropy=0.0,
+                    load_entropy=0.0, utilization=z.copy(), dropped=n - kept)
+    p = softmax(l32, tau)
+    P = p.mean(axis=0)
+    f = n / B
+    plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    ent = float(-plogp.sum(axis=1).mean())
+    a = n / (B * k)
+    alog = np.where(a > 0, a * np.log(np.where(a > 0, a, 1.0)), 0.0)
+    util = kept / C if C > 0 else np.zeros(E)
+    return dict(prob_mean=P, token_frac=f, aux_loss=float((f * P).sum()), entropy=ent,
+                load_entropy=float(-alog.sum()), utilization=util, dropped=n - kept)
