@@ -23,7 +23,8 @@ from ._lib import MoEError, Problem  # noqa: F401
 
 __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
            "workspace_bytes", "weights_bytes", "pack_weights", "gate", "route", "dispatch",
-           "expert_ffn", "combine", "unpack", "forward", "MoEError", "Problem", "lib"]
+           "expert_ffn", "combine", "unpack", "forward", "routing_stats", "MoEError", "Problem",
+           "lib"]
 
 
 def lib():
@@ -33,12 +34,32 @@ def lib():
 def make_problem(B: int, d: int, E: int, k: int, c: float = 1.0, f: int = 8,
                  act: str = "gelu", x_dtype: str = "bf16", C: int = -1, n_ranks: int = 1,
                  e_begin: int = 0, e_end: Optional[int] = None, tau: float = 1.0,
-                 add_residual: bool = False) -> Problem:
-    return Problem(B=B, d=d, E=E, k=k, c=c, C=C, n_ranks=n_ranks, e_begin=e_begin,
-                   e_end=E if e_end is None else e_end, f=f,
-                   act={"gelu": L.MOE_GELU, "swiglu": L.MOE_SWIGLU}[act],
-                   x_dtype={"f32": L.MOE_F32, "bf16": L.MOE_BF16}[x_dtype], tau=tau,
-                   add_residual=int(bool(add_residual)))
+                 add_residual: bool = False, unavailable=None) -> Problem:
+    """``unavailable``: optional device tensor of E uint8 (or bool); a
+    nonzero entry gives that expert capacity 0.  The problem keeps a
+    reference to it."""
+    p = Problem(B=B, d=d, E=E, k=k, c=c, C=C, n_ranks=n_ranks, e_begin=e_begin,
+                e_end=E if e_end is None else e_end, f=f,
+                act={"gelu": L.MOE_GELU, "swiglu": L.MOE_SWIGLU}[act],
+                x_dtype={"f32": L.MOE_F32, "bf16": L.MOE_BF16}[x_dtype], tau=tau,
+                add_residual=int(bool(add_residual)))
+    set_unavailable(p, unavailable)
+    return p
+
+
+def set_unavailable(p: Problem, mask) -> None:
+    """Attach (or with None, clear) the per-expert unavailable mask."""
+    if mask is None:
+        p.expert_unavailable = None
+        p._mask = None
+        return
+    if mask.dtype == torch.bool:
+        mask = mask.to(torch.uint8)
+    if mask.dtype != torch.uint8 or not mask.is_cuda or mask.numel() != p.E:
+        raise ValueError("unavailable must be a device uint8/bool tensor of E entries")
+    mask = mask.contiguous()
+    p._mask = mask
+    p.expert_unavailable = mask.data_ptr()
 
 
 def capacity(B: int, k: int, E: int, c: float) -> int:
@@ -58,7 +79,8 @@ def validate(p: Problem) -> int:
 
 
 def workspace_bytes(p: Problem, op: str = "forward") -> int:
-    o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD}[op]
+    o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD,
+         "routing_stats": L.MOE_OP_ROUTING_STATS}[op]
     return lib().moe_workspace_bytes(ctypes.byref(p), o)
 
 
@@ -134,6 +156,31 @@ def route(p: Problem, logits, topk_idx=None, topk_w=None):
     L.check(lib().moe_route(ctypes.byref(p), _p(logits), _p(topk_idx), _p(topk_w), _stream()),
             "moe_route")
     return topk_idx, topk_w
+
+
+def routing_stats(p: Problem, logits, expert_load, expert_count, ws=None) -> dict:
+    """Routing-health signals from the logits and the dispatch counts:
+    prob_mean, token_frac, utilization [E] float32, dropped [E] int32 and
+    summary [5] float64 (aux loss, routing entropy, load entropy, dropped
+    total, kept total), all device tensors."""
+    _check(p)
+    B, E = p.B, p.E
+    dev = expert_load.device
+    if B > 0:
+        _need(logits, "logits", B * E, 4)
+    _need(expert_load, "expert_load", E, 4)
+    _need(expert_count, "expert_count", E, 4)
+    o = dict(prob_mean=torch.empty(E, dtype=torch.float32, device=dev),
+             token_frac=torch.empty(E, dtype=torch.float32, device=dev),
+             utilization=torch.empty(E, dtype=torch.float32, device=dev),
+             dropped=torch.empty(E, dtype=torch.int32, device=dev),
+             summary=torch.empty(5, dtype=torch.float64, device=dev))
+    out = L.RoutingStats(**{n: o[n].data_ptr() for n in o})
+    ws = _ws(p, "routing_stats", ws, dev)
+    L.check(lib().moe_routing_stats(ctypes.byref(p), _p(logits) if B > 0 else None,
+                                    _p(expert_load), _p(expert_count), ctypes.byref(out), _p(ws),
+                                    ws.numel(), _stream()), "moe_routing_stats")
+    return o
 
 
 def dispatch(p: Problem, x, topk_idx, ws=None) -> dict:

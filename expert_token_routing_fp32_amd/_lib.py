@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
-MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD = 0, 1, 2
+MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS = 0, 1, 2, 3
 
 
 class Problem(ctypes.Structure):
@@ -32,7 +32,14 @@ class Problem(ctypes.Structure):
         ("x_dtype", ctypes.c_int32),
         ("tau", ctypes.c_float),
         ("add_residual", ctypes.c_int32),
+        ("expert_unavailable", ctypes.c_void_p),
     ]
+
+
+class RoutingStats(ctypes.Structure):
+    """moe_routing_stats_t: device pointers (or NULL)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "prob_mean", "token_frac", "utilization", "dropped", "summary")]
 
 
 class ForwardOut(ctypes.Structure):
@@ -71,6 +78,8 @@ _SIGS = {
     "moe_unpack": (ctypes.c_int, [_P, _V, _V, _V, _V]),
     "moe_forward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.POINTER(ForwardOut), _V,
                                    ctypes.c_size_t, _V]),
+    "moe_routing_stats": (ctypes.c_int, [_P, _V, _V, _V, ctypes.POINTER(RoutingStats), _V,
+                                         ctypes.c_size_t, _V]),
 }
 
 _lib = None

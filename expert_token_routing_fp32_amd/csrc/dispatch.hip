@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kSlotThreads) void slot_hist_kernel(const int32_t* 
 // One block.  Thread (g, e) of G = 1024/Epad groups walks a contiguous range
 // of tiles for expert e.
 __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
-    int32_t* __restrict__ hist, int n_tiles, int E, int Epad, int C, int D,
+    int32_t* __restrict__ hist, int n_tiles, int E, int Epad, int C,
+    const uint8_t* __restrict__ unavail, int D,
     int32_t* __restrict__ expert_load, int32_t* __restrict__ expert_count,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
   __shared__ int gsum[kScanThreads];
@@ -104,7 +105,8 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
   }
   int kept = 0;
   if (g == 0 && e < E) {
-    kept = tot < C ? tot : C;
+    const int ce = (unavail && unavail[e]) ? 0 : C;  // an unavailable expert keeps nothing
+    kept = tot < ce ? tot : ce;
     if (expert_load) expert_load[e] = tot;
     expert_count[e] = kept;
   }
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
 // separate single-workgroup scan launch.
 template <bool FUSED>
 __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C, int64_t BK,
+    const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C,
+    const uint8_t* __restrict__ unavail, int64_t BK,
     int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset_in,
     int32_t* __restrict__ pos, uint8_t* __restrict__ keep, int32_t* __restrict__ dest,
     int32_t* __restrict__ pack_src, int n_tiles, int D, int32_t* __restrict__ expert_load,
@@ -147,9 +150,13 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   const int64_t n = BK - q0 < tile ? BK - q0 : tile;
   for (int i = tid; i < tile; i += kSlotThreads) ebuf[i] = i < n ? load_expert(idx, q0 + i, B, k, E) : -1;
   for (int i = tid; i < 4 * E; i += kSlotThreads) wb[i] = 0;
+  // capacity of each expert: C, or 0 for one marked unavailable
+  int* cap = wb + 4 * E;
+  for (int i = tid; i < E; i += kSlotThreads) cap[i] = (unavail && unavail[i]) ? 0 : C;
+  __syncthreads();
   // FUSED: sbase [E] bases of this tile, soff [E + 1] expert offsets of the
   // kept rows, then scratch
-  int* sbase = wb + 4 * E;
+  int* sbase = cap + E;
   int* soff = sbase + E;
   if constexpr (FUSED) {
     int* pb = soff + E + 1;          // [G][E] partial sums of the earlier tiles
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
           st += pt[g * E + e];
         }
         sbase[e] = sb;
-        kept[u] = st < C ? st : C;
+        kept[u] = st < cap[e] ? st : cap[e];
         if (b == 0) {
           if (expert_load) expert_load[e] = st;
           expert_count[e] = kept[u];
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
       const int64_t j = q / B;
       const int64_t t = q - j * B;
       const int64_t o = t * k + j;
-      const bool kp = e >= 0 && p < C;
+      const bool kp = e >= 0 && p < cap[e];
       const int dr = kp ? expert_offset[e] + p : -1;
       pos[o] = p;
       keep[o] = kp ? 1 : 0;
@@ -332,7 +339,8 @@ size_t slot_ws_bytes(int64_t B, int k, int E) {
   return (size_t)(p.n_tiles > 0 ? p.n_tiles : 1) * E * sizeof(int32_t);
 }
 
-hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int D, int32_t* pos,
+hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
+                        const uint8_t* unavail, int D, int32_t* pos,
                         uint8_t* keep, int32_t* dest, int32_t* expert_load, int32_t* expert_count,
                         int32_t* expert_offset, int32_t* rank_offset, int32_t* pack_src,
                         int32_t* ws_hist, hipStream_t s) {
@@ -350,19 +358,20 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int 
                      (reinterpret_cast<uintptr_t>(ws_hist) & 15u) == 0;
   if (!fused)
     hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
-                       Epad, C, D, expert_load, expert_count, expert_offset, rank_offset);
+                       Epad, C, unavail, D, expert_load, expert_count, expert_offset, rank_offset);
   if (p.n_tiles > 0) {
-    // ebuf, per-wavefront counts; fused: + bases, offsets, 2 x 1024 partials, 4 wave sums
-    const size_t lds = (size_t)(p.tile + 4 * E + (fused ? 2 * E + 1 + 2 * 4 * kSlotThreads + 4 : 0)) *
+    // ebuf, per-wavefront counts, capacities; fused: + bases, offsets,
+    // 2 x 1024 partials, 4 wave sums
+    const size_t lds = (size_t)(p.tile + 5 * E + (fused ? 2 * E + 1 + 2 * 4 * kSlotThreads + 4 : 0)) *
                        sizeof(int);
     if (fused)
       hipLaunchKernelGGL(slot_rank_kernel<true>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx,
-                         B, k, E, nbits, C, p.BK, p.tile, ws_hist, nullptr, pos, keep, dest,
+                         B, k, E, nbits, C, unavail, p.BK, p.tile, ws_hist, nullptr, pos, keep, dest,
                          pack_src, p.n_tiles, D, expert_load, expert_count, expert_offset,
                          rank_offset);
     else
       hipLaunchKernelGGL(slot_rank_kernel<false>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s,
-                         idx, B, k, E, nbits, C, p.BK, p.tile, ws_hist, expert_offset, pos, keep,
+                         idx, B, k, E, nbits, C, unavail, p.BK, p.tile, ws_hist, expert_offset, pos, keep,
                          dest, pack_src, p.n_tiles, D, nullptr, nullptr, nullptr, nullptr);
   }
   return hipGetLastError();

@@ -164,6 +164,8 @@ size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op) {
       return ffn_ws(p);
     case MOE_OP_FORWARD:
       return carve_forward(p, nullptr, nullptr, nullptr);
+    case MOE_OP_ROUTING_STATS:
+      return moek::stats_ws_bytes(p->B, p->E);
   }
   return SIZE_MAX;
 }
@@ -195,6 +197,25 @@ moe_status_t moe_gate(const moe_problem_t* p, const void* x, const float* Wg, co
                                       p->E, nullptr, stream));
 }
 
+moe_status_t moe_routing_stats(const moe_problem_t* p, const float* logits,
+                               const int32_t* expert_load, const int32_t* expert_count,
+                               const moe_routing_stats_t* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!out || !expert_load || !expert_count) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!logits || !a4(logits))) return MOE_ERR_INVALID;
+  if (!a4(expert_load) || !a4(expert_count) || !a4(out->prob_mean) || !a4(out->token_frac) ||
+      !a4(out->utilization) || !a4(out->dropped) ||
+      (reinterpret_cast<uintptr_t>(out->summary) & 7u) != 0)
+    return MOE_ERR_INVALID;
+  const size_t need = moek::stats_ws_bytes(p->B, p->E);
+  if (need > 0 && (!ws || ws_bytes < need || !a4(ws))) return MOE_ERR_WORKSPACE;
+  return hip_status(moek::launch_routing_stats(
+      logits, p->B, p->E, p->k, capacity_of(p), p->tau, expert_load, expert_count,
+      out->prob_mean, out->token_frac, out->utilization, out->dropped, out->summary, ws, stream));
+}
+
 moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* topk_idx,
                        float* topk_w, hipStream_t stream) {
   moe_status_t st = moe_validate(p);
@@ -217,7 +238,8 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
   if (p->B > 0 && (!a16(x) || !a16(packed))) return MOE_ERR_INVALID;
   if (!ws || ws_bytes < dispatch_ws(p)) return MOE_ERR_WORKSPACE;
   const int C = capacity_of(p);
-  hipError_t e = moek::launch_slots(topk_idx, p->B, p->k, p->E, C, p->n_ranks, pos, keep, dest,
+  hipError_t e = moek::launch_slots(topk_idx, p->B, p->k, p->E, C, p->expert_unavailable,
+                                    p->n_ranks, pos, keep, dest,
                                     expert_load, expert_count, expert_offset, rank_offset,
                                     pack_src, static_cast<int32_t*>(ws), stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -324,7 +346,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
     e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
   mark(2);
   if (e == hipSuccess)
-    e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->n_ranks, b.pos, b.keep, b.dest, b.load,
+    e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->expert_unavailable, p->n_ranks, b.pos,
+                           b.keep, b.dest, b.load,
                            b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
   // events 3 and 4: the expert FFN's first dispatch start and last dispatch

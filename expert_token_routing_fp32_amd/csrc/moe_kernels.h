@@ -141,10 +141,20 @@ struct SlotPlan {
 SlotPlan slot_plan(int64_t B, int k);
 size_t slot_ws_bytes(int64_t B, int k, int E);
 
-hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C, int D,
+// unavail: optional [E] device mask; a nonzero entry gives that expert
+// capacity 0 (every assignment to it is dropped)
+hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
+                        const uint8_t* unavail, int D,
                         int32_t* pos, uint8_t* keep, int32_t* dest, int32_t* expert_load,
                         int32_t* expert_count, int32_t* expert_offset, int32_t* rank_offset,
                         int32_t* pack_src, int32_t* ws_hist, hipStream_t s);
+
+// routing-health signals (health.hip): workspace bytes and the two launches
+size_t stats_ws_bytes(int64_t B, int E);
+hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, int C, float tau,
+                                const int32_t* load, const int32_t* count, float* prob_mean,
+                                float* token_frac, float* utilization, int32_t* dropped,
+                                double* summary, void* ws, hipStream_t s);
 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k,
                        int d, uint16_t* packed, hipStream_t s);

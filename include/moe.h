@@ -69,7 +69,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act_t;
 
 /* Which call a workspace is sized for (moe_workspace_bytes). */
-typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_FFN = 1, MOE_OP_FORWARD = 2 } moe_op_t;
+typedef enum {
+  MOE_OP_DISPATCH = 0,
+  MOE_OP_FFN = 1,
+  MOE_OP_FORWARD = 2,
+  MOE_OP_ROUTING_STATS = 3
+} moe_op_t;
 
 /* The problem statement: B tokens of hidden size d, E experts, top-k routing
  * with capacity factor c and per-expert capacity C = ceil((B*k/E)*c)
@@ -92,6 +97,13 @@ typedef struct {
   int32_t x_dtype;    /* moe_dtype_t of x and y                              */
   float tau;          /* softmax temperature (> 0), 1 by default             */
   int32_t add_residual; /* 1: y = x + combine; 0: y = combine              */
+  /* DEVICE [E] uint8 or NULL.  A nonzero entry marks the expert unavailable
+   * ("Expert Parallelism", inferensys.com glossary, "Risk and Threat
+   * Considerations": an expert can become unavailable): its capacity is 0,
+   * so every assignment to it is dropped exactly like overflow (keep = 0,
+   * dest = -1, expert_count = 0).  NULL: every expert has capacity C.
+   * Read by moe_dispatch and moe_forward; owned by the caller. */
+  const uint8_t* expert_unavailable;
 } moe_problem_t;
 
 /* ---- host-only helpers (no GPU work) ---------------------------------- */
@@ -126,7 +138,9 @@ const char* moe_status_str(moe_status_t s);
  *   Wg     [d][E]  float32
  *   bias   [E]     float32, or NULL for none
  *   logits [B][E]  float32, out
- * Computed in fp32 on the vector ALUs with blocked accumulation. */
+ * fp32 x: the vector ALUs.  bf16 x: the matrix cores, with every fp32 weight
+ * split exactly into three bf16 parts (hi + mid + lo), so each product is
+ * exact and the sum is accumulated in fp32. */
 moe_status_t moe_gate(const moe_problem_t* p, const void* x, const float* Wg,
                       const float* bias, float* logits, hipStream_t stream);
 
@@ -227,6 +241,43 @@ moe_status_t moe_combine(const moe_problem_t* p, const moe_bf16_t* ret,
 moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret,
                         const int32_t* dest, moe_bf16_t* out,
                         hipStream_t stream);
+
+/* Routing-health signals of one batch ("Expert Parallelism", inferensys.com
+ * glossary, "Practitioner Guidance": expert utilisation and routing entropy
+ * as health signals; narrativegoldmine.com, "Components and Architecture",
+ * auxiliary load-balancing loss: per expert, the fraction of tokens routed
+ * to it times the fraction of routing probability it receives;
+ * theinfinity.ai, figure text: each expert's bar is the share of its
+ * capacity in use).  With p_t = softmax(logits_t / tau), n_e = expert_load,
+ * kept_e = expert_count and C the problem's capacity:
+ *   prob_mean   [E] float   P_e = (1/B) sum_t p_te
+ *   token_frac  [E] float   f_e = n_e / B (sums to k)
+ *   utilization [E] float   kept_e / C (0 when C = 0)
+ *   dropped     [E] int32   n_e - kept_e
+ *   summary     [5] double  aux loss sum_e f_e P_e (the caller applies the
+ *                           coefficient), routing entropy (mean over tokens
+ *                           of -sum_e p_te ln p_te, nats), load entropy
+ *                           (-sum_e a_e ln a_e, a_e = n_e / (B k), nats),
+ *                           dropped total, kept total
+ * Any field may be NULL (not written).  With B = 0 the floats are 0. */
+typedef struct {
+  float* prob_mean;
+  float* token_frac;
+  float* utilization;
+  int32_t* dropped;
+  double* summary;
+} moe_routing_stats_t;
+
+/* Fills *out (device buffers) from the router logits [B][E] float32 and the
+ * dispatch counts expert_load / expert_count [E] int32 (as written by
+ * moe_dispatch or moe_forward).  Deterministic: fixed-order reductions,
+ * per-block fp32 partial sums combined in double.
+ *   ws / ws_bytes  workspace, >= moe_workspace_bytes(p, MOE_OP_ROUTING_STATS) */
+moe_status_t moe_routing_stats(const moe_problem_t* p, const float* logits,
+                               const int32_t* expert_load,
+                               const int32_t* expert_count,
+                               const moe_routing_stats_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* Optional outputs of moe_forward; any NULL field lives in the workspace. */
 typedef struct {

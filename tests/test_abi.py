@@ -63,11 +63,14 @@ def test_ctypes_layout_matches_c(L, tmp_path):
         pytest.skip("no gcc")
     fields = [f for f, _ in L.Problem._fields_]
     ofields = [f for f, _ in L.ForwardOut._fields_]
+    sfields = [f for f, _ in L.RoutingStats._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){",
              'printf("%zu\\n", sizeof(moe_problem_t));']
     lines += [f'printf("%zu\\n", offsetof(moe_problem_t, {f}));' for f in fields]
     lines += ['printf("%zu\\n", sizeof(moe_forward_out_t));']
     lines += [f'printf("%zu\\n", offsetof(moe_forward_out_t, {f}));' for f in ofields]
+    lines += ['printf("%zu\\n", sizeof(moe_routing_stats_t));']
+    lines += [f'printf("%zu\\n", offsetof(moe_routing_stats_t, {f}));' for f in sfields]
     lines += ["return 0;}"]
     c = tmp_path / "layout.c"
     c.write_text("\n".join(lines))
@@ -80,6 +83,7 @@ def test_ctypes_layout_matches_c(L, tmp_path):
     vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     want = [ctypes.sizeof(L.Problem)] + [getattr(L.Problem, f).offset for f in fields]
     want += [ctypes.sizeof(L.ForwardOut)] + [getattr(L.ForwardOut, f).offset for f in ofields]
+    want += [ctypes.sizeof(L.RoutingStats)] + [getattr(L.RoutingStats, f).offset for f in sfields]
     assert vals == want
 
 
@@ -124,8 +128,11 @@ def test_max_kept_and_workspace(L, lib):
     assert lib.moe_max_kept(ctypes.byref(p)) == min(64 * 2, 8 * min(C, 64))
     p2 = _prob(L, C=3)
     assert lib.moe_max_kept(ctypes.byref(p2)) == 8 * 3
-    for op in (L.MOE_OP_DISPATCH, L.MOE_OP_FFN, L.MOE_OP_FORWARD):
+    for op in (L.MOE_OP_DISPATCH, L.MOE_OP_FFN, L.MOE_OP_FORWARD, L.MOE_OP_ROUTING_STATS):
         assert 0 < lib.moe_workspace_bytes(ctypes.byref(p), op) < 1 << 30
+    # routing statistics: one fp32 row of E + 1 partial sums per block
+    assert lib.moe_workspace_bytes(ctypes.byref(p), L.MOE_OP_ROUTING_STATS) % (4 * 9) == 0
+    assert lib.moe_workspace_bytes(ctypes.byref(_prob(L, B=0)), L.MOE_OP_ROUTING_STATS) == 0
 
 
 def test_status_strings(lib):
@@ -153,3 +160,12 @@ def test_calls_reject_before_launch(L, lib):
     unaligned = ctypes.c_void_p((1 << 20) + 2)
     r = lib.moe_gate(ctypes.byref(p), unaligned, fake, None, fake, None)
     assert r == L.MOE_ERR_INVALID
+    assert lib.moe_routing_stats(ctypes.byref(p), fake, fake, fake, None, None, 0,
+                                 None) == L.MOE_ERR_INVALID
+    out = L.RoutingStats(prob_mean=1 << 20, token_frac=1 << 20, utilization=1 << 20,
+                         dropped=1 << 20, summary=1 << 20)
+    assert lib.moe_routing_stats(ctypes.byref(p), fake, fake, fake, ctypes.byref(out), None, 0,
+                                 None) == L.MOE_ERR_WORKSPACE
+    out.summary = (1 << 20) + 4  # doubles need 8-byte alignment
+    assert lib.moe_routing_stats(ctypes.byref(p), fake, fake, fake, ctypes.byref(out), fake,
+                                 1 << 30, None) == L.MOE_ERR_INVALID

@@ -148,3 +148,28 @@ def test_combine(wl):
     if dropped_all.size:
         assert (got[dropped_all] == 0).all()
         say(f"  {name}: {dropped_all.size} fully dropped tokens give 0")
+
+
+def test_routing_stats(wl):
+    """Routing-health signals from the oracle's logits and counts: P_e and the
+    routing entropy (fp32 per token, fixed-order sums) within 1e-5; the
+    count-derived values (f_e, kept / C, drops, load entropy, totals) to
+    float rounding or bit for bit."""
+    import expert_token_routing_fp32_amd as moe
+    name, w, inp, ref, d = wl
+    p = problem_for(w)
+    s = moe.routing_stats(p, to_dev(ref["logits"]), to_dev(ref["expert_load"]),
+                          to_dev(ref["expert_count"]))
+    exp = oracle.routing_stats(ref["logits"], ref["expert_load"], ref["expert_count"], ref["C"],
+                               w.k, w.tau)
+    np.testing.assert_allclose(to_np(s["prob_mean"]), exp["prob_mean"], rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(to_np(s["token_frac"]), exp["token_frac"], rtol=1e-7)
+    np.testing.assert_allclose(to_np(s["utilization"]), exp["utilization"], rtol=1e-7)
+    np.testing.assert_array_equal(to_np(s["dropped"]), exp["dropped"])
+    sm = to_np(s["summary"])
+    np.testing.assert_allclose(sm[0], exp["aux_loss"], rtol=1e-5)
+    np.testing.assert_allclose(sm[1], exp["entropy"], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(sm[2], exp["load_entropy"], rtol=1e-12, atol=1e-14)
+    assert sm[3] == exp["dropped"].sum() and sm[4] == ref["expert_count"].sum()
+    say(f"  {name}: aux {sm[0]:.6f} entropy {sm[1]:.4f} nats load entropy {sm[2]:.4f} "
+        f"dropped {int(sm[3])}")
