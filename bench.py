@@ -267,6 +267,24 @@ def main():
     eo = o["expert_offset"].cpu().numpy()
     alg = algorithmic(w, keep, eo)
 
+    # routing-health signals of the same batch (an optional call after the
+    # forward, not part of the timed step): timed alone with events
+    ws_stats = torch.empty(max(moe.workspace_bytes(p, "routing_stats"), 1), dtype=torch.uint8,
+                           device=dev)
+    for _ in range(3):
+        hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"], ws=ws_stats)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"], ws=ws_stats)
+    e1.record()
+    torch.cuda.synchronize()
+    t_stats = e0.elapsed_time(e1) / reps * 1e-3
+    hsum = hs["summary"].cpu().numpy()
+    # algorithmic bytes: the logits once, the counts, the per-expert outputs
+    stats_bytes = w.B * w.E * 4 + w.E * (2 * 4 + 4 * 4) + 5 * 8
+
     ffn_gbs = alg["ffn_bytes"] / t_ffn_live / 1e9
     ffn_tflops = alg["ffn_flop"] / t_ffn_live / 1e12
     ffn_bound = "hbm" if alg["ffn_bytes"] / (HBM_PEAK_GBS * 1e9) >= \
@@ -308,6 +326,12 @@ def main():
         "route_pack_combine_gbs": round(rpc_bytes / rpc_t / 1e9, 1),
         "route_pack_combine_hbm_frac": round(rpc_bytes / rpc_t / 1e9 / HBM_PEAK_GBS, 4),
         "kept": alg["K"], "kept_local": alg["Kloc"], "dropped": int(w.B * w.k - alg["K"]),
+        "routing_stats_us": round(t_stats * 1e6, 2),
+        "routing_stats_hbm_frac": round(stats_bytes / t_stats / 1e9 / HBM_PEAK_GBS, 4),
+        "routing_health": {"aux_loss": round(float(hsum[0]), 6),
+                           "entropy_nats": round(float(hsum[1]), 5),
+                           "load_entropy_nats": round(float(hsum[2]), 5),
+                           "dropped": int(hsum[3]), "kept": int(hsum[4])},
     }
 
     out = {

@@ -10,14 +10,17 @@
 // "Expert Parallelism" (theinfinity.ai), figure text: each expert's bar is
 // the share of its capacity in use.
 //
-// Two launches, both deterministic (every sum in a fixed order):
+// Three launches, all deterministic (every sum in a fixed order):
 //   stats_partial  L lanes per token (the router's lane geometry), V logits
 //                  per lane; per token the softmax and its entropy
 //                  ln S - (sum_e e^z z) / S with z = (g - max g) / tau; each
 //                  block sums p over its token range per expert and the
-//                  entropies, in fp32, into one row of the workspace
-//   stats_final    one block: the rows summed per expert in double, then
-//                  P_e, f_e, kept / C, drops and the scalar signals
+//                  entropies in fp32, into column e (and E) of a
+//                  column-major [E + 1][blocks] table
+//   stats_column   one wavefront per column: the block partials loaded
+//                  coalesced and added in double by a fixed butterfly
+//   stats_final    one block: P_e, f_e, kept / C, drops and the scalar
+//                  signals (fixed-tree sums in double)
 // The logits are read once (B E 4 bytes); everything else is O(E) per block.
 #include "moe_kernels.h"
 
@@ -81,17 +84,34 @@ __global__ __launch_bounds__(kStatThreads) void stats_partial_kernel(
   for (int u = 0; u < V; ++u) red[g * (L * V) + u * L + li] = acc[u];
   if (li == 0) hred[g] = hacc;
   __syncthreads();
-  float* out = part + (int64_t)blockIdx.x * (E + 1);
+  const int nblk = gridDim.x;
   for (int e = tid; e < E; e += kStatThreads) {
     float sum = 0.f;
     for (int gg = 0; gg < G; ++gg) sum += red[gg * (L * V) + e];
-    out[e] = sum;
+    part[(int64_t)e * nblk + blockIdx.x] = sum;
   }
   if (tid == 0) {
     float sum = 0.f;
     for (int gg = 0; gg < G; ++gg) sum += hred[gg];
-    out[E] = sum;
+    part[(int64_t)E * nblk + blockIdx.x] = sum;
   }
+}
+
+// Column c of the partial table (c < E: expert c; c == E: entropies), one
+// wavefront each: lane l adds blocks l, l + 64, ... in double, then a
+// butterfly over the 64 lanes (the same pairing every time).
+__global__ __launch_bounds__(256) void stats_column_kernel(const float* __restrict__ part,
+                                                           int nblk, int ncol,
+                                                           double* __restrict__ colsum) {
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= ncol) return;
+  const float* col = part + (int64_t)c * nblk;
+  double s = 0.0;
+  for (int b = lane; b < nblk; b += 64) s += (double)col[b];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) colsum[c] = s;
 }
 
 // fixed-tree sum over the block (deterministic)
@@ -110,7 +130,7 @@ __device__ T block_sum(T v, T* sh) {
 }
 
 __global__ __launch_bounds__(kFinalThreads) void stats_final_kernel(
-    const float* __restrict__ part, int nblk, int64_t B, int E, int k, int C,
+    const double* __restrict__ colsum, int64_t B, int E, int k, int C,
     const int32_t* __restrict__ load, const int32_t* __restrict__ count,
     float* __restrict__ prob_mean, float* __restrict__ token_frac,
     float* __restrict__ utilization, int32_t* __restrict__ dropped, double* __restrict__ summary) {
@@ -121,9 +141,7 @@ __global__ __launch_bounds__(kFinalThreads) void stats_final_kernel(
   double aux = 0.0, lent = 0.0;
   long long drop_t = 0, kept_t = 0;
   for (int e = tid; e < E; e += kFinalThreads) {
-    double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += (double)part[(int64_t)b * (E + 1) + e];
-    const double P = B > 0 ? s / Bd : 0.0;
+    const double P = B > 0 ? colsum[e] / Bd : 0.0;
     const int n = load[e], kept = count[e];
     const double f = B > 0 ? (double)n / Bd : 0.0;
     if (prob_mean) prob_mean[e] = (float)P;
@@ -141,10 +159,8 @@ __global__ __launch_bounds__(kFinalThreads) void stats_final_kernel(
   drop_t = block_sum(drop_t, shl);
   kept_t = block_sum(kept_t, shl);
   if (tid == 0 && summary) {
-    double h = 0.0;
-    for (int b = 0; b < nblk; ++b) h += (double)part[(int64_t)b * (E + 1) + E];
     summary[0] = aux;
-    summary[1] = B > 0 ? h / Bd : 0.0;
+    summary[1] = B > 0 ? colsum[E] / Bd : 0.0;
     summary[2] = lent;
     summary[3] = (double)drop_t;
     summary[4] = (double)kept_t;
@@ -178,8 +194,14 @@ void launch_partial(const float* logits, int64_t B, int E, float inv_tau, int nb
 
 }  // namespace
 
+// partial table [E + 1][blocks] fp32, then the column sums [E + 1] double
+static size_t stats_table_bytes(int64_t B, int E) {
+  const size_t t = (size_t)stats_blocks(B, E) * (size_t)(E + 1) * sizeof(float);
+  return (t + 7) & ~(size_t)7;
+}
+
 size_t stats_ws_bytes(int64_t B, int E) {
-  return (size_t)stats_blocks(B, E) * (size_t)(E + 1) * sizeof(float);
+  return B > 0 ? stats_table_bytes(B, E) + (size_t)(E + 1) * sizeof(double) : 0;
 }
 
 hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, int C, float tau,
@@ -188,7 +210,9 @@ hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, in
                                 double* summary, void* ws, hipStream_t s) {
   const int nblk = stats_blocks(B, E);
   float* part = static_cast<float*>(ws);
+  double* colsum = nullptr;
   if (nblk > 0) {
+    colsum = reinterpret_cast<double*>(static_cast<char*>(ws) + stats_table_bytes(B, E));
     const int64_t tpb = (B + nblk - 1) / nblk;
     const float it = 1.0f / tau;
     if (E <= 1) launch_partial<1, 1>(logits, B, E, it, nblk, tpb, part, s);
@@ -202,9 +226,11 @@ hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, in
     else if (E <= 256) launch_partial<16, 16>(logits, B, E, it, nblk, tpb, part, s);
     else if (E <= 512) launch_partial<16, 32>(logits, B, E, it, nblk, tpb, part, s);
     else launch_partial<64, 16>(logits, B, E, it, nblk, tpb, part, s);
+    hipLaunchKernelGGL(stats_column_kernel, dim3((E + 1 + 3) / 4), dim3(256), 0, s, part, nblk,
+                       E + 1, colsum);
   }
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, part, nblk, B, E, k,
-                     C, load, count, prob_mean, token_frac, utilization, dropped, summary);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinalThreads), 0, s, colsum, B, E, k, C,
+                     load, count, prob_mean, token_frac, utilization, dropped, summary);
   return hipGetLastError();
 }
 
