@@ -72,7 +72,7 @@ __all__ = [
     "capacity", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "gate_logits",
     "softmax", "route", "assign_slots", "layout", "pack", "gelu", "silu",
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
-    "expert_capacities", "routing_stats",
+    "expert_capacities", "routing_stats", "shared_ffn",
 ]
 
 
@@ -384,10 +384,26 @@ def expert_ffn(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
 # ----------------------------------------------------------------------------
 # step 6: combine
 # ----------------------------------------------------------------------------
+def shared_ffn(x: np.ndarray, W1, W2, W3, act: str,
+               tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """Output of a shared expert, float64 [B, d] (or [len(tokens), d]).
+
+    [EP-notes] "Major Variants and Families", shared expert routing: one
+    expert processes every token in addition to the routed experts (a dense
+    path beside them).  It is an expert like the others (``expert_mlp``,
+    W1/W3 [f, d], W2 [d, f]) applied to every token's input, with weight 1.
+    Pin: a shared expert equals a routed expert that every token chooses
+    with probability 1 (E = 1, k = 1, no drops), computed through route,
+    slots, layout, expert_ffn and combine (test_oracle_shared)."""
+    rows = x if tokens is None else x[np.asarray(tokens, dtype=np.int64)]
+    return expert_mlp(_x_values(rows), W1, W2, W3, act)
+
+
 def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
             x_residual: Optional[np.ndarray] = None,
             tokens: Optional[np.ndarray] = None,
-            ret_rows: Optional[np.ndarray] = None) -> np.ndarray:
+            ret_rows: Optional[np.ndarray] = None,
+            shared: Optional[np.ndarray] = None) -> np.ndarray:
     """y[t] = sum_j [kept] w[t, j] * ret[dest[t, j]] (+ x[t]), float64.
 
     [EP-notes] "Components and Architecture", expert combine: the k outputs
@@ -399,8 +415,11 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
 
     ``tokens`` restricts the output to those tokens ([len(tokens), d]);
     ``ret_rows`` says which packed rows ``ret`` holds (sorted), when it holds
-    only some.  Pins: dense soft-mixture equivalence without drops, C = 0
-    gives 0 (test_oracle_combine_special)."""
+    only some.  ``shared`` (rows for the same tokens) is a shared expert's
+    output, added with weight 1 ([EP-notes] "Major Variants and Families",
+    shared expert routing).  Pins: dense soft-mixture equivalence without
+    drops, C = 0 gives 0 (test_oracle_combine_special); the shared expert
+    as a routed expert every token chooses (test_oracle_shared)."""
     B, k = dest.shape
     tt = np.arange(B) if tokens is None else np.asarray(tokens, dtype=np.int64)
     acc = np.zeros((tt.size, ret.shape[1]))
@@ -410,6 +429,8 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
         m = dj >= 0
         r = dj[m] if ret_rows is None else np.searchsorted(ret_rows, dj[m])
         acc[m] += w32[tt[m], j][:, None] * ret[r]
+    if shared is not None:
+        acc += np.asarray(shared, dtype=np.float64)
     if x_residual is not None:
         acc += _x_values(x_residual[tt])
     return acc
@@ -421,14 +442,16 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
 def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
             n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
             tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
-            logits: Optional[np.ndarray] = None, unavailable=None) -> dict:
+            logits: Optional[np.ndarray] = None, unavailable=None,
+            shared: Optional[tuple] = None) -> dict:
     """All steps in the pages' order ([EP-notes] "Formal Algorithm";
     [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
     and slots, pack, expert FFN, unpack + weighted combine (+ residual).
 
     ``logits`` may be given to skip the gate (routing tests feed the router
     directly); without expert weights only the integer steps and the pack
-    run."""
+    run.  ``shared`` = (W1s, W3s, W2s) adds a shared expert's output to every
+    token's combine."""
     B = x.shape[0]
     E = Wg.shape[1] if Wg is not None else logits.shape[1]
     e_end = E if e_end is None else e_end
@@ -448,7 +471,11 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
     if W1 is not None:
         ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3, act)
         out["ret"] = ret
-        out["y"] = combine(ret, dest, w, x if add_residual else None)
+        sh = None
+        if shared is not None:
+            sh = shared_ffn(x, shared[0], shared[2], shared[1], act)
+            out["shared_out"] = sh
+        out["y"] = combine(ret, dest, w, x if add_residual else None, shared=sh)
     return out
 
 
