@@ -23,8 +23,8 @@ from ._lib import MoEError, Problem  # noqa: F401
 
 __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
            "workspace_bytes", "weights_bytes", "pack_weights", "gate", "route", "dispatch",
-           "expert_ffn", "combine", "unpack", "forward", "routing_stats", "MoEError", "Problem",
-           "lib"]
+           "expert_ffn", "combine", "unpack", "forward", "routing_stats", "shared_problem",
+           "shared_ffn", "MoEError", "Problem", "lib"]
 
 
 def lib():
@@ -78,9 +78,15 @@ def validate(p: Problem) -> int:
     return lib().moe_validate(ctypes.byref(p))
 
 
+def shared_problem(p: Problem, f: int, act: str = "swiglu") -> Problem:
+    """The problem of a shared expert beside the routed layer p: same B and
+    d, one expert that every token uses, its own f and activation."""
+    return make_problem(B=p.B, d=p.d, E=1, k=1, c=1.0, f=f, act=act, x_dtype="bf16")
+
+
 def workspace_bytes(p: Problem, op: str = "forward") -> int:
     o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD,
-         "routing_stats": L.MOE_OP_ROUTING_STATS}[op]
+         "routing_stats": L.MOE_OP_ROUTING_STATS, "shared_ffn": L.MOE_OP_SHARED_FFN}[op]
     return lib().moe_workspace_bytes(ctypes.byref(p), o)
 
 
@@ -246,7 +252,23 @@ def expert_ffn(p: Problem, packed, expert_offset, wpacked, ret=None, ws=None):
     return ret
 
 
-def combine(p: Problem, ret, dest, topk_w, x_residual=None, y=None):
+def shared_ffn(ps: Problem, x, wpacked, out=None, ws=None):
+    """A shared expert on every token: out [B, d] bf16 (as int16 bits)."""
+    _check(ps)
+    B, d = ps.B, ps.d
+    _need(x, "x", B * d, 2)
+    if out is None:
+        out = torch.empty((B, d), dtype=torch.int16, device=x.device)
+    _need(out, "out", B * d, 2)
+    ws = _ws(ps, "shared_ffn", ws, x.device)
+    L.check(lib().moe_shared_ffn(ctypes.byref(ps), _p(x), _p(wpacked), _p(out), _p(ws),
+                                 ws.numel(), _stream()), "moe_shared_ffn")
+    return out
+
+
+def combine(p: Problem, ret, dest, topk_w, x_residual=None, y=None, shared_out=None):
+    """``shared_out``: a shared expert's rows [B, d] bf16, added with weight 1
+    (moe_combine_shared)."""
     _check(p)
     B, d, k = p.B, p.d, p.k
     _need(ret, "ret", max_kept(p) * d, 2)
@@ -258,6 +280,13 @@ def combine(p: Problem, ret, dest, topk_w, x_residual=None, y=None):
         y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
                         device=ret.device)
     _need(y, "y", B * d, _xsize(p))
+    if shared_out is not None:
+        _need(shared_out, "shared_out", B * d, 2)
+        L.check(lib().moe_combine_shared(ctypes.byref(p), _p(ret), _p(dest), _p(topk_w),
+                                         _p(shared_out),
+                                         _p(x_residual if p.add_residual else None), _p(y),
+                                         _stream()), "moe_combine_shared")
+        return y
     L.check(lib().moe_combine(ctypes.byref(p), _p(ret), _p(dest), _p(topk_w),
                               _p(x_residual if p.add_residual else None), _p(y), _stream()),
             "moe_combine")
@@ -284,14 +313,16 @@ STAGES = ("gate", "route", "dispatch", "expert_ffn", "combine")
 
 
 def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None,
-            stage_events=None):
+            stage_events=None, shared=None):
     """The whole layer on the current stream (``wpacked`` from pack_weights).
     With ``outputs`` the intermediate tensors are allocated and returned too
     (``packed`` then holds the expert outputs of the local rows, in place).
     ``stage_events``: optional six timing-enabled ``torch.cuda.Event`` (or
     None); the library records them at the boundaries of the STAGES (before
     the first, after each); events 3 and 4 come from the expert FFN's first
-    and last kernel dispatches themselves (their start and end timestamps)."""
+    and last kernel dispatches themselves (their start and end timestamps).
+    ``shared`` = (ps, wpacked_shared) adds a shared expert on every token
+    (moe_forward_shared; ps from shared_problem)."""
     _check(p)
     B, d, E, k = p.B, p.d, p.E, p.k
     dev = x.device
@@ -330,6 +361,18 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
             if ev.cuda_event == 0:  # torch creates the HIP event on first record
                 ev.record()
             outp.events[i] = ev.cuda_event
+    if shared is not None:
+        ps, wps = shared
+        _check(ps)
+        n = lib().moe_forward_shared_workspace_bytes(ctypes.byref(p), ctypes.byref(ps))
+        if ws is None:
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        _need(ws, "ws", n, 1)
+        L.check(lib().moe_forward_shared(ctypes.byref(p), ctypes.byref(ps), _p(x), _p(Wg),
+                                         _p(bias), _p(wpacked), _p(wps), _p(y),
+                                         ctypes.byref(outp) if outp is not None else None,
+                                         _p(ws), ws.numel(), _stream()), "moe_forward_shared")
+        return (y, o) if outputs else y
     n = workspace_bytes(p, "forward")
     if ws is None:
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
-MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS = 0, 1, 2, 3
+MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS, MOE_OP_SHARED_FFN = range(5)
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +80,11 @@ _SIGS = {
                                    ctypes.c_size_t, _V]),
     "moe_routing_stats": (ctypes.c_int, [_P, _V, _V, _V, ctypes.POINTER(RoutingStats), _V,
                                          ctypes.c_size_t, _V]),
+    "moe_shared_ffn": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "moe_combine_shared": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V]),
+    "moe_forward_shared_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
+    "moe_forward_shared": (ctypes.c_int, [_P, _P, _V, _V, _V, _V, _V, _V,
+                                          ctypes.POINTER(ForwardOut), _V, ctypes.c_size_t, _V]),
 }
 
 _lib = None

@@ -28,12 +28,15 @@ unsigned grid_for(int64_t work, int threads) {
 // One wavefront per token row, one lane per 16-byte chunk: block (4 tokens)
 // x (64 chunks), grid (ceil(B / 4), ceil(d / 512)).  The token index is
 // wavefront-uniform, so dest and the weights come through scalar loads; the
-// expert rows are read once, non-temporally.
-template <bool XBF16, bool RES>
+// expert rows are read once, non-temporally.  SH: a shared expert's output
+// row (bf16, "Major Variants and Families", shared expert routing) is added
+// with weight 1 after the routed sum, before the residual.
+template <bool XBF16, bool RES, bool SH>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t* __restrict__ ret, const int32_t* __restrict__ dest,
-    const float* __restrict__ w, const void* __restrict__ xres, void* __restrict__ y, int64_t B,
-    int k, int d, int64_t kmax) {
+    const float* __restrict__ w, const void* __restrict__ xres,
+    const uint16_t* __restrict__ shared, void* __restrict__ y, int64_t B, int k, int d,
+    int64_t kmax) {
   const int cpr = d / 8;
   const int c = blockIdx.x * 64 + (threadIdx.x & 63);
   const int64_t ntb = (B + 3) / 4;
@@ -53,6 +56,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] = fmaf(wj, f[u], acc[u]);
       }
+    }
+    if (SH) {
+      float sv[8];
+      unpack8(__builtin_nontemporal_load((const u32x4*)(shared + t * d + c * 8)), sv);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += sv[u];
     }
     if (RES) {
       float xr[8];
@@ -115,9 +124,21 @@ __global__ __launch_bounds__(256) void copy_remote_kernel(const uint16_t* __rest
 
 }  // namespace
 
+template <bool XBF16, bool RES>
+void launch_combine_t(dim3 g, const uint16_t* ret, const int32_t* dest, const float* w,
+                      const void* x_res, const uint16_t* shared, void* y, int64_t B, int k, int d,
+                      int64_t kmax, hipStream_t s) {
+  if (shared)
+    hipLaunchKernelGGL((combine_kernel<XBF16, RES, true>), g, dim3(256), 0, s, ret, dest, w,
+                       x_res, shared, y, B, k, d, kmax);
+  else
+    hipLaunchKernelGGL((combine_kernel<XBF16, RES, false>), g, dim3(256), 0, s, ret, dest, w,
+                       x_res, shared, y, B, k, d, kmax);
+}
+
 hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
-                          int64_t kmax, hipStream_t s) {
+                          int64_t kmax, hipStream_t s, const uint16_t* shared) {
   if (B == 0) return hipSuccess;
   // x: 512-column piece of the rows (fastest in dispatch order, so
   // consecutive workgroups cover consecutive pieces of the same rows);
@@ -126,18 +147,14 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
   const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16) {
     if (x_res)
-      hipLaunchKernelGGL((combine_kernel<true, true>), dim3(g), dim3(256), 0, s, ret, dest, w,
-                         x_res, y, B, k, d, kmax);
+      launch_combine_t<true, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
     else
-      hipLaunchKernelGGL((combine_kernel<true, false>), dim3(g), dim3(256), 0, s, ret, dest, w,
-                         x_res, y, B, k, d, kmax);
+      launch_combine_t<true, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
   } else {
     if (x_res)
-      hipLaunchKernelGGL((combine_kernel<false, true>), dim3(g), dim3(256), 0, s, ret, dest, w,
-                         x_res, y, B, k, d, kmax);
+      launch_combine_t<false, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
     else
-      hipLaunchKernelGGL((combine_kernel<false, false>), dim3(g), dim3(256), 0, s, ret, dest, w,
-                         x_res, y, B, k, d, kmax);
+      launch_combine_t<false, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
   }
   return hipGetLastError();
 }

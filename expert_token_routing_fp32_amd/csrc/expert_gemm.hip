@@ -718,6 +718,25 @@ hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uin
   return hipGetLastError();
 }
 
+namespace {
+// expert_offset {0, B} of the shared expert: one lane per entry
+__global__ void shared_offsets_kernel(int32_t* __restrict__ eo, int32_t B) {
+  const int i = threadIdx.x;
+  if (i < 2) eo[i] = i == 0 ? 0 : B;
+}
+}  // namespace
+
+hipError_t launch_shared_ffn(const uint16_t* x, int64_t B, int d, int f, bool swiglu,
+                             const void* wp, uint16_t* H, int32_t* eo, uint16_t* out,
+                             hipStream_t s, hipEvent_t ev_stop) {
+  if (B <= 0) return ev_stop ? hipEventRecord(ev_stop, s) : hipSuccess;
+  hipLaunchKernelGGL(shared_offsets_kernel, dim3(1), dim3(64), 0, s, eo, (int32_t)B);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_expert_ffn(x, eo, 0, 1, (int)B, (int)B, d, f, swiglu, wp, H, out, s, nullptr,
+                           ev_stop);
+}
+
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,

@@ -54,6 +54,11 @@ int64_t kloc_of(const moe_problem_t* p) {
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 size_t ffn_ws(const moe_problem_t* p) { return align_up((size_t)kloc_of(p) * p->f * 2); }
+// scratch of a shared expert (moe_shared_ffn): expert_offset {0, B} in one
+// aligned slot, then H [B][f] bf16
+size_t shared_ws(const moe_problem_t* ps) {
+  return align_up(2 * sizeof(int32_t)) + align_up((size_t)ps->B * ps->f * 2);
+}
 size_t dispatch_ws(const moe_problem_t* p) {
   return align_up(moek::slot_ws_bytes(p->B, p->k, p->E));
 }
@@ -166,6 +171,8 @@ size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op) {
       return carve_forward(p, nullptr, nullptr, nullptr);
     case MOE_OP_ROUTING_STATS:
       return moek::stats_ws_bytes(p->B, p->E);
+    case MOE_OP_SHARED_FFN:
+      return shared_ws(p);
   }
   return SIZE_MAX;
 }
@@ -316,9 +323,34 @@ moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret, const int
   return hip_status(moek::launch_unpack(ret, dest, p->B, p->k, p->d, kmax_of(p), out, stream));
 }
 
-moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg, const float* bias,
-                         const void* wpacked, void* y, moe_forward_out_t* out, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The shared expert of moe_forward_shared: its problem, packed weights and
+// scratch (expert_offset {0, B}, hidden activations, output rows).
+struct SharedRun {
+  const moe_problem_t* ps;
+  const void* wp;
+  int32_t* eo;
+  uint16_t* H;
+  uint16_t* S;
+};
+
+moe_status_t check_shared(const moe_problem_t* ps) {
+  moe_status_t st = moe_validate(ps);
+  if (st != MOE_OK) return st;
+  if (ps->E != 1 || ps->k != 1 || ps->e_begin != 0 || ps->e_end != 1) return MOE_ERR_INVALID;
+  if (ps->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The layer on one stream (moe_forward; with sh, moe_forward_shared).  ws
+// holds the routed layer's buffers (carve_forward) only.
+moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* Wg,
+                           const float* bias, const void* wpacked, void* y,
+                           moe_forward_out_t* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                           const SharedRun* sh) {
   moe_status_t st = moe_validate(p);
   if (st != MOE_OK) return st;
   const bool swiglu = p->act == MOE_SWIGLU;
@@ -351,22 +383,96 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
                            b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
   // events 3 and 4: the expert FFN's first dispatch start and last dispatch
-  // end (no marker packets between the launches)
+  // end (no marker packets between the launches); with a shared expert its
+  // GEMMs follow the routed ones inside the same pair
+  hipEvent_t ev3 = out ? out->events[3] : nullptr, ev4 = out ? out->events[4] : nullptr;
   if (p->B > 0) {
     if (e == hipSuccess)
       e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                   rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
-                                  stream, out ? out->events[3] : nullptr,
-                                  out ? out->events[4] : nullptr);
+                                  stream, ev3, sh ? nullptr : ev4);
+    if (e == hipSuccess && sh)
+      e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
+                                  sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,
+                                  ev4);
   } else {
     mark(3);
     mark(4);
   }
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
-                             p->k, p->d, kmax_of(p), stream);
+                             p->k, p->d, kmax_of(p), stream, sh ? sh->S : nullptr);
   mark(5);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg, const float* bias,
+                         const void* wpacked, void* y, moe_forward_out_t* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return forward_chain(p, x, Wg, bias, wpacked, y, out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status_t moe_shared_ffn(const moe_problem_t* ps, const moe_bf16_t* x, const void* wpacked,
+                            moe_bf16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_shared(ps);
+  if (st != MOE_OK) return st;
+  if (ps->B == 0) return MOE_OK;
+  if (!x || !wpacked || !out || !a16(x) || !a16(wpacked) || !a16(out)) return MOE_ERR_INVALID;
+  if (!ws || ws_bytes < shared_ws(ps) || !a16(ws)) return MOE_ERR_WORKSPACE;
+  int32_t* eo = static_cast<int32_t*>(ws);
+  uint16_t* H = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + align_up(8));
+  return hip_status(moek::launch_shared_ffn(x, ps->B, ps->d, ps->f, ps->act == MOE_SWIGLU,
+                                            wpacked, H, eo, out, stream));
+}
+
+moe_status_t moe_combine_shared(const moe_problem_t* p, const moe_bf16_t* ret,
+                                const int32_t* dest, const float* topk_w,
+                                const moe_bf16_t* shared_out, const void* x_residual, void* y,
+                                hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!ret || !dest || !topk_w || !y || !shared_out)) return MOE_ERR_INVALID;
+  if (p->B > 0 && p->add_residual && !x_residual) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(ret) || !a16(y) || !a16(shared_out) ||
+                   (p->add_residual && !a16(x_residual))))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_combine(ret, dest, topk_w, p->add_residual ? x_residual : nullptr,
+                                         p->x_dtype == MOE_BF16, y, p->B, p->k, p->d,
+                                         kmax_of(p), stream, shared_out));
+}
+
+size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p, const moe_problem_t* ps) {
+  if (moe_validate(p) != MOE_OK || check_shared(ps) != MOE_OK) return SIZE_MAX;
+  return carve_forward(p, nullptr, nullptr, nullptr) + shared_ws(ps) +
+         align_up((size_t)p->B * p->d * 2);
+}
+
+moe_status_t moe_forward_shared(const moe_problem_t* p, const moe_problem_t* ps, const void* x,
+                                const float* Wg, const float* bias, const void* wpacked,
+                                const void* wpacked_shared, void* y, moe_forward_out_t* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  st = check_shared(ps);
+  if (st != MOE_OK) return st;
+  if (ps->B != p->B || ps->d != p->d) return MOE_ERR_INVALID;
+  if (p->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->B > 0 && (!wpacked_shared || !a16(wpacked_shared))) return MOE_ERR_INVALID;
+  const size_t nf = carve_forward(p, out, nullptr, nullptr);
+  const size_t need = nf + shared_ws(ps) + align_up((size_t)p->B * p->d * 2);
+  if (p->B > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  SharedRun sh;
+  sh.ps = ps;
+  sh.wp = wpacked_shared;
+  sh.eo = p->B > 0 ? reinterpret_cast<int32_t*>(base + nf) : nullptr;
+  sh.H = p->B > 0 ? reinterpret_cast<uint16_t*>(base + nf + align_up(8)) : nullptr;
+  sh.S = p->B > 0 ? reinterpret_cast<uint16_t*>(base + nf + shared_ws(ps)) : nullptr;
+  return forward_chain(p, x, Wg, bias, wpacked, y, out, ws, nf, stream, &sh);
 }
 
 }  // extern "C"

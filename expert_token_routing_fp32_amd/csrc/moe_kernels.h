@@ -159,9 +159,18 @@ hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, in
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k,
                        int d, uint16_t* packed, hipStream_t s);
 
+// shared (optional): a shared expert's output rows [B][d] bf16, added with
+// weight 1
 hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
-                          int64_t kmax, hipStream_t s);
+                          int64_t kmax, hipStream_t s, const uint16_t* shared = nullptr);
+
+// The shared expert: one expert over every token's row of x (bf16) -- the
+// grouped GEMM with expert_offset = {0, B} (written into eo, 2 int32 of
+// device scratch), hidden activations in H [B][f].
+hipError_t launch_shared_ffn(const uint16_t* x, int64_t B, int d, int f, bool swiglu,
+                             const void* wp, uint16_t* H, int32_t* eo, uint16_t* out,
+                             hipStream_t s, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_unpack(const uint16_t* ret, const int32_t* dest, int64_t B, int k, int d,
                          int64_t kmax, uint16_t* out, hipStream_t s);

@@ -73,7 +73,8 @@ typedef enum {
   MOE_OP_DISPATCH = 0,
   MOE_OP_FFN = 1,
   MOE_OP_FORWARD = 2,
-  MOE_OP_ROUTING_STATS = 3
+  MOE_OP_ROUTING_STATS = 3,
+  MOE_OP_SHARED_FFN = 4
 } moe_op_t;
 
 /* The problem statement: B tokens of hidden size d, E experts, top-k routing
@@ -315,6 +316,55 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* x, const float* Wg,
                          const float* bias, const void* wpacked, void* y,
                          moe_forward_out_t* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* ---- shared expert --------------------------------------------------- */
+
+/* A shared expert ("Expert Parallelism", narrativegoldmine.com, "Major
+ * Variants and Families", shared expert routing: one or more experts
+ * process every token in addition to the routed experts, a dense path
+ * beside them).  It is described by its own problem ps: the same B and d as
+ * the routed layer, E = 1, k = 1, e_begin = 0, e_end = 1, its own f and
+ * act, x_dtype BF16 (other x types return MOE_ERR_UNSUPPORTED); its weights
+ * are packed with moe_pack_weights(ps, W1s, W3s, W2s, ...).
+ *
+ * moe_shared_ffn: out[t] = W2s . act(W1s . x[t]) for every token (bf16
+ * operands, fp32 accumulation, the hidden activation stored as bf16), on
+ * the expert GEMM of moe_expert_ffn with all B rows as one expert.
+ *   x       [B][d] bf16
+ *   wpacked moe_pack_weights(ps, ...) output
+ *   out     [B][d] bf16 out
+ *   ws      >= moe_workspace_bytes(ps, MOE_OP_SHARED_FFN), 16-byte aligned */
+moe_status_t moe_shared_ffn(const moe_problem_t* ps, const moe_bf16_t* x,
+                            const void* wpacked, moe_bf16_t* out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* moe_combine plus a shared expert's rows, added with weight 1 after the
+ * routed sum (and before the residual):
+ * y[t] = sum_j topk_w[t,j] ret[dest[t,j]] + shared_out[t] (+ x[t]).
+ *   shared_out [B][d] bf16 (moe_shared_ffn's out); the rest as moe_combine */
+moe_status_t moe_combine_shared(const moe_problem_t* p, const moe_bf16_t* ret,
+                                const int32_t* dest, const float* topk_w,
+                                const moe_bf16_t* shared_out,
+                                const void* x_residual, void* y,
+                                hipStream_t stream);
+
+/* Workspace of moe_forward_shared (SIZE_MAX if either problem is invalid). */
+size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p,
+                                          const moe_problem_t* ps);
+
+/* moe_forward with a shared expert: the routed layer of p, the shared
+ * expert of ps on every token (after the routed expert GEMMs, inside the
+ * same stage events 3 and 4), and the combine of moe_combine_shared.
+ * x_dtype must be BF16 for both problems; ps->B == p->B, ps->d == p->d.
+ *   wpacked_shared  moe_pack_weights(ps, ...) output
+ *   ws >= moe_forward_shared_workspace_bytes(p, ps), 16-byte aligned;
+ *   the other arguments as moe_forward. */
+moe_status_t moe_forward_shared(const moe_problem_t* p, const moe_problem_t* ps,
+                                const void* x, const float* Wg,
+                                const float* bias, const void* wpacked,
+                                const void* wpacked_shared, void* y,
+                                moe_forward_out_t* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -169,3 +169,29 @@ def test_calls_reject_before_launch(L, lib):
     out.summary = (1 << 20) + 4  # doubles need 8-byte alignment
     assert lib.moe_routing_stats(ctypes.byref(p), fake, fake, fake, ctypes.byref(out), fake,
                                  1 << 30, None) == L.MOE_ERR_INVALID
+
+
+def test_shared_expert_host_checks(L, lib):
+    """The shared expert's problem must be a single always-chosen expert on
+    bf16 activations; its workspace holds H [B][f] (checked without a GPU)."""
+    ps = _prob(L, E=1, k=1, c=1.0, n_ranks=1, e_begin=0, e_end=1, f=48)
+    n = lib.moe_workspace_bytes(ctypes.byref(ps), L.MOE_OP_SHARED_FFN)
+    assert n >= 64 * 48 * 2
+    p = _prob(L)
+    m = lib.moe_forward_shared_workspace_bytes(ctypes.byref(p), ctypes.byref(ps))
+    assert m >= lib.moe_workspace_bytes(ctypes.byref(p), L.MOE_OP_FORWARD) + n + 64 * 32 * 2
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.moe_shared_ffn(ctypes.byref(p), fake, fake, fake, fake, 1 << 30,
+                              None) == L.MOE_ERR_INVALID            # E != 1
+    f32 = _prob(L, E=1, k=1, c=1.0, n_ranks=1, e_begin=0, e_end=1, x_dtype=L.MOE_F32)
+    assert lib.moe_shared_ffn(ctypes.byref(f32), fake, fake, fake, fake, 1 << 30,
+                              None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_shared_ffn(ctypes.byref(ps), fake, fake, fake, None, 0,
+                              None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_shared_workspace_bytes(ctypes.byref(p), ctypes.byref(p)) == \
+        ctypes.c_size_t(-1).value
+    bad_b = _prob(L, B=65, E=1, k=1, c=1.0, n_ranks=1, e_begin=0, e_end=1)
+    assert lib.moe_forward_shared(ctypes.byref(p), ctypes.byref(bad_b), fake, fake, None, fake,
+                                  fake, fake, None, fake, 1 << 30, None) == L.MOE_ERR_INVALID
+    assert lib.moe_combine_shared(ctypes.byref(p), fake, fake, fake, None, None, fake,
+                                  None) == L.MOE_ERR_INVALID
