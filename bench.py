@@ -13,6 +13,7 @@ timed region.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times: the "
                          "kernel of known traffic that HBM byte counters are scaled by")
+    ap.add_argument("--shared-expert", type=int, default=0, metavar="F",
+                    help="add a shared expert of hidden size F (same activation) on every "
+                         "token: moe_forward_shared (bf16 workloads)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only time the matrix-core ceiling probe (libmoe_probe.so) with random "
                          "and with near-constant bf16 operands")
@@ -144,7 +148,7 @@ def measured_traffic(workload: str):
     return rec["expert_ffn_bytes"] if h.hexdigest()[:16] == rec["src_sha256_16"] else None
 
 
-def cpu_baseline(w, inp, budget_s: float) -> dict:
+def cpu_baseline(w, inp, budget_s: float, shared=None) -> dict:
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -156,7 +160,7 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
         t0 = time.perf_counter()
         oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"], k=w.k,
                        c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end,
-                       tau=w.tau)
+                       tau=w.tau, shared=shared)
         t_tot += time.perf_counter() - t0
         reps += 1
     return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
@@ -214,6 +218,28 @@ def main():
     wp = moe.pack_weights(p, W1, W3, W2)
     del W1, W2, W3
     ws = torch.empty(moe.workspace_bytes(p, "forward"), dtype=torch.uint8, device=dev)
+    shared = None
+    fs = args.shared_expert
+    if fs > 0:
+        if not bf16:
+            raise SystemExit("--shared-expert needs a bf16 workload")
+        # seeded bf16 weights of std 1/sqrt(fan_in), like the routed experts
+        rs = np.random.default_rng(w.seed + 1000)
+
+        def bw(shape, fan_in):
+            a = rs.normal(scale=fan_in ** -0.5, size=shape).astype(np.float32)
+            return d16(moe_synth.f32_to_bf16_bits(a))
+        S1 = bw((1, fs, w.d), w.d)
+        S3 = bw((1, fs, w.d), w.d) if w.act == "swiglu" else None
+        S2 = bw((1, w.d, fs), fs)
+        ps = moe.shared_problem(p, fs, w.act)
+        shared = (ps, moe.pack_weights(ps, S1, S3, S2))
+        shared_np = (S1.cpu().numpy().view(np.uint16)[0],
+                     None if S3 is None else S3.cpu().numpy().view(np.uint16)[0],
+                     S2.cpu().numpy().view(np.uint16)[0])
+        del S1, S2, S3
+        ws = torch.empty(moe.lib().moe_forward_shared_workspace_bytes(
+            ctypes.byref(p), ctypes.byref(ps)), dtype=torch.uint8, device=dev)
     y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
@@ -238,7 +264,7 @@ def main():
     def step(ev=None):
         if flush is not None:
             flush.fill_(1)
-        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev)
+        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev, shared=shared)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -261,11 +287,18 @@ def main():
     log(f"[bench] {sec_per_step * 1e3:.3f} ms/step; " +
         ", ".join(f"{k} {v * 1e6:.1f} us" for k, v in stage_s.items()))
 
-    _, o = moe.forward(p, x, Wg, bias, wp, outputs=True)
+    _, o = moe.forward(p, x, Wg, bias, wp, outputs=True, shared=shared)
     torch.cuda.synchronize()
     keep = o["keep"].cpu().numpy().astype(bool)
     eo = o["expert_offset"].cpu().numpy()
     alg = algorithmic(w, keep, eo)
+    if shared is not None:
+        # the shared expert on every token: its weights once, x read, its
+        # output rows written (FFN stage) and read again by the combine
+        nmat_s = 3 if w.act == "swiglu" else 2
+        alg["ffn_flop"] += 2.0 * w.B * w.d * fs * nmat_s
+        alg["ffn_bytes"] += 2.0 * w.d * fs * nmat_s + 4.0 * w.B * w.d
+        alg["combine_bytes"] += 2.0 * w.B * w.d
 
     # routing-health signals of the same batch (an optional call after the
     # forward, not part of the timed step): timed alone with events
@@ -295,7 +328,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = measured_traffic(w.name) if shared is None else None
     roof["kernel"] = "expert FFN: grouped_gemm_kernel GEMM1 (act) + GEMM2, one moe_expert_ffn call"
     roof["algorithmic_bytes"] = alg["ffn_bytes"]
     roof["algorithmic_flop"] = alg["ffn_flop"]
@@ -349,14 +382,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} d={w.d} E={w.E} top-{w.k} c={w.c} "
                                f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
-                               f"local experts [{w.e_begin},{w.e_end})",
+                               f"local experts [{w.e_begin},{w.e_end})"
+                               + (f" + shared expert f={fs}" if shared is not None else ""),
                    "global_batch": w.B, "cache": "cold" if args.cold else "warm"},
         "roofline": roof,
         "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds,
+                                           shared_np if shared is not None else None)
     print(json.dumps(out), flush=True)
 
 
