@@ -72,7 +72,8 @@ __all__ = [
     "capacity", "bf16_bits_to_f64", "f32_to_bf16_bits_rne", "gate_logits",
     "softmax", "route", "assign_slots", "layout", "pack", "gelu", "silu",
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
-    "expert_capacities", "routing_stats", "shared_ffn",
+    "expert_capacities", "routing_stats", "shared_ffn", "router_probs", "expert_choice",
+    "expert_choice_combine", "forward_expert_choice",
 ]
 
 
@@ -527,3 +528,98 @@ def routing_stats(logits: np.ndarray, expert_load: np.ndarray, expert_count: np.
     util = kept / C if C > 0 else np.zeros(E)
     return dict(prob_mean=P, token_frac=f, aux_loss=float((f * P).sum()), entropy=ent,
                 load_entropy=float(-alog.sum()), utilization=util, dropped=n - kept)
+
+
+# ----------------------------------------------------------------------------
+# expert-choice routing (a variant)
+# ----------------------------------------------------------------------------
+def router_probs(logits: np.ndarray, tau: float = 1.0) -> np.ndarray:
+    """The router's probabilities p_t = softmax(g_t / tau), rounded once to
+    float32 [B, E]: the scores expert-choice routing ranks tokens by.  The
+    choice below is decided on these float32 values (the precision the GPU
+    holds them in), so both sides rank the same numbers.  Pins: as
+    ``softmax``."""
+    return softmax(logits, tau).astype(np.float32)
+
+
+def expert_choice(probs: np.ndarray, C: int):
+    """Every expert chooses its top-C tokens of the batch by score.
+
+    [EP-notes] "Major Variants and Families", expert choice routing: each
+    expert picks its top-C tokens from the batch instead of each token
+    picking experts, so every expert processes exactly C tokens and a token
+    may be chosen by any number of experts, including none.  Readings: the
+    score of (t, e) is the router probability p_te (float32); C is the
+    problem's capacity, at most B; among equal scores the lower token index
+    wins; an expert's rows are packed in token order, experts one after the
+    other; the weight of a chosen pair is p_te.
+
+    Returns sel int32 [B, E] (packed row of (t, e), or -1), expert_offset
+    int32 [E + 1] (= e * min(C, B)), pack_src int32 [E * min(C, B)] (token of
+    each row) and pack_w float32 (p_te of each row).  Uses one library
+    primitive per expert, a lexicographic sort by (-score, token).  Pins: a
+    rank-counting brute force, exact balance, ties, C >= B (every expert
+    takes every token) (test_oracle_expert_choice)."""
+    p = np.asarray(probs, dtype=np.float32)
+    B, E = p.shape
+    Ce = min(int(C), B)
+    sel = np.full((B, E), -1, dtype=np.int32)
+    pack_src = np.empty(E * Ce, dtype=np.int32)
+    pack_w = np.empty(E * Ce, dtype=np.float32)
+    t_idx = np.arange(B)
+    for e in range(E):
+        order = np.lexsort((t_idx, -p[:, e].astype(np.float64)))  # score desc, token asc
+        chosen = np.sort(order[:Ce])
+        rows = e * Ce + np.arange(Ce)
+        sel[chosen, e] = rows
+        pack_src[rows] = chosen
+        pack_w[rows] = p[chosen, e]
+    expert_offset = (np.arange(E + 1) * Ce).astype(np.int32)
+    return sel, expert_offset, pack_src, pack_w
+
+
+def expert_choice_combine(ret: np.ndarray, sel: np.ndarray, pack_w: np.ndarray,
+                          x_residual: Optional[np.ndarray] = None,
+                          tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[t] = sum over experts e that chose t, in expert order, of
+    p_te * ret[row(t, e)] (+ x[t]), float64; a token no expert chose gets 0
+    (plus the residual) -- [EP-notes] "Components and Architecture", expert
+    combine weighted by the gating probabilities.  Pin: with C >= B it is the
+    dense soft mixture sum_e p_te E_e(x_t) (test_oracle_expert_choice)."""
+    B, E = sel.shape
+    tt = np.arange(B) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    acc = np.zeros((tt.size, ret.shape[1]))
+    w = np.asarray(pack_w, dtype=np.float32).astype(np.float64)
+    for e in range(E):
+        r = sel[tt, e].astype(np.int64)
+        m = r >= 0
+        acc[m] += w[r[m]][:, None] * ret[r[m]]
+    if x_residual is not None:
+        acc += _x_values(x_residual[tt])
+    return acc
+
+
+def forward_expert_choice(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
+                          tau: float = 1.0, C: Optional[int] = None,
+                          add_residual: bool = False,
+                          probs: Optional[np.ndarray] = None) -> dict:
+    """The layer with expert-choice routing: gate, router probabilities,
+    every expert's top-C tokens, pack, expert FFN, weighted combine.  C
+    defaults to the problem's capacity ceil((B*k/E)*c) (k is the average
+    number of experts per token).  ``probs`` may be given (the GPU's float32
+    probabilities) so that the choice is taken on the same numbers."""
+    B = x.shape[0]
+    logits = gate_logits(x, Wg, bias)
+    E = logits.shape[1]
+    if probs is None:
+        probs = router_probs(logits, tau)
+    if C is None:
+        C = capacity(B, k, E, c)
+    sel, eo, src, pw = expert_choice(probs, C)
+    out = dict(logits=logits, probs=probs, C=C, sel=sel, expert_offset=eo, pack_src=src,
+               pack_w=pw, packed=pack(x, src))
+    if W1 is not None:
+        ret = expert_ffn(x, src, eo, 0, E, W1, W2, W3, act)
+        out["ret"] = ret
+        out["y"] = expert_choice_combine(ret, sel, pw, x if add_residual else None)
+    return out
