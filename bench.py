@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times: the "
                          "kernel of known traffic that HBM byte counters are scaled by")
+    ap.add_argument("--routing", default="token", choices=["token", "expert_choice"],
+                    help="expert_choice: every expert picks its top-C tokens "
+                         "(moe_forward_expert_choice; all experts local)")
     ap.add_argument("--shared-expert", type=int, default=0, metavar="F",
                     help="add a shared expert of hidden size F (same activation) on every "
                          "token: moe_forward_shared (bf16 workloads)")
@@ -129,6 +132,29 @@ def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
     )
 
 
+def algorithmic_ec(w, sel_t: np.ndarray, R: int) -> dict:
+    """The same accounting for expert-choice routing (R = E * min(C, B)
+    rows): the router writes the probabilities and reads them once per
+    choice pass; the pack reads each chosen token once and writes R rows;
+    the combine reads R rows, the token's sel entries and writes y."""
+    B, d, E, f = w.B, w.d, w.E, w.f
+    sx = 2 if w.x_dtype == "bf16" else 4
+    nmat = 3 if w.act == "swiglu" else 2
+    t_act = int((sel_t >= 0).any(axis=0).sum())
+    active = int((sel_t >= 0).any(axis=1).sum())
+    return dict(
+        gate_flop=2.0 * B * d * E,
+        gate_bytes=B * d * sx + 4.0 * d * E + 4.0 * B * E,
+        route_bytes=B * E * (4.0 + 4.0 + 4.0) + R * 8.0,
+        slot_bytes=0.0,
+        pack_bytes=t_act * d * sx + 2.0 * d * R,
+        ffn_flop=2.0 * d * f * nmat * R,
+        ffn_bytes=active * 2.0 * d * f * nmat + 4.0 * d * R,
+        combine_bytes=2.0 * d * R + B * d * sx + 4.0 * B * E,
+        K=R, Kloc=R, t_act=t_act, active_local=active,
+    )
+
+
 def measured_traffic(workload: str):
     """HBM bytes per expert-FFN call from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (scaled by a plain copy's reading), or None when there is
@@ -148,7 +174,7 @@ def measured_traffic(workload: str):
     return rec["expert_ffn_bytes"] if h.hexdigest()[:16] == rec["src_sha256_16"] else None
 
 
-def cpu_baseline(w, inp, budget_s: float, shared=None) -> dict:
+def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False) -> dict:
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -158,9 +184,13 @@ def cpu_baseline(w, inp, budget_s: float, shared=None) -> dict:
     reps, t_tot = 0, 0.0
     while reps == 0 or (t_tot < budget_s and reps < 20):
         t0 = time.perf_counter()
-        oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"], k=w.k,
-                       c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end,
-                       tau=w.tau, shared=shared)
+        if ec:
+            oracle.forward_expert_choice(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"],
+                                         inp["W2"], k=w.k, c=w.c, act=w.act, tau=w.tau)
+        else:
+            oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+                           k=w.k, c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin,
+                           e_end=w.e_end, tau=w.tau, shared=shared)
         t_tot += time.perf_counter() - t0
         reps += 1
     return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
@@ -218,6 +248,15 @@ def main():
     wp = moe.pack_weights(p, W1, W3, W2)
     del W1, W2, W3
     ws = torch.empty(moe.workspace_bytes(p, "forward"), dtype=torch.uint8, device=dev)
+    ec = args.routing == "expert_choice"
+    if ec:
+        if w.e_begin != 0 or w.e_end != w.E:
+            raise SystemExit("--routing expert_choice needs every expert local "
+                             f"({w.name} runs experts [{w.e_begin},{w.e_end}) of {w.E})")
+        if args.shared_expert:
+            raise SystemExit("--shared-expert goes with token-choice routing")
+        ws = torch.empty(moe.workspace_bytes(p, "forward_expert_choice"), dtype=torch.uint8,
+                         device=dev)
     shared = None
     fs = args.shared_expert
     if fs > 0:
@@ -264,7 +303,10 @@ def main():
     def step(ev=None):
         if flush is not None:
             flush.fill_(1)
-        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev, shared=shared)
+        if ec:
+            moe.forward_expert_choice(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev)
+        else:
+            moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=ev, shared=shared)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -287,11 +329,16 @@ def main():
     log(f"[bench] {sec_per_step * 1e3:.3f} ms/step; " +
         ", ".join(f"{k} {v * 1e6:.1f} us" for k, v in stage_s.items()))
 
-    _, o = moe.forward(p, x, Wg, bias, wp, outputs=True, shared=shared)
-    torch.cuda.synchronize()
-    keep = o["keep"].cpu().numpy().astype(bool)
-    eo = o["expert_offset"].cpu().numpy()
-    alg = algorithmic(w, keep, eo)
+    if ec:
+        _, o = moe.forward_expert_choice(p, x, Wg, bias, wp, outputs=True)
+        torch.cuda.synchronize()
+        alg = algorithmic_ec(w, o["sel_t"].cpu().numpy(), moe.expert_choice_rows(p))
+    else:
+        _, o = moe.forward(p, x, Wg, bias, wp, outputs=True, shared=shared)
+        torch.cuda.synchronize()
+        keep = o["keep"].cpu().numpy().astype(bool)
+        eo = o["expert_offset"].cpu().numpy()
+        alg = algorithmic(w, keep, eo)
     if shared is not None:
         # the shared expert on every token: its weights once, x read, its
         # output rows written (FFN stage) and read again by the combine
@@ -302,21 +349,33 @@ def main():
 
     # routing-health signals of the same batch (an optional call after the
     # forward, not part of the timed step): timed alone with events
-    ws_stats = torch.empty(max(moe.workspace_bytes(p, "routing_stats"), 1), dtype=torch.uint8,
-                           device=dev)
-    for _ in range(3):
-        hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"], ws=ws_stats)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
-    e0.record()
-    for _ in range(reps):
-        hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"], ws=ws_stats)
-    e1.record()
-    torch.cuda.synchronize()
-    t_stats = e0.elapsed_time(e1) / reps * 1e-3
-    hsum = hs["summary"].cpu().numpy()
-    # algorithmic bytes: the logits once, the counts, the per-expert outputs
-    stats_bytes = w.B * w.E * 4 + w.E * (2 * 4 + 4 * 4) + 5 * 8
+    health = {}
+    if not ec:
+        ws_stats = torch.empty(max(moe.workspace_bytes(p, "routing_stats"), 1),
+                               dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"],
+                                   ws=ws_stats)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"],
+                                   ws=ws_stats)
+        e1.record()
+        torch.cuda.synchronize()
+        t_stats = e0.elapsed_time(e1) / reps * 1e-3
+        hsum = hs["summary"].cpu().numpy()
+        # algorithmic bytes: the logits once, the counts, the per-expert outputs
+        stats_bytes = w.B * w.E * 4 + w.E * (2 * 4 + 4 * 4) + 5 * 8
+        health = {
+            "routing_stats_us": round(t_stats * 1e6, 2),
+            "routing_stats_hbm_frac": round(stats_bytes / t_stats / 1e9 / HBM_PEAK_GBS, 4),
+            "routing_health": {"aux_loss": round(float(hsum[0]), 6),
+                               "entropy_nats": round(float(hsum[1]), 5),
+                               "load_entropy_nats": round(float(hsum[2]), 5),
+                               "dropped": int(hsum[3]), "kept": int(hsum[4])},
+        }
 
     ffn_gbs = alg["ffn_bytes"] / t_ffn_live / 1e9
     ffn_tflops = alg["ffn_flop"] / t_ffn_live / 1e12
@@ -328,7 +387,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(w.name) if shared is None else None
+    roof["traffic"] = measured_traffic(w.name) if shared is None and not ec else None
     roof["kernel"] = "expert FFN: grouped_gemm_kernel GEMM1 (act) + GEMM2, one moe_expert_ffn call"
     roof["algorithmic_bytes"] = alg["ffn_bytes"]
     roof["algorithmic_flop"] = alg["ffn_flop"]
@@ -358,14 +417,14 @@ def main():
         "expert_gemm_hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
         "route_pack_combine_gbs": round(rpc_bytes / rpc_t / 1e9, 1),
         "route_pack_combine_hbm_frac": round(rpc_bytes / rpc_t / 1e9 / HBM_PEAK_GBS, 4),
-        "kept": alg["K"], "kept_local": alg["Kloc"], "dropped": int(w.B * w.k - alg["K"]),
-        "routing_stats_us": round(t_stats * 1e6, 2),
-        "routing_stats_hbm_frac": round(stats_bytes / t_stats / 1e9 / HBM_PEAK_GBS, 4),
-        "routing_health": {"aux_loss": round(float(hsum[0]), 6),
-                           "entropy_nats": round(float(hsum[1]), 5),
-                           "load_entropy_nats": round(float(hsum[2]), 5),
-                           "dropped": int(hsum[3]), "kept": int(hsum[4])},
+        "kept": alg["K"], "kept_local": alg["Kloc"],
+        "dropped": None if ec else int(w.B * w.k - alg["K"]),
+        **health,
     }
+    if ec:
+        breakdown["expert_choice"] = {"rows": alg["K"], "tokens_chosen": alg["t_act"],
+                                      "route_us_is": "router probabilities + the choice",
+                                      "dispatch_us_is": "gather pack"}
 
     out = {
         "metric": METRIC,
@@ -383,7 +442,8 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} d={w.d} E={w.E} top-{w.k} c={w.c} "
                                f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
                                f"local experts [{w.e_begin},{w.e_end})"
-                               + (f" + shared expert f={fs}" if shared is not None else ""),
+                               + (f" + shared expert f={fs}" if shared is not None else "")
+                               + (", expert-choice routing" if ec else ""),
                    "global_batch": w.B, "cache": "cold" if args.cold else "warm"},
         "roofline": roof,
         "breakdown": breakdown,
@@ -391,7 +451,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds,
-                                           shared_np if shared is not None else None)
+                                           shared_np if shared is not None else None, ec)
     print(json.dumps(out), flush=True)
 
 

@@ -24,7 +24,9 @@ from ._lib import MoEError, Problem  # noqa: F401
 __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
            "workspace_bytes", "weights_bytes", "pack_weights", "gate", "route", "dispatch",
            "expert_ffn", "combine", "unpack", "forward", "routing_stats", "shared_problem",
-           "shared_ffn", "MoEError", "Problem", "lib"]
+           "shared_ffn", "router_probs", "expert_choice", "expert_choice_pack",
+           "expert_choice_combine", "forward_expert_choice", "expert_choice_rows", "MoEError",
+           "Problem", "lib"]
 
 
 def lib():
@@ -86,7 +88,8 @@ def shared_problem(p: Problem, f: int, act: str = "swiglu") -> Problem:
 
 def workspace_bytes(p: Problem, op: str = "forward") -> int:
     o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD,
-         "routing_stats": L.MOE_OP_ROUTING_STATS, "shared_ffn": L.MOE_OP_SHARED_FFN}[op]
+         "routing_stats": L.MOE_OP_ROUTING_STATS, "shared_ffn": L.MOE_OP_SHARED_FFN,
+         "forward_expert_choice": L.MOE_OP_FORWARD_EXPERT_CHOICE}[op]
     return lib().moe_workspace_bytes(ctypes.byref(p), o)
 
 
@@ -380,4 +383,115 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
     L.check(lib().moe_forward(ctypes.byref(p), _p(x), _p(Wg), _p(bias), _p(wpacked), _p(y),
                               ctypes.byref(outp) if outp is not None else None, _p(ws),
                               ws.numel(), _stream()), "moe_forward")
+    return (y, o) if outputs else y
+
+
+# ---------------------------------------------------------------------------
+# expert-choice routing: every expert picks its top-C tokens of the batch
+def expert_choice_rows(p: Problem) -> int:
+    return lib().moe_expert_choice_rows(ctypes.byref(p))
+
+
+def router_probs(p: Problem, logits, probs_t=None):
+    """p_te = softmax(logits_t / tau), transposed: [E, B] float32."""
+    _check(p)
+    B, E = p.B, p.E
+    _need(logits, "logits", B * E, 4)
+    if probs_t is None:
+        probs_t = torch.empty((E, B), dtype=torch.float32, device=logits.device)
+    _need(probs_t, "probs_t", B * E, 4)
+    L.check(lib().moe_router_probs(ctypes.byref(p), _p(logits), _p(probs_t), _stream()),
+            "moe_router_probs")
+    return probs_t
+
+
+def expert_choice(p: Problem, probs_t) -> dict:
+    """Every expert's top-min(C, B) tokens: sel_t [E, B], expert_offset [E+1],
+    pack_src [R], pack_w [R] (R = expert_choice_rows(p))."""
+    _check(p)
+    B, E = p.B, p.E
+    dev = probs_t.device
+    _need(probs_t, "probs_t", B * E, 4)
+    R = expert_choice_rows(p)
+    o = dict(sel_t=torch.empty((E, B), dtype=torch.int32, device=dev),
+             expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+             pack_src=torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+             pack_w=torch.empty(max(R, 1), dtype=torch.float32, device=dev))
+    L.check(lib().moe_expert_choice(ctypes.byref(p), _p(probs_t), _p(o["sel_t"]),
+                                    _p(o["expert_offset"]), _p(o["pack_src"]), _p(o["pack_w"]),
+                                    _stream()), "moe_expert_choice")
+    return o
+
+
+def expert_choice_pack(p: Problem, x, pack_src, packed=None):
+    _check(p)
+    R = expert_choice_rows(p)
+    _need(x, "x", p.B * p.d, _xsize(p))
+    if packed is None:
+        packed = torch.empty((max(R, 1), p.d), dtype=torch.int16, device=x.device)
+    _need(packed, "packed", R * p.d, 2)
+    L.check(lib().moe_expert_choice_pack(ctypes.byref(p), _p(x), _p(pack_src), _p(packed),
+                                         _stream()), "moe_expert_choice_pack")
+    return packed
+
+
+def expert_choice_combine(p: Problem, ret, sel_t, pack_w, x_residual=None, y=None):
+    _check(p)
+    B, d = p.B, p.d
+    _need(sel_t, "sel_t", B * p.E, 4)
+    if y is None:
+        y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
+                        device=sel_t.device)
+    _need(y, "y", B * d, _xsize(p))
+    L.check(lib().moe_expert_choice_combine(ctypes.byref(p), _p(ret), _p(sel_t), _p(pack_w),
+                                            _p(x_residual if p.add_residual else None), _p(y),
+                                            _stream()), "moe_expert_choice_combine")
+    return y
+
+
+_EC_FIELDS = ("logits", "probs_t", "sel_t", "expert_offset", "pack_src", "pack_w", "packed")
+
+
+def forward_expert_choice(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False,
+                          ws=None, stage_events=None):
+    """The layer with expert-choice routing (moe_forward_expert_choice);
+    ``stage_events`` as in ``forward``."""
+    _check(p)
+    B, d, E = p.B, p.d, p.E
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
+                        device=dev)
+    o = None
+    outp = None
+    if outputs:
+        R = max(expert_choice_rows(p), 1)
+        o = dict(logits=torch.empty((B, E), dtype=torch.float32, device=dev),
+                 probs_t=torch.empty((E, B), dtype=torch.float32, device=dev),
+                 sel_t=torch.empty((E, B), dtype=torch.int32, device=dev),
+                 expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                 pack_src=torch.empty(R, dtype=torch.int32, device=dev),
+                 pack_w=torch.empty(R, dtype=torch.float32, device=dev),
+                 packed=torch.empty((R, d), dtype=torch.int16, device=dev))
+        outp = L.ExpertChoiceOut(**{n: o[n].data_ptr() for n in _EC_FIELDS})
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        if outp is None:
+            outp = L.ExpertChoiceOut()
+        for i, ev in enumerate(stage_events):
+            if ev is None:
+                continue
+            if ev.cuda_event == 0:
+                ev.record()
+            outp.events[i] = ev.cuda_event
+    n = workspace_bytes(p, "forward_expert_choice")
+    if ws is None:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", n, 1)
+    L.check(lib().moe_forward_expert_choice(ctypes.byref(p), _p(x), _p(Wg), _p(bias),
+                                            _p(wpacked), _p(y),
+                                            ctypes.byref(outp) if outp is not None else None,
+                                            _p(ws), ws.numel(), _stream()),
+            "moe_forward_expert_choice")
     return (y, o) if outputs else y

@@ -12,7 +12,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
-MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS, MOE_OP_SHARED_FFN = range(5)
+(MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS, MOE_OP_SHARED_FFN,
+ MOE_OP_FORWARD_EXPERT_CHOICE) = range(6)
 
 
 class Problem(ctypes.Structure):
@@ -51,6 +52,13 @@ class ForwardOut(ctypes.Structure):
         ("events", ctypes.c_void_p * 6)]
 
 
+class ExpertChoiceOut(ctypes.Structure):
+    """moe_expert_choice_out_t: device pointers or NULL."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "probs_t", "sel_t", "expert_offset", "pack_src", "pack_w", "packed")] + [
+        ("events", ctypes.c_void_p * 6)]
+
+
 class MoEError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -85,6 +93,14 @@ _SIGS = {
     "moe_forward_shared_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
     "moe_forward_shared": (ctypes.c_int, [_P, _P, _V, _V, _V, _V, _V, _V,
                                           ctypes.POINTER(ForwardOut), _V, ctypes.c_size_t, _V]),
+    "moe_expert_choice_rows": (ctypes.c_int64, [_P]),
+    "moe_router_probs": (ctypes.c_int, [_P, _V, _V, _V]),
+    "moe_expert_choice": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
+    "moe_expert_choice_pack": (ctypes.c_int, [_P, _V, _V, _V, _V]),
+    "moe_expert_choice_combine": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
+    "moe_forward_expert_choice": (ctypes.c_int, [_P, _V, _V, _V, _V, _V,
+                                                 ctypes.POINTER(ExpertChoiceOut), _V,
+                                                 ctypes.c_size_t, _V]),
 }
 
 _lib = None

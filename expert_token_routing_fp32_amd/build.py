@@ -23,6 +23,7 @@ PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 PROBE_SOURCES = ["probe_mfma.hip"]
 
 SOURCES = ["moe_api.hip", "gate.hip", "route.hip", "dispatch.hip", "combine.hip", "health.hip",
+           "choice.hip",
            "expert_gemm.hip"]
 
 # packed-fp32 VALU forms are disabled: ordinary fp32 code only

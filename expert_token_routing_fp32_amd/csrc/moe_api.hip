@@ -54,6 +54,28 @@ int64_t kloc_of(const moe_problem_t* p) {
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 size_t ffn_ws(const moe_problem_t* p) { return align_up((size_t)kloc_of(p) * p->f * 2); }
+// rows of an expert-choice layout: E * min(C, B)
+int64_t ec_rows(const moe_problem_t* p) {
+  const int64_t C = capacity_of(p);
+  return (int64_t)p->E * (C < p->B ? C : p->B);
+}
+
+struct EcBufs {
+  float* logits;
+  float* probs_t;
+  int32_t* sel_t;
+  int32_t* eo;
+  int32_t* pack_src;
+  float* pack_w;
+  uint16_t* packed;
+  uint16_t* H;
+  void* wsplit;
+};
+
+// workspace of moe_forward_expert_choice: fields the caller did not supply,
+// H [R][f], the router's split weight copy when the gate uses one
+size_t carve_ec(const moe_problem_t* p, const moe_expert_choice_out_t* o, void* ws, EcBufs* b);
+
 // scratch of a shared expert (moe_shared_ffn): expert_offset {0, B} in one
 // aligned slot, then H [B][f] bf16
 size_t shared_ws(const moe_problem_t* ps) {
@@ -119,6 +141,29 @@ size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* w
   return c.off;
 }
 
+size_t carve_ec(const moe_problem_t* p, const moe_expert_choice_out_t* o, void* ws, EcBufs* b) {
+  moe_expert_choice_out_t none;
+  std::memset(&none, 0, sizeof(none));
+  if (!o) o = &none;
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  const size_t BE = (size_t)p->B * p->E, R = (size_t)ec_rows(p);
+  EcBufs t;
+  t.logits = c.take(o->logits, BE * 4);
+  t.probs_t = c.take(o->probs_t, BE * 4);
+  t.sel_t = c.take(o->sel_t, BE * 4);
+  t.eo = c.take(o->expert_offset, (size_t)(p->E + 1) * 4);
+  t.pack_src = c.take(o->pack_src, R * 4);
+  t.pack_w = c.take(o->pack_w, R * 4);
+  t.packed = c.take(reinterpret_cast<uint16_t*>(o->packed), R * p->d * 2);
+  t.H = c.take<uint16_t>(nullptr, R * p->f * 2);
+  t.wsplit = moek::gate_use_split(p->x_dtype == MOE_BF16, p->B, p->d, p->E)
+                 ? c.take<char>(nullptr, moek::gate_split_bytes(p->d, p->E))
+                 : nullptr;
+  if (b) *b = t;
+  return c.off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,6 +218,8 @@ size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op) {
       return moek::stats_ws_bytes(p->B, p->E);
     case MOE_OP_SHARED_FFN:
       return shared_ws(p);
+    case MOE_OP_FORWARD_EXPERT_CHOICE:
+      return carve_ec(p, nullptr, nullptr, nullptr);
   }
   return SIZE_MAX;
 }
@@ -473,6 +520,114 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, const moe_problem_t* ps,
   sh.H = p->B > 0 ? reinterpret_cast<uint16_t*>(base + nf + align_up(8)) : nullptr;
   sh.S = p->B > 0 ? reinterpret_cast<uint16_t*>(base + nf + shared_ws(ps)) : nullptr;
   return forward_chain(p, x, Wg, bias, wpacked, y, out, ws, nf, stream, &sh);
+}
+
+int64_t moe_expert_choice_rows(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return -1;
+  return ec_rows(p);
+}
+
+static moe_status_t check_ec(const moe_problem_t* p) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->e_begin != 0 || p->e_end != p->E) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t moe_router_probs(const moe_problem_t* p, const float* logits, float* probs_t,
+                              hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!logits || !probs_t || !a4(logits) || !a4(probs_t))) return MOE_ERR_INVALID;
+  return hip_status(moek::launch_router_probs(logits, p->B, p->E, p->tau, probs_t, stream));
+}
+
+moe_status_t moe_expert_choice(const moe_problem_t* p, const float* probs_t, int32_t* sel_t,
+                               int32_t* expert_offset, int32_t* pack_src, float* pack_w,
+                               hipStream_t stream) {
+  moe_status_t st = check_ec(p);
+  if (st != MOE_OK) return st;
+  if (!expert_offset || !a4(expert_offset)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!probs_t || !sel_t || !a4(probs_t) || !a4(sel_t))) return MOE_ERR_INVALID;
+  if (ec_rows(p) > 0 && (!pack_src || !pack_w || !a4(pack_src) || !a4(pack_w)))
+    return MOE_ERR_INVALID;
+  const int64_t C = capacity_of(p);
+  const int Ce = (int)(C < p->B ? C : p->B);
+  return hip_status(moek::launch_expert_choice(probs_t, p->B, p->E, Ce, sel_t, expert_offset,
+                                               pack_src, pack_w, stream));
+}
+
+moe_status_t moe_expert_choice_pack(const moe_problem_t* p, const void* x,
+                                    const int32_t* pack_src, moe_bf16_t* packed,
+                                    hipStream_t stream) {
+  moe_status_t st = check_ec(p);
+  if (st != MOE_OK) return st;
+  const int64_t R = ec_rows(p);
+  if (R > 0 && (!x || !pack_src || !packed || !a16(x) || !a16(packed))) return MOE_ERR_INVALID;
+  return hip_status(
+      moek::launch_ec_pack(x, p->x_dtype == MOE_BF16, pack_src, R, p->d, packed, stream));
+}
+
+moe_status_t moe_expert_choice_combine(const moe_problem_t* p, const moe_bf16_t* ret,
+                                       const int32_t* sel_t, const float* pack_w,
+                                       const void* x_residual, void* y, hipStream_t stream) {
+  moe_status_t st = check_ec(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!sel_t || !y || !a16(y))) return MOE_ERR_INVALID;
+  if (p->B > 0 && ec_rows(p) > 0 && (!ret || !pack_w || !a16(ret))) return MOE_ERR_INVALID;
+  if (p->B > 0 && p->add_residual && (!x_residual || !a16(x_residual))) return MOE_ERR_INVALID;
+  return hip_status(moek::launch_ec_combine(ret, sel_t, pack_w,
+                                            p->add_residual ? x_residual : nullptr,
+                                            p->x_dtype == MOE_BF16, y, p->B, p->E, p->d, stream));
+}
+
+moe_status_t moe_forward_expert_choice(const moe_problem_t* p, const void* x, const float* Wg,
+                                       const float* bias, const void* wpacked, void* y,
+                                       moe_expert_choice_out_t* out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  moe_status_t st = check_ec(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!x || !Wg || !y || !wpacked)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a16(y) || !a4(Wg) || (bias && !a4(bias)) || !a16(wpacked)))
+    return MOE_ERR_INVALID;
+  if (out && out->packed && !a16(out->packed)) return MOE_ERR_INVALID;
+  const size_t need = carve_ec(p, out, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  EcBufs b;
+  carve_ec(p, out, ws, &b);
+  const bool xb = p->x_dtype == MOE_BF16;
+  const int64_t C = capacity_of(p);
+  const int Ce = (int)(C < p->B ? C : p->B);
+  const int64_t R = ec_rows(p);
+  hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (e == hipSuccess && out && out->events[i]) e = hipEventRecord(out->events[i], stream);
+  };
+  mark(0);
+  if (e == hipSuccess)
+    e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, b.wsplit, stream);
+  mark(1);
+  if (e == hipSuccess)
+    e = moek::launch_router_probs(b.logits, p->B, p->E, p->tau, b.probs_t, stream);
+  if (e == hipSuccess)
+    e = moek::launch_expert_choice(b.probs_t, p->B, p->E, Ce, b.sel_t, b.eo, b.pack_src,
+                                   b.pack_w, stream);
+  mark(2);
+  if (e == hipSuccess) e = moek::launch_ec_pack(x, xb, b.pack_src, R, p->d, b.packed, stream);
+  if (R > 0) {
+    if (e == hipSuccess)
+      e = moek::launch_expert_ffn(b.packed, b.eo, 0, p->E, Ce, Ce, p->d, p->f,
+                                  p->act == MOE_SWIGLU, wpacked, b.H, b.packed, stream,
+                                  out ? out->events[3] : nullptr, out ? out->events[4] : nullptr);
+  } else {
+    mark(3);
+    mark(4);
+  }
+  if (e == hipSuccess)
+    e = moek::launch_ec_combine(b.packed, b.sel_t, b.pack_w, p->add_residual ? x : nullptr, xb,
+                                y, p->B, p->E, p->d, stream);
+  mark(5);
+  return hip_status(e);
 }
 
 }  // extern "C"

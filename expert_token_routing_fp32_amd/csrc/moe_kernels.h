@@ -149,6 +149,21 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
                         int32_t* expert_count, int32_t* expert_offset, int32_t* rank_offset,
                         int32_t* pack_src, int32_t* ws_hist, hipStream_t s);
 
+// expert-choice routing (choice.hip): router probabilities transposed
+// [E][B]; every expert's top-Ce tokens (sel_t [E][B]: packed row or -1;
+// rows e*Ce.. in token order, pack_src / pack_w per row; expert_offset
+// e*Ce); the gather pack; the combine over the experts that chose a token
+hipError_t launch_router_probs(const float* logits, int64_t B, int E, float tau, float* probs_t,
+                               hipStream_t s);
+hipError_t launch_expert_choice(const float* probs_t, int64_t B, int E, int Ce, int32_t* sel_t,
+                                int32_t* expert_offset, int32_t* pack_src, float* pack_w,
+                                hipStream_t s);
+hipError_t launch_ec_pack(const void* x, bool x_bf16, const int32_t* pack_src, int64_t rows,
+                          int d, uint16_t* packed, hipStream_t s);
+hipError_t launch_ec_combine(const uint16_t* ret, const int32_t* sel_t, const float* pack_w,
+                             const void* x_res, bool x_bf16, void* y, int64_t B, int E, int d,
+                             hipStream_t s);
+
 // routing-health signals (health.hip): workspace bytes and the two launches
 size_t stats_ws_bytes(int64_t B, int E);
 hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, int C, float tau,

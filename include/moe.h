@@ -74,7 +74,8 @@ typedef enum {
   MOE_OP_FFN = 1,
   MOE_OP_FORWARD = 2,
   MOE_OP_ROUTING_STATS = 3,
-  MOE_OP_SHARED_FFN = 4
+  MOE_OP_SHARED_FFN = 4,
+  MOE_OP_FORWARD_EXPERT_CHOICE = 5
 } moe_op_t;
 
 /* The problem statement: B tokens of hidden size d, E experts, top-k routing
@@ -365,6 +366,87 @@ moe_status_t moe_forward_shared(const moe_problem_t* p, const moe_problem_t* ps,
                                 const void* wpacked_shared, void* y,
                                 moe_forward_out_t* out, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
+
+/* ---- expert-choice routing -------------------------------------------- */
+
+/* Expert-choice routing ("Expert Parallelism", narrativegoldmine.com,
+ * "Major Variants and Families", expert choice routing): instead of each
+ * token choosing k experts, every expert chooses its top-C tokens of the
+ * batch, so every expert processes exactly Ce = min(C, B) tokens and a token
+ * may be chosen by any number of experts (including none).  C is the
+ * problem's capacity ceil((B*k/E)*c), k read as the average number of
+ * experts per token.  The score of (t, e) is the router probability
+ * p_te = softmax(logits_t / tau)_e in fp32; among equal scores the lower
+ * token wins; expert e's rows are e*Ce .. e*Ce + Ce - 1, in token order; the
+ * weight of a chosen pair is p_te.  All experts must be local
+ * (e_begin = 0, e_end = E; otherwise MOE_ERR_UNSUPPORTED).  R = E * Ce rows. */
+
+/* R = E * min(C, B), the rows of an expert-choice layout; -1 if invalid. */
+int64_t moe_expert_choice_rows(const moe_problem_t* p);
+
+/* probs_t [E][B] float32 out: p_te, transposed (one expert's scores
+ * contiguous).  logits [B][E] float32. */
+moe_status_t moe_router_probs(const moe_problem_t* p, const float* logits,
+                              float* probs_t, hipStream_t stream);
+
+/* Every expert's top-Ce tokens from probs_t [E][B]:
+ *   sel_t         [E][B] int32 out: packed row of (t, e), or -1
+ *   expert_offset [E+1]  int32 out: e * Ce
+ *   pack_src      [R]    int32 out: token of each row
+ *   pack_w        [R]    float32 out: p_te of each row
+ * Exact (a radix select on the fp32 bit patterns and an ordered pass). */
+moe_status_t moe_expert_choice(const moe_problem_t* p, const float* probs_t,
+                               int32_t* sel_t, int32_t* expert_offset,
+                               int32_t* pack_src, float* pack_w,
+                               hipStream_t stream);
+
+/* packed[r] = bf16(x[pack_src[r]]) for the R rows.  x [B][d] x_dtype. */
+moe_status_t moe_expert_choice_pack(const moe_problem_t* p, const void* x,
+                                    const int32_t* pack_src, moe_bf16_t* packed,
+                                    hipStream_t stream);
+
+/* y[t] = sum over the experts e that chose t, in expert order, of
+ * p_te * ret[row(t, e)] (+ x[t]), fp32; 0 (or x[t]) for a token no expert
+ * chose.  ret [R][d] bf16 (moe_expert_ffn on the expert-choice layout,
+ * expert_offset from moe_expert_choice), sel_t and pack_w as written by
+ * moe_expert_choice; x_residual as in moe_combine. */
+moe_status_t moe_expert_choice_combine(const moe_problem_t* p,
+                                       const moe_bf16_t* ret,
+                                       const int32_t* sel_t,
+                                       const float* pack_w,
+                                       const void* x_residual, void* y,
+                                       hipStream_t stream);
+
+/* Optional outputs of moe_forward_expert_choice; NULL fields live in the
+ * workspace.  packed holds ret after the call (FFN in place).  events: as
+ * moe_forward_out_t's (0 before the gate, 1 after it, 2 after the router
+ * probabilities and the choice, 3 / 4 the expert FFN's first dispatch
+ * start and last dispatch end, 5 after the combine; the pack falls in
+ * 2 -> 3). */
+typedef struct {
+  float* logits;          /* [B][E] */
+  float* probs_t;         /* [E][B] */
+  int32_t* sel_t;         /* [E][B] */
+  int32_t* expert_offset; /* [E+1]  */
+  int32_t* pack_src;      /* [R]    */
+  float* pack_w;          /* [R]    */
+  moe_bf16_t* packed;     /* [R][d] */
+  hipEvent_t events[6];
+} moe_expert_choice_out_t;
+
+/* The layer with expert-choice routing on one stream: gate, router
+ * probabilities, every expert's top-Ce tokens, gather pack, expert FFN (the
+ * grouped GEMM of moe_expert_ffn, Ce rows per expert), combine.  (Use this
+ * entry for the expert FFN of an expert-choice layout: moe_expert_ffn's
+ * workspace is sized for the token-choice layout's Kmax rows, and R can be
+ * larger.)
+ *   ws >= moe_workspace_bytes(p, MOE_OP_FORWARD_EXPERT_CHOICE); the other
+ *   arguments as moe_forward (wpacked: moe_pack_weights of all E experts). */
+moe_status_t moe_forward_expert_choice(const moe_problem_t* p, const void* x,
+                                       const float* Wg, const float* bias,
+                                       const void* wpacked, void* y,
+                                       moe_expert_choice_out_t* out, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,7 @@ def test_ctypes_layout_matches_c(L, tmp_path):
     fields = [f for f, _ in L.Problem._fields_]
     ofields = [f for f, _ in L.ForwardOut._fields_]
     sfields = [f for f, _ in L.RoutingStats._fields_]
+    efields = [f for f, _ in L.ExpertChoiceOut._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){",
              'printf("%zu\\n", sizeof(moe_problem_t));']
     lines += [f'printf("%zu\\n", offsetof(moe_problem_t, {f}));' for f in fields]
@@ -71,6 +72,8 @@ def test_ctypes_layout_matches_c(L, tmp_path):
     lines += [f'printf("%zu\\n", offsetof(moe_forward_out_t, {f}));' for f in ofields]
     lines += ['printf("%zu\\n", sizeof(moe_routing_stats_t));']
     lines += [f'printf("%zu\\n", offsetof(moe_routing_stats_t, {f}));' for f in sfields]
+    lines += ['printf("%zu\\n", sizeof(moe_expert_choice_out_t));']
+    lines += [f'printf("%zu\\n", offsetof(moe_expert_choice_out_t, {f}));' for f in efields]
     lines += ["return 0;}"]
     c = tmp_path / "layout.c"
     c.write_text("\n".join(lines))
@@ -84,6 +87,8 @@ def test_ctypes_layout_matches_c(L, tmp_path):
     want = [ctypes.sizeof(L.Problem)] + [getattr(L.Problem, f).offset for f in fields]
     want += [ctypes.sizeof(L.ForwardOut)] + [getattr(L.ForwardOut, f).offset for f in ofields]
     want += [ctypes.sizeof(L.RoutingStats)] + [getattr(L.RoutingStats, f).offset for f in sfields]
+    want += [ctypes.sizeof(L.ExpertChoiceOut)] + [getattr(L.ExpertChoiceOut, f).offset
+                                                  for f in efields]
     assert vals == want
 
 
@@ -195,3 +200,19 @@ def test_shared_expert_host_checks(L, lib):
                                   fake, fake, None, fake, 1 << 30, None) == L.MOE_ERR_INVALID
     assert lib.moe_combine_shared(ctypes.byref(p), fake, fake, fake, None, None, fake,
                                   None) == L.MOE_ERR_INVALID
+
+
+def test_expert_choice_host_checks(L, lib):
+    """Rows E * min(C, B); all experts must be local; workspace carving."""
+    p = _prob(L, n_ranks=1)          # B 64, E 8, k 2, c 1.25 -> C 20
+    assert lib.moe_expert_choice_rows(ctypes.byref(p)) == 8 * 20
+    big = _prob(L, n_ranks=1, C=1000)
+    assert lib.moe_expert_choice_rows(ctypes.byref(big)) == 8 * 64
+    assert lib.moe_workspace_bytes(ctypes.byref(p), L.MOE_OP_FORWARD_EXPERT_CHOICE) > \
+        8 * 20 * (32 + 48) * 2
+    part = _prob(L, n_ranks=2, e_begin=0, e_end=4)
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.moe_expert_choice(ctypes.byref(part), fake, fake, fake, fake, fake,
+                                 None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward_expert_choice(ctypes.byref(p), fake, fake, None, fake, fake, None,
+                                         None, 0, None) == L.MOE_ERR_WORKSPACE
