@@ -30,7 +30,7 @@ namespace moek {
 namespace {
 
 constexpr int kProbThreads = 256;
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 
 template <int L, int V>
 __global__ __launch_bounds__(kProbThreads) void probs_kernel(const float* __restrict__ logits,
@@ -72,8 +72,25 @@ __device__ __forceinline__ unsigned long long lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Block-wide exclusive prefix of a 0/1 flag over the 256 threads in thread
-// order; returns this thread's prefix and writes the block total to *tot.
+// hist[digit] += 1 for every valid lane, one LDS atomic per distinct digit
+// in the wavefront: 8 ballots find the lanes sharing a lane's digit (the
+// scores of one expert cluster around 1/E, so most lanes share the top
+// digits and per-lane atomics on one address would serialize)
+__device__ __forceinline__ void hist_add(int* hist, unsigned digit, bool valid) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (digit >> b) & 1u;
+    const unsigned long long bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  if (valid && (m & lanes_below(lane)) == 0) atomicAdd(&hist[digit], __popcll(m));
+}
+
+// Block-wide exclusive prefix of a 0/1 flag over the block's threads in
+// thread order; returns this thread's prefix and writes the block total to
+// *tot.
 __device__ __forceinline__ int block_flag_prefix(bool f, int* wcnt, int* tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const unsigned long long b = __ballot(f);
@@ -92,37 +109,65 @@ __device__ __forceinline__ int block_flag_prefix(bool f, int* wcnt, int* tot) {
   return before + in_wave;
 }
 
+// COL_LDS: the expert's column of scores is first copied into LDS (one pass
+// with every load in flight), and the five passes below read it there
+// instead of paying the memory latency once per chunk and pass.
+template <bool COL_LDS>
 __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(
     const float* __restrict__ probs_t, int64_t B, int Ce, int32_t* __restrict__ sel_t,
     int32_t* __restrict__ pack_src, float* __restrict__ pack_w) {
   __shared__ int hist[256];
   __shared__ int wcnt[kSelThreads / 64];
+  __shared__ int bsum[4];
   __shared__ unsigned s_prefix;
   __shared__ int s_need;
+  extern __shared__ unsigned colbuf[];
   const int e = blockIdx.x, tid = threadIdx.x;
-  const float* col = probs_t + (int64_t)e * B;
-  const unsigned* key = reinterpret_cast<const unsigned*>(col);
+  const unsigned* gkey = reinterpret_cast<const unsigned*>(probs_t + (int64_t)e * B);
+  if (COL_LDS) {
+    for (int64_t t = tid; t < B; t += kSelThreads) colbuf[t] = gkey[t];
+    __syncthreads();
+  }
+  const unsigned* key = COL_LDS ? colbuf : gkey;
   // threshold T: the Ce-th largest key; need = how many keys == T to take
   unsigned prefix = 0u, mask = 0u;
   int need = Ce;
   if (Ce > 0 && Ce < B) {
     for (int dgt = 3; dgt >= 0; --dgt) {
       const int sh = 8 * dgt;
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
-      for (int64_t t = tid; t < B; t += kSelThreads) {
-        const unsigned kk = key[t];
-        if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> sh) & 255u], 1);
+      // every lane of a wavefront runs the same trip count (the ballots)
+      for (int64_t t0 = 0; t0 < B; t0 += kSelThreads) {
+        const int64_t t = t0 + tid;
+        const unsigned kk = t < B ? key[t] : 0u;
+        hist_add(hist, (kk >> sh) & 255u, t < B && (kk & mask) == prefix);
       }
       __syncthreads();
-      if (tid == 0) {
-        int above = 0, b = 255;
-        for (; b > 0; --b) {
-          if (above + hist[b] >= need) break;
-          above += hist[b];
+      // the bin holding the need-th largest key: thread i < 256 takes bin
+      // 255 - i, so an inclusive prefix over i counts the keys in bins >= b;
+      // exactly one bin has fewer than need above it and need or more up to
+      // and including it
+      int h = 0, incl = 0;
+      const int lane = tid & 63, wave = tid >> 6;
+      if (tid < 256) {
+        h = hist[255 - tid];
+        incl = h;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int v = __shfl_up(incl, off);
+          if (lane >= off) incl += v;
         }
-        s_prefix = prefix | ((unsigned)b << sh);
-        s_need = need - above;
+        if (lane == 63) bsum[wave] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        for (int w = 0; w < wave; ++w) incl += bsum[w];
+        const int above = incl - h;
+        if (above < need && incl >= need) {
+          s_prefix = prefix | ((unsigned)(255 - tid) << sh);
+          s_need = need - above;
+        }
       }
       __syncthreads();
       prefix = s_prefix;
@@ -150,7 +195,7 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(
       sel_t[(int64_t)e * B + t] = take ? row : -1;
       if (take) {
         pack_src[row] = (int32_t)t;
-        pack_w[row] = col[t];
+        pack_w[row] = __uint_as_float(kk);
       }
     }
     eq_before += eq_tot;
@@ -290,8 +335,13 @@ hipError_t launch_expert_choice(const float* probs_t, int64_t B, int E, int Ce, 
     hipLaunchKernelGGL(ec_offsets_kernel, dim3((E + 1 + 255) / 256), dim3(256), 0, s,
                        expert_offset, E, Ce);
   if (B == 0 || E == 0) return hipGetLastError();
-  hipLaunchKernelGGL(ec_select_kernel, dim3(E), dim3(kSelThreads), 0, s, probs_t, B, Ce, sel_t,
-                     pack_src, pack_w);
+  // the column in LDS up to 36864 tokens (144 KB beside the small arrays)
+  if (B <= 36864)
+    hipLaunchKernelGGL((ec_select_kernel<true>), dim3(E), dim3(kSelThreads), (size_t)B * 4, s,
+                       probs_t, B, Ce, sel_t, pack_src, pack_w);
+  else
+    hipLaunchKernelGGL((ec_select_kernel<false>), dim3(E), dim3(kSelThreads), 0, s, probs_t, B,
+                       Ce, sel_t, pack_src, pack_w);
   return hipGetLastError();
 }
 
