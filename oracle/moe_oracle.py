@@ -73,7 +73,7 @@ __all__ = [
     "softmax", "route", "assign_slots", "layout", "pack", "gelu", "silu",
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
     "expert_capacities", "routing_stats", "shared_ffn", "router_probs", "expert_choice",
-    "expert_choice_combine", "forward_expert_choice",
+    "expert_choice_combine", "forward_expert_choice", "assign_slots_redirect",
 ]
 
 
@@ -251,8 +251,65 @@ def assign_slots(idx: np.ndarray, E: int, C: int, unavailable=None):
     return pos.astype(np.int32), keep, load.astype(np.int32), count.astype(np.int32)
 
 
+def assign_slots_redirect(ranked: np.ndarray, k: int, E: int, C: int, unavailable=None):
+    """Slot assignment where overflow is redirected to the next-best expert.
+
+    [EP-notes] "Components and Architecture", token dispatch and capacity
+    factor: tokens routed to a full expert are dropped or redirected to a
+    secondary expert (a fallback routing).  Reading (one fallback round):
+    round 1 is ``assign_slots`` on the top-k choices; then the m-th dropped
+    choice of a token (m counted in j order) is redirected to the token's
+    (k + m)-th ranked expert -- outside its top-k, distinct for each of its
+    redirected choices, none if k + m >= the ranks given -- and the
+    redirected assignments claim the capacity left, C_e - kept_e, in the
+    original claim order q = j*B + t; what does not fit is dropped.
+
+    ``ranked`` [B, K2] are each token's experts by rank (K2 >= k).  Returns
+    expert [B, k] (the expert an assignment ends with: its own, its
+    fallback, or its own when dropped), rank [B, k] (its column in
+    ``ranked``), slot [B, k], keep [B, k], load (n_e of the top-k choices)
+    and count (kept per expert, both rounds).  Pins: a sequential claim
+    queue, capacity and distinctness invariants, the drop policy when
+    nothing overflows (test_oracle_redirect)."""
+    ranked = np.asarray(ranked, dtype=np.int64)
+    B = ranked.shape[0]
+    K2 = ranked.shape[1]
+    idx = ranked[:, :k]
+    pos1, keep1, load, count1 = assign_slots(idx, E, C, unavailable)
+    cap = expert_capacities(E, C, unavailable)
+    rank = np.tile(np.arange(k), (B, 1))
+    fb = np.full((B, k), -1, dtype=np.int64)
+    for t in range(B):
+        m = 0
+        for j in range(k):
+            if not keep1[t, j]:
+                if k + m < K2:
+                    fb[t, j] = ranked[t, k + m]
+                    rank[t, j] = k + m
+                m += 1
+    rem = cap - count1
+    # round 2: redirected assignments in q order claim the remaining slots
+    e_q = fb.T.reshape(-1)
+    valid = e_q >= 0
+    pos2_q = np.full(B * k, -1, dtype=np.int64)
+    vq = np.nonzero(valid)[0]
+    order = vq[np.argsort(e_q[vq], kind="stable")]
+    sorted_e = e_q[order]
+    start = np.searchsorted(sorted_e, np.arange(E))
+    pos2_q[order] = np.arange(order.size) - start[sorted_e]
+    pos2 = pos2_q.reshape(k, B).T
+    keep2 = (fb >= 0) & (pos2 < np.where(fb >= 0, rem[np.maximum(fb, 0)], 0))
+    expert = np.where(keep1, idx, np.where(keep2, fb, idx))
+    rank = np.where(keep1 | ~keep2, np.tile(np.arange(k), (B, 1)), rank)
+    slot = np.where(keep1, pos1, np.where(keep2, count1[np.maximum(fb, 0)] + pos2, -1))
+    keep = keep1 | keep2
+    count = count1 + np.bincount(fb[keep2], minlength=E).astype(count1.dtype)
+    return (expert.astype(np.int32), rank.astype(np.int32), slot.astype(np.int32), keep,
+            load, count.astype(np.int32))
+
+
 def layout(idx: np.ndarray, pos: np.ndarray, keep: np.ndarray, E: int, D: int,
-           C: int, unavailable=None):
+           C: int, unavailable=None, count: Optional[np.ndarray] = None):
     """Compact, expert-major packed layout (hence grouped by destination rank).
 
     expert_offset = exclusive prefix sum of kept_e (E+1 entries);
@@ -264,8 +321,11 @@ def layout(idx: np.ndarray, pos: np.ndarray, keep: np.ndarray, E: int, D: int,
     Pins: worked-example fixture; bijection/segment invariants
     (test_oracle_slots)."""
     idx = np.asarray(idx, dtype=np.int64)
-    load = np.bincount(idx.reshape(-1), minlength=E)
-    kept = np.minimum(load, expert_capacities(E, C, unavailable))
+    if count is None:
+        load = np.bincount(idx.reshape(-1), minlength=E)
+        kept = np.minimum(load, expert_capacities(E, C, unavailable))
+    else:
+        kept = np.asarray(count, dtype=np.int64)
     expert_offset = np.zeros(E + 1, dtype=np.int64)
     expert_offset[1:] = np.cumsum(kept)
     rank_offset = expert_offset[np.arange(D + 1) * (E // D)]
@@ -444,7 +504,7 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
             n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
             tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
             logits: Optional[np.ndarray] = None, unavailable=None,
-            shared: Optional[tuple] = None) -> dict:
+            shared: Optional[tuple] = None, overflow: str = "drop") -> dict:
     """All steps in the pages' order ([EP-notes] "Formal Algorithm";
     [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
     and slots, pack, expert FFN, unpack + weighted combine (+ residual).
@@ -452,18 +512,30 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
     ``logits`` may be given to skip the gate (routing tests feed the router
     directly); without expert weights only the integer steps and the pack
     run.  ``shared`` = (W1s, W3s, W2s) adds a shared expert's output to every
-    token's combine."""
+    token's combine.  ``overflow`` = "next" redirects overflow to the
+    token's next-best experts (``assign_slots_redirect``, the router giving
+    min(2k, E) ranked choices); idx / w then hold the expert and weight each
+    assignment ends with."""
     B = x.shape[0]
     E = Wg.shape[1] if Wg is not None else logits.shape[1]
     e_end = E if e_end is None else e_end
     if logits is None:
         logits = gate_logits(x, Wg, bias)
-    idx, w = route(logits, k, tau)
     if C is None:
         C = capacity(B, k, E, c)
-    pos, keep, load, count = assign_slots(idx, E, C, unavailable)
-    expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C,
-                                                        unavailable)
+    if overflow == "next":
+        ranked, pr = route(logits, min(2 * k, E), tau)
+        idx, rk, pos, keep, load, count = assign_slots_redirect(ranked, k, E, C, unavailable)
+        w = np.take_along_axis(pr, rk.astype(np.int64), axis=1)
+        expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C,
+                                                            unavailable, count=count)
+    elif overflow == "drop":
+        idx, w = route(logits, k, tau)
+        pos, keep, load, count = assign_slots(idx, E, C, unavailable)
+        expert_offset, rank_offset, dest, pack_src = layout(idx, pos, keep, E, n_ranks, C,
+                                                            unavailable)
+    else:
+        raise ValueError(overflow)
     packed = pack(x, pack_src)
     out = dict(logits=logits, idx=idx, w=w, C=C, pos=pos, keep=keep,
                expert_load=load, expert_count=count, expert_offset=expert_offset,
