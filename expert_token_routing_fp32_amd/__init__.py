@@ -36,15 +36,18 @@ def lib():
 def make_problem(B: int, d: int, E: int, k: int, c: float = 1.0, f: int = 8,
                  act: str = "gelu", x_dtype: str = "bf16", C: int = -1, n_ranks: int = 1,
                  e_begin: int = 0, e_end: Optional[int] = None, tau: float = 1.0,
-                 add_residual: bool = False, unavailable=None) -> Problem:
+                 add_residual: bool = False, unavailable=None,
+                 overflow: str = "drop") -> Problem:
     """``unavailable``: optional device tensor of E uint8 (or bool); a
     nonzero entry gives that expert capacity 0.  The problem keeps a
-    reference to it."""
+    reference to it.  ``overflow``: "drop", or "next" (forward only: dropped
+    choices are redirected to the token's next-best experts)."""
     p = Problem(B=B, d=d, E=E, k=k, c=c, C=C, n_ranks=n_ranks, e_begin=e_begin,
                 e_end=E if e_end is None else e_end, f=f,
                 act={"gelu": L.MOE_GELU, "swiglu": L.MOE_SWIGLU}[act],
                 x_dtype={"f32": L.MOE_F32, "bf16": L.MOE_BF16}[x_dtype], tau=tau,
-                add_residual=int(bool(add_residual)))
+                add_residual=int(bool(add_residual)),
+                overflow={"drop": L.MOE_OVERFLOW_DROP, "next": L.MOE_OVERFLOW_NEXT}[overflow])
     set_unavailable(p, unavailable)
     return p
 

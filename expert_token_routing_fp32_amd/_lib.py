@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT = 0, 1
 (MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS, MOE_OP_SHARED_FFN,
  MOE_OP_FORWARD_EXPERT_CHOICE) = range(6)
 
@@ -34,6 +35,7 @@ class Problem(ctypes.Structure):
         ("tau", ctypes.c_float),
         ("add_residual", ctypes.c_int32),
         ("expert_unavailable", ctypes.c_void_p),
+        ("overflow", ctypes.c_int32),
     ]
 
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_hist_kernel(const int32_t* 
 // of tiles for expert e.
 __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
     int32_t* __restrict__ hist, int n_tiles, int E, int Epad, int C,
-    const uint8_t* __restrict__ unavail, int D,
+    const uint8_t* __restrict__ unavail, const int32_t* __restrict__ cap_in, int D,
     int32_t* __restrict__ expert_load, int32_t* __restrict__ expert_count,
     int32_t* __restrict__ expert_offset, int32_t* __restrict__ rank_offset) {
   __shared__ int gsum[kScanThreads];
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
   }
   int kept = 0;
   if (g == 0 && e < E) {
-    const int ce = (unavail && unavail[e]) ? 0 : C;  // an unavailable expert keeps nothing
+    // an unavailable expert keeps nothing; cap_in: per-expert capacities
+    const int ce = cap_in ? cap_in[e] : (unavail && unavail[e]) ? 0 : C;
     kept = tot < ce ? tot : ce;
     if (expert_load) expert_load[e] = tot;
     expert_count[e] = kept;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
 template <bool FUSED>
 __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C,
-    const uint8_t* __restrict__ unavail, int64_t BK,
+    const uint8_t* __restrict__ unavail, const int32_t* __restrict__ cap_in, int64_t BK,
     int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset_in,
     int32_t* __restrict__ pos, uint8_t* __restrict__ keep, int32_t* __restrict__ dest,
     int32_t* __restrict__ pack_src, int n_tiles, int D, int32_t* __restrict__ expert_load,
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   for (int i = tid; i < 4 * E; i += kSlotThreads) wb[i] = 0;
   // capacity of each expert: C, or 0 for one marked unavailable
   int* cap = wb + 4 * E;
-  for (int i = tid; i < E; i += kSlotThreads) cap[i] = (unavail && unavail[i]) ? 0 : C;
+  for (int i = tid; i < E; i += kSlotThreads)
+    cap[i] = cap_in ? cap_in[i] : (unavail && unavail[i]) ? 0 : C;
   __syncthreads();
   // FUSED: sbase [E] bases of this tile, soff [E + 1] expert offsets of the
   // kept rows, then scratch
@@ -343,7 +345,7 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
                         const uint8_t* unavail, int D, int32_t* pos,
                         uint8_t* keep, int32_t* dest, int32_t* expert_load, int32_t* expert_count,
                         int32_t* expert_offset, int32_t* rank_offset, int32_t* pack_src,
-                        int32_t* ws_hist, hipStream_t s) {
+                        int32_t* ws_hist, hipStream_t s, const int32_t* cap_in) {
   const SlotPlan p = slot_plan(B, k);
   int Epad = 1;
   while (Epad < E) Epad <<= 1;
@@ -358,7 +360,8 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
                      (reinterpret_cast<uintptr_t>(ws_hist) & 15u) == 0;
   if (!fused)
     hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
-                       Epad, C, unavail, D, expert_load, expert_count, expert_offset, rank_offset);
+                       Epad, C, unavail, cap_in, D, expert_load, expert_count, expert_offset,
+                       rank_offset);
   if (p.n_tiles > 0) {
     // ebuf, per-wavefront counts, capacities; fused: + bases, offsets,
     // 2 x 1024 partials, 4 wave sums
@@ -366,12 +369,14 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
                        sizeof(int);
     if (fused)
       hipLaunchKernelGGL(slot_rank_kernel<true>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx,
-                         B, k, E, nbits, C, unavail, p.BK, p.tile, ws_hist, nullptr, pos, keep, dest,
+                         B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist, nullptr, pos,
+                         keep, dest,
                          pack_src, p.n_tiles, D, expert_load, expert_count, expert_offset,
                          rank_offset);
     else
       hipLaunchKernelGGL(slot_rank_kernel<false>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s,
-                         idx, B, k, E, nbits, C, unavail, p.BK, p.tile, ws_hist, expert_offset, pos, keep,
+                         idx, B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist,
+                         expert_offset, pos, keep,
                          dest, pack_src, p.n_tiles, D, nullptr, nullptr, nullptr, nullptr);
   }
   return hipGetLastError();
@@ -389,6 +394,154 @@ hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t 
     hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
   else
     hipLaunchKernelGGL(pack_kernel<false>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Overflow redirected to the next-best expert ("Expert Parallelism",
+// narrativegoldmine.com, "Components and Architecture": tokens routed to a
+// full expert are dropped or redirected to a secondary expert).  One
+// fallback round: round 1 is the slot assignment of the top-k choices; the
+// m-th dropped choice of a token then goes to its (k + m)-th ranked expert
+// and the redirected assignments claim the capacity left, in the original
+// claim order (the slot kernels again, with per-expert capacities); the
+// merge numbers round-2 rows after the expert's round-1 rows.
+namespace {
+
+__global__ __launch_bounds__(256) void split_ranked_kernel(const int32_t* __restrict__ ranked,
+                                                           int64_t n, int K2, int k,
+                                                           int32_t* __restrict__ idx) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / k;
+    const int j = (int)(i - t * k);
+    idx[i] = ranked[t * K2 + j];
+  }
+}
+
+__global__ __launch_bounds__(256) void fallback_kernel(
+    const int32_t* __restrict__ ranked, const uint8_t* __restrict__ keep1,
+    const int32_t* __restrict__ count1, int64_t B, int K2, int k, int E, int C,
+    const uint8_t* __restrict__ unavail, int32_t* __restrict__ fb, int32_t* __restrict__ rk,
+    int32_t* __restrict__ rem) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < E) {
+    const int cap = (unavail && unavail[t]) ? 0 : C;
+    rem[t] = cap - count1[t];
+  }
+  if (t >= B) return;
+  int m = 0;
+  for (int j = 0; j < k; ++j) {
+    int f = -1, r = j;
+    if (!keep1[t * k + j]) {
+      r = k + m;
+      if (r < K2) f = ranked[t * K2 + r];
+      ++m;
+    }
+    fb[t * k + j] = f;
+    rk[t * k + j] = r;
+  }
+}
+
+__global__ __launch_bounds__(1024) void merge_offsets_kernel(
+    const int32_t* __restrict__ count1, const int32_t* __restrict__ count2, int E, int D,
+    int32_t* __restrict__ count, int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ rank_offset) {
+  __shared__ int sc[1024];
+  const int tid = threadIdx.x;  // E <= 1024: one expert per thread
+  const int c = tid < E ? count1[tid] + count2[tid] : 0;
+  if (tid < E) count[tid] = c;
+  sc[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  // sc[i]: inclusive prefix over experts 0..i
+  if (tid <= E) expert_offset[tid] = tid == 0 ? 0 : sc[tid - 1];
+  if (tid <= D) {
+    const int i = tid * (E / D);
+    rank_offset[tid] = i == 0 ? 0 : sc[i - 1];
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(
+    const float* __restrict__ ranked_w, int64_t B, int K2, int k,
+    const uint8_t* __restrict__ keep1, const int32_t* __restrict__ pos1,
+    const int32_t* __restrict__ fb, const int32_t* __restrict__ rk,
+    const uint8_t* __restrict__ keep2, const int32_t* __restrict__ pos2,
+    const int32_t* __restrict__ count1, const int32_t* __restrict__ expert_offset,
+    int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ pos,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ dest, int32_t* __restrict__ pack_src) {
+  const int64_t n = B * k;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / k;
+    int e = idx[i];
+    int slot = -1;
+    float wt = ranked_w[t * K2 + (i - t * k)];
+    bool kp = false;
+    if (keep1[i]) {
+      slot = pos1[i];
+      kp = true;
+    } else if (fb[i] >= 0 && keep2[i]) {
+      e = fb[i];
+      slot = count1[e] + pos2[i];
+      wt = ranked_w[t * K2 + rk[i]];
+      kp = true;
+    }
+    idx[i] = e;
+    w[i] = wt;
+    pos[i] = slot;
+    keep[i] = kp ? 1 : 0;
+    const int r = kp ? expert_offset[e] + slot : -1;
+    dest[i] = r;
+    if (kp) pack_src[r] = (int32_t)t;
+  }
+}
+
+unsigned flat_grid(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  if (g > 65535) g = 65535;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_split_ranked(const int32_t* ranked, int64_t B, int K2, int k, int32_t* idx,
+                               hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_ranked_kernel, dim3(flat_grid(B * k)), dim3(256), 0, s, ranked, B * k,
+                     K2, k, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_fallback(const int32_t* ranked, const uint8_t* keep1, const int32_t* count1,
+                           int64_t B, int K2, int k, int E, int C, const uint8_t* unavail,
+                           int32_t* fb, int32_t* rk, int32_t* rem, hipStream_t s) {
+  const int64_t n = B > E ? B : E;
+  hipLaunchKernelGGL(fallback_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ranked,
+                     keep1, count1, B, K2, k, E, C, unavail, fb, rk, rem);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_offsets(const int32_t* count1, const int32_t* count2, int E, int D,
+                                int32_t* count, int32_t* expert_offset, int32_t* rank_offset,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(merge_offsets_kernel, dim3(1), dim3(1024), 0, s, count1, count2, E, D, count,
+                     expert_offset, rank_offset);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* ranked_w, int64_t B, int K2, int k, const uint8_t* keep1,
+                        const int32_t* pos1, const int32_t* fb, const int32_t* rk,
+                        const uint8_t* keep2, const int32_t* pos2, const int32_t* count1,
+                        const int32_t* expert_offset, int32_t* idx, float* w, int32_t* pos,
+                        uint8_t* keep, int32_t* dest, int32_t* pack_src, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(flat_grid(B * k)), dim3(256), 0, s, ranked_w, B, K2, k,
+                     keep1, pos1, fb, rk, keep2, pos2, count1, expert_offset, idx, w, pos, keep,
+                     dest, pack_src);
   return hipGetLastError();
 }
 

@@ -109,6 +109,11 @@ struct FwdBufs {
   int32_t* hist;
   uint16_t* H;
   void* wsplit;  // split copy of the router weights, or null
+  // overflow redirected (MOE_OVERFLOW_NEXT): ranked choices and both rounds
+  int32_t* ranked;
+  float* ranked_w;
+  int32_t *pos1, *count1, *fb, *rk, *rem, *pos2, *load2, *count2, *eo2, *ro2, *dest2, *ps2;
+  uint8_t *keep1, *keep2;
 };
 
 size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* ws, FwdBufs* b) {
@@ -137,6 +142,25 @@ size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* w
   t.wsplit = moek::gate_use_split(p->x_dtype == MOE_BF16, p->B, p->d, p->E)
                  ? c.take<char>(nullptr, moek::gate_split_bytes(p->d, p->E))
                  : nullptr;
+  if (p->overflow == MOE_OVERFLOW_NEXT) {
+    const size_t K2 = (size_t)(2 * p->k < p->E ? 2 * p->k : p->E);
+    t.ranked = c.take<int32_t>(nullptr, (size_t)p->B * K2 * 4);
+    t.ranked_w = c.take<float>(nullptr, (size_t)p->B * K2 * 4);
+    t.pos1 = c.take<int32_t>(nullptr, BKn * 4);
+    t.keep1 = c.take<uint8_t>(nullptr, BKn);
+    t.count1 = c.take<int32_t>(nullptr, (size_t)p->E * 4);
+    t.fb = c.take<int32_t>(nullptr, BKn * 4);
+    t.rk = c.take<int32_t>(nullptr, BKn * 4);
+    t.rem = c.take<int32_t>(nullptr, (size_t)p->E * 4);
+    t.pos2 = c.take<int32_t>(nullptr, BKn * 4);
+    t.keep2 = c.take<uint8_t>(nullptr, BKn);
+    t.load2 = c.take<int32_t>(nullptr, (size_t)p->E * 4);
+    t.count2 = c.take<int32_t>(nullptr, (size_t)p->E * 4);
+    t.eo2 = c.take<int32_t>(nullptr, (size_t)(p->E + 1) * 4);
+    t.ro2 = c.take<int32_t>(nullptr, (size_t)(p->n_ranks + 1) * 4);
+    t.dest2 = c.take<int32_t>(nullptr, BKn * 4);
+    t.ps2 = c.take<int32_t>(nullptr, km * 4);
+  }
   if (b) *b = t;
   return c.off;
 }
@@ -198,6 +222,10 @@ moe_status_t moe_validate(const moe_problem_t* p) {
   if (p->x_dtype != MOE_F32 && p->x_dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (!(p->tau > 0.0f) || !std::isfinite(p->tau)) return MOE_ERR_INVALID;
   if (p->add_residual != 0 && p->add_residual != 1) return MOE_ERR_INVALID;
+  if (p->overflow != MOE_OVERFLOW_DROP && p->overflow != MOE_OVERFLOW_NEXT)
+    return MOE_ERR_INVALID;
+  if (p->overflow == MOE_OVERFLOW_NEXT && (2 * p->k < p->E ? 2 * p->k : p->E) > kMaxK)
+    return MOE_ERR_UNSUPPORTED;
   if (p->E > kMaxE || p->k > kMaxK || p->d > kMaxDim || p->f > kMaxDim)
     return MOE_ERR_UNSUPPORTED;
   if (p->B > kMaxB || p->B > (int64_t)INT32_MAX / p->k) return MOE_ERR_UNSUPPORTED;
@@ -286,6 +314,7 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
                           hipStream_t stream) {
   moe_status_t st = moe_validate(p);
   if (st != MOE_OK) return st;
+  if (p->overflow != MOE_OVERFLOW_DROP) return MOE_ERR_UNSUPPORTED;  // needs ranked choices
   if (!expert_count || !expert_offset || !rank_offset) return MOE_ERR_INVALID;
   if (p->B > 0 && (!x || !topk_idx || !pos || !keep || !dest || !pack_src || !packed))
     return MOE_ERR_INVALID;
@@ -421,13 +450,44 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
   if (e == hipSuccess)
     e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, b.wsplit, stream);
   mark(1);
-  if (e == hipSuccess)
-    e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
+  const bool redirect = p->overflow == MOE_OVERFLOW_NEXT;
+  const int K2 = 2 * p->k < p->E ? 2 * p->k : p->E;
+  if (e == hipSuccess) {
+    if (redirect)
+      e = moek::launch_route(b.logits, p->B, p->E, K2, p->tau, b.ranked, b.ranked_w, stream);
+    else
+      e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
+  }
   mark(2);
-  if (e == hipSuccess)
-    e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->expert_unavailable, p->n_ranks, b.pos,
-                           b.keep, b.dest, b.load,
-                           b.count, b.eo, b.ro, b.pack_src, b.hist, stream);
+  if (!redirect) {
+    if (e == hipSuccess)
+      e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->expert_unavailable, p->n_ranks,
+                             b.pos, b.keep, b.dest, b.load, b.count, b.eo, b.ro, b.pack_src,
+                             b.hist, stream);
+  } else {
+    // round 1 on the top-k choices, the fallbacks of the dropped ones, round
+    // 2 on the capacity left, then the merged layout (dest / pack_src of the
+    // two rounds' own layouts are scratch)
+    if (e == hipSuccess) e = moek::launch_split_ranked(b.ranked, p->B, K2, p->k, b.idx, stream);
+    if (e == hipSuccess)
+      e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->expert_unavailable, p->n_ranks,
+                             b.pos1, b.keep1, b.dest2, b.load, b.count1, b.eo2, b.ro2, b.ps2,
+                             b.hist, stream);
+    if (e == hipSuccess)
+      e = moek::launch_fallback(b.ranked, b.keep1, b.count1, p->B, K2, p->k, p->E, C,
+                                p->expert_unavailable, b.fb, b.rk, b.rem, stream);
+    if (e == hipSuccess)
+      e = moek::launch_slots(b.fb, p->B, p->k, p->E, C, nullptr, p->n_ranks, b.pos2, b.keep2,
+                             b.dest2, b.load2, b.count2, b.eo2, b.ro2, b.ps2, b.hist, stream,
+                             b.rem);
+    if (e == hipSuccess)
+      e = moek::launch_merge_offsets(b.count1, b.count2, p->E, p->n_ranks, b.count, b.eo, b.ro,
+                                     stream);
+    if (e == hipSuccess)
+      e = moek::launch_merge(b.ranked_w, p->B, K2, p->k, b.keep1, b.pos1, b.fb, b.rk, b.keep2,
+                             b.pos2, b.count1, b.eo, b.idx, b.w, b.pos, b.keep, b.dest,
+                             b.pack_src, stream);
+  }
   if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
   // events 3 and 4: the expert FFN's first dispatch start and last dispatch
   // end (no marker packets between the launches); with a shared expert its

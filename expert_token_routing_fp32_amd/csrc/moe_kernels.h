@@ -142,12 +142,35 @@ SlotPlan slot_plan(int64_t B, int k);
 size_t slot_ws_bytes(int64_t B, int k, int E);
 
 // unavail: optional [E] device mask; a nonzero entry gives that expert
-// capacity 0 (every assignment to it is dropped)
+// capacity 0 (every assignment to it is dropped).  cap_in: optional [E]
+// device capacities used instead of C and the mask.
 hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
                         const uint8_t* unavail, int D,
                         int32_t* pos, uint8_t* keep, int32_t* dest, int32_t* expert_load,
                         int32_t* expert_count, int32_t* expert_offset, int32_t* rank_offset,
-                        int32_t* pack_src, int32_t* ws_hist, hipStream_t s);
+                        int32_t* pack_src, int32_t* ws_hist, hipStream_t s,
+                        const int32_t* cap_in = nullptr);
+
+// Overflow redirected to the next-best expert (one fallback round).
+//   split: idx [B][k] = ranked [B][K2] columns 0..k-1
+//   fallback: the m-th dropped choice of a token -> its rank k + m (fb = -1
+//     past K2), rk = that rank; rem[e] = capacity - kept in round 1
+//   merge_offsets (one block): count = count1 + count2, offsets, rank offsets
+//   merge: final expert / weight / slot / keep / dest / pack_src per
+//     assignment from both rounds
+hipError_t launch_split_ranked(const int32_t* ranked, int64_t B, int K2, int k, int32_t* idx,
+                               hipStream_t s);
+hipError_t launch_fallback(const int32_t* ranked, const uint8_t* keep1, const int32_t* count1,
+                           int64_t B, int K2, int k, int E, int C, const uint8_t* unavail,
+                           int32_t* fb, int32_t* rk, int32_t* rem, hipStream_t s);
+hipError_t launch_merge_offsets(const int32_t* count1, const int32_t* count2, int E, int D,
+                                int32_t* count, int32_t* expert_offset, int32_t* rank_offset,
+                                hipStream_t s);
+hipError_t launch_merge(const float* ranked_w, int64_t B, int K2, int k, const uint8_t* keep1,
+                        const int32_t* pos1, const int32_t* fb, const int32_t* rk,
+                        const uint8_t* keep2, const int32_t* pos2, const int32_t* count1,
+                        const int32_t* expert_offset, int32_t* idx, float* w, int32_t* pos,
+                        uint8_t* keep, int32_t* dest, int32_t* pack_src, hipStream_t s);
 
 // expert-choice routing (choice.hip): router probabilities transposed
 // [E][B]; every expert's top-Ce tokens (sel_t [E][B]: packed row or -1;

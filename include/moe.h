@@ -67,6 +67,7 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act_t;
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_NEXT = 1 } moe_overflow_t;
 
 /* Which call a workspace is sized for (moe_workspace_bytes). */
 typedef enum {
@@ -106,6 +107,20 @@ typedef struct {
    * dest = -1, expert_count = 0).  NULL: every expert has capacity C.
    * Read by moe_dispatch and moe_forward; owned by the caller. */
   const uint8_t* expert_unavailable;
+  /* moe_overflow_t: what happens to an assignment past its expert's
+   * capacity ("Expert Parallelism", narrativegoldmine.com, "Components and
+   * Architecture": overflow tokens are dropped or redirected to a secondary
+   * expert).  MOE_OVERFLOW_DROP (0): dropped.  MOE_OVERFLOW_NEXT (1, read
+   * by moe_forward only; moe_dispatch returns MOE_ERR_UNSUPPORTED): one
+   * fallback round -- the m-th dropped choice of a token goes to its
+   * (k + m)-th ranked expert (the router ranks min(2k, E) experts, so
+   * min(2k, E) <= 16) and claims the capacity left after the first round, in
+   * the original claim order q = j*B + t; what does not fit is dropped.
+   * moe_forward's outputs then describe where each assignment ended:
+   * topk_idx / topk_w the final expert and its probability, pos the slot
+   * (-1 when dropped), expert_load the first-round n_e, expert_count the
+   * rows kept in both rounds. */
+  int32_t overflow;
 } moe_problem_t;
 
 /* ---- host-only helpers (no GPU work) ---------------------------------- */

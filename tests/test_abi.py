@@ -216,3 +216,20 @@ def test_expert_choice_host_checks(L, lib):
                                  None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_forward_expert_choice(ctypes.byref(p), fake, fake, None, fake, fake, None,
                                          None, 0, None) == L.MOE_ERR_WORKSPACE
+
+
+def test_overflow_policy_checks(L, lib):
+    """overflow: 0 drop, 1 redirect (forward only; the router ranks
+    min(2k, E) <= 16 experts)."""
+    assert lib.moe_validate(ctypes.byref(_prob(L, overflow=1))) == 0
+    assert lib.moe_validate(ctypes.byref(_prob(L, overflow=2))) == L.MOE_ERR_INVALID
+    wide = _prob(L, E=64, k=9, e_end=64, overflow=1)    # 18 ranked choices
+    assert lib.moe_validate(ctypes.byref(wide)) == L.MOE_ERR_UNSUPPORTED
+    p = _prob(L, overflow=1)
+    fake = ctypes.c_void_p(1 << 20)
+    r = lib.moe_dispatch(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                         fake, fake, fake, 1 << 30, None)
+    assert r == L.MOE_ERR_UNSUPPORTED
+    # the redirect's extra buffers live in the forward workspace
+    assert lib.moe_workspace_bytes(ctypes.byref(p), L.MOE_OP_FORWARD) > \
+        lib.moe_workspace_bytes(ctypes.byref(_prob(L)), L.MOE_OP_FORWARD)
