@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--routing", default="token", choices=["token", "expert_choice"],
                     help="expert_choice: every expert picks its top-C tokens "
                          "(moe_forward_expert_choice; all experts local)")
+    ap.add_argument("--overflow", default="drop", choices=["drop", "next"],
+                    help="next: assignments past capacity are redirected to the token's "
+                         "next-best experts (moe_problem_t.overflow)")
     ap.add_argument("--shared-expert", type=int, default=0, metavar="F",
                     help="add a shared expert of hidden size F (same activation) on every "
                          "token: moe_forward_shared (bf16 workloads)")
@@ -174,7 +177,8 @@ def measured_traffic(workload: str):
     return rec["expert_ffn_bytes"] if h.hexdigest()[:16] == rec["src_sha256_16"] else None
 
 
-def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False) -> dict:
+def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
+                 overflow: str = "drop") -> dict:
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -190,7 +194,7 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False) -> dict
         else:
             oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
                            k=w.k, c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin,
-                           e_end=w.e_end, tau=w.tau, shared=shared)
+                           e_end=w.e_end, tau=w.tau, shared=shared, overflow=overflow)
         t_tot += time.perf_counter() - t0
         reps += 1
     return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
@@ -242,7 +246,8 @@ def main():
     if w.act == "swiglu":
         W3 = d16(inp["W3"] if bf16 else inp["W3_bits"])
     p = moe.make_problem(B=w.B, d=w.d, E=w.E, k=w.k, c=w.c, f=w.f, act=w.act, x_dtype=w.x_dtype,
-                         n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end, tau=w.tau)
+                         n_ranks=w.n_ranks, e_begin=w.e_begin, e_end=w.e_end, tau=w.tau,
+                         overflow=args.overflow)
     # expert weights in the library's blocked layout: a one-time conversion at
     # load, like reading a checkpoint -- not part of the timed step
     wp = moe.pack_weights(p, W1, W3, W2)
@@ -253,8 +258,8 @@ def main():
         if w.e_begin != 0 or w.e_end != w.E:
             raise SystemExit("--routing expert_choice needs every expert local "
                              f"({w.name} runs experts [{w.e_begin},{w.e_end}) of {w.E})")
-        if args.shared_expert:
-            raise SystemExit("--shared-expert goes with token-choice routing")
+        if args.shared_expert or args.overflow != "drop":
+            raise SystemExit("--shared-expert and --overflow go with token-choice routing")
         ws = torch.empty(moe.workspace_bytes(p, "forward_expert_choice"), dtype=torch.uint8,
                          device=dev)
     shared = None
@@ -443,7 +448,9 @@ def main():
                                f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
                                f"local experts [{w.e_begin},{w.e_end})"
                                + (f" + shared expert f={fs}" if shared is not None else "")
-                               + (", expert-choice routing" if ec else ""),
+                               + (", expert-choice routing" if ec else "")
+                               + (", overflow to the next-best expert"
+                                  if args.overflow == "next" else ""),
                    "global_batch": w.B, "cache": "cold" if args.cold else "warm"},
         "roofline": roof,
         "breakdown": breakdown,
@@ -451,7 +458,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds,
-                                           shared_np if shared is not None else None, ec)
+                                           shared_np if shared is not None else None, ec,
+                                           args.overflow)
     print(json.dumps(out), flush=True)
 
 
