@@ -361,15 +361,18 @@ def main():
         for _ in range(3):
             hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"],
                                    ws=ws_stats)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
-        e0.record()
-        for _ in range(reps):
+        # events around each call (the three launches of one call are
+        # enqueued back to back by the library; between calls the host
+        # allocates the outputs), median of 20
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(20)]
+        for e0, e1 in pairs:
+            e0.record()
             hs = moe.routing_stats(p, o["logits"], o["expert_load"], o["expert_count"],
                                    ws=ws_stats)
-        e1.record()
+            e1.record()
         torch.cuda.synchronize()
-        t_stats = e0.elapsed_time(e1) / reps * 1e-3
+        t_stats = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e-3
         hsum = hs["summary"].cpu().numpy()
         # algorithmic bytes: the logits once, the counts, the per-expert outputs
         stats_bytes = w.B * w.E * 4 + w.E * (2 * 4 + 4 * 4) + 5 * 8

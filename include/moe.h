@@ -16,6 +16,19 @@
  *                  all-to-all becomes the identity on one GPU)
  *   moe_forward    all of the above, enqueued back to back
  *
+ * and, beside that path, the variants and signals the pages also describe:
+ *
+ *   moe_routing_stats   routing-health signals (utilisation, drops,
+ *                       auxiliary loss, routing and load entropy)
+ *   expert_unavailable  (a moe_problem_t field) experts with capacity 0
+ *   overflow            (a moe_problem_t field) overflow redirected to the
+ *                       next-best expert instead of dropped
+ *   moe_shared_ffn, moe_combine_shared, moe_forward_shared
+ *                       a shared expert on every token
+ *   moe_router_probs, moe_expert_choice, moe_expert_choice_pack,
+ *   moe_expert_choice_combine, moe_forward_expert_choice
+ *                       expert-choice routing (experts pick their tokens)
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Every pointer argument is DEVICE memory unless stated otherwise; the
