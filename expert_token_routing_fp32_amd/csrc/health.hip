@@ -114,17 +114,18 @@ __global__ __launch_bounds__(256) void stats_column_kernel(const float* __restri
   if (lane == 0) colsum[c] = s;
 }
 
-// fixed-tree sum over the block (deterministic)
+// fixed-order sum over the block (deterministic): a butterfly inside each
+// wavefront, then the 16 wavefront totals in wavefront order
 template <typename T>
 __device__ T block_sum(T v, T* sh) {
   const int tid = threadIdx.x;
-  sh[tid] = v;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if ((tid & 63) == 0) sh[tid >> 6] = v;
   __syncthreads();
-  for (int off = kFinalThreads / 2; off >= 1; off >>= 1) {
-    if (tid < off) sh[tid] += sh[tid + off];
-    __syncthreads();
-  }
-  const T r = sh[0];
+  T r = 0;
+#pragma unroll
+  for (int w = 0; w < kFinalThreads / 64; ++w) r += sh[w];
   __syncthreads();
   return r;
 }
@@ -134,8 +135,8 @@ __global__ __launch_bounds__(kFinalThreads) void stats_final_kernel(
     const int32_t* __restrict__ load, const int32_t* __restrict__ count,
     float* __restrict__ prob_mean, float* __restrict__ token_frac,
     float* __restrict__ utilization, int32_t* __restrict__ dropped, double* __restrict__ summary) {
-  __shared__ double shd[kFinalThreads];
-  __shared__ long long shl[kFinalThreads];
+  __shared__ double shd[kFinalThreads / 64];
+  __shared__ long long shl[kFinalThreads / 64];
   const int tid = threadIdx.x;
   const double Bd = (double)B;
   double aux = 0.0, lent = 0.0;
