@@ -197,8 +197,17 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
                            e_end=w.e_end, tau=w.tau, shared=shared, overflow=overflow)
         t_tot += time.perf_counter() - t0
         reps += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"the whole {w.name} batch ({w.B} tokens), oracle forward run {reps} times "
                       f"({t_tot:.1f} s), float64 NumPy, input generation excluded"}
 
@@ -324,6 +333,16 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / args.steps
+    flush_s = 0.0
+    if flush is not None:
+        # the cold protocol's 512 MB write runs before every step, inside the
+        # timed loop: time the same number of writes alone and take them out
+        f0 = time.perf_counter()
+        for _ in range(args.steps):
+            flush.fill_(1)
+        torch.cuda.synchronize()
+        flush_s = (time.perf_counter() - f0) / args.steps
+        sec_per_step -= flush_s
     t_ffn_live = sum(evs[i][3].elapsed_time(evs[i][4]) for i in sampled) / len(sampled) * 1e-3
     for i in range(args.steps):
         step(evs[i])
@@ -454,7 +473,8 @@ def main():
                                + (", expert-choice routing" if ec else "")
                                + (", overflow to the next-best expert"
                                   if args.overflow == "next" else ""),
-                   "global_batch": w.B, "cache": "cold" if args.cold else "warm"},
+                   "global_batch": w.B, "cache": "cold" if args.cold else "warm",
+                   **({"cold_flush_ms_excluded": round(flush_s * 1e3, 4)} if args.cold else {})},
         "roofline": roof,
         "breakdown": breakdown,
     }
