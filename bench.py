@@ -296,22 +296,30 @@ def main():
     y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
-    # HIP events recorded by the library on its stream at the stage
-    # boundaries inside moe_forward (before the gate, after each of gate,
-    # route, dispatch, expert FFN, combine).  The two around the expert FFN
-    # are taken from its first and last kernel dispatches (start and end
-    # timestamps of the launches, no marker packets); each of the other
-    # records costs a few microseconds of stream time.  The timed steps
-    # record only the FFN pair, and only on every `stride`-th step (at least
-    # 10 sampled steps); a second run of as many steps records all six on
-    # every step for the breakdown.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # HIP events recorded by the library on its stream.  moe_forward takes
+    # every one from the dispatch timestamps of a stage's own kernels (start
+    # of its first, end of its last: no marker packets), so each stage's
+    # time is its kernels' and the gaps between launches are measured apart.
+    # The expert-choice forward records marker events at its stage
+    # boundaries, except around the expert FFN.  The timed steps record only
+    # the FFN pair, and only on every `stride`-th step (at least 10 sampled
+    # steps); a second run of as many steps records them all on every step
+    # for the breakdown.
+    if ec:
+        n_ev, ffn_ev = 6, (3, 4)
+        pairs = {"gate": (0, 1), "route": (1, 2), "dispatch": (2, 3), "expert_ffn": (3, 4),
+                 "combine": (4, 5)}
+        gaps = {}
+    else:
+        n_ev, ffn_ev = moe.N_STAGE_EVENTS, moe.STAGE_EVENTS["expert_ffn"]
+        pairs, gaps = moe.STAGE_EVENTS, moe.LAUNCH_GAPS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()
     stride = max(1, args.steps // 10)
     sampled = list(range(0, args.steps, stride))
-    ffn_only = [[None, None, None, r[3], r[4], None] if i % stride == 0 else None
+    ffn_only = [[r[j] if j in ffn_ev else None for j in range(n_ev)] if i % stride == 0 else None
                 for i, r in enumerate(evs)]
 
     def step(ev=None):
@@ -343,12 +351,16 @@ def main():
         torch.cuda.synchronize()
         flush_s = (time.perf_counter() - f0) / args.steps
         sec_per_step -= flush_s
-    t_ffn_live = sum(evs[i][3].elapsed_time(evs[i][4]) for i in sampled) / len(sampled) * 1e-3
+    a, b = ffn_ev
+    t_ffn_live = sum(evs[i][a].elapsed_time(evs[i][b]) for i in sampled) / len(sampled) * 1e-3
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    stage_s = {name: sum(r[j].elapsed_time(r[j + 1]) for r in evs) / len(evs) * 1e-3
-               for j, name in enumerate(moe.STAGES)}
+    def mean_s(ab):
+        return sum(r[ab[0]].elapsed_time(r[ab[1]]) for r in evs) / len(evs) * 1e-3
+
+    stage_s = {name: mean_s(ab) for name, ab in pairs.items()}
+    gap_s = {name: mean_s(ab) for name, ab in gaps.items()}
     t_gate, t_route, t_disp, t_comb = (stage_s[k] for k in ("gate", "route", "dispatch", "combine"))
     log(f"[bench] {sec_per_step * 1e3:.3f} ms/step; " +
         ", ".join(f"{k} {v * 1e6:.1f} us" for k, v in stage_s.items()))
@@ -427,7 +439,8 @@ def main():
     rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]
     rpc_t = t_route + t_disp + t_comb
     breakdown = {
-        "timing": "moe_forward stage events over a second run of the same number of steps",
+        "timing": ("stage events over a second run of the same number of steps"
+                   + ("" if ec else ": each stage from its own kernels' dispatch start and end")),
         "expert_ffn_us_breakdown_run": round(stage_s["expert_ffn"] * 1e6, 2),
         "gate_us": round(t_gate * 1e6, 2),
         # bf16 activations: three bf16 MFMA products per fp32 multiply-add
@@ -439,6 +452,7 @@ def main():
         "dispatch_us": round(t_disp * 1e6, 2),
         "expert_ffn_us": round(t_ffn_live * 1e6, 2),
         "combine_us": round(t_comb * 1e6, 2),
+        **({"launch_gaps_us": {k: round(v * 1e6, 2) for k, v in gap_s.items()}} if gap_s else {}),
         "expert_gemm_tflops": round(ffn_tflops, 1),
         "expert_gemm_mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "expert_gemm_hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),

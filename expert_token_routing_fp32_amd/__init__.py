@@ -315,7 +315,13 @@ _OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_lo
                "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")
 
 
-STAGES = ("gate", "route", "dispatch", "expert_ffn", "combine")
+# forward's stage events: the start and end of each stage's kernels
+# (dispatch timestamps); the gaps between launches lie between the pairs
+N_STAGE_EVENTS = L.MOE_STAGE_EVENTS
+STAGE_EVENTS = {"gate": (0, 1), "route": (2, 3), "dispatch": (3, 4), "expert_ffn": (5, 6),
+                "combine": (7, 8)}
+LAUNCH_GAPS = {"gate_route": (1, 2), "before_ffn": (4, 5), "after_ffn": (6, 7)}
+STAGES = tuple(STAGE_EVENTS)
 
 
 def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None,
@@ -323,10 +329,10 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
     """The whole layer on the current stream (``wpacked`` from pack_weights).
     With ``outputs`` the intermediate tensors are allocated and returned too
     (``packed`` then holds the expert outputs of the local rows, in place).
-    ``stage_events``: optional six timing-enabled ``torch.cuda.Event`` (or
-    None); the library records them at the boundaries of the STAGES (before
-    the first, after each); events 3 and 4 come from the expert FFN's first
-    and last kernel dispatches themselves (their start and end timestamps).
+    ``stage_events``: optional N_STAGE_EVENTS timing-enabled
+    ``torch.cuda.Event`` (or None); the library records them from the start
+    and end of each stage's own kernels (STAGE_EVENTS gives the pair of each
+    stage, LAUNCH_GAPS the pairs around the gaps between launches).
     ``shared`` = (ps, wpacked_shared) adds a shared expert on every token
     (moe_forward_shared; ps from shared_problem)."""
     _check(p)
@@ -357,8 +363,8 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
                  packed=torch.empty((km, d), dtype=torch.int16, device=dev))
         outp = L.ForwardOut(**{n: o[n].data_ptr() for n in _OUT_FIELDS})
     if stage_events is not None:
-        if len(stage_events) != 6:
-            raise ValueError("stage_events needs 6 events")
+        if len(stage_events) != N_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {N_STAGE_EVENTS} events")
         if outp is None:
             outp = L.ForwardOut()
         for i, ev in enumerate(stage_events):

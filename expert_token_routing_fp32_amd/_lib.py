@@ -39,6 +39,9 @@ class Problem(ctypes.Structure):
     ]
 
 
+MOE_STAGE_EVENTS = 9  # events of moe_forward_out_t
+
+
 class RoutingStats(ctypes.Structure):
     """moe_routing_stats_t: device pointers (or NULL)."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
@@ -46,12 +49,12 @@ class RoutingStats(ctypes.Structure):
 
 
 class ForwardOut(ctypes.Structure):
-    """moe_forward_out_t: device pointers or NULL, then six hipEvent_t
-    handles (or NULL) recorded at the stage boundaries."""
+    """moe_forward_out_t: device pointers or NULL, then MOE_STAGE_EVENTS
+    hipEvent_t handles (or NULL) taken from the stages' kernel dispatches."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
         "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")] + [
-        ("events", ctypes.c_void_p * 6)]
+        ("events", ctypes.c_void_p * MOE_STAGE_EVENTS)]
 
 
 class ExpertChoiceOut(ctypes.Structure):

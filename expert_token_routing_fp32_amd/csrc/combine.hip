@@ -13,6 +13,7 @@
 //
 // All three kernels are row copies/gathers bound by HBM: one thread moves a
 // 16-byte chunk (8 bf16), consecutive threads walk a row.
+#include "launch.h"
 #include "moe_kernels.h"
 
 namespace moek {
@@ -127,18 +128,19 @@ __global__ __launch_bounds__(256) void copy_remote_kernel(const uint16_t* __rest
 template <bool XBF16, bool RES>
 void launch_combine_t(dim3 g, const uint16_t* ret, const int32_t* dest, const float* w,
                       const void* x_res, const uint16_t* shared, void* y, int64_t B, int k, int d,
-                      int64_t kmax, hipStream_t s) {
+                      int64_t kmax, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (shared)
-    hipLaunchKernelGGL((combine_kernel<XBF16, RES, true>), g, dim3(256), 0, s, ret, dest, w,
-                       x_res, shared, y, B, k, d, kmax);
+    launch_timed((combine_kernel<XBF16, RES, true>), g, dim3(256), 0, s, e0, e1, ret,
+                 dest, w, x_res, shared, y, B, k, d, kmax);
   else
-    hipLaunchKernelGGL((combine_kernel<XBF16, RES, false>), g, dim3(256), 0, s, ret, dest, w,
-                       x_res, shared, y, B, k, d, kmax);
+    launch_timed((combine_kernel<XBF16, RES, false>), g, dim3(256), 0, s, e0, e1, ret,
+                 dest, w, x_res, shared, y, B, k, d, kmax);
 }
 
 hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
-                          int64_t kmax, hipStream_t s, const uint16_t* shared) {
+                          int64_t kmax, hipStream_t s, const uint16_t* shared, hipEvent_t e0,
+                          hipEvent_t e1) {
   if (B == 0) return hipSuccess;
   // x: 512-column piece of the rows (fastest in dispatch order, so
   // consecutive workgroups cover consecutive pieces of the same rows);
@@ -147,14 +149,14 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
   const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16) {
     if (x_res)
-      launch_combine_t<true, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
+      launch_combine_t<true, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s, e0, e1);
     else
-      launch_combine_t<true, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
+      launch_combine_t<true, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s, e0, e1);
   } else {
     if (x_res)
-      launch_combine_t<false, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
+      launch_combine_t<false, true>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s, e0, e1);
     else
-      launch_combine_t<false, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s);
+      launch_combine_t<false, false>(g, ret, dest, w, x_res, shared, y, B, k, d, kmax, s, e0, e1);
   }
   return hipGetLastError();
 }

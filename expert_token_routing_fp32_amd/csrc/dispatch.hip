@@ -19,6 +19,7 @@
 //              bases in LDS carry the order across the four wavefronts and
 //              across chunks.  Writes pos, keep, dest, pack_src.
 // pack then moves each token row once from x into its kept packed rows.
+#include "launch.h"
 #include "moe_kernels.h"
 
 namespace moek {
@@ -383,7 +384,7 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
 }
 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
-                       uint16_t* packed, hipStream_t s) {
+                       uint16_t* packed, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (B == 0) return hipSuccess;
   // x: 512-column piece of the rows (fastest in dispatch order, so
   // consecutive workgroups cover consecutive pieces of the same rows);
@@ -391,9 +392,11 @@ hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t 
   const int64_t ntb = (B + 3) / 4;
   const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16)
-    hipLaunchKernelGGL(pack_kernel<true>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
+    launch_timed(pack_kernel<true>, dim3(g), dim3(256), 0, s, e0, e1, x, dest, B, k, d,
+                 packed);
   else
-    hipLaunchKernelGGL(pack_kernel<false>, dim3(g), dim3(256), 0, s, x, dest, B, k, d, packed);
+    launch_timed(pack_kernel<false>, dim3(g), dim3(256), 0, s, e0, e1, x, dest, B, k, d,
+                 packed);
   return hipGetLastError();
 }
 

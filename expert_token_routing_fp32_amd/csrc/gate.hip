@@ -26,6 +26,7 @@
 // four waves split each 128-wide slice of d; blocked accumulation keeps the
 // fp32 error near sqrt(32) + sqrt(d/32) roundings; the four wave totals are
 // added in a fixed order).
+#include "launch.h"
 #include "moe_kernels.h"
 
 namespace moek {
@@ -379,17 +380,19 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 template <int MI, int EB, int KS>
 hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* wsp,
                               const float* bias, float* logits, int64_t B, int d, int E,
-                              hipStream_t s) {
+                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int neb = (E + 31) / 32;
   dim3 grid((unsigned)((B + 32 * MI - 1) / (32 * MI)), (unsigned)((neb + EB - 1) / EB));
   const size_t lds = (size_t)EB * (KS - 1) * MI * 16 * 64 * sizeof(float);
   const size_t ring = (size_t)3 * KS * 32 * MI * 128;
   if (wsp)
-    hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS, true>), grid, dim3(64 * EB * KS),
-                       lds > ring ? lds : ring, s, x, Wg, wsp, bias, logits, B, d, E);
+    launch_timed((gate_lds_kernel<MI, EB, KS, true>), grid, dim3(64 * EB * KS),
+                 lds > ring ? lds : ring, s, e0, e1, x, Wg, wsp, bias, logits, B, d,
+                 E);
   else
-    hipLaunchKernelGGL((gate_lds_kernel<MI, EB, KS, false>), grid, dim3(64 * EB * KS),
-                       lds > ring ? lds : ring, s, x, Wg, wsp, bias, logits, B, d, E);
+    launch_timed((gate_lds_kernel<MI, EB, KS, false>), grid, dim3(64 * EB * KS),
+                 lds > ring ? lds : ring, s, e0, e1, x, Wg, wsp, bias, logits, B, d,
+                 E);
   return hipGetLastError();
 }
 
@@ -399,16 +402,16 @@ hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* w
 template <int EB, int KS>
 hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const u32x4* wsp,
                                const float* bias, float* logits, int64_t B, int d, int E,
-                               hipStream_t s) {
+                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int MI_MAX = KS >= 8 ? 1 : KS >= 4 ? 2 : 4;
   constexpr int MI_MIN = EB >= 8 ? 2 : 1;
   if constexpr (MI_MAX >= 4)
-    if (mi >= 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+    if (mi >= 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
   if constexpr (MI_MAX >= 2)
     if (mi >= 2 || MI_MIN >= 2)
-      return launch_gate_mfma_t<2, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+      return launch_gate_mfma_t<2, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
   if constexpr (MI_MIN <= 1)
-    return launch_gate_mfma_t<1, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s);
+    return launch_gate_mfma_t<1, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
   return hipErrorInvalidValue;
 }
 
@@ -448,34 +451,35 @@ GatePlan gate_plan(int64_t B, int d, int E, bool split) {
 
 hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const u32x4* wsp,
                             const float* bias, float* logits, int64_t B, int d, int E,
-                            hipStream_t s) {
+                            hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const GatePlan g = gate_plan(B, d, E, wsp != nullptr);
   const int eb = g.eb, ks = g.ks, mi = g.mi;
   switch (eb * 16 + ks) {
-    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
-    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s);
+    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
   }
 }
 
 template <int BE, int TM>
 hipError_t launch_gate_t(const void* x, bool x_bf16, const float* Wg, const float* bias,
-                         float* logits, int64_t B, int d, int E, hipStream_t s) {
+                         float* logits, int64_t B, int d, int E, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1) {
   constexpr int BT = (kWave / (BE / 4)) * TM;
   dim3 grid((unsigned)((B + BT - 1) / BT), (unsigned)((E + BE - 1) / BE));
   if (x_bf16)
-    hipLaunchKernelGGL((gate_kernel<BE, TM, true>), grid, dim3(kGateThreads), 0, s, x, Wg, bias,
-                       logits, B, d, E);
+    launch_timed((gate_kernel<BE, TM, true>), grid, dim3(kGateThreads), 0, s, e0, e1,
+                 x, Wg, bias, logits, B, d, E);
   else
-    hipLaunchKernelGGL((gate_kernel<BE, TM, false>), grid, dim3(kGateThreads), 0, s, x, Wg, bias,
-                       logits, B, d, E);
+    launch_timed((gate_kernel<BE, TM, false>), grid, dim3(kGateThreads), 0, s, e0, e1,
+                 x, Wg, bias, logits, B, d, E);
   return hipGetLastError();
 }
 
@@ -497,24 +501,27 @@ bool gate_use_split(bool x_bf16, int64_t B, int d, int E) {
 }
 
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
-                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s) {
+                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s,
+                       hipEvent_t e0, hipEvent_t e1) {
   if (B == 0) return hipSuccess;
   if (x_bf16 && wsplit) {
     const int neb = (E + 31) / 32, nks = (d + 15) / 16;
     const int64_t n = (int64_t)neb * nks * 64;
     const int64_t g = (n + 255) / 256;
-    hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0, s,
-                       Wg, d, E, neb, nks, static_cast<u32x4*>(wsplit));
+    // the start event goes with the first of the two launches
+    launch_timed(gate_split_kernel, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0,
+                 s, e0, nullptr, Wg, d, E, neb, nks, static_cast<u32x4*>(wsplit));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    e0 = nullptr;
   }
   if (x_bf16)
     return launch_gate_mfma(static_cast<const uint16_t*>(x), Wg, static_cast<const u32x4*>(wsplit),
-                            bias, logits, B, d, E, s);
-  if (E > 32) return launch_gate_t<64, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s);
-  if (E > 16) return launch_gate_t<32, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s);
-  if (E > 8) return launch_gate_t<16, 2>(x, x_bf16, Wg, bias, logits, B, d, E, s);
-  return launch_gate_t<8, 1>(x, x_bf16, Wg, bias, logits, B, d, E, s);
+                            bias, logits, B, d, E, s, e0, e1);
+  if (E > 32) return launch_gate_t<64, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
+  if (E > 16) return launch_gate_t<32, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
+  if (E > 8) return launch_gate_t<16, 2>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
+  return launch_gate_t<8, 1>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
 }
 
 }  // namespace moek

@@ -443,22 +443,29 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
   const bool xb = p->x_dtype == MOE_BF16;
   const int C = capacity_of(p);
   hipError_t e = hipSuccess;
-  auto mark = [&](int i) {
-    if (e == hipSuccess && out && out->events[i]) e = hipEventRecord(out->events[i], stream);
-  };
-  mark(0);
+  // stage events: dispatch timestamps of the stages' own kernels (no marker
+  // packets); with no tokens there are no kernels and every event is a marker
+  hipEvent_t ev[MOE_STAGE_EVENTS] = {};
+  if (out)
+    for (int i = 0; i < MOE_STAGE_EVENTS; ++i) ev[i] = out->events[i];
+  if (p->B == 0) {
+    for (int i = 0; i < MOE_STAGE_EVENTS && e == hipSuccess; ++i)
+      if (ev[i]) e = hipEventRecord(ev[i], stream);
+    for (int i = 0; i < MOE_STAGE_EVENTS; ++i) ev[i] = nullptr;
+  }
   if (e == hipSuccess)
-    e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, b.wsplit, stream);
-  mark(1);
+    e = moek::launch_gate(x, xb, Wg, bias, b.logits, p->B, p->d, p->E, b.wsplit, stream, ev[0],
+                          ev[1]);
   const bool redirect = p->overflow == MOE_OVERFLOW_NEXT;
   const int K2 = 2 * p->k < p->E ? 2 * p->k : p->E;
   if (e == hipSuccess) {
     if (redirect)
-      e = moek::launch_route(b.logits, p->B, p->E, K2, p->tau, b.ranked, b.ranked_w, stream);
+      e = moek::launch_route(b.logits, p->B, p->E, K2, p->tau, b.ranked, b.ranked_w, stream,
+                             ev[2], ev[3]);
     else
-      e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream);
+      e = moek::launch_route(b.logits, p->B, p->E, p->k, p->tau, b.idx, b.w, stream, ev[2],
+                             ev[3]);
   }
-  mark(2);
   if (!redirect) {
     if (e == hipSuccess)
       e = moek::launch_slots(b.idx, p->B, p->k, p->E, C, p->expert_unavailable, p->n_ranks,
@@ -488,28 +495,22 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
                              b.pos2, b.count1, b.eo, b.idx, b.w, b.pos, b.keep, b.dest,
                              b.pack_src, stream);
   }
-  if (e == hipSuccess) e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream);
-  // events 3 and 4: the expert FFN's first dispatch start and last dispatch
-  // end (no marker packets between the launches); with a shared expert its
-  // GEMMs follow the routed ones inside the same pair
-  hipEvent_t ev3 = out ? out->events[3] : nullptr, ev4 = out ? out->events[4] : nullptr;
+  if (e == hipSuccess)
+    e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream, nullptr, ev[4]);
+  // with a shared expert its GEMMs follow the routed ones inside the FFN pair
   if (p->B > 0) {
     if (e == hipSuccess)
       e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                   rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
-                                  stream, ev3, sh ? nullptr : ev4);
+                                  stream, ev[5], sh ? nullptr : ev[6]);
     if (e == hipSuccess && sh)
       e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
                                   sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,
-                                  ev4);
-  } else {
-    mark(3);
-    mark(4);
+                                  ev[6]);
   }
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
-                             p->k, p->d, kmax_of(p), stream, sh ? sh->S : nullptr);
-  mark(5);
+                             p->k, p->d, kmax_of(p), stream, sh ? sh->S : nullptr, ev[7], ev[8]);
   return hip_status(e);
 }
 

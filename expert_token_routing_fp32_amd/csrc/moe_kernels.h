@@ -2,6 +2,7 @@
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -123,14 +124,19 @@ __device__ __forceinline__ void route_token(const float* row, int E, int k, floa
 // ---- launchers --------------------------------------------------------------
 // wsplit: device scratch of gate_split_bytes(d, E) for the split copy of the
 // router weights (bf16 x only), or null to split inside the gate kernel;
-// both give bit-identical logits
+// both give bit-identical logits.
+// Events e0 / e1 (optional, on these launchers and the FFN's): recorded from
+// the start of the first kernel dispatch and the end of the last
+// (hipExtLaunchKernelGGL), so timing them adds no marker packets.
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
-                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s);
+                       float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s,
+                       hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 size_t gate_split_bytes(int d, int E);
 bool gate_use_split(bool x_bf16, int64_t B, int d, int E);
 
 hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,
-                        int32_t* idx, float* w, hipStream_t s);
+                        int32_t* idx, float* w, hipStream_t s, hipEvent_t e0 = nullptr,
+                        hipEvent_t e1 = nullptr);
 
 // slot assignment: tile geometry shared by the three kernels
 struct SlotPlan {
@@ -195,13 +201,15 @@ hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, in
                                 double* summary, void* ws, hipStream_t s);
 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k,
-                       int d, uint16_t* packed, hipStream_t s);
+                       int d, uint16_t* packed, hipStream_t s, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr);
 
 // shared (optional): a shared expert's output rows [B][d] bf16, added with
 // weight 1
 hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float* w,
                           const void* x_res, bool x_bf16, void* y, int64_t B, int k, int d,
-                          int64_t kmax, hipStream_t s, const uint16_t* shared = nullptr);
+                          int64_t kmax, hipStream_t s, const uint16_t* shared = nullptr,
+                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // The shared expert: one expert over every token's row of x (bf16) -- the
 // grouped GEMM with expert_offset = {0, B} (written into eo, 2 int32 of

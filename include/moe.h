@@ -309,6 +309,9 @@ moe_status_t moe_routing_stats(const moe_problem_t* p, const float* logits,
                                const moe_routing_stats_t* out, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* Number of stage events of moe_forward_out_t. */
+#define MOE_STAGE_EVENTS 9
+
 /* Optional outputs of moe_forward; any NULL field lives in the workspace. */
 typedef struct {
   float* logits;          /* [B][E]   */
@@ -325,15 +328,17 @@ typedef struct {
   moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
                              outputs overwrite the local rows in place) */
   /* Optional timing: each non-NULL events[i] is recorded on the call's
-   * stream at a stage boundary -- 0 before the gate, 1 after the gate, 2
-   * after the route, 3 at the start of the expert FFN's first kernel, 4 at
-   * the end of its last kernel, 5 after the combine -- so a caller can time
-   * stages inside a running sequence of forwards.  Events 3 and 4 are taken
-   * from the FFN dispatches' own start and end timestamps (3 -> 4 is the
-   * FFN's kernel time; the launch gap before it counts in 2 -> 3); the
-   * others are marker records, each costing a few microseconds of stream
-   * time.  The caller owns the events (created with timing enabled). */
-  hipEvent_t events[6];
+   * stream from the dispatch timestamps of the stages' own kernels
+   * (hipExtLaunchKernelGGL start / end events; no marker packets):
+   *   0 gate start          1 gate end
+   *   2 route start         3 route end
+   *   4 dispatch end (the pack kernel; 3 -> 4 is the slot kernels + pack)
+   *   5 expert FFN start    6 expert FFN end
+   *   7 combine start       8 combine end
+   * so 1 -> 2, 4 -> 5 and 6 -> 7 are the gaps between launches.  With
+   * B == 0 no kernel runs and every event is recorded as a marker.  The
+   * caller owns the events (created with timing enabled). */
+  hipEvent_t events[MOE_STAGE_EVENTS];
 } moe_forward_out_t;
 
 /* The whole layer, enqueued on one stream with no host synchronisation:
@@ -383,7 +388,7 @@ size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p,
 
 /* moe_forward with a shared expert: the routed layer of p, the shared
  * expert of ps on every token (after the routed expert GEMMs, inside the
- * same stage events 3 and 4), and the combine of moe_combine_shared.
+ * stage events 5 and 6), and the combine of moe_combine_shared.
  * x_dtype must be BF16 for both problems; ps->B == p->B, ps->d == p->d.
  *   wpacked_shared  moe_pack_weights(ps, ...) output
  *   ws >= moe_forward_shared_workspace_bytes(p, ps), 16-byte aligned;
@@ -446,11 +451,11 @@ moe_status_t moe_expert_choice_combine(const moe_problem_t* p,
                                        hipStream_t stream);
 
 /* Optional outputs of moe_forward_expert_choice; NULL fields live in the
- * workspace.  packed holds ret after the call (FFN in place).  events: as
- * moe_forward_out_t's (0 before the gate, 1 after it, 2 after the router
- * probabilities and the choice, 3 / 4 the expert FFN's first dispatch
- * start and last dispatch end, 5 after the combine; the pack falls in
- * 2 -> 3). */
+ * workspace.  packed holds ret after the call (FFN in place).  events:
+ * each non-NULL one recorded on the stream -- 0 before the gate, 1 after
+ * it, 2 after the router probabilities and the choice (markers), 3 / 4 the
+ * expert FFN's first dispatch start and last dispatch end, 5 after the
+ * combine (marker); the pack falls in 2 -> 3. */
 typedef struct {
   float* logits;          /* [B][E] */
   float* probs_t;         /* [E][B] */

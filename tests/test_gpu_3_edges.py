@@ -171,3 +171,31 @@ def test_pack_combine_past_the_grid_cap():
     w = torch.ones(B, 1, dtype=torch.float32, device="cuda")
     y = moe.combine(p, o["packed"], o["dest"], w)
     assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [dict(B=0), dict(B=96), dict(B=96, x_dtype="f32"),
+                                   dict(B=16384, E=128, e_end=128, d=128, f=64),
+                                   dict(B=96, E=8, n_ranks=2, e_begin=4, e_end=4)])
+def test_stage_events_follow_the_kernels(shape):
+    """moe_forward's stage events come from the dispatch timestamps of each
+    stage's kernels, in stream order, so every consecutive pair is ordered
+    (the gate's split copy, a forward with no local experts and an empty
+    batch, where every event is a marker, included), and the output is the
+    same as without events."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    w = _wl(name="events", **shape)
+    inp = moe_synth.make_inputs(w)
+    p = problem_for(w)
+    x = to_dev(inp["x"]) if w.B else torch.empty((0, w.d), dtype=torch.int16, device="cuda")
+    Wg = to_dev(inp["Wg"])
+    wp = packed_weights_for_gpu(p, inp)
+    say(f"[stage events] {w}")
+    y0 = moe.forward(p, x, Wg, None, wp)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)]
+    y1 = moe.forward(p, x, Wg, None, wp, stage_events=evs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(y1), to_np(y0))
+    for i in range(moe.N_STAGE_EVENTS - 1):
+        assert evs[i].elapsed_time(evs[i + 1]) >= -1e-3, i
+    assert evs[0].elapsed_time(evs[-1]) >= 0

@@ -102,10 +102,11 @@ def test_forward_shared(act):
     p = problem_for(w)
     ps = moe.shared_problem(p, fs, act)
     wp = packed_weights_for_gpu(p, inp)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)]
     y, o = moe.forward(p, to_dev(inp["x"]), to_dev(inp["Wg"]), None, wp, outputs=True,
                        stage_events=evs, shared=(ps, _pack_shared(ps, S1, S3, S2)))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(o["dest"]), ref["dest"])
     assert_bf16_close(oracle.bf16_bits_to_f64(to_np(y)), ref["y"], what=f"forward+shared {act}")
-    assert evs[3].elapsed_time(evs[4]) > 0
+    a, b = moe.STAGE_EVENTS["expert_ffn"]
+    assert evs[a].elapsed_time(evs[b]) > 0
