@@ -7,8 +7,12 @@ segments, grouped expert MLP on bf16 MFMA, weighted combine.  Inputs are
 seeded synthetic tensors of the workload's shape, resident in HBM before the
 timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload uniform] [--cold]
+  python bench.py [--steps K] [--warmup W] [--workload ep_share] [--cold]
                   [--no-cpu-baseline] [--gpus 1]
+
+The default workload is the largest one that fits one GPU: one rank's share
+of a 256-expert top-8 expert-parallel layer (32768 tokens, d = 7168, 32
+local SwiGLU experts of 2048), whose expert GEMM is matrix-core bound.
 """
 from __future__ import annotations
 
@@ -40,11 +44,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="uniform")
+    ap.add_argument("--workload", default="ep_share")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MB buffer before every step (flushes L2 and MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-tokens", type=int, default=0, metavar="N",
+                    help="tokens of the CPU oracle's sample (default: the whole batch up to "
+                         "4096 tokens, else the first 1024 tokens as a batch of their own)")
+    ap.add_argument("--no-cold-pass", action="store_true",
+                    help="skip the extra cold-cache pass of the default run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times: the "
                          "kernel of known traffic that HBM byte counters are scaled by")
@@ -178,23 +187,34 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
-                 overflow: str = "drop") -> dict:
+                 overflow: str = "drop", n_tokens: int = 0) -> dict:
+    """The oracle as it stands, timed on the host on a bounded sample: the
+    first n_tokens tokens of the batch as a batch of their own (same weights,
+    capacity from their own count), whole forward, repeated for about
+    budget_s seconds; tokens/s = sample tokens x runs / time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    if n_tokens <= 0:
+        n_tokens = w.B if w.B <= 4096 else 1024
+    n_tokens = min(n_tokens, w.B)
+    xs = inp["x"][:n_tokens]
+    sh = None
+    if shared is not None:
+        sh = shared
     reps, t_tot = 0, 0.0
     while reps == 0 or (t_tot < budget_s and reps < 20):
         t0 = time.perf_counter()
         if ec:
-            oracle.forward_expert_choice(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"],
+            oracle.forward_expert_choice(xs, inp["Wg"], inp["bias"], inp["W1"], inp["W3"],
                                          inp["W2"], k=w.k, c=w.c, act=w.act, tau=w.tau)
         else:
-            oracle.forward(inp["x"], inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
+            oracle.forward(xs, inp["Wg"], inp["bias"], inp["W1"], inp["W3"], inp["W2"],
                            k=w.k, c=w.c, act=w.act, n_ranks=w.n_ranks, e_begin=w.e_begin,
-                           e_end=w.e_end, tau=w.tau, shared=shared, overflow=overflow)
+                           e_end=w.e_end, tau=w.tau, shared=sh, overflow=overflow)
         t_tot += time.perf_counter() - t0
         reps += 1
     model = ""
@@ -206,10 +226,13 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
                     break
     except OSError:  # pragma: no cover
         pass
-    return {"value": round(w.B * reps / t_tot, 1), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": model,
-            "sample": f"the whole {w.name} batch ({w.B} tokens), oracle forward run {reps} times "
-                      f"({t_tot:.1f} s), float64 NumPy, input generation excluded"}
+    what = (f"the whole {w.name} batch ({w.B} tokens)" if n_tokens == w.B else
+            f"the first {n_tokens} of the {w.B} tokens of the {w.name} batch as a batch of "
+            f"their own (same weights and shape, capacity from {n_tokens} tokens)")
+    return {"value": round(n_tokens * reps / t_tot, 1), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle", "cpu_model": model,
+            "sample": f"{what}, oracle forward run {reps} times ({t_tot:.1f} s), float64 NumPy, "
+                      "input generation excluded"}
 
 
 def main():
@@ -282,9 +305,9 @@ def main():
         def bw(shape, fan_in):
             a = rs.normal(scale=fan_in ** -0.5, size=shape).astype(np.float32)
             return d16(moe_synth.f32_to_bf16_bits(a))
-        S1 = bw((1, fs, w.d), w.d)
-        S3 = bw((1, fs, w.d), w.d) if w.act == "swiglu" else None
-        S2 = bw((1, w.d, fs), fs)
+        S1 = bw((1, w.d, fs), w.d)
+        S3 = bw((1, w.d, fs), w.d) if w.act == "swiglu" else None
+        S2 = bw((1, fs, w.d), fs)
         ps = moe.shared_problem(p, fs, w.act)
         shared = (ps, moe.pack_weights(ps, S1, S3, S2))
         shared_np = (S1.cpu().numpy().view(np.uint16)[0],
@@ -361,6 +384,24 @@ def main():
 
     stage_s = {name: mean_s(ab) for name, ab in pairs.items()}
     gap_s = {name: mean_s(ab) for name, ab in gaps.items()}
+    # per-step device time of the breakdown run: first kernel's start to the
+    # last kernel's end (events from the dispatches), median over the steps
+    last_ev = n_ev - 1
+    warm_med = float(np.median([r[0].elapsed_time(r[last_ev]) for r in evs])) * 1e-3
+    cold_med = None
+    if not args.cold and not args.no_cold_pass:
+        # the same steps after a 512 MB write each (flushes L2 and the MALL);
+        # the write runs before the first event, so it is not in the time
+        fl = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for i in range(args.steps):
+            fl.fill_(1)
+            if ec:
+                moe.forward_expert_choice(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=evs[i])
+            else:
+                moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, stage_events=evs[i], shared=shared)
+        torch.cuda.synchronize()
+        cold_med = float(np.median([r[0].elapsed_time(r[last_ev]) for r in evs])) * 1e-3
+        del fl
     t_gate, t_route, t_disp, t_comb = (stage_s[k] for k in ("gate", "route", "dispatch", "combine"))
     log(f"[bench] {sec_per_step * 1e3:.3f} ms/step; " +
         ", ".join(f"{k} {v * 1e6:.1f} us" for k, v in stage_s.items()))
@@ -439,6 +480,12 @@ def main():
     rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]
     rpc_t = t_route + t_disp + t_comb
     breakdown = {
+        "step_ms_median": {
+            "warm": round(warm_med * 1e3, 4),
+            **({"cold": round(cold_med * 1e3, 4)} if cold_med is not None else {}),
+            "timing": ("first kernel's dispatch start to the last kernel's end, median over "
+                       f"{args.steps} steps; warm: the breakdown run; cold: the same steps, "
+                       "each after a 512 MB write that flushes L2 and the MALL")},
         "timing": ("stage events over a second run of the same number of steps"
                    + ("" if ec else ": each stage from its own kernels' dispatch start and end")),
         "expert_ffn_us_breakdown_run": round(stage_s["expert_ffn"] * 1e6, 2),
@@ -496,7 +543,7 @@ def main():
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds,
                                            shared_np if shared is not None else None, ec,
-                                           args.overflow)
+                                           args.overflow, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

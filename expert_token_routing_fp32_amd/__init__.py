@@ -218,22 +218,38 @@ def dispatch(p: Problem, x, topk_idx, ws=None) -> dict:
     return o
 
 
+def _shape(t, name: str, shape: tuple) -> None:
+    """Exact shape check (the library sees only pointers, so a matrix given
+    transposed would have the right size and the wrong meaning)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def pack_weights(p: Problem, W1, W3, W2, out=None):
-    """The local experts' weights (W1, W3: [n_local, f, d]; W2: [n_local, d, f],
-    bf16) in the blocked layout the expert GEMM streams; done once per model."""
+    """The local experts' weights in the blocked layout the expert GEMM
+    streams; done once per model.  [in, out] matrices as the layer's
+    configurations print them: W1, W3 [n_local, d, f], W2 [n_local, f, d]
+    (bf16), so that an expert computes act(x @ W1) @ W2."""
     _check(p)
     d, f = p.d, p.f
     nl = p.e_end - p.e_begin
+    if nl > 0:
+        _shape(W1, "W1", (nl, d, f))
+        _shape(W2, "W2", (nl, f, d))
+        if p.act == L.MOE_SWIGLU:
+            _shape(W3, "W3", (nl, d, f))
     n = weights_bytes(p)
     dev = W2.device if W2 is not None else torch.device("cuda")
     if out is None:
         out = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
     _need(out, "wpacked", n, 1)
     if nl > 0:
-        _need(W1, "W1", nl * f * d, 2)
-        _need(W2, "W2", nl * d * f, 2)
+        _need(W1, "W1", nl * d * f, 2)
+        _need(W2, "W2", nl * f * d, 2)
         if p.act == L.MOE_SWIGLU:
-            _need(W3, "W3", nl * f * d, 2)
+            _need(W3, "W3", nl * d * f, 2)
     L.check(lib().moe_pack_weights(ctypes.byref(p), _p(W1), _p(W3 if p.act == L.MOE_SWIGLU else None),
                                    _p(W2), _p(out), out.numel(), _stream()), "moe_pack_weights")
     return out

@@ -1,10 +1,11 @@
 // Expert-choice routing: every expert picks its top-C tokens of the batch.
 //
 // "Expert Parallelism" (narrativegoldmine.com), "Major Variants and
-// Families", expert choice routing: instead of each token choosing its
-// top-k experts, each expert chooses its top-C tokens from the batch, so
-// every expert processes exactly C tokens (balanced by construction) and a
-// token may be chosen by any number of experts.
+// Families", expert choice routing.  The rule implemented: the selection
+// runs per expert over the batch, not per token over the experts; expert e
+// keeps the C_e tokens with the highest scores in its column, so every
+// expert gets the same row count and a token can end up with several
+// experts or with none.
 //
 // Scores are the router probabilities p_te = softmax(g_t / tau)_e in fp32;
 // among equal scores the lower token wins; an expert's rows are packed in

@@ -461,11 +461,12 @@ __global__ __launch_bounds__(1024) void merge_offsets_kernel(
     sc[tid] += v;
     __syncthreads();
   }
-  // sc[i]: inclusive prefix over experts 0..i
-  if (tid <= E) expert_offset[tid] = tid == 0 ? 0 : sc[tid - 1];
-  if (tid <= D) {
-    const int i = tid * (E / D);
-    rank_offset[tid] = i == 0 ? 0 : sc[i - 1];
+  // sc[i]: inclusive prefix over experts 0..i.  E + 1 and D + 1 entries:
+  // with E (or D) = 1024 the last one is past the block's 1024 threads.
+  for (int i = tid; i <= E; i += 1024) expert_offset[i] = i == 0 ? 0 : sc[i - 1];
+  for (int r = tid; r <= D; r += 1024) {
+    const int i = r * (E / D);
+    rank_offset[r] = i == 0 ? 0 : sc[i - 1];
   }
 }
 

@@ -7,10 +7,11 @@
 // expert FFN cost.
 //
 // Two launches per call, each a grouped GEMM over the experts' contiguous
-// packed segments (rows [expert_offset[e], expert_offset[e+1])):
-//   GEMM1  H   = act(X . W1^T)               (GELU)   or
-//          H   = silu(X . W1^T) * (X . W3^T)  (SwiGLU, both products in one tile)
-//   GEMM2  Out = H . W2^T
+// packed segments (rows [expert_offset[e], expert_offset[e+1])), with the
+// weights as [in, out] matrices (W1, W3 [d][f], W2 [f][d]):
+//   GEMM1  H   = act(X . W1)              (GELU)   or
+//          H   = silu(X . W1) * (X . W3)  (SwiGLU, both products in one tile)
+//   GEMM2  Out = H . W2
 //
 // Weight streaming.  With ~100-2000 rows per expert the GEMMs of the smaller
 // workloads are bound by reading the weights from HBM once.  Weights are
@@ -645,10 +646,13 @@ hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s,
 // 32 KB block; inside it wavefront w's 8 KB, then MFMA step s's 2 KB, then
 // column block cb's 1 KB, then lane l's 16 bytes = K values
 // kt*64 + 16 s + 8 (l / 32) .. +7 of weight-tile row j = 64 w + 32 cb + l % 32
-// (zeros past N or K).  Tile row j is weight row nt*256 + j (GELU, plain);
-// for SwiGLU, block cb = 0 of wavefront w is W1 rows nt*128 + 32 w .. +31
-// and block cb = 1 the W3 rows of the same hidden units, so both products
-// of a hidden unit land in the same lane.
+// (zeros past N or K).  Tile row j is output column nt*256 + j (GELU,
+// plain); for SwiGLU, block cb = 0 of wavefront w holds the W1 columns of
+// hidden units nt*128 + 32 w .. +31 and block cb = 1 the W3 columns of the
+// same units, so both products of a hidden unit land in the same lane.
+// The source matrices are [in, out] per expert (W[e][k][n], K rows of Nw
+// columns: x . W), so a lane gathers its 8 K values from 8 rows; lanes
+// l % 32 read consecutive columns of one row, 64 bytes together.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ W0,
                                                            const uint16_t* __restrict__ W1,
                                                            int n_exp, int Nw, int K, int n_tiles,
@@ -677,7 +681,15 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
       src = W0;
     }
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (n < Nw && k < K) v = *(const u32x4*)(src + ((int64_t)e * Nw + n) * K + k);
+    if (n < Nw && k < K) {
+      // K is a multiple of 8, so k < K covers k .. k + 7
+      const uint16_t* col = src + ((int64_t)e * K + k) * Nw + n;
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = col[(int64_t)i * Nw];
+      v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                h[6] | (h[7] << 16)};
+    }
     *(u32x4*)(out + q * 8) = v;
   }
 }

@@ -269,9 +269,18 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   float wv[PS ? 1 : NSL][4][8];
   u32x4 wq[PS ? NSL : 1][4][3];
-  // PS: this wavefront's expert block in the split copy, and its first K step
+  // PS: this wavefront's expert block in the split copy, and its first K step.
+  // The copy holds neb = ceil(E / 32) blocks; a wavefront whose block lies
+  // past them (the last row of the grid when EB does not divide neb) reads
+  // the last block instead -- in bounds, and its results are never stored
+  // (e >= E below).
+  // Likewise a K range that starts past d (more K ranges than d needs)
+  // reads no step of its own: its base is clamped to the block's last step.
   const int nks = (d + 15) / 16;
-  const u32x4* wsb = Wsp + ((int64_t)(blockIdx.y * EB + eb) * nks + kb / 16) * 3 * 64 + lane;
+  const int neb = (E + 31) / 32;
+  const int ebs = (int)blockIdx.y * EB + eb < neb ? (int)blockIdx.y * EB + eb : neb - 1;
+  const int kb16 = kb / 16 < nks ? kb / 16 : nks - 1;
+  const u32x4* wsb = Wsp + ((int64_t)ebs * nks + kb16) * 3 * 64 + lane;
 
   // stage s (clamped to the last one): weights, then rows.  K chunks past
   // the end of the row read the row's last chunk; their weights are zero.
@@ -487,6 +496,35 @@ hipError_t launch_gate_t(const void* x, bool x_bf16, const float* Wg, const floa
 
 size_t gate_split_bytes(int d, int E) {
   return (size_t)((E + 31) / 32) * ((d + 15) / 16) * 3 * 1024;
+}
+
+// Exclusive end (bytes) of what gate_lds_kernel<..., PS = true> reads from
+// the split copy at (B, d, E), walking the launch the plan gives: every
+// workgroup row, wavefront expert block and K range, every stage and MFMA
+// step, with the kernel's own index arithmetic.
+int64_t gate_split_read_end(int64_t B, int d, int E) {
+  const GatePlan g = gate_plan(B, d, E, true);
+  const int neb = (E + 31) / 32, nks = (d + 15) / 16;
+  const int64_t gy = (neb + g.eb - 1) / g.eb;
+  const int kspan = (d + 64 * g.ks - 1) / (64 * g.ks) * 64;
+  const int nst = kspan / 64;
+  int64_t end = 0;
+  for (int64_t by = 0; by < gy; ++by)
+    for (int eb = 0; eb < g.eb; ++eb)
+      for (int kq = 0; kq < g.ks; ++kq) {
+        const int kb = kq * kspan, ke = kb + kspan < d ? kb + kspan : d;
+        const int ebs = by * g.eb + eb < neb ? (int)(by * g.eb + eb) : neb - 1;
+        const int kb16 = kb / 16 < nks ? kb / 16 : nks - 1;
+        const int64_t base = ((int64_t)ebs * nks + kb16) * 3 * 64;
+        for (int sc = 0; sc < nst; ++sc)
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = kb + 64 * sc + 16 * j < ke;
+            const int64_t st = ok ? (int64_t)(4 * sc + j) * 3 * 64 : 0;
+            const int64_t last = base + st + 2 * 64 + 63;  // part 2, lane 63
+            if (16 * (last + 1) > end) end = 16 * (last + 1);
+          }
+      }
+  return end;
 }
 
 bool gate_use_split(bool x_bf16, int64_t B, int d, int E) {

@@ -5,8 +5,9 @@
 // "Expert Parallelism" (inferensys.com glossary), "Practitioner Guidance":
 // expert utilisation and routing entropy are first-class health signals.
 // "Expert Parallelism" (narrativegoldmine.com), "Components and
-// Architecture", auxiliary load-balancing loss: per expert, the fraction of
-// tokens routed to it times the fraction of routing probability it receives.
+// Architecture", auxiliary load-balancing loss (the Switch form): computed
+// here as sum_e f_e P_e, f_e the share of tokens that chose expert e and P_e
+// its mean router probability.
 // "Expert Parallelism" (theinfinity.ai), figure text: each expert's bar is
 // the share of its capacity in use.
 //

@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "moe.h"
+#include "moe_check.h"
 #include "moe_kernels.h"
 
 namespace {
@@ -692,3 +693,11 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, const void* x, co
 }
 
 }  // extern "C"
+
+extern "C" int32_t moe_check_gate_split_reach(int64_t B, int32_t d, int32_t E, int64_t* read_end,
+                                              int64_t* copy_bytes) {
+  if (B < 1 || d < 8 || d % 8 || E < 1 || E > kMaxE || !read_end || !copy_bytes) return -1;
+  *read_end = moek::gate_split_read_end(B, d, E);
+  *copy_bytes = (int64_t)moek::gate_split_bytes(d, E);
+  return moek::gate_use_split(true, B, d, E) ? 1 : 0;
+}

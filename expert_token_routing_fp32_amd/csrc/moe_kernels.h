@@ -133,6 +133,9 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float*
                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 size_t gate_split_bytes(int d, int E);
 bool gate_use_split(bool x_bf16, int64_t B, int d, int E);
+// host-only: exclusive end of the split copy's bytes the split-copy gate
+// launch reads at (B, d, E) (a self-check of the launch plan)
+int64_t gate_split_read_end(int64_t B, int d, int E);
 
 hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,
                         int32_t* idx, float* w, hipStream_t s, hipEvent_t e0 = nullptr,

@@ -49,12 +49,13 @@
  *   of 8.
  * - Sizes: Kmax = min(B*k, E*C) bounds the number of kept assignments K; the
  *   exact K is expert_offset[E], known only on the device.
- * - Expert weights are given output-major, one matrix per expert: W1 and W3
- *   are [n_local][f][d] and W2 is [n_local][d][f], where
- *   n_local = e_end - e_begin; expert e computes W2 . act(W1 . x) (GELU) or
- *   W2 . (silu(W1 . x) * (W3 . x)) (SwiGLU), with no biases.  The expert GEMM
- *   streams them from a blocked copy made once by moe_pack_weights (see
- *   there); moe_expert_ffn and moe_forward take that copy.
+ * - Expert weights are [in, out] matrices, one per expert, row-major, as the
+ *   layer's configurations print them: W1 and W3 are [n_local][d][f] and W2
+ *   is [n_local][f][d], where n_local = e_end - e_begin; expert e computes,
+ *   on a token row x, act(x . W1) . W2 (GELU) or (silu(x . W1) * (x . W3)) . W2
+ *   (SwiGLU), with no biases.  The expert GEMM streams them from a blocked
+ *   copy made once by moe_pack_weights (see there); moe_expert_ffn and
+ *   moe_forward take that copy.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -219,15 +220,21 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x,
 size_t moe_weights_bytes(const moe_problem_t* p);
 
 /* Rearranges the local experts' weights into the blocked layout the expert
- * GEMM streams: per expert, per output tile (256 rows of W1 or W2, or 128
- * rows of W1 plus the same 128 rows of W3 for SwiGLU) and per 64-wide K
- * slice, one contiguous 32 KB block whose rows and 16-byte chunks are in the
- * order the GEMM keeps them in LDS; padding past f or d is zero.  A one-time
- * format conversion (weights are parameters), not part of the layer; the
- * caller does it when the weights are loaded and owns the copy.
- *   W1, W3  [n_local][f][d] bf16 (W3 only for SwiGLU, else NULL)
- *   W2      [n_local][d][f] bf16
- *   wpacked moe_weights_bytes(p) bytes, 16-byte aligned, out */
+ * GEMM streams: per expert, per output tile (256 output columns of W1 or W2,
+ * or 128 columns of W1 plus the same 128 columns of W3 for SwiGLU) and per
+ * 64-wide K slice, one contiguous 32 KB block whose columns and 16-byte K
+ * chunks are in the order the GEMM's matrix-core fragments take them;
+ * padding past f or d is zero.  A one-time format conversion (weights are
+ * parameters), not part of the layer; the caller does it when the weights
+ * are loaded and owns the copy ("Expert Parallelism", narrativegoldmine.com,
+ * "Components and Architecture", Expert GEMM: each expert is a standard
+ * MLP, x . W1 then x . W2).
+ *   W1, W3  [n_local][d][f] bf16, [in, out] (W3 only for SwiGLU, else NULL)
+ *   W2      [n_local][f][d] bf16, [in, out]
+ *   wpacked moe_weights_bytes(p) bytes, 16-byte aligned, out
+ * The library cannot see tensor shapes: a matrix in the transposed layout
+ * has the same size and is not detected here (the Python binding checks
+ * full shapes). */
 moe_status_t moe_pack_weights(const moe_problem_t* p, const moe_bf16_t* W1,
                               const moe_bf16_t* W3, const moe_bf16_t* W2,
                               void* wpacked, size_t wpacked_bytes,
@@ -275,8 +282,8 @@ moe_status_t moe_unpack(const moe_problem_t* p, const moe_bf16_t* ret,
 /* Routing-health signals of one batch ("Expert Parallelism", inferensys.com
  * glossary, "Practitioner Guidance": expert utilisation and routing entropy
  * as health signals; narrativegoldmine.com, "Components and Architecture",
- * auxiliary load-balancing loss: per expert, the fraction of tokens routed
- * to it times the fraction of routing probability it receives;
+ * auxiliary load-balancing loss, Switch form: sum over experts of the token
+ * share f_e times the mean router probability P_e;
  * theinfinity.ai, figure text: each expert's bar is the share of its
  * capacity in use).  With p_t = softmax(logits_t / tau), n_e = expert_load,
  * kept_e = expert_count and C the problem's capacity:
@@ -341,8 +348,16 @@ typedef struct {
   hipEvent_t events[MOE_STAGE_EVENTS];
 } moe_forward_out_t;
 
-/* The whole layer, enqueued on one stream with no host synchronisation:
+/* The whole layer, enqueued on one stream with no host synchronisation, in
+ * the order of "Expert Parallelism" (narrativegoldmine.com), "Formal
+ * Algorithm: Expert Parallelism Forward Pass" -- router logits, softmax and
+ * top-k, dispatch under the capacity, expert computation, weighted combine
+ * (and the residual when add_residual) -- with the two all-to-alls of "Expert
+ * Parallelism and the All-to-All Bottleneck", "The Mechanism of Expert
+ * Parallelism", replaced by the on-device pack and the identity return:
  * gate, route, dispatch, expert FFN (in place on the packed rows), combine.
+ * Errors: as the stage calls (checks before any launch); MOE_ERR_WORKSPACE
+ * when ws is smaller than moe_workspace_bytes(p, MOE_OP_FORWARD).
  *   x [B][d] x_dtype; Wg [d][E] f32; bias [E] f32 or NULL;
  *   wpacked as in moe_expert_ffn; y [B][d] x_dtype out;
  *   out may be NULL; ws >= moe_workspace_bytes(p, MOE_OP_FORWARD). */

@@ -27,10 +27,11 @@ the *input format*, not arithmetic):
 
 * ``x``   [B, d]: float32 for the toy workload, bf16 bits (uint16) otherwise.
 * ``Wg``  [d, E] float32; router logits are ``x @ Wg (+ bias)``.
-* ``W1``, ``W3`` [E_loc, f, d] and ``W2`` [E_loc, d, f]: each expert matrix is
-  stored output-major, so one expert computes ``W2 @ act(W1 @ x)``.  bf16 bits,
-  except the toy workload, which keeps float32 originals in ``W*`` and their
-  bf16 round-to-nearest-even copies in ``W*_bits``.
+* ``W1``, ``W3`` [E_loc, d, f] and ``W2`` [E_loc, f, d]: each expert matrix is
+  stored [in, out] row-major, as the workloads print them (``W1[d x f]``,
+  ``W2[f x d]``), so one expert computes ``act(x @ W1) @ W2`` on a row x.
+  bf16 bits, except the toy workload, which keeps float32 originals in ``W*``
+  and their bf16 round-to-nearest-even copies in ``W*_bits``.
 * ``bias`` [E] float32 or None.
 
 Random numbers: NumPy PCG64 streams derived from ``SeedSequence(seed)``; one
@@ -183,10 +184,10 @@ def make_inputs(w: Workload, with_weights: bool = True) -> dict:
     if with_weights:
         sd1 = 1.0 / math.sqrt(w.d)
         sd2 = 1.0 / math.sqrt(w.f)
-        inp["W1"] = _expert_weights(s_w1, w, w.f, w.d, sd1, to_bf16=bf16)
-        inp["W3"] = (_expert_weights(s_w3, w, w.f, w.d, sd1, to_bf16=bf16)
+        inp["W1"] = _expert_weights(s_w1, w, w.d, w.f, sd1, to_bf16=bf16)
+        inp["W3"] = (_expert_weights(s_w3, w, w.d, w.f, sd1, to_bf16=bf16)
                      if w.act == "swiglu" else None)
-        inp["W2"] = _expert_weights(s_w2, w, w.d, w.f, sd2, to_bf16=bf16)
+        inp["W2"] = _expert_weights(s_w2, w, w.f, w.d, sd2, to_bf16=bf16)
         if not bf16:
             # the expert GEMM consumes bf16 operands: keep rounded copies
             for n in ("W1", "W3", "W2"):

@@ -53,8 +53,9 @@ design notes of the repository):
   order, then all second choices, ...; a dropped assignment contributes zero;
 * the packed buffer is compact and expert-major (hence destination-rank
   major), rows of one expert in claim order;
-* an expert is W2 . act(W1 . x) with exact-erf GELU, or
-  W2 . (silu(W1 . x) * (W3 . x)) for SwiGLU, with no biases;
+* an expert is act(x W1) W2 on a row x with exact-erf GELU, or
+  (silu(x W1) * (x W3)) W2 for SwiGLU, with no biases; the weights are
+  [in, out] matrices as the workloads print them (W1, W3 [d, f], W2 [f, d]);
 * rows owned by experts that do not run on this GPU come back unchanged (the
   missing collective is the identity).
 
@@ -74,6 +75,7 @@ __all__ = [
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
     "expert_capacities", "routing_stats", "shared_ffn", "router_probs", "expert_choice",
     "expert_choice_combine", "forward_expert_choice", "assign_slots_redirect",
+    "combine_by_segment",
 ]
 
 
@@ -391,23 +393,23 @@ def _w(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
 
 def expert_mlp(xr: np.ndarray, W1: np.ndarray, W2: np.ndarray,
                W3: Optional[np.ndarray], act: str) -> np.ndarray:
-    """One expert on rows xr [n, d] (float64): W2 . act(W1 . x) per row.
+    """One expert on rows xr [n, d] (float64): act(xr W1) W2.
 
     [EP-notes] "Components and Architecture", Expert GEMM: the expert is a
-    standard transformer MLP.  W1, W3: [f, d]; W2: [d, f] (output-major),
-    bf16 bits or float32.  GELU is exact-erf; SwiGLU is
-    silu(W1 x) * (W3 x); no biases.  Pins: an independent float64 library
-    MLP, E = 1 plain-MLP reduction (test_oracle_ffn)."""
+    standard transformer MLP.  W1, W3: [d, f]; W2: [f, d] ([in, out], the
+    layout the workloads print), bf16 bits or float32.  GELU is exact-erf;
+    SwiGLU is silu(x W1) * (x W3); no biases.  Pins: an independent float64
+    library MLP, E = 1 plain-MLP reduction (test_oracle_ffn)."""
     w1 = _w(W1)
     w2 = _w(W2)
-    h = xr @ w1.T
+    h = xr @ w1
     if act == "gelu":
         h = gelu(h)
     elif act == "swiglu":
-        h = silu(h) * (xr @ _w(W3).T)
+        h = silu(h) * (xr @ _w(W3))
     else:
         raise ValueError(act)
-    return h @ w2.T
+    return h @ w2
 
 
 def expert_ffn(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
@@ -452,7 +454,7 @@ def shared_ffn(x: np.ndarray, W1, W2, W3, act: str,
     [EP-notes] "Major Variants and Families", shared expert routing: one
     expert processes every token in addition to the routed experts (a dense
     path beside them).  It is an expert like the others (``expert_mlp``,
-    W1/W3 [f, d], W2 [d, f]) applied to every token's input, with weight 1.
+    W1/W3 [d, f], W2 [f, d]) applied to every token's input, with weight 1.
     Pin: a shared expert equals a routed expert that every token chooses
     with probability 1 (E = 1, k = 1, no drops), computed through route,
     slots, layout, expert_ffn and combine (test_oracle_shared)."""
@@ -497,6 +499,50 @@ def combine(ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
     return acc
 
 
+def combine_by_segment(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
+                       e_begin: int, e_end: int, W1, W2, W3, act: str,
+                       dest: np.ndarray, w: np.ndarray,
+                       x_residual: Optional[np.ndarray] = None,
+                       shared: Optional[np.ndarray] = None) -> np.ndarray:
+    """The same y as ``combine(expert_ffn(...), dest, w, ...)`` without
+    holding the whole return buffer: the packed rows are taken one expert
+    segment at a time (its MLP for a local expert, the packed values for a
+    remote one, as ``expert_ffn``), and each row's weighted value is added
+    to its token's sum at once.  The terms of a token are therefore added in
+    expert order rather than in j order; in float64 the two sums differ by a
+    few float64 ulps.  For large batches (the return buffer of 262144 rows of
+    7168 would take 15 GB in float64).  Pin: equal to the j-order combine
+    within 1e-13 on small layers, with and without remote rows, drops and
+    the residual (test_oracle_combine_special)."""
+    B, k = dest.shape
+    d = x.shape[1]
+    pack_src = np.asarray(pack_src, dtype=np.int64)
+    w32 = np.asarray(w, dtype=np.float32).astype(np.float64)
+    # which choice j of its token each packed row is
+    j_of = np.empty(pack_src.shape[0], dtype=np.int64)
+    for j in range(k):
+        m = dest[:, j] >= 0
+        j_of[dest[m, j].astype(np.int64)] = j
+    acc = np.zeros((B, d))
+    E = expert_offset.shape[0] - 1
+    for e in range(E):
+        a, b = int(expert_offset[e]), int(expert_offset[e + 1])
+        if b <= a:
+            continue
+        rows = np.arange(a, b)
+        seg = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3, act,
+                         rows=rows) if e_begin <= e < e_end else \
+            bf16_bits_to_f64(pack(x, pack_src[rows]))
+        t = pack_src[rows]
+        # a token appears at most once in one expert's segment
+        acc[t] += w32[t, j_of[rows]][:, None] * seg
+    if shared is not None:
+        acc += np.asarray(shared, dtype=np.float64)
+    if x_residual is not None:
+        acc += _x_values(x_residual)
+    return acc
+
+
 # ----------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------
@@ -504,7 +550,8 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
             n_ranks: int = 1, e_begin: int = 0, e_end: Optional[int] = None,
             tau: float = 1.0, C: Optional[int] = None, add_residual: bool = False,
             logits: Optional[np.ndarray] = None, unavailable=None,
-            shared: Optional[tuple] = None, overflow: str = "drop") -> dict:
+            shared: Optional[tuple] = None, overflow: str = "drop",
+            keep_ret: Optional[bool] = None) -> dict:
     """All steps in the pages' order ([EP-notes] "Formal Algorithm";
     [EP-a2a] "The Mechanism of Expert Parallelism"): gate, top-k, capacity
     and slots, pack, expert FFN, unpack + weighted combine (+ residual).
@@ -515,7 +562,9 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
     token's combine.  ``overflow`` = "next" redirects overflow to the
     token's next-best experts (``assign_slots_redirect``, the router giving
     min(2k, E) ranked choices); idx / w then hold the expert and weight each
-    assignment ends with."""
+    assignment ends with.  ``keep_ret``: hold the whole return buffer and
+    return it as ``ret`` (default: when it has at most 2^26 values); without
+    it y comes from ``combine_by_segment``."""
     B = x.shape[0]
     E = Wg.shape[1] if Wg is not None else logits.shape[1]
     e_end = E if e_end is None else e_end
@@ -542,13 +591,20 @@ def forward(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str,
                rank_offset=rank_offset, dest=dest, pack_src=pack_src,
                packed=packed)
     if W1 is not None:
-        ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3, act)
-        out["ret"] = ret
+        if keep_ret is None:
+            keep_ret = pack_src.shape[0] * x.shape[1] <= (1 << 26)
         sh = None
         if shared is not None:
             sh = shared_ffn(x, shared[0], shared[2], shared[1], act)
             out["shared_out"] = sh
-        out["y"] = combine(ret, dest, w, x if add_residual else None, shared=sh)
+        if keep_ret:
+            ret = expert_ffn(x, pack_src, expert_offset, e_begin, e_end, W1, W2, W3, act)
+            out["ret"] = ret
+            out["y"] = combine(ret, dest, w, x if add_residual else None, shared=sh)
+        else:
+            out["y"] = combine_by_segment(x, pack_src, expert_offset, e_begin, e_end, W1, W2,
+                                          W3, act, dest, w, x if add_residual else None,
+                                          shared=sh)
     return out
 
 
@@ -563,10 +619,10 @@ def routing_stats(logits: np.ndarray, expert_load: np.ndarray, expert_count: np.
     entropy are first-class health signals; [EP-infinity] figure text: the
     bar of an expert is the share of its capacity used, a dashed bar an
     expert at capacity that drops; [EP-notes] "Components and
-    Architecture", auxiliary load-balancing loss: the Switch loss penalises,
-    per expert, the product of the fraction of tokens routed to it and the
-    fraction of routing probability it receives (the caller applies the
-    coefficient; the page prints no scaling by E).
+    Architecture", auxiliary load-balancing loss, Switch form: here
+    sum_e f_e P_e with f_e the share of tokens that chose e and P_e its mean
+    router probability (the caller applies the coefficient; the page prints
+    no scaling by E).
 
     Readings (the pages give no formulas):
       prob_mean[e]  P_e = (1/B) sum_t p_te, p_t = softmax(g_t / tau);
@@ -617,10 +673,11 @@ def router_probs(logits: np.ndarray, tau: float = 1.0) -> np.ndarray:
 def expert_choice(probs: np.ndarray, C: int):
     """Every expert chooses its top-C tokens of the batch by score.
 
-    [EP-notes] "Major Variants and Families", expert choice routing: each
-    expert picks its top-C tokens from the batch instead of each token
-    picking experts, so every expert processes exactly C tokens and a token
-    may be chosen by any number of experts, including none.  Readings: the
+    [EP-notes] "Major Variants and Families", expert choice routing: the
+    selection runs per expert over the batch's tokens rather than per token
+    over the experts; expert e keeps the C tokens scoring highest in its
+    column, so all experts get equal row counts and a token may be kept by
+    several experts or by none.  Readings: the
     score of (t, e) is the router probability p_te (float32); C is the
     problem's capacity, at most B; among equal scores the lower token index
     wins; an expert's rows are packed in token order, experts one after the

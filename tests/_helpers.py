@@ -129,3 +129,62 @@ def sample_rows(eo: np.ndarray, e_begin: int, e_end: int, n: int, seed: int = 0)
     if rows.size > n:
         rows = np.sort(rng.choice(rows, size=n, replace=False))
     return rows
+
+
+def row_slices(M: int, bm: int = 256):
+    """The row slices the grouped expert GEMM cuts an expert's M rows into:
+    ceil(M / bm) slices over which the ceil(M / 32) row blocks of 32 are
+    dealt as evenly as possible (the first nb % nsl slices take one block
+    more).  Returns [(first_row, n_rows)], relative to the expert's first
+    row.  Used only to choose which rows a test compares."""
+    if M <= 0:
+        return []
+    nsl = (M + bm - 1) // bm
+    nb = (M + 31) // 32
+    q, r = divmod(nb, nsl)
+    out = []
+    for m in range(nsl):
+        m0 = 32 * (m * q + min(m, r))
+        span = 32 * (q + (1 if m < r else 0))
+        out.append((m0, min(M - m0, span)))
+    return out
+
+
+def tile_rows(eo: np.ndarray, e_begin: int, e_end: int, seed: int = 0):
+    """Packed rows that hit every tile of the grouped expert GEMM: for every
+    local expert, the first and last row of each of its row slices and one
+    random row of each of its 32-row blocks (every sampled row is compared
+    over all output columns, so every output tile of that slice is hit).
+    Returns (rows, stats) with the counts of experts, slices and blocks."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    n_exp = n_sl = n_blk = 0
+    for e in range(e_begin, e_end):
+        a, b = int(eo[e]), int(eo[e + 1])
+        M = b - a
+        if M <= 0:
+            continue
+        n_exp += 1
+        for m0, n in row_slices(M):
+            n_sl += 1
+            rows += [a + m0, a + m0 + n - 1]
+        for b0 in range(0, M, 32):
+            n_blk += 1
+            rows.append(a + b0 + int(rng.integers(0, min(32, M - b0))))
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    return rows, dict(experts=n_exp, slices=n_sl, blocks=n_blk, rows=int(rows.size))
+
+
+def assert_bf16_close_per_expert(got, ref, rows, eo, e_begin, e_end, tol=TOL_BF16, what=""):
+    """The bf16 tolerance on the whole tensor and on each expert's rows alone
+    (a small-magnitude expert cannot hide behind a large one)."""
+    assert_bf16_close(got, ref, tol, what)
+    worst, we = 0.0, -1
+    for e in range(e_begin, e_end):
+        m = (rows >= int(eo[e])) & (rows < int(eo[e + 1]))
+        if m.any():
+            r = rel_err(got[m], ref[m])
+            if r > worst:
+                worst, we = r, e
+            assert r <= tol, f"{what}: expert {e}: {r} > {tol}"
+    say(f"  {what}: worst expert {we}: max|d|/max|ref| = {worst:.3e}")

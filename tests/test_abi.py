@@ -249,3 +249,27 @@ def test_stage_event_count_and_pairs_match_the_header(L):
     assert all(a < b for a, b in pairs)
     assert pairs[0][0] == 0 and pairs[-1][1] == n - 1
     assert all(p[1] == q[0] for p, q in zip(pairs, pairs[1:]))
+
+
+def test_check_header_symbols_are_exported(lib):
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_check.h")).read(),
+                 flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    assert names == ["moe_check_gate_split_reach"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_pack_weights_checks_full_shapes(L, lib):
+    """Weights are [in, out] per expert (W1, W3 [n_local, d, f], W2
+    [n_local, f, d]); the same tensors transposed have the same size and must
+    be refused by their shape, before anything is allocated or launched."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    p = moe.make_problem(B=64, d=32, E=4, k=2, c=1.0, f=48, act="swiglu")
+    W1 = torch.zeros(4, 32, 48, dtype=torch.bfloat16)
+    W2 = torch.zeros(4, 48, 32, dtype=torch.bfloat16)
+    for args, what in [((W1.transpose(1, 2), W1, W2), "W1"), ((W1, W1, W2.transpose(1, 2)), "W2"),
+                       ((W1, W1.transpose(1, 2), W2), "W3"), ((W1[:2], W1, W2), "W1")]:
+        with pytest.raises(ValueError, match=f"{what}: shape"):
+            moe.pack_weights(p, *args)

@@ -7,16 +7,20 @@ the expert FFN), so each kernel is judged on its own:
 * fp32 logits and gate weights within 1e-5 * max(1, |ref|);
 * bf16 outputs within max|d| / max|ref| <= 2e-2.
 
-The expert MLP is checked on all rows for the small workloads and on sampled
-rows (first/last of every local expert plus random ones) for the large ones,
-where the float64 oracle would take minutes."""
+The expert MLP is checked on every local row where the float64 oracle takes
+seconds (kept local rows x f up to 4096 x 8192: toy, uniform, skewed) and
+otherwise on rows that hit every tile of the grouped GEMM's schedule (the
+first and last row of every row slice and one row of every 32-row block of
+every local expert, compared over all output columns), per expert as well as
+over the whole tensor."""
 import numpy as np
 import pytest
 
 import oracle
 from moe_synth import ORDER
-from _helpers import (assert_bf16_close, assert_f32_close, problem_for, sample_rows, say,
-                      to_dev, to_np, packed_weights_for_gpu, workload)
+from _helpers import (assert_bf16_close, assert_bf16_close_per_expert, assert_f32_close,
+                      problem_for, say, tile_rows, to_dev, to_np, packed_weights_for_gpu,
+                      workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,15 +102,22 @@ def test_expert_ffn(wl):
     keep_copy = packed_d.clone()
     eo_d = to_dev(eo)
     ret = moe.expert_ffn(p, packed_d, eo_d, d["wp"])
-    full = w.B * w.f <= 4096 * 4096
-    rows = np.arange(int(eo[w.e_begin]), int(eo[w.e_end])) if full else \
-        sample_rows(eo, w.e_begin, w.e_end, 96)
+    kloc = int(eo[w.e_end]) - int(eo[w.e_begin])
+    full = kloc * w.f <= 4096 * 8192
+    if full:
+        rows = np.arange(int(eo[w.e_begin]), int(eo[w.e_end]))
+        say(f"  {name}: all {rows.size} local rows")
+    else:
+        rows, st = tile_rows(eo, w.e_begin, w.e_end)
+        say(f"  {name}: {st['rows']} of {kloc} local rows, covering {st['experts']} experts, "
+            f"{st['slices']} row slices, {st['blocks']} 32-row blocks")
     exp = oracle.expert_ffn(inp["x"], ref["pack_src"], eo, w.e_begin, w.e_end, inp["W1"],
                             inp["W2"], inp["W3"], w.act, rows=rows)
     rows_t = torch.from_numpy(rows).to("cuda")
     got_bits = to_np(ret[rows_t])
     got = oracle.bf16_bits_to_f64(got_bits)
-    assert_bf16_close(got, exp, what=f"{name} ret ({len(rows)} local rows)")
+    assert_bf16_close_per_expert(got, exp, rows, eo, w.e_begin, w.e_end,
+                                 what=f"{name} ret ({len(rows)} local rows)")
     # rows of experts that run on other ranks come back unchanged
     lo, hi = int(eo[w.e_begin]), int(eo[w.e_end])
     if lo > 0:

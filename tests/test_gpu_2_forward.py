@@ -65,12 +65,25 @@ def run_forward(w, inp, ref, name, n_sample=48):
     kdiff = np.nonzero((gkeep != ref["keep"]).any(axis=1) | (gi != ref["idx"]).any(axis=1))[0]
     assert kdiff.size <= 3 * diff.size
     agree = np.setdiff1d(np.arange(w.B), kdiff)
-    # y on sampled agreeing tokens (all of them for the small workloads)
-    if w.B * w.f <= 4096 * 4096:
+    # y on every agreeing token for the small workloads; otherwise on
+    # sampled agreeing tokens that reach every local expert (the tokens of
+    # its first and last row and of one random row), plus random ones
+    K_all = int(ref["expert_offset"][-1])
+    if K_all * w.f <= 4096 * 8192 and w.B * w.d <= 16384 * 2048:
         tokens = agree
     else:
         rng = np.random.default_rng(2)
-        tokens = np.sort(rng.choice(agree, size=min(n_sample, agree.size), replace=False))
+        eo, ps = ref["expert_offset"], ref["pack_src"]
+        pick = []
+        for e in range(w.e_begin, w.e_end):
+            a, b = int(eo[e]), int(eo[e + 1])
+            if b > a:
+                pick += [int(ps[a]), int(ps[b - 1]), int(ps[int(rng.integers(a, b))])]
+        pick += list(rng.choice(agree, size=min(n_sample, agree.size), replace=False))
+        tokens = np.intersect1d(np.unique(np.array(pick, dtype=np.int64)), agree)
+        reached = np.unique(ref["idx"][tokens][ref["keep"][tokens]])
+        local = reached[(reached >= w.e_begin) & (reached < w.e_end)]
+        say(f"  {name}: {tokens.size} sampled tokens reach {local.size} local experts")
     dsub = ref["dest"][tokens]
     rows = np.unique(dsub[dsub >= 0])
     ret = oracle.expert_ffn(inp["x"], ref["pack_src"], ref["expert_offset"], w.e_begin, w.e_end,
@@ -101,7 +114,8 @@ def test_forward_is_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("B,d,E", [(8192, 320, 128), (16384, 328, 100), (16384, 512, 256)])
+@pytest.mark.parametrize("B,d,E", [(8192, 320, 128), (16384, 328, 100), (16384, 512, 256),
+                                   (8192, 512, 160)])
 def test_forward_gate_matches_moe_gate(B, d, E):
     """Where that fills the CUs (here: every shape) the forward splits the
     router weights once into a bf16 copy before the gate; moe_gate splits
@@ -109,15 +123,17 @@ def test_forward_gate_matches_moe_gate(B, d, E):
     The MFMAs see the same three parts in the same order, so the logits must
     be bit-identical.  Shapes: a K range whose last 64-k stage lies past d
     (d = 320 over two K ranges), d not a multiple of 16 with E not a multiple
-    of 32, and 256 experts in one workgroup."""
+    of 32, 256 experts in one workgroup, and 160 experts (5 blocks of 32
+    over workgroups of 4: the second row of workgroups has three blocks past
+    the last one, which must read only inside the split copy)."""
     import torch
     import expert_token_routing_fp32_amd as moe
     p = moe.make_problem(B=B, d=d, E=E, k=2, c=1.25, f=16, act="gelu", x_dtype="bf16")
     g = torch.Generator(device="cuda").manual_seed(B + d + E)
     x = torch.randn(B, d, device="cuda", generator=g).to(torch.bfloat16)
     Wg = torch.randn(d, E, device="cuda", generator=g) * d ** -0.5
-    W1 = (torch.randn(E, 16, d, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
-    W2 = (torch.randn(E, d, 16, device="cuda", generator=g) * 0.25).to(torch.bfloat16)
+    W1 = (torch.randn(E, d, 16, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
+    W2 = (torch.randn(E, 16, d, device="cuda", generator=g) * 0.25).to(torch.bfloat16)
     wp = moe.pack_weights(p, W1, None, W2)
     say(f"[gate split] B={B} d={d} E={E}")
     lg = moe.gate(p, x, Wg)

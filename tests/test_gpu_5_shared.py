@@ -19,12 +19,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _shared_weights(rng, d, f, swiglu):
-    """bf16 bits of W1s [1, f, d], W3s, W2s [1, d, f] with std 1/sqrt(fan_in)."""
+    """bf16 bits of W1s [1, d, f], W3s, W2s [1, f, d] with std 1/sqrt(fan_in)."""
     def bf(a):
         return oracle.f32_to_bf16_bits_rne(a.astype(np.float32))
-    W1 = bf(rng.normal(scale=d ** -0.5, size=(1, f, d)))
-    W3 = bf(rng.normal(scale=d ** -0.5, size=(1, f, d))) if swiglu else None
-    W2 = bf(rng.normal(scale=f ** -0.5, size=(1, d, f)))
+    W1 = bf(rng.normal(scale=d ** -0.5, size=(1, d, f)))
+    W3 = bf(rng.normal(scale=d ** -0.5, size=(1, d, f))) if swiglu else None
+    W2 = bf(rng.normal(scale=f ** -0.5, size=(1, f, d)))
     return W1, W3, W2
 
 

@@ -43,6 +43,10 @@ CHOICE_CASES = {
     "whole_batch": dict(B=90, E=6, k=6, c=1.0, ties=False),
     "one_expert": dict(B=333, E=1, k=1, c=0.5, ties=True),
     "ep_share_shape": dict(B=32768, E=256, k=8, c=1.25, ties=False),
+    # past 36864 tokens the score column no longer fits in LDS and the
+    # select reads it from global memory (the other kernel variant)
+    "column_in_global": dict(B=40000, E=8, k=2, c=1.0, ties=False),
+    "column_in_global_ties": dict(B=40000, E=8, k=2, c=1.0, ties=True),
 }
 
 

@@ -65,8 +65,10 @@ def _wl(**kw):
 
 @pytest.mark.parametrize("kw", [dict(), dict(E=6, e_end=6, k=2, B=300),
                                 dict(E=32, e_end=32, k=4, B=700, act="swiglu", f=40),
-                                dict(E=8, e_end=8, k=8, B=200, c=0.5)],
-                         ids=["fused_scan", "separate_scan_E6", "k4_swiglu", "k_equals_E"])
+                                dict(E=8, e_end=8, k=8, B=200, c=0.5),
+                                dict(E=1024, e_end=1024, n_ranks=1024, k=2, B=600)],
+                         ids=["fused_scan", "separate_scan_E6", "k4_swiglu", "k_equals_E",
+                              "E1024_D1024"])
 def test_forward_redirect(kw):
     w = _wl(**kw)
     say(f"[redirect] {w}")

@@ -25,12 +25,12 @@ def _dense_mixture(x, Wg, bias, W1, W3, W2, k, act):
         G[t, order] = p[t, order]
     y = torch.zeros_like(tx)
     for e in range(E):
-        h = torch.nn.functional.linear(tx, torch.from_numpy(W1[e]).double())
+        h = tx @ torch.from_numpy(W1[e]).double()
         if act == "gelu":
             h = torch.nn.functional.gelu(h)
         else:
-            h = torch.nn.functional.silu(h) * torch.nn.functional.linear(tx, torch.from_numpy(W3[e]).double())
-        y += G[:, e:e + 1] * torch.nn.functional.linear(h, torch.from_numpy(W2[e]).double())
+            h = torch.nn.functional.silu(h) * (tx @ torch.from_numpy(W3[e]).double())
+        y += G[:, e:e + 1] * (h @ torch.from_numpy(W2[e]).double())
     return y.numpy()
 
 
@@ -41,9 +41,9 @@ def test_no_drop_equals_dense_topk_mixture(act, k):
     x = rng.standard_normal((B, d)).astype(np.float32)
     Wg = rng.standard_normal((d, E)).astype(np.float32)
     bias = rng.standard_normal(E).astype(np.float32)
-    W1 = rng.standard_normal((E, f, d)).astype(np.float32) / 3
-    W3 = rng.standard_normal((E, f, d)).astype(np.float32) / 3
-    W2 = rng.standard_normal((E, d, f)).astype(np.float32) / 3
+    W1 = rng.standard_normal((E, d, f)).astype(np.float32) / 3
+    W3 = rng.standard_normal((E, d, f)).astype(np.float32) / 3
+    W2 = rng.standard_normal((E, f, d)).astype(np.float32) / 3
     out = oracle.forward(x, Wg, bias, W1, W3 if act == "swiglu" else None, W2,
                          k=k, c=float(E), act=act)  # c = E -> C = B*k, no drops
     assert out["keep"].all()
@@ -57,8 +57,8 @@ def test_zero_capacity_gives_zero_output_and_residual_passthrough():
     B, d, f, E = 4, 8, 8, 3
     x = rng.standard_normal((B, d)).astype(np.float32)
     Wg = rng.standard_normal((d, E)).astype(np.float32)
-    W1 = rng.standard_normal((E, f, d)).astype(np.float32)
-    W2 = rng.standard_normal((E, d, f)).astype(np.float32)
+    W1 = rng.standard_normal((E, d, f)).astype(np.float32)
+    W2 = rng.standard_normal((E, f, d)).astype(np.float32)
     out = oracle.forward(x, Wg, None, W1, None, W2, k=2, c=1.0, act="gelu", C=0)
     assert (out["y"] == 0).all()
     out = oracle.forward(x, Wg, None, W1, None, W2, k=2, c=1.0, act="gelu", C=0,
@@ -72,8 +72,8 @@ def test_remote_rows_come_back_unchanged():
     B, d, f, E = 10, 8, 8, 4
     x = f32_to_bf16_bits(rng.standard_normal((B, d)).astype(np.float32))
     Wg = rng.standard_normal((d, E)).astype(np.float32)
-    W1 = f32_to_bf16_bits(rng.standard_normal((2, f, d)).astype(np.float32))
-    W2 = f32_to_bf16_bits(rng.standard_normal((2, d, f)).astype(np.float32))
+    W1 = f32_to_bf16_bits(rng.standard_normal((2, d, f)).astype(np.float32))
+    W2 = f32_to_bf16_bits(rng.standard_normal((2, f, d)).astype(np.float32))
     out = oracle.forward(x, Wg, None, W1, None, W2, k=2, c=4.0, act="gelu",
                          n_ranks=2, e_begin=0, e_end=2)
     eo = out["expert_offset"]
@@ -111,3 +111,27 @@ def test_bf16_round_to_nearest_even():
     a = (rng.standard_normal(10000) * 10).astype(np.float32)
     t = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
     np.testing.assert_array_equal(oracle.f32_to_bf16_bits_rne(a), t)
+
+
+@pytest.mark.parametrize("case", ["local", "remote_rows", "drops_residual"])
+def test_combine_by_segment_equals_j_order_combine(case):
+    """The memory-bounded combine (one expert segment at a time) gives the
+    j-order combine's y up to float64 rounding."""
+    rng = np.random.default_rng({"local": 23, "remote_rows": 29, "drops_residual": 31}[case])
+    B, d, f, E, k = 40, 16, 24, 8, 3
+    x = f32_to_bf16_bits(rng.standard_normal((B, d)).astype(np.float32))
+    Wg = rng.standard_normal((d, E)).astype(np.float32)
+    nl = 4 if case == "remote_rows" else E
+    W1 = f32_to_bf16_bits((rng.standard_normal((nl, d, f)) / 4).astype(np.float32))
+    W3 = f32_to_bf16_bits((rng.standard_normal((nl, d, f)) / 4).astype(np.float32))
+    W2 = f32_to_bf16_bits((rng.standard_normal((nl, f, d)) / 5).astype(np.float32))
+    kw = dict(k=k, c=0.5 if case == "drops_residual" else 4.0, act="swiglu",
+              add_residual=case == "drops_residual")
+    if case == "remote_rows":
+        kw.update(n_ranks=2, e_begin=0, e_end=4)
+    a = oracle.forward(x, Wg, None, W1, W3, W2, keep_ret=True, **kw)
+    b = oracle.forward(x, Wg, None, W1, W3, W2, keep_ret=False, **kw)
+    if case == "drops_residual":
+        assert (~a["keep"]).any()
+    assert "ret" not in b
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-13, atol=1e-13)

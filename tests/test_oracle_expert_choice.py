@@ -62,9 +62,9 @@ def test_equal_scores_pick_the_first_tokens():
 def _layer(rng, B, d, f, E, act):
     x = rng.normal(size=(B, d)).astype(np.float32)
     Wg = rng.normal(scale=0.7, size=(d, E)).astype(np.float32)
-    W1 = rng.normal(scale=d ** -0.5, size=(E, f, d)).astype(np.float32)
-    W3 = rng.normal(scale=d ** -0.5, size=(E, f, d)).astype(np.float32) if act == "swiglu" else None
-    W2 = rng.normal(scale=f ** -0.5, size=(E, d, f)).astype(np.float32)
+    W1 = rng.normal(scale=d ** -0.5, size=(E, d, f)).astype(np.float32)
+    W3 = rng.normal(scale=d ** -0.5, size=(E, d, f)).astype(np.float32) if act == "swiglu" else None
+    W2 = rng.normal(scale=f ** -0.5, size=(E, f, d)).astype(np.float32)
     return x, Wg, W1, W3, W2
 
 

@@ -57,19 +57,19 @@ def test_expert_mlp_against_library(act):
     rng = np.random.default_rng(7)
     n, d, f = 9, 16, 40
     xr = rng.standard_normal((n, d))
-    W1 = f32_to_bf16_bits(rng.standard_normal((f, d)).astype(np.float32) / 4)
-    W3 = f32_to_bf16_bits(rng.standard_normal((f, d)).astype(np.float32) / 4)
-    W2 = f32_to_bf16_bits(rng.standard_normal((d, f)).astype(np.float32) / 6)
+    W1 = f32_to_bf16_bits(rng.standard_normal((d, f)).astype(np.float32) / 4)
+    W3 = f32_to_bf16_bits(rng.standard_normal((d, f)).astype(np.float32) / 4)
+    W2 = f32_to_bf16_bits(rng.standard_normal((f, d)).astype(np.float32) / 6)
     out = oracle.expert_mlp(xr, W1, W2, W3 if act == "swiglu" else None, act)
     # independent: torch float64, weights widened by torch's own bf16 type
     tw = lambda b: torch.from_numpy(b.astype(np.int16)).view(torch.bfloat16).double()
     tx = torch.from_numpy(xr)
-    h = torch.nn.functional.linear(tx, tw(W1))
+    h = torch.matmul(tx, tw(W1))
     if act == "gelu":
         h = torch.nn.functional.gelu(h, approximate="none")
     else:
-        h = torch.nn.functional.silu(h) * torch.nn.functional.linear(tx, tw(W3))
-    ref = torch.nn.functional.linear(h, tw(W2)).numpy()
+        h = torch.nn.functional.silu(h) * torch.matmul(tx, tw(W3))
+    ref = torch.matmul(h, tw(W2)).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
@@ -79,12 +79,12 @@ def test_single_expert_reduces_to_plain_mlp():
     B, d, f = 6, 8, 16
     x = rng.standard_normal((B, d)).astype(np.float32)
     Wg = rng.standard_normal((d, 1)).astype(np.float32)
-    W1 = rng.standard_normal((1, f, d)).astype(np.float32)
-    W2 = rng.standard_normal((1, d, f)).astype(np.float32)
+    W1 = rng.standard_normal((1, d, f)).astype(np.float32)
+    W2 = rng.standard_normal((1, f, d)).astype(np.float32)
     out = oracle.forward(x, Wg, None, W1, None, W2, k=1, c=1.0, act="gelu")
     assert (out["w"] == 1.0).all()
     tx = torch.from_numpy(x).double()
-    ref = torch.nn.functional.linear(
-        torch.nn.functional.gelu(torch.nn.functional.linear(tx, torch.from_numpy(W1[0]).double())),
+    ref = torch.matmul(
+        torch.nn.functional.gelu(torch.matmul(tx, torch.from_numpy(W1[0]).double())),
         torch.from_numpy(W2[0]).double()).numpy()
     np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)

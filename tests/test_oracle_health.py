@@ -3,10 +3,9 @@
 "Expert Parallelism" (inferensys.com glossary), "Practitioner Guidance":
 expert utilisation and routing entropy are health signals; "Risk and Threat
 Considerations": an expert can become unavailable.  "Expert Parallelism"
-(narrativegoldmine.com), "Components and Architecture": the Switch auxiliary
-loss multiplies, per expert, the fraction of tokens routed to it by the
-fraction of routing probability it receives; tokens routed to a full expert
-are dropped.  "Expert Parallelism" (theinfinity.ai), figure text: a bar is
+(narrativegoldmine.com), "Components and Architecture": the Switch-form
+auxiliary loss, here sum_e f_e P_e (token share times mean router
+probability per expert); a full expert drops what it cannot take.  "Expert Parallelism" (theinfinity.ai), figure text: a bar is
 the share of an expert's capacity in use.
 
 The statistics are pinned by closed forms (equal logits, one-hot logits, a

@@ -14,9 +14,9 @@ import oracle
 
 
 def _weights(rng, d, f, swiglu):
-    W1 = rng.normal(scale=d ** -0.5, size=(1, f, d)).astype(np.float32)
-    W3 = rng.normal(scale=d ** -0.5, size=(1, f, d)).astype(np.float32) if swiglu else None
-    W2 = rng.normal(scale=f ** -0.5, size=(1, d, f)).astype(np.float32)
+    W1 = rng.normal(scale=d ** -0.5, size=(1, d, f)).astype(np.float32)
+    W3 = rng.normal(scale=d ** -0.5, size=(1, d, f)).astype(np.float32) if swiglu else None
+    W2 = rng.normal(scale=f ** -0.5, size=(1, f, d)).astype(np.float32)
     return W1, W3, W2
 
 
@@ -43,8 +43,8 @@ def test_forward_adds_the_shared_output_to_every_token():
     B, d, f, E = 40, 16, 24, 6
     x = rng.normal(size=(B, d)).astype(np.float32)
     Wg = rng.normal(size=(d, E)).astype(np.float32)
-    W1 = rng.normal(scale=0.25, size=(E, f, d)).astype(np.float32)
-    W2 = rng.normal(scale=0.2, size=(E, d, f)).astype(np.float32)
+    W1 = rng.normal(scale=0.25, size=(E, d, f)).astype(np.float32)
+    W2 = rng.normal(scale=0.2, size=(E, f, d)).astype(np.float32)
     S1, _, S2 = _weights(rng, d, f, False)
     base = oracle.forward(x, Wg, None, W1, None, W2, k=2, c=0.75, act="gelu", C=2)
     with_sh = oracle.forward(x, Wg, None, W1, None, W2, k=2, c=0.75, act="gelu", C=2,

@@ -12,7 +12,7 @@ def test_deterministic_and_shapes():
     for n in ("x", "Wg", "W1", "W2"):
         np.testing.assert_array_equal(a[n], b[n])
     assert a["x"].shape == (64, 32) and a["x"].dtype == np.uint16
-    assert a["W1"].shape == (8, 48, 32) and a["W2"].shape == (8, 32, 48)
+    assert a["W1"].shape == (8, 32, 48) and a["W2"].shape == (8, 48, 32)
     assert a["W3"] is None
 
 
@@ -26,7 +26,7 @@ def test_expert_weights_independent_of_local_range():
 def test_toy_keeps_fp32_and_rounded_copies():
     a = make_inputs(WORKLOADS["toy"])
     assert a["x"].dtype == np.float32 and a["x"].shape == (6, 16)
-    assert a["W1"].shape == (8, 32, 16) and a["W1_bits"].dtype == np.uint16
+    assert a["W1"].shape == (8, 16, 32) and a["W1_bits"].dtype == np.uint16
 
 
 def test_zipf_bias():
