@@ -23,6 +23,7 @@ from ._lib import MoEError, Problem  # noqa: F401
 
 __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate",
            "workspace_bytes", "weights_bytes", "pack_weights", "gate", "route", "dispatch",
+           "dispatch_noalloc",
            "expert_ffn", "combine", "unpack", "forward", "routing_stats", "shared_problem",
            "shared_ffn", "router_probs", "expert_choice", "expert_choice_pack",
            "expert_choice_combine", "forward_expert_choice", "expert_choice_rows", "MoEError",
@@ -225,6 +226,45 @@ def _shape(t, name: str, shape: tuple) -> None:
         raise ValueError(f"{name} is required")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def dispatch_noalloc(p: Problem, x, topk_idx, out: Optional[dict] = None) -> dict:
+    """``dispatch`` through moe_dispatch_noalloc: the library's own
+    device-resident table instead of a workspace (for callers that cannot
+    allocate).  ``out``: optional dict of preallocated output tensors (the
+    keys ``dispatch`` returns); missing ones are allocated here, by the
+    caller's side, never by the library."""
+    _check(p)
+    B, d, E, k, D = p.B, p.d, p.E, p.k, p.n_ranks
+    dev = topk_idx.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(topk_idx, "topk_idx", B * k, 4)
+    km = max_kept(p)
+    i32 = dict(dtype=torch.int32, device=dev)
+    make = dict(pos=lambda: torch.empty((B, k), **i32),
+                keep=lambda: torch.empty((B, k), dtype=torch.uint8, device=dev),
+                dest=lambda: torch.empty((B, k), **i32),
+                expert_load=lambda: torch.empty(E, **i32),
+                expert_count=lambda: torch.empty(E, **i32),
+                expert_offset=lambda: torch.empty(E + 1, **i32),
+                rank_offset=lambda: torch.empty(D + 1, **i32),
+                pack_src=lambda: torch.empty(max(km, 1), **i32),
+                packed=lambda: torch.empty((max(km, 1), d), dtype=torch.int16, device=dev))
+    o = dict(out or {})
+    for key, fn in make.items():
+        if key not in o:
+            o[key] = fn()
+    for key, n, sz in [("pos", B * k, 4), ("keep", B * k, 1), ("dest", B * k, 4),
+                       ("expert_load", E, 4), ("expert_count", E, 4),
+                       ("expert_offset", E + 1, 4), ("rank_offset", D + 1, 4),
+                       ("pack_src", km, 4), ("packed", km * d, 2)]:
+        _need(o[key], key, n, sz)
+    L.check(lib().moe_dispatch_noalloc(ctypes.byref(p), _p(x), _p(topk_idx), _p(o["pos"]),
+                                       _p(o["keep"]), _p(o["dest"]), _p(o["expert_load"]),
+                                       _p(o["expert_count"]), _p(o["expert_offset"]),
+                                       _p(o["rank_offset"]), _p(o["pack_src"]), _p(o["packed"]),
+                                       _stream()), "moe_dispatch_noalloc")
+    return o
 
 
 def pack_weights(p: Problem, W1, W3, W2, out=None):

@@ -40,6 +40,7 @@ class Problem(ctypes.Structure):
 
 
 MOE_STAGE_EVENTS = 9  # events of moe_forward_out_t
+MOE_DISPATCH_NOALLOC_SCRATCH_BYTES = 16 << 20  # table of moe_dispatch_noalloc
 
 
 class RoutingStats(ctypes.Structure):
@@ -84,6 +85,8 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_P, _V, _V, _V, _V]),
     "moe_dispatch": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                     ctypes.c_size_t, _V]),
+    "moe_dispatch_noalloc": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                            _V]),
     "moe_weights_bytes": (ctypes.c_size_t, [_P]),
     "moe_pack_weights": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),

@@ -215,6 +215,28 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x,
                           moe_bf16_t* packed, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Size of the device-resident table moe_dispatch_noalloc works in. */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* moe_dispatch with no workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as
+ * moe_dispatch, except that the slot kernels' scratch (a per-tile expert
+ * count table, moe_workspace_bytes(p, MOE_OP_DISPATCH) bytes) lives in a
+ * fixed device array of MOE_DISPATCH_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; nothing is
+ * allocated or freed by the call.  Problems whose table exceeds that size
+ * return MOE_ERR_UNSUPPORTED before any launch (use moe_dispatch); a
+ * failure looking up the array's device address returns MOE_ERR_HIP.  All
+ * calls on one GPU share the array: calls that may overlap on one GPU (on
+ * unordered streams) race and must not be issued; calls ordered on one
+ * stream are fine (nothing in the array needs to start at zero). */
+moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* x,
+                                  const int32_t* topk_idx, int32_t* pos, uint8_t* keep,
+                                  int32_t* dest, int32_t* expert_load, int32_t* expert_count,
+                                  int32_t* expert_offset, int32_t* rank_offset,
+                                  int32_t* pack_src, moe_bf16_t* packed, hipStream_t stream);
+
 /* Bytes of the blocked expert-weight copy for problem p (SIZE_MAX if p is
  * invalid). */
 size_t moe_weights_bytes(const moe_problem_t* p);

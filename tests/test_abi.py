@@ -273,3 +273,22 @@ def test_pack_weights_checks_full_shapes(L, lib):
                        ((W1, W1.transpose(1, 2), W2), "W3"), ((W1[:2], W1, W2), "W1")]:
         with pytest.raises(ValueError, match=f"{what}: shape"):
             moe.pack_weights(p, *args)
+
+
+def test_dispatch_noalloc_host_checks(L, lib):
+    """Refusals that happen on the host, before the table's device address is
+    looked up or anything is launched: a table past the fixed size, a bad
+    problem, the overflow redirect (a forward-only policy)."""
+    import expert_token_routing_fp32_amd as moe
+    big = moe.make_problem(B=1 << 21, d=64, E=1024, k=8, c=1.0, f=16)
+    assert moe.workspace_bytes(big, "dispatch") > L.MOE_DISPATCH_NOALLOC_SCRATCH_BYTES
+    v = ctypes.c_void_p(16)
+    args = (v,) * 11 + (None,)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(big), *args) == L.MOE_ERR_UNSUPPORTED
+    bad = moe.make_problem(B=64, d=12, E=8, k=2)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(bad), *args) == L.MOE_ERR_INVALID
+    nxt = moe.make_problem(B=64, d=16, E=8, k=2, overflow="next")
+    assert lib.moe_dispatch_noalloc(ctypes.byref(nxt), *args) == L.MOE_ERR_UNSUPPORTED
+    src = open(HEADER).read()
+    assert "#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in src
+    assert L.MOE_DISPATCH_NOALLOC_SCRATCH_BYTES == 16 << 20
