@@ -13,6 +13,10 @@ computed in float64 (NumPy) unless the definition itself fixes a precision:
 * expert choice is a decision on those float32 logits;
 * everything else (softmax, expert FFN, combine) stays in float64.
 
+It also holds the layer's backward pass (gradients for a given output
+gradient, with the routing decisions held fixed and an optional auxiliary
+load-balancing term), in float64, as the steps of the forward in reverse.
+
 Pages followed (cited by page title and section):
 
 [EP-glossary]  "Expert Parallelism", inferensys.com glossary: the gating
@@ -75,7 +79,8 @@ __all__ = [
     "expert_mlp", "expert_ffn", "combine", "unpack", "forward", "rank_of_expert",
     "expert_capacities", "routing_stats", "shared_ffn", "router_probs", "expert_choice",
     "expert_choice_combine", "forward_expert_choice", "assign_slots_redirect",
-    "combine_by_segment",
+    "combine_by_segment", "combine_backward", "route_backward", "expert_mlp_backward",
+    "expert_ffn_backward", "dispatch_backward", "gate_backward", "backward",
 ]
 
 
@@ -752,3 +757,229 @@ def forward_expert_choice(x, Wg, bias, W1, W3, W2, *, k: int, c: float, act: str
         out["ret"] = ret
         out["y"] = expert_choice_combine(ret, sel, pw, x if add_residual else None)
     return out
+
+
+# ----------------------------------------------------------------------------
+# backward pass (training)
+# ----------------------------------------------------------------------------
+# [EP-notes] "About": the sparsely gated layer is trained by backpropagation
+# together with an auxiliary load-balancing loss; "Formal Algorithm", last
+# step: the auxiliary loss is added to the training loss.  The pages give no
+# backward formulas; the readings (also in the design notes):
+#
+# * the loss is L = sum_t <dy_t, y_t> + aux_coef * L_aux for a given output
+#   gradient dy, with L_aux = sum_e f_e P_e as in ``routing_stats``: the token
+#   shares f_e = n_e / B are counts (constant), P_e = (1/B) sum_t p_te is
+#   differentiable;
+# * the expert choice (top-k) and the capacity decision are piecewise
+#   constant: no gradient flows through them, only through the gate weights
+#   w_tj = p_{t, idx_tj} and the expert outputs; a dropped assignment is
+#   absent from y, so it gets zero gradient (dw = 0, no expert rows);
+# * rows of experts that run on other ranks come back unchanged in the
+#   forward (identity return), so their gradient passes back unchanged;
+# * everything in float64 on the defined input values (bf16 inputs widened
+#   exactly), like the forward.
+
+
+def combine_backward(dy: np.ndarray, ret: np.ndarray, dest: np.ndarray, w: np.ndarray,
+                     rows: Optional[np.ndarray] = None):
+    """Gradient of y[t] = sum_j [kept] w[t,j] ret[dest[t,j]] (+ x[t]).
+
+    Returns dret [K, d] (or [len(rows), d] for the packed rows listed in
+    ``rows``, sorted) with dret[dest[t,j]] = w[t,j] dy[t], and dw [B, k] with
+    dw[t,j] = <dy[t], ret[dest[t,j]]> for kept assignments, 0 for dropped
+    ones.  ``ret`` is the full return buffer, or with ``rows`` only those
+    rows (the dw of assignments whose row is not listed is then not
+    computed: NaN).  w is taken at float32 precision as in ``combine``.
+    Pins: central finite differences of ``combine`` and torch float64
+    autograd (test_oracle_backward)."""
+    B, k = dest.shape
+    dyv = np.asarray(dy, dtype=np.float64)
+    w32 = np.asarray(w, dtype=np.float32).astype(np.float64)
+    d = dyv.shape[1]
+    nrow = ret.shape[0] if rows is None else len(rows)
+    dret = np.zeros((nrow, d))
+    dw = np.zeros((B, k))
+    for j in range(k):
+        dj = dest[:, j].astype(np.int64)
+        kept = dj >= 0
+        if rows is None:
+            t = np.nonzero(kept)[0]
+            r = dj[t]
+            dret[r] = w32[t, j][:, None] * dyv[t]
+            dw[t, j] = np.einsum("ij,ij->i", dyv[t], ret[r])
+        else:
+            pos = np.searchsorted(rows, dj)
+            pos = np.minimum(pos, max(len(rows) - 1, 0))
+            listed = kept & (len(rows) > 0) & (np.asarray(rows)[pos] == dj)
+            t = np.nonzero(listed)[0]
+            dret[pos[t]] = w32[t, j][:, None] * dyv[t]
+            dw[t, j] = np.einsum("ij,ij->i", dyv[t], ret[pos[t]])
+            dw[kept & ~listed, j] = np.nan
+    return dret, dw
+
+
+def route_backward(logits: np.ndarray, idx: np.ndarray, dw: np.ndarray, tau: float = 1.0,
+                   aux_coef: float = 0.0, expert_load: Optional[np.ndarray] = None):
+    """Gradient of the loss with respect to the router logits [B, E].
+
+    The gate weights are w[t,j] = p[t, idx[t,j]] with p_t = softmax(g_t / tau)
+    ([EP-notes] "Formal Algorithm": w_t = p_{t,e(t)}), so with
+    dp[t,e] = sum_j [idx[t,j] = e] dw[t,j] (+ aux_coef f_e / B from
+    L_aux = sum_e f_e P_e, f_e = n_e / B constant):
+    dl[t,e] = (1 / tau) p[t,e] (dp[t,e] - sum_e' p[t,e'] dp[t,e']).
+    ``expert_load`` (n_e) is needed when aux_coef != 0.  Pins: central finite
+    differences of softmax + top-k weights with the choice held fixed, and
+    of the auxiliary loss (test_oracle_backward)."""
+    p = softmax(logits, tau)
+    B, E = p.shape
+    dp = np.zeros((B, E))
+    idx = np.asarray(idx, dtype=np.int64)
+    np.add.at(dp, (np.repeat(np.arange(B), idx.shape[1]), idx.reshape(-1)),
+              np.asarray(dw, dtype=np.float64).reshape(-1))
+    if aux_coef != 0.0:
+        f = np.asarray(expert_load, dtype=np.float64) / B
+        dp += aux_coef * f[None, :] / B
+    s = (p * dp).sum(axis=1, keepdims=True)
+    return p * (dp - s) / float(tau)
+
+
+def expert_mlp_backward(xr: np.ndarray, W1, W2, W3, act: str, dout: np.ndarray):
+    """Gradient of one expert out = act(xr W1) W2 (SwiGLU: (silu(xr W1) *
+    (xr W3)) W2) on rows xr [n, d] for the output gradient dout [n, d].
+
+    With z1 = xr W1 (z3 = xr W3), h = gelu(z1) or silu(z1) z3:
+    dh = dout W2^T; GELU: dz1 = dh gelu'(z1), gelu'(z) = Phi(z) + z phi(z);
+    SwiGLU: dz1 = dh z3 silu'(z1), silu'(z) = s (1 + z (1 - s)), s the
+    logistic, dz3 = dh silu(z1); dxr = dz1 W1^T (+ dz3 W3^T);
+    dW1 = xr^T dz1, dW3 = xr^T dz3, dW2 = h^T dout.
+    Returns (dxr, dW1, dW2, dW3 or None), float64.  Pins: central finite
+    differences and torch float64 autograd (test_oracle_backward)."""
+    w1 = _w(W1)
+    w2 = _w(W2)
+    z1 = xr @ w1
+    dout = np.asarray(dout, dtype=np.float64)
+    dh = dout @ w2.T
+    if act == "gelu":
+        h = gelu(z1)
+        phi = np.exp(-0.5 * z1 * z1) / math.sqrt(2.0 * math.pi)
+        Phi = 0.5 * (1.0 + _erf(z1 / math.sqrt(2.0)))
+        dz1 = dh * (Phi + z1 * phi)
+        dxr = dz1 @ w1.T
+        return dxr, xr.T @ dz1, h.T @ dout, None
+    if act == "swiglu":
+        w3 = _w(W3)
+        z3 = xr @ w3
+        s = 1.0 / (1.0 + np.exp(-z1))
+        h = z1 * s * z3
+        dz1 = dh * z3 * s * (1.0 + z1 * (1.0 - s))
+        dz3 = dh * z1 * s
+        dxr = dz1 @ w1.T + dz3 @ w3.T
+        return dxr, xr.T @ dz1, h.T @ dout, xr.T @ dz3
+    raise ValueError(act)
+
+
+def _erf(z):
+    from scipy.special import erf
+    return erf(z)
+
+
+def expert_ffn_backward(x: np.ndarray, pack_src: np.ndarray, expert_offset: np.ndarray,
+                        e_begin: int, e_end: int, W1, W2, W3, act: str, dret: np.ndarray,
+                        rows: Optional[np.ndarray] = None,
+                        experts: Optional[list] = None):
+    """Backward of ``expert_ffn``: dXp (the gradient of each packed row's
+    input) and the local experts' weight gradients.
+
+    dret is [K, d] (or the listed ``rows`` only, sorted).  A local expert's
+    rows get ``expert_mlp_backward``; rows of other ranks' experts pass
+    dret through unchanged (the identity return).  Weight gradients are
+    computed for ``experts`` (default: every local expert), each from all of
+    its rows -- so with ``rows`` given they must include every row of those
+    experts.  Returns (dXp, {e: (dW1, dW2, dW3)})."""
+    pack_src = np.asarray(pack_src, dtype=np.int64)
+    K = pack_src.shape[0]
+    r_all = np.arange(K) if rows is None else np.asarray(rows, dtype=np.int64)
+    dXp = np.array(dret, dtype=np.float64, copy=True)
+    grads = {}
+    want = list(range(e_begin, e_end)) if experts is None else list(experts)
+    for e in range(e_begin, e_end):
+        a, b = int(expert_offset[e]), int(expert_offset[e + 1])
+        sel = np.nonzero((r_all >= a) & (r_all < b))[0]
+        i = e - e_begin
+        if sel.size == 0:
+            if e in want:
+                d, f = _w(W1[i]).shape
+                grads[e] = (np.zeros((d, f)), np.zeros((f, d)),
+                            None if W3 is None else np.zeros((d, f)))
+            continue
+        if e in want and sel.size != b - a:
+            raise ValueError(f"expert {e}: weight gradients need all of its rows")
+        xr = _x_values(x[pack_src[r_all[sel]]])
+        dxr, dW1, dW2, dW3 = expert_mlp_backward(xr, W1[i], W2[i],
+                                                 None if W3 is None else W3[i], act,
+                                                 dret[sel])
+        dXp[sel] = dxr
+        if e in want:
+            grads[e] = (dW1, dW2, dW3)
+    return dXp, grads
+
+
+def dispatch_backward(dXp: np.ndarray, dest: np.ndarray, tokens: Optional[np.ndarray] = None,
+                      rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Backward of the pack: packed[r] = x[pack_src[r]], so
+    dx[t] = sum_j [kept] dXp[dest[t,j]] ([B, d], or the listed tokens).
+    ``rows`` says which packed rows dXp holds (sorted), when only some.
+    Pin: the adjoint identity <pack(x), v> = <x, dispatch_backward(v)>
+    (test_oracle_backward)."""
+    B, k = dest.shape
+    tt = np.arange(B) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((tt.size, dXp.shape[1]))
+    for j in range(k):
+        dj = dest[tt, j].astype(np.int64)
+        m = dj >= 0
+        r = dj[m] if rows is None else np.searchsorted(rows, dj[m])
+        out[m] += dXp[r]
+    return out
+
+
+def gate_backward(x: np.ndarray, Wg: np.ndarray, dlogits: np.ndarray):
+    """Backward of g = x Wg + b: dx = dl Wg^T [B, d], dWg = x^T dl [d, E],
+    db = sum_t dl [E], float64 (x at its defined values).  Pin: central
+    finite differences (test_oracle_backward)."""
+    xv = _x_values(x)
+    wg = np.asarray(Wg, dtype=np.float32).astype(np.float64)
+    dl = np.asarray(dlogits, dtype=np.float64)
+    return dl @ wg.T, xv.T @ dl, dl.sum(axis=0)
+
+
+def backward(x, Wg, bias, W1, W3, W2, fwd: dict, dy, *, act: str, e_begin: int = 0,
+             e_end: Optional[int] = None, tau: float = 1.0, aux_coef: float = 0.0,
+             add_residual: bool = False) -> dict:
+    """All gradients of the layer for the output gradient dy, given the
+    forward's results ``fwd`` (``forward``'s dict with ``ret``): the steps of
+    the forward in reverse -- combine, expert FFN, pack, route, gate.
+
+    Returns dx [B, d], dWg [d, E], dbias [E], dW1 / dW3 [n_local, d, f],
+    dW2 [n_local, f, d], dlogits [B, E], dw [B, k], dret and dXp [K, d]
+    (float64).  Pins: torch float64 autograd of the whole layer with the
+    routing held fixed, finite differences (test_oracle_backward)."""
+    E = fwd["logits"].shape[1]
+    e_end = E if e_end is None else e_end
+    dest, w = fwd["dest"], fwd["w"]
+    dret, dw = combine_backward(dy, fwd["ret"], dest, w)
+    dl = route_backward(fwd["logits"], fwd["idx"], dw, tau, aux_coef, fwd["expert_load"])
+    dXp, g = expert_ffn_backward(x, fwd["pack_src"], fwd["expert_offset"], e_begin, e_end,
+                                 W1, W2, W3, act, dret)
+    dx = dispatch_backward(dXp, dest)
+    dxg, dWg, db = gate_backward(x, Wg, dl)
+    dx += dxg
+    if add_residual:
+        dx += np.asarray(dy, dtype=np.float64)
+    n_local = e_end - e_begin
+    dW1 = np.stack([g[e][0] for e in range(e_begin, e_end)]) if n_local else None
+    dW2 = np.stack([g[e][1] for e in range(e_begin, e_end)]) if n_local else None
+    dW3 = (np.stack([g[e][2] for e in range(e_begin, e_end)])
+           if n_local and W3 is not None else None)
+    return dict(dx=dx, dWg=dWg, dbias=db, dW1=dW1, dW3=dW3, dW2=dW2, dlogits=dl, dw=dw,
+                dret=dret, dXp=dXp)
