@@ -26,7 +26,9 @@ __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate
            "dispatch_noalloc",
            "expert_ffn", "combine", "unpack", "forward", "routing_stats", "shared_problem",
            "shared_ffn", "router_probs", "expert_choice", "expert_choice_pack",
-           "expert_choice_combine", "forward_expert_choice", "expert_choice_rows", "MoEError",
+           "expert_choice_combine", "forward_expert_choice", "expert_choice_rows",
+           "combine_backward", "route_backward", "weights_bwd_bytes", "pack_weights_bwd",
+           "expert_ffn_backward", "dispatch_backward", "gate_backward", "backward", "MoEError",
            "Problem", "lib"]
 
 
@@ -93,7 +95,9 @@ def shared_problem(p: Problem, f: int, act: str = "swiglu") -> Problem:
 def workspace_bytes(p: Problem, op: str = "forward") -> int:
     o = {"dispatch": L.MOE_OP_DISPATCH, "ffn": L.MOE_OP_FFN, "forward": L.MOE_OP_FORWARD,
          "routing_stats": L.MOE_OP_ROUTING_STATS, "shared_ffn": L.MOE_OP_SHARED_FFN,
-         "forward_expert_choice": L.MOE_OP_FORWARD_EXPERT_CHOICE}[op]
+         "forward_expert_choice": L.MOE_OP_FORWARD_EXPERT_CHOICE,
+         "expert_ffn_backward": L.MOE_OP_EXPERT_FFN_BACKWARD,
+         "gate_backward": L.MOE_OP_GATE_BACKWARD, "backward": L.MOE_OP_BACKWARD}[op]
     return lib().moe_workspace_bytes(ctypes.byref(p), o)
 
 
@@ -560,3 +564,189 @@ def forward_expert_choice(p: Problem, x, Wg, bias, wpacked, y=None, outputs: boo
                                             _p(ws), ws.numel(), _stream()),
             "moe_forward_expert_choice")
     return (y, o) if outputs else y
+
+
+# ---------------------------------------------------------------------------
+# backward pass (training): gradients for an output gradient dy, with the
+# routing decisions of the forward held fixed
+def combine_backward(p: Problem, dy, ret, dest, topk_w, dret=None, dw=None):
+    """dret [max_kept, d] bf16 (as int16 bits; rows of dropped assignments
+    untouched) and dw [B, k] float32."""
+    _check(p)
+    B, d, k = p.B, p.d, p.k
+    km = max_kept(p)
+    _need(dy, "dy", B * d, _xsize(p))
+    _need(ret, "ret", km * d, 2)
+    _need(dest, "dest", B * k, 4)
+    _need(topk_w, "topk_w", B * k, 4)
+    if dret is None:
+        dret = torch.zeros((max(km, 1), d), dtype=torch.int16, device=dy.device)
+    if dw is None:
+        dw = torch.empty((B, k), dtype=torch.float32, device=dy.device)
+    _need(dret, "dret", km * d, 2)
+    _need(dw, "dw", B * k, 4)
+    L.check(lib().moe_combine_backward(ctypes.byref(p), _p(dy), _p(ret), _p(dest), _p(topk_w),
+                                       _p(dret), _p(dw), _stream()), "moe_combine_backward")
+    return dret, dw
+
+
+def route_backward(p: Problem, logits, topk_idx, dw, expert_load=None, aux_coef: float = 0.0,
+                   dlogits=None):
+    """dlogits [B, E] float32 (aux_coef scales the auxiliary load-balancing
+    loss sum_e f_e P_e; it needs expert_load)."""
+    _check(p)
+    B, E, k = p.B, p.E, p.k
+    _need(logits, "logits", B * E, 4)
+    _need(topk_idx, "topk_idx", B * k, 4)
+    _need(dw, "dw", B * k, 4)
+    if aux_coef != 0.0:
+        _need(expert_load, "expert_load", E, 4)
+    if dlogits is None:
+        dlogits = torch.empty((B, E), dtype=torch.float32, device=logits.device)
+    _need(dlogits, "dlogits", B * E, 4)
+    L.check(lib().moe_route_backward(ctypes.byref(p), _p(logits), _p(topk_idx), _p(dw),
+                                     _p(expert_load), ctypes.c_float(aux_coef), _p(dlogits),
+                                     _stream()), "moe_route_backward")
+    return dlogits
+
+
+def weights_bwd_bytes(p: Problem) -> int:
+    return lib().moe_weights_bwd_bytes(ctypes.byref(p))
+
+
+def pack_weights_bwd(p: Problem, W1, W3, W2, out=None):
+    """The local experts' weights rearranged for the expert backward (same
+    [in, out] inputs as pack_weights)."""
+    _check(p)
+    d, f = p.d, p.f
+    nl = p.e_end - p.e_begin
+    if nl > 0:
+        _shape(W1, "W1", (nl, d, f))
+        _shape(W2, "W2", (nl, f, d))
+        if p.act == L.MOE_SWIGLU:
+            _shape(W3, "W3", (nl, d, f))
+    n = weights_bwd_bytes(p)
+    dev = W2.device if W2 is not None else torch.device("cuda")
+    if out is None:
+        out = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    _need(out, "wpacked_bwd", n, 1)
+    if nl > 0:
+        _need(W1, "W1", nl * d * f, 2)
+        _need(W2, "W2", nl * f * d, 2)
+        if p.act == L.MOE_SWIGLU:
+            _need(W3, "W3", nl * d * f, 2)
+    L.check(lib().moe_pack_weights_bwd(ctypes.byref(p), _p(W1),
+                                       _p(W3 if p.act == L.MOE_SWIGLU else None), _p(W2),
+                                       _p(out), out.numel(), _stream()), "moe_pack_weights_bwd")
+    return out
+
+
+def expert_ffn_backward(p: Problem, x, pack_src, expert_offset, wpacked, wpacked_bwd, dret,
+                        ws=None):
+    """dret [max_kept, d] bf16 is overwritten in place: its local rows
+    become the gradient of the packed input rows.  Returns dict dxp (= dret),
+    dW1, dW3 (SwiGLU, else None) [n_local, d, f] and dW2 [n_local, f, d]
+    float32."""
+    _check(p)
+    B, d, f = p.B, p.d, p.f
+    nl = p.e_end - p.e_begin
+    km = max_kept(p)
+    dev = dret.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(pack_src, "pack_src", km, 4)
+    _need(expert_offset, "expert_offset", p.E + 1, 4)
+    _need(dret, "dret", km * d, 2)
+    sw = p.act == L.MOE_SWIGLU
+    f32 = dict(dtype=torch.float32, device=dev)
+    dW1 = torch.empty((max(nl, 1), d, f), **f32)
+    dW2 = torch.empty((max(nl, 1), f, d), **f32)
+    dW3 = torch.empty((max(nl, 1), d, f), **f32) if sw else None
+    if nl > 0:
+        _need(wpacked, "wpacked", weights_bytes(p), 1)
+        _need(wpacked_bwd, "wpacked_bwd", weights_bwd_bytes(p), 1)
+    ws = _ws(p, "expert_ffn_backward", ws, dev)
+    L.check(lib().moe_expert_ffn_backward(ctypes.byref(p), _p(x), _p(pack_src),
+                                          _p(expert_offset), _p(wpacked), _p(wpacked_bwd),
+                                          _p(dret), _p(dW1), _p(dW3), _p(dW2), _p(ws),
+                                          ws.numel(), _stream()), "moe_expert_ffn_backward")
+    return dict(dxp=dret, dW1=dW1[:nl], dW3=None if dW3 is None else dW3[:nl], dW2=dW2[:nl])
+
+
+def dispatch_backward(p: Problem, dxp, dest, dy=None, dx_acc=None):
+    """dx_acc [B, d] float32 = sum_j dxp[dest[t, j]] (+ dy with the residual)."""
+    _check(p)
+    B, d, k = p.B, p.d, p.k
+    _need(dxp, "dxp", max_kept(p) * d, 2)
+    _need(dest, "dest", B * k, 4)
+    if p.add_residual:
+        _need(dy, "dy", B * d, _xsize(p))
+    if dx_acc is None:
+        dx_acc = torch.empty((B, d), dtype=torch.float32, device=dxp.device)
+    _need(dx_acc, "dx_acc", B * d, 4)
+    L.check(lib().moe_dispatch_backward(ctypes.byref(p), _p(dxp), _p(dest),
+                                        _p(dy if p.add_residual else None), _p(dx_acc),
+                                        _stream()), "moe_dispatch_backward")
+    return dx_acc
+
+
+def gate_backward(p: Problem, x, Wg, dlogits, dx_acc=None, ws=None):
+    """dx [B, d] (x dtype) = dlogits Wg^T (+ dx_acc), dWg [d, E] and dbias
+    [E] float32."""
+    _check(p)
+    B, d, E = p.B, p.d, p.E
+    dev = dlogits.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(Wg, "Wg", d * E, 4)
+    _need(dlogits, "dlogits", B * E, 4)
+    if dx_acc is not None:
+        _need(dx_acc, "dx_acc", B * d, 4)
+    dx = torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16 else torch.float32,
+                     device=dev)
+    dWg = torch.empty((d, E), dtype=torch.float32, device=dev)
+    dbias = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws(p, "gate_backward", ws, dev)
+    L.check(lib().moe_gate_backward(ctypes.byref(p), _p(x), _p(Wg), _p(dlogits), _p(dx_acc),
+                                    _p(dx), _p(dWg), _p(dbias), _p(ws), ws.numel(), _stream()),
+            "moe_gate_backward")
+    return dx, dWg, dbias
+
+
+def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef: float = 0.0,
+             ws=None) -> dict:
+    """All gradients of the layer (moe_backward).  ``saved``: the dict of
+    ``forward(..., outputs=True)`` (logits, topk_idx, topk_w, dest,
+    expert_load, expert_offset, pack_src, and packed = the expert outputs).
+    Returns dx, dWg, dbias, dW1, dW3 (SwiGLU, else None), dW2, dlogits, dw."""
+    _check(p)
+    B, d, E, k, f = p.B, p.d, p.E, p.k, p.f
+    nl = p.e_end - p.e_begin
+    dev = dy.device
+    _need(x, "x", B * d, _xsize(p))
+    _need(Wg, "Wg", d * E, 4)
+    _need(dy, "dy", B * d, _xsize(p))
+    sw = p.act == L.MOE_SWIGLU
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty((B, d), dtype=torch.bfloat16 if p.x_dtype == L.MOE_BF16
+                            else torch.float32, device=dev),
+             dWg=torch.empty((d, E), **f32), dbias=torch.empty(E, **f32),
+             dW1=torch.empty((max(nl, 1), d, f), **f32), dW2=torch.empty((max(nl, 1), f, d), **f32),
+             dW3=torch.empty((max(nl, 1), d, f), **f32) if sw else None,
+             dlogits=torch.empty((B, E), **f32), dw=torch.empty((B, k), **f32))
+    sv = L.Saved(logits=saved["logits"].data_ptr(), topk_idx=saved["topk_idx"].data_ptr(),
+                 topk_w=saved["topk_w"].data_ptr(), dest=saved["dest"].data_ptr(),
+                 expert_load=saved["expert_load"].data_ptr(),
+                 expert_offset=saved["expert_offset"].data_ptr(),
+                 pack_src=saved["pack_src"].data_ptr(), ret=saved["packed"].data_ptr())
+    gr = L.Grads(**{n: (g[n].data_ptr() if g[n] is not None else None)
+                    for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dlogits", "dw")})
+    n = workspace_bytes(p, "backward")
+    if ws is None:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _need(ws, "ws", n, 1)
+    L.check(lib().moe_backward(ctypes.byref(p), _p(x), _p(Wg), _p(wpacked), _p(wpacked_bwd),
+                               ctypes.byref(sv), _p(dy), ctypes.c_float(aux_coef),
+                               ctypes.byref(gr), _p(ws), ws.numel(), _stream()), "moe_backward")
+    for key in ("dW1", "dW2", "dW3"):
+        if g[key] is not None:
+            g[key] = g[key][:nl]
+    return g

@@ -14,7 +14,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT = 0, 1
 (MOE_OP_DISPATCH, MOE_OP_FFN, MOE_OP_FORWARD, MOE_OP_ROUTING_STATS, MOE_OP_SHARED_FFN,
- MOE_OP_FORWARD_EXPERT_CHOICE) = range(6)
+ MOE_OP_FORWARD_EXPERT_CHOICE, MOE_OP_EXPERT_FFN_BACKWARD, MOE_OP_GATE_BACKWARD,
+ MOE_OP_BACKWARD) = range(9)
 
 
 class Problem(ctypes.Structure):
@@ -65,6 +66,19 @@ class ExpertChoiceOut(ctypes.Structure):
         ("events", ctypes.c_void_p * 6)]
 
 
+class Saved(ctypes.Structure):
+    """moe_saved_t: the forward's outputs the backward reads."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "topk_idx", "topk_w", "dest", "expert_load", "expert_offset", "pack_src",
+        "ret")]
+
+
+class Grads(ctypes.Structure):
+    """moe_grads_t: the gradients moe_backward writes (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dlogits", "dw")]
+
+
 class MoEError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -109,6 +123,18 @@ _SIGS = {
     "moe_forward_expert_choice": (ctypes.c_int, [_P, _V, _V, _V, _V, _V,
                                                  ctypes.POINTER(ExpertChoiceOut), _V,
                                                  ctypes.c_size_t, _V]),
+    "moe_combine_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V]),
+    "moe_route_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_float, _V, _V]),
+    "moe_weights_bwd_bytes": (ctypes.c_size_t, [_P]),
+    "moe_pack_weights_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "moe_expert_ffn_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                               ctypes.c_size_t, _V]),
+    "moe_dispatch_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V]),
+    "moe_gate_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
+                                         _V]),
+    "moe_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.POINTER(Saved), _V,
+                                    ctypes.c_float, ctypes.POINTER(Grads), _V, ctypes.c_size_t,
+                                    _V]),
 }
 
 _lib = None

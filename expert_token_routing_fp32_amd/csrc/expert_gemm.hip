@@ -63,7 +63,11 @@ constexpr int kP = 4;                     // pipeline depth (stages in flight + 
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kXcd = 8;
 
-enum { MODE_GELU = 0, MODE_SWIGLU = 1, MODE_PLAIN = 2 };
+// MODE_DGELU / MODE_DSWIGLU (backward): the tile's products are dH, the
+// gradient of the hidden activation; the epilogue reads the pre-activations
+// Z of the same rows and writes dZ = dH * gelu'(Z), or dZ1 = dH Z3 silu'(Z1)
+// and dZ3 = dH silu(Z1) (at columns u and f + u of a 2f-wide row).
+enum { MODE_GELU = 0, MODE_SWIGLU = 1, MODE_PLAIN = 2, MODE_DGELU = 3, MODE_DSWIGLU = 4 };
 
 struct GemmArgs {
   const uint16_t* A;         // rows of length K
@@ -75,6 +79,11 @@ struct GemmArgs {
   int K, Nout;
   int n_tiles_n, nk;
   int n_local;               // experts e_begin .. e_begin + n_local - 1
+  // backward epilogues: pre-activations Z (rows as Out's, zw per row) and
+  // the output row stride (Nout is then the valid column count, f)
+  const uint16_t* Z;
+  int zw;
+  int ldo;
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -104,6 +113,28 @@ __device__ __forceinline__ float gelu_erf(float z) {
 // reciprocal
 __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504f));
+}
+// GELU'(z) = Phi(z) + z phi(z).  With the same erf approximation (A & S
+// 7.1.26, x = |z| / sqrt 2): Phi(z) = 1 - q / 2 for z >= 0 and q / 2 for
+// z < 0, q = poly(t) e^{-z^2 / 2}; phi(z) = e^{-z^2 / 2} / sqrt(2 pi).
+__device__ __forceinline__ float dgelu_erf(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164188f, az, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752f);
+  const float hq = 0.5f * p * e;
+  const float Phi = z >= 0.0f ? 1.0f - hq : hq;
+  return fmaf(z * 0.39894228f, e, Phi);
+}
+// column of hidden unit u's W1 product in the recomputed SwiGLU
+// pre-activations (the GEMM1 tile order: per 128 units, four 64-column
+// groups of 32 W1 then 32 W3 products)
+__device__ __forceinline__ int zcol_w1(int u) {
+  return (u >> 7) * 256 + ((u >> 5) & 3) * 64 + (u & 31);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -352,7 +383,91 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       }
     }
   }
-  {
+  if constexpr (MODE == MODE_DGELU || MODE == MODE_DSWIGLU) {
+    // Backward epilogue of tile `tile`: acc[c][i][r] is dH at row 32 i +
+    // 8 (r / 4) + 4 lg + r % 4 of the slice and hidden unit
+    // u = 256 tile + 64 wave + 32 c + l32.  Output q (dZ, or dZ1 then dZ3)
+    // goes through the same LDS staging as the forward's: 32 rows x 64
+    // columns per wavefront, stored as 16-byte row segments.
+    const bool odd = lane & 1;
+    const uint16_t* zb = a.Z + o_row0 * a.zw;
+    uint16_t* out = a.Out + o_row0 * a.ldo;
+    const int nval = a.Nout;
+    char* stg = smem + kStageOff + wave * 32 * 128;
+    const int col0 = tile * 256 + 64 * wave;
+    // row pairs per chunk: fewer than the forward's, the Z values of a chunk
+    // being live beside the prefetched weights
+    constexpr int kEb = 2;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+#pragma unroll
+      for (int q = 0; q < (MODE == MODE_DSWIGLU ? 2 : 1); ++q) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int u = col0 + 32 * c + l32;
+#pragma unroll
+          for (int r0 = 0; r0 < 16; r0 += 2 * kEb) {
+            // Opaque row stride: keeps this chunk's Z loads here instead of
+            // letting the compiler hoist every load of the tile (and spill).
+            int zw = a.zw;
+            asm volatile("" : "+s"(zw));
+            const int uc = MODE == MODE_DGELU ? u : zcol_w1(u);
+            float z1v[2 * kEb], z3v[2 * kEb];
+#pragma unroll
+            for (int g = 0; g < 2 * kEb; ++g) {
+              const int r = r0 + g;
+              const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+              const bool ok = row < rows && u < nval;
+              const int64_t zo = (int64_t)(ok ? row : 0) * zw + uc;
+              z1v[g] = ok ? bf16_lo(zb[zo]) : 0.f;
+              z3v[g] = (MODE == MODE_DSWIGLU && ok) ? bf16_lo(zb[zo + 32]) : 0.f;
+            }
+            float v0[kEb], v1[kEb];
+#pragma unroll
+            for (int g = 0; g < kEb; ++g) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int r = r0 + 2 * g + h;
+                const float dh = acc_read(acc[c][i][r]);
+                const float z1 = z1v[2 * g + h], z3 = z3v[2 * g + h];
+                float val;
+                if (MODE == MODE_DGELU) {
+                  val = dh * dgelu_erf(z1);
+                } else {
+                  const float sg = __builtin_amdgcn_rcpf(
+                      1.0f + __builtin_amdgcn_exp2f(z1 * -1.44269504f));
+                  val = q == 0 ? dh * z3 * sg * fmaf(z1, 1.0f - sg, 1.0f) : dh * z1 * sg;
+                }
+                if (h == 0) v0[g] = val; else v1[g] = val;
+              }
+            }
+#pragma unroll
+            for (int g = 0; g < kEb; ++g) {
+              const int r = r0 + 2 * g;
+              const float got = swap_adjacent(odd ? v0[g] : v1[g]);
+              const float lo = odd ? got : v0[g];
+              const float hi = odd ? v1[g] : got;
+              const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+              *(unsigned int*)(stg + rin * 128 + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // block i of output q: 32 rows x 64 columns, 16-byte segments
+#pragma unroll
+        for (int qq = 0; qq < 32 * 8 / 64; ++qq) {
+          const int sgi = lane + 64 * qq;
+          const int rin = sgi / 8, sg8 = sgi % 8;
+          const u32x4 v = *(const u32x4*)(stg + rin * 128 + sg8 * 16);
+          const int row = 32 * i + rin, col = col0 + 8 * sg8;
+          if (row < rows && col < nval)
+            *(u32x4*)(out + ((int64_t)row * a.ldo + q * nval + col)) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmcnt<0>();
+  } else {
         // Epilogue of tile `tile`.  acc[c][i][r] is row 8 (r / 4) +
         // 4 lg + r % 4 of row block i, column l32 of the wavefront's weight
         // block c.  Rows r and r + 1 (r even) are adjacent: lanes 2j and
@@ -796,6 +911,137 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g2.nk = geo2.nk;
   g2.n_local = n_local;
   return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s, nullptr, ev_stop);
+}
+
+}  // namespace moek
+
+// ---------------------------------------------------------------------------
+// Backward pass on the same grouped GEMM.
+namespace moek {
+namespace {
+
+// Blocked layout (as pack_weights_kernel's) from output-major sources:
+// weight-tile row n of K stage kt holds value(n, k) = srcA[e][n][k] for
+// k < Ka and srcB[e][n][k - Ka] beyond (rows of Ka values; Ka a multiple of
+// 8, so a lane's 8 K values come from one source as one 16-byte load).
+__global__ __launch_bounds__(256) void pack_weights_nmajor_kernel(
+    const uint16_t* __restrict__ srcA, const uint16_t* __restrict__ srcB, int Ka, int n_exp,
+    int Nw, int K, int n_tiles, int nk, uint16_t* __restrict__ out) {
+  const int64_t total = (int64_t)n_exp * n_tiles * nk * (kWStage / 16);
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int l = (int)(q & 63);
+    const int cb = (int)((q >> 6) & 1);
+    const int s = (int)((q >> 7) & 3);
+    const int w = (int)((q >> 9) & 3);
+    int64_t rest = q >> 11;
+    const int kt = (int)(rest % nk);
+    rest /= nk;
+    const int nt = (int)(rest % n_tiles);
+    const int e = (int)(rest / n_tiles);
+    const int k = kt * BK + 16 * s + 8 * (l >> 5);
+    const int n = nt * 256 + 64 * w + 32 * cb + (l & 31);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < Nw && k < K) {
+      const uint16_t* src = k < Ka ? srcA : srcB;
+      const int kk = k < Ka ? k : k - Ka;
+      v = *(const u32x4*)(src + ((int64_t)e * Nw + n) * Ka + kk);
+    }
+    *(u32x4*)(out + q * 8) = v;
+  }
+}
+
+int zw_of(int f, bool swiglu) { return swiglu ? geo(1, f, 8, true).n_tiles * 256 : f; }
+
+// the two blocked backward matrices: dH's (N = f, K = d; rows of W2) and
+// dX's (N = d, K = f or 2 f; rows of W1, then W3)
+Geo geo_b1(int n_local, int d, int f) { return geo(n_local, f, d, false); }
+Geo geo_b2(int n_local, int d, int f, bool swiglu) {
+  return geo(n_local, d, swiglu ? 2 * f : f, false);
+}
+
+GemmArgs ffn_args(const uint16_t* A, const int32_t* eo, const void* Wp, uint16_t* Out,
+                  int a_local, int o_local, int e_begin, int K, int Nout, const Geo& g,
+                  int n_local) {
+  GemmArgs a{};
+  a.A = A;
+  a.eo = eo;
+  a.Wp = static_cast<const uint16_t*>(Wp);
+  a.Out = Out;
+  a.a_local = a_local;
+  a.o_local = o_local;
+  a.e_begin = e_begin;
+  a.K = K;
+  a.Nout = Nout;
+  a.n_tiles_n = g.n_tiles;
+  a.nk = g.nk;
+  a.n_local = n_local;
+  a.ldo = Nout;
+  return a;
+}
+
+}  // namespace
+
+int expert_ffn_zw(int f, bool swiglu) { return zw_of(f, swiglu); }
+
+size_t packed_weights_bwd_bytes(int n_local, int d, int f, bool swiglu) {
+  return geo_b1(n_local, d, f).bytes + geo_b2(n_local, d, f, swiglu).bytes;
+}
+
+hipError_t launch_pack_weights_bwd(const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                                   int n_local, int d, int f, bool swiglu, void* wpb,
+                                   hipStream_t s) {
+  if (n_local <= 0) return hipSuccess;
+  const Geo g1 = geo_b1(n_local, d, f), g2 = geo_b2(n_local, d, f, swiglu);
+  uint16_t* o1 = static_cast<uint16_t*>(wpb);
+  uint16_t* o2 = reinterpret_cast<uint16_t*>(static_cast<char*>(wpb) + g1.bytes);
+  auto blocks = [](size_t bytes) {
+    int64_t g = (int64_t)(bytes / 16 + 255) / 256;
+    return (unsigned)(g > (1 << 20) ? (1 << 20) : g);
+  };
+  // dH = dret W2^T: value(n, k) = W2[e][n][k], n < f, k < d
+  hipLaunchKernelGGL(pack_weights_nmajor_kernel, dim3(blocks(g1.bytes)), dim3(256), 0, s, W2,
+                     nullptr, d, n_local, f, d, g1.n_tiles, g1.nk, o1);
+  // dX = [dZ1 | dZ3] [W1 | W3]^T: value(n, k) = W1[e][n][k] (k < f), W3[e][n][k - f]
+  hipLaunchKernelGGL(pack_weights_nmajor_kernel, dim3(blocks(g2.bytes)), dim3(256), 0, s, W1,
+                     swiglu ? W3 : nullptr, f, n_local, d, swiglu ? 2 * f : f, g2.n_tiles, g2.nk,
+                     o2);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_recompute(const uint16_t* xloc, const int32_t* expert_offset, int e_begin,
+                                int n_local, int rows_max, int rows_hint, int d, int f,
+                                bool swiglu, const void* wp, uint16_t* Z, hipStream_t s) {
+  if (n_local <= 0 || rows_max <= 0) return hipSuccess;
+  const Geo g1 = geo(n_local, f, d, swiglu);
+  GemmArgs a = ffn_args(xloc, expert_offset, wp, Z, 1, 1, e_begin, d, zw_of(f, swiglu), g1,
+                        n_local);
+  return launch_gemm<MODE_PLAIN>(a, (rows_max + BM - 1) / BM, rows_hint >= 384, s);
+}
+
+hipError_t launch_ffn_dact(const uint16_t* dret, const int32_t* expert_offset, int e_begin,
+                           int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                           const void* wpb, const uint16_t* Z, uint16_t* dZ, hipStream_t s) {
+  if (n_local <= 0 || rows_max <= 0) return hipSuccess;
+  const Geo g = geo_b1(n_local, d, f);
+  GemmArgs a = ffn_args(dret, expert_offset, wpb, dZ, 0, 1, e_begin, d, f, g, n_local);
+  a.Z = Z;
+  a.zw = zw_of(f, swiglu);
+  a.ldo = swiglu ? 2 * f : f;
+  const int mt = (rows_max + BM - 1) / BM;
+  return swiglu ? launch_gemm<MODE_DSWIGLU>(a, mt, rows_hint >= 384, s)
+                : launch_gemm<MODE_DGELU>(a, mt, rows_hint >= 384, s);
+}
+
+hipError_t launch_ffn_dgrad(const uint16_t* dZ, const int32_t* expert_offset, int e_begin,
+                            int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                            const void* wpb, uint16_t* dxp, hipStream_t s) {
+  if (n_local <= 0 || rows_max <= 0) return hipSuccess;
+  const Geo g1 = geo_b1(n_local, d, f), g2 = geo_b2(n_local, d, f, swiglu);
+  const void* w2 = static_cast<const char*>(wpb) + g1.bytes;
+  GemmArgs a = ffn_args(dZ, expert_offset, w2, dxp, 1, 0, e_begin, swiglu ? 2 * f : f, d, g2,
+                        n_local);
+  return launch_gemm<MODE_PLAIN>(a, (rows_max + BM - 1) / BM, rows_hint >= 384, s);
 }
 
 }  // namespace moek

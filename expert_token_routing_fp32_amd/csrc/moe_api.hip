@@ -189,6 +189,102 @@ size_t carve_ec(const moe_problem_t* p, const moe_expert_choice_out_t* o, void* 
   return c.off;
 }
 
+// ---- backward workspaces -------------------------------------------------
+struct FfnBwdBufs {
+  uint16_t *xloc, *Z, *dZ, *X8, *H8, *dret8, *dZ8;
+};
+// expert FFN backward: the local rows' inputs, recomputed pre-activations,
+// dZ, and the RB8 operands of the weight-gradient GEMMs
+size_t carve_ffn_bwd(const moe_problem_t* p, void* ws, FfnBwdBufs* b) {
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  const bool sw = p->act == MOE_SWIGLU;
+  const size_t kl = (size_t)kloc_of(p);
+  const size_t nl = (size_t)(p->e_end - p->e_begin);
+  const size_t r8 = (size_t)moek::rb8_rows(rows_per_expert(p));
+  const size_t zw = (size_t)moek::expert_ffn_zw(p->f, sw);
+  const size_t zwd = sw ? 2 * (size_t)p->f : (size_t)p->f;
+  FfnBwdBufs t;
+  t.xloc = c.take<uint16_t>(nullptr, kl * p->d * 2);
+  t.Z = c.take<uint16_t>(nullptr, kl * zw * 2);
+  t.dZ = c.take<uint16_t>(nullptr, kl * zwd * 2);
+  t.X8 = c.take<uint16_t>(nullptr, nl * r8 * p->d * 2);
+  t.H8 = c.take<uint16_t>(nullptr, nl * r8 * p->f * 2);
+  t.dret8 = c.take<uint16_t>(nullptr, nl * r8 * p->d * 2);
+  t.dZ8 = c.take<uint16_t>(nullptr, nl * r8 * zwd * 2);
+  if (b) *b = t;
+  return c.off;
+}
+
+struct GateBwdBufs {
+  uint16_t *dl_s[2], *wg_s[2], *x8[3], *dl8[3];
+  float* part;
+};
+int pad32(int v) { return (v + 31) / 32 * 32; }
+// split-K of the token contraction of dWg: enough workgroups to fill the
+// CUs, at least 1024 tokens per split
+struct GateSplit {
+  int G, Ks;
+};
+GateSplit gate_split(const moe_problem_t* p) {
+  const int64_t Br = moek::rb8_rows(p->B);
+  if (Br == 0) return GateSplit{1, 32};
+  const int64_t tiles = (int64_t)((p->d + 1 + 127) / 128) * ((p->E + 127) / 128);
+  int64_t G = (1024 + tiles - 1) / tiles;
+  const int64_t gmax = (Br + 1023) / 1024;
+  if (G > gmax) G = gmax;
+  if (G < 1) G = 1;
+  if (G > 64) G = 64;
+  int64_t Ks = (Br + G - 1) / G;
+  Ks = (Ks + 31) / 32 * 32;
+  G = (Br + Ks - 1) / Ks;
+  GateSplit s;
+  s.G = (int)G;
+  s.Ks = (int)Ks;
+  return s;
+}
+// gate backward: the split router operands (row-major for dx, RB8 over the
+// tokens for dWg and the bias) and x in RB8 with a ones column
+size_t carve_gate_bwd(const moe_problem_t* p, void* ws, GateBwdBufs* b) {
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  const size_t B = (size_t)p->B, Ep = (size_t)pad32(p->E), d = (size_t)p->d;
+  const size_t Br = (size_t)moek::rb8_rows(p->B);
+  const int nx = p->x_dtype == MOE_BF16 ? 1 : 3;
+  GateBwdBufs t{};
+  for (int i = 0; i < 2; ++i) t.dl_s[i] = c.take<uint16_t>(nullptr, B * Ep * 2);
+  for (int i = 0; i < 2; ++i) t.wg_s[i] = c.take<uint16_t>(nullptr, d * Ep * 2);
+  for (int i = 0; i < nx; ++i) t.x8[i] = c.take<uint16_t>(nullptr, Br * (d + 8) * 2);
+  for (int i = 0; i < 3; ++i) t.dl8[i] = c.take<uint16_t>(nullptr, Br * Ep * 2);
+  const GateSplit gs = gate_split(p);
+  t.part = c.take<float>(nullptr, (size_t)gs.G * (d + 1) * p->E * 4);
+  if (b) *b = t;
+  return c.off;
+}
+
+struct BwdBufs {
+  uint16_t* dret;
+  float *dw, *dl, *dx_acc;
+  void *ffn_ws, *gate_ws;
+  size_t ffn_bytes, gate_bytes;
+};
+size_t carve_bwd(const moe_problem_t* p, const moe_grads_t* g, void* ws, BwdBufs* b) {
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  const size_t BK = (size_t)p->B * p->k, BE = (size_t)p->B * p->E;
+  BwdBufs t;
+  t.dret = c.take<uint16_t>(nullptr, (size_t)kmax_of(p) * p->d * 2);
+  t.dw = c.take(g ? g->dw : nullptr, BK * 4);
+  t.dl = c.take(g ? g->dlogits : nullptr, BE * 4);
+  t.dx_acc = c.take<float>(nullptr, (size_t)p->B * p->d * 4);
+  t.ffn_bytes = carve_ffn_bwd(p, nullptr, nullptr);
+  t.ffn_ws = c.take<char>(nullptr, t.ffn_bytes);
+  t.gate_bytes = carve_gate_bwd(p, nullptr, nullptr);
+  t.gate_ws = c.take<char>(nullptr, t.gate_bytes);
+  if (b) *b = t;
+  return c.off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,6 +345,12 @@ size_t moe_workspace_bytes(const moe_problem_t* p, moe_op_t op) {
       return shared_ws(p);
     case MOE_OP_FORWARD_EXPERT_CHOICE:
       return carve_ec(p, nullptr, nullptr, nullptr);
+    case MOE_OP_EXPERT_FFN_BACKWARD:
+      return carve_ffn_bwd(p, nullptr, nullptr);
+    case MOE_OP_GATE_BACKWARD:
+      return carve_gate_bwd(p, nullptr, nullptr);
+    case MOE_OP_BACKWARD:
+      return carve_bwd(p, nullptr, nullptr, nullptr);
   }
   return SIZE_MAX;
 }
@@ -701,3 +803,372 @@ extern "C" int32_t moe_check_gate_split_reach(int64_t B, int32_t d, int32_t E, i
   *copy_bytes = (int64_t)moek::gate_split_bytes(d, E);
   return moek::gate_use_split(true, B, d, E) ? 1 : 0;
 }
+
+// ---------------------------------------------------------------------------
+// backward pass
+namespace {
+
+moe_status_t check_bwd(const moe_problem_t* p) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->overflow != MOE_OVERFLOW_DROP) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// the expert FFN backward on carved scratch (shared by the stage call and
+// the chain)
+hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pack_src,
+                        const int32_t* eo, const void* wp, const void* wpb, uint16_t* dret,
+                        float* dW1, float* dW3, float* dW2, void* ws, hipStream_t s) {
+  const int nl = p->e_end - p->e_begin;
+  if (nl <= 0 || p->B == 0) return hipSuccess;
+  FfnBwdBufs b;
+  carve_ffn_bwd(p, ws, &b);
+  const bool sw = p->act == MOE_SWIGLU, xb = p->x_dtype == MOE_BF16;
+  const int d = p->d, f = p->f, zw = moek::expert_ffn_zw(f, sw), zwd = sw ? 2 * f : f;
+  const int rpe = (int)rows_per_expert(p), rh = rows_hint(p);
+  const int64_t kl = kloc_of(p);
+  hipError_t e = moek::launch_gather_rows(x, xb, pack_src, eo, p->e_begin, p->e_end, p->B, d, kl,
+                                          b.xloc, s);
+  // Z = X W1 (, X W3): the forward's first GEMM without its activation
+  if (e == hipSuccess)
+    e = moek::launch_ffn_recompute(b.xloc, eo, p->e_begin, nl, rpe, rh, d, f, sw, wp, b.Z, s);
+  // RB8 operands of the weight gradients: X, H = act(Z), dret (local rows)
+  if (e == hipSuccess)
+    e = moek::launch_relayout_rb8(0, b.xloc, d, eo, p->e_begin, 1, nl, rpe, d, d, -1, b.X8, s);
+  if (e == hipSuccess)
+    e = moek::launch_relayout_rb8(sw ? 2 : 1, b.Z, zw, eo, p->e_begin, 1, nl, rpe, f, zw, -1,
+                                  b.H8, s);
+  // dret is indexed by the absolute packed row
+  if (e == hipSuccess)
+    e = moek::launch_relayout_rb8(0, dret, d, eo, p->e_begin, 0, nl, rpe, d, d, -1, b.dret8, s);
+  // dZ = dact(dret W2^T, Z), then dZ in RB8
+  if (e == hipSuccess)
+    e = moek::launch_ffn_dact(dret, eo, p->e_begin, nl, rpe, rh, d, f, sw, wpb, b.Z, b.dZ, s);
+  if (e == hipSuccess)
+    e = moek::launch_relayout_rb8(0, b.dZ, zwd, eo, p->e_begin, 1, nl, rpe, zwd, zwd, -1, b.dZ8,
+                                  s);
+  // dX = dZ [W1 | W3]^T over dret's local rows
+  if (e == hipSuccess)
+    e = moek::launch_ffn_dgrad(b.dZ, eo, p->e_begin, nl, rpe, rh, d, f, sw, wpb, dret, s);
+  const int64_t r8 = moek::rb8_rows(rpe);
+  // dW2 = H^T dret: C[m < f][n < d]
+  if (e == hipSuccess) {
+    moek::KGemm q{};
+    q.A[0] = b.H8;
+    q.B[0] = b.dret8;
+    q.nseg = 1;
+    q.a_w = f;
+    q.b_w = d;
+    q.a_es = r8 * f;
+    q.b_es = r8 * d;
+    q.a_rows = f;
+    q.b_rows = d;
+    q.eo = eo;
+    q.e_begin = p->e_begin;
+    q.groups = nl;
+    q.M = f;
+    q.N = d;
+    q.C0 = dW2;
+    q.ldc0 = d;
+    q.c0_es = (int64_t)f * d;
+    q.M0 = f;
+    q.N0 = d;
+    e = moek::launch_kgemm(q, s);
+  }
+  // [dW1 | dW3] = X^T [dZ1 | dZ3]: C[m < d][n < zwd], columns past f to dW3
+  if (e == hipSuccess) {
+    moek::KGemm q{};
+    q.A[0] = b.X8;
+    q.B[0] = b.dZ8;
+    q.nseg = 1;
+    q.a_w = d;
+    q.b_w = zwd;
+    q.a_es = r8 * d;
+    q.b_es = r8 * zwd;
+    q.a_rows = d;
+    q.b_rows = zwd;
+    q.eo = eo;
+    q.e_begin = p->e_begin;
+    q.groups = nl;
+    q.M = d;
+    q.N = zwd;
+    q.C0 = dW1;
+    q.ldc0 = f;
+    q.c0_es = (int64_t)d * f;
+    q.M0 = d;
+    q.N0 = f;
+    if (sw) {
+      q.C1 = dW3;
+      q.ldc1 = f;
+      q.c1_es = (int64_t)d * f;
+      q.r1 = 0;
+      q.col1 = f;
+      q.M1 = d;
+      q.N1 = f;
+    }
+    e = moek::launch_kgemm(q, s);
+  }
+  return e;
+}
+
+hipError_t gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                         const float* dl, const float* dx_acc, void* dx, float* dWg, float* dbias,
+                         void* ws, hipStream_t s) {
+  if (p->B == 0) return hipSuccess;
+  GateBwdBufs b;
+  carve_gate_bwd(p, ws, &b);
+  const bool xb = p->x_dtype == MOE_BF16;
+  const int d = p->d, E = p->E, Ep = pad32(E);
+  const int64_t B = p->B;
+  hipError_t e = moek::launch_split_rows(dl, B, E, Ep, b.dl_s[0], b.dl_s[1], nullptr, s);
+  if (e == hipSuccess) e = moek::launch_split_rows(Wg, d, E, Ep, b.wg_s[0], b.wg_s[1], nullptr, s);
+  // dx = dl Wg^T + dx_acc over K = E: (hi, hi) + (hi, mid) + (mid, hi)
+  if (e == hipSuccess) {
+    moek::KGemm q{};
+    const uint16_t* As[3] = {b.dl_s[0], b.dl_s[0], b.dl_s[1]};
+    const uint16_t* Bs[3] = {b.wg_s[0], b.wg_s[1], b.wg_s[0]};
+    for (int i = 0; i < 3; ++i) {
+      q.A[i] = As[i];
+      q.B[i] = Bs[i];
+    }
+    q.nseg = 3;
+    q.a_row = q.b_row = true;
+    q.a_ld = Ep;
+    q.b_ld = Ep;
+    q.a_rows = (int)(B < 2147483647 ? B : 2147483647);
+    q.b_rows = d;
+    q.K = Ep;
+    q.groups = 1;
+    q.M = (int)B;
+    q.N = d;
+    q.mode = 1;
+    q.M0 = (int)B;
+    q.N0 = d;
+    q.ldc0 = d;
+    q.add = dx_acc;
+    q.ld_add = d;
+    q.xo = dx;
+    q.x_bf16 = xb ? 1 : 0;
+    e = moek::launch_kgemm(q, s);
+  }
+  // [dWg ; dbias] = [x | 1]^T dl over the tokens
+  if (e == hipSuccess) {
+    if (xb)
+      e = moek::launch_relayout_rb8(0, static_cast<const uint16_t*>(x), d, nullptr, 0, 0, 1, B,
+                                    d + 8, d, d, b.x8[0], s);
+    else
+      e = moek::launch_split_rb8(static_cast<const float*>(x), B, d, d + 8, d, b.x8[0], b.x8[1],
+                                 b.x8[2], s);
+  }
+  if (e == hipSuccess)
+    e = moek::launch_split_rb8(dl, B, E, Ep, -1, b.dl8[0], b.dl8[1], b.dl8[2], s);
+  if (e == hipSuccess) {
+    moek::KGemm q{};
+    if (xb) {
+      for (int i = 0; i < 3; ++i) {
+        q.A[i] = b.x8[0];
+        q.B[i] = b.dl8[i];
+      }
+      q.nseg = 3;
+    } else {
+      const int ai[6] = {0, 0, 1, 0, 2, 1}, bi[6] = {0, 1, 0, 2, 0, 1};
+      for (int i = 0; i < 6; ++i) {
+        q.A[i] = b.x8[ai[i]];
+        q.B[i] = b.dl8[bi[i]];
+      }
+      q.nseg = 6;
+    }
+    // split-K over the tokens: group g sums tokens g Ks .. (g + 1) Ks into
+    // its own [d + 1][E] partial; the partials are then added in g order
+    const GateSplit gs = gate_split(p);
+    q.a_w = d + 8;
+    q.b_w = Ep;
+    q.a_es = (int64_t)gs.Ks * (d + 8);
+    q.b_es = (int64_t)gs.Ks * Ep;
+    q.a_rows = d + 8;
+    q.b_rows = E;
+    q.K = gs.Ks;
+    q.Ktot = (int)moek::rb8_rows(B);
+    q.groups = gs.G;
+    q.M = d + 1;
+    q.N = E;
+    q.C0 = b.part;
+    q.ldc0 = E;
+    q.c0_es = (int64_t)(d + 1) * E;
+    q.M0 = d + 1;
+    q.N0 = E;
+    e = moek::launch_kgemm(q, s);
+    if (e == hipSuccess) e = moek::launch_sum_parts(b.part, gs.G, d, E, dWg, dbias, s);
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_combine_backward(const moe_problem_t* p, const void* dy, const moe_bf16_t* ret,
+                                  const int32_t* dest, const float* topk_w, moe_bf16_t* dret,
+                                  float* dw, hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!dy || !ret || !dest || !topk_w || !dret || !dw)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(dy) || !a16(ret) || !a16(dret) || !a4(dest) || !a4(topk_w) || !a4(dw)))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_combine_bwd(dy, p->x_dtype == MOE_BF16, ret, dest, topk_w, p->B,
+                                             p->k, p->d, kmax_of(p), dret, dw, stream));
+}
+
+moe_status_t moe_route_backward(const moe_problem_t* p, const float* logits,
+                                const int32_t* topk_idx, const float* dw,
+                                const int32_t* expert_load, float aux_coef, float* dlogits,
+                                hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  if (!std::isfinite(aux_coef)) return MOE_ERR_INVALID;
+  if (aux_coef != 0.0f && (!expert_load || !a4(expert_load))) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!logits || !topk_idx || !dw || !dlogits)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a4(logits) || !a4(topk_idx) || !a4(dw) || !a4(dlogits)))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_route_bwd(logits, topk_idx, dw, expert_load, aux_coef, p->B,
+                                           p->E, p->k, p->tau, dlogits, stream));
+}
+
+size_t moe_weights_bwd_bytes(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return SIZE_MAX;
+  return moek::packed_weights_bwd_bytes(p->e_end - p->e_begin, p->d, p->f,
+                                        p->act == MOE_SWIGLU);
+}
+
+moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
+                                  const moe_bf16_t* W3, const moe_bf16_t* W2, void* wpb,
+                                  size_t wpb_bytes, hipStream_t stream) {
+  moe_status_t st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool sw = p->act == MOE_SWIGLU;
+  const int nl = p->e_end - p->e_begin;
+  if (nl == 0) return MOE_OK;
+  if (!W1 || !W2 || (sw && !W3) || !wpb) return MOE_ERR_INVALID;
+  if (!a16(W1) || !a16(W2) || (sw && !a16(W3)) || !a16(wpb)) return MOE_ERR_INVALID;
+  if (wpb_bytes < moek::packed_weights_bwd_bytes(nl, p->d, p->f, sw)) return MOE_ERR_WORKSPACE;
+  return hip_status(
+      moek::launch_pack_weights_bwd(W1, sw ? W3 : nullptr, W2, nl, p->d, p->f, sw, wpb, stream));
+}
+
+moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
+                                     const int32_t* pack_src, const int32_t* expert_offset,
+                                     const void* wpacked, const void* wpacked_bwd,
+                                     moe_bf16_t* dret, float* dW1, float* dW3, float* dW2,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  const bool sw = p->act == MOE_SWIGLU;
+  const int nl = p->e_end - p->e_begin;
+  if (nl == 0) return MOE_OK;
+  if (!expert_offset || !a4(expert_offset)) return MOE_ERR_INVALID;
+  if (!wpacked || !wpacked_bwd || !dW1 || !dW2 || (sw && !dW3)) return MOE_ERR_INVALID;
+  if (!a16(wpacked) || !a16(wpacked_bwd) || !a4(dW1) || !a4(dW2) || (sw && !a4(dW3)))
+    return MOE_ERR_INVALID;
+  if (p->B > 0 && (!x || !pack_src || !dret || !a16(x) || !a16(dret) || !a4(pack_src)))
+    return MOE_ERR_INVALID;
+  const size_t need = carve_ffn_bwd(p, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
+  if (p->B == 0) {
+    // no rows: every weight gradient is zero
+    const int64_t n = (int64_t)nl * p->d * p->f;
+    hipError_t e = moek::launch_fill_zero(dW1, n, stream);
+    if (e == hipSuccess) e = moek::launch_fill_zero(dW2, n, stream);
+    if (e == hipSuccess && sw) e = moek::launch_fill_zero(dW3, n, stream);
+    return hip_status(e);
+  }
+  return hip_status(ffn_backward(p, x, pack_src, expert_offset, wpacked, wpacked_bwd, dret, dW1,
+                                 sw ? dW3 : nullptr, dW2, ws, stream));
+}
+
+moe_status_t moe_dispatch_backward(const moe_problem_t* p, const moe_bf16_t* dxp,
+                                   const int32_t* dest, const void* dy, float* dx_acc,
+                                   hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  if (p->B > 0 && (!dxp || !dest || !dx_acc || (p->add_residual && !dy))) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(dxp) || !a4(dest) || !a16(dx_acc) || (p->add_residual && !a16(dy))))
+    return MOE_ERR_INVALID;
+  return hip_status(moek::launch_unpack_sum(dxp, dest, dy, p->x_dtype == MOE_BF16,
+                                            p->add_residual != 0, p->B, p->k, p->d, kmax_of(p),
+                                            dx_acc, stream));
+}
+
+moe_status_t moe_gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                               const float* dlogits, const float* dx_acc, void* dx, float* dWg,
+                               float* dbias, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  if (!dWg || !a4(dWg) || (dbias && !a4(dbias))) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!x || !Wg || !dlogits || !dx)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a4(Wg) || !a4(dlogits) || !a4(dx) || (dx_acc && !a4(dx_acc))))
+    return MOE_ERR_INVALID;
+  const size_t need = carve_gate_bwd(p, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
+  if (p->B == 0) {
+    hipError_t e = moek::launch_fill_zero(dWg, (int64_t)p->d * p->E, stream);
+    if (e == hipSuccess && dbias) e = moek::launch_fill_zero(dbias, p->E, stream);
+    return hip_status(e);
+  }
+  return hip_status(gate_backward(p, x, Wg, dlogits, dx_acc, dx, dWg, dbias, ws, stream));
+}
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                          const void* wpacked, const void* wpacked_bwd, const moe_saved_t* sv,
+                          const void* dy, float aux_coef, const moe_grads_t* g, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_bwd(p);
+  if (st != MOE_OK) return st;
+  if (!sv || !g) return MOE_ERR_INVALID;
+  if (!std::isfinite(aux_coef)) return MOE_ERR_INVALID;
+  const bool sw = p->act == MOE_SWIGLU;
+  const int nl = p->e_end - p->e_begin;
+  if (!g->dWg || (nl > 0 && (!g->dW1 || !g->dW2 || (sw && !g->dW3)))) return MOE_ERR_INVALID;
+  if (nl > 0 && (!wpacked || !wpacked_bwd || !a16(wpacked) || !a16(wpacked_bwd)))
+    return MOE_ERR_INVALID;
+  if (!sv->expert_offset || (aux_coef != 0.0f && !sv->expert_load)) return MOE_ERR_INVALID;
+  if (p->B > 0 && (!x || !Wg || !dy || !g->dx || !sv->logits || !sv->topk_idx || !sv->topk_w ||
+                   !sv->dest || !sv->pack_src || !sv->ret))
+    return MOE_ERR_INVALID;
+  if (p->B > 0 && (!a16(x) || !a16(dy) || !a16(sv->ret) || !a4(g->dx)))
+    return MOE_ERR_INVALID;
+  if ((g->dw && !a4(g->dw)) || (g->dlogits && !a4(g->dlogits))) return MOE_ERR_INVALID;
+  const size_t need = carve_bwd(p, g, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
+  BwdBufs b;
+  carve_bwd(p, g, ws, &b);
+  const bool xb = p->x_dtype == MOE_BF16;
+  hipError_t e = hipSuccess;
+  if (p->B == 0) {
+    if (nl > 0) {
+      const int64_t n = (int64_t)nl * p->d * p->f;
+      e = moek::launch_fill_zero(g->dW1, n, stream);
+      if (e == hipSuccess) e = moek::launch_fill_zero(g->dW2, n, stream);
+      if (e == hipSuccess && sw) e = moek::launch_fill_zero(g->dW3, n, stream);
+    }
+    if (e == hipSuccess) e = moek::launch_fill_zero(g->dWg, (int64_t)p->d * p->E, stream);
+    if (e == hipSuccess && g->dbias) e = moek::launch_fill_zero(g->dbias, p->E, stream);
+    return hip_status(e);
+  }
+  e = moek::launch_combine_bwd(dy, xb, sv->ret, sv->dest, sv->topk_w, p->B, p->k, p->d,
+                               kmax_of(p), b.dret, b.dw, stream);
+  if (e == hipSuccess)
+    e = moek::launch_route_bwd(sv->logits, sv->topk_idx, b.dw, sv->expert_load, aux_coef, p->B,
+                               p->E, p->k, p->tau, b.dl, stream);
+  if (e == hipSuccess && nl > 0)
+    e = ffn_backward(p, x, sv->pack_src, sv->expert_offset, wpacked, wpacked_bwd, b.dret, g->dW1,
+                     sw ? g->dW3 : nullptr, g->dW2, b.ffn_ws, stream);
+  if (e == hipSuccess)
+    e = moek::launch_unpack_sum(b.dret, sv->dest, dy, xb, p->add_residual != 0, p->B, p->k, p->d,
+                                kmax_of(p), b.dx_acc, stream);
+  if (e == hipSuccess)
+    e = gate_backward(p, x, Wg, b.dl, b.dx_acc, g->dx, g->dWg, g->dbias, b.gate_ws, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -243,4 +243,88 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// ---- backward pass (backward.hip, wgrad.hip, expert_gemm.hip) -------------
+hipError_t launch_combine_bwd(const void* dy, bool x_bf16, const uint16_t* ret,
+                              const int32_t* dest, const float* w, int64_t B, int k, int d,
+                              int64_t kmax, uint16_t* dret, float* dw, hipStream_t s);
+// load: expert_load [E] (read when aux_coef != 0)
+hipError_t launch_route_bwd(const float* logits, const int32_t* idx, const float* dw,
+                            const int32_t* load, float aux_coef, int64_t B, int E, int k,
+                            float tau, float* dl, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, bool x_bf16, const int32_t* pack_src,
+                              const int32_t* eo, int e_begin, int e_end, int64_t B, int d,
+                              int64_t rows_max, uint16_t* out, hipStream_t s);
+// rows of one RB8 segment: the row capacity rounded up to 32
+int64_t rb8_rows(int64_t rows);
+// mode 0 copy, 1 GELU of Z, 2 SwiGLU of the interleaved Z1/Z3 columns
+// rel: src rows are local (row 0 = expert_offset[e_begin]); else absolute
+hipError_t launch_relayout_rb8(int mode, const uint16_t* src, int64_t src_ld, const int32_t* eo,
+                               int e_begin, int rel, int n_seg, int64_t rows_cap, int W,
+                               int src_w, int one_col, uint16_t* out, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// out0[m][n] (m < M0) / out1[n] (m == M0) = sum over g of part[g][m][n], in g
+// order; part is [G][M0 + 1][N]
+hipError_t launch_sum_parts(const float* part, int G, int M0, int N, float* out0, float* out1,
+                            hipStream_t s);
+hipError_t launch_split_rows(const float* src, int64_t rows, int cols, int Wp, uint16_t* o0,
+                             uint16_t* o1, uint16_t* o2, hipStream_t s);
+hipError_t launch_split_rb8(const float* src, int64_t rows, int cols, int Wp, int one_col,
+                            uint16_t* o0, uint16_t* o1, uint16_t* o2, hipStream_t s);
+hipError_t launch_unpack_sum(const uint16_t* dxp, const int32_t* dest, const void* dy,
+                             bool x_bf16, bool residual, int64_t B, int k, int d, int64_t kmax,
+                             float* dx_acc, hipStream_t s);
+
+// Grouped K-fragment GEMM (wgrad.hip): C_g = sum over segments of A B^T with
+// K-fragment operands, RB8 (a_row false: a_w columns) or row-major (a_row
+// true: a_ld).  Groups: K from expert_offset (eo, e_begin) or K.
+struct KGemm {
+  const uint16_t* A[6];
+  const uint16_t* B[6];
+  int nseg;
+  bool a_row, b_row;
+  int64_t a_ld, b_ld;
+  int a_w, b_w;
+  int64_t a_es, b_es;  // per-group element offsets
+  int a_rows, b_rows;  // valid rows m of A and n of B (loads are clamped)
+  const int32_t* eo;
+  int e_begin;
+  int K;
+  int Ktot;  // > 0 (eo null): split-K, group g takes rows g K .. min((g+1) K, Ktot)
+  int groups, M, N;
+  int mode;  // 0: fp32 into C0 (m < M0, n < N0) or C1 at (m - r1, n - col1);
+             // 1: acc + add stored to xo (bf16 or fp32), rows M0, cols N0, stride ldc0
+  float* C0;
+  int64_t ldc0, c0_es;
+  int M0, N0;
+  float* C1;
+  int64_t ldc1, c1_es;
+  int r1, col1, M1, N1;
+  const float* add;
+  int64_t ld_add;
+  void* xo;
+  int x_bf16;
+};
+hipError_t launch_kgemm(const KGemm& q, hipStream_t s);
+
+// Expert FFN backward pieces on the forward's grouped GEMM:
+//   recompute:  Z = X_loc W1 (no activation; SwiGLU: W1 and W3 products in
+//               the GEMM1 tile order, zw = expert_ffn_zw columns)
+//   dact:       dZ = dact(dret W2^T, Z) ([dZ1 | dZ3] for SwiGLU), local rows
+//   dgrad:      dXp = dZ [W1 | W3]^T, written over the local rows of dret
+// wpb: the blocked backward weights (launch_pack_weights_bwd).
+int expert_ffn_zw(int f, bool swiglu);
+size_t packed_weights_bwd_bytes(int n_local, int d, int f, bool swiglu);
+hipError_t launch_pack_weights_bwd(const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                                   int n_local, int d, int f, bool swiglu, void* wpb,
+                                   hipStream_t s);
+hipError_t launch_ffn_recompute(const uint16_t* xloc, const int32_t* expert_offset, int e_begin,
+                                int n_local, int rows_max, int rows_hint, int d, int f,
+                                bool swiglu, const void* wp, uint16_t* Z, hipStream_t s);
+hipError_t launch_ffn_dact(const uint16_t* dret, const int32_t* expert_offset, int e_begin,
+                           int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                           const void* wpb, const uint16_t* Z, uint16_t* dZ, hipStream_t s);
+hipError_t launch_ffn_dgrad(const uint16_t* dZ, const int32_t* expert_offset, int e_begin,
+                            int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
+                            const void* wpb, uint16_t* dxp, hipStream_t s);
+
 }  // namespace moek

@@ -90,7 +90,10 @@ typedef enum {
   MOE_OP_FORWARD = 2,
   MOE_OP_ROUTING_STATS = 3,
   MOE_OP_SHARED_FFN = 4,
-  MOE_OP_FORWARD_EXPERT_CHOICE = 5
+  MOE_OP_FORWARD_EXPERT_CHOICE = 5,
+  MOE_OP_EXPERT_FFN_BACKWARD = 6,
+  MOE_OP_GATE_BACKWARD = 7,
+  MOE_OP_BACKWARD = 8
 } moe_op_t;
 
 /* The problem statement: B tokens of hidden size d, E experts, top-k routing
@@ -517,6 +520,128 @@ moe_status_t moe_forward_expert_choice(const moe_problem_t* p, const void* x,
                                        const void* wpacked, void* y,
                                        moe_expert_choice_out_t* out, void* ws,
                                        size_t ws_bytes, hipStream_t stream);
+
+/* ---- backward pass (training) ------------------------------------------ */
+
+/* The layer's gradients for an output gradient dy ("Expert Parallelism",
+ * narrativegoldmine.com, "About": the sparsely gated layer is trained by
+ * backpropagation with an auxiliary load-balancing loss; "Formal
+ * Algorithm", last step: the auxiliary loss joins the training loss).  The
+ * loss is L = sum_t <dy_t, y_t> + aux_coef * sum_e f_e P_e (f_e = n_e / B
+ * counts, constant; P_e the mean router probability).  The top-k choice and
+ * the capacity decision are held fixed: gradient flows through the gate
+ * weights w_tj = p_{t, idx_tj} and the expert outputs only, and a dropped
+ * assignment gets none.  Rows of other ranks' experts pass their gradient
+ * back unchanged (their forward return is the identity).  Supported: the
+ * drop policy (MOE_OVERFLOW_NEXT returns MOE_ERR_UNSUPPORTED), with or
+ * without the residual, any local expert range, the unavailable mask (it
+ * only shows in dest).  Matrix products run on bf16 matrix cores with fp32
+ * accumulation: dret, the recomputed pre-activations Z, dZ and H are bf16;
+ * the router's fp32 operands are split exactly into bf16 parts.  Every call
+ * checks its arguments on the host before any launch. */
+
+/* Combine backward: dret[dest[t,j]] = topk_w[t,j] * dy[t] (bf16) and
+ * dw[t,j] = <dy[t], ret[dest[t,j]]> (fp32; 0 for a dropped choice).
+ *   dy [B][d] x_dtype; ret [Kmax][d] bf16 (the forward's expert outputs);
+ *   dest, topk_w [B][k]; dret [Kmax][d] bf16 out (rows of dropped
+ *   assignments are not written); dw [B][k] float out. */
+moe_status_t moe_combine_backward(const moe_problem_t* p, const void* dy, const moe_bf16_t* ret,
+                                  const int32_t* dest, const float* topk_w, moe_bf16_t* dret,
+                                  float* dw, hipStream_t stream);
+
+/* Router backward: with p_t = softmax(logits_t / tau) and
+ * dp[t,e] = sum_j [topk_idx[t,j] = e] dw[t,j] + aux_coef n_e / B^2,
+ * dlogits[t,e] = p[t,e] (dp[t,e] - sum_e' p[t,e'] dp[t,e']) / tau.
+ *   logits [B][E]; topk_idx, dw [B][k]; expert_load [E] (n_e; may be NULL
+ *   when aux_coef == 0); dlogits [B][E] float out. */
+moe_status_t moe_route_backward(const moe_problem_t* p, const float* logits,
+                                const int32_t* topk_idx, const float* dw,
+                                const int32_t* expert_load, float aux_coef, float* dlogits,
+                                hipStream_t stream);
+
+/* Bytes of the blocked backward copy of the local experts' weights. */
+size_t moe_weights_bwd_bytes(const moe_problem_t* p);
+
+/* The weights rearranged for the expert backward's matrix products (the
+ * transposed roles: dH = dret . W2^T and dX = [dZ1 | dZ3] . [W1 | W3]^T),
+ * from the same [in, out] matrices as moe_pack_weights; a format
+ * conversion done when the weights change, owned by the caller.
+ *   W1, W3 [n_local][d][f]; W2 [n_local][f][d]; wpacked_bwd
+ *   moe_weights_bwd_bytes(p) bytes, 16-byte aligned, out. */
+moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
+                                  const moe_bf16_t* W3, const moe_bf16_t* W2,
+                                  void* wpacked_bwd, size_t wpacked_bwd_bytes,
+                                  hipStream_t stream);
+
+/* Expert FFN backward.  For each local expert and its packed rows
+ * (X = x[pack_src[r]], bf16): the pre-activations Z = X . W1 (and X . W3)
+ * are recomputed, then dH = dret . W2^T, dZ = dH * act'(Z) (SwiGLU:
+ * dZ1 = dH Z3 silu'(Z1), dZ3 = dH silu(Z1)), dX = dZ1 . W1^T (+ dZ3 . W3^T),
+ * dW2 = H^T . dret, dW1 = X^T . dZ1, dW3 = X^T . dZ3 (H = act(Z), bf16).
+ * dret is overwritten in place: its local rows become dX, the gradient of
+ * the packed rows (other rows already are: the identity return).
+ *   x [B][d] x_dtype; pack_src, expert_offset as written by the forward;
+ *   wpacked (moe_pack_weights), wpacked_bwd (moe_pack_weights_bwd);
+ *   dret [Kmax][d] bf16 in/out; dW1, dW3 [n_local][d][f], dW2
+ *   [n_local][f][d] float out (dW3 NULL unless SwiGLU); an expert with no
+ *   rows gets zero gradients.
+ *   ws >= moe_workspace_bytes(p, MOE_OP_EXPERT_FFN_BACKWARD), 16-byte aligned */
+moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
+                                     const int32_t* pack_src, const int32_t* expert_offset,
+                                     const void* wpacked, const void* wpacked_bwd,
+                                     moe_bf16_t* dret, float* dW1, float* dW3, float* dW2,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch (pack) backward: dx_acc[t] = sum_j dXp[dest[t,j]] over kept
+ * choices, in j order, plus dy[t] when the problem adds the residual.
+ *   dxp [Kmax][d] bf16; dest [B][k]; dy [B][d] x_dtype (read only with the
+ *   residual); dx_acc [B][d] float out. */
+moe_status_t moe_dispatch_backward(const moe_problem_t* p, const moe_bf16_t* dxp,
+                                   const int32_t* dest, const void* dy, float* dx_acc,
+                                   hipStream_t stream);
+
+/* Gate backward: dx = dlogits . Wg^T (+ dx_acc), dWg = x^T . dlogits,
+ * dbias = sum_t dlogits[t] (bias of the logits).
+ *   x [B][d] x_dtype; Wg [d][E]; dlogits [B][E]; dx_acc [B][d] float or
+ *   NULL; dx [B][d] x_dtype out; dWg [d][E] float out; dbias [E] float out
+ *   or NULL.  ws >= moe_workspace_bytes(p, MOE_OP_GATE_BACKWARD). */
+moe_status_t moe_gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                               const float* dlogits, const float* dx_acc, void* dx, float* dWg,
+                               float* dbias, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* What the backward reads from the forward (moe_forward's outputs, with
+ * packed holding the expert outputs after the call). */
+typedef struct {
+  const float* logits;          /* [B][E]   */
+  const int32_t* topk_idx;      /* [B][k]   */
+  const float* topk_w;          /* [B][k]   */
+  const int32_t* dest;          /* [B][k]   */
+  const int32_t* expert_load;   /* [E]      */
+  const int32_t* expert_offset; /* [E+1]    */
+  const int32_t* pack_src;      /* [Kmax]   */
+  const moe_bf16_t* ret;        /* [Kmax][d] */
+} moe_saved_t;
+
+/* The gradients moe_backward writes; dW3 only for SwiGLU, dbias may be
+ * NULL, dlogits / dw NULL -> workspace. */
+typedef struct {
+  void* dx;       /* [B][d] x_dtype      */
+  float* dWg;     /* [d][E]              */
+  float* dbias;   /* [E]                 */
+  float* dW1;     /* [n_local][d][f]     */
+  float* dW3;     /* [n_local][d][f]     */
+  float* dW2;     /* [n_local][f][d]     */
+  float* dlogits; /* [B][E]              */
+  float* dw;      /* [B][k]              */
+} moe_grads_t;
+
+/* The whole backward on one stream: combine, route, expert FFN, dispatch
+ * and gate backward, in that order (the forward's steps reversed).
+ *   ws >= moe_workspace_bytes(p, MOE_OP_BACKWARD), 16-byte aligned. */
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                          const void* wpacked, const void* wpacked_bwd, const moe_saved_t* saved,
+                          const void* dy, float aux_coef, const moe_grads_t* grads, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -820,7 +820,8 @@ def combine_backward(dy: np.ndarray, ret: np.ndarray, dest: np.ndarray, w: np.nd
 
 
 def route_backward(logits: np.ndarray, idx: np.ndarray, dw: np.ndarray, tau: float = 1.0,
-                   aux_coef: float = 0.0, expert_load: Optional[np.ndarray] = None):
+                   aux_coef: float = 0.0, expert_load: Optional[np.ndarray] = None,
+                   batch: Optional[int] = None):
     """Gradient of the loss with respect to the router logits [B, E].
 
     The gate weights are w[t,j] = p[t, idx[t,j]] with p_t = softmax(g_t / tau)
@@ -828,7 +829,9 @@ def route_backward(logits: np.ndarray, idx: np.ndarray, dw: np.ndarray, tau: flo
     dp[t,e] = sum_j [idx[t,j] = e] dw[t,j] (+ aux_coef f_e / B from
     L_aux = sum_e f_e P_e, f_e = n_e / B constant):
     dl[t,e] = (1 / tau) p[t,e] (dp[t,e] - sum_e' p[t,e'] dp[t,e']).
-    ``expert_load`` (n_e) is needed when aux_coef != 0.  Pins: central finite
+    ``expert_load`` (n_e) is needed when aux_coef != 0.  ``batch``: the
+    batch size B of the auxiliary term when ``logits`` holds only some of
+    the batch's tokens (default: its row count).  Pins: central finite
     differences of softmax + top-k weights with the choice held fixed, and
     of the auxiliary loss (test_oracle_backward)."""
     p = softmax(logits, tau)
@@ -838,8 +841,9 @@ def route_backward(logits: np.ndarray, idx: np.ndarray, dw: np.ndarray, tau: flo
     np.add.at(dp, (np.repeat(np.arange(B), idx.shape[1]), idx.reshape(-1)),
               np.asarray(dw, dtype=np.float64).reshape(-1))
     if aux_coef != 0.0:
-        f = np.asarray(expert_load, dtype=np.float64) / B
-        dp += aux_coef * f[None, :] / B
+        Bb = B if batch is None else int(batch)
+        f = np.asarray(expert_load, dtype=np.float64) / Bb
+        dp += aux_coef * f[None, :] / Bb
     s = (p * dp).sum(axis=1, keepdims=True)
     return p * (dp - s) / float(tau)
 
