@@ -66,6 +66,14 @@ def parse():
     ap.add_argument("--shared-expert", type=int, default=0, metavar="F",
                     help="add a shared expert of hidden size F (same activation) on every "
                          "token: moe_forward_shared (bf16 workloads)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's backward pass (moe_backward, for a seeded output "
+                         "gradient, on one forward's saved outputs) instead of the forward")
+    ap.add_argument("--aux-coef", type=float, default=0.01,
+                    help="auxiliary load-balancing loss coefficient of --backward")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only time the HBM streaming probes (libmoe_probe.so): read-only, "
+                         "write-only and copy over 4 GiB buffers")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only time the matrix-core ceiling probe (libmoe_probe.so) with random "
                          "and with near-constant bf16 operands")
@@ -119,6 +127,58 @@ def mfma_probe(torch) -> dict:
                      "frac_of_2500": round(flop / mean / 1e12 / 2500.0, 4)}
     return {"mfma_probe": res, "grid": grid, "iters": iters, "tflop_per_launch": round(flop / 1e12, 3),
             "warmup_launches": 200, "rounds": 3, "launches_per_round": 5}
+
+
+def hbm_probe(torch) -> dict:
+    """What HBM sustains for plain streams on this part: read-only (each
+    16-byte chunk loaded once, folded into a register), write-only and copy
+    kernels over 4 GiB buffers (far past the 256 MB MALL), one grid of 8
+    workgroups per CU.  After 5 untimed launches of each, 3 rounds of 5
+    launches per kind; reported: mean over the rounds in GB/s (bytes moved:
+    read, written, or read + written)."""
+    import ctypes
+    here = os.path.dirname(os.path.abspath(__file__))
+    lib = ctypes.CDLL(os.path.join(here, "expert_token_routing_fp32_amd", "libmoe_probe.so"))
+    lib.moe_probe_hbm.restype = ctypes.c_int
+    lib.moe_probe_hbm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    nbytes = 4 << 30
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    grid = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def call(mode):
+        rc = lib.moe_probe_hbm(mode, ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                               nbytes, ctypes.c_void_p(out.data_ptr()), grid,
+                               ctypes.c_void_p(stream.cuda_stream))
+        assert rc == 0, rc
+
+    kinds = (("read", 0, 1), ("write", 1, 1), ("copy", 2, 2))
+    for _, mode, _ in kinds:
+        for _ in range(5):
+            call(mode)
+    torch.cuda.synchronize()
+    res = {}
+    for name, mode, mult in kinds:
+        rounds = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                call(mode)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rounds.append(e0.elapsed_time(e1) / 5 * 1e-3)
+        mean = sum(rounds) / len(rounds)
+        res[name] = {"us_per_launch": round(mean * 1e6, 1),
+                     "gbs": round(mult * nbytes / mean / 1e9, 1),
+                     "gbs_rounds": [round(mult * nbytes / r / 1e9, 1) for r in rounds],
+                     "frac_of_8000": round(mult * nbytes / mean / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"hbm_probe": res, "bytes": nbytes, "grid": grid, "rounds": 3,
+            "launches_per_round": 5}
 
 
 def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
@@ -235,6 +295,121 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
                       "input generation excluded"}
 
 
+def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
+    """The backward pass: one forward (outputs kept), then moe_backward on
+    those outputs and a seeded output gradient, W untimed + K timed calls
+    bracketed by synchronizations; then the same number of calls of the
+    stage entry points with events between them for the breakdown."""
+    bf16 = w.x_dtype == "bf16"
+    y, o = moe.forward(p, x, Wg, bias, wp, outputs=True)
+    rs = np.random.default_rng(w.seed + 7)
+    dy_np = rs.standard_normal((w.B, w.d)).astype(np.float32)
+    if bf16:
+        import moe_synth
+        dy = torch.from_numpy(moe_synth.f32_to_bf16_bits(dy_np).view(np.int16)).to(dev)
+    else:
+        dy = torch.from_numpy(dy_np).to(dev)
+    ws = torch.empty(moe.workspace_bytes(p, "backward"), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        return moe.backward(p, x, Wg, wp, wpb, o, dy, aux_coef=args.aux_coef, ws=ws)
+    log(f"[bench] backward: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] backward: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+
+    # breakdown: the stage calls of the same chain, events between them
+    keys = ("combine", "route", "expert_ffn", "dispatch", "gate")
+    per = {k_: [] for k_ in keys}
+    km = moe.max_kept(p)
+    dret = torch.empty((max(km, 1), w.d), dtype=torch.int16, device=dev)
+    dwb = torch.empty((w.B, w.k), dtype=torch.float32, device=dev)
+    dlb = torch.empty((w.B, w.E), dtype=torch.float32, device=dev)
+    accb = torch.empty((w.B, w.d), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(moe.workspace_bytes(p, "expert_ffn_backward"), 1), dtype=torch.uint8,
+                       device=dev)
+    ws_g = torch.empty(max(moe.workspace_bytes(p, "gate_backward"), 1), dtype=torch.uint8,
+                       device=dev)
+    for _ in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        moe.combine_backward(p, dy, o["packed"], o["dest"], o["topk_w"], dret=dret, dw=dwb)
+        ev[1].record()
+        moe.route_backward(p, o["logits"], o["topk_idx"], dwb, o["expert_load"], args.aux_coef,
+                           dlogits=dlb)
+        ev[2].record()
+        moe.expert_ffn_backward(p, x, o["pack_src"], o["expert_offset"], wp, wpb, dret, ws=ws_f)
+        ev[3].record()
+        moe.dispatch_backward(p, dret, o["dest"], dy if p.add_residual else None, dx_acc=accb)
+        ev[4].record()
+        moe.gate_backward(p, x, Wg, dlb, dx_acc=accb, ws=ws_g)
+        ev[5].record()
+        torch.cuda.synchronize()
+        for i, k_ in enumerate(keys):
+            per[k_].append(ev[i].elapsed_time(ev[i + 1]) * 1e-3)
+    med = {k_: float(np.median(v)) for k_, v in per.items()}
+    keep = o["keep"].cpu().numpy().astype(bool)
+    eo = o["expert_offset"].cpu().numpy()
+    alg = algorithmic(w, keep, eo)
+    # the expert backward's algorithmic work: dX and the weight gradients,
+    # twice the forward's FLOPs (the recomputed pre-activations are extra)
+    ffn_flop = 2.0 * alg["ffn_flop"]
+    t_ffn = med["expert_ffn"]
+    tfl = ffn_flop / t_ffn / 1e12
+    sx = 2 if bf16 else 4
+    K, B, d, E, k = alg["K"], w.B, w.d, w.E, w.k
+    # combine backward: dy once, ret and dret rows once each, dw; dispatch
+    # backward: dXp rows once, dx_acc written (fp32)
+    comb_bytes = B * d * sx + 2.0 * 2 * d * K + 8.0 * B * k
+    disp_bytes = 2.0 * d * K + 4.0 * B * d
+    out = {
+        "metric": "MoE-layer backward tokens/s on 1 MI355X (moe_backward)",
+        "value": round(w.B / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} d={w.d} E={w.E} top-{w.k} c={w.c} "
+                               f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
+                               f"local experts [{w.e_begin},{w.e_end}), backward, "
+                               f"aux_coef={args.aux_coef}",
+                   "global_batch": w.B},
+        "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "expert FFN backward (moe_expert_ffn_backward: recompute, dH with "
+                               "the activation derivative, dX, weight gradients, re-layouts)",
+                     "algorithmic_flop": ffn_flop, "avg_launch_us": round(t_ffn * 1e6, 2),
+                     "timing": "HIP events around the stage call, median over the steps"},
+        "breakdown": {
+            **{f"{k_}_backward_us": round(v * 1e6, 2) for k_, v in med.items()},
+            "combine_backward_hbm_frac": round(comb_bytes / med["combine"] / 1e9 / HBM_PEAK_GBS,
+                                               4),
+            "dispatch_backward_hbm_frac": round(disp_bytes / med["dispatch"] / 1e9
+                                                / HBM_PEAK_GBS, 4),
+            "gate_backward_mfma_frac": round(
+                4.0 * B * d * E * 3 / med["gate"] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "timing": "stage calls with events between them (host enqueue gaps included), "
+                      "median over the steps",
+            "kept": K, "kept_local": alg["Kloc"],
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -255,6 +430,10 @@ def main():
 
     if args.mfma_probe:
         print(json.dumps(mfma_probe(torch)))
+        return
+
+    if args.hbm_probe:
+        print(json.dumps(hbm_probe(torch)))
         return
 
     import expert_token_routing_fp32_amd as moe
@@ -317,6 +496,17 @@ def main():
         ws = torch.empty(moe.lib().moe_forward_shared_workspace_bytes(
             ctypes.byref(p), ctypes.byref(ps)), dtype=torch.uint8, device=dev)
     y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+    if args.backward:
+        if ec or shared is not None or args.overflow != "drop":
+            raise SystemExit("--backward goes with token-choice routing, the drop policy and "
+                             "no shared expert")
+        W1 = d16(inp["W1"] if bf16 else inp["W1_bits"])
+        W2 = d16(inp["W2"] if bf16 else inp["W2_bits"])
+        W3 = d16(inp["W3"] if bf16 else inp["W3_bits"]) if w.act == "swiglu" else None
+        wpb = moe.pack_weights_bwd(p, W1, W3, W2)
+        del W1, W2, W3
+        bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev)
+        return
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
     # HIP events recorded by the library on its stream.  moe_forward takes

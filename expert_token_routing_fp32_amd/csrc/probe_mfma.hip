@@ -91,3 +91,38 @@ extern "C" double moe_probe_mfma_flop(int grid, int iters) {
   // per wavefront and iteration: 64 MFMAs of 32 x 32 x 16 multiply-adds
   return (double)grid * 4.0 * (double)iters * 64.0 * (2.0 * 32 * 32 * 16);
 }
+
+// ---- HBM streaming probes ----------------------------------------------------
+namespace {
+
+__global__ __launch_bounds__(256) void hbm_probe_kernel(int mode, const p_u32x4* __restrict__ src,
+                                                        p_u32x4* __restrict__ dst, int64_t n,
+                                                        unsigned* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (mode == 0) {
+    unsigned acc = 0u;
+    for (; i < n; i += stride) {
+      const p_u32x4 v = __builtin_nontemporal_load(src + i);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+  } else if (mode == 1) {
+    const p_u32x4 v = {(unsigned)i, 1u, 2u, 3u};
+    for (; i < n; i += stride) __builtin_nontemporal_store(v, dst + i);
+  } else {
+    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  }
+}
+
+}  // namespace
+
+extern "C" int moe_probe_hbm(int mode, const void* src, void* dst, size_t bytes, unsigned* out,
+                             int grid, hipStream_t stream) {
+  if (mode < 0 || mode > 2 || bytes == 0 || bytes % 16 || grid < 1) return 1;
+  if ((mode != 1 && !src) || (mode != 0 && !dst) || (mode == 0 && !out)) return 1;
+  hipLaunchKernelGGL(hbm_probe_kernel, dim3(grid), dim3(256), 0, stream, mode,
+                     static_cast<const p_u32x4*>(src), static_cast<p_u32x4*>(dst),
+                     (int64_t)(bytes / 16), out);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}

@@ -6,7 +6,8 @@
  * sustain on this part when nothing but the GEMM's inner-loop mix runs:
  * one wavefront per SIMD, bf16 MFMAs 32x32x16 with fp32 accumulation, A
  * fragments re-read from LDS, no global memory traffic.  bench.py
- * --mfma-probe times it with HIP events.
+ * --mfma-probe times it with HIP events; bench.py --hbm-probe times the
+ * streaming read, write and copy probes below.
  */
 #ifndef MOE_PROBE_H
 #define MOE_PROBE_H
@@ -29,6 +30,18 @@ int moe_probe_mfma(float* out, int grid, int iters, int random_data, hipStream_t
 
 /* Floating-point operations of one moe_probe_mfma launch with these sizes. */
 double moe_probe_mfma_flop(int grid, int iters);
+
+/* HBM bandwidth probes (the memory side of the rooflines): one launch on
+ * `stream` over `bytes` (a multiple of 16) of device memory, each thread
+ * moving 16-byte chunks in a grid-stride loop over `grid` workgroups of 256:
+ *   mode 0  read only: every chunk of src is loaded (non-temporally) and
+ *           folded into one word per thread, written to out[grid * 256]
+ *   mode 1  write only: every chunk of dst is stored (non-temporally)
+ *   mode 2  copy: src chunks stored to dst
+ * Returns 0, 1 for invalid arguments (nothing launched), 2 for a launch
+ * error.  Asynchronous. */
+int moe_probe_hbm(int mode, const void* src, void* dst, size_t bytes, unsigned* out, int grid,
+                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_probe_library_exports_its_header():
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
-    assert names == ["moe_probe_mfma", "moe_probe_mfma_flop"]
+    assert names == ["moe_probe_hbm", "moe_probe_mfma", "moe_probe_mfma_flop"]
     probe = ctypes.CDLL(os.path.join(ROOT, "expert_token_routing_fp32_amd", "libmoe_probe.so"))
     for n in names:
         assert hasattr(probe, n), n
@@ -55,6 +55,12 @@ def test_probe_library_exports_its_header():
     probe.moe_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
     assert probe.moe_probe_mfma(None, 256, 10, 1, None) == 1
+    probe.moe_probe_hbm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    assert probe.moe_probe_hbm(3, None, None, 16, None, 1, None) == 1
+    assert probe.moe_probe_hbm(0, None, None, 16, None, 1, None) == 1
+    assert probe.moe_probe_hbm(1, None, ctypes.c_void_p(16), 15, None, 1, None) == 1
 
 
 def test_ctypes_layout_matches_c(L, tmp_path):
