@@ -351,8 +351,9 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict
 // padded with zeros to a multiple of 32), split into parts; one thread per
 // (8-row group, column).  one_col >= 0: that column is 1 (in part hi).
 __global__ __launch_bounds__(256) void split_rb8_kernel(const float* __restrict__ src,
-                                                        int64_t rows, int cols, int Wp,
-                                                        int one_col, uint16_t* __restrict__ o0,
+                                                        int64_t rows, int cols, int64_t ld,
+                                                        int trans, int Wp, int one_col,
+                                                        uint16_t* __restrict__ o0,
                                                         uint16_t* __restrict__ o1,
                                                         uint16_t* __restrict__ o2) {
   const int64_t groups = (rows + 31) / 32 * 4;
@@ -366,7 +367,9 @@ __global__ __launch_bounds__(256) void split_rb8_kernel(const float* __restrict_
     for (int u = 0; u < 8; ++u) {
       const int64_t r = g * 8 + u;
       float v = 0.f;
-      if (r < rows) v = c < cols ? src[r * cols + c] : (c == one_col ? 1.0f : 0.f);
+      if (r < rows)
+        v = c < cols ? (trans ? src[(int64_t)c * ld + r] : src[r * ld + c])
+                     : (c == one_col ? 1.0f : 0.f);
       split3f(v, a[u], b[u], e[u]);
     }
     const int64_t o = i * 8;
@@ -546,12 +549,13 @@ hipError_t launch_split_rows(const float* src, int64_t rows, int cols, int Wp, u
   return hipGetLastError();
 }
 
-hipError_t launch_split_rb8(const float* src, int64_t rows, int cols, int Wp, int one_col,
-                            uint16_t* o0, uint16_t* o1, uint16_t* o2, hipStream_t s) {
+hipError_t launch_split_rb8(const float* src, int64_t rows, int cols, int64_t ld, bool trans,
+                            int Wp, int one_col, uint16_t* o0, uint16_t* o1, uint16_t* o2,
+                            hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   const int64_t total = (rows + 31) / 32 * 4 * Wp;
   hipLaunchKernelGGL(split_rb8_kernel, dim3(bgrid(total, 256)), dim3(256), 0, s, src, rows, cols,
-                     Wp, one_col, o0, o1, o2);
+                     ld, trans ? 1 : 0, Wp, one_col, o0, o1, o2);
   return hipGetLastError();
 }
 

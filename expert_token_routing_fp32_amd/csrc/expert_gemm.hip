@@ -384,87 +384,80 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
     }
   }
   if constexpr (MODE == MODE_DGELU || MODE == MODE_DSWIGLU) {
-    // Backward epilogue of tile `tile`: acc[c][i][r] is dH at row 32 i +
-    // 8 (r / 4) + 4 lg + r % 4 of the slice and hidden unit
-    // u = 256 tile + 64 wave + 32 c + l32.  Output q (dZ, or dZ1 then dZ3)
-    // goes through the same LDS staging as the forward's: 32 rows x 64
-    // columns per wavefront, stored as 16-byte row segments.
+    // Backward epilogue of tile `tile`: the products are dH for hidden units
+    // u = 256 tile + 64 wave + 32 c + l32.  They are staged through LDS as
+    // bf16 exactly like the plain epilogue's outputs (32 rows x 64 units per
+    // wavefront); then each lane takes 16-byte row segments (8 units of one
+    // row), loads the matching pre-activations Z as 16-byte vectors and
+    // writes dZ = dH * gelu'(Z), or dZ1 = dH Z3 silu'(Z1) and dZ3 = dH
+    // silu(Z1) at columns u and f + u, as 16-byte stores.
     const bool odd = lane & 1;
+    int ldo = a.ldo;
+    asm volatile("" : "+s"(ldo));
+    uint16_t* out = a.Out + o_row0 * ldo;
     const uint16_t* zb = a.Z + o_row0 * a.zw;
-    uint16_t* out = a.Out + o_row0 * a.ldo;
     const int nval = a.Nout;
     char* stg = smem + kStageOff + wave * 32 * 128;
     const int col0 = tile * 256 + 64 * wave;
-    // row pairs per chunk: fewer than the forward's, the Z values of a chunk
-    // being live beside the prefetched weights
-    constexpr int kEb = 2;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
 #pragma unroll
-      for (int q = 0; q < (MODE == MODE_DSWIGLU ? 2 : 1); ++q) {
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int u = col0 + 32 * c + l32;
+        for (int r0 = 0; r0 < 16; r0 += 2 * kEpg) {
+          float v0[kEpg], v1[kEpg];
 #pragma unroll
-          for (int r0 = 0; r0 < 16; r0 += 2 * kEb) {
-            // Opaque row stride: keeps this chunk's Z loads here instead of
-            // letting the compiler hoist every load of the tile (and spill).
-            int zw = a.zw;
-            asm volatile("" : "+s"(zw));
-            const int uc = MODE == MODE_DGELU ? u : zcol_w1(u);
-            float z1v[2 * kEb], z3v[2 * kEb];
+          for (int g = 0; g < kEpg; ++g) {
+            const int r = r0 + 2 * g;
+            v0[g] = acc_read(acc[c][i][r]);
+            v1[g] = acc_read(acc[c][i][r + 1]);
+          }
 #pragma unroll
-            for (int g = 0; g < 2 * kEb; ++g) {
-              const int r = r0 + g;
-              const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-              const bool ok = row < rows && u < nval;
-              const int64_t zo = (int64_t)(ok ? row : 0) * zw + uc;
-              z1v[g] = ok ? bf16_lo(zb[zo]) : 0.f;
-              z3v[g] = (MODE == MODE_DSWIGLU && ok) ? bf16_lo(zb[zo + 32]) : 0.f;
+          for (int g = 0; g < kEpg; ++g) {
+            const int r = r0 + 2 * g;
+            const float got = swap_adjacent(odd ? v0[g] : v1[g]);
+            const float lo = odd ? got : v0[g];
+            const float hi = odd ? v1[g] : got;
+            const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
+            *(unsigned int*)(stg + rin * 128 + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // one segment at a time (not unrolled: the loads of all four would
+      // be hoisted together and crowd the live accumulators)
+#pragma unroll 1
+      for (int qq = 0; qq < 32 * 8 / 64; ++qq) {
+        const int sgi = lane + 64 * qq;
+        const int rin = sgi / 8, sg8 = sgi % 8;
+        const int row = 32 * i + rin, u0 = col0 + 8 * sg8;
+        if (row < rows && u0 < nval) {
+          float dh[8], z1[8], o1[8];
+          unpack8(*(const u32x4*)(stg + rin * 128 + sg8 * 16), dh);
+          const uint16_t* zr = zb + (int64_t)row * a.zw;
+          if (MODE == MODE_DGELU) {
+            unpack8(*(const u32x4*)(zr + u0), z1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o1[e] = dh[e] * dgelu_erf(z1[e]);
+            *(u32x4*)(out + ((int64_t)row * ldo + u0)) = pack8(o1);
+          } else {
+            float z3[8], o3[8];
+            const uint16_t* zp = zr + zcol_w1(u0);
+            unpack8(*(const u32x4*)zp, z1);
+            unpack8(*(const u32x4*)(zp + 32), z3);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float sg = __builtin_amdgcn_rcpf(
+                  1.0f + __builtin_amdgcn_exp2f(z1[e] * -1.44269504f));
+              o1[e] = dh[e] * z3[e] * sg * fmaf(z1[e], 1.0f - sg, 1.0f);
+              o3[e] = dh[e] * z1[e] * sg;
             }
-            float v0[kEb], v1[kEb];
-#pragma unroll
-            for (int g = 0; g < kEb; ++g) {
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const int r = r0 + 2 * g + h;
-                const float dh = acc_read(acc[c][i][r]);
-                const float z1 = z1v[2 * g + h], z3 = z3v[2 * g + h];
-                float val;
-                if (MODE == MODE_DGELU) {
-                  val = dh * dgelu_erf(z1);
-                } else {
-                  const float sg = __builtin_amdgcn_rcpf(
-                      1.0f + __builtin_amdgcn_exp2f(z1 * -1.44269504f));
-                  val = q == 0 ? dh * z3 * sg * fmaf(z1, 1.0f - sg, 1.0f) : dh * z1 * sg;
-                }
-                if (h == 0) v0[g] = val; else v1[g] = val;
-              }
-            }
-#pragma unroll
-            for (int g = 0; g < kEb; ++g) {
-              const int r = r0 + 2 * g;
-              const float got = swap_adjacent(odd ? v0[g] : v1[g]);
-              const float lo = odd ? got : v0[g];
-              const float hi = odd ? v1[g] : got;
-              const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
-              *(unsigned int*)(stg + rin * 128 + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            *(u32x4*)(out + ((int64_t)row * ldo + u0)) = pack8(o1);
+            *(u32x4*)(out + ((int64_t)row * ldo + nval + u0)) = pack8(o3);
           }
         }
-        // block i of output q: 32 rows x 64 columns, 16-byte segments
-#pragma unroll
-        for (int qq = 0; qq < 32 * 8 / 64; ++qq) {
-          const int sgi = lane + 64 * qq;
-          const int rin = sgi / 8, sg8 = sgi % 8;
-          const u32x4 v = *(const u32x4*)(stg + rin * 128 + sg8 * 16);
-          const int row = 32 * i + rin, col = col0 + 8 * sg8;
-          if (row < rows && col < nval)
-            *(u32x4*)(out + ((int64_t)row * a.ldo + q * nval + col)) = v;
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<0>();
   } else {

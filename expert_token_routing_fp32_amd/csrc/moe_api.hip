@@ -217,7 +217,7 @@ size_t carve_ffn_bwd(const moe_problem_t* p, void* ws, FfnBwdBufs* b) {
 }
 
 struct GateBwdBufs {
-  uint16_t *dl_s[2], *wg_s[2], *x8[3], *dl8[3];
+  uint16_t *dlt[2], *wgt[2], *x8[3], *dl8[3];
   float* part;
 };
 int pad32(int v) { return (v + 31) / 32 * 32; }
@@ -235,6 +235,9 @@ GateSplit gate_split(const moe_problem_t* p) {
   if (G > gmax) G = gmax;
   if (G < 1) G = 1;
   if (G > 64) G = 64;
+  // each group's slice of x in RB8 stays under 1 GB (32-bit offsets)
+  const int64_t gmin = (Br * (int64_t)(p->d + 8) * 2 + (1LL << 30) - 1) >> 30;
+  if (G < gmin) G = gmin;
   int64_t Ks = (Br + G - 1) / G;
   Ks = (Ks + 31) / 32 * 32;
   G = (Br + Ks - 1) / Ks;
@@ -252,8 +255,9 @@ size_t carve_gate_bwd(const moe_problem_t* p, void* ws, GateBwdBufs* b) {
   const size_t Br = (size_t)moek::rb8_rows(p->B);
   const int nx = p->x_dtype == MOE_BF16 ? 1 : 3;
   GateBwdBufs t{};
-  for (int i = 0; i < 2; ++i) t.dl_s[i] = c.take<uint16_t>(nullptr, B * Ep * 2);
-  for (int i = 0; i < 2; ++i) t.wg_s[i] = c.take<uint16_t>(nullptr, d * Ep * 2);
+  // dl and Wg in RB8 over the experts (the contraction of dx = dl Wg^T)
+  for (int i = 0; i < 2; ++i) t.dlt[i] = c.take<uint16_t>(nullptr, B * Ep * 2);
+  for (int i = 0; i < 2; ++i) t.wgt[i] = c.take<uint16_t>(nullptr, d * Ep * 2);
   for (int i = 0; i < nx; ++i) t.x8[i] = c.take<uint16_t>(nullptr, Br * (d + 8) * 2);
   for (int i = 0; i < 3; ++i) t.dl8[i] = c.take<uint16_t>(nullptr, Br * Ep * 2);
   const GateSplit gs = gate_split(p);
@@ -862,8 +866,8 @@ hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pa
     q.b_w = d;
     q.a_es = r8 * f;
     q.b_es = r8 * d;
-    q.a_rows = f;
-    q.b_rows = d;
+    q.a_bytes = 2 * r8 * f * nl;
+    q.b_bytes = 2 * r8 * d * nl;
     q.eo = eo;
     q.e_begin = p->e_begin;
     q.groups = nl;
@@ -886,8 +890,8 @@ hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pa
     q.b_w = zwd;
     q.a_es = r8 * d;
     q.b_es = r8 * zwd;
-    q.a_rows = d;
-    q.b_rows = zwd;
+    q.a_bytes = 2 * r8 * d * nl;
+    q.b_bytes = 2 * r8 * zwd * nl;
     q.eo = eo;
     q.e_begin = p->e_begin;
     q.groups = nl;
@@ -921,23 +925,25 @@ hipError_t gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
   const bool xb = p->x_dtype == MOE_BF16;
   const int d = p->d, E = p->E, Ep = pad32(E);
   const int64_t B = p->B;
-  hipError_t e = moek::launch_split_rows(dl, B, E, Ep, b.dl_s[0], b.dl_s[1], nullptr, s);
-  if (e == hipSuccess) e = moek::launch_split_rows(Wg, d, E, Ep, b.wg_s[0], b.wg_s[1], nullptr, s);
-  // dx = dl Wg^T + dx_acc over K = E: (hi, hi) + (hi, mid) + (mid, hi)
+  // dx = dl Wg^T + dx_acc, contracting over the experts: dl and Wg in RB8
+  // over e (parts hi, mid; three products (hi, hi) + (hi, mid) + (mid, hi))
+  hipError_t e = moek::launch_split_rb8(dl, E, (int)B, E, true, (int)B, -1, b.dlt[0], b.dlt[1],
+                                        nullptr, s);
+  if (e == hipSuccess)
+    e = moek::launch_split_rb8(Wg, E, d, E, true, d, -1, b.wgt[0], b.wgt[1], nullptr, s);
   if (e == hipSuccess) {
     moek::KGemm q{};
-    const uint16_t* As[3] = {b.dl_s[0], b.dl_s[0], b.dl_s[1]};
-    const uint16_t* Bs[3] = {b.wg_s[0], b.wg_s[1], b.wg_s[0]};
+    const uint16_t* As[3] = {b.dlt[0], b.dlt[0], b.dlt[1]};
+    const uint16_t* Bs[3] = {b.wgt[0], b.wgt[1], b.wgt[0]};
     for (int i = 0; i < 3; ++i) {
       q.A[i] = As[i];
       q.B[i] = Bs[i];
     }
     q.nseg = 3;
-    q.a_row = q.b_row = true;
-    q.a_ld = Ep;
-    q.b_ld = Ep;
-    q.a_rows = (int)(B < 2147483647 ? B : 2147483647);
-    q.b_rows = d;
+    q.a_w = (int)B;
+    q.b_w = d;
+    q.a_bytes = (int64_t)Ep * B * 2;
+    q.b_bytes = (int64_t)Ep * d * 2;
     q.K = Ep;
     q.groups = 1;
     q.M = (int)B;
@@ -958,11 +964,11 @@ hipError_t gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
       e = moek::launch_relayout_rb8(0, static_cast<const uint16_t*>(x), d, nullptr, 0, 0, 1, B,
                                     d + 8, d, d, b.x8[0], s);
     else
-      e = moek::launch_split_rb8(static_cast<const float*>(x), B, d, d + 8, d, b.x8[0], b.x8[1],
-                                 b.x8[2], s);
+      e = moek::launch_split_rb8(static_cast<const float*>(x), B, d, d, false, d + 8, d, b.x8[0],
+                                 b.x8[1], b.x8[2], s);
   }
   if (e == hipSuccess)
-    e = moek::launch_split_rb8(dl, B, E, Ep, -1, b.dl8[0], b.dl8[1], b.dl8[2], s);
+    e = moek::launch_split_rb8(dl, B, E, E, false, Ep, -1, b.dl8[0], b.dl8[1], b.dl8[2], s);
   if (e == hipSuccess) {
     moek::KGemm q{};
     if (xb) {
@@ -982,14 +988,15 @@ hipError_t gate_backward(const moe_problem_t* p, const void* x, const float* Wg,
     // split-K over the tokens: group g sums tokens g Ks .. (g + 1) Ks into
     // its own [d + 1][E] partial; the partials are then added in g order
     const GateSplit gs = gate_split(p);
+    const int64_t Br = moek::rb8_rows(B);
     q.a_w = d + 8;
     q.b_w = Ep;
     q.a_es = (int64_t)gs.Ks * (d + 8);
     q.b_es = (int64_t)gs.Ks * Ep;
-    q.a_rows = d + 8;
-    q.b_rows = E;
+    q.a_bytes = Br * (d + 8) * 2;
+    q.b_bytes = Br * Ep * 2;
     q.K = gs.Ks;
-    q.Ktot = (int)moek::rb8_rows(B);
+    q.Ktot = (int)Br;
     q.groups = gs.G;
     q.M = d + 1;
     q.N = E;

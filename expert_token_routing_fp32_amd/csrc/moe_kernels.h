@@ -268,24 +268,25 @@ hipError_t launch_sum_parts(const float* part, int G, int M0, int N, float* out0
                             hipStream_t s);
 hipError_t launch_split_rows(const float* src, int64_t rows, int cols, int Wp, uint16_t* o0,
                              uint16_t* o1, uint16_t* o2, hipStream_t s);
-hipError_t launch_split_rb8(const float* src, int64_t rows, int cols, int Wp, int one_col,
-                            uint16_t* o0, uint16_t* o1, uint16_t* o2, hipStream_t s);
+// RB8 of an fp32 matrix split into bf16 parts: element (r, c) = src[r ld + c]
+// (trans: src[c ld + r]) for r < rows, c < cols; rows padded to 32 with zeros
+hipError_t launch_split_rb8(const float* src, int64_t rows, int cols, int64_t ld, bool trans,
+                            int Wp, int one_col, uint16_t* o0, uint16_t* o1, uint16_t* o2,
+                            hipStream_t s);
 hipError_t launch_unpack_sum(const uint16_t* dxp, const int32_t* dest, const void* dy,
                              bool x_bf16, bool residual, int64_t B, int k, int d, int64_t kmax,
                              float* dx_acc, hipStream_t s);
 
 // Grouped K-fragment GEMM (wgrad.hip): C_g = sum over segments of A B^T with
-// K-fragment operands, RB8 (a_row false: a_w columns) or row-major (a_row
-// true: a_ld).  Groups: K from expert_offset (eo, e_begin) or K.
+// both operands in the RB8 layout (a_w / b_w columns).  Groups: K from
+// expert_offset (eo, e_begin) or K.
 struct KGemm {
   const uint16_t* A[6];
   const uint16_t* B[6];
   int nseg;
-  bool a_row, b_row;
-  int64_t a_ld, b_ld;
   int a_w, b_w;
-  int64_t a_es, b_es;  // per-group element offsets
-  int a_rows, b_rows;  // valid rows m of A and n of B (loads are clamped)
+  int64_t a_es, b_es;        // per-group element offsets
+  int64_t a_bytes, b_bytes;  // bytes of each segment's operand (reads past: zeros)
   const int32_t* eo;
   int e_begin;
   int K;

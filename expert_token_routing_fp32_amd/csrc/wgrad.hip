@@ -1,25 +1,29 @@
 // Grouped "K-fragment" GEMM on bf16 matrix cores for the backward pass:
 //   C_g[m][n] = sum_s sum_k A_s,g(m, k) B_s,g(n, k)        (fp32 accumulation)
-// over groups g (experts) and up to six operand pairs s (segments) that
-// share the contraction length K_g.  Used for the weight gradients of the
-// experts (the contraction runs over an expert's rows: dW2 = H^T dret,
-// [dW1 | dW3] = X^T [dZ1 | dZ3]) and for the router's gradients (dWg and the
-// bias gradient over the tokens, dx = dlogits Wg^T over the experts), the
-// fp32 router operands split exactly into bf16 parts.
+// over groups g (experts, or slices of a long contraction) and up to six
+// operand pairs s (segments) that share the contraction length K_g.  Used
+// for the weight gradients of the experts (the contraction runs over an
+// expert's rows: dW2 = H^T dret, [dW1 | dW3] = X^T [dZ1 | dZ3]) and for the
+// router's gradients (dWg and the bias gradient over the tokens, dx =
+// dlogits Wg^T over the experts), the fp32 router operands split exactly
+// into bf16 parts.
 //
-// Operands are read as 16-byte K fragments: fragment (kg, m) -- the 8
-// values k = 8 kg .. 8 kg + 7 of row m -- at element base + kg sg + m sm.
-// Two layouts give that:
-//   RB8  (sm = 8, sg = 8 W): 8 consecutive rows of one column contiguous
-//        (the re-layout kernels write it), for contractions over rows;
-//   ROW  (sm = ld, sg = 8): plain row-major with K contiguous.
-// K_g (rows of expert g, or a constant) is padded with zero fragments to a
-// multiple of 32 in the operands.
+// Operands are in the RB8 layout: fragment (kg, m) -- the 8 values
+// k = 8 kg .. 8 kg + 7 of row m -- is the 16 bytes at ((kg W + m) 8)
+// elements from the group's base, so one k group of 256 consecutive rows is
+// 4 KB of contiguous memory.  K_g is padded with zero fragments to a
+// multiple of 32.
 //
-// Tile 128 x 128 x 32 per workgroup of 4 wavefronts (2 x 2, each 64 x 64 =
-// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16); LDS double buffer, one
-// barrier per 32-deep stage; the next stage's global loads are in flight
-// while the current one is multiplied.
+// Tile 256 x 256 x 32 per workgroup of 4 wavefronts (2 x 2, each 128 x 128 =
+// 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in the AGPRs, one
+// wavefront per SIMD): each 16-byte fragment read from LDS feeds four MFMAs.
+// Operands go global -> LDS by buffer loads that write LDS directly into a
+// 4-slot ring, three stages ahead (wavefront w loads k group w of both
+// operands, 8 loads of 64 x 16 bytes per stage); loads past a group's data
+// read zeros.  Vector-memory loads complete in issue order, so waiting until
+// two stages' loads are outstanding means the oldest stage has landed; one
+// barrier per stage then makes every wavefront's part visible and frees the
+// slot the next issue overwrites.
 #include "moe_kernels.h"
 
 namespace moek {
@@ -27,26 +31,27 @@ namespace {
 
 typedef __bf16 kb16x8 __attribute__((ext_vector_type(8)));
 typedef float kf32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void k_lds_void_t;
 
-constexpr int KBM = 128, KBN = 128;
-// 16-byte chunks per LDS plane (one 8-deep k group): 128 + 4 pad, so that
-// the four planes start 16 banks apart (the row-major store pattern writes
-// four planes' chunks of one row together)
-constexpr int KPL = 132;
+constexpr int KBM = 256, KBN = 256;
+constexpr int KPL = 256;                   // 16-byte chunks per k group in LDS
+constexpr int KSLOT = 2 * 4 * KPL * 16;    // one stage: A then B, 32 KB
+constexpr int KR = 4;                      // ring slots
+constexpr int KLOADS = 8;                  // loads per wavefront per stage
 
 struct KArgsDev {
   const uint16_t* A[6];
   const uint16_t* Bm[6];
   int nseg;
-  int64_t a_sm, a_sg, a_es;
-  int64_t b_sm, b_sg, b_es;
-  int Ma, Nb;
-  const int32_t* eo;  // K_g = eo[e_begin + g + 1] - eo[e_begin + g] when set
+  int a_w, b_w;              // RB8 widths (columns) of A and B
+  int64_t a_es, b_es;        // per-group element offsets
+  int64_t a_bytes, b_bytes;  // bytes of each segment's operand from its base
+  const int32_t* eo;         // K_g = eo[e_begin + g + 1] - eo[e_begin + g] when set
   int e_begin;
-  int Kc;             // otherwise this K (split-K: group g takes rows g Kc ..
-  int Ktot;           // .. min((g + 1) Kc, Ktot) when Ktot > 0)
+  int Kc;                    // otherwise this K (split-K: group g takes rows g Kc ..
+  int Ktot;                  // .. min((g + 1) Kc, Ktot) when Ktot > 0)
   int tiles_m, tiles_n;
-  int mode;           // 0: fp32 store to C0 / C1; 1: (acc + add) stored as bf16 / fp32
+  int mode;                  // 0: fp32 store to C0 / C1; 1: (acc + add) stored as bf16 / fp32
   float* C0;
   int64_t ldc0, c0_es;
   int M0, N0;
@@ -59,15 +64,89 @@ struct KArgsDev {
   int x_bf16;
 };
 
-// one 16-byte fragment of operand p at (kg, m): clamped to a valid row m
-__device__ __forceinline__ u32x4 kfrag(const uint16_t* p, int64_t sm, int64_t sg, int kg, int m) {
-  return *(const u32x4*)(p + (int64_t)kg * sg + (int64_t)m * sm);
+template <int N>
+__device__ __forceinline__ void k_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <bool AROW, bool BROW>
-__global__ __launch_bounds__(256) void kgemm_kernel(KArgsDev a) {
-  __shared__ __attribute__((aligned(16))) u32x4 sa[2][4 * KPL];
-  __shared__ __attribute__((aligned(16))) u32x4 sb[2][4 * KPL];
+__device__ __forceinline__ void k_dma16(rsrc_t rs, uint32_t off, char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (k_lds_void_t*)lds, 16, off, 0, 0, 0);
+}
+
+// one accumulator element, read out of the accumulation registers where it
+// is used
+__device__ __forceinline__ float kacc(float x) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+  return v;
+}
+
+// one output element
+__device__ __forceinline__ void kstore(const KArgsDev& a, int g, int m, int n, float v) {
+  if (a.mode == 0) {
+    if (m < a.M0 && n < a.N0) {
+      a.C0[(int64_t)g * a.c0_es + (int64_t)m * a.ldc0 + n] = v;
+    } else if (a.C1) {
+      const int mm = m - a.r1, nn = n - a.col1;
+      if (mm >= 0 && mm < a.M1 && nn >= 0 && nn < a.N1)
+        a.C1[(int64_t)g * a.c1_es + (int64_t)mm * a.ldc1 + nn] = v;
+    }
+  } else if (m < a.M0 && n < a.N0) {
+    const float o = v + (a.add ? a.add[(int64_t)m * a.ld_add + n] : 0.f);
+    const int64_t off = (int64_t)m * a.ldc0 + n;
+    if (a.x_bf16)
+      static_cast<uint16_t*>(a.xo)[off] = (uint16_t)f32_to_bf16(o);
+    else
+      static_cast<float*>(a.xo)[off] = o;
+  }
+}
+
+// four consecutive output elements (n .. n + 3) of row m: one 16-byte fp32
+// store (8-byte bf16) when they all fall inside C0 (or the stored output)
+// and the destination is aligned, element by element otherwise
+__device__ __forceinline__ void kstore4(const KArgsDev& a, int g, int m, int n, f32x4 v) {
+  if (a.mode == 0) {
+    if (m < a.M0 && n + 3 < a.N0 && (a.ldc0 & 3) == 0) {
+      float* p = a.C0 + (int64_t)g * a.c0_es + (int64_t)m * a.ldc0 + n;
+      if ((reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+        *reinterpret_cast<f32x4*>(p) = v;
+        return;
+      }
+    }
+  } else if (m < a.M0 && n + 3 < a.N0 && (a.ldc0 & 3) == 0 && (a.ld_add & 3) == 0) {
+    const int64_t off = (int64_t)m * a.ldc0 + n;
+    const float* ap = a.add ? a.add + (int64_t)m * a.ld_add + n : nullptr;
+    if ((!ap || (reinterpret_cast<uintptr_t>(ap) & 15u) == 0)) {
+      f32x4 o = v;
+      if (ap) o += *reinterpret_cast<const f32x4*>(ap);
+      if (a.x_bf16) {
+        uint16_t* q = static_cast<uint16_t*>(a.xo) + off;
+        if ((reinterpret_cast<uintptr_t>(q) & 7u) == 0) {
+          *reinterpret_cast<u32x2*>(q) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          return;
+        }
+      } else {
+        float* q = static_cast<float*>(a.xo) + off;
+        if ((reinterpret_cast<uintptr_t>(q) & 15u) == 0) {
+          *reinterpret_cast<f32x4*>(q) = o;
+          return;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kstore(a, g, m, n + u, v[u]);
+}
+
+// bytes of an operand readable from group g's base (0 past the end)
+__device__ __forceinline__ uint32_t kbytes(int64_t total, int64_t es, int g) {
+  const int64_t left = total - 2 * es * g;
+  return left > 0 ? (uint32_t)(left < 0x7fffffffLL ? left : 0x7fffffffLL) : 0u;
+}
+
+__global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
+  __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT];
   const int g = blockIdx.y;
   const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
   const int m0 = tm * KBM, n0 = tn * KBN;
@@ -85,112 +164,106 @@ __global__ __launch_bounds__(256) void kgemm_kernel(KArgsDev a) {
   }
   const int nks = K / 32;  // stages per segment
   const int nst = nks * a.nseg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lo16 = 16u * lane;
 
-  // global -> register mapping of one stage: 512 chunks per operand, two per
-  // thread.  RB8: chunk q -> (kg = q / 128, m = q % 128), consecutive
-  // threads read consecutive 16-byte chunks of one k group.  ROW: chunk q ->
-  // (m = q / 4, kg = q % 4), 64 contiguous bytes of a row per 4 threads.
-  int am[2], ak[2], bm_[2], bk[2];
+  // Stage st (clamped to the last one: the issues past the end reload it
+  // into a slot nobody reads again, so every step issues the same loads):
+  // wavefront `wave` loads k group `wave` of the stage, rows m0 .. m0 + 255
+  // of A and n0 .. n0 + 255 of B, as 4 + 4 loads of 64 chunks.
+  auto issue = [&](int st, int slot) {
+    const int sc = st < nst ? st : nst - 1;
+    const int sgm = sc / nks, kg = (sc - sgm * nks) * 4 + wave;
+    const rsrc_t ra = make_rsrc(a.A[sgm] + (int64_t)g * a.a_es, kbytes(a.a_bytes, a.a_es, g));
+    const rsrc_t rb = make_rsrc(a.Bm[sgm] + (int64_t)g * a.b_es, kbytes(a.b_bytes, a.b_es, g));
+    char* la = smem + slot * KSLOT + wave * KPL * 16;
+    char* lb = la + 4 * KPL * 16;
+    const uint32_t oa = 16u * ((uint32_t)kg * (uint32_t)a.a_w + (uint32_t)m0);
+    const uint32_t ob = 16u * ((uint32_t)kg * (uint32_t)a.b_w + (uint32_t)n0);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int q = tid + 256 * h;
-    am[h] = AROW ? q >> 2 : q & 127;
-    ak[h] = AROW ? q & 3 : q >> 7;
-    bm_[h] = BROW ? q >> 2 : q & 127;
-    bk[h] = BROW ? q & 3 : q >> 7;
-  }
-  int amc[2], bmc[2];
+    for (int p = 0; p < 4; ++p) k_dma16(ra, oa + 1024u * p + lo16, la + 1024 * p);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int ma = m0 + am[h], nb = n0 + bm_[h];
-    amc[h] = ma < a.Ma ? ma : a.Ma - 1;
-    bmc[h] = nb < a.Nb ? nb : a.Nb - 1;
-  }
-  u32x4 ra[2], rb[2];
-  auto gload = [&](int st) {
-    const int sgm = st / nks, kg0 = (st - sgm * nks) * 4;
-    const uint16_t* A = a.A[sgm] + (int64_t)g * a.a_es;
-    const uint16_t* Bp = a.Bm[sgm] + (int64_t)g * a.b_es;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[h] = kfrag(A, a.a_sm, a.a_sg, kg0 + ak[h], amc[h]);
-      rb[h] = kfrag(Bp, a.b_sm, a.b_sg, kg0 + bk[h], bmc[h]);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sa[buf][ak[h] * KPL + am[h]] = ra[h];
-      sb[buf][bk[h] * KPL + bm_[h]] = rb[h];
-    }
+    for (int p = 0; p < 4; ++p) k_dma16(rb, ob + 1024u * p + lo16, lb + 1024 * p);
   };
 
-  kf32x16 acc[2][2];
+  kf32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (nst > 0) {
-    gload(0);
-    swrite(0);
-    __syncthreads();
-  }
   const int l32 = lane & 31, lh = lane >> 5;
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
+  if (nst > 0) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int kgl = 2 * s2 + lh;  // this lane's k group in the stage
-      kb16x8 fa[2], fb[2];
+    for (int p = 0; p < KR - 1; ++p) issue(p, p);
+    for (int st = 0; st < nst; ++st) {
+      // stage st has landed (this wavefront's loads) once at most two
+      // stages' loads are outstanding; the barrier makes every wavefront's
+      // part visible and retires the reads of slot (st - 1) % KR
+      k_wait_vmcnt<(KR - 2) * KLOADS>();
+      // compiler barriers: no LDS read of this stage moves above the
+      // hardware barrier, no read of the last stage below it
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(st + KR - 1, (st + KR - 1) % KR);
+      const u32x4* sa = reinterpret_cast<const u32x4*>(smem + (st % KR) * KSLOT);
+      const u32x4* sb = sa + 4 * KPL;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = __builtin_bit_cast(kb16x8, sa[buf][kgl * KPL + wm * 64 + i * 32 + l32]);
-        fb[i] = __builtin_bit_cast(kb16x8, sb[buf][kgl * KPL + wn * 64 + i * 32 + l32]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kgl = 2 * s2 + lh;  // this lane's k group in the stage
+        kb16x8 fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = __builtin_bit_cast(kb16x8, sa[kgl * KPL + wm * 128 + i * 32 + l32]);
+          fb[i] = __builtin_bit_cast(kb16x8, sb[kgl * KPL + wn * 128 + i * 32 + l32]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (st + 1 < nst) swrite(buf ^ 1);
+    // the reloads past the end still write the ring
+    k_wait_vmcnt<0>();
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][r] is C[m][n] with m = m0 + 64 wm + 32 i + 8 (r / 4)
-  // + 4 lh + r % 4 and n = n0 + 64 wn + 32 j + l32
+  // epilogue: acc[i][j][r] is C[m][n] with m = m0 + 128 wm + 32 i + 8 (r / 4)
+  // + 4 lh + r % 4 and n = n0 + 128 wn + 32 j + l32.  Each 32 x 32 block goes
+  // through a wavefront-private 4 KB of LDS (the ring is free now): the
+  // unrolled part only moves registers to LDS, and the stores, with their
+  // bounds and destinations, run in a plain loop of 16 rounds in which lanes
+  // write consecutive columns.
+  float* stg = reinterpret_cast<float*>(smem) + wave * 1024;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int n = n0 + 64 * wn + 32 * j + l32;
-        const float v = acc[i][j][r];
-        if (a.mode == 0) {
-          if (m < a.M0 && n < a.N0) {
-            a.C0[(int64_t)g * a.c0_es + (int64_t)m * a.ldc0 + n] = v;
-          } else if (a.C1) {
-            const int mm = m - a.r1, nn = n - a.col1;
-            if (mm >= 0 && mm < a.M1 && nn >= 0 && nn < a.N1)
-              a.C1[(int64_t)g * a.c1_es + (int64_t)mm * a.ldc1 + nn] = v;
-          }
-        } else if (m < a.M0 && n < a.N0) {
-          const float o = v + (a.add ? a.add[(int64_t)m * a.ld_add + n] : 0.f);
-          const int64_t off = (int64_t)m * a.ldc0 + n;
-          if (a.x_bf16)
-            static_cast<uint16_t*>(a.xo)[off] = (uint16_t)f32_to_bf16(o);
-          else
-            static_cast<float*>(a.xo)[off] = o;
-        }
+      for (int r = 0; r < 16; ++r)
+        stg[(8 * (r >> 2) + 4 * lh + (r & 3)) * 32 + l32] = kacc(acc[i][j][r]);
+      // LDS operations of one wavefront complete in order; the barriers keep
+      // the compiler from moving the reads above the writes (or the next
+      // block's writes above these reads)
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const int mb = m0 + 128 * wm + 32 * i, nb = n0 + 128 * wn + 32 * j;
+      // four rounds: lane -> row 8 q + lane / 8, columns 4 (lane % 8) .. + 3
+#pragma unroll 1
+      for (int q = 0; q < 4; ++q) {
+        const int row = 8 * q + (lane >> 3), c4 = 4 * (lane & 7);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * 32 + c4);
+        kstore4(a, g, mb + row, nb + c4, v);
       }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
 }
 
 }  // namespace
@@ -204,14 +277,12 @@ hipError_t launch_kgemm(const KGemm& q, hipStream_t s) {
     a.Bm[i] = q.B[i];
   }
   a.nseg = q.nseg;
-  a.a_sm = q.a_row ? q.a_ld : 8;
-  a.a_sg = q.a_row ? 8 : (int64_t)8 * q.a_w;
+  a.a_w = q.a_w;
+  a.b_w = q.b_w;
   a.a_es = q.a_es;
-  a.b_sm = q.b_row ? q.b_ld : 8;
-  a.b_sg = q.b_row ? 8 : (int64_t)8 * q.b_w;
   a.b_es = q.b_es;
-  a.Ma = q.a_rows;
-  a.Nb = q.b_rows;
+  a.a_bytes = q.a_bytes;
+  a.b_bytes = q.b_bytes;
   a.eo = q.eo;
   a.e_begin = q.e_begin;
   a.Kc = (q.K + 31) / 32 * 32;
@@ -235,17 +306,20 @@ hipError_t launch_kgemm(const KGemm& q, hipStream_t s) {
   a.ld_add = q.ld_add;
   a.xo = q.xo;
   a.x_bf16 = q.x_bf16;
+  // every byte offset inside one group's operand is 32-bit: the groups'
+  // extents (or the whole operand for one group) stay below 2 GB, and so
+  // do the offsets the tiles reach (k groups x width x 16 bytes)
+  const int64_t ga = q.a_es > 0 ? 2 * q.a_es : q.a_bytes;
+  const int64_t gb = q.b_es > 0 ? 2 * q.b_es : q.b_bytes;
+  if (ga > 0x7fffffffLL || gb > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int64_t kmax = q.eo ? 0 : a.Kc;
+  if (kmax > 0 && ((int64_t)kmax / 8 * q.a_w * 16 > 0x7fffffffLL ||
+                   (int64_t)kmax / 8 * q.b_w * 16 > 0x7fffffffLL))
+    return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > 2147483647 || q.groups > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles, (unsigned)q.groups);
-  if (q.a_row && q.b_row)
-    hipLaunchKernelGGL((kgemm_kernel<true, true>), grid, dim3(256), 0, s, a);
-  else if (q.a_row)
-    hipLaunchKernelGGL((kgemm_kernel<true, false>), grid, dim3(256), 0, s, a);
-  else if (q.b_row)
-    hipLaunchKernelGGL((kgemm_kernel<false, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((kgemm_kernel<false, false>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kgemm_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
