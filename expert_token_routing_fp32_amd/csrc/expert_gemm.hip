@@ -182,11 +182,14 @@ __device__ __forceinline__ int swz(int r, int ch) {
   return r * kRowBytes + ((ch ^ swz_key(r)) << 4);
 }
 
-// Activation ring for a tile of NS row blocks: kP slots, each the tile's
-// 64-wide K slice of its 32 NS rows (one 32-row DMA round per block).
+// Activation ring for a tile of NS row blocks: kP slots of the size of an
+// 8-block tile's 64-wide K slice, holding the tile's 32 NS rows (one 32-row
+// DMA round per block).  The slots sit at the same offsets whatever NS is,
+// so a run's prologue, which writes slots 0 .. kP - 2, never touches the
+// last slot of the run before (that one may still be read).
 template <int NS>
 struct Ring {
-  static constexpr int A_BYTES = NS * 32 * kRowBytes;
+  static constexpr int A_BYTES = 8 * 32 * kRowBytes;
   static constexpr int LOADS = NS + 8;  // vector-memory loads per thread per stage
 };
 static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
@@ -459,7 +462,6 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vmcnt<0>();
   } else {
         // Epilogue of tile `tile`.  acc[c][i][r] is row 8 (r / 4) +
         // 4 lg + r % 4 of row block i, column l32 of the wavefront's weight
@@ -546,14 +548,16 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-    // the counter now also holds stores, which are not ordered with the
-    // loads: wait for everything before the next tile's first stage
-    wait_vmcnt<0>();
   }
   }
 #undef ISSUE
-  wait_vmcnt<0>();
-  __syncthreads();
+  // No wait for the epilogue's stores, and no barrier: the stores drain
+  // while the next run's loads are issued.  The stage waits stay correct
+  // with stores in the counter -- at most N operations outstanding means at
+  // most N loads outstanding, and loads complete in issue order -- and the
+  // next run's prologue writes only ring slots 0 .. kP - 2, which every
+  // wavefront finished reading before the barrier of this run's last stage
+  // (its epilogue staging area is its own).
 }
 
 // Persistent over an equal share of the active tiles.  Expert el has
@@ -627,18 +631,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int loc0 = eos[0];
   if (XS) {
     // Matrix-core-bound launches (hundreds of rows per expert): tiles are
-    // ordered (expert, output tile, row slice) and cut into chunks of nx
-    // consecutive tiles, one per workgroup of an XCD (the workgroups b with
-    // b % 8 == x sit on XCD x: workgroups are dealt round-robin over the 8
-    // XCDs); chunk c goes to XCD c % 8.  At any moment an XCD then works on
-    // a compact patch of one expert -- few row slices x few output tiles --
-    // so the activation slices and weight tiles it streams are shared
-    // through its L2, and every XCD gets a share of every expert (experts
-    // differ in rows, so whole experts per XCD would not balance).
+    // ordered (expert, output tile, row slice) and cut into 8 equal
+    // contiguous ranges, one per XCD (the workgroups b with b % 8 == x sit
+    // on XCD x: workgroups are dealt round-robin over the 8 XCDs); the nx
+    // workgroups of an XCD take its tiles in turn, nx consecutive tiles at a
+    // time.  At any moment an XCD then works on a compact patch of one
+    // expert -- few row slices x few output tiles -- so the activation
+    // slices and weight tiles it streams are shared through its L2, an
+    // expert's weights are read by one or two XCDs only, and every XCD gets
+    // the same number of tiles (experts differ in rows, so whole experts
+    // per XCD would not balance, and dealing chunks of nx tiles round-robin
+    // leaves the XCDs a chunk apart when the chunk count is not a multiple
+    // of 8).
     const int x = b % kXcd, j = b / kXcd;
-    const int nx = G / kXcd;  // workgroups per XCD in the full rounds (G >= 8)
-    if (j >= nx) return;      // the G % 8 extra workgroups have no chunk slot
-    for (int64_t t = (int64_t)x * nx + j; t < total; t += (int64_t)kXcd * nx) {
+    const int nx = G / kXcd;  // workgroups per XCD (G >= 8)
+    if (j >= nx) return;      // the G % 8 extra workgroups take no tiles
+    const int64_t xe = total * (x + 1) / kXcd;
+    for (int64_t t = total * x / kXcd + j; t < xe; t += nx) {
       const int p = (int)(t / a.n_tiles_n);
       int lo = 0, hi = nl - 1;
       while (lo < hi) {
