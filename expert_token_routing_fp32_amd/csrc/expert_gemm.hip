@@ -159,11 +159,6 @@ __device__ __forceinline__ float acc_read(float a) {
   return v;
 }
 
-// value of lane l ^ 1 (DPP quad permutation [1, 0, 3, 2])
-__device__ __forceinline__ float swap_adjacent(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-
 // wait until at most N vector-memory operations of this wavefront are in flight
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -195,13 +190,12 @@ struct Ring {
 static_assert(kP * Ring<8>::A_BYTES <= kLdsBytes, "activation ring exceeds LDS");
 // LDS past the ring: the tile scheduler's scan arrays (4 (1029 + 1025) bytes),
 // then the epilogue's staging area, 32 rows x 64 bf16 columns per wavefront
-// row pairs whose epilogue work is interleaved (1, 2, 4 or 8)
-#ifndef MOE_EPG
-#define MOE_EPG 4
-#endif
-constexpr int kEpg = MOE_EPG;
 constexpr int kStageOff = kP * Ring<8>::A_BYTES + 8448;
-static_assert(kStageOff + (kThreads / 64) * 32 * 128 <= kLdsBytes, "staging area exceeds LDS");
+// staged row of 64 bf16 columns, padded by 16 bytes: the 8-byte writes of
+// the 32 rows of a block then spread over the banks, and rows stay 16-byte
+// aligned for the read-back
+constexpr int kStgRow = 64 * 2 + 16;
+static_assert(kStageOff + (kThreads / 64) * 32 * kStgRow <= kLdsBytes, "staging area exceeds LDS");
 static_assert((kP - 2) * Ring<8>::LOADS < 64, "vmcnt range");
 
 // Weight fragment load.  Streaming launches (each weight byte used by one
@@ -217,7 +211,11 @@ __device__ __forceinline__ u32x4 load_w(const char* p) {
 // A run of `ntile` consecutive output tiles (n0 .. n0+ntile-1) of one expert
 // and one row slice of `rows` <= 32 NS rows.  Wavefront w (one per SIMD)
 // owns the 64 weight rows 64w .. 64w+63 of each tile -- two 32-column MFMA
-// blocks -- and all NS row blocks: 2 NS accumulators of 16 registers.
+// blocks -- and all NS row blocks: 2 NS accumulators of 16 registers.  The
+// weight fragment is the matrix instruction's first operand, so an
+// accumulator holds the transposed block: register r of lane l is row l % 32
+// of the block, column 8 (r / 4) + 4 (l / 32) + r % 4 -- four consecutive
+// columns of one row in registers 4q .. 4q + 3.
 //
 // The run is one pipeline over ntile * nk stages of 64 K; nk is a multiple
 // of kP, so tile ends fall on the last step of the unrolled group and the
@@ -363,8 +361,8 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           const bf16x8 af = as_bf16x8(fa[i]);
-          acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc[0][i], 0, 0, 0);
-          acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc[1][i], 0, 0, 0);
+          acc[0][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, af, acc[0][i], 0, 0, 0);
+          acc[1][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, af, acc[1][i], 0, 0, 0);
           if (s_ < 3) fa[i] = *(const u32x4*)(sa + swz(32 * i + l32, chn));
           else if (PRE) fa[i] = *(const u32x4*)(sn + swz(32 * i + l32, lg));
 #pragma unroll
@@ -388,44 +386,32 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   }
   if constexpr (MODE == MODE_DGELU || MODE == MODE_DSWIGLU) {
     // Backward epilogue of tile `tile`: the products are dH for hidden units
-    // u = 256 tile + 64 wave + 32 c + l32.  They are staged through LDS as
-    // bf16 exactly like the plain epilogue's outputs (32 rows x 64 units per
-    // wavefront); then each lane takes 16-byte row segments (8 units of one
+    // 256 tile + 64 wave + 32 c + (column in the block).  They are staged
+    // through LDS as bf16 exactly like the plain epilogue's outputs (32 rows
+    // x 64 units per wavefront); then each lane takes 16-byte row segments (8 units of one
     // row), loads the matching pre-activations Z as 16-byte vectors and
     // writes dZ = dH * gelu'(Z), or dZ1 = dH Z3 silu'(Z1) and dZ3 = dH
     // silu(Z1) at columns u and f + u, as 16-byte stores.
-    const bool odd = lane & 1;
     int ldo = a.ldo;
     asm volatile("" : "+s"(ldo));
     uint16_t* out = a.Out + o_row0 * ldo;
     const uint16_t* zb = a.Z + o_row0 * a.zw;
     const int nval = a.Nout;
-    char* stg = smem + kStageOff + wave * 32 * 128;
+    char* stg = smem + kStageOff + wave * 32 * kStgRow;
     const int col0 = tile * 256 + 64 * wave;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += 2 * kEpg) {
-          float v0[kEpg], v1[kEpg];
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
 #pragma unroll
-          for (int g = 0; g < kEpg; ++g) {
-            const int r = r0 + 2 * g;
-            v0[g] = acc_read(acc[c][i][r]);
-            v1[g] = acc_read(acc[c][i][r + 1]);
-          }
-#pragma unroll
-          for (int g = 0; g < kEpg; ++g) {
-            const int r = r0 + 2 * g;
-            const float got = swap_adjacent(odd ? v0[g] : v1[g]);
-            const float lo = odd ? got : v0[g];
-            const float hi = odd ? v1[g] : got;
-            const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
-            *(unsigned int*)(stg + rin * 128 + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < 4; ++j) v[j] = acc_read(acc[c][i][4 * q + j]);
+          *(uint2*)(stg + l32 * kStgRow + (32 * c + 8 * q + 4 * lg) * 2) =
+              uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // one segment at a time (not unrolled: the loads of all four would
       // be hoisted together and crowd the live accumulators)
@@ -436,7 +422,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
         const int row = 32 * i + rin, u0 = col0 + 8 * sg8;
         if (row < rows && u0 < nval) {
           float dh[8], z1[8], o1[8];
-          unpack8(*(const u32x4*)(stg + rin * 128 + sg8 * 16), dh);
+          unpack8(*(const u32x4*)(stg + rin * kStgRow + sg8 * 16), dh);
           const uint16_t* zr = zb + (int64_t)row * a.zw;
           if (MODE == MODE_DGELU) {
             unpack8(*(const u32x4*)(zr + u0), z1);
@@ -463,18 +449,16 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-        // Epilogue of tile `tile`.  acc[c][i][r] is row 8 (r / 4) +
-        // 4 lg + r % 4 of row block i, column l32 of the wavefront's weight
-        // block c.  Rows r and r + 1 (r even) are adjacent: lanes 2j and
-        // 2j + 1 swap one value so that the even lane holds columns
-        // (2j, 2j+1) of row r and the odd lane the same columns of row r + 1.
-        // Each 32-row block is staged through LDS (4 KB per wavefront, in a
-        // part of LDS the ring does not use now) and leaves as 16-byte row
-        // segments, so every store writes whole 128-byte lines.  The staging
-        // area is private to the wavefront and lies past the ring, so no
-        // barrier guards it.
+        // Epilogue of tile `tile`.  Registers 4q .. 4q + 3 of acc[c][i] are
+        // columns 32 c + 8 q + 4 lg .. + 3 of row l32 of row block i (of the
+        // wavefront's weight block c); the activation is applied, the four
+        // values are converted to bf16 and written to LDS as one 8-byte
+        // piece.  Each 32-row block is staged that way (in a part of LDS the
+        // ring does not use now) and leaves as 16-byte row segments, so
+        // every store writes whole 128-byte lines.  The staging area is
+        // private to the wavefront and lies past the ring, so no barrier
+        // guards it.
         const int nt = tile;
-        const bool odd = lane & 1;
         // Opaque copy of the row length: without it the compiler hoists every
         // row address of the epilogue out of the tile loop and spills them.
         int nout = a.Nout;
@@ -482,46 +466,36 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
         uint16_t* out = a.Out + o_row0 * nout;
         // output columns of this wavefront: 64 (SwiGLU: 32 hidden units)
         constexpr int WCOLS = MODE == MODE_SWIGLU ? 32 : 64;
-        constexpr int RB = WCOLS * 2;  // bytes per staged row
-        char* stg = smem + kStageOff + wave * 32 * RB;
+        char* stg = smem + kStageOff + wave * 32 * kStgRow;
         const int col0 = MODE == MODE_SWIGLU ? nt * 128 + 32 * wave : nt * 256 + 64 * wave;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
 #pragma unroll
           for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
             // SwiGLU: block 0 holds the W1 products and block 1 the W3
-            // products of hidden units 32 wave + l32, in the same lanes
-            // kEpg row pairs at a time: their dependency chains (read-out,
-            // activation with exp2 and reciprocal, conversion, lane swap)
-            // interleave, while the temporaries stay few enough not to
-            // crowd the live accumulators and prefetched weights
+            // products of the same hidden units, in the same lanes and
+            // registers.  Two 4-column pieces at a time: their dependency
+            // chains (read-out, activation with exp2 and reciprocal,
+            // conversion) interleave while the temporaries stay few.
 #pragma unroll
-            for (int r0 = 0; r0 < 16; r0 += 2 * kEpg) {
-              float v0[kEpg], v1[kEpg];
+            for (int q0 = 0; q0 < 4; q0 += 2) {
+              float v[2][4];
 #pragma unroll
-              for (int g = 0; g < kEpg; ++g) {
-                const int r = r0 + 2 * g;
-                if (MODE == MODE_SWIGLU) {
-                  v0[g] = silu_f(acc_read(acc[0][i][r])) * acc_read(acc[1][i][r]);
-                  v1[g] = silu_f(acc_read(acc[0][i][r + 1])) * acc_read(acc[1][i][r + 1]);
-                } else {
-                  v0[g] = acc_read(acc[c][i][r]);
-                  v1[g] = acc_read(acc[c][i][r + 1]);
-                  if (MODE == MODE_GELU) {
-                    v0[g] = gelu_erf(v0[g]);
-                    v1[g] = gelu_erf(v1[g]);
+              for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const int r = 4 * (q0 + g) + j;
+                  if (MODE == MODE_SWIGLU) {
+                    v[g][j] = silu_f(acc_read(acc[0][i][r])) * acc_read(acc[1][i][r]);
+                  } else {
+                    v[g][j] = acc_read(acc[c][i][r]);
+                    if (MODE == MODE_GELU) v[g][j] = gelu_erf(v[g][j]);
                   }
                 }
-              }
 #pragma unroll
-              for (int g = 0; g < kEpg; ++g) {
-                const int r = r0 + 2 * g;
-                const float got = swap_adjacent(odd ? v0[g] : v1[g]);
-                const float lo = odd ? got : v0[g];  // column (l32 & ~1)
-                const float hi = odd ? v1[g] : got;  // the next column
-                const int rin = 8 * (r >> 2) + 4 * lg + (r & 3) + (odd ? 1 : 0);
-                *(unsigned int*)(stg + rin * RB + (32 * c + (l32 & ~1)) * 2) = pack_bf16x2(lo, hi);
-              }
+              for (int g = 0; g < 2; ++g)
+                *(uint2*)(stg + l32 * kStgRow + (32 * c + 8 * (q0 + g) + 4 * lg) * 2) =
+                    uint2{pack_bf16x2(v[g][0], v[g][1]), pack_bf16x2(v[g][2], v[g][3])};
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -531,7 +505,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
           for (int q = 0; q < 32 * SPR / 64; ++q) {
             const int sgi = lane + 64 * q;
             const int rin = sgi / SPR, sg = sgi % SPR;
-            const u32x4 v = *(const u32x4*)(stg + rin * RB + sg * 16);
+            const u32x4 v = *(const u32x4*)(stg + rin * kStgRow + sg * 16);
             const int row = 32 * i + rin, col = col0 + 8 * sg;
             // The hidden activations H (GELU / SwiGLU launch) are read back
             // only by the second GEMM, after the whole launch: stored

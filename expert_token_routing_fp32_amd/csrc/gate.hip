@@ -336,13 +336,24 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
           } else {
             split3(wv[u][j], hi, mid, lo);
           }
+          // the three products of a row block accumulate into one register
+          // set, so the parts go round the row blocks (lo of every block,
+          // then mid, then hi): consecutive matrix instructions are
+          // independent whenever MI > 1, and each accumulator still adds
+          // lo, mid, hi in that order
+          g_bf16x8 a[MI];
 #pragma unroll
-          for (int i = 0; i < MI; ++i) {
-            const g_bf16x8 a = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, lo), acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, mid), acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(g_bf16x8, hi), acc[i], 0, 0, 0);
-          }
+          for (int i = 0; i < MI; ++i)
+            a[i] = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, lo), acc[i], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, mid), acc[i], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, hi), acc[i], 0, 0, 0);
         }
       }
     }
