@@ -146,8 +146,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // global_load_lds against the LDS-read counter as well, and then has to wait
 // for every outstanding LDS read (lgkmcnt(0)) before each MFMA step instead
 // of only the ones that step consumes.
-__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t off, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, off, 0, 0, 0);
+// The LDS address is a 32-bit offset: converting a generic pointer instead
+// costs a null check (three scalar instructions) per load.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t off, uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(uintptr_t)lds, 16, off, 0, 0, 0);
+}
+// 32-bit LDS offset of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_off(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 // One accumulator element, read out of the accumulation registers where it
@@ -281,13 +287,13 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   // this wavefront's rows of ring slot 0; made opaque once per stage below,
   // so that the per-slot, per-round LDS addresses are recomputed where they
   // are used instead of all being hoisted into scalar registers
-  char* lds_w = smem + 8 * wave * kRowBytes;
+  uint32_t lds_w = lds_off(smem) + 8 * wave * kRowBytes;
   const char* iss_w = wbase;
   // K chunks past K (and whole padding stages) have zero weights, so the
   // activation side may load anything finite there: clamp into the row.
 #define ISSUE(SLOT)                                                                \
   {                                                                                \
-    char* st_ = lds_w + (SLOT) * R::A_BYTES;                                       \
+    const uint32_t st_ = lds_w + (SLOT) * R::A_BYTES;                              \
     const int kc_ = iss_k * BK + dcol;                                             \
     const uint32_t cb_ = 2u * (uint32_t)(kc_ < K ? kc_ : K - 8);                   \
     _Pragma("unroll") for (int i_ = 0; i_ < NS; ++i_)                              \
@@ -339,7 +345,7 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
       // whose issue stalls (memory queues full) stalls the matrix core too;
       // spread out, the stalls fall in the gaps between MFMAs.
       constexpr int NL = NS + 8;
-      char* ist_ = lds_w + ((u + kP - 1) % kP) * R::A_BYTES;
+      const uint32_t ist_ = lds_w + ((u + kP - 1) % kP) * R::A_BYTES;
       const int ikc_ = iss_k * BK + dcol;
       const uint32_t icb_ = 2u * (uint32_t)(ikc_ < K ? ikc_ : K - 8);
       const char* iwb_ = iss_w + wlane;

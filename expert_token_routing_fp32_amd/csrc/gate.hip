@@ -218,8 +218,10 @@ __device__ __forceinline__ void g_wait_vmcnt() {
 // into LDS at lds + 16 * lane (buffer_load_dwordx4 ... lds).  The descriptor
 // is built here, not in the kernel body: a kernel with a local of the
 // descriptor type gets no host-side launch stub.
-__device__ __forceinline__ void g_dma16(const void* base, uint32_t bytes, uint32_t off, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (g_lds_void_t*)lds, 16, off, 0, 0, 0);
+// lds: a 32-bit LDS offset (a generic pointer would cost a null check per load)
+__device__ __forceinline__ void g_dma16(const void* base, uint32_t bytes, uint32_t off, uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (g_lds_void_t*)(uintptr_t)lds, 16, off,
+                                           0, 0, 0);
 }
 __device__ __forceinline__ int g_swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
@@ -228,6 +230,7 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wg, const u32x4* __restrict__ Wsp,
     const float* __restrict__ bias, float* __restrict__ logits, int64_t B, int d, int E) {
   extern __shared__ __attribute__((aligned(16))) char gsm[];
+  const uint32_t gsm_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)gsm;
   constexpr int SLOT = 32 * MI * 128;  // one stage (64 k) of the block's rows
   constexpr int NSL = 3;
   constexpr int ND = 4 * MI / EB;      // DMA instructions per wave per stage
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
       }                                                                              \
     }                                                                                \
     const int kx_ = kb + 64 * sc_;                                                   \
-    char* sl_ = gsm + ((S) % NSL) * KS * SLOT;                                       \
+    const uint32_t sl_ = gsm_lds + ((S) % NSL) * KS * SLOT;                          \
     _Pragma("unroll") for (int q_ = 0; q_ < ND; ++q_) {                              \
       const int kk_ = kx_ + dcol[q_];                                                \
       g_dma16(xblk, xbytes, xrow[q_] + 2u * (kk_ < d ? kk_ : d - 8), sl_ + dofs[q_]); \

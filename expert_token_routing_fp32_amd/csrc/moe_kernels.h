@@ -69,9 +69,87 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // of arg-max by (logit descending, index ascending); lane li == 0 writes
 // idx_t[j] and the raw probability w_t[j].  Lanes past E hold nothing, so
 // the butterfly trees combine the same values in the same order for any L.
+// Value of lane (li - N) mod 16 of this lane's row of 16 lanes (DPP row
+// rotation: a VALU operand modifier, no LDS round trip).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ int row_ror(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x120 + N, 0xF, 0xF, false);
+}
+
+// L = 16: a token's lanes are one DPP row, so the reductions rotate within
+// the row.  After rotations by 8, 4, 2, 1 every lane holds the same sum, and
+// the same one as the xor butterfly gives: at each level the partial sums
+// repeat with the period the xor partner and the rotation partner share.
+// Each arg-max round is a max over the row, then the least index among the
+// lanes holding it (a min over the row).
+template <int V>
+__device__ __forceinline__ void route_token16(const float* row, int E, int k, float inv_tau,
+                                              int li, bool tok, int32_t* idx_t, float* w_t) {
+  float v[V];
+  bool ok[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int e = li + u * 16;
+    ok[u] = tok && e < E;
+    v[u] = ok[u] ? row[e] : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < V; ++u) m = fmaxf(m, v[u]);
+  m = fmaxf(m, row_ror<8>(m));
+  m = fmaxf(m, row_ror<4>(m));
+  m = fmaxf(m, row_ror<2>(m));
+  m = fmaxf(m, row_ror<1>(m));
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (ok[u]) s += expf((v[u] - m) * inv_tau);
+  s += row_ror<8>(s);
+  s += row_ror<4>(s);
+  s += row_ror<2>(s);
+  s += row_ror<1>(s);
+  unsigned taken = 0u;
+  for (int j = 0; j < k; ++j) {
+    // the lane's best untaken logit; u ascends with the index, so a strict
+    // comparison keeps the lowest index among equal values (entries past E
+    // are -inf and never taken)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      if (!((taken >> u) & 1u) && v[u] > bv) {
+        bv = v[u];
+        bi = li + u * 16;
+      }
+    }
+    float mv = fmaxf(bv, row_ror<8>(bv));
+    mv = fmaxf(mv, row_ror<4>(mv));
+    mv = fmaxf(mv, row_ror<2>(mv));
+    mv = fmaxf(mv, row_ror<1>(mv));
+    int ci = bv == mv ? bi : 0x7fffffff;
+    ci = min(ci, row_ror<8>(ci));
+    ci = min(ci, row_ror<4>(ci));
+    ci = min(ci, row_ror<2>(ci));
+    ci = min(ci, row_ror<1>(ci));
+    if (ci != 0x7fffffff && (ci & 15) == li) taken |= 1u << (ci >> 4);
+    if (li == 0 && tok) {
+      idx_t[j] = ci;
+      w_t[j] = expf((mv - m) * inv_tau) / s;
+    }
+  }
+}
+
 template <int L, int V>
 __device__ __forceinline__ void route_token(const float* row, int E, int k, float inv_tau,
                                             int li, bool tok, int32_t* idx_t, float* w_t) {
+  if constexpr (L == 16) {
+    route_token16<V>(row, E, k, inv_tau, li, tok, idx_t, w_t);
+    return;
+  }
   float v[V];
   bool ok[V];
 #pragma unroll

@@ -70,8 +70,9 @@ __device__ __forceinline__ void k_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void k_dma16(rsrc_t rs, uint32_t off, char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (k_lds_void_t*)lds, 16, off, 0, 0, 0);
+// lds: a 32-bit LDS offset (a generic pointer would cost a null check per load)
+__device__ __forceinline__ void k_dma16(rsrc_t rs, uint32_t off, uint32_t lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (k_lds_void_t*)(uintptr_t)lds, 16, off, 0, 0, 0);
 }
 
 // one accumulator element, read out of the accumulation registers where it
@@ -147,6 +148,7 @@ __device__ __forceinline__ uint32_t kbytes(int64_t total, int64_t es, int g) {
 
 __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
   __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int g = blockIdx.y;
   const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
   const int m0 = tm * KBM, n0 = tn * KBN;
@@ -178,8 +180,8 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
     const int sgm = sc / nks, kg = (sc - sgm * nks) * 4 + wave;
     const rsrc_t ra = make_rsrc(a.A[sgm] + (int64_t)g * a.a_es, kbytes(a.a_bytes, a.a_es, g));
     const rsrc_t rb = make_rsrc(a.Bm[sgm] + (int64_t)g * a.b_es, kbytes(a.b_bytes, a.b_es, g));
-    char* la = smem + slot * KSLOT + wave * KPL * 16;
-    char* lb = la + 4 * KPL * 16;
+    const uint32_t la = smem_lds + slot * KSLOT + wave * KPL * 16;
+    const uint32_t lb = la + 4 * KPL * 16;
     const uint32_t oa = 16u * ((uint32_t)kg * (uint32_t)a.a_w + (uint32_t)m0);
     const uint32_t ob = 16u * ((uint32_t)kg * (uint32_t)a.b_w + (uint32_t)n0);
 #pragma unroll
