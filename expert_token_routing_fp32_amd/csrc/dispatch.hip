@@ -51,9 +51,11 @@ __device__ __forceinline__ int load_expert(const int32_t* idx, int64_t q, int64_
   return ((unsigned)e < (unsigned)E) ? e : -1;
 }
 
+// Per-tile expert counts: hist[tile][e], or (trans) hist[e][tile] -- each
+// expert's counts over the tiles contiguous, for the multi-block scan.
 __global__ __launch_bounds__(kSlotThreads) void slot_hist_kernel(const int32_t* __restrict__ idx,
                                                                 int64_t B, int k, int E,
-                                                                int64_t BK, int tile,
+                                                                int64_t BK, int tile, int trans,
                                                                 int32_t* __restrict__ hist) {
   extern __shared__ int h[];
   for (int e = threadIdx.x; e < E; e += kSlotThreads) h[e] = 0;
@@ -65,7 +67,49 @@ __global__ __launch_bounds__(kSlotThreads) void slot_hist_kernel(const int32_t* 
     if (e >= 0) atomicAdd(&h[e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kSlotThreads) hist[(int64_t)blockIdx.x * E + e] = h[e];
+  for (int e = threadIdx.x; e < E; e += kSlotThreads)
+    hist[trans ? (int64_t)e * gridDim.x + blockIdx.x : (int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Multi-block scan of a transposed count table: block e turns row e (expert
+// e's counts over the n_tiles tiles) into its exclusive prefix in place and
+// writes n_e and min(n_e, C_e).  The expert offsets (a prefix over the
+// experts' kept counts) are formed by every rank block from those counts.
+__global__ __launch_bounds__(kSlotThreads) void slot_scan_rows_kernel(
+    int32_t* __restrict__ histT, int n_tiles, int C, const uint8_t* __restrict__ unavail,
+    const int32_t* __restrict__ cap_in, int32_t* __restrict__ expert_load,
+    int32_t* __restrict__ expert_count) {
+  __shared__ int wsum[kSlotThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  int32_t* row = histT + (int64_t)e * n_tiles;
+  int carry = 0;
+  for (int t0 = 0; t0 < n_tiles; t0 += kSlotThreads) {
+    const int t = t0 + tid;
+    const int v = t < n_tiles ? row[t] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int pre = carry + incl - v, all = carry;
+#pragma unroll
+    for (int w = 0; w < kSlotThreads / 64; ++w) {
+      if (w < wave) pre += wsum[w];
+      all += wsum[w];
+    }
+    if (t < n_tiles) row[t] = pre;
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int ce = cap_in ? cap_in[e] : (unavail && unavail[e]) ? 0 : C;
+    if (expert_load) expert_load[e] = carry;
+    expert_count[e] = carry < ce ? carry : ce;
+  }
 }
 
 // One block.  Thread (g, e) of G = 1024/Epad groups walks a contiguous range
@@ -133,15 +177,16 @@ __global__ __launch_bounds__(kScanThreads) void slot_scan_kernel(
 // tile's per-expert bases (the counts of the tiles before it), the totals
 // n_e, min(n_e, C) and the expert offsets; block 0 also writes the scan's
 // outputs.  Used when the count table is small (n_tiles x E <= 16384,
-// E % 4 == 0): re-reading it in every block then costs less than the
-// separate single-workgroup scan launch.
+// E % 4 == 0): re-reading it in every block then costs less than a separate
+// scan launch.  Otherwise `base` is the transposed table of exclusive
+// prefixes (slot_scan_rows_kernel), which also wrote the kept counts; every
+// block forms the expert offsets from those and block 0 writes them.
 template <bool FUSED>
 __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     const int32_t* __restrict__ idx, int64_t B, int k, int E, int nbits, int C,
     const uint8_t* __restrict__ unavail, const int32_t* __restrict__ cap_in, int64_t BK,
-    int tile, const int32_t* __restrict__ base, const int32_t* __restrict__ expert_offset_in,
-    int32_t* __restrict__ pos, uint8_t* __restrict__ keep, int32_t* __restrict__ dest,
-    int32_t* __restrict__ pack_src, int n_tiles, int D, int32_t* __restrict__ expert_load,
+    int tile, const int32_t* __restrict__ base, int32_t* __restrict__ pos,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ dest, int32_t* __restrict__ pack_src, int n_tiles, int D, int32_t* __restrict__ expert_load,
     int32_t* __restrict__ expert_count, int32_t* __restrict__ expert_offset_out,
     int32_t* __restrict__ rank_offset) {
   extern __shared__ int sm[];
@@ -157,14 +202,15 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   for (int i = tid; i < E; i += kSlotThreads)
     cap[i] = cap_in ? cap_in[i] : (unavail && unavail[i]) ? 0 : C;
   __syncthreads();
-  // FUSED: sbase [E] bases of this tile, soff [E + 1] expert offsets of the
-  // kept rows, then scratch
+  // FUSED: sbase [E] bases of this tile; soff [E + 1] expert offsets of the
+  // kept rows; then scratch
   int* sbase = cap + E;
   int* soff = sbase + E;
+  int* wsum = soff + E + 1;
+  int kept[4];
   if constexpr (FUSED) {
-    int* pb = soff + E + 1;          // [G][E] partial sums of the earlier tiles
+    int* pb = wsum + 4;               // [G][E] partial sums of the earlier tiles
     int* pt = pb + kSlotThreads * 4;  // [G][E] partial totals
-    int* wsum = pt + kSlotThreads * 4;
     // thread (g, c): experts 4c .. 4c + 3 (one 16-byte load per tile) over
     // the g-th of G tile groups
     const int E4 = E / 4;
@@ -195,8 +241,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     }
     __syncthreads();
     // thread tid: experts 4 tid .. 4 tid + 3 (E <= 1024): bases, totals,
-    // kept counts, then an exclusive scan of the kept counts over experts
-    int kept[4], run = 0;
+    // kept counts
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = 4 * tid + u;
@@ -214,8 +259,19 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
           expert_count[e] = kept[u];
         }
       }
-      run += kept[u];
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = 4 * tid + u;
+      kept[u] = e < E ? expert_count[e] : 0;
+    }
+  }
+  {
+    // exclusive scan of the kept counts over the experts
+    int run = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) run += kept[u];
     int incl = run;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -235,13 +291,11 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
     if (tid == kSlotThreads - 1) soff[E] = pre;
   }
   __syncthreads();
-  if constexpr (FUSED) {
-    if (blockIdx.x == 0) {
-      for (int i = tid; i <= E; i += kSlotThreads) expert_offset_out[i] = soff[i];
-      for (int r = tid; r <= D; r += kSlotThreads) rank_offset[r] = soff[r * (E / D)];
-    }
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= E; i += kSlotThreads) expert_offset_out[i] = soff[i];
+    for (int r = tid; r <= D; r += kSlotThreads) rank_offset[r] = soff[r * (E / D)];
   }
-  const int32_t* expert_offset = FUSED ? soff : expert_offset_in;
+  const int32_t* expert_offset = soff;
 
   const int S = tile / 4;  // contiguous share of each wavefront (multiple of 64)
   const unsigned long long lt = lanemask_lt(lane);
@@ -254,7 +308,7 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += kSlotThreads) {
-    int b = FUSED ? sbase[e] : base[(int64_t)blockIdx.x * E + e];
+    int b = FUSED ? sbase[e] : base[(int64_t)e * n_tiles + blockIdx.x];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int cnt = wb[w * E + e];
@@ -327,7 +381,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
 
 // Claim-order tiles of 256 .. 2048 assignments: small enough that the
 // histogram and rank passes run on many workgroups, large enough that the
-// single-workgroup scan over (tile, expert) stays short (<= ~256 tiles).
+// count table stays small (<= ~256 tiles).
 SlotPlan slot_plan(int64_t B, int k) {
   SlotPlan p;
   p.BK = B * k;
@@ -352,33 +406,38 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
   while (Epad < E) Epad <<= 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  if (p.n_tiles > 0) {
-    hipLaunchKernelGGL(slot_hist_kernel, dim3(p.n_tiles), dim3(kSlotThreads), E * sizeof(int), s,
-                       idx, B, k, E, p.BK, p.tile, ws_hist);
-  }
-  // small count tables: the rank blocks scan them themselves (no scan launch)
+  // small count tables: the rank blocks scan them themselves (no scan
+  // launch); larger ones are scanned by one block per expert over a
+  // transposed table; an empty batch only needs the single-block scan's zeros
   const bool fused = p.n_tiles > 0 && E % 4 == 0 && (int64_t)p.n_tiles * E <= 16384 &&
                      (reinterpret_cast<uintptr_t>(ws_hist) & 15u) == 0;
-  if (!fused)
+  const bool rows = p.n_tiles > 0 && !fused;
+  if (p.n_tiles > 0) {
+    hipLaunchKernelGGL(slot_hist_kernel, dim3(p.n_tiles), dim3(kSlotThreads), E * sizeof(int), s,
+                       idx, B, k, E, p.BK, p.tile, rows ? 1 : 0, ws_hist);
+  }
+  if (rows)
+    hipLaunchKernelGGL(slot_scan_rows_kernel, dim3(E), dim3(kSlotThreads), 0, s, ws_hist,
+                       p.n_tiles, C, unavail, cap_in, expert_load, expert_count);
+  else if (!fused)
     hipLaunchKernelGGL(slot_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws_hist, p.n_tiles, E,
                        Epad, C, unavail, cap_in, D, expert_load, expert_count, expert_offset,
                        rank_offset);
   if (p.n_tiles > 0) {
-    // ebuf, per-wavefront counts, capacities; fused: + bases, offsets,
-    // 2 x 1024 partials, 4 wave sums
-    const size_t lds = (size_t)(p.tile + 5 * E + (fused ? 2 * E + 1 + 2 * 4 * kSlotThreads + 4 : 0)) *
-                       sizeof(int);
+    // ebuf, per-wavefront counts, capacities, bases, offsets, 4 wave sums;
+    // fused: + 2 x 1024 partials
+    const size_t lds =
+        (size_t)(p.tile + 7 * E + 5 + (fused ? 2 * 4 * kSlotThreads : 0)) * sizeof(int);
     if (fused)
       hipLaunchKernelGGL(slot_rank_kernel<true>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s, idx,
-                         B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist, nullptr, pos,
-                         keep, dest,
-                         pack_src, p.n_tiles, D, expert_load, expert_count, expert_offset,
+                         B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist, pos, keep,
+                         dest, pack_src, p.n_tiles, D, expert_load, expert_count, expert_offset,
                          rank_offset);
     else
       hipLaunchKernelGGL(slot_rank_kernel<false>, dim3(p.n_tiles), dim3(kSlotThreads), lds, s,
-                         idx, B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist,
-                         expert_offset, pos, keep,
-                         dest, pack_src, p.n_tiles, D, nullptr, nullptr, nullptr, nullptr);
+                         idx, B, k, E, nbits, C, unavail, cap_in, p.BK, p.tile, ws_hist, pos,
+                         keep, dest, pack_src, p.n_tiles, D, nullptr, expert_count,
+                         expert_offset, rank_offset);
   }
   return hipGetLastError();
 }

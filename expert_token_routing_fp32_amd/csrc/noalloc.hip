@@ -11,7 +11,8 @@
 // ever passed to kernels.
 //
 // Nothing in the table needs to start at zero: the histogram kernel writes
-// every (tile, expert) count before the scan or rank kernels read it.  All
+// every (tile, expert) count, and clears the multi-block scan's completion
+// counter, before the scan or rank kernels read them.  All
 // calls on one GPU share the table, so calls that overlap on one GPU (on
 // different streams, unordered) race and must not be issued.
 #include <mutex>
