@@ -513,18 +513,25 @@ def main():
     # every one from the dispatch timestamps of a stage's own kernels (start
     # of its first, end of its last: no marker packets), so each stage's
     # time is its kernels' and the gaps between launches are measured apart.
+    # A launch that carries an event gets a gap of a few microseconds on
+    # each side (the runtime's timestamping); launches without events follow
+    # each other with none.  So the timed steps carry events only on every
+    # `stride`-th step (at least 10 sampled steps), and those time one GEMM
+    # of the expert FFN each, by its own start and end: GEMM1 on the even
+    # sampled steps, GEMM2 on the odd ones; the FFN's time is the sum of the
+    # two means.  A second run of as many steps records every event on every
+    # step for the breakdown (there too the FFN is the sum of its GEMMs).
     # The expert-choice forward records marker events at its stage
-    # boundaries, except around the expert FFN.  The timed steps record only
-    # the FFN pair, and only on every `stride`-th step (at least 10 sampled
-    # steps); a second run of as many steps records them all on every step
-    # for the breakdown.
+    # boundaries, except around the expert FFN (one pair).
     if ec:
-        n_ev, ffn_ev = 6, (3, 4)
+        n_ev = 6
+        ffn_parts = [(3, 4)]
         pairs = {"gate": (0, 1), "route": (1, 2), "dispatch": (2, 3), "expert_ffn": (3, 4),
                  "combine": (4, 5)}
         gaps = {}
     else:
-        n_ev, ffn_ev = moe.N_STAGE_EVENTS, moe.STAGE_EVENTS["expert_ffn"]
+        n_ev = moe.N_STAGE_EVENTS
+        ffn_parts = [moe.FFN_GEMM_EVENTS["gemm1"], moe.FFN_GEMM_EVENTS["gemm2"]]
         pairs, gaps = moe.STAGE_EVENTS, moe.LAUNCH_GAPS
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     for row in evs:
@@ -532,8 +539,12 @@ def main():
             e.record()
     stride = max(1, args.steps // 10)
     sampled = list(range(0, args.steps, stride))
-    ffn_only = [[r[j] if j in ffn_ev else None for j in range(n_ev)] if i % stride == 0 else None
-                for i, r in enumerate(evs)]
+    # which FFN part each sampled step times (all parts on one step when
+    # there are fewer sampled steps than parts)
+    part_of = {i: [ffn_parts[n % len(ffn_parts)]] if len(sampled) >= len(ffn_parts) else ffn_parts
+               for n, i in enumerate(sampled)}
+    ffn_only = [[r[j] if any(j in ab for ab in part_of[i]) else None for j in range(n_ev)]
+                if i in part_of else None for i, r in enumerate(evs)]
 
     def step(ev=None):
         if flush is not None:
@@ -564,8 +575,10 @@ def main():
         torch.cuda.synchronize()
         flush_s = (time.perf_counter() - f0) / args.steps
         sec_per_step -= flush_s
-    a, b = ffn_ev
-    t_ffn_live = sum(evs[i][a].elapsed_time(evs[i][b]) for i in sampled) / len(sampled) * 1e-3
+    t_ffn_live = 0.0
+    for ab in ffn_parts:
+        on = [i for i in sampled if ab in part_of[i]]
+        t_ffn_live += sum(evs[i][ab[0]].elapsed_time(evs[i][ab[1]]) for i in on) / len(on) * 1e-3
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
@@ -573,6 +586,7 @@ def main():
         return sum(r[ab[0]].elapsed_time(r[ab[1]]) for r in evs) / len(evs) * 1e-3
 
     stage_s = {name: mean_s(ab) for name, ab in pairs.items()}
+    stage_s["expert_ffn"] = sum(mean_s(ab) for ab in ffn_parts)
     gap_s = {name: mean_s(ab) for name, ab in gaps.items()}
     # per-step device time of the breakdown run: first kernel's start to the
     # last kernel's end (events from the dispatches), median over the steps
@@ -662,9 +676,12 @@ def main():
     roof["algorithmic_bytes"] = alg["ffn_bytes"]
     roof["algorithmic_flop"] = alg["ffn_flop"]
     roof["avg_launch_us"] = round(t_ffn_live * 1e6, 2)
-    roof["timing"] = ("HIP events taken from the start of the expert FFN's first kernel and "
-                      "the end of its last (hipExtLaunchKernelGGL on the forward's stream), "
-                      f"averaged over {len(sampled)} of the {args.steps} timed steps "
+    roof["timing"] = (("HIP events from the start and end of the expert FFN's kernels" if ec else
+                       "HIP events from the start and end of each of the expert FFN's two GEMM "
+                       "kernels (GEMM1 on half the sampled steps, GEMM2 on the other half; the "
+                       "FFN is the sum of their means)") +
+                      " (hipExtLaunchKernelGGL on the forward's stream), sampled on "
+                      f"{len(sampled)} of the {args.steps} timed steps "
                       f"({'all' if stride == 1 else f'every {stride}th'})")
 
     rpc_bytes = alg["route_bytes"] + alg["slot_bytes"] + alg["pack_bytes"] + alg["combine_bytes"]

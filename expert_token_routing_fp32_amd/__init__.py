@@ -29,7 +29,7 @@ __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate
            "expert_choice_combine", "forward_expert_choice", "expert_choice_rows",
            "combine_backward", "route_backward", "weights_bwd_bytes", "pack_weights_bwd",
            "expert_ffn_backward", "dispatch_backward", "gate_backward", "backward", "MoEError",
-           "Problem", "lib"]
+           "Problem", "lib", "FFN_GEMM_EVENTS"]
 
 
 def lib():
@@ -376,11 +376,14 @@ _OUT_FIELDS = ("logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_lo
 
 
 # forward's stage events: the start and end of each stage's kernels
-# (dispatch timestamps); the gaps between launches lie between the pairs
+# (dispatch timestamps); the expert FFN's two GEMMs also have their own
+# pairs; the gaps between launches lie between the pairs
 N_STAGE_EVENTS = L.MOE_STAGE_EVENTS
-STAGE_EVENTS = {"gate": (0, 1), "route": (2, 3), "dispatch": (3, 4), "expert_ffn": (5, 6),
-                "combine": (7, 8)}
-LAUNCH_GAPS = {"gate_route": (1, 2), "before_ffn": (4, 5), "after_ffn": (6, 7)}
+STAGE_EVENTS = {"gate": (0, 1), "route": (2, 3), "dispatch": (3, 4), "expert_ffn": (5, 8),
+                "combine": (9, 10)}
+FFN_GEMM_EVENTS = {"gemm1": (5, 6), "gemm2": (7, 8)}
+LAUNCH_GAPS = {"gate_route": (1, 2), "before_ffn": (4, 5), "between_gemms": (6, 7),
+               "after_ffn": (8, 9)}
 STAGES = tuple(STAGE_EVENTS)
 
 

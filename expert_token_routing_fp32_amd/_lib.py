@@ -40,7 +40,7 @@ class Problem(ctypes.Structure):
     ]
 
 
-MOE_STAGE_EVENTS = 9  # events of moe_forward_out_t
+MOE_STAGE_EVENTS = 11  # events of moe_forward_out_t
 MOE_DISPATCH_NOALLOC_SCRATCH_BYTES = 16 << 20  # table of moe_dispatch_noalloc
 
 

@@ -42,8 +42,7 @@
 //    rows per expert): chunks of consecutive tiles are dealt round-robin
 //    over the XCDs, so each XCD works on a compact patch of one expert at a
 //    time and every XCD gets a share of every expert.
-#include <hip/hip_ext.h>
-
+#include "launch.h"
 #include "moe_kernels.h"
 
 namespace moek {
@@ -716,7 +715,9 @@ int device_cus() {
 // One workgroup per CU (the LDS ring takes most of the 160 KB), no more
 // workgroups than there could be tiles.  e0 / e1 (optional) take the
 // dispatch's start / end timestamps; with no tiles they are recorded as
-// markers.
+// markers.  Without events the plain launch is used: the timestamped launch
+// leaves a gap of about 5 us on each side of the kernel (measured in kernel
+// traces; the plain launches follow each other with none).
 template <int MODE>
 hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s,
                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
@@ -730,11 +731,9 @@ hipError_t launch_gemm(GemmArgs g, int m_tiles, bool mfma_bound, hipStream_t s,
   const int cus = device_cus();
   const int grid = bound < cus ? (int)bound : cus;
   if (mfma_bound && grid >= kXcd)
-    hipExtLaunchKernelGGL((grouped_gemm_kernel<MODE, true>), dim3(grid), dim3(kThreads), 0, s, e0,
-                          e1, 0, g);
+    launch_timed(grouped_gemm_kernel<MODE, true>, dim3(grid), dim3(kThreads), 0, s, e0, e1, g);
   else
-    hipExtLaunchKernelGGL((grouped_gemm_kernel<MODE, false>), dim3(grid), dim3(kThreads), 0, s, e0,
-                          e1, 0, g);
+    launch_timed(grouped_gemm_kernel<MODE, false>, dim3(grid), dim3(kThreads), 0, s, e0, e1, g);
   return hipGetLastError();
 }
 
@@ -849,11 +848,12 @@ hipError_t launch_shared_ffn(const uint16_t* x, int64_t B, int d, int f, bool sw
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
-                             hipEvent_t ev_start, hipEvent_t ev_stop) {
+                             hipEvent_t ev_start, hipEvent_t ev_stop, hipEvent_t ev_mid_end,
+                             hipEvent_t ev_mid_start) {
   if (n_local <= 0 || rows_max <= 0) {
     hipError_t e = hipSuccess;
-    if (ev_start) e = hipEventRecord(ev_start, s);
-    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
+    for (hipEvent_t ev : {ev_start, ev_mid_end, ev_mid_start, ev_stop})
+      if (e == hipSuccess && ev) e = hipEventRecord(ev, s);
     return e;
   }
   // a 256-column tile does 2 * rows FLOP per weight byte; above ~384 rows per
@@ -875,8 +875,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g1.n_tiles_n = geo1.n_tiles;
   g1.nk = geo1.nk;
   g1.n_local = n_local;
-  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s, ev_start)
-                          : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s, ev_start);
+  hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end)
+                          : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end);
   if (err != hipSuccess) return err;
 
   GemmArgs g2{};
@@ -892,7 +892,7 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g2.n_tiles_n = geo2.n_tiles;
   g2.nk = geo2.nk;
   g2.n_local = n_local;
-  return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s, nullptr, ev_stop);
+  return launch_gemm<MODE_PLAIN>(g2, m_tiles, mfma_bound, s, ev_mid_start, ev_stop);
 }
 
 }  // namespace moek

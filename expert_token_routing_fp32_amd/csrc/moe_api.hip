@@ -609,15 +609,15 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
     if (e == hipSuccess)
       e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                   rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
-                                  stream, ev[5], sh ? nullptr : ev[6]);
+                                  stream, ev[5], sh ? nullptr : ev[8], ev[6], ev[7]);
     if (e == hipSuccess && sh)
       e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
                                   sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,
-                                  ev[6]);
+                                  ev[8]);
   }
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
-                             p->k, p->d, kmax_of(p), stream, sh ? sh->S : nullptr, ev[7], ev[8]);
+                             p->k, p->d, kmax_of(p), stream, sh ? sh->S : nullptr, ev[9], ev[10]);
   return hip_status(e);
 }
 

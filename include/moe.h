@@ -342,7 +342,7 @@ moe_status_t moe_routing_stats(const moe_problem_t* p, const float* logits,
                                size_t ws_bytes, hipStream_t stream);
 
 /* Number of stage events of moe_forward_out_t. */
-#define MOE_STAGE_EVENTS 9
+#define MOE_STAGE_EVENTS 11
 
 /* Optional outputs of moe_forward; any NULL field lives in the workspace. */
 typedef struct {
@@ -365,11 +365,16 @@ typedef struct {
    *   0 gate start          1 gate end
    *   2 route start         3 route end
    *   4 dispatch end (the pack kernel; 3 -> 4 is the slot kernels + pack)
-   *   5 expert FFN start    6 expert FFN end
-   *   7 combine start       8 combine end
-   * so 1 -> 2, 4 -> 5 and 6 -> 7 are the gaps between launches.  With
-   * B == 0 no kernel runs and every event is recorded as a marker.  The
-   * caller owns the events (created with timing enabled). */
+   *   5 expert FFN start    6 end of its first GEMM
+   *   7 start of its second GEMM (after the routed GEMMs: the shared
+   *     expert's, when there is one)      8 expert FFN end
+   *   9 combine start      10 combine end
+   * so 1 -> 2, 4 -> 5, 6 -> 7 and 8 -> 9 are the gaps between launches.  A
+   * launch that carries an event is timestamped by the runtime, which
+   * leaves a gap of a few microseconds on each side of it; launches without
+   * events follow each other with none, so time a stage on its own steps.
+   * With B == 0 no kernel runs and every event is recorded as a marker.
+   * The caller owns the events (created with timing enabled). */
   hipEvent_t events[MOE_STAGE_EVENTS];
 } moe_forward_out_t;
 

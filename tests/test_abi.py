@@ -243,15 +243,18 @@ def test_overflow_policy_checks(L, lib):
 
 def test_stage_event_count_and_pairs_match_the_header(L):
     """The header's MOE_STAGE_EVENTS, the binding's constant and the stage /
-    gap pairs agree: each pair is ordered, the stages and the gaps together
-    walk the events 0 .. MOE_STAGE_EVENTS - 1 in order (dispatch runs from
-    the route's end to the pack's end, so it shares event 3 with the
-    route)."""
+    gap pairs agree: each pair is ordered, the stages (the expert FFN as its
+    two GEMMs) and the gaps together walk the events 0 .. MOE_STAGE_EVENTS - 1
+    in order (dispatch runs from the route's end to the pack's end, so it
+    shares event 3 with the route), and the FFN's pair spans its GEMMs'."""
     import expert_token_routing_fp32_amd as moe
     text = open(os.path.join(ROOT, "include", "moe.h")).read()
     n = int(re.search(r"#define MOE_STAGE_EVENTS (\d+)", text).group(1))
     assert n == L.MOE_STAGE_EVENTS == moe.N_STAGE_EVENTS == len(L.ForwardOut().events)
-    pairs = sorted(list(moe.STAGE_EVENTS.values()) + list(moe.LAUNCH_GAPS.values()))
+    stages = {k: v for k, v in moe.STAGE_EVENTS.items() if k != "expert_ffn"}
+    g1, g2 = moe.FFN_GEMM_EVENTS["gemm1"], moe.FFN_GEMM_EVENTS["gemm2"]
+    assert moe.STAGE_EVENTS["expert_ffn"] == (g1[0], g2[1])
+    pairs = sorted(list(stages.values()) + [g1, g2] + list(moe.LAUNCH_GAPS.values()))
     assert all(a < b for a, b in pairs)
     assert pairs[0][0] == 0 and pairs[-1][1] == n - 1
     assert all(p[1] == q[0] for p, q in zip(pairs, pairs[1:]))
