@@ -20,7 +20,12 @@
 //              scheduling
 //   operands = x rows staged in LDS by DMA, shared by the EB waves of a K
 //              range; weights straight from global memory into registers
-//              (the lane's expert column, 8 k per step), split there
+//              (the lane's expert column, 8 k per step), split there; or,
+//              in moe_forward, from a copy of the weights made at the start
+//              of the call: their bf16 parts in the lanes' order (the split
+//              copy), or the fp32 values in the lanes' order (the blocked
+//              copy: two 16-byte loads per step instead of eight 4-byte
+//              ones)
 //
 // fp32 activations: the vector ALUs (a block owns BT tokens x BE experts;
 // four waves split each 128-wide slice of d; blocked accumulation keeps the
@@ -200,13 +205,38 @@ __global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict
   }
 }
 
+// Blocked fp32 copy of the router weights, in the order the gate's lanes
+// load them: for expert block eb (32 experts) and K step ks (16 k), 64 lanes
+// x 32 bytes as two 1 KB halves -- half hf of lane l holds k = 16 ks +
+// 8 (l / 32) + 4 hf .. +3 of expert 32 eb + l % 32 (zeros past d or E).
+// One thread per (eb, ks, lane).
+__global__ __launch_bounds__(256) void gate_block_kernel(const float* __restrict__ Wg, int d,
+                                                         int E, int neb, int nks,
+                                                         f32x4* __restrict__ out) {
+  const int64_t n = (int64_t)neb * nks * 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int lane = (int)(i & 63);
+    const int64_t bk = i >> 6;  // eb * nks + ks
+    const int ks = (int)(bk % nks), eb = (int)(bk / nks);
+    const int e = 32 * eb + (lane & 31);
+    const int k0 = 16 * ks + 8 * (lane >> 5);
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (e < E && k0 + q < d) ? Wg[(int64_t)(k0 + q) * E + e] : 0.f;
+    out[(bk * 2 + 0) * 64 + lane] = f32x4{v[0], v[1], v[2], v[3]};
+    out[(bk * 2 + 1) * 64 + lane] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
 // The token rows are staged once per block in LDS, shared by the EB waves
 // of one K range.  Stages of 64 k; a 3-slot ring filled by DMA
 // (buffer_load_dwordx4 ... lds, rows bank-swizzled) two stages ahead; the
 // lane's weight column (8 k per MFMA step) prefetched two stages ahead in
-// registers and split there, or (PS) its three bf16 parts loaded as they
-// are from the split copy (gate_split_kernel): 3 16-byte loads per step
-// instead of 8 4-byte loads and the split.
+// registers and split there, or its three bf16 parts loaded as they are
+// from the split copy (gate_split_kernel: 3 16-byte loads per step instead
+// of 8 4-byte loads and the split), or its 8 fp32 values loaded from the
+// blocked copy (gate_block_kernel: 2 16-byte loads) and split there.
+enum GateW { kWDirect = 0, kWSplit = 1, kWBlock = 2 };
 typedef __attribute__((address_space(3))) void g_lds_void_t;
 
 template <int N>
@@ -225,7 +255,51 @@ __device__ __forceinline__ void g_dma16(const void* base, uint32_t bytes, uint32
 }
 __device__ __forceinline__ int g_swz(int r, int ch) { return r * 128 + ((ch ^ ((r >> 1) & 7)) << 4); }
 
-template <int MI, int EB, int KS, bool PS>
+// The MFMA steps of one 64-k stage: sa = the stage's rows in LDS (this K
+// range's slot), the lane's weights for the stage as the copy's 16-byte
+// parts (wq) or as fp32 values (wv).
+template <int MI, int WM, int NP>
+__device__ __forceinline__ void gl_mul(g_f32x16 (&acc)[MI], const char* sa, const u32x4 (&wq)[4][NP],
+                                       const float (&wv)[4][8], int l32, int h) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 hi, mid, lo;
+    if constexpr (WM == kWSplit) {
+      lo = wq[j][0];
+      mid = wq[j][1];
+      hi = wq[j][2];
+    } else if constexpr (WM == kWBlock) {
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[q] = __uint_as_float(wq[j][0][q]);
+        f[4 + q] = __uint_as_float(wq[j][NP - 1][q]);
+      }
+      split3(f, hi, mid, lo);
+    } else {
+      split3(wv[j], hi, mid, lo);
+    }
+    // the three products of a row block accumulate into one register set,
+    // so the parts go round the row blocks (lo of every block, then mid,
+    // then hi): consecutive matrix instructions are independent whenever
+    // MI > 1, and each accumulator still adds lo, mid, hi in that order
+    g_bf16x8 a[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      a[i] = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, lo), acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, mid), acc[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, hi), acc[i], 0, 0, 0);
+  }
+}
+
+template <int MI, int EB, int KS, int WM>
 __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wg, const u32x4* __restrict__ Wsp,
     const float* __restrict__ bias, float* __restrict__ logits, int64_t B, int d, int E) {
@@ -235,7 +309,9 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
   constexpr int NSL = 3;
   constexpr int ND = 4 * MI / EB;      // DMA instructions per wave per stage
   static_assert(ND >= 1 && ND * EB == 4 * MI, "rows split evenly over the expert waves");
-  constexpr int LOADS = (PS ? 12 : 32) + ND;  // vector-memory loads per wave per stage
+  constexpr bool PS = WM != kWDirect;  // weights from a copy in the lanes' order
+  constexpr int NP = WM == kWSplit ? 3 : 2;  // 16-byte loads per lane and MFMA step
+  constexpr int LOADS = (PS ? 4 * NP : 32) + ND;  // vector-memory loads per wave per stage
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int eb = w % EB, kq = w / EB;
@@ -263,7 +339,10 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
     dcol[q] = 8 * ((lane & 7) ^ ((row >> 1) & 7));
     dofs[q] = kq * SLOT + 8 * (eb + EB * q) * 128;
   }
-  const float* wc = Wg + (e0 + l32 < E ? e0 + l32 : E - 1);
+  // weight loads go through buffer descriptors over the wavefront's own K
+  // range, so K steps past it read zeros: no select on a loaded value (which
+  // would make the compiler wait for the load there and undo the prefetch)
+  const int ec = e0 + l32 < E ? e0 + l32 : E - 1;  // past E: any valid column, never stored
 
   g_f32x16 acc[MI];
 #pragma unroll
@@ -271,8 +350,8 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   float wv[PS ? 1 : NSL][4][8];
-  u32x4 wq[PS ? NSL : 1][4][3];
-  // PS: this wavefront's expert block in the split copy, and its first K step.
+  u32x4 wq[PS ? NSL : 1][4][NP];
+  // PS: this wavefront's expert block in the copy, and its first K step.
   // The copy holds neb = ceil(E / 32) blocks; a wavefront whose block lies
   // past them (the last row of the grid when EB does not divide neb) reads
   // the last block instead -- in bounds, and its results are never stored
@@ -283,7 +362,11 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
   const int neb = (E + 31) / 32;
   const int ebs = (int)blockIdx.y * EB + eb < neb ? (int)blockIdx.y * EB + eb : neb - 1;
   const int kb16 = kb / 16 < nks ? kb / 16 : nks - 1;
-  const u32x4* wsb = Wsp + ((int64_t)ebs * nks + kb16) * 3 * 64 + lane;
+  // PS: the copy's K steps kb / 16 .. ceil(ke / 16) of this expert block
+  const int nvalid = ke > kb ? (ke - kb + 15) / 16 : 0;
+  const rsrc_t wrs =
+      PS ? make_rsrc(Wsp + ((int64_t)ebs * nks + kb16) * NP * 64, (uint32_t)nvalid * NP * 1024u)
+         : make_rsrc(Wg + (int64_t)kb * E, 4u * (uint32_t)(ke > kb ? ke - kb : 0) * (uint32_t)E);
 
   // stage s (clamped to the last one): weights, then rows.  K chunks past
   // the end of the row read the row's last chunk; their weights are zero.
@@ -291,24 +374,18 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
   {                                                                                  \
     const int sc_ = (S) < nst ? (S) : nst - 1;                                       \
     if constexpr (PS) {                                                              \
-      /* a K step past this wave's range reads the wave's first step (in the */      \
-      /* copy) and is then zeroed; the copy itself holds zeros past d        */      \
-      _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                             \
-        const bool ok_ = kb + 64 * sc_ + 16 * j_ < ke;                               \
-        const int64_t st_ = ok_ ? (int64_t)(4 * sc_ + j_) * 3 * 64 : 0;              \
-        _Pragma("unroll") for (int p_ = 0; p_ < 3; ++p_)                             \
-          wq[B_][j_][p_] = wsb[st_ + p_ * 64];                                       \
-        if (!ok_) wq[B_][j_][0] = wq[B_][j_][1] = wq[B_][j_][2] = u32x4{0u, 0u, 0u, 0u}; \
-      }                                                                              \
+      /* steps past the wave's K range lie past the descriptor: zeros */             \
+      _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                               \
+        _Pragma("unroll") for (int p_ = 0; p_ < NP; ++p_)                            \
+          wq[B_][j_][p_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128( \
+              wrs, (uint32_t)(((4 * sc_ + j_) * NP + p_) * 64 + lane) * 16u, 0, 0));  \
     } else {                                                                         \
+      /* rows k >= ke lie past the descriptor: zeros */                              \
       _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_) {                             \
-        const int k_ = kb + 64 * sc_ + 16 * j_ + 8 * h;                              \
-        const bool ok_ = k_ < ke;                                                    \
-        const float* wp_ = wc + (int64_t)(ok_ ? k_ : 0) * E;                         \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                           \
-          const float v_ = wp_[(int64_t)i_ * E];                                     \
-          wv[B_][j_][i_] = ok_ ? v_ : 0.f;                                           \
-        }                                                                            \
+        const uint32_t r_ = (uint32_t)(64 * sc_ + 16 * j_ + 8 * h);                  \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                             \
+          wv[B_][j_][i_] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(     \
+              wrs, ((r_ + i_) * (uint32_t)E + (uint32_t)ec) * 4u, 0, 0));            \
       }                                                                              \
     }                                                                                \
     const int kx_ = kb + 64 * sc_;                                                   \
@@ -318,49 +395,31 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
       g_dma16(xblk, xbytes, xrow[q_] + 2u * (kk_ < d ? kk_ : d - 8), sl_ + dofs[q_]); \
     }                                                                                \
   }
+  // one stage: wait for stage s (at most one stage's loads left in flight),
+  // barrier, issue stage s + 2 into the slot stage s - 1 used, multiply
+#define GL_STAGE(S, U)                                                               \
+  {                                                                                  \
+    g_wait_vmcnt<LOADS>();                                                           \
+    __builtin_amdgcn_s_barrier();                                                    \
+    GL_ISSUE((S) + 2, ((U) + 2) % NSL)                                               \
+    __builtin_amdgcn_sched_barrier(0);                                               \
+    gl_mul<MI, WM, NP>(acc, gsm + ((S) % NSL) * KS * SLOT + kq * SLOT, wq[(U) % NSL_Q], \
+                       wv[(U) % NSL_V], l32, h);                                     \
+  }
+  constexpr int NSL_Q = PS ? NSL : 1, NSL_V = PS ? 1 : NSL;
   GL_ISSUE(0, 0)
   GL_ISSUE(1, 1)
-  for (int s0 = 0; s0 < nst; s0 += NSL) {
+  // whole groups of NSL stages, then the remainder: no condition inside the
+  // unrolled group, so the compiler can see which loads each step waits for
+  // (with one, its own waits fall back to nearly every load in flight)
+  const int nfull = nst - nst % NSL;
+  for (int s0 = 0; s0 < nfull; s0 += NSL) {
 #pragma unroll
-    for (int u = 0; u < NSL; ++u) {
-      const int s = s0 + u;
-      if (s < nst) {
-        g_wait_vmcnt<LOADS>();
-        __builtin_amdgcn_s_barrier();
-        GL_ISSUE(s + 2, (u + 2) % NSL)
-        const char* sa = gsm + (s % NSL) * KS * SLOT + kq * SLOT;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 hi, mid, lo;
-          if constexpr (PS) {
-            lo = wq[u][j][0];
-            mid = wq[u][j][1];
-            hi = wq[u][j][2];
-          } else {
-            split3(wv[u][j], hi, mid, lo);
-          }
-          // the three products of a row block accumulate into one register
-          // set, so the parts go round the row blocks (lo of every block,
-          // then mid, then hi): consecutive matrix instructions are
-          // independent whenever MI > 1, and each accumulator still adds
-          // lo, mid, hi in that order
-          g_bf16x8 a[MI];
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-            a[i] = __builtin_bit_cast(g_bf16x8, *(const u32x4*)(sa + g_swz(32 * i + l32, 2 * j + h)));
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, lo), acc[i], 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, mid), acc[i], 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < MI; ++i)
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(g_bf16x8, hi), acc[i], 0, 0, 0);
-        }
-      }
-    }
+    for (int u = 0; u < NSL; ++u) GL_STAGE(s0 + u, u)
   }
+  if (nst - nfull > 0) GL_STAGE(nfull, 0)
+  if (nst - nfull > 1) GL_STAGE(nfull + 1, 1)
+#undef GL_STAGE
 #undef GL_ISSUE
   g_wait_vmcnt<0>();
   __syncthreads();
@@ -401,21 +460,23 @@ __global__ __launch_bounds__(64 * EB * KS) void gate_lds_kernel(
 }
 
 template <int MI, int EB, int KS>
-hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* wsp,
+hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* wsp, int wm,
                               const float* bias, float* logits, int64_t B, int d, int E,
                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int neb = (E + 31) / 32;
   dim3 grid((unsigned)((B + 32 * MI - 1) / (32 * MI)), (unsigned)((neb + EB - 1) / EB));
   const size_t lds = (size_t)EB * (KS - 1) * MI * 16 * 64 * sizeof(float);
   const size_t ring = (size_t)3 * KS * 32 * MI * 128;
-  if (wsp)
-    launch_timed((gate_lds_kernel<MI, EB, KS, true>), grid, dim3(64 * EB * KS),
-                 lds > ring ? lds : ring, s, e0, e1, x, Wg, wsp, bias, logits, B, d,
-                 E);
+  const size_t sh = lds > ring ? lds : ring;
+  if (wm == kWSplit)
+    launch_timed((gate_lds_kernel<MI, EB, KS, kWSplit>), grid, dim3(64 * EB * KS), sh, s, e0, e1,
+                 x, Wg, wsp, bias, logits, B, d, E);
+  else if (wm == kWBlock)
+    launch_timed((gate_lds_kernel<MI, EB, KS, kWBlock>), grid, dim3(64 * EB * KS), sh, s, e0, e1,
+                 x, Wg, wsp, bias, logits, B, d, E);
   else
-    launch_timed((gate_lds_kernel<MI, EB, KS, false>), grid, dim3(64 * EB * KS),
-                 lds > ring ? lds : ring, s, e0, e1, x, Wg, wsp, bias, logits, B, d,
-                 E);
+    launch_timed((gate_lds_kernel<MI, EB, KS, kWDirect>), grid, dim3(64 * EB * KS), sh, s, e0,
+                 e1, x, Wg, wsp, bias, logits, B, d, E);
   return hipGetLastError();
 }
 
@@ -424,17 +485,17 @@ hipError_t launch_gate_mfma_t(const uint16_t* x, const float* Wg, const u32x4* w
 // shared by the EB waves); only those shapes are compiled.
 template <int EB, int KS>
 hipError_t launch_gate_mfma_mi(int mi, const uint16_t* x, const float* Wg, const u32x4* wsp,
-                               const float* bias, float* logits, int64_t B, int d, int E,
+                               int wm, const float* bias, float* logits, int64_t B, int d, int E,
                                hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int MI_MAX = KS >= 8 ? 1 : KS >= 4 ? 2 : 4;
   constexpr int MI_MIN = EB >= 8 ? 2 : 1;
   if constexpr (MI_MAX >= 4)
-    if (mi >= 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    if (mi >= 4) return launch_gate_mfma_t<4, EB, KS>(x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
   if constexpr (MI_MAX >= 2)
     if (mi >= 2 || MI_MIN >= 2)
-      return launch_gate_mfma_t<2, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+      return launch_gate_mfma_t<2, EB, KS>(x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
   if constexpr (MI_MIN <= 1)
-    return launch_gate_mfma_t<1, EB, KS>(x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    return launch_gate_mfma_t<1, EB, KS>(x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
   return hipErrorInvalidValue;
 }
 
@@ -472,22 +533,22 @@ GatePlan gate_plan(int64_t B, int d, int E, bool split) {
   return g;
 }
 
-hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const u32x4* wsp,
+hipError_t launch_gate_mfma(const uint16_t* x, const float* Wg, const u32x4* wsp, int wm,
                             const float* bias, float* logits, int64_t B, int d, int E,
                             hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  const GatePlan g = gate_plan(B, d, E, wsp != nullptr);
+  const GatePlan g = gate_plan(B, d, E, wm == kWSplit);
   const int eb = g.eb, ks = g.ks, mi = g.mi;
   switch (eb * 16 + ks) {
-    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
-    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, wsp, bias, logits, B, d, E, s, e0, e1);
+    case 8 * 16 + 1: return launch_gate_mfma_mi<8, 1>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 4 * 16 + 2: return launch_gate_mfma_mi<4, 2>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 4 * 16 + 1: return launch_gate_mfma_mi<4, 1>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 4: return launch_gate_mfma_mi<2, 4>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 2: return launch_gate_mfma_mi<2, 2>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 2 * 16 + 1: return launch_gate_mfma_mi<2, 1>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 8: return launch_gate_mfma_mi<1, 8>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 4: return launch_gate_mfma_mi<1, 4>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    case 1 * 16 + 2: return launch_gate_mfma_mi<1, 2>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
+    default: return launch_gate_mfma_mi<1, 1>(mi, x, Wg, wsp, wm, bias, logits, B, d, E, s, e0, e1);
   }
 }
 
@@ -511,13 +572,19 @@ hipError_t launch_gate_t(const void* x, bool x_bf16, const float* Wg, const floa
 size_t gate_split_bytes(int d, int E) {
   return (size_t)((E + 31) / 32) * ((d + 15) / 16) * 3 * 1024;
 }
+size_t gate_block_bytes(int d, int E) {
+  return (size_t)((E + 31) / 32) * ((d + 15) / 16) * 2 * 1024;
+}
 
-// Exclusive end (bytes) of what gate_lds_kernel<..., PS = true> reads from
-// the split copy at (B, d, E), walking the launch the plan gives: every
-// workgroup row, wavefront expert block and K range, every stage and MFMA
-// step, with the kernel's own index arithmetic.
+// Exclusive end (bytes) of what gate_lds_kernel reads from the weight copy
+// the forward would use at (B, d, E) (split: 3 parts per step, blocked: 2),
+// walking the launch the plan gives: every workgroup row, wavefront expert
+// block and K range, every stage and MFMA step, with the kernel's own index
+// arithmetic.
 int64_t gate_split_read_end(int64_t B, int d, int E) {
-  const GatePlan g = gate_plan(B, d, E, true);
+  const bool split = gate_use_split(true, B, d, E);
+  const int np = split ? 3 : 2;
+  const GatePlan g = gate_plan(B, d, E, split);
   const int neb = (E + 31) / 32, nks = (d + 15) / 16;
   const int64_t gy = (neb + g.eb - 1) / g.eb;
   const int kspan = (d + 64 * g.ks - 1) / (64 * g.ks) * 64;
@@ -529,12 +596,12 @@ int64_t gate_split_read_end(int64_t B, int d, int E) {
         const int kb = kq * kspan, ke = kb + kspan < d ? kb + kspan : d;
         const int ebs = by * g.eb + eb < neb ? (int)(by * g.eb + eb) : neb - 1;
         const int kb16 = kb / 16 < nks ? kb / 16 : nks - 1;
-        const int64_t base = ((int64_t)ebs * nks + kb16) * 3 * 64;
+        const int64_t base = ((int64_t)ebs * nks + kb16) * np * 64;
         for (int sc = 0; sc < nst; ++sc)
           for (int j = 0; j < 4; ++j) {
             const bool ok = kb + 64 * sc + 16 * j < ke;
-            const int64_t st = ok ? (int64_t)(4 * sc + j) * 3 * 64 : 0;
-            const int64_t last = base + st + 2 * 64 + 63;  // part 2, lane 63
+            const int64_t st = ok ? (int64_t)(4 * sc + j) * np * 64 : 0;
+            const int64_t last = base + st + (np - 1) * 64 + 63;  // last part, lane 63
             if (16 * (last + 1) > end) end = 16 * (last + 1);
           }
       }
@@ -552,24 +619,47 @@ bool gate_use_split(bool x_bf16, int64_t B, int d, int E) {
   return gate_plan(B, d, E, false).blocks < 256 && gate_plan(B, d, E, true).blocks > 128;
 }
 
+// The blocked fp32 copy: the same bytes per workgroup as reading Wg itself,
+// in two 16-byte loads per MFMA step instead of eight 4-byte ones.  Worth its
+// launch on large gates (EP share: 256 workgroups that each read all of
+// Wg); small ones keep the direct loads.
+bool gate_use_block(bool x_bf16, int64_t B, int d, int E) {
+  return x_bf16 && !gate_use_split(x_bf16, B, d, E) && B * E >= ((int64_t)1 << 22) && d >= 64;
+}
+
+size_t gate_copy_bytes(bool x_bf16, int64_t B, int d, int E) {
+  if (gate_use_split(x_bf16, B, d, E)) return gate_split_bytes(d, E);
+  if (gate_use_block(x_bf16, B, d, E)) return gate_block_bytes(d, E);
+  return 0;
+}
+
 hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float* bias,
                        float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s,
                        hipEvent_t e0, hipEvent_t e1) {
   if (B == 0) return hipSuccess;
+  int wm = kWDirect;
   if (x_bf16 && wsplit) {
     const int neb = (E + 31) / 32, nks = (d + 15) / 16;
     const int64_t n = (int64_t)neb * nks * 64;
     const int64_t g = (n + 255) / 256;
+    const dim3 grid((unsigned)(g < 65536 ? g : 65536));
     // the start event goes with the first of the two launches
-    launch_timed(gate_split_kernel, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0,
-                 s, e0, nullptr, Wg, d, E, neb, nks, static_cast<u32x4*>(wsplit));
+    if (gate_use_split(x_bf16, B, d, E)) {
+      wm = kWSplit;
+      launch_timed(gate_split_kernel, grid, dim3(256), 0, s, e0, nullptr, Wg, d, E, neb, nks,
+                   static_cast<u32x4*>(wsplit));
+    } else {
+      wm = kWBlock;
+      launch_timed(gate_block_kernel, grid, dim3(256), 0, s, e0, nullptr, Wg, d, E, neb, nks,
+                   static_cast<f32x4*>(wsplit));
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e0 = nullptr;
   }
   if (x_bf16)
     return launch_gate_mfma(static_cast<const uint16_t*>(x), Wg, static_cast<const u32x4*>(wsplit),
-                            bias, logits, B, d, E, s, e0, e1);
+                            wm, bias, logits, B, d, E, s, e0, e1);
   if (E > 32) return launch_gate_t<64, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
   if (E > 16) return launch_gate_t<32, 4>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);
   if (E > 8) return launch_gate_t<16, 2>(x, x_bf16, Wg, bias, logits, B, d, E, s, e0, e1);

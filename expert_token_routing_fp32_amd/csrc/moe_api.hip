@@ -140,8 +140,9 @@ size_t carve_forward(const moe_problem_t* p, const moe_forward_out_t* o, void* w
   t.packed = c.take(reinterpret_cast<uint16_t*>(o->packed), km * p->d * 2);
   t.hist = c.take<int32_t>(nullptr, dispatch_ws(p));
   t.H = c.take<uint16_t>(nullptr, ffn_ws(p));
-  t.wsplit = moek::gate_use_split(p->x_dtype == MOE_BF16, p->B, p->d, p->E)
-                 ? c.take<char>(nullptr, moek::gate_split_bytes(p->d, p->E))
+  t.wsplit = moek::gate_copy_bytes(p->x_dtype == MOE_BF16, p->B, p->d, p->E) > 0
+                 ? c.take<char>(nullptr, moek::gate_copy_bytes(p->x_dtype == MOE_BF16, p->B,
+                                                               p->d, p->E))
                  : nullptr;
   if (p->overflow == MOE_OVERFLOW_NEXT) {
     const size_t K2 = (size_t)(2 * p->k < p->E ? 2 * p->k : p->E);
@@ -182,8 +183,9 @@ size_t carve_ec(const moe_problem_t* p, const moe_expert_choice_out_t* o, void* 
   t.pack_w = c.take(o->pack_w, R * 4);
   t.packed = c.take(reinterpret_cast<uint16_t*>(o->packed), R * p->d * 2);
   t.H = c.take<uint16_t>(nullptr, R * p->f * 2);
-  t.wsplit = moek::gate_use_split(p->x_dtype == MOE_BF16, p->B, p->d, p->E)
-                 ? c.take<char>(nullptr, moek::gate_split_bytes(p->d, p->E))
+  t.wsplit = moek::gate_copy_bytes(p->x_dtype == MOE_BF16, p->B, p->d, p->E) > 0
+                 ? c.take<char>(nullptr, moek::gate_copy_bytes(p->x_dtype == MOE_BF16, p->B,
+                                                               p->d, p->E))
                  : nullptr;
   if (b) *b = t;
   return c.off;
@@ -804,8 +806,9 @@ extern "C" int32_t moe_check_gate_split_reach(int64_t B, int32_t d, int32_t E, i
                                               int64_t* copy_bytes) {
   if (B < 1 || d < 8 || d % 8 || E < 1 || E > kMaxE || !read_end || !copy_bytes) return -1;
   *read_end = moek::gate_split_read_end(B, d, E);
-  *copy_bytes = (int64_t)moek::gate_split_bytes(d, E);
-  return moek::gate_use_split(true, B, d, E) ? 1 : 0;
+  *copy_bytes = (int64_t)(moek::gate_use_split(true, B, d, E) ? moek::gate_split_bytes(d, E)
+                                                               : moek::gate_block_bytes(d, E));
+  return moek::gate_use_split(true, B, d, E) ? 1 : moek::gate_use_block(true, B, d, E) ? 2 : 0;
 }
 
 // ---------------------------------------------------------------------------

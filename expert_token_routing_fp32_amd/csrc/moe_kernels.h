@@ -200,9 +200,11 @@ __device__ __forceinline__ void route_token(const float* row, int E, int k, floa
 }
 
 // ---- launchers --------------------------------------------------------------
-// wsplit: device scratch of gate_split_bytes(d, E) for the split copy of the
-// router weights (bf16 x only), or null to split inside the gate kernel;
-// both give bit-identical logits.
+// wsplit: device scratch of gate_copy_bytes(...) for a copy of the router
+// weights in the gate lanes' order (bf16 x only: the split copy of bf16
+// parts, or the blocked fp32 copy, whichever gate_use_split /
+// gate_use_block picks), or null to load Wg directly; all give
+// bit-identical logits.
 // Events e0 / e1 (optional, on these launchers and the FFN's): recorded from
 // the start of the first kernel dispatch and the end of the last
 // (hipExtLaunchKernelGGL), so timing them adds no marker packets.
@@ -210,9 +212,14 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* Wg, const float*
                        float* logits, int64_t B, int d, int E, void* wsplit, hipStream_t s,
                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 size_t gate_split_bytes(int d, int E);
+size_t gate_block_bytes(int d, int E);
 bool gate_use_split(bool x_bf16, int64_t B, int d, int E);
-// host-only: exclusive end of the split copy's bytes the split-copy gate
-// launch reads at (B, d, E) (a self-check of the launch plan)
+bool gate_use_block(bool x_bf16, int64_t B, int d, int E);
+// bytes of the weight copy the forward uses at this shape (0: none)
+size_t gate_copy_bytes(bool x_bf16, int64_t B, int d, int E);
+// host-only: exclusive end of the bytes the gate launch reads from the
+// weight copy the forward would use at (B, d, E), bf16 x (a self-check of
+// the launch plan)
 int64_t gate_split_read_end(int64_t B, int d, int E);
 
 hipError_t launch_route(const float* logits, int64_t B, int E, int k, float tau,

@@ -115,17 +115,19 @@ def test_forward_is_deterministic():
 
 
 @pytest.mark.parametrize("B,d,E", [(8192, 320, 128), (16384, 328, 100), (16384, 512, 256),
-                                   (8192, 512, 160)])
+                                   (8192, 512, 160), (32768, 512, 256), (32768, 328, 200)])
 def test_forward_gate_matches_moe_gate(B, d, E):
-    """Where that fills the CUs (here: every shape) the forward splits the
-    router weights once into a bf16 copy before the gate; moe_gate splits
-    them inside its kernel.
+    """Where that fills the CUs (the first four shapes) the forward splits
+    the router weights once into a copy of bf16 parts before the gate; on
+    large gates whose grid is full already (the last two) it copies them in
+    the lanes' order as fp32 and splits in the kernel; moe_gate loads Wg
+    directly and splits inside its kernel.
     The MFMAs see the same three parts in the same order, so the logits must
     be bit-identical.  Shapes: a K range whose last 64-k stage lies past d
     (d = 320 over two K ranges), d not a multiple of 16 with E not a multiple
-    of 32, 256 experts in one workgroup, and 160 experts (5 blocks of 32
-    over workgroups of 4: the second row of workgroups has three blocks past
-    the last one, which must read only inside the split copy)."""
+    of 32, 256 experts in one workgroup, and 160 and 200 experts (5 or 7
+    blocks of 32 over workgroups of 4: the second row of workgroups has
+    blocks past the last one, which must read only inside the copy)."""
     import torch
     import expert_token_routing_fp32_amd as moe
     p = moe.make_problem(B=B, d=d, E=E, k=2, c=1.25, f=16, act="gelu", x_dtype="bf16")
@@ -135,7 +137,7 @@ def test_forward_gate_matches_moe_gate(B, d, E):
     W1 = (torch.randn(E, d, 16, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
     W2 = (torch.randn(E, 16, d, device="cuda", generator=g) * 0.25).to(torch.bfloat16)
     wp = moe.pack_weights(p, W1, None, W2)
-    say(f"[gate split] B={B} d={d} E={E}")
+    say(f"[gate copy] B={B} d={d} E={E}")
     lg = moe.gate(p, x, Wg)
     _, o = moe.forward(p, x, Wg, None, wp, outputs=True)
     torch.cuda.synchronize()
