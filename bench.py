@@ -181,8 +181,11 @@ def hbm_probe(torch) -> dict:
             "launches_per_round": 5}
 
 
-def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
-    """Bytes / FLOPs the method must move / compute for one forward, per step."""
+def algorithmic(w, keep: np.ndarray, eo: np.ndarray, dest: np.ndarray) -> dict:
+    """Bytes / FLOPs the method must move / compute for one forward, per step.
+    With bf16 tokens the forward's first GEMM reads the local rows from x
+    itself (counted in the FFN's bytes), so the pack reads the tokens with a
+    kept choice on another rank and writes only those rows."""
     B, d, E, k, f = w.B, w.d, w.E, w.k, w.f
     sx = 2 if w.x_dtype == "bf16" else 4
     K = int(eo[-1])
@@ -191,12 +194,18 @@ def algorithmic(w, keep: np.ndarray, eo: np.ndarray) -> dict:
     nmat = 3 if w.act == "swiglu" else 2
     active_local = int(sum(1 for e in range(w.e_begin, w.e_end) if eo[e + 1] > eo[e]))
     t_act = int(keep.any(axis=1).sum())
+    gather = w.x_dtype == "bf16" and B * d * 2 < (1 << 32) and w.e_end > w.e_begin
+    if gather:
+        remote = (dest >= 0) & ((dest < lo) | (dest >= hi))
+        pack_bytes = int(remote.any(axis=1).sum()) * d * sx + 2.0 * d * int(remote.sum())
+    else:
+        pack_bytes = t_act * d * sx + 2.0 * d * K
     return dict(
         gate_flop=2.0 * B * d * E,
         gate_bytes=B * d * sx + 4.0 * d * E + 4.0 * B * E,
         route_bytes=B * (4.0 * E + 8.0 * k),
         slot_bytes=B * k * (4 + 4 + 1 + 4) + 4.0 * K,
-        pack_bytes=t_act * d * sx + 2.0 * d * K,
+        pack_bytes=pack_bytes,
         ffn_flop=2.0 * d * f * nmat * Kloc,
         ffn_bytes=active_local * 2.0 * d * f * nmat + 4.0 * d * Kloc,
         combine_bytes=2.0 * d * K + B * d * sx + 8.0 * k * B,
@@ -357,7 +366,7 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
     med = {k_: float(np.median(v)) for k_, v in per.items()}
     keep = o["keep"].cpu().numpy().astype(bool)
     eo = o["expert_offset"].cpu().numpy()
-    alg = algorithmic(w, keep, eo)
+    alg = algorithmic(w, keep, eo, o["dest"].cpu().numpy())
     # the expert backward's algorithmic work: dX and the weight gradients,
     # twice the forward's FLOPs (the recomputed pre-activations are extra)
     ffn_flop = 2.0 * alg["ffn_flop"]
@@ -619,7 +628,7 @@ def main():
         torch.cuda.synchronize()
         keep = o["keep"].cpu().numpy().astype(bool)
         eo = o["expert_offset"].cpu().numpy()
-        alg = algorithmic(w, keep, eo)
+        alg = algorithmic(w, keep, eo, o["dest"].cpu().numpy())
     if shared is not None:
         # the shared expert on every token: its weights once, x read, its
         # output rows written (FFN stage) and read again by the combine

@@ -353,8 +353,12 @@ __global__ __launch_bounds__(kSlotThreads) void slot_rank_kernel(
 template <bool XBF16>
 __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
                                                    const int32_t* __restrict__ dest, int64_t B,
-                                                   int k, int d, uint16_t* __restrict__ packed) {
+                                                   int k, int d, uint16_t* __restrict__ packed,
+                                                   const int32_t* __restrict__ skip_eo, int skip_b,
+                                                   int skip_e) {
   const int cpr = d / 8;
+  // rows [lo, hi) are not written (an empty range when there is no skip)
+  const int lo = skip_eo ? skip_eo[skip_b] : 0, hi = skip_eo ? skip_eo[skip_e] : 0;
   const int c = blockIdx.x * 64 + (threadIdx.x & 63);
   const int64_t ntb = (B + 3) / 4;
   for (int64_t tb = blockIdx.y; tb < ntb; tb += gridDim.y) {
@@ -372,7 +376,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ x,
     }
     for (int j = 0; j < k; ++j) {
       const int r = dest[t * k + j];
-      if (r >= 0) __builtin_nontemporal_store(v, (u32x4*)(packed + (int64_t)r * d + c * 8));
+      if (r >= 0 && (r < lo || r >= hi))
+        __builtin_nontemporal_store(v, (u32x4*)(packed + (int64_t)r * d + c * 8));
     }
   }
 }
@@ -443,7 +448,8 @@ hipError_t launch_slots(const int32_t* idx, int64_t B, int k, int E, int C,
 }
 
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k, int d,
-                       uint16_t* packed, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                       uint16_t* packed, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                       const int32_t* skip_eo, int skip_b, int skip_e) {
   if (B == 0) return hipSuccess;
   // x: 512-column piece of the rows (fastest in dispatch order, so
   // consecutive workgroups cover consecutive pieces of the same rows);
@@ -452,10 +458,10 @@ hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t 
   const dim3 g((unsigned)((d / 8 + 63) / 64), (unsigned)(ntb < 65535 ? ntb : 65535));
   if (x_bf16)
     launch_timed(pack_kernel<true>, dim3(g), dim3(256), 0, s, e0, e1, x, dest, B, k, d,
-                 packed);
+                 packed, skip_eo, skip_b, skip_e);
   else
     launch_timed(pack_kernel<false>, dim3(g), dim3(256), 0, s, e0, e1, x, dest, B, k, d,
-                 packed);
+                 packed, skip_eo, skip_b, skip_e);
   return hipGetLastError();
 }
 

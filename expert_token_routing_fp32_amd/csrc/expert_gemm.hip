@@ -83,6 +83,11 @@ struct GemmArgs {
   const uint16_t* Z;
   int zw;
   int ldo;
+  // gather (optional): row r of the A operand is row gidx[r] of A, a matrix
+  // of src_rows rows (the forward's first GEMM reads the token rows of x
+  // through pack_src instead of a packed copy)
+  const int32_t* gidx;
+  int64_t src_rows;
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -262,14 +267,18 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   // 4 GB).
   const int drow = 8 * wave + (lane >> 3);
   const int dcol = 8 * ((lane & 7) ^ swz_key(drow));  // K offset of the lane's chunk
-  const char* abase = reinterpret_cast<const char*>(a.A + a_row0 * K);
-  // the row slice as one buffer: rows x K bf16
-  const rsrc_t ars = make_rsrc(abase, 2u * (uint32_t)rows * (uint32_t)K);
+  // the row slice as one buffer (rows x K bf16), or with a gather the whole
+  // source matrix, each lane's row through the index
+  const bool gat = a.gidx != nullptr;
+  const char* abase = reinterpret_cast<const char*>(gat ? a.A : a.A + a_row0 * K);
+  const rsrc_t ars =
+      make_rsrc(abase, 2u * (uint32_t)(gat ? a.src_rows : (int64_t)rows) * (uint32_t)K);
   uint32_t arow[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int r = 32 * i + drow;
-    arow[i] = 2u * (uint32_t)(r < rows ? r : rows - 1) * (uint32_t)K;  // past the segment: any valid row
+    const int rr = r < rows ? r : rows - 1;  // past the segment: any valid row
+    arow[i] = 2u * (uint32_t)(gat ? a.gidx[a_row0 + rr] : rr) * (uint32_t)K;
   }
   // this wavefront's weight fragments: stage G of the run at G * kWStage
   const char* wbase = reinterpret_cast<const char*>(a.Wp) +
@@ -849,7 +858,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
                              hipEvent_t ev_start, hipEvent_t ev_stop, hipEvent_t ev_mid_end,
-                             hipEvent_t ev_mid_start) {
+                             hipEvent_t ev_mid_start, const uint16_t* gx, const int32_t* gidx,
+                             int64_t gx_rows) {
   if (n_local <= 0 || rows_max <= 0) {
     hipError_t e = hipSuccess;
     for (hipEvent_t ev : {ev_start, ev_mid_end, ev_mid_start, ev_stop})
@@ -875,6 +885,11 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
   g1.n_tiles_n = geo1.n_tiles;
   g1.nk = geo1.nk;
   g1.n_local = n_local;
+  if (gidx) {
+    g1.A = gx;
+    g1.gidx = gidx;
+    g1.src_rows = gx_rows;
+  }
   hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end)
                           : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end);
   if (err != hipSuccess) return err;

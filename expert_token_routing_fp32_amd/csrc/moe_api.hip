@@ -604,14 +604,28 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
                              b.pos2, b.count1, b.eo, b.idx, b.w, b.pos, b.keep, b.dest,
                              b.pack_src, stream);
   }
-  if (e == hipSuccess)
-    e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream, nullptr, ev[4]);
+  // bf16 tokens: the first GEMM gathers the local experts' rows from x
+  // through pack_src, so the pack writes only the rows bound for the other
+  // ranks (nothing at all when every expert is local); the local rows of
+  // packed receive the expert outputs as before
+  const bool gather =
+      xb && n_local > 0 && (int64_t)p->B * p->d * 2 < ((int64_t)1 << 32);
+  if (e == hipSuccess) {
+    if (gather && p->e_begin == 0 && p->e_end == p->E) {
+      if (ev[4]) e = hipEventRecord(ev[4], stream);
+    } else {
+      e = moek::launch_pack(x, xb, b.dest, p->B, p->k, p->d, b.packed, stream, nullptr, ev[4],
+                            gather ? b.eo : nullptr, p->e_begin, p->e_end);
+    }
+  }
   // with a shared expert its GEMMs follow the routed ones inside the FFN pair
   if (p->B > 0) {
     if (e == hipSuccess)
       e = moek::launch_expert_ffn(b.packed, b.eo, p->e_begin, n_local, (int)rows_per_expert(p),
                                   rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
-                                  stream, ev[5], sh ? nullptr : ev[8], ev[6], ev[7]);
+                                  stream, ev[5], sh ? nullptr : ev[8], ev[6], ev[7],
+                                  gather ? static_cast<const uint16_t*>(x) : nullptr,
+                                  gather ? b.pack_src : nullptr, p->B);
     if (e == hipSuccess && sh)
       e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
                                   sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,

@@ -288,9 +288,12 @@ hipError_t launch_routing_stats(const float* logits, int64_t B, int E, int k, in
                                 float* token_frac, float* utilization, int32_t* dropped,
                                 double* summary, void* ws, hipStream_t s);
 
+// skip_eo (optional): packed rows [skip_eo[skip_b], skip_eo[skip_e]) are
+// not written (the forward's first GEMM gathers those rows from x itself)
 hipError_t launch_pack(const void* x, bool x_bf16, const int32_t* dest, int64_t B, int k,
                        int d, uint16_t* packed, hipStream_t s, hipEvent_t e0 = nullptr,
-                       hipEvent_t e1 = nullptr);
+                       hipEvent_t e1 = nullptr, const int32_t* skip_eo = nullptr, int skip_b = 0,
+                       int skip_e = 0);
 
 // shared (optional): a shared expert's output rows [B][d] bf16, added with
 // weight 1
@@ -324,11 +327,16 @@ hipError_t launch_pack_weights(const uint16_t* W1, const uint16_t* W3, const uin
 // last launch's end, ev_mid_end / ev_mid_start by the first launch's end and
 // the second's start (HIP fills them from the dispatches' own timestamps,
 // no marker packets); recorded as plain markers if nothing is launched.
+// gidx (optional): the first GEMM reads its rows from gx ([gx_rows][d]
+// bf16, 2 gx_rows d < 2^32) through the index -- packed row r is gx row
+// gidx[r] -- instead of from packed.
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,
                              int n_local, int rows_max, int rows_hint, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                             hipEvent_t ev_mid_end = nullptr, hipEvent_t ev_mid_start = nullptr);
+                             hipEvent_t ev_mid_end = nullptr, hipEvent_t ev_mid_start = nullptr,
+                             const uint16_t* gx = nullptr, const int32_t* gidx = nullptr,
+                             int64_t gx_rows = 0);
 
 // ---- backward pass (backward.hip, wgrad.hip, expert_gemm.hip) -------------
 hipError_t launch_combine_bwd(const void* dy, bool x_bf16, const uint16_t* ret,

@@ -364,7 +364,9 @@ typedef struct {
    * (hipExtLaunchKernelGGL start / end events; no marker packets):
    *   0 gate start          1 gate end
    *   2 route start         3 route end
-   *   4 dispatch end (the pack kernel; 3 -> 4 is the slot kernels + pack)
+   *   4 dispatch end (the pack kernel; 3 -> 4 is the slot kernels + pack;
+   *     a marker after the slot kernels when the pack has nothing to write:
+   *     bf16 tokens and every expert local, see below)
    *   5 expert FFN start    6 end of its first GEMM
    *   7 start of its second GEMM (after the routed GEMMs: the shared
    *     expert's, when there is one)      8 expert FFN end
@@ -386,6 +388,11 @@ typedef struct {
  * Parallelism and the All-to-All Bottleneck", "The Mechanism of Expert
  * Parallelism", replaced by the on-device pack and the identity return:
  * gate, route, dispatch, expert FFN (in place on the packed rows), combine.
+ * With bf16 tokens the expert FFN's first GEMM reads the local experts'
+ * rows straight from x through pack_src, and the pack writes only the rows
+ * bound for other ranks (nothing when every expert is local): the same rows
+ * in the same order as moe_dispatch + moe_expert_ffn, without the local
+ * copy's round trip through HBM.
  * Errors: as the stage calls (checks before any launch); MOE_ERR_WORKSPACE
  * when ws is smaller than moe_workspace_bytes(p, MOE_OP_FORWARD).
  *   x [B][d] x_dtype; Wg [d][E] f32; bias [E] f32 or NULL;
