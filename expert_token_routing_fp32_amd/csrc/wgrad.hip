@@ -51,6 +51,7 @@ struct KArgsDev {
   int Kc;                    // otherwise this K (split-K: group g takes rows g Kc ..
   int Ktot;                  // .. min((g + 1) Kc, Ktot) when Ktot > 0)
   int tiles_m, tiles_n;
+  int groups;
   int mode;                  // 0: fp32 store to C0 / C1; 1: (acc + add) stored as bf16 / fp32
   float* C0;
   int64_t ldc0, c0_es;
@@ -114,6 +115,16 @@ __device__ __forceinline__ void kstore4(const KArgsDev& a, int g, int m, int n, 
         *reinterpret_cast<f32x4*>(p) = v;
         return;
       }
+    } else if (a.C1 && n >= a.N0 && (a.ldc1 & 3) == 0) {
+      // all four in the second output (dW3 beside dW1)
+      const int mm = m - a.r1, nn = n - a.col1;
+      if (mm >= 0 && mm < a.M1 && nn >= 0 && nn + 3 < a.N1) {
+        float* p = a.C1 + (int64_t)g * a.c1_es + (int64_t)mm * a.ldc1 + nn;
+        if ((reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+          *reinterpret_cast<f32x4*>(p) = v;
+          return;
+        }
+      }
     }
   } else if (m < a.M0 && n + 3 < a.N0 && (a.ldc0 & 3) == 0 && (a.ld_add & 3) == 0) {
     const int64_t off = (int64_t)m * a.ldc0 + n;
@@ -146,11 +157,10 @@ __device__ __forceinline__ uint32_t kbytes(int64_t total, int64_t es, int g) {
   return left > 0 ? (uint32_t)(left < 0x7fffffffLL ? left : 0x7fffffffLL) : 0u;
 }
 
-__global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
-  __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT];
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  const int g = blockIdx.y;
-  const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+// One 256 x 256 output tile of group g.
+__device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32_t smem_lds, int g,
+                                           int tile) {
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
   const int m0 = tm * KBM, n0 = tn * KBN;
   int K;
   if (a.eo) {
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       }
     }
     // the reloads past the end still write the ring
@@ -236,36 +246,110 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][r] is C[m][n] with m = m0 + 128 wm + 32 i + 8 (r / 4)
-  // + 4 lh + r % 4 and n = n0 + 128 wn + 32 j + l32.  Each 32 x 32 block goes
-  // through a wavefront-private 4 KB of LDS (the ring is free now): the
-  // unrolled part only moves registers to LDS, and the stores, with their
-  // bounds and destinations, run in a plain loop of 16 rounds in which lanes
-  // write consecutive columns.
+  // epilogue: the B fragment is the matrix instruction's first operand, so
+  // acc[i][j] holds the block transposed: registers 4q .. 4q + 3 of lane l
+  // are C[m][n .. n + 3] with m = m0 + 128 wm + 32 i + l % 32 and n = n0 +
+  // 128 wn + 32 j + 8 q + 4 (l / 32) -- four consecutive columns of one row,
+  // stored straight from the accumulators as one 16-byte piece (no LDS
+  // staging); the two lanes of a row write 32 contiguous bytes.
+  // The common case -- a mode-0 tile wholly inside one of the two outputs,
+  // rows 16-byte aligned -- stores unconditionally; other tiles go element
+  // by element through kstore4.
+  float* fbase = nullptr;
+  int64_t fld = 0;
+  if (a.mode == 0 && m0 + KBM <= a.M0) {
+    if (n0 + KBN <= a.N0 && (a.ldc0 & 3) == 0) {
+      fbase = a.C0 + (int64_t)g * a.c0_es + (int64_t)m0 * a.ldc0 + n0;
+      fld = a.ldc0;
+    } else if (a.C1 && n0 >= a.N0 && (a.ldc1 & 3) == 0 && m0 - a.r1 >= 0 &&
+               m0 + KBM - a.r1 <= a.M1 && n0 - a.col1 >= 0 && n0 + KBN - a.col1 <= a.N1) {
+      fbase = a.C1 + (int64_t)g * a.c1_es + (int64_t)(m0 - a.r1) * a.ldc1 + (n0 - a.col1);
+      fld = a.ldc1;
+    }
+    if (reinterpret_cast<uintptr_t>(fbase) & 15u) fbase = nullptr;
+  }
+  if (fbase) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mr = 128 * wm + 32 * i + l32, nc = 128 * wn + 32 * j + 4 * lh;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]),
+                           kacc(acc[i][j][4 * q + 2]), kacc(acc[i][j][4 * q + 3])};
+          *reinterpret_cast<f32x4*>(fbase + (int64_t)mr * fld + nc + 8 * q) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    return;
+  }
+  // other tiles: each 32 x 32 block through a wavefront-private 4 KB of LDS
+  // (the ring is free now); the unrolled part only moves registers to LDS,
+  // and the stores, with their bounds and destinations, run in a plain loop
+  // of 4 rounds in which lanes write consecutive columns
   float* stg = reinterpret_cast<float*>(smem) + wave * 1024;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        stg[(8 * (r >> 2) + 4 * lh + (r & 3)) * 32 + l32] = kacc(acc[i][j][r]);
-      // LDS operations of one wavefront complete in order; the barriers keep
-      // the compiler from moving the reads above the writes (or the next
-      // block's writes above these reads)
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(stg + l32 * 32 + 8 * q + 4 * lh) =
+            f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]), kacc(acc[i][j][4 * q + 2]),
+                  kacc(acc[i][j][4 * q + 3])};
+      // LDS operations of one wavefront complete in order; the compiler
+      // barrier keeps the reads below the writes (and the next block's
+      // writes below these reads)
+      asm volatile("" ::: "memory");
       const int mb = m0 + 128 * wm + 32 * i, nb = n0 + 128 * wn + 32 * j;
-      // four rounds: lane -> row 8 q + lane / 8, columns 4 (lane % 8) .. + 3
+      // four rounds: lane -> row 8 r + lane / 8, columns 4 (lane % 8) .. + 3
 #pragma unroll 1
-      for (int q = 0; q < 4; ++q) {
-        const int row = 8 * q + (lane >> 3), c4 = 4 * (lane & 7);
+      for (int r = 0; r < 4; ++r) {
+        const int row = 8 * r + (lane >> 3), c4 = 4 * (lane & 7);
         const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * 32 + c4);
         kstore4(a, g, mb + row, nb + c4, v);
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      asm volatile("" ::: "memory");
     }
+  // every wavefront is done with its staging area before the next tile's
+  // loads fill the ring (all wavefronts of a tile take the same path)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Persistent: one workgroup per CU walks the tiles, ordered (group, tile)
+// and cut into 8 equal contiguous ranges, one per XCD (workgroups are dealt
+// round-robin over the XCDs), so an XCD works on few groups at a time and
+// their operands are shared through its L2.  (One launch of a workgroup per
+// tile left a fifth of the CUs idle: the in-order dispatch of workgroups
+// waits for the XCD whose turn it is.)
+__global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
+  __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const int tiles = a.tiles_m * a.tiles_n;
+  const int64_t total = (int64_t)tiles * a.groups;
+  const int G = gridDim.x, b = blockIdx.x;
+  int64_t t0, t1, step;
+  if (G >= 8) {
+    const int x = b % 8, j = b / 8, nx = G / 8;
+    if (j >= nx) return;
+    t0 = total * x / 8 + j;
+    t1 = total * (x + 1) / 8;
+    step = nx;
+  } else {
+    t0 = b;
+    t1 = total;
+    step = G;
+  }
+  for (int64_t t = t0; t < t1; t += step) {
+    // (each tile ends its stage loop with a barrier, after which no
+    // wavefront reads the ring; the epilogue's stores drain while the next
+    // tile's loads are issued)
+    kgemm_tile(a, smem, smem_lds, (int)(t / tiles), (int)(t % tiles));
+  }
 }
 
 }  // namespace
@@ -320,8 +404,15 @@ hipError_t launch_kgemm(const KGemm& q, hipStream_t s) {
     return hipErrorInvalidValue;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > 2147483647 || q.groups > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles, (unsigned)q.groups);
-  hipLaunchKernelGGL(kgemm_kernel, grid, dim3(256), 0, s, a);
+  a.groups = q.groups;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int64_t total = tiles * q.groups;
+  const int grid = (int)(total < cus ? total : cus);
+  hipLaunchKernelGGL(kgemm_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
