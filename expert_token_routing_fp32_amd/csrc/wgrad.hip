@@ -268,6 +268,42 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
     }
     if (reinterpret_cast<uintptr_t>(fbase) & 15u) fbase = nullptr;
   }
+  // mode 1 (out = acc + add, stored as bf16 or fp32) on a full tile with
+  // 16-byte aligned rows: unconditional vector loads and stores too
+  if (a.mode == 1 && m0 + KBM <= a.M0 && n0 + KBN <= a.N0 && (a.ldc0 & 3) == 0 &&
+      (!a.add || (a.ld_add & 3) == 0)) {
+    const float* ab = a.add ? a.add + (int64_t)m0 * a.ld_add + n0 : nullptr;
+    const int64_t o0 = (int64_t)m0 * a.ldc0 + n0;
+    const bool al = (!ab || (reinterpret_cast<uintptr_t>(ab) & 15u) == 0) &&
+                    (a.x_bf16 ? (reinterpret_cast<uintptr_t>(static_cast<uint16_t*>(a.xo) + o0) & 7u) == 0
+                              : (reinterpret_cast<uintptr_t>(static_cast<float*>(a.xo) + o0) & 15u) == 0);
+    if (al) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int mr = 128 * wm + 32 * i + l32, nc = 128 * wn + 32 * j + 4 * lh;
+          f32x4 ad[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ad[q] = ab ? *reinterpret_cast<const f32x4*>(ab + (int64_t)mr * a.ld_add + nc + 8 * q)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]),
+                                  kacc(acc[i][j][4 * q + 2]), kacc(acc[i][j][4 * q + 3])} + ad[q];
+            const int64_t off = o0 + (int64_t)mr * a.ldc0 + nc + 8 * q;
+            if (a.x_bf16)
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.xo) + off) =
+                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            else
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.xo) + off) = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      return;
+    }
+  }
   if (fbase) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
