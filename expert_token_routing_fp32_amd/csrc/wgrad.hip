@@ -35,9 +35,9 @@ typedef __attribute__((address_space(3))) void k_lds_void_t;
 
 constexpr int KBM = 256, KBN = 256;
 constexpr int KPL = 256;                   // 16-byte chunks per k group in LDS
-constexpr int KSLOT = 2 * 4 * KPL * 16;    // one stage: A then B, 32 KB
-constexpr int KR = 4;                      // ring slots
-constexpr int KLOADS = 8;                  // loads per wavefront per stage
+constexpr int KSLOT = 4 * KPL * 16;        // one stage of A in LDS: 16 KB
+constexpr int KR = 4;                      // ring slots (LDS for A, registers for B)
+constexpr int KLOADS = 4 + 8;              // loads per wavefront per stage: A to LDS, B
 
 struct KArgsDev {
   const uint16_t* A[6];
@@ -181,24 +181,53 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lo16 = 16u * lane;
 
-  // Stage st (clamped to the last one: the issues past the end reload it
-  // into a slot nobody reads again, so every step issues the same loads):
-  // wavefront `wave` loads k group `wave` of the stage, rows m0 .. m0 + 255
-  // of A and n0 .. n0 + 255 of B, as 4 + 4 loads of 64 chunks.
-  auto issue = [&](int st, int slot) {
-    const int sc = st < nst ? st : nst - 1;
-    const int sgm = sc / nks, kg = (sc - sgm * nks) * 4 + wave;
-    const rsrc_t ra = make_rsrc(a.A[sgm] + (int64_t)g * a.a_es, kbytes(a.a_bytes, a.a_es, g));
-    const rsrc_t rb = make_rsrc(a.Bm[sgm] + (int64_t)g * a.b_es, kbytes(a.b_bytes, a.b_es, g));
-    const uint32_t la = smem_lds + slot * KSLOT + wave * KPL * 16;
-    const uint32_t lb = la + 4 * KPL * 16;
-    const uint32_t oa = 16u * ((uint32_t)kg * (uint32_t)a.a_w + (uint32_t)m0);
-    const uint32_t ob = 16u * ((uint32_t)kg * (uint32_t)a.b_w + (uint32_t)n0);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) k_dma16(ra, oa + 1024u * p + lo16, la + 1024 * p);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) k_dma16(rb, ob + 1024u * p + lo16, lb + 1024 * p);
-  };
+  int csg = -1;
+  rsrc_t ra, rb;
+  const int l32 = lane & 31, lh = lane >> 5;
+  // B fragments of a stage in registers: [slot][half][column block]
+  u32x4 bq[KR][2][4];
+  // Issue of stage ST into slot SLOT (clamped to the last stage: the issues
+  // past the end reload it, and nobody reads it again, so every stage
+  // issues the same loads), in 12 parts: A's k group `wave` (rows m0 ..
+  // m0 + 255, parts 0-3, 64 chunks each) into LDS slot SLOT, then this
+  // wavefront's B fragments (columns n0 + 128 wn .. + 127, the lane's k
+  // groups 2 h + lh; parts 4-11) straight into registers bq[SLOT].  KSEG
+  // sets the stage's descriptors and offsets; KPART issues one part.
+  // The segment's descriptors are built when the segment changes, not on
+  // every stage: their base pointers come from the kernel arguments through
+  // scalar loads whose wait would otherwise open every stage.
+  uint32_t ia_la = 0, ia_oa = 0, ia_kq = 0;
+#define KSEG(ST, SLOT)                                                                 \
+  {                                                                                    \
+    const int sc_ = (ST) < nst ? (ST) : nst - 1;                                       \
+    const int sgm_ = sc_ / nks;                                                        \
+    ia_kq = (uint32_t)(sc_ - sgm_ * nks) * 4;                                          \
+    if (sgm_ != csg) {                                                                 \
+      ra = make_rsrc(a.A[sgm_] + (int64_t)g * a.a_es, kbytes(a.a_bytes, a.a_es, g));   \
+      rb = make_rsrc(a.Bm[sgm_] + (int64_t)g * a.b_es, kbytes(a.b_bytes, a.b_es, g));  \
+      csg = sgm_;                                                                      \
+    }                                                                                  \
+    ia_la = smem_lds + (SLOT) * KSLOT + wave * KPL * 16;                               \
+    ia_oa = 16u * ((ia_kq + wave) * (uint32_t)a.a_w + (uint32_t)m0) + lo16;            \
+  }
+#define KPART(Q, SLOT)                                                                 \
+  {                                                                                    \
+    if ((Q) < 4) {                                                                     \
+      k_dma16(ra, ia_oa + 1024u * ((Q) & 3), ia_la + 1024 * ((Q) & 3));                \
+    } else {                                                                           \
+      constexpr int h_ = ((Q) - 4) >> 2, j_ = ((Q) - 4) & 3;                           \
+      bq[SLOT][h_][j_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128( \
+          rb, 16u * ((ia_kq + 2 * h_ + lh) * (uint32_t)a.b_w +                         \
+                     (uint32_t)(n0 + 128 * wn + 32 * j_ + l32)), 0, 0));                \
+    }                                                                                  \
+  }
+#define KISSUE(ST, SLOT)                                                               \
+  {                                                                                    \
+    KSEG(ST, SLOT)                                                                     \
+    KPART(0, SLOT) KPART(1, SLOT) KPART(2, SLOT) KPART(3, SLOT)                        \
+    KPART(4, SLOT) KPART(5, SLOT) KPART(6, SLOT) KPART(7, SLOT)                        \
+    KPART(8, SLOT) KPART(9, SLOT) KPART(10, SLOT) KPART(11, SLOT)                      \
+  }
 
   kf32x16 acc[4][4];
 #pragma unroll
@@ -208,43 +237,79 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int l32 = lane & 31, lh = lane >> 5;
   if (nst > 0) {
+    // A fragments: fa[0] the current stage's first half, read during the
+    // previous stage; fa[1] its second half
+    kb16x8 fa[2][4];
+    const int abase = wm * 128 + l32;
+    // Stage ST in slot U: wait until stages ST and ST + 1 have landed (one
+    // stage's loads outstanding: they complete in issue order), a barrier
+    // that makes every wavefront's A parts visible and retires the reads of
+    // the slot the issue below refills; then 8 groups of 4 MFMAs (half h,
+    // row block i) with, after group (h, i), the LDS read of the fragment
+    // that group frees -- the second half's during the first, the next
+    // stage's first half during the second -- and parts of the issue of
+    // stage ST + KR - 1, spread so that a load whose issue stalls does not
+    // hold the matrix core for long.
+#define KGROUP(U, H, I, P0, P1)                                                        \
+  {                                                                                    \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                   \
+      acc[I][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                            \
+          __builtin_bit_cast(kb16x8, bq[U][H][j_]), fa[H][I], acc[I][j_], 0, 0, 0);    \
+    if ((H) == 0)                                                                      \
+      fa[1][I] = __builtin_bit_cast(kb16x8, sa_[(2 + lh) * KPL + abase + (I) * 32]);   \
+    else                                                                               \
+      fa[0][I] = __builtin_bit_cast(kb16x8, sn_[lh * KPL + abase + (I) * 32]);          \
+    KPART(P0, ((U) + KR - 1) % KR)                                                     \
+    if ((P1) >= 0) KPART(P1, ((U) + KR - 1) % KR)                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+  }
+#define KSTAGE(ST, U)                                                                  \
+  {                                                                                    \
+    k_wait_vmcnt<(KR - 3) * KLOADS>();                                                 \
+    asm volatile("" ::: "memory");                                                     \
+    __builtin_amdgcn_s_barrier();                                                      \
+    asm volatile("" ::: "memory");                                                     \
+    KSEG((ST) + KR - 1, ((U) + KR - 1) % KR)                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    const u32x4* sa_ = reinterpret_cast<const u32x4*>(smem + (U) * KSLOT);             \
+    const u32x4* sn_ = reinterpret_cast<const u32x4*>(smem + (((U) + 1) % KR) * KSLOT); \
+    KGROUP(U, 0, 0, 0, 1) KGROUP(U, 0, 1, 2, 3) KGROUP(U, 0, 2, 4, 5)                   \
+    KGROUP(U, 0, 3, 6, -1) KGROUP(U, 1, 0, 7, 8) KGROUP(U, 1, 1, 9, -1)                \
+    KGROUP(U, 1, 2, 10, -1) KGROUP(U, 1, 3, 11, -1)                                    \
+  }
+    KISSUE(0, 0)
+    KISSUE(1, 1)
+    KISSUE(2, 2)
+    // stage 0 has landed (stage 1 may not yet): the first half's fragments
+    k_wait_vmcnt<2 * KLOADS>();
+    __builtin_amdgcn_s_barrier();
+    {
+      const u32x4* s0_ = reinterpret_cast<const u32x4*>(smem);
 #pragma unroll
-    for (int p = 0; p < KR - 1; ++p) issue(p, p);
-    for (int st = 0; st < nst; ++st) {
-      // stage st has landed (this wavefront's loads) once at most two
-      // stages' loads are outstanding; the barrier makes every wavefront's
-      // part visible and retires the reads of slot (st - 1) % KR
-      k_wait_vmcnt<(KR - 2) * KLOADS>();
-      // compiler barriers: no LDS read of this stage moves above the
-      // hardware barrier, no read of the last stage below it
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      issue(st + KR - 1, (st + KR - 1) % KR);
-      const u32x4* sa = reinterpret_cast<const u32x4*>(smem + (st % KR) * KSLOT);
-      const u32x4* sb = sa + 4 * KPL;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kgl = 2 * s2 + lh;  // this lane's k group in the stage
-        kb16x8 fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          fa[i] = __builtin_bit_cast(kb16x8, sa[kgl * KPL + wm * 128 + i * 32 + l32]);
-          fb[i] = __builtin_bit_cast(kb16x8, sb[kgl * KPL + wn * 128 + i * 32 + l32]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) fa[0][i] = __builtin_bit_cast(kb16x8, s0_[lh * KPL + abase + i * 32]);
     }
+    // whole groups of KR stages (register slots fixed at compile time), then
+    // the remainder
+    const int nfull = nst - nst % KR;
+    for (int st0 = 0; st0 < nfull; st0 += KR) {
+      KSTAGE(st0, 0)
+      KSTAGE(st0 + 1, 1)
+      KSTAGE(st0 + 2, 2)
+      KSTAGE(st0 + 3, 3)
+    }
+    if (nst - nfull > 0) KSTAGE(nfull, 0)
+    if (nst - nfull > 1) KSTAGE(nfull + 1, 1)
+    if (nst - nfull > 2) KSTAGE(nfull + 2, 2)
+#undef KSTAGE
+#undef KGROUP
     // the reloads past the end still write the ring
     k_wait_vmcnt<0>();
     __syncthreads();
   }
+#undef KISSUE
+#undef KPART
+#undef KSEG
 
   // epilogue: the B fragment is the matrix instruction's first operand, so
   // acc[i][j] holds the block transposed: registers 4q .. 4q + 3 of lane l
