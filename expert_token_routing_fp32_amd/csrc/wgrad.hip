@@ -37,7 +37,9 @@ constexpr int KBM = 256, KBN = 256;
 constexpr int KPL = 256;                   // 16-byte chunks per k group in LDS
 constexpr int KSLOT = 4 * KPL * 16;        // one stage of A in LDS: 16 KB
 constexpr int KR = 4;                      // ring slots (LDS for A, registers for B)
-constexpr int KLOADS = 4 + 8;              // loads per wavefront per stage: A to LDS, B
+constexpr int KLOADS = 4 + 4;              // loads per wavefront per stage: A to LDS, B
+constexpr int KSTG_ROW = 64 + 4;           // floats per row of the epilogue staging (padded)
+constexpr int KSTG_WAVE = 32 * KSTG_ROW * 4;  // a wavefront's staging area: 32 rows x 64 columns
 
 struct KArgsDev {
   const uint16_t* A[6];
@@ -157,169 +159,46 @@ __device__ __forceinline__ uint32_t kbytes(int64_t total, int64_t es, int g) {
   return left > 0 ? (uint32_t)(left < 0x7fffffffLL ? left : 0x7fffffffLL) : 0u;
 }
 
-// One 256 x 256 output tile of group g.
-__device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32_t smem_lds, int g,
-                                           int tile) {
-  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
-  const int m0 = tm * KBM, n0 = tn * KBN;
+// A tile: 256 x 256 outputs of group g at (m0, n0), nst stages of 32 k
+// (nks per segment).
+struct KTile {
+  int g, m0, n0, nks, nst;
+};
+
+__device__ __forceinline__ KTile ktile(const KArgsDev& a, int64_t t) {
+  const int tiles = a.tiles_m * a.tiles_n;
+  KTile r;
+  r.g = (int)(t / tiles);
+  const int tile = (int)(t % tiles);
+  r.m0 = tile / a.tiles_n * KBM;
+  r.n0 = tile % a.tiles_n * KBN;
   int K;
   if (a.eo) {
-    K = a.eo[a.e_begin + g + 1] - a.eo[a.e_begin + g];
+    K = a.eo[a.e_begin + r.g + 1] - a.eo[a.e_begin + r.g];
     K = (K + 31) / 32 * 32;
   } else {
     K = a.Kc;
     if (a.Ktot > 0) {
-      const int left = a.Ktot - g * a.Kc;
+      const int left = a.Ktot - r.g * a.Kc;
       K = left < K ? left : K;
       K = K > 0 ? K : 0;
     }
   }
-  const int nks = K / 32;  // stages per segment
-  const int nst = nks * a.nseg;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t lo16 = 16u * lane;
+  r.nks = K / 32;
+  r.nst = r.nks * a.nseg;
+  return r;
+}
 
-  int csg = -1;
-  rsrc_t ra, rb;
+// Epilogue of the tile (g, m0, n0): the B fragment is the matrix
+// instruction's first operand, so acc[i][j] holds the block transposed:
+// registers 4q .. 4q + 3 of lane l are C[m][n .. n + 3] with m = m0 + 32 i +
+// l % 32 and n = n0 + 64 wave + 32 j + 8 q + 4 (l / 32) -- four consecutive
+// columns of one row.  The common case -- a mode-0 tile wholly inside one of
+// the two outputs, rows 16-byte aligned -- stores unconditionally; other
+// tiles go element by element through kstore4.
+__device__ __forceinline__ void kgemm_epilogue(const KArgsDev& a, char* smem, kf32x16 (&acc)[8][2],
+                                               int g, int m0, int n0, int wave, int lane) {
   const int l32 = lane & 31, lh = lane >> 5;
-  // B fragments of a stage in registers: [slot][half][column block]
-  u32x4 bq[KR][2][4];
-  // Issue of stage ST into slot SLOT (clamped to the last stage: the issues
-  // past the end reload it, and nobody reads it again, so every stage
-  // issues the same loads), in 12 parts: A's k group `wave` (rows m0 ..
-  // m0 + 255, parts 0-3, 64 chunks each) into LDS slot SLOT, then this
-  // wavefront's B fragments (columns n0 + 128 wn .. + 127, the lane's k
-  // groups 2 h + lh; parts 4-11) straight into registers bq[SLOT].  KSEG
-  // sets the stage's descriptors and offsets; KPART issues one part.
-  // The segment's descriptors are built when the segment changes, not on
-  // every stage: their base pointers come from the kernel arguments through
-  // scalar loads whose wait would otherwise open every stage.
-  uint32_t ia_la = 0, ia_oa = 0, ia_kq = 0;
-#define KSEG(ST, SLOT)                                                                 \
-  {                                                                                    \
-    const int sc_ = (ST) < nst ? (ST) : nst - 1;                                       \
-    const int sgm_ = sc_ / nks;                                                        \
-    ia_kq = (uint32_t)(sc_ - sgm_ * nks) * 4;                                          \
-    if (sgm_ != csg) {                                                                 \
-      ra = make_rsrc(a.A[sgm_] + (int64_t)g * a.a_es, kbytes(a.a_bytes, a.a_es, g));   \
-      rb = make_rsrc(a.Bm[sgm_] + (int64_t)g * a.b_es, kbytes(a.b_bytes, a.b_es, g));  \
-      csg = sgm_;                                                                      \
-    }                                                                                  \
-    ia_la = smem_lds + (SLOT) * KSLOT + wave * KPL * 16;                               \
-    ia_oa = 16u * ((ia_kq + wave) * (uint32_t)a.a_w + (uint32_t)m0) + lo16;            \
-  }
-#define KPART(Q, SLOT)                                                                 \
-  {                                                                                    \
-    if ((Q) < 4) {                                                                     \
-      k_dma16(ra, ia_oa + 1024u * ((Q) & 3), ia_la + 1024 * ((Q) & 3));                \
-    } else {                                                                           \
-      constexpr int h_ = ((Q) - 4) >> 2, j_ = ((Q) - 4) & 3;                           \
-      bq[SLOT][h_][j_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128( \
-          rb, 16u * ((ia_kq + 2 * h_ + lh) * (uint32_t)a.b_w +                         \
-                     (uint32_t)(n0 + 128 * wn + 32 * j_ + l32)), 0, 0));                \
-    }                                                                                  \
-  }
-#define KISSUE(ST, SLOT)                                                               \
-  {                                                                                    \
-    KSEG(ST, SLOT)                                                                     \
-    KPART(0, SLOT) KPART(1, SLOT) KPART(2, SLOT) KPART(3, SLOT)                        \
-    KPART(4, SLOT) KPART(5, SLOT) KPART(6, SLOT) KPART(7, SLOT)                        \
-    KPART(8, SLOT) KPART(9, SLOT) KPART(10, SLOT) KPART(11, SLOT)                      \
-  }
-
-  kf32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  if (nst > 0) {
-    // A fragments: fa[0] the current stage's first half, read during the
-    // previous stage; fa[1] its second half
-    kb16x8 fa[2][4];
-    const int abase = wm * 128 + l32;
-    // Stage ST in slot U: wait until stages ST and ST + 1 have landed (one
-    // stage's loads outstanding: they complete in issue order), a barrier
-    // that makes every wavefront's A parts visible and retires the reads of
-    // the slot the issue below refills; then 8 groups of 4 MFMAs (half h,
-    // row block i) with, after group (h, i), the LDS read of the fragment
-    // that group frees -- the second half's during the first, the next
-    // stage's first half during the second -- and parts of the issue of
-    // stage ST + KR - 1, spread so that a load whose issue stalls does not
-    // hold the matrix core for long.
-#define KGROUP(U, H, I, P0, P1)                                                        \
-  {                                                                                    \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                   \
-      acc[I][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                            \
-          __builtin_bit_cast(kb16x8, bq[U][H][j_]), fa[H][I], acc[I][j_], 0, 0, 0);    \
-    if ((H) == 0)                                                                      \
-      fa[1][I] = __builtin_bit_cast(kb16x8, sa_[(2 + lh) * KPL + abase + (I) * 32]);   \
-    else                                                                               \
-      fa[0][I] = __builtin_bit_cast(kb16x8, sn_[lh * KPL + abase + (I) * 32]);          \
-    KPART(P0, ((U) + KR - 1) % KR)                                                     \
-    if ((P1) >= 0) KPART(P1, ((U) + KR - 1) % KR)                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
-  }
-#define KSTAGE(ST, U)                                                                  \
-  {                                                                                    \
-    k_wait_vmcnt<(KR - 3) * KLOADS>();                                                 \
-    asm volatile("" ::: "memory");                                                     \
-    __builtin_amdgcn_s_barrier();                                                      \
-    asm volatile("" ::: "memory");                                                     \
-    KSEG((ST) + KR - 1, ((U) + KR - 1) % KR)                                           \
-    __builtin_amdgcn_sched_barrier(0);                                                 \
-    const u32x4* sa_ = reinterpret_cast<const u32x4*>(smem + (U) * KSLOT);             \
-    const u32x4* sn_ = reinterpret_cast<const u32x4*>(smem + (((U) + 1) % KR) * KSLOT); \
-    KGROUP(U, 0, 0, 0, 1) KGROUP(U, 0, 1, 2, 3) KGROUP(U, 0, 2, 4, 5)                   \
-    KGROUP(U, 0, 3, 6, -1) KGROUP(U, 1, 0, 7, 8) KGROUP(U, 1, 1, 9, -1)                \
-    KGROUP(U, 1, 2, 10, -1) KGROUP(U, 1, 3, 11, -1)                                    \
-  }
-    KISSUE(0, 0)
-    KISSUE(1, 1)
-    KISSUE(2, 2)
-    // stage 0 has landed (stage 1 may not yet): the first half's fragments
-    k_wait_vmcnt<2 * KLOADS>();
-    __builtin_amdgcn_s_barrier();
-    {
-      const u32x4* s0_ = reinterpret_cast<const u32x4*>(smem);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[0][i] = __builtin_bit_cast(kb16x8, s0_[lh * KPL + abase + i * 32]);
-    }
-    // whole groups of KR stages (register slots fixed at compile time), then
-    // the remainder
-    const int nfull = nst - nst % KR;
-    for (int st0 = 0; st0 < nfull; st0 += KR) {
-      KSTAGE(st0, 0)
-      KSTAGE(st0 + 1, 1)
-      KSTAGE(st0 + 2, 2)
-      KSTAGE(st0 + 3, 3)
-    }
-    if (nst - nfull > 0) KSTAGE(nfull, 0)
-    if (nst - nfull > 1) KSTAGE(nfull + 1, 1)
-    if (nst - nfull > 2) KSTAGE(nfull + 2, 2)
-#undef KSTAGE
-#undef KGROUP
-    // the reloads past the end still write the ring
-    k_wait_vmcnt<0>();
-    __syncthreads();
-  }
-#undef KISSUE
-#undef KPART
-#undef KSEG
-
-  // epilogue: the B fragment is the matrix instruction's first operand, so
-  // acc[i][j] holds the block transposed: registers 4q .. 4q + 3 of lane l
-  // are C[m][n .. n + 3] with m = m0 + 128 wm + 32 i + l % 32 and n = n0 +
-  // 128 wn + 32 j + 8 q + 4 (l / 32) -- four consecutive columns of one row,
-  // stored straight from the accumulators as one 16-byte piece (no LDS
-  // staging); the two lanes of a row write 32 contiguous bytes.
-  // The common case -- a mode-0 tile wholly inside one of the two outputs,
-  // rows 16-byte aligned -- stores unconditionally; other tiles go element
-  // by element through kstore4.
   float* fbase = nullptr;
   int64_t fld = 0;
   if (a.mode == 0 && m0 + KBM <= a.M0) {
@@ -343,21 +222,25 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
                     (a.x_bf16 ? (reinterpret_cast<uintptr_t>(static_cast<uint16_t*>(a.xo) + o0) & 7u) == 0
                               : (reinterpret_cast<uintptr_t>(static_cast<float*>(a.xo) + o0) & 15u) == 0);
     if (al) {
+      // opaque, so that the per-row offsets are not hoisted out of the tile
+      // loop (and spilled)
+      int64_t ldo = a.ldc0, lda = a.ld_add;
+      asm volatile("" : "+s"(ldo), "+s"(lda));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int mr = 128 * wm + 32 * i + l32, nc = 128 * wn + 32 * j + 4 * lh;
+        for (int j = 0; j < 2; ++j) {
+          const int mr = 32 * i + l32, nc = 64 * wave + 32 * j + 4 * lh;
           f32x4 ad[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            ad[q] = ab ? *reinterpret_cast<const f32x4*>(ab + (int64_t)mr * a.ld_add + nc + 8 * q)
+            ad[q] = ab ? *reinterpret_cast<const f32x4*>(ab + (int64_t)mr * lda + nc + 8 * q)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4 v = f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]),
                                   kacc(acc[i][j][4 * q + 2]), kacc(acc[i][j][4 * q + 3])} + ad[q];
-            const int64_t off = o0 + (int64_t)mr * a.ldc0 + nc + 8 * q;
+            const int64_t off = o0 + (int64_t)mr * ldo + nc + 8 * q;
             if (a.x_bf16)
               *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.xo) + off) =
                   u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -370,30 +253,55 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
     }
   }
   if (fbase) {
+    // Each block row i (32 rows x this wavefront's 64 columns) goes through
+    // the wavefront's own staging area in LDS (outside the ring, so no
+    // barrier): written in the accumulator layout, read back as rows, and
+    // stored 4 rows x 256 contiguous bytes per instruction.  Stored straight
+    // from the accumulators, every instruction would touch 32 rows with 32
+    // bytes each, and the stores, issued at a fraction of the rate, would
+    // take as long as a quarter of the tile's matrix work.  LDS operations
+    // of one wavefront complete in order, so the reads see the writes and
+    // the next block's writes wait for the reads.
+    float* stg = reinterpret_cast<float*>(smem + KR * KSLOT + wave * KSTG_WAVE);
+    // opaque, so that the per-row offsets are not all hoisted out of the
+    // tile loop (and spilled)
+    asm volatile("" : "+s"(fld));
+    const int rr = lane >> 4, cc = 4 * (lane & 15);
+    float* ob = fbase + 64 * wave + (int64_t)rr * fld + cc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int mr = 128 * wm + 32 * i + l32, nc = 128 * wn + 32 * j + 4 * lh;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]),
-                           kacc(acc[i][j][4 * q + 2]), kacc(acc[i][j][4 * q + 3])};
-          *reinterpret_cast<f32x4*>(fbase + (int64_t)mr * fld + nc + 8 * q) = v;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(stg + l32 * KSTG_ROW + 32 * j + 8 * q + 4 * lh) =
+              f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]), kacc(acc[i][j][4 * q + 2]),
+                    kacc(acc[i][j][4 * q + 3])};
+      asm volatile("" ::: "memory");
+      // all eight reads, then the eight stores (one read per store, each
+      // waited for, would serialize the LDS latency)
+      f32x4 rv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        rv[t] = *reinterpret_cast<const f32x4*>(stg + (4 * t + rr) * KSTG_ROW + cc);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<f32x4*>(ob + (int64_t)(32 * i + 4 * t) * fld) = rv[t];
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
     return;
   }
-  // other tiles: each 32 x 32 block through a wavefront-private 4 KB of LDS
-  // (the ring is free now); the unrolled part only moves registers to LDS,
-  // and the stores, with their bounds and destinations, run in a plain loop
-  // of 4 rounds in which lanes write consecutive columns
-  float* stg = reinterpret_cast<float*>(smem) + wave * 1024;
+  // other tiles: each 32 x 32 block through the wavefront's staging area;
+  // the unrolled part only moves registers to LDS, and the stores, with
+  // their bounds and destinations, run in a plain loop of 4 rounds in which
+  // lanes write consecutive columns
+  float* stg = reinterpret_cast<float*>(smem + KR * KSLOT + wave * KSTG_WAVE);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(stg + l32 * 32 + 8 * q + 4 * lh) =
@@ -403,7 +311,7 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
       // barrier keeps the reads below the writes (and the next block's
       // writes below these reads)
       asm volatile("" ::: "memory");
-      const int mb = m0 + 128 * wm + 32 * i, nb = n0 + 128 * wn + 32 * j;
+      const int mb = m0 + 32 * i, nb = n0 + 64 * wave + 32 * j;
       // four rounds: lane -> row 8 r + lane / 8, columns 4 (lane % 8) .. + 3
 #pragma unroll 1
       for (int r = 0; r < 4; ++r) {
@@ -413,13 +321,8 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
       }
       asm volatile("" ::: "memory");
     }
-  // every wavefront is done with its staging area before the next tile's
-  // loads fill the ring (all wavefronts of a tile take the same path)
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
+
 
 // Persistent: one workgroup per CU walks the tiles, ordered (group, tile)
 // and cut into 8 equal contiguous ranges, one per XCD (workgroups are dealt
@@ -428,7 +331,7 @@ __device__ __forceinline__ void kgemm_tile(const KArgsDev& a, char* smem, uint32
 // tile left a fifth of the CUs idle: the in-order dispatch of workgroups
 // waits for the XCD whose turn it is.)
 __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
-  __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT];
+  __shared__ __attribute__((aligned(16))) char smem[KR * KSLOT + 4 * KSTG_WAVE];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const int tiles = a.tiles_m * a.tiles_n;
   const int64_t total = (int64_t)tiles * a.groups;
@@ -445,12 +348,157 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
     t1 = total;
     step = G;
   }
-  for (int64_t t = t0; t < t1; t += step) {
-    // (each tile ends its stage loop with a barrier, after which no
-    // wavefront reads the ring; the epilogue's stores drain while the next
-    // tile's loads are issued)
-    kgemm_tile(a, smem, smem_lds, (int)(t / tiles), (int)(t % tiles));
+  if (t0 >= t1) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lo16 = 16u * lane;
+  const int l32 = lane & 31, lh = lane >> 5;
+  KTile ct = ktile(a, t0);
+  // The segment's descriptors are built when the segment changes (csg = -1
+  // for a new tile), not on every stage: their base pointers come from the
+  // kernel arguments through scalar loads whose wait would otherwise open
+  // every stage.
+  int csg = -1;
+  rsrc_t ra, rb;
+  // Each wavefront computes all 256 rows of the tile against its own 64
+  // columns n0 + 64 wave .. + 63: A (shared by the four) comes through LDS,
+  // B (this wavefront's alone) straight from memory into registers.
+  // B fragments of a stage: [slot][half][column block]
+  u32x4 bq[KR][2][2];
+  // Issue of stage ST into slot SLOT (clamped to the last
+  // stage: the issues past the end reload it, and nobody reads it again, so
+  // every stage issues the same loads), in 8 parts: A's k group `wave`
+  // (rows m0 .. m0 + 255, parts 0-3, 64 chunks each) into LDS slot SLOT,
+  // then this wavefront's B fragments (the lane's k groups 2 h + lh; parts
+  // 4-7) into registers bq[SLOT].  KSEG sets the stage's descriptors and
+  // offsets; KPART issues one part.
+  uint32_t ia_la = 0, ia_oa = 0, ia_kq = 0;
+#define KSEG(ST, SLOT)                                                                 \
+  {                                                                                    \
+    const int sc_ = (ST) < ct.nst ? (ST) : ct.nst - 1;                                 \
+    const int sgm_ = sc_ / ct.nks;                                                     \
+    ia_kq = (uint32_t)(sc_ - sgm_ * ct.nks) * 4;                                       \
+    if (sgm_ != csg) {                                                                 \
+      ra = make_rsrc(a.A[sgm_] + (int64_t)ct.g * a.a_es, kbytes(a.a_bytes, a.a_es, ct.g)); \
+      rb = make_rsrc(a.Bm[sgm_] + (int64_t)ct.g * a.b_es, kbytes(a.b_bytes, a.b_es, ct.g)); \
+      csg = sgm_;                                                                      \
+    }                                                                                  \
+    ia_la = smem_lds + (SLOT) * KSLOT + wave * KPL * 16;                               \
+    ia_oa = 16u * ((ia_kq + wave) * (uint32_t)a.a_w + (uint32_t)ct.m0) + lo16;         \
   }
+#define KPART(Q, SLOT)                                                                 \
+  {                                                                                    \
+    if ((Q) < 4) {                                                                     \
+      k_dma16(ra, ia_oa + 1024u * ((Q) & 3), ia_la + 1024 * ((Q) & 3));                \
+    } else {                                                                           \
+      constexpr int h_ = ((Q) - 4) >> 1, j_ = ((Q) - 4) & 1;                           \
+      bq[SLOT][h_][j_] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128( \
+          rb, 16u * ((ia_kq + 2 * h_ + lh) * (uint32_t)a.b_w +                         \
+                     (uint32_t)(ct.n0 + 64 * wave + 32 * j_ + l32)), 0, 0));            \
+    }                                                                                  \
+  }
+#define KISSUE(ST, SLOT)                                                               \
+  {                                                                                    \
+    KSEG(ST, SLOT)                                                                     \
+    KPART(0, SLOT) KPART(1, SLOT) KPART(2, SLOT) KPART(3, SLOT)                        \
+    KPART(4, SLOT) KPART(5, SLOT) KPART(6, SLOT) KPART(7, SLOT)                        \
+  }
+  // Stage ST in slot U: wait until stages ST and ST + 1 have landed (one
+  // stage's loads outstanding: they complete in issue order), a barrier that
+  // makes every wavefront's A parts visible and retires the reads of the
+  // slot the issue below refills; then 16 groups of 2 MFMAs (half h, row
+  // block i) with, after group (h, i), the LDS read of the fragment that
+  // group frees -- the second half's during the first, the next stage's
+  // first half during the second -- and after every second group one part
+  // of the issue of stage ST + KR - 1, spread so that a load whose issue
+  // stalls does not hold the matrix core for long.
+#define KGROUP(U, H, I)                                                                \
+  {                                                                                    \
+    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                   \
+      acc[I][j_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                            \
+          __builtin_bit_cast(kb16x8, bq[U][H][j_]), fa[H][I], acc[I][j_], 0, 0, 0);    \
+    if ((H) == 0)                                                                      \
+      fa[1][I] = __builtin_bit_cast(kb16x8, sa_[(2 + lh) * KPL + l32 + (I) * 32]);     \
+    else                                                                               \
+      fa[0][I] = __builtin_bit_cast(kb16x8, sn_[lh * KPL + l32 + (I) * 32]);            \
+    if ((I) & 1) KPART(4 * (H) + ((I) >> 1), ((U) + KR - 1) % KR)                      \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+  }
+#define KSTAGE(ST, U)                                                                  \
+  {                                                                                    \
+    k_wait_vmcnt<(KR - 3) * KLOADS>();                                                 \
+    asm volatile("" ::: "memory");                                                     \
+    __builtin_amdgcn_s_barrier();                                                      \
+    asm volatile("" ::: "memory");                                                     \
+    KSEG((ST) + KR - 1, ((U) + KR - 1) % KR)                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    const u32x4* sa_ = reinterpret_cast<const u32x4*>(smem + (U) * KSLOT);             \
+    const u32x4* sn_ = reinterpret_cast<const u32x4*>(smem + (((U) + 1) % KR) * KSLOT); \
+    KGROUP(U, 0, 0) KGROUP(U, 0, 1) KGROUP(U, 0, 2) KGROUP(U, 0, 3)                    \
+    KGROUP(U, 0, 4) KGROUP(U, 0, 5) KGROUP(U, 0, 6) KGROUP(U, 0, 7)                    \
+    KGROUP(U, 1, 0) KGROUP(U, 1, 1) KGROUP(U, 1, 2) KGROUP(U, 1, 3)                    \
+    KGROUP(U, 1, 4) KGROUP(U, 1, 5) KGROUP(U, 1, 6) KGROUP(U, 1, 7)                    \
+  }
+
+  for (int64_t t = t0; t < t1; t += step) {
+    if (t != t0) {
+      ct = ktile(a, t);
+      csg = -1;
+    }
+    if (ct.nst > 0) {
+      KISSUE(0, 0)
+      KISSUE(1, 1)
+      KISSUE(2, 2)
+    }
+    kf32x16 acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    if (ct.nst > 0) {
+      const int nst = ct.nst;
+      // A fragments: fa[0] the current stage's first half, read during the
+      // previous stage; fa[1] its second half
+      kb16x8 fa[2][8];
+      // stage 0 has landed (stage 1 may not yet): the first half's fragments
+      k_wait_vmcnt<2 * KLOADS>();
+      __builtin_amdgcn_s_barrier();
+      {
+        const u32x4* s0_ = reinterpret_cast<const u32x4*>(smem);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fa[0][i] = __builtin_bit_cast(kb16x8, s0_[lh * KPL + l32 + i * 32]);
+      }
+      // whole groups of KR stages (register slots fixed at compile time),
+      // then the remainder
+      const int nfull = nst - nst % KR;
+      for (int st0 = 0; st0 < nfull; st0 += KR) {
+        KSTAGE(st0, 0)
+        KSTAGE(st0 + 1, 1)
+        KSTAGE(st0 + 2, 2)
+        KSTAGE(st0 + 3, 3)
+      }
+      if (nst - nfull > 0) KSTAGE(nfull, 0)
+      if (nst - nfull > 1) KSTAGE(nfull + 1, 1)
+      if (nst - nfull > 2) KSTAGE(nfull + 2, 2)
+      // every wavefront is done reading the ring before the next tile's
+      // loads refill it (the reloads past the end may still be in flight:
+      // each wavefront's loads land in issue order, and the epilogue does
+      // not use the ring)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    kgemm_epilogue(a, smem, acc, ct.g, ct.m0, ct.n0, wave, lane);
+  }
+#undef KSTAGE
+#undef KGROUP
+#undef KISSUE
+#undef KPART
+#undef KSEG
 }
 
 }  // namespace
