@@ -231,8 +231,11 @@ struct GateSplit {
 GateSplit gate_split(const moe_problem_t* p) {
   const int64_t Br = moek::rb8_rows(p->B);
   if (Br == 0) return GateSplit{1, 32};
-  const int64_t tiles = (int64_t)((p->d + 1 + 127) / 128) * ((p->E + 127) / 128);
-  int64_t G = (1024 + tiles - 1) / tiles;
+  // as many groups as one round of workgroups over the 256 CUs holds (the
+  // weight-gradient GEMM's tiles are 256 x 256; a second round for a few
+  // tiles would double the time)
+  const int64_t tiles = (int64_t)((p->d + 1 + 255) / 256) * ((p->E + 255) / 256);
+  int64_t G = 256 / tiles;
   const int64_t gmax = (Br + 1023) / 1024;
   if (G > gmax) G = gmax;
   if (G < 1) G = 1;

@@ -189,6 +189,27 @@ __device__ __forceinline__ KTile ktile(const KArgsDev& a, int64_t t) {
   return r;
 }
 
+// Block row I of the accumulators (32 rows x this wavefront's 64 columns)
+// through the wavefront's staging area `stg`: written in the accumulator
+// layout, read back as rows -- RV[t] holds row 4 t + lane / 16, columns
+// 4 (lane % 16) .. + 3 of the block row.  All eight reads are issued before
+// any is used (one read per use, each waited for, would serialize the LDS
+// latency).  LDS operations of one wavefront complete in order, so the
+// reads see the writes and the next block row's writes wait for the reads.
+#define KSTAGE_ROWS(I, RV)                                                               \
+  {                                                                                      \
+    _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_)                                     \
+      _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                                   \
+        *reinterpret_cast<f32x4*>(stg + l32 * KSTG_ROW + 32 * j_ + 8 * q_ + 4 * lh) =    \
+            f32x4{kacc(acc[I][j_][4 * q_]), kacc(acc[I][j_][4 * q_ + 1]),                \
+                  kacc(acc[I][j_][4 * q_ + 2]), kacc(acc[I][j_][4 * q_ + 3])};           \
+    asm volatile("" ::: "memory");                                                       \
+    _Pragma("unroll") for (int t_ = 0; t_ < 8; ++t_)                                     \
+      RV[t_] = *reinterpret_cast<const f32x4*>(stg + (4 * t_ + (lane >> 4)) * KSTG_ROW + \
+                                               4 * (lane & 15));                         \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+  }
+
 // Epilogue of the tile (g, m0, n0): the B fragment is the matrix
 // instruction's first operand, so acc[i][j] holds the block transposed:
 // registers 4q .. 4q + 3 of lane l are C[m][n .. n + 3] with m = m0 + 32 i +
@@ -226,42 +247,44 @@ __device__ __forceinline__ void kgemm_epilogue(const KArgsDev& a, char* smem, kf
       // loop (and spilled)
       int64_t ldo = a.ldc0, lda = a.ld_add;
       asm volatile("" : "+s"(ldo), "+s"(lda));
+      // rows through the staging area as in the mode-0 case below; the
+      // addend rows are loaded first, so their latency overlaps the staging
+      float* stg = reinterpret_cast<float*>(smem + KR * KSLOT + wave * KSTG_WAVE);
+      const int rr = lane >> 4, cc = 4 * (lane & 15);
+      const int64_t orow = o0 + (int64_t)rr * ldo + 64 * wave + cc;
+      const float* ar = ab ? ab + (int64_t)rr * lda + 64 * wave + cc : nullptr;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i) {
+        f32x4 ad[8];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int mr = 32 * i + l32, nc = 64 * wave + 32 * j + 4 * lh;
-          f32x4 ad[4];
+        for (int t = 0; t < 8; ++t)
+          ad[t] = ar ? *reinterpret_cast<const f32x4*>(ar + (int64_t)(32 * i + 4 * t) * lda)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 rv[8];
+        KSTAGE_ROWS(i, rv)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ad[q] = ab ? *reinterpret_cast<const f32x4*>(ab + (int64_t)mr * lda + nc + 8 * q)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]),
-                                  kacc(acc[i][j][4 * q + 2]), kacc(acc[i][j][4 * q + 3])} + ad[q];
-            const int64_t off = o0 + (int64_t)mr * ldo + nc + 8 * q;
-            if (a.x_bf16)
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.xo) + off) =
-                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            else
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.xo) + off) = v;
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < 8; ++t) {
+          const f32x4 v = rv[t] + ad[t];
+          const int64_t off = orow + (int64_t)(32 * i + 4 * t) * ldo;
+          if (a.x_bf16)
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.xo) + off) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          else
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.xo) + off) = v;
         }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
       return;
     }
   }
   if (fbase) {
-    // Each block row i (32 rows x this wavefront's 64 columns) goes through
-    // the wavefront's own staging area in LDS (outside the ring, so no
-    // barrier): written in the accumulator layout, read back as rows, and
-    // stored 4 rows x 256 contiguous bytes per instruction.  Stored straight
-    // from the accumulators, every instruction would touch 32 rows with 32
-    // bytes each, and the stores, issued at a fraction of the rate, would
-    // take as long as a quarter of the tile's matrix work.  LDS operations
-    // of one wavefront complete in order, so the reads see the writes and
-    // the next block's writes wait for the reads.
+    // Each block row goes through the wavefront's own staging area in LDS
+    // (outside the ring, so no barrier) and is stored 4 rows x 256
+    // contiguous bytes per instruction.  Stored straight from the
+    // accumulators, every instruction would touch 32 rows with 32 bytes
+    // each, and the stores, issued at a fraction of the rate, would take as
+    // long as a quarter of the tile's matrix work.
     float* stg = reinterpret_cast<float*>(smem + KR * KSLOT + wave * KSTG_WAVE);
     // opaque, so that the per-row offsets are not all hoisted out of the
     // tile loop (and spilled)
@@ -270,21 +293,8 @@ __device__ __forceinline__ void kgemm_epilogue(const KArgsDev& a, char* smem, kf
     float* ob = fbase + 64 * wave + (int64_t)rr * fld + cc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(stg + l32 * KSTG_ROW + 32 * j + 8 * q + 4 * lh) =
-              f32x4{kacc(acc[i][j][4 * q]), kacc(acc[i][j][4 * q + 1]), kacc(acc[i][j][4 * q + 2]),
-                    kacc(acc[i][j][4 * q + 3])};
-      asm volatile("" ::: "memory");
-      // all eight reads, then the eight stores (one read per store, each
-      // waited for, would serialize the LDS latency)
       f32x4 rv[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        rv[t] = *reinterpret_cast<const f32x4*>(stg + (4 * t + rr) * KSTG_ROW + cc);
-      __builtin_amdgcn_sched_barrier(0);
+      KSTAGE_ROWS(i, rv)
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         *reinterpret_cast<f32x4*>(ob + (int64_t)(32 * i + 4 * t) * fld) = rv[t];
@@ -323,6 +333,8 @@ __device__ __forceinline__ void kgemm_epilogue(const KArgsDev& a, char* smem, kf
     }
 }
 
+
+#undef KSTAGE_ROWS
 
 // Persistent: one workgroup per CU walks the tiles, ordered (group, tile)
 // and cut into 8 equal contiguous ranges, one per XCD (workgroups are dealt
