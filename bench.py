@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only time the matrix-core ceiling probe (libmoe_probe.so) with random "
                          "and with near-constant bf16 operands")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor library's dense bf16 GEMM (torch.matmul) at the "
+                         "expert FFN's shapes, for comparison with the grouped expert GEMM")
     return ap.parse_args()
 
 
@@ -127,6 +130,43 @@ def mfma_probe(torch) -> dict:
                      "frac_of_2500": round(flop / mean / 1e12 / 2500.0, 4)}
     return {"mfma_probe": res, "grid": grid, "iters": iters, "tflop_per_launch": round(flop / 1e12, 3),
             "warmup_launches": 200, "rounds": 3, "launches_per_round": 5}
+
+
+def library_gemm(torch) -> dict:
+    """The vendor library's dense bf16 GEMM (torch.matmul, which dispatches
+    to hipBLASLt on this image) at the expert FFN's shapes: the kept local
+    rows of the EP-share and mixtral workloads as one dense matrix (a single
+    large GEMM, easier than the grouped one), and one EP-share expert's
+    rows.  Random normal bf16 operands, the right operand contiguous
+    [K][N]; 5 untimed calls, then 20 timed between HIP events.  A
+    comparison point for the grouped expert GEMM, not part of the layer."""
+    shapes = [("ep_share GEMM1 (W1 and W3), all kept local rows", 32976, 7168, 4096),
+              ("ep_share GEMM2 (W2), all kept local rows", 32976, 2048, 7168),
+              ("ep_share GEMM1, one expert's rows", 1031, 7168, 4096),
+              ("mixtral GEMM1 (W1 and W3), all kept rows", 16264, 4096, 28672),
+              ("mixtral GEMM2 (W2), all kept rows", 16264, 14336, 4096)]
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(0)
+    res = []
+    for name, M, K, N in shapes:
+        a = torch.randn(M, K, device="cuda:0", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(K, N, device="cuda:0", dtype=torch.bfloat16, generator=g).contiguous()
+        for _ in range(5):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        tf = 2.0 * M * N * K / us / 1e6
+        res.append({"shape": name, "M": M, "K": K, "N": N, "us": round(us, 1),
+                    "tflops": round(tf, 1), "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        del a, b, c
+    return {"library_gemm": res, "calls": 20, "warmup_calls": 5, "dtype": "bf16",
+            "operands": "random normal"}
 
 
 def hbm_probe(torch) -> dict:
@@ -443,6 +483,10 @@ def main():
 
     if args.hbm_probe:
         print(json.dumps(hbm_probe(torch)))
+        return
+
+    if args.library_gemm:
+        print(json.dumps(library_gemm(torch)))
         return
 
     import expert_token_routing_fp32_amd as moe
