@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's backward pass (moe_backward, for a seeded output "
                          "gradient, on one forward's saved outputs) instead of the forward")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: the forward does not save the first expert GEMM's "
+                         "pre-activations, and the backward recomputes them")
     ap.add_argument("--aux-coef", type=float, default=0.01,
                     help="auxiliary load-balancing loss coefficient of --backward")
     ap.add_argument("--hbm-probe", action="store_true",
@@ -345,12 +348,13 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
 
 
 def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
-    """The backward pass: one forward (outputs kept), then moe_backward on
-    those outputs and a seeded output gradient, W untimed + K timed calls
+    """The backward pass: one forward (outputs kept, and the first expert
+    GEMM's pre-activations unless --recompute), then moe_backward on those
+    outputs and a seeded output gradient, W untimed + K timed calls
     bracketed by synchronizations; then the same number of calls of the
     stage entry points with events between them for the breakdown."""
     bf16 = w.x_dtype == "bf16"
-    y, o = moe.forward(p, x, Wg, bias, wp, outputs=True)
+    y, o = moe.forward(p, x, Wg, bias, wp, outputs=True, save_z=not args.recompute)
     rs = np.random.default_rng(w.seed + 7)
     dy_np = rs.standard_normal((w.B, w.d)).astype(np.float32)
     if bf16:
@@ -394,7 +398,8 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
         moe.route_backward(p, o["logits"], o["topk_idx"], dwb, o["expert_load"], args.aux_coef,
                            dlogits=dlb)
         ev[2].record()
-        moe.expert_ffn_backward(p, x, o["pack_src"], o["expert_offset"], wp, wpb, dret, ws=ws_f)
+        moe.expert_ffn_backward(p, x, o["pack_src"], o["expert_offset"], wp, wpb, dret, ws=ws_f,
+                                z=o.get("z"))
         ev[3].record()
         moe.dispatch_backward(p, dret, o["dest"], dy if p.add_residual else None, dx_acc=accb)
         ev[4].record()
@@ -408,7 +413,8 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
     eo = o["expert_offset"].cpu().numpy()
     alg = algorithmic(w, keep, eo, o["dest"].cpu().numpy())
     # the expert backward's algorithmic work: dX and the weight gradients,
-    # twice the forward's FLOPs (the recomputed pre-activations are extra)
+    # twice the forward's FLOPs (recomputed pre-activations, with
+    # --recompute, are extra)
     ffn_flop = 2.0 * alg["ffn_flop"]
     t_ffn = med["expert_ffn"]
     tfl = ffn_flop / t_ffn / 1e12
@@ -435,12 +441,16 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
                                f"{w.act} f={w.f} x={w.x_dtype} D={w.n_ranks} "
                                f"local experts [{w.e_begin},{w.e_end}), backward, "
                                f"aux_coef={args.aux_coef}",
-                   "global_batch": w.B},
+                   "global_batch": w.B,
+                   "pre_activations": "recomputed" if args.recompute else
+                                      "saved by the forward (moe_forward_out_t.z)"},
         "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": "expert FFN backward (moe_expert_ffn_backward: recompute, dH with "
-                               "the activation derivative, dX, weight gradients, re-layouts)",
+                     "kernel": "expert FFN backward (moe_expert_ffn_backward: dH with the "
+                               "activation derivative, dX, weight gradients, re-layouts"
+                               + (", and the recomputed pre-activations)" if args.recompute
+                                  else ")"),
                      "algorithmic_flop": ffn_flop, "avg_launch_us": round(t_ffn * 1e6, 2),
                      "timing": "HIP events around the stage call, median over the steps"},
         "breakdown": {

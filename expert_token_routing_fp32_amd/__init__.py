@@ -29,6 +29,7 @@ __all__ = ["make_problem", "capacity", "problem_capacity", "max_kept", "validate
            "expert_choice_combine", "forward_expert_choice", "expert_choice_rows",
            "combine_backward", "route_backward", "weights_bwd_bytes", "pack_weights_bwd",
            "expert_ffn_backward", "dispatch_backward", "gate_backward", "backward", "MoEError",
+           "saved_z_bytes",
            "Problem", "lib", "FFN_GEMM_EVENTS"]
 
 
@@ -388,10 +389,12 @@ STAGES = tuple(STAGE_EVENTS)
 
 
 def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=None,
-            stage_events=None, shared=None):
+            stage_events=None, shared=None, save_z: bool = False):
     """The whole layer on the current stream (``wpacked`` from pack_weights).
     With ``outputs`` the intermediate tensors are allocated and returned too
-    (``packed`` then holds the expert outputs of the local rows, in place).
+    (``packed`` then holds the expert outputs of the local rows, in place);
+    with ``save_z`` as well, ``z``: the first expert GEMM's pre-activations,
+    which backward() then reads instead of recomputing them.
     ``stage_events``: optional N_STAGE_EVENTS timing-enabled
     ``torch.cuda.Event`` (or None); the library records them from the start
     and end of each stage's own kernels (STAGE_EVENTS gives the pair of each
@@ -425,6 +428,11 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
                  rank_offset=torch.empty(p.n_ranks + 1, **i32), pack_src=torch.empty(km, **i32),
                  packed=torch.empty((km, d), dtype=torch.int16, device=dev))
         outp = L.ForwardOut(**{n: o[n].data_ptr() for n in _OUT_FIELDS})
+        if save_z:
+            o["z"] = torch.empty(max(saved_z_bytes(p) // 2, 1), dtype=torch.int16, device=dev)
+            outp.z = o["z"].data_ptr()
+    elif save_z:
+        raise ValueError("save_z needs outputs=True")
     if stage_events is not None:
         if len(stage_events) != N_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {N_STAGE_EVENTS} events")
@@ -617,6 +625,11 @@ def weights_bwd_bytes(p: Problem) -> int:
     return lib().moe_weights_bwd_bytes(ctypes.byref(p))
 
 
+def saved_z_bytes(p: Problem) -> int:
+    """Bytes of the forward's saved pre-activations (moe_saved_z_bytes)."""
+    return lib().moe_saved_z_bytes(ctypes.byref(p))
+
+
 def pack_weights_bwd(p: Problem, W1, W3, W2, out=None):
     """The local experts' weights rearranged for the expert backward (same
     [in, out] inputs as pack_weights)."""
@@ -645,11 +658,12 @@ def pack_weights_bwd(p: Problem, W1, W3, W2, out=None):
 
 
 def expert_ffn_backward(p: Problem, x, pack_src, expert_offset, wpacked, wpacked_bwd, dret,
-                        ws=None):
+                        ws=None, z=None):
     """dret [max_kept, d] bf16 is overwritten in place: its local rows
-    become the gradient of the packed input rows.  Returns dict dxp (= dret),
-    dW1, dW3 (SwiGLU, else None) [n_local, d, f] and dW2 [n_local, f, d]
-    float32."""
+    become the gradient of the packed input rows.  ``z``: the forward's
+    saved pre-activations (``forward(..., save_z=True)``) or None to
+    recompute them.  Returns dict dxp (= dret), dW1, dW3 (SwiGLU, else None)
+    [n_local, d, f] and dW2 [n_local, f, d] float32."""
     _check(p)
     B, d, f = p.B, p.d, p.f
     nl = p.e_end - p.e_begin
@@ -667,10 +681,12 @@ def expert_ffn_backward(p: Problem, x, pack_src, expert_offset, wpacked, wpacked
     if nl > 0:
         _need(wpacked, "wpacked", weights_bytes(p), 1)
         _need(wpacked_bwd, "wpacked_bwd", weights_bwd_bytes(p), 1)
+    if z is not None:
+        _need(z, "z", saved_z_bytes(p) // 2, 2)
     ws = _ws(p, "expert_ffn_backward", ws, dev)
     L.check(lib().moe_expert_ffn_backward(ctypes.byref(p), _p(x), _p(pack_src),
                                           _p(expert_offset), _p(wpacked), _p(wpacked_bwd),
-                                          _p(dret), _p(dW1), _p(dW3), _p(dW2), _p(ws),
+                                          _p(z), _p(dret), _p(dW1), _p(dW3), _p(dW2), _p(ws),
                                           ws.numel(), _stream()), "moe_expert_ffn_backward")
     return dict(dxp=dret, dW1=dW1[:nl], dW3=None if dW3 is None else dW3[:nl], dW2=dW2[:nl])
 
@@ -718,7 +734,9 @@ def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef:
              ws=None) -> dict:
     """All gradients of the layer (moe_backward).  ``saved``: the dict of
     ``forward(..., outputs=True)`` (logits, topk_idx, topk_w, dest,
-    expert_load, expert_offset, pack_src, and packed = the expert outputs).
+    expert_load, expert_offset, pack_src, and packed = the expert outputs;
+    with ``save_z=True`` also z, the pre-activations the backward then does
+    not recompute).
     Returns dx, dWg, dbias, dW1, dW3 (SwiGLU, else None), dW2, dlogits, dw."""
     _check(p)
     B, d, E, k, f = p.B, p.d, p.E, p.k, p.f
@@ -739,7 +757,8 @@ def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef:
                  topk_w=saved["topk_w"].data_ptr(), dest=saved["dest"].data_ptr(),
                  expert_load=saved["expert_load"].data_ptr(),
                  expert_offset=saved["expert_offset"].data_ptr(),
-                 pack_src=saved["pack_src"].data_ptr(), ret=saved["packed"].data_ptr())
+                 pack_src=saved["pack_src"].data_ptr(), ret=saved["packed"].data_ptr(),
+                 z=saved["z"].data_ptr() if saved.get("z") is not None else None)
     gr = L.Grads(**{n: (g[n].data_ptr() if g[n] is not None else None)
                     for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dlogits", "dw")})
     n = workspace_bytes(p, "backward")

@@ -55,7 +55,7 @@ class ForwardOut(ctypes.Structure):
     hipEvent_t handles (or NULL) taken from the stages' kernel dispatches."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
-        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed")] + [
+        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed", "z")] + [
         ("events", ctypes.c_void_p * MOE_STAGE_EVENTS)]
 
 
@@ -70,7 +70,7 @@ class Saved(ctypes.Structure):
     """moe_saved_t: the forward's outputs the backward reads."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "dest", "expert_load", "expert_offset", "pack_src",
-        "ret")]
+        "ret", "z")]
 
 
 class Grads(ctypes.Structure):
@@ -128,7 +128,8 @@ _SIGS = {
     "moe_weights_bwd_bytes": (ctypes.c_size_t, [_P]),
     "moe_pack_weights_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "moe_expert_ffn_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
-                                               ctypes.c_size_t, _V]),
+                                               _V, ctypes.c_size_t, _V]),
+    "moe_saved_z_bytes": (ctypes.c_size_t, [_P]),
     "moe_dispatch_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V]),
     "moe_gate_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
                                          _V]),

@@ -88,6 +88,12 @@ struct GemmArgs {
   // through pack_src instead of a packed copy)
   const int32_t* gidx;
   int64_t src_rows;
+  // GELU / SwiGLU launch, optional: the pre-activations themselves, stored
+  // as the plain launch of the same weights would store them (rows as
+  // Out's, zs_w per row), for a backward pass that then need not recompute
+  // them
+  uint16_t* Zs;
+  int zs_w;
 };
 
 // GELU with the exact-erf definition, 0.5 z (1 + erf(z / sqrt 2)).  erf is
@@ -484,6 +490,37 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
         const int col0 = MODE == MODE_SWIGLU ? nt * 128 + 32 * wave : nt * 256 + 64 * wave;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
+          if (MODE != MODE_PLAIN && a.Zs) {
+            // the pre-activations of block i first, through the same
+            // staging area, exactly as the plain launch stores its outputs
+            // (both weight blocks, 64 columns per wavefront); non-temporal,
+            // as only a later backward pass reads them
+            int zs_w = a.zs_w;
+            asm volatile("" : "+s"(zs_w));
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = acc_read(acc[c][i][4 * q + j]);
+                *(uint2*)(stg + l32 * kStgRow + (32 * c + 8 * q + 4 * lg) * 2) =
+                    uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              }
+            __builtin_amdgcn_sched_barrier(0);
+            uint16_t* zo = a.Zs + o_row0 * zs_w;
+            const int zc0 = nt * 256 + 64 * wave;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int sgi = lane + 64 * q;
+              const int rin = sgi / 8, sg = sgi % 8;
+              const u32x4 v = *(const u32x4*)(stg + rin * kStgRow + sg * 16);
+              const int row = 32 * i + rin, col = zc0 + 8 * sg;
+              if (row < rows && col < zs_w)
+                __builtin_nontemporal_store(v, (u32x4*)(zo + (row * zs_w + col)));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
           for (int c = 0; c < (MODE == MODE_SWIGLU ? 1 : 2); ++c) {
             // SwiGLU: block 0 holds the W1 products and block 1 the W3
@@ -859,7 +896,7 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
                              const void* wp, uint16_t* H, uint16_t* ret, hipStream_t s,
                              hipEvent_t ev_start, hipEvent_t ev_stop, hipEvent_t ev_mid_end,
                              hipEvent_t ev_mid_start, const uint16_t* gx, const int32_t* gidx,
-                             int64_t gx_rows) {
+                             int64_t gx_rows, uint16_t* zsave) {
   if (n_local <= 0 || rows_max <= 0) {
     hipError_t e = hipSuccess;
     for (hipEvent_t ev : {ev_start, ev_mid_end, ev_mid_start, ev_stop})
@@ -890,6 +927,8 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
     g1.gidx = gidx;
     g1.src_rows = gx_rows;
   }
+  g1.Zs = zsave;
+  g1.zs_w = expert_ffn_zw(f, swiglu);
   hipError_t err = swiglu ? launch_gemm<MODE_SWIGLU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end)
                           : launch_gemm<MODE_GELU>(g1, m_tiles, mfma_bound, s, ev_start, ev_mid_end);
   if (err != hipSuccess) return err;

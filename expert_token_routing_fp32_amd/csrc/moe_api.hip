@@ -548,6 +548,7 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
   if (p->B > 0 && (!a16(x) || !a16(y) || !a4(Wg) || (bias && !a4(bias)))) return MOE_ERR_INVALID;
   if (wpacked && !a16(wpacked)) return MOE_ERR_INVALID;
   if (out && out->packed && !a16(out->packed)) return MOE_ERR_INVALID;
+  if (out && out->z && !a16(out->z)) return MOE_ERR_INVALID;
   const size_t need = carve_forward(p, out, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   FwdBufs b;
@@ -628,7 +629,7 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
                                   rows_hint(p), p->d, p->f, swiglu, wpacked, b.H, b.packed,
                                   stream, ev[5], sh ? nullptr : ev[8], ev[6], ev[7],
                                   gather ? static_cast<const uint16_t*>(x) : nullptr,
-                                  gather ? b.pack_src : nullptr, p->B);
+                                  gather ? b.pack_src : nullptr, p->B, out ? out->z : nullptr);
     if (e == hipSuccess && sh)
       e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
                                   sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,
@@ -842,8 +843,9 @@ moe_status_t check_bwd(const moe_problem_t* p) {
 // the expert FFN backward on carved scratch (shared by the stage call and
 // the chain)
 hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pack_src,
-                        const int32_t* eo, const void* wp, const void* wpb, uint16_t* dret,
-                        float* dW1, float* dW3, float* dW2, void* ws, hipStream_t s) {
+                        const int32_t* eo, const void* wp, const void* wpb, const uint16_t* zsaved,
+                        uint16_t* dret, float* dW1, float* dW3, float* dW2, void* ws,
+                        hipStream_t s) {
   const int nl = p->e_end - p->e_begin;
   if (nl <= 0 || p->B == 0) return hipSuccess;
   FfnBwdBufs b;
@@ -854,21 +856,23 @@ hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pa
   const int64_t kl = kloc_of(p);
   hipError_t e = moek::launch_gather_rows(x, xb, pack_src, eo, p->e_begin, p->e_end, p->B, d, kl,
                                           b.xloc, s);
-  // Z = X W1 (, X W3): the forward's first GEMM without its activation
-  if (e == hipSuccess)
+  // Z = X W1 (, X W3): the forward's first GEMM without its activation,
+  // unless the forward saved it (the same kernel and order: the same bits)
+  const uint16_t* Z = zsaved ? zsaved : b.Z;
+  if (e == hipSuccess && !zsaved)
     e = moek::launch_ffn_recompute(b.xloc, eo, p->e_begin, nl, rpe, rh, d, f, sw, wp, b.Z, s);
   // RB8 operands of the weight gradients: X, H = act(Z), dret (local rows)
   if (e == hipSuccess)
     e = moek::launch_relayout_rb8(0, b.xloc, d, eo, p->e_begin, 1, nl, rpe, d, d, -1, b.X8, s);
   if (e == hipSuccess)
-    e = moek::launch_relayout_rb8(sw ? 2 : 1, b.Z, zw, eo, p->e_begin, 1, nl, rpe, f, zw, -1,
+    e = moek::launch_relayout_rb8(sw ? 2 : 1, Z, zw, eo, p->e_begin, 1, nl, rpe, f, zw, -1,
                                   b.H8, s);
   // dret is indexed by the absolute packed row
   if (e == hipSuccess)
     e = moek::launch_relayout_rb8(0, dret, d, eo, p->e_begin, 0, nl, rpe, d, d, -1, b.dret8, s);
   // dZ = dact(dret W2^T, Z), then dZ in RB8
   if (e == hipSuccess)
-    e = moek::launch_ffn_dact(dret, eo, p->e_begin, nl, rpe, rh, d, f, sw, wpb, b.Z, b.dZ, s);
+    e = moek::launch_ffn_dact(dret, eo, p->e_begin, nl, rpe, rh, d, f, sw, wpb, Z, b.dZ, s);
   if (e == hipSuccess)
     e = moek::launch_relayout_rb8(0, b.dZ, zwd, eo, p->e_begin, 1, nl, rpe, zwd, zwd, -1, b.dZ8,
                                   s);
@@ -1062,6 +1066,11 @@ moe_status_t moe_route_backward(const moe_problem_t* p, const float* logits,
                                            p->E, p->k, p->tau, dlogits, stream));
 }
 
+size_t moe_saved_z_bytes(const moe_problem_t* p) {
+  if (moe_validate(p) != MOE_OK) return SIZE_MAX;
+  return (size_t)kloc_of(p) * (size_t)moek::expert_ffn_zw(p->f, p->act == MOE_SWIGLU) * 2;
+}
+
 size_t moe_weights_bwd_bytes(const moe_problem_t* p) {
   if (moe_validate(p) != MOE_OK) return SIZE_MAX;
   return moek::packed_weights_bwd_bytes(p->e_end - p->e_begin, p->d, p->f,
@@ -1086,8 +1095,9 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
 moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
                                      const int32_t* pack_src, const int32_t* expert_offset,
                                      const void* wpacked, const void* wpacked_bwd,
-                                     moe_bf16_t* dret, float* dW1, float* dW3, float* dW2,
-                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+                                     const moe_bf16_t* z, moe_bf16_t* dret, float* dW1,
+                                     float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
   moe_status_t st = check_bwd(p);
   if (st != MOE_OK) return st;
   const bool sw = p->act == MOE_SWIGLU;
@@ -1099,6 +1109,7 @@ moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
     return MOE_ERR_INVALID;
   if (p->B > 0 && (!x || !pack_src || !dret || !a16(x) || !a16(dret) || !a4(pack_src)))
     return MOE_ERR_INVALID;
+  if (z && !a16(z)) return MOE_ERR_INVALID;
   const size_t need = carve_ffn_bwd(p, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
   if (p->B == 0) {
@@ -1109,8 +1120,8 @@ moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
     if (e == hipSuccess && sw) e = moek::launch_fill_zero(dW3, n, stream);
     return hip_status(e);
   }
-  return hip_status(ffn_backward(p, x, pack_src, expert_offset, wpacked, wpacked_bwd, dret, dW1,
-                                 sw ? dW3 : nullptr, dW2, ws, stream));
+  return hip_status(ffn_backward(p, x, pack_src, expert_offset, wpacked, wpacked_bwd, z, dret,
+                                 dW1, sw ? dW3 : nullptr, dW2, ws, stream));
 }
 
 moe_status_t moe_dispatch_backward(const moe_problem_t* p, const moe_bf16_t* dxp,
@@ -1164,6 +1175,7 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
     return MOE_ERR_INVALID;
   if (p->B > 0 && (!a16(x) || !a16(dy) || !a16(sv->ret) || !a4(g->dx)))
     return MOE_ERR_INVALID;
+  if (sv->z && !a16(sv->z)) return MOE_ERR_INVALID;
   if ((g->dw && !a4(g->dw)) || (g->dlogits && !a4(g->dlogits))) return MOE_ERR_INVALID;
   const size_t need = carve_bwd(p, g, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
@@ -1188,8 +1200,8 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
     e = moek::launch_route_bwd(sv->logits, sv->topk_idx, b.dw, sv->expert_load, aux_coef, p->B,
                                p->E, p->k, p->tau, b.dl, stream);
   if (e == hipSuccess && nl > 0)
-    e = ffn_backward(p, x, sv->pack_src, sv->expert_offset, wpacked, wpacked_bwd, b.dret, g->dW1,
-                     sw ? g->dW3 : nullptr, g->dW2, b.ffn_ws, stream);
+    e = ffn_backward(p, x, sv->pack_src, sv->expert_offset, wpacked, wpacked_bwd, sv->z, b.dret,
+                     g->dW1, sw ? g->dW3 : nullptr, g->dW2, b.ffn_ws, stream);
   if (e == hipSuccess)
     e = moek::launch_unpack_sum(b.dret, sv->dest, dy, xb, p->add_residual != 0, p->B, p->k, p->d,
                                 kmax_of(p), b.dx_acc, stream);

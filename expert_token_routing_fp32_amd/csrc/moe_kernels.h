@@ -336,7 +336,7 @@ hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offse
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
                              hipEvent_t ev_mid_end = nullptr, hipEvent_t ev_mid_start = nullptr,
                              const uint16_t* gx = nullptr, const int32_t* gidx = nullptr,
-                             int64_t gx_rows = 0);
+                             int64_t gx_rows = 0, uint16_t* zsave = nullptr);
 
 // ---- backward pass (backward.hip, wgrad.hip, expert_gemm.hip) -------------
 hipError_t launch_combine_bwd(const void* dy, bool x_bf16, const uint16_t* ret,

@@ -359,6 +359,12 @@ typedef struct {
   int32_t* pack_src;      /* [Kmax]   */
   moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
                              outputs overwrite the local rows in place) */
+  moe_bf16_t* z;          /* optional, moe_saved_z_bytes(p) bytes, 16-byte
+                             aligned: the local rows' pre-activations
+                             X . W1 (and X . W3), bf16, stored by the first
+                             expert GEMM for moe_backward, which then does
+                             not recompute them; NULL: not stored (and not
+                             in the workspace either) */
   /* Optional timing: each non-NULL events[i] is recorded on the call's
    * stream from the dispatch timestamps of the stages' own kernels
    * (hipExtLaunchKernelGGL start / end events; no marker packets):
@@ -571,6 +577,12 @@ moe_status_t moe_route_backward(const moe_problem_t* p, const float* logits,
                                 const int32_t* expert_load, float aux_coef, float* dlogits,
                                 hipStream_t stream);
 
+/* Bytes of moe_forward_out_t.z: Kloc rows (the local experts' row
+ * capacity) of the first expert GEMM's output width, bf16.  The backward
+ * reads it in place of recomputing that GEMM; the values are the same bits
+ * (the same kernel, the same order of operations). */
+size_t moe_saved_z_bytes(const moe_problem_t* p);
+
 /* Bytes of the blocked backward copy of the local experts' weights. */
 size_t moe_weights_bwd_bytes(const moe_problem_t* p);
 
@@ -587,7 +599,8 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
 
 /* Expert FFN backward.  For each local expert and its packed rows
  * (X = x[pack_src[r]], bf16): the pre-activations Z = X . W1 (and X . W3)
- * are recomputed, then dH = dret . W2^T, dZ = dH * act'(Z) (SwiGLU:
+ * are taken from z when the forward saved them (moe_forward_out_t.z) or
+ * recomputed (z NULL), then dH = dret . W2^T, dZ = dH * act'(Z) (SwiGLU:
  * dZ1 = dH Z3 silu'(Z1), dZ3 = dH silu(Z1)), dX = dZ1 . W1^T (+ dZ3 . W3^T),
  * dW2 = H^T . dret, dW1 = X^T . dZ1, dW3 = X^T . dZ3 (H = act(Z), bf16).
  * dret is overwritten in place: its local rows become dX, the gradient of
@@ -601,8 +614,9 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
 moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
                                      const int32_t* pack_src, const int32_t* expert_offset,
                                      const void* wpacked, const void* wpacked_bwd,
-                                     moe_bf16_t* dret, float* dW1, float* dW3, float* dW2,
-                                     void* ws, size_t ws_bytes, hipStream_t stream);
+                                     const moe_bf16_t* z, moe_bf16_t* dret, float* dW1,
+                                     float* dW3, float* dW2, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* Dispatch (pack) backward: dx_acc[t] = sum_j dXp[dest[t,j]] over kept
  * choices, in j order, plus dy[t] when the problem adds the residual.
@@ -632,6 +646,7 @@ typedef struct {
   const int32_t* expert_offset; /* [E+1]    */
   const int32_t* pack_src;      /* [Kmax]   */
   const moe_bf16_t* ret;        /* [Kmax][d] */
+  const moe_bf16_t* z;          /* moe_forward_out_t.z, or NULL: recompute */
 } moe_saved_t;
 
 /* The gradients moe_backward writes; dW3 only for SwiGLU, dbias may be

@@ -292,3 +292,41 @@ def test_backward_empty_batch():
     torch.cuda.synchronize()
     for key in ("dWg", "dbias", "dW1", "dW2", "dW3"):
         assert float(g[key].abs().max()) == 0.0, key
+
+
+@pytest.mark.parametrize("name", ["gelu_drops_residual", "swiglu_remote", "swiglu_f32_x",
+                                  "uniform", "ep_share"])
+def test_backward_saved_z_matches_recompute(name):
+    """The forward's saved pre-activations (save_z) are the bits the
+    backward's recompute produces (the same kernel, the same order), so
+    every gradient is bit-identical either way, and saving them leaves the
+    forward's outputs unchanged."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    w = SMALL[name] if name in SMALL else moe_synth.WORKLOADS[name]
+    res = name == "gelu_drops_residual"
+    say(f"[saved z {name}]")
+    inp = moe_synth.make_inputs(w)
+    p = problem_for(w, add_residual=res)
+    x, Wg = to_dev(inp["x"]), to_dev(inp["Wg"])
+    bias = None if inp["bias"] is None else to_dev(inp["bias"])
+    wp = packed_weights_for_gpu(p, inp)
+    wpb = _wpb(p, inp)
+    y0, o0 = moe.forward(p, x, Wg, bias, wp, outputs=True)
+    y1, o1 = moe.forward(p, x, Wg, bias, wp, outputs=True, save_z=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    K = int(o0["expert_offset"][-1])  # rows past the kept ones are not written
+    for key in ("dest", "expert_offset", "pack_src", "packed"):
+        a, b = (o0[key], o1[key]) if key in ("dest", "expert_offset") else \
+            (o0[key][:K], o1[key][:K])
+        assert torch.equal(a, b), key
+    dy = to_dev(_dy(w, seed=9))
+    g0 = moe.backward(p, x, Wg, wp, wpb, o0, dy, aux_coef=AUX)
+    g1 = moe.backward(p, x, Wg, wp, wpb, o1, dy, aux_coef=AUX)
+    torch.cuda.synchronize()
+    for key, v in g0.items():
+        if v is not None:
+            assert torch.equal(v, g1[key]), key
+    say(f"  {len(g0)} gradients bit-identical with the saved pre-activations "
+        f"({moe.saved_z_bytes(p) / 1e6:.1f} MB)")
