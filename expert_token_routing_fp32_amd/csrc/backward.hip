@@ -228,19 +228,23 @@ __device__ __forceinline__ int zcol1(int u) { return (u >> 7) * 256 + ((u >> 5) 
 // grid.x: n_seg * groups_per_seg (groups past a segment's zero padding
 // exit); grid.y: column tiles (at most 257).  Segment s holds source rows
 // [seg_lo(s), seg_hi(s)) (relative to src), from expert_offset when eo is
-// given, else one segment of rows_const rows.
+// given, else one segment of rows_const rows.  With ridx (and eo, rel), row
+// r of the segments is row ridx[expert_offset[e_begin] + r] of src (the
+// local experts' rows of x through pack_src, with no gathered copy); an
+// index outside [0, src_rows) reads as a zero row.
 template <int MODE>
 __global__ __launch_bounds__(256) void relayout_rb8_kernel(
     const uint16_t* __restrict__ src, int64_t src_ld, const int32_t* __restrict__ eo,
     int e_begin, int rel, int64_t rows_const, int gps, int W, int src_w, int one_col,
-    uint16_t* __restrict__ out, int64_t out_seg) {
+    uint16_t* __restrict__ out, int64_t out_seg, const int32_t* __restrict__ ridx,
+    int64_t src_rows) {
   __shared__ uint16_t tile[8][256 + 8];
   const int seg = blockIdx.x / gps, g = blockIdx.x % gps;
-  int64_t lo, n;
+  int64_t lo, n, base = 0;
   if (eo) {
     // rel: src holds the local rows only (row 0 = expert_offset[e_begin]);
     // otherwise src is indexed by the absolute packed row
-    const int64_t base = rel ? eo[e_begin] : 0;
+    base = rel ? eo[e_begin] : 0;
     lo = eo[e_begin + seg] - base;
     n = eo[e_begin + seg + 1] - eo[e_begin + seg];
   } else {
@@ -258,8 +262,13 @@ __global__ __launch_bounds__(256) void relayout_rb8_kernel(
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = 0.f;
-    if (r < n) {
-      const uint16_t* rowp = src + (lo + r) * src_ld;
+    int64_t sr = lo + r;
+    if (ridx && r < n) {
+      sr = ridx[base + lo + r];
+      if (sr < 0 || sr >= src_rows) sr = -1;
+    }
+    if (r < n && sr >= 0) {
+      const uint16_t* rowp = src + sr * src_ld;
       if (MODE == RL_COPY) {
         if (c + 8 <= src_w) {
           unpack8(*(const u32x4*)(rowp + c), v);
@@ -517,7 +526,8 @@ int64_t rb8_rows(int64_t rows) { return (rows + 31) / 32 * 32; }
 
 hipError_t launch_relayout_rb8(int mode, const uint16_t* src, int64_t src_ld, const int32_t* eo,
                                int e_begin, int rel, int n_seg, int64_t rows_cap, int W,
-                               int src_w, int one_col, uint16_t* out, hipStream_t s) {
+                               int src_w, int one_col, uint16_t* out, hipStream_t s,
+                               const int32_t* ridx, int64_t src_rows) {
   if (n_seg <= 0 || rows_cap <= 0) return hipSuccess;
   const int64_t R8 = rb8_rows(rows_cap);
   const int gps = (int)(R8 / 8);
@@ -528,15 +538,18 @@ hipError_t launch_relayout_rb8(int mode, const uint16_t* src, int64_t src_ld, co
   switch (mode) {
     case RL_GELU:
       hipLaunchKernelGGL(relayout_rb8_kernel<RL_GELU>, g, dim3(256), 0, s, src, src_ld, eo,
-                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg);
+                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg,
+                         ridx, src_rows);
       break;
     case RL_SWIGLU:
       hipLaunchKernelGGL(relayout_rb8_kernel<RL_SWIGLU>, g, dim3(256), 0, s, src, src_ld, eo,
-                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg);
+                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg,
+                         ridx, src_rows);
       break;
     default:
       hipLaunchKernelGGL(relayout_rb8_kernel<RL_COPY>, g, dim3(256), 0, s, src, src_ld, eo,
-                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg);
+                         e_begin, rel, rows_cap, gps, W, src_w, one_col, out, out_seg,
+                         ridx, src_rows);
   }
   return hipGetLastError();
 }

@@ -854,8 +854,14 @@ hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pa
   const int d = p->d, f = p->f, zw = moek::expert_ffn_zw(f, sw), zwd = sw ? 2 * f : f;
   const int rpe = (int)rows_per_expert(p), rh = rows_hint(p);
   const int64_t kl = kloc_of(p);
-  hipError_t e = moek::launch_gather_rows(x, xb, pack_src, eo, p->e_begin, p->e_end, p->B, d, kl,
-                                          b.xloc, s);
+  // The local rows X = x[pack_src[r]]: gathered for the recompute, or, with
+  // the pre-activations saved and bf16 tokens, read through pack_src by the
+  // RB8 re-layout with no gathered copy.
+  const bool direct = zsaved && xb;
+  hipError_t e = hipSuccess;
+  if (!direct)
+    e = moek::launch_gather_rows(x, xb, pack_src, eo, p->e_begin, p->e_end, p->B, d, kl, b.xloc,
+                                 s);
   // Z = X W1 (, X W3): the forward's first GEMM without its activation,
   // unless the forward saved it (the same kernel and order: the same bits)
   const uint16_t* Z = zsaved ? zsaved : b.Z;
@@ -863,7 +869,10 @@ hipError_t ffn_backward(const moe_problem_t* p, const void* x, const int32_t* pa
     e = moek::launch_ffn_recompute(b.xloc, eo, p->e_begin, nl, rpe, rh, d, f, sw, wp, b.Z, s);
   // RB8 operands of the weight gradients: X, H = act(Z), dret (local rows)
   if (e == hipSuccess)
-    e = moek::launch_relayout_rb8(0, b.xloc, d, eo, p->e_begin, 1, nl, rpe, d, d, -1, b.X8, s);
+    e = direct ? moek::launch_relayout_rb8(0, static_cast<const uint16_t*>(x), d, eo, p->e_begin,
+                                           1, nl, rpe, d, d, -1, b.X8, s, pack_src, p->B)
+               : moek::launch_relayout_rb8(0, b.xloc, d, eo, p->e_begin, 1, nl, rpe, d, d, -1,
+                                           b.X8, s);
   if (e == hipSuccess)
     e = moek::launch_relayout_rb8(sw ? 2 : 1, Z, zw, eo, p->e_begin, 1, nl, rpe, f, zw, -1,
                                   b.H8, s);

@@ -355,7 +355,8 @@ int64_t rb8_rows(int64_t rows);
 // rel: src rows are local (row 0 = expert_offset[e_begin]); else absolute
 hipError_t launch_relayout_rb8(int mode, const uint16_t* src, int64_t src_ld, const int32_t* eo,
                                int e_begin, int rel, int n_seg, int64_t rows_cap, int W,
-                               int src_w, int one_col, uint16_t* out, hipStream_t s);
+                               int src_w, int one_col, uint16_t* out, hipStream_t s,
+                               const int32_t* ridx = nullptr, int64_t src_rows = 0);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 // out0[m][n] (m < M0) / out1[n] (m == M0) = sum over g of part[g][m][n], in g
 // order; part is [G][M0 + 1][N]
