@@ -14,16 +14,18 @@
 // 4 KB of contiguous memory.  K_g is padded with zero fragments to a
 // multiple of 32.
 //
-// Tile 256 x 256 x 32 per workgroup of 4 wavefronts (2 x 2, each 128 x 128 =
-// 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, accumulators in the AGPRs, one
-// wavefront per SIMD): each 16-byte fragment read from LDS feeds four MFMAs.
-// Operands go global -> LDS by buffer loads that write LDS directly into a
-// 4-slot ring, three stages ahead (wavefront w loads k group w of both
-// operands, 8 loads of 64 x 16 bytes per stage); loads past a group's data
-// read zeros.  Vector-memory loads complete in issue order, so waiting until
-// two stages' loads are outstanding means the oldest stage has landed; one
-// barrier per stage then makes every wavefront's part visible and frees the
-// slot the next issue overwrites.
+// Tile 256 x 256, K in stages of 32, per workgroup of 4 wavefronts (one
+// per SIMD, one workgroup per CU, persistent over a range of tiles): each
+// wavefront computes all 256 rows against its own 64 columns (8 x 2 blocks
+// of v_mfma_f32_32x32x16_bf16, accumulators in the AGPRs).  A, shared by
+// the four, goes global -> LDS by buffer loads that write LDS directly into
+// a 4-slot ring (wavefront w loads k group w, 4 loads of 64 x 16 bytes per
+// stage); each wavefront's B fragments go global -> registers into a 4-slot
+// register ring (4 loads per stage); both three stages ahead, loads past a
+// group's data reading zeros.  Vector-memory loads complete in issue order,
+// so waiting until one stage's loads are outstanding means the two oldest
+// stages have landed; one barrier per stage then makes every wavefront's A
+// parts visible and frees the slot the next issue overwrites.
 #include "moe_kernels.h"
 
 namespace moek {

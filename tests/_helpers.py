@@ -62,6 +62,23 @@ def assert_f32_close(got, ref, tol=TOL_F32, what=""):
     assert m <= tol, f"{what}: {m} > {tol}"
 
 
+def assert_sum_close(got, ref, abs_sum, n, what=""):
+    """fp32 results that are sums of n products: within TOL_F32 max(1, |ref|)
+    or within the standard forward error bound of an n-term fp32 sum,
+    gamma_n = n u / (1 - n u) (u = 2^-24) times the sum of the terms'
+    magnitudes (abs_sum, same shape), whichever is larger -- a fixed bound
+    does not scale with the length of the contraction."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    u = 2.0 ** -24
+    gamma = n * u / (1.0 - n * u)
+    tol = np.maximum(TOL_F32 * np.maximum(1.0, np.abs(ref)), gamma * np.asarray(abs_sum))
+    r = np.abs(got - ref) / tol
+    m = float(r.max()) if r.size else 0.0
+    say(f"  {what}: max |d| / bound = {m:.3f} (n = {n})")
+    assert m <= 1.0, f"{what}: {m} of the bound"
+
+
 def rel_err(got, ref) -> float:
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
