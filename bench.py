@@ -347,14 +347,18 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
                       "input generation excluded"}
 
 
-def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
+def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev, shared=None):
     """The backward pass: one forward (outputs kept, and the first expert
     GEMM's pre-activations unless --recompute), then moe_backward on those
     outputs and a seeded output gradient, W untimed + K timed calls
     bracketed by synchronizations; then the same number of calls of the
-    stage entry points with events between them for the breakdown."""
+    stage entry points with events between them for the breakdown.  With a
+    shared expert (``shared`` = (ps, packed, packed backward copy)) the
+    chain is moe_backward_shared, and the shared expert's FFN backward is a
+    stage of its own in the breakdown."""
     bf16 = w.x_dtype == "bf16"
-    y, o = moe.forward(p, x, Wg, bias, wp, outputs=True, save_z=not args.recompute)
+    y, o = moe.forward(p, x, Wg, bias, wp, outputs=True, save_z=not args.recompute,
+                       shared=None if shared is None else shared[:2])
     rs = np.random.default_rng(w.seed + 7)
     dy_np = rs.standard_normal((w.B, w.d)).astype(np.float32)
     if bf16:
@@ -362,11 +366,17 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
         dy = torch.from_numpy(moe_synth.f32_to_bf16_bits(dy_np).view(np.int16)).to(dev)
     else:
         dy = torch.from_numpy(dy_np).to(dev)
-    ws = torch.empty(moe.workspace_bytes(p, "backward"), dtype=torch.uint8, device=dev)
+    if shared is None:
+        nws = moe.workspace_bytes(p, "backward")
+    else:
+        nws = moe.lib().moe_backward_shared_workspace_bytes(ctypes.byref(p),
+                                                           ctypes.byref(shared[0]))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
-        return moe.backward(p, x, Wg, wp, wpb, o, dy, aux_coef=args.aux_coef, ws=ws)
+        return moe.backward(p, x, Wg, wp, wpb, o, dy, aux_coef=args.aux_coef, ws=ws,
+                            shared=shared)
     log(f"[bench] backward: warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -379,7 +389,8 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
     sec = (time.perf_counter() - t0) / args.steps
 
     # breakdown: the stage calls of the same chain, events between them
-    keys = ("combine", "route", "expert_ffn", "dispatch", "gate")
+    keys = ("combine", "route", "expert_ffn", "dispatch") + \
+        (("shared_ffn",) if shared is not None else ()) + ("gate",)
     per = {k_: [] for k_ in keys}
     km = moe.max_kept(p)
     dret = torch.empty((max(km, 1), w.d), dtype=torch.int16, device=dev)
@@ -390,8 +401,15 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
                        device=dev)
     ws_g = torch.empty(max(moe.workspace_bytes(p, "gate_backward"), 1), dtype=torch.uint8,
                        device=dev)
+    if shared is not None:
+        ps_ = shared[0]
+        s_src = torch.arange(w.B, dtype=torch.int32, device=dev)
+        s_eo = torch.tensor([0, w.B], dtype=torch.int32, device=dev)
+        s_dret = torch.empty((w.B, w.d), dtype=torch.int16, device=dev)
+        ws_s = torch.empty(max(moe.workspace_bytes(ps_, "expert_ffn_backward"), 1),
+                           dtype=torch.uint8, device=dev)
     for _ in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(keys) + 1)]
         ev[0].record()
         moe.combine_backward(p, dy, o["packed"], o["dest"], o["topk_w"], dret=dret, dw=dwb)
         ev[1].record()
@@ -403,8 +421,12 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
         ev[3].record()
         moe.dispatch_backward(p, dret, o["dest"], dy if p.add_residual else None, dx_acc=accb)
         ev[4].record()
+        if shared is not None:
+            s_dret.copy_(dy)
+            moe.expert_ffn_backward(ps_, x, s_src, s_eo, shared[1], shared[2], s_dret, ws=ws_s)
+            ev[5].record()
         moe.gate_backward(p, x, Wg, dlb, dx_acc=accb, ws=ws_g)
-        ev[5].record()
+        ev[len(keys)].record()
         torch.cuda.synchronize()
         for i, k_ in enumerate(keys):
             per[k_].append(ev[i].elapsed_time(ev[i + 1]) * 1e-3)
@@ -443,7 +465,8 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev):
                                f"aux_coef={args.aux_coef}",
                    "global_batch": w.B,
                    "pre_activations": "recomputed" if args.recompute else
-                                      "saved by the forward (moe_forward_out_t.z)"},
+                                      "saved by the forward (moe_forward_out_t.z)",
+                   **({"shared_expert_f": shared[0].f} if shared is not None else {})},
         "roofline": {"bound": "mfma", "achieved": round(tfl, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None,
@@ -552,6 +575,8 @@ def main():
         S2 = bw((1, fs, w.d), fs)
         ps = moe.shared_problem(p, fs, w.act)
         shared = (ps, moe.pack_weights(ps, S1, S3, S2))
+        shared_bwd = (ps, shared[1], moe.pack_weights_bwd(ps, S1, S3, S2)) if args.backward \
+            else None
         shared_np = (S1.cpu().numpy().view(np.uint16)[0],
                      None if S3 is None else S3.cpu().numpy().view(np.uint16)[0],
                      S2.cpu().numpy().view(np.uint16)[0])
@@ -560,15 +585,15 @@ def main():
             ctypes.byref(p), ctypes.byref(ps)), dtype=torch.uint8, device=dev)
     y = torch.empty((w.B, w.d), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
     if args.backward:
-        if ec or shared is not None or args.overflow != "drop":
-            raise SystemExit("--backward goes with token-choice routing, the drop policy and "
-                             "no shared expert")
+        if ec or args.overflow != "drop":
+            raise SystemExit("--backward goes with token-choice routing and the drop policy")
         W1 = d16(inp["W1"] if bf16 else inp["W1_bits"])
         W2 = d16(inp["W2"] if bf16 else inp["W2_bits"])
         W3 = d16(inp["W3"] if bf16 else inp["W3_bits"]) if w.act == "swiglu" else None
         wpb = moe.pack_weights_bwd(p, W1, W3, W2)
         del W1, W2, W3
-        bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev)
+        bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev,
+                       shared_bwd if shared is not None else None)
         return
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 

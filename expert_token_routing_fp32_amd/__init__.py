@@ -731,12 +731,14 @@ def gate_backward(p: Problem, x, Wg, dlogits, dx_acc=None, ws=None):
 
 
 def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef: float = 0.0,
-             ws=None) -> dict:
+             ws=None, shared=None) -> dict:
     """All gradients of the layer (moe_backward).  ``saved``: the dict of
     ``forward(..., outputs=True)`` (logits, topk_idx, topk_w, dest,
     expert_load, expert_offset, pack_src, and packed = the expert outputs;
     with ``save_z=True`` also z, the pre-activations the backward then does
-    not recompute).
+    not recompute).  ``shared`` = (ps, wpacked_shared, wpacked_shared_bwd)
+    for the layer of ``forward(..., shared=...)`` (moe_backward_shared): the
+    result then also holds dW1s, dW3s (SwiGLU, else None) and dW2s.
     Returns dx, dWg, dbias, dW1, dW3 (SwiGLU, else None), dW2, dlogits, dw."""
     _check(p)
     B, d, E, k, f = p.B, p.d, p.E, p.k, p.f
@@ -761,13 +763,33 @@ def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef:
                  z=saved["z"].data_ptr() if saved.get("z") is not None else None)
     gr = L.Grads(**{n: (g[n].data_ptr() if g[n] is not None else None)
                     for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dlogits", "dw")})
-    n = workspace_bytes(p, "backward")
-    if ws is None:
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    _need(ws, "ws", n, 1)
-    L.check(lib().moe_backward(ctypes.byref(p), _p(x), _p(Wg), _p(wpacked), _p(wpacked_bwd),
-                               ctypes.byref(sv), _p(dy), ctypes.c_float(aux_coef),
-                               ctypes.byref(gr), _p(ws), ws.numel(), _stream()), "moe_backward")
+    if shared is not None:
+        ps, wps, wpsb = shared
+        _check(ps)
+        fs = ps.f
+        ssw = ps.act == L.MOE_SWIGLU
+        g["dW1s"] = torch.empty((d, fs), **f32)
+        g["dW2s"] = torch.empty((fs, d), **f32)
+        g["dW3s"] = torch.empty((d, fs), **f32) if ssw else None
+        n = lib().moe_backward_shared_workspace_bytes(ctypes.byref(p), ctypes.byref(ps))
+        if ws is None:
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        _need(ws, "ws", n, 1)
+        L.check(lib().moe_backward_shared(ctypes.byref(p), ctypes.byref(ps), _p(x), _p(Wg),
+                                          _p(wpacked), _p(wpacked_bwd), _p(wps), _p(wpsb),
+                                          ctypes.byref(sv), _p(dy), ctypes.c_float(aux_coef),
+                                          ctypes.byref(gr), _p(g["dW1s"]), _p(g["dW3s"]),
+                                          _p(g["dW2s"]), _p(ws), ws.numel(), _stream()),
+                "moe_backward_shared")
+    else:
+        n = workspace_bytes(p, "backward")
+        if ws is None:
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        _need(ws, "ws", n, 1)
+        L.check(lib().moe_backward(ctypes.byref(p), _p(x), _p(Wg), _p(wpacked),
+                                   _p(wpacked_bwd), ctypes.byref(sv), _p(dy),
+                                   ctypes.c_float(aux_coef), ctypes.byref(gr), _p(ws),
+                                   ws.numel(), _stream()), "moe_backward")
     for key in ("dW1", "dW2", "dW3"):
         if g[key] is not None:
             g[key] = g[key][:nl]

@@ -136,6 +136,11 @@ _SIGS = {
     "moe_backward": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.POINTER(Saved), _V,
                                     ctypes.c_float, ctypes.POINTER(Grads), _V, ctypes.c_size_t,
                                     _V]),
+    "moe_backward_shared_workspace_bytes": (ctypes.c_size_t, [_P, _P]),
+    "moe_backward_shared": (ctypes.c_int, [_P, _P, _V, _V, _V, _V, _V, _V,
+                                           ctypes.POINTER(Saved), _V, ctypes.c_float,
+                                           ctypes.POINTER(Grads), _V, _V, _V, _V,
+                                           ctypes.c_size_t, _V]),
 }
 
 _lib = None

@@ -435,6 +435,37 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     p[i] = 0.f;
 }
 
+// shared expert backward: its rows are the tokens in order (pack_src[t] = t,
+// expert_offset {0, B}), and its output gradient is dy (bf16) itself
+__global__ __launch_bounds__(256) void shared_bwd_prep_kernel(int32_t* __restrict__ pack_src,
+                                                              int32_t* __restrict__ eo,
+                                                              const u32x4* __restrict__ dy,
+                                                              u32x4* __restrict__ dret, int64_t B,
+                                                              int64_t nchunks) {
+  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t st = (int64_t)gridDim.x * 256;
+  if (i0 < 2) eo[i0] = i0 == 0 ? 0 : (int32_t)B;
+  for (int64_t i = i0; i < B; i += st) pack_src[i] = (int32_t)i;
+  for (int64_t i = i0; i < nchunks; i += st) dret[i] = dy[i];
+}
+
+// acc[i] += v[i] (bf16), 8 elements per thread (n a multiple of 8)
+__global__ __launch_bounds__(256) void add_bf16_kernel(float* __restrict__ acc,
+                                                       const uint16_t* __restrict__ v,
+                                                       int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * 256) {
+    float f[8];
+    unpack8(*(const u32x4*)(v + i * 8), f);
+    float4* a = reinterpret_cast<float4*>(acc + i * 8);
+    float4 a0 = a[0], a1 = a[1];
+    a0.x += f[0]; a0.y += f[1]; a0.z += f[2]; a0.w += f[3];
+    a1.x += f[4]; a1.y += f[5]; a1.z += f[6]; a1.w += f[7];
+    a[0] = a0;
+    a[1] = a1;
+  }
+}
+
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ part, int G,
                                                         int M0, int N, float* __restrict__ out0,
                                                         float* __restrict__ out1) {
@@ -460,6 +491,22 @@ hipError_t launch_sum_parts(const float* part, int G, int M0, int N, float* out0
 }
 
 // zeros by a kernel (not a memset node: callers may capture the stream)
+hipError_t launch_shared_bwd_prep(int32_t* pack_src, int32_t* eo, const uint16_t* dy,
+                                  uint16_t* dret, int64_t B, int d, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const int64_t nchunks = B * d / 8;
+  hipLaunchKernelGGL(shared_bwd_prep_kernel, dim3(bgrid(nchunks > B ? nchunks : B, 256)),
+                     dim3(256), 0, s, pack_src, eo, reinterpret_cast<const u32x4*>(dy),
+                     reinterpret_cast<u32x4*>(dret), B, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_bf16(float* acc, const uint16_t* v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(add_bf16_kernel, dim3(bgrid(n / 8, 256)), dim3(256), 0, s, acc, v, n / 8);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0 || !p) return hipSuccess;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(bgrid(n, 256)), dim3(256), 0, s, p, n);

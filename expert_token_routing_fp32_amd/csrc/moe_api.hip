@@ -1165,10 +1165,41 @@ moe_status_t moe_gate_backward(const moe_problem_t* p, const void* x, const floa
   return hip_status(gate_backward(p, x, Wg, dlogits, dx_acc, dx, dWg, dbias, ws, stream));
 }
 
-moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg,
-                          const void* wpacked, const void* wpacked_bwd, const moe_saved_t* sv,
-                          const void* dy, float aux_coef, const moe_grads_t* g, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The shared expert of moe_backward_shared: its problem, packed weights,
+// weight gradients, and its part of the workspace (after the routed one).
+struct SharedBwd {
+  const moe_problem_t* ps;
+  const void *wp, *wpb;
+  float *dW1, *dW3, *dW2;
+};
+// shared expert part of the backward workspace: its rows' indices (the
+// tokens), expert_offset {0, B}, its output gradient (bf16 dy, overwritten
+// by its input gradient), the expert FFN backward's scratch
+struct SharedBwdBufs {
+  int32_t *pack_src, *eo;
+  uint16_t* dret;
+  void* ffn_ws;
+};
+size_t carve_shared_bwd(const moe_problem_t* ps, void* ws, SharedBwdBufs* b) {
+  Carve c;
+  c.base = static_cast<char*>(ws);
+  SharedBwdBufs t;
+  t.pack_src = c.take<int32_t>(nullptr, (size_t)ps->B * 4);
+  t.eo = c.take<int32_t>(nullptr, 2 * 4);
+  t.dret = c.take<uint16_t>(nullptr, (size_t)ps->B * ps->d * 2);
+  t.ffn_ws = c.take<char>(nullptr, carve_ffn_bwd(ps, nullptr, nullptr));
+  if (b) *b = t;
+  return c.off;
+}
+
+moe_status_t backward_chain(const moe_problem_t* p, const void* x, const float* Wg,
+                            const void* wpacked, const void* wpacked_bwd, const moe_saved_t* sv,
+                            const void* dy, float aux_coef, const moe_grads_t* g, void* ws,
+                            size_t ws_bytes, hipStream_t stream, const SharedBwd* sh) {
   moe_status_t st = check_bwd(p);
   if (st != MOE_OK) return st;
   if (!sv || !g) return MOE_ERR_INVALID;
@@ -1186,7 +1217,19 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
     return MOE_ERR_INVALID;
   if (sv->z && !a16(sv->z)) return MOE_ERR_INVALID;
   if ((g->dw && !a4(g->dw)) || (g->dlogits && !a4(g->dlogits))) return MOE_ERR_INVALID;
-  const size_t need = carve_bwd(p, g, nullptr, nullptr);
+  const bool ssw = sh && sh->ps->act == MOE_SWIGLU;
+  if (sh) {
+    st = check_shared(sh->ps);
+    if (st != MOE_OK) return st;
+    if (sh->ps->B != p->B || sh->ps->d != p->d) return MOE_ERR_INVALID;
+    if (p->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!sh->wp || !sh->wpb || !a16(sh->wp) || !a16(sh->wpb)) return MOE_ERR_INVALID;
+    if (!sh->dW1 || !sh->dW2 || (ssw && !sh->dW3) || !a4(sh->dW1) || !a4(sh->dW2) ||
+        (ssw && !a4(sh->dW3)))
+      return MOE_ERR_INVALID;
+  }
+  const size_t routed = align_up(carve_bwd(p, g, nullptr, nullptr));
+  const size_t need = routed + (sh ? carve_shared_bwd(sh->ps, nullptr, nullptr) : 0);
   if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return MOE_ERR_WORKSPACE;
   BwdBufs b;
   carve_bwd(p, g, ws, &b);
@@ -1198,6 +1241,12 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
       e = moek::launch_fill_zero(g->dW1, n, stream);
       if (e == hipSuccess) e = moek::launch_fill_zero(g->dW2, n, stream);
       if (e == hipSuccess && sw) e = moek::launch_fill_zero(g->dW3, n, stream);
+    }
+    if (sh) {
+      const int64_t n = (int64_t)p->d * sh->ps->f;
+      if (e == hipSuccess) e = moek::launch_fill_zero(sh->dW1, n, stream);
+      if (e == hipSuccess) e = moek::launch_fill_zero(sh->dW2, n, stream);
+      if (e == hipSuccess && ssw) e = moek::launch_fill_zero(sh->dW3, n, stream);
     }
     if (e == hipSuccess) e = moek::launch_fill_zero(g->dWg, (int64_t)p->d * p->E, stream);
     if (e == hipSuccess && g->dbias) e = moek::launch_fill_zero(g->dbias, p->E, stream);
@@ -1214,9 +1263,52 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
   if (e == hipSuccess)
     e = moek::launch_unpack_sum(b.dret, sv->dest, dy, xb, p->add_residual != 0, p->B, p->k, p->d,
                                 kmax_of(p), b.dx_acc, stream);
+  if (sh) {
+    // the shared expert's output entered y with weight 1: its output
+    // gradient is dy; its input gradient joins the routed one before the
+    // router's
+    SharedBwdBufs s;
+    carve_shared_bwd(sh->ps, static_cast<char*>(ws) + routed, &s);
+    if (e == hipSuccess)
+      e = moek::launch_shared_bwd_prep(s.pack_src, s.eo, static_cast<const uint16_t*>(dy), s.dret,
+                                       p->B, p->d, stream);
+    if (e == hipSuccess)
+      e = ffn_backward(sh->ps, x, s.pack_src, s.eo, sh->wp, sh->wpb, nullptr, s.dret, sh->dW1,
+                       ssw ? sh->dW3 : nullptr, sh->dW2, s.ffn_ws, stream);
+    if (e == hipSuccess) e = moek::launch_add_bf16(b.dx_acc, s.dret, p->B * p->d, stream);
+  }
   if (e == hipSuccess)
     e = gate_backward(p, x, Wg, b.dl, b.dx_acc, g->dx, g->dWg, g->dbias, b.gate_ws, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg,
+                          const void* wpacked, const void* wpacked_bwd, const moe_saved_t* sv,
+                          const void* dy, float aux_coef, const moe_grads_t* g, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return backward_chain(p, x, Wg, wpacked, wpacked_bwd, sv, dy, aux_coef, g, ws, ws_bytes,
+                        stream, nullptr);
+}
+
+size_t moe_backward_shared_workspace_bytes(const moe_problem_t* p, const moe_problem_t* ps) {
+  if (check_bwd(p) != MOE_OK || check_shared(ps) != MOE_OK) return SIZE_MAX;
+  return align_up(carve_bwd(p, nullptr, nullptr, nullptr)) + carve_shared_bwd(ps, nullptr, nullptr);
+}
+
+moe_status_t moe_backward_shared(const moe_problem_t* p, const moe_problem_t* ps, const void* x,
+                                 const float* Wg, const void* wpacked, const void* wpacked_bwd,
+                                 const void* wpacked_shared, const void* wpacked_shared_bwd,
+                                 const moe_saved_t* saved, const void* dy, float aux_coef,
+                                 const moe_grads_t* grads, float* dW1s, float* dW3s, float* dW2s,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ps) return MOE_ERR_INVALID;
+  const SharedBwd sh{ps, wpacked_shared, wpacked_shared_bwd, dW1s, dW3s, dW2s};
+  return backward_chain(p, x, Wg, wpacked, wpacked_bwd, saved, dy, aux_coef, grads, ws, ws_bytes,
+                        stream, &sh);
 }
 
 }  // extern "C"

@@ -358,6 +358,11 @@ hipError_t launch_relayout_rb8(int mode, const uint16_t* src, int64_t src_ld, co
                                int src_w, int one_col, uint16_t* out, hipStream_t s,
                                const int32_t* ridx = nullptr, int64_t src_rows = 0);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// shared expert backward: pack_src[t] = t, expert_offset {0, B}, dret = dy
+// (bf16 [B][d]); and acc += v (fp32 += bf16, n a multiple of 8)
+hipError_t launch_shared_bwd_prep(int32_t* pack_src, int32_t* eo, const uint16_t* dy,
+                                  uint16_t* dret, int64_t B, int d, hipStream_t s);
+hipError_t launch_add_bf16(float* acc, const uint16_t* v, int64_t n, hipStream_t s);
 // out0[m][n] (m < M0) / out1[n] (m == M0) = sum over g of part[g][m][n], in g
 // order; part is [G][M0 + 1][N]
 hipError_t launch_sum_parts(const float* part, int G, int M0, int N, float* out0, float* out1,

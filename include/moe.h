@@ -670,6 +670,30 @@ moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg
                           const void* dy, float aux_coef, const moe_grads_t* grads, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* Workspace of moe_backward_shared (SIZE_MAX if either problem is invalid). */
+size_t moe_backward_shared_workspace_bytes(const moe_problem_t* p,
+                                           const moe_problem_t* ps);
+
+/* moe_backward for the layer of moe_forward_shared: the routed backward of
+ * p, and the shared expert of ps ("Expert Parallelism", narrativegoldmine.com,
+ * "Major Variants and Families", shared expert routing), whose output joins y
+ * with weight 1, so that its output gradient is dy itself: its weight
+ * gradients, and its input gradient added (in fp32) to the tokens' routed
+ * input gradient before the router's part is added.
+ *   ps as for moe_forward_shared (same B and d, E = 1, bf16 x);
+ *   wpacked_shared, wpacked_shared_bwd: moe_pack_weights(ps, ...) and
+ *   moe_pack_weights_bwd(ps, ...); dW1s, dW3s [d][fs] (dW3s only for a
+ *   SwiGLU shared expert, else NULL), dW2s [fs][d] float out;
+ *   ws >= moe_backward_shared_workspace_bytes(p, ps), 16-byte aligned;
+ *   the other arguments as moe_backward. */
+moe_status_t moe_backward_shared(const moe_problem_t* p, const moe_problem_t* ps,
+                                 const void* x, const float* Wg, const void* wpacked,
+                                 const void* wpacked_bwd, const void* wpacked_shared,
+                                 const void* wpacked_shared_bwd, const moe_saved_t* saved,
+                                 const void* dy, float aux_coef, const moe_grads_t* grads,
+                                 float* dW1s, float* dW3s, float* dW2s, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

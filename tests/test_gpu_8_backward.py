@@ -341,3 +341,60 @@ def test_backward_saved_z_matches_recompute(name):
             assert torch.equal(v, g1[key]), key
     say(f"  {len(g0)} gradients bit-identical with the saved pre-activations "
         f"({moe.saved_z_bytes(p) / 1e6:.1f} MB)")
+
+
+def _shared_weights(rng, d, f, swiglu):
+    """bf16 bits of a shared expert's W1s [1, d, f], W3s, W2s [1, f, d]."""
+    def bf(a):
+        return oracle.f32_to_bf16_bits_rne(a.astype(np.float32))
+    W1 = bf(rng.normal(scale=d ** -0.5, size=(1, d, f)))
+    W3 = bf(rng.normal(scale=d ** -0.5, size=(1, d, f))) if swiglu else None
+    W2 = bf(rng.normal(scale=f ** -0.5, size=(1, f, d)))
+    return W1, W3, W2
+
+
+@pytest.mark.parametrize("B,d,f,E,act,fs,sact", [(256, 64, 96, 8, "gelu", 128, "gelu"),
+                                                 (300, 72, 40, 8, "swiglu", 200, "swiglu"),
+                                                 (4096, 1024, 1024, 64, "gelu", 1024, "swiglu")])
+def test_backward_shared(B, d, f, E, act, fs, sact):
+    """moe_backward_shared: the routed gradients are moe_backward's bit for
+    bit (the shared expert changes only dx); the shared expert's weight
+    gradients and its part of dx against the oracle's expert FFN backward
+    with every token as the one expert's rows and dy as its output
+    gradient."""
+    import torch
+    import expert_token_routing_fp32_amd as moe
+    w = moe_synth.Workload(name="bshared", B=B, d=d, E=E, k=2, c=1.0, f=f, act=act,
+                           x_dtype="bf16", n_ranks=1, e_begin=0, e_end=E, router_std=None,
+                           zipf_bias=False, tau=1.0, seed=4)
+    say(f"[backward shared] B={B} d={d} f={f} E={E} {act}, shared f={fs} {sact}")
+    inp = moe_synth.make_inputs(w)
+    S1, S3, S2 = _shared_weights(np.random.default_rng(9), d, fs, sact == "swiglu")
+    p = problem_for(w)
+    ps = moe.shared_problem(p, fs, sact)
+    x, Wg = to_dev(inp["x"]), to_dev(inp["Wg"])
+    wp = packed_weights_for_gpu(p, inp)
+    wpb = _wpb(p, inp)
+    d3 = None if S3 is None else to_dev(S3)
+    wps = moe.pack_weights(ps, to_dev(S1), d3, to_dev(S2))
+    wpsb = moe.pack_weights_bwd(ps, to_dev(S1), d3, to_dev(S2))
+    y, o = moe.forward(p, x, Wg, None, wp, outputs=True, shared=(ps, wps))
+    dy = _dy(w, seed=7)
+    g = moe.backward(p, x, Wg, wp, wpb, o, to_dev(dy), aux_coef=AUX, shared=(ps, wps, wpsb))
+    g0 = moe.backward(p, x, Wg, wp, wpb, o, to_dev(dy), aux_coef=AUX)
+    torch.cuda.synchronize()
+    for key in ("dW1", "dW2", "dW3", "dWg", "dbias", "dlogits", "dw"):
+        if g0[key] is not None:
+            assert torch.equal(g[key], g0[key]), key
+    dXs, grs = oracle.expert_ffn_backward(inp["x"], np.arange(B), np.array([0, B]), 0, 1, S1, S2,
+                                          S3, sact, _x_vals(dy))
+    for name, gi in (("dW1s", 0), ("dW2s", 1), ("dW3s", 2)):
+        if grs[0][gi] is None:
+            assert g[name] is None
+            continue
+        e = rel_err(to_np(g[name]), grs[0][gi])
+        say(f"  {name}: max|d|/max|ref| = {e:.3e}")
+        assert e <= 2e-2, (name, e)
+    dx_s = oracle.bf16_bits_to_f64(to_np(g["dx"]))
+    dx_0 = oracle.bf16_bits_to_f64(to_np(g0["dx"]))
+    assert_bf16_close(dx_s, dx_0 + dXs, what="dx with the shared expert")
