@@ -423,7 +423,8 @@ def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev, share
         ev[4].record()
         if shared is not None:
             s_dret.copy_(dy)
-            moe.expert_ffn_backward(ps_, x, s_src, s_eo, shared[1], shared[2], s_dret, ws=ws_s)
+            moe.expert_ffn_backward(ps_, x, s_src, s_eo, shared[1], shared[2], s_dret, ws=ws_s,
+                                    z=o.get("z_shared"))
             ev[5].record()
         moe.gate_backward(p, x, Wg, dlb, dx_acc=accb, ws=ws_g)
         ev[len(keys)].record()

@@ -394,7 +394,8 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
     With ``outputs`` the intermediate tensors are allocated and returned too
     (``packed`` then holds the expert outputs of the local rows, in place);
     with ``save_z`` as well, ``z``: the first expert GEMM's pre-activations,
-    which backward() then reads instead of recomputing them.
+    which backward() then reads instead of recomputing them (and with a
+    shared expert ``z_shared``, its own).
     ``stage_events``: optional N_STAGE_EVENTS timing-enabled
     ``torch.cuda.Event`` (or None); the library records them from the start
     and end of each stage's own kernels (STAGE_EVENTS gives the pair of each
@@ -431,6 +432,10 @@ def forward(p: Problem, x, Wg, bias, wpacked, y=None, outputs: bool = False, ws=
         if save_z:
             o["z"] = torch.empty(max(saved_z_bytes(p) // 2, 1), dtype=torch.int16, device=dev)
             outp.z = o["z"].data_ptr()
+            if shared is not None:
+                o["z_shared"] = torch.empty(max(saved_z_bytes(shared[0]) // 2, 1),
+                                            dtype=torch.int16, device=dev)
+                outp.z_shared = o["z_shared"].data_ptr()
     elif save_z:
         raise ValueError("save_z needs outputs=True")
     if stage_events is not None:
@@ -760,7 +765,9 @@ def backward(p: Problem, x, Wg, wpacked, wpacked_bwd, saved: dict, dy, aux_coef:
                  expert_load=saved["expert_load"].data_ptr(),
                  expert_offset=saved["expert_offset"].data_ptr(),
                  pack_src=saved["pack_src"].data_ptr(), ret=saved["packed"].data_ptr(),
-                 z=saved["z"].data_ptr() if saved.get("z") is not None else None)
+                 z=saved["z"].data_ptr() if saved.get("z") is not None else None,
+                 z_shared=saved["z_shared"].data_ptr()
+                 if shared is not None and saved.get("z_shared") is not None else None)
     gr = L.Grads(**{n: (g[n].data_ptr() if g[n] is not None else None)
                     for n in ("dx", "dWg", "dbias", "dW1", "dW3", "dW2", "dlogits", "dw")})
     if shared is not None:

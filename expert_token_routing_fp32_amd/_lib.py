@@ -55,7 +55,8 @@ class ForwardOut(ctypes.Structure):
     hipEvent_t handles (or NULL) taken from the stages' kernel dispatches."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "pos", "keep", "dest", "expert_load",
-        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed", "z")] + [
+        "expert_count", "expert_offset", "rank_offset", "pack_src", "packed", "z",
+        "z_shared")] + [
         ("events", ctypes.c_void_p * MOE_STAGE_EVENTS)]
 
 
@@ -70,7 +71,7 @@ class Saved(ctypes.Structure):
     """moe_saved_t: the forward's outputs the backward reads."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "logits", "topk_idx", "topk_w", "dest", "expert_load", "expert_offset", "pack_src",
-        "ret", "z")]
+        "ret", "z", "z_shared")]
 
 
 class Grads(ctypes.Structure):

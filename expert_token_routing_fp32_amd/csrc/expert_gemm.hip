@@ -882,13 +882,13 @@ __global__ void shared_offsets_kernel(int32_t* __restrict__ eo, int32_t B) {
 
 hipError_t launch_shared_ffn(const uint16_t* x, int64_t B, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, int32_t* eo, uint16_t* out,
-                             hipStream_t s, hipEvent_t ev_stop) {
+                             hipStream_t s, hipEvent_t ev_stop, uint16_t* zsave) {
   if (B <= 0) return ev_stop ? hipEventRecord(ev_stop, s) : hipSuccess;
   hipLaunchKernelGGL(shared_offsets_kernel, dim3(1), dim3(64), 0, s, eo, (int32_t)B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_expert_ffn(x, eo, 0, 1, (int)B, (int)B, d, f, swiglu, wp, H, out, s, nullptr,
-                           ev_stop);
+                           ev_stop, nullptr, nullptr, nullptr, nullptr, 0, zsave);
 }
 
 hipError_t launch_expert_ffn(const uint16_t* packed, const int32_t* expert_offset, int e_begin,

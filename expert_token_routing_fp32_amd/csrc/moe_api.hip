@@ -549,6 +549,7 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
   if (wpacked && !a16(wpacked)) return MOE_ERR_INVALID;
   if (out && out->packed && !a16(out->packed)) return MOE_ERR_INVALID;
   if (out && out->z && !a16(out->z)) return MOE_ERR_INVALID;
+  if (out && out->z_shared && (!sh || !a16(out->z_shared))) return MOE_ERR_INVALID;
   const size_t need = carve_forward(p, out, nullptr, nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   FwdBufs b;
@@ -633,7 +634,7 @@ moe_status_t forward_chain(const moe_problem_t* p, const void* x, const float* W
     if (e == hipSuccess && sh)
       e = moek::launch_shared_ffn(static_cast<const uint16_t*>(x), p->B, p->d, sh->ps->f,
                                   sh->ps->act == MOE_SWIGLU, sh->wp, sh->H, sh->eo, sh->S, stream,
-                                  ev[8]);
+                                  ev[8], out ? out->z_shared : nullptr);
   }
   if (e == hipSuccess)
     e = moek::launch_combine(b.packed, b.dest, b.w, p->add_residual ? x : nullptr, xb, y, p->B,
@@ -1216,6 +1217,7 @@ moe_status_t backward_chain(const moe_problem_t* p, const void* x, const float* 
   if (p->B > 0 && (!a16(x) || !a16(dy) || !a16(sv->ret) || !a4(g->dx)))
     return MOE_ERR_INVALID;
   if (sv->z && !a16(sv->z)) return MOE_ERR_INVALID;
+  if (sv->z_shared && (!sh || !a16(sv->z_shared))) return MOE_ERR_INVALID;
   if ((g->dw && !a4(g->dw)) || (g->dlogits && !a4(g->dlogits))) return MOE_ERR_INVALID;
   const bool ssw = sh && sh->ps->act == MOE_SWIGLU;
   if (sh) {
@@ -1273,8 +1275,8 @@ moe_status_t backward_chain(const moe_problem_t* p, const void* x, const float* 
       e = moek::launch_shared_bwd_prep(s.pack_src, s.eo, static_cast<const uint16_t*>(dy), s.dret,
                                        p->B, p->d, stream);
     if (e == hipSuccess)
-      e = ffn_backward(sh->ps, x, s.pack_src, s.eo, sh->wp, sh->wpb, nullptr, s.dret, sh->dW1,
-                       ssw ? sh->dW3 : nullptr, sh->dW2, s.ffn_ws, stream);
+      e = ffn_backward(sh->ps, x, s.pack_src, s.eo, sh->wp, sh->wpb, sv->z_shared, s.dret,
+                       sh->dW1, ssw ? sh->dW3 : nullptr, sh->dW2, s.ffn_ws, stream);
     if (e == hipSuccess) e = moek::launch_add_bf16(b.dx_acc, s.dret, p->B * p->d, stream);
   }
   if (e == hipSuccess)

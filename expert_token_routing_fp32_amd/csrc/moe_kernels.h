@@ -307,7 +307,8 @@ hipError_t launch_combine(const uint16_t* ret, const int32_t* dest, const float*
 // device scratch), hidden activations in H [B][f].
 hipError_t launch_shared_ffn(const uint16_t* x, int64_t B, int d, int f, bool swiglu,
                              const void* wp, uint16_t* H, int32_t* eo, uint16_t* out,
-                             hipStream_t s, hipEvent_t ev_stop = nullptr);
+                             hipStream_t s, hipEvent_t ev_stop = nullptr,
+                             uint16_t* zsave = nullptr);
 
 hipError_t launch_unpack(const uint16_t* ret, const int32_t* dest, int64_t B, int k, int d,
                          int64_t kmax, uint16_t* out, hipStream_t s);

@@ -365,6 +365,11 @@ typedef struct {
                              expert GEMM for moe_backward, which then does
                              not recompute them; NULL: not stored (and not
                              in the workspace either) */
+  moe_bf16_t* z_shared;   /* moe_forward_shared only, optional,
+                             moe_saved_z_bytes(ps) bytes, 16-byte aligned:
+                             the same for the shared expert (all B rows),
+                             read by moe_backward_shared; NULL: not stored.
+                             Must be NULL for moe_forward. */
   /* Optional timing: each non-NULL events[i] is recorded on the call's
    * stream from the dispatch timestamps of the stages' own kernels
    * (hipExtLaunchKernelGGL start / end events; no marker packets):
@@ -647,6 +652,8 @@ typedef struct {
   const int32_t* pack_src;      /* [Kmax]   */
   const moe_bf16_t* ret;        /* [Kmax][d] */
   const moe_bf16_t* z;          /* moe_forward_out_t.z, or NULL: recompute */
+  const moe_bf16_t* z_shared;   /* moe_forward_out_t.z_shared (moe_backward_shared
+                                   only), or NULL: recompute */
 } moe_saved_t;
 
 /* The gradients moe_backward writes; dW3 only for SwiGLU, dbias may be

@@ -361,7 +361,8 @@ def test_backward_shared(B, d, f, E, act, fs, sact):
     bit (the shared expert changes only dx); the shared expert's weight
     gradients and its part of dx against the oracle's expert FFN backward
     with every token as the one expert's rows and dy as its output
-    gradient."""
+    gradient; and every gradient bit-identical when the forward saved both
+    experts' pre-activations."""
     import torch
     import expert_token_routing_fp32_amd as moe
     w = moe_synth.Workload(name="bshared", B=B, d=d, E=E, k=2, c=1.0, f=f, act=act,
@@ -398,3 +399,11 @@ def test_backward_shared(B, d, f, E, act, fs, sact):
     dx_s = oracle.bf16_bits_to_f64(to_np(g["dx"]))
     dx_0 = oracle.bf16_bits_to_f64(to_np(g0["dx"]))
     assert_bf16_close(dx_s, dx_0 + dXs, what="dx with the shared expert")
+    # with both experts' pre-activations saved by the forward: the same bits
+    y1, o1 = moe.forward(p, x, Wg, None, wp, outputs=True, shared=(ps, wps), save_z=True)
+    g1 = moe.backward(p, x, Wg, wp, wpb, o1, to_dev(dy), aux_coef=AUX, shared=(ps, wps, wpsb))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1)
+    for key, v in g.items():
+        if v is not None:
+            assert torch.equal(v, g1[key]), key
