@@ -360,16 +360,19 @@ typedef struct {
   moe_bf16_t* packed;     /* [Kmax][d]: holds ret after the call (the expert
                              outputs overwrite the local rows in place) */
   moe_bf16_t* z;          /* optional, moe_saved_z_bytes(p) bytes, 16-byte
-                             aligned: the local rows' pre-activations
-                             X . W1 (and X . W3), bf16, stored by the first
-                             expert GEMM for moe_backward, which then does
-                             not recompute them; NULL: not stored (and not
-                             in the workspace either) */
+                             aligned (else MOE_ERR_INVALID): the local rows'
+                             pre-activations X . W1 (and X . W3), bf16, in
+                             the first expert GEMM's own column order (to be
+                             passed back, not read), stored by that GEMM for
+                             moe_backward, which then does not recompute
+                             them; NULL: not stored (and not in the
+                             workspace either) */
   moe_bf16_t* z_shared;   /* moe_forward_shared only, optional,
                              moe_saved_z_bytes(ps) bytes, 16-byte aligned:
                              the same for the shared expert (all B rows),
                              read by moe_backward_shared; NULL: not stored.
-                             Must be NULL for moe_forward. */
+                             Must be NULL for moe_forward (else
+                             MOE_ERR_INVALID). */
   /* Optional timing: each non-NULL events[i] is recorded on the call's
    * stream from the dispatch timestamps of the stages' own kernels
    * (hipExtLaunchKernelGGL start / end events; no marker packets):
