@@ -380,23 +380,33 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
   // B (this wavefront's alone) straight from memory into registers.
   // B fragments of a stage: [slot][half][column block]
   u32x4 bq[KR][2][2];
-  // Issue of stage ST into slot SLOT (clamped to the last
-  // stage: the issues past the end reload it, and nobody reads it again, so
-  // every stage issues the same loads), in 8 parts: A's k group `wave`
-  // (rows m0 .. m0 + 255, parts 0-3, 64 chunks each) into LDS slot SLOT,
-  // then this wavefront's B fragments (the lane's k groups 2 h + lh; parts
-  // 4-7) into registers bq[SLOT].  KSEG sets the stage's descriptors and
-  // offsets; KPART issues one part.
+  // Issue of the next stage into slot SLOT (after the last stage the issues
+  // reload it, and nobody reads it again, so every stage issues the same
+  // loads), in 8 parts: A's k group `wave` (rows m0 .. m0 + 255, parts 0-3,
+  // 64 chunks each) into LDS slot SLOT, then this wavefront's B fragments
+  // (the lane's k groups 2 h + lh; parts 4-7) into registers bq[SLOT].
+  // KSEG sets the stage's descriptors and offsets; KPART issues one part.
+  // The stages of a tile are issued in order, so the stage (is_st), its
+  // segment (is_seg) and its k step in the segment (is_k) are counters
+  // advanced by one per issue, up to the last stage: no division of the
+  // stage index by the steps per segment (a scalar division of some 70
+  // instructions ahead of every stage's barrier).
   uint32_t ia_la = 0, ia_oa = 0, ia_kq = 0;
-#define KSEG(ST, SLOT)                                                                 \
+  int is_st = 0, is_k = 0, is_seg = 0;
+#define KSEG(SLOT)                                                                     \
   {                                                                                    \
-    const int sc_ = (ST) < ct.nst ? (ST) : ct.nst - 1;                                 \
-    const int sgm_ = sc_ / ct.nks;                                                     \
-    ia_kq = (uint32_t)(sc_ - sgm_ * ct.nks) * 4;                                       \
-    if (sgm_ != csg) {                                                                 \
-      ra = make_rsrc(a.A[sgm_] + (int64_t)ct.g * a.a_es, kbytes(a.a_bytes, a.a_es, ct.g)); \
-      rb = make_rsrc(a.Bm[sgm_] + (int64_t)ct.g * a.b_es, kbytes(a.b_bytes, a.b_es, ct.g)); \
-      csg = sgm_;                                                                      \
+    ia_kq = (uint32_t)is_k * 4;                                                        \
+    if (is_seg != csg) {                                                               \
+      ra = make_rsrc(a.A[is_seg] + (int64_t)ct.g * a.a_es, kbytes(a.a_bytes, a.a_es, ct.g)); \
+      rb = make_rsrc(a.Bm[is_seg] + (int64_t)ct.g * a.b_es, kbytes(a.b_bytes, a.b_es, ct.g)); \
+      csg = is_seg;                                                                    \
+    }                                                                                  \
+    if (is_st < ct.nst - 1) {                                                          \
+      ++is_st;                                                                         \
+      if (++is_k == ct.nks) {                                                          \
+        is_k = 0;                                                                      \
+        ++is_seg;                                                                      \
+      }                                                                                \
     }                                                                                  \
     ia_la = smem_lds + (SLOT) * KSLOT + wave * KPL * 16;                               \
     ia_oa = 16u * ((ia_kq + wave) * (uint32_t)a.a_w + (uint32_t)ct.m0) + lo16;         \
@@ -412,9 +422,9 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
                      (uint32_t)(ct.n0 + 64 * wave + 32 * j_ + l32)), 0, 0));            \
     }                                                                                  \
   }
-#define KISSUE(ST, SLOT)                                                               \
+#define KISSUE(SLOT)                                                                   \
   {                                                                                    \
-    KSEG(ST, SLOT)                                                                     \
+    KSEG(SLOT)                                                                         \
     KPART(0, SLOT) KPART(1, SLOT) KPART(2, SLOT) KPART(3, SLOT)                        \
     KPART(4, SLOT) KPART(5, SLOT) KPART(6, SLOT) KPART(7, SLOT)                        \
   }
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
     asm volatile("" ::: "memory");                                                     \
     __builtin_amdgcn_s_barrier();                                                      \
     asm volatile("" ::: "memory");                                                     \
-    KSEG((ST) + KR - 1, ((U) + KR - 1) % KR)                                           \
+    KSEG(((U) + KR - 1) % KR)                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                 \
     const u32x4* sa_ = reinterpret_cast<const u32x4*>(smem + (U) * KSLOT);             \
     const u32x4* sn_ = reinterpret_cast<const u32x4*>(smem + (((U) + 1) % KR) * KSLOT); \
@@ -460,10 +470,11 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
       ct = ktile(a, t);
       csg = -1;
     }
+    is_st = is_k = is_seg = 0;
     if (ct.nst > 0) {
-      KISSUE(0, 0)
-      KISSUE(1, 1)
-      KISSUE(2, 2)
+      KISSUE(0)
+      KISSUE(1)
+      KISSUE(2)
     }
     kf32x16 acc[8][2];
 #pragma unroll
@@ -498,10 +509,15 @@ __global__ __launch_bounds__(256, 1) void kgemm_kernel(KArgsDev a) {
       if (nst - nfull > 0) KSTAGE(nfull, 0)
       if (nst - nfull > 1) KSTAGE(nfull + 1, 1)
       if (nst - nfull > 2) KSTAGE(nfull + 2, 2)
+      // The reloads past the end land before the epilogue.  Left in flight,
+      // they reach the next tile's first stages on the path through the
+      // remainder stages above, and the compiler, which cannot tell that
+      // path's register slots from the loop's, then waits for nearly all of
+      // the two stages ahead at the start of every group of KR stages.
+      k_wait_vmcnt<0>();
       // every wavefront is done reading the ring before the next tile's
-      // loads refill it (the reloads past the end may still be in flight:
-      // each wavefront's loads land in issue order, and the epilogue does
-      // not use the ring)
+      // loads refill it (each wavefront's loads land in issue order, and the
+      // epilogue does not use the ring)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
