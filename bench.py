@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--shared-expert", type=int, default=0, metavar="F",
                     help="add a shared expert of hidden size F (same activation) on every "
                          "token: moe_forward_shared (bf16 workloads)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured once in a HIP graph and replayed "
+                         "(torch.cuda.CUDAGraph; token-choice routing): the rate without the "
+                         "host's per-launch cost, reported beside the eager one")
     ap.add_argument("--backward", action="store_true",
                     help="time the layer's backward pass (moe_backward, for a seeded output "
                          "gradient, on one forward's saved outputs) instead of the forward")
@@ -345,6 +349,34 @@ def cpu_baseline(w, inp, budget_s: float, shared=None, ec: bool = False,
             "cores": int(threads), "kind": "oracle", "cpu_model": model,
             "sample": f"{what}, oracle forward run {reps} times ({t_tot:.1f} s), float64 NumPy, "
                       "input generation excluded"}
+
+
+def graph_replay(args, p, x, Wg, bias, wp, y, ws, shared, w, torch, moe):
+    """The same forward captured once in a HIP graph (the library enqueues
+    kernels only) and replayed: warmup replays, then the timed ones between
+    synchronisations, as the eager steps.  Only the host's launch cost
+    differs, which is what bounds the small workloads."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, shared=shared)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(p, x, Wg, bias, wp, y=y, ws=ws, shared=shared)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    log(f"[bench] graph replay: {sec * 1e3:.4f} ms/step")
+    return {"ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(w.B / sec, 1),
+            "timing": f"{args.steps} replays of one captured forward between two "
+                      "synchronisations (wall clock)"}
 
 
 def bench_backward(args, w, inp, p, x, Wg, bias, wp, wpb, torch, moe, dev, shared=None):
@@ -805,6 +837,9 @@ def main():
         "dropped": None if ec else int(w.B * w.k - alg["K"]),
         **health,
     }
+    if args.graph and not ec:
+        breakdown["graph_replay"] = graph_replay(args, p, x, Wg, bias, wp, y, ws, shared, w,
+                                                 torch, moe)
     if ec:
         breakdown["expert_choice"] = {"rows": alg["K"], "tokens_chosen": alg["t_act"],
                                       "route_us_is": "router probabilities + the choice",
