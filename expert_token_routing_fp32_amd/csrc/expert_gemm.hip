@@ -274,8 +274,13 @@ __device__ __forceinline__ void gemm_run(const GemmArgs& a, char* __restrict__ s
   const int drow = 8 * wave + (lane >> 3);
   const int dcol = 8 * ((lane & 7) ^ swz_key(drow));  // K offset of the lane's chunk
   // the row slice as one buffer (rows x K bf16), or with a gather the whole
-  // source matrix, each lane's row through the index
-  const bool gat = a.gidx != nullptr;
+  // source matrix, each lane's row through the index.  Only the first GEMM
+  // (GELU / SwiGLU) gathers: in the other modes the gather is compiled out,
+  // since a possible index load leaves a wait for every outstanding memory
+  // operation where the two ways of forming the row offset meet -- with the
+  // previous tile's epilogue stores still in flight, at every tile.
+  constexpr bool kCanGather = MODE == MODE_GELU || MODE == MODE_SWIGLU;
+  const bool gat = kCanGather && a.gidx != nullptr;
   const char* abase = reinterpret_cast<const char*>(gat ? a.A : a.A + a_row0 * K);
   const rsrc_t ars =
       make_rsrc(abase, 2u * (uint32_t)(gat ? a.src_rows : (int64_t)rows) * (uint32_t)K);
