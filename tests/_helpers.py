@@ -12,7 +12,7 @@ import numpy as np
 import moe_synth
 import oracle
 
-# tolerances (the benchmark spec): fp32 logits and gate weights |d| <= 1e-5 max(1, |ref|);
+# tolerances of the parity tests: fp32 logits and gate weights |d| <= 1e-5 max(1, |ref|);
 # bf16 tensors max|d| / max|ref| <= 2e-2
 TOL_F32 = 1e-5
 TOL_BF16 = 2e-2

@@ -1,7 +1,7 @@
 """Per-step parity of the HIP path against the CPU oracle on the five
 workloads at their full sizes.  Every step is fed the oracle's own inputs for
 it (logits into the router, expert choices into the dispatch, packed rows into
-the expert FFN), so each kernel is judged on its own:
+the expert FFN), so each kernel is checked on its own:
 
 * integer and byte outputs bit-exact;
 * fp32 logits and gate weights within 1e-5 * max(1, |ref|);
