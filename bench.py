@@ -529,7 +529,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer has no cross-GPU step in this build)", file=sys.stderr)
+              "(the layer runs on one GPU's share of tokens; it has no cross-GPU step)", file=sys.stderr)
         sys.exit(2)
     import torch
 
