@@ -330,7 +330,11 @@ typedef struct {
   double* summary;
 } moe_routing_stats_t;
 
-/* Fills *out (device buffers) from the router logits [B][E] float32 and the
+/* Routing-health signals ("Expert Parallelism", inferensys.com glossary,
+ * Practitioner Guidance: utilization and routing entropy as health signals;
+ * "Expert Parallelism", narrativegoldmine.com, "Components and
+ * Architecture": the auxiliary load-balancing loss).
+ * Fills *out (device buffers) from the router logits [B][E] float32 and the
  * dispatch counts expert_load / expert_count [E] int32 (as written by
  * moe_dispatch or moe_forward).  Deterministic: fixed-order reductions,
  * per-block fp32 partial sums combined in double.
@@ -438,7 +442,9 @@ moe_status_t moe_shared_ffn(const moe_problem_t* ps, const moe_bf16_t* x,
                             const void* wpacked, moe_bf16_t* out, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
-/* moe_combine plus a shared expert's rows, added with weight 1 after the
+/* Shared expert ("Expert Parallelism", narrativegoldmine.com, "Major
+ * Variants and Families", shared expert routing).
+ * moe_combine plus a shared expert's rows, added with weight 1 after the
  * routed sum (and before the residual):
  * y[t] = sum_j topk_w[t,j] ret[dest[t,j]] + shared_out[t] (+ x[t]).
  *   shared_out [B][d] bf16 (moe_shared_ffn's out); the rest as moe_combine */
@@ -452,7 +458,9 @@ moe_status_t moe_combine_shared(const moe_problem_t* p, const moe_bf16_t* ret,
 size_t moe_forward_shared_workspace_bytes(const moe_problem_t* p,
                                           const moe_problem_t* ps);
 
-/* moe_forward with a shared expert: the routed layer of p, the shared
+/* Shared expert ("Expert Parallelism", narrativegoldmine.com, "Major
+ * Variants and Families", shared expert routing).
+ * moe_forward with a shared expert: the routed layer of p, the shared
  * expert of ps on every token (after the routed expert GEMMs, inside the
  * stage events 5 and 6), and the combine of moe_combine_shared.
  * x_dtype must be BF16 for both problems; ps->B == p->B, ps->d == p->d.
@@ -575,7 +583,10 @@ moe_status_t moe_combine_backward(const moe_problem_t* p, const void* dy, const 
                                   const int32_t* dest, const float* topk_w, moe_bf16_t* dret,
                                   float* dw, hipStream_t stream);
 
-/* Router backward: with p_t = softmax(logits_t / tau) and
+/* "Expert Parallelism", narrativegoldmine.com, "Formal Algorithm" (the
+ * weights w_t = p_{t,e(t)}; the auxiliary loss joins the training loss) and
+ * "Components and Architecture" (auxiliary load-balancing loss).
+ * Router backward: with p_t = softmax(logits_t / tau) and
  * dp[t,e] = sum_j [topk_idx[t,j] = e] dw[t,j] + aux_coef n_e / B^2,
  * dlogits[t,e] = p[t,e] (dp[t,e] - sum_e' p[t,e'] dp[t,e']) / tau.
  *   logits [B][E]; topk_idx, dw [B][k]; expert_load [E] (n_e; may be NULL
@@ -605,7 +616,10 @@ moe_status_t moe_pack_weights_bwd(const moe_problem_t* p, const moe_bf16_t* W1,
                                   void* wpacked_bwd, size_t wpacked_bwd_bytes,
                                   hipStream_t stream);
 
-/* Expert FFN backward.  For each local expert and its packed rows
+/* "Expert Parallelism", narrativegoldmine.com, "Components and
+ * Architecture" (the expert GEMM: a standard MLP per expert) and "About"
+ * (training by backpropagation).
+ * Expert FFN backward.  For each local expert and its packed rows
  * (X = x[pack_src[r]], bf16): the pre-activations Z = X . W1 (and X . W3)
  * are taken from z when the forward saved them (moe_forward_out_t.z) or
  * recomputed (z NULL), then dH = dret . W2^T, dZ = dH * act'(Z) (SwiGLU:
@@ -626,7 +640,9 @@ moe_status_t moe_expert_ffn_backward(const moe_problem_t* p, const void* x,
                                      float* dW3, float* dW2, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
 
-/* Dispatch (pack) backward: dx_acc[t] = sum_j dXp[dest[t,j]] over kept
+/* "Expert Parallelism and the All-to-All Bottleneck", "The Mechanism of
+ * Expert Parallelism": the rows travel to their experts and back.
+ * Dispatch (pack) backward: dx_acc[t] = sum_j dXp[dest[t,j]] over kept
  * choices, in j order, plus dy[t] when the problem adds the residual.
  *   dxp [Kmax][d] bf16; dest [B][k]; dy [B][d] x_dtype (read only with the
  *   residual); dx_acc [B][d] float out. */
@@ -634,7 +650,9 @@ moe_status_t moe_dispatch_backward(const moe_problem_t* p, const moe_bf16_t* dxp
                                    const int32_t* dest, const void* dy, float* dx_acc,
                                    hipStream_t stream);
 
-/* Gate backward: dx = dlogits . Wg^T (+ dx_acc), dWg = x^T . dlogits,
+/* "Expert Parallelism", narrativegoldmine.com, "Formal Algorithm": the
+ * router logits as a linear projection of the token.
+ * Gate backward: dx = dlogits . Wg^T (+ dx_acc), dWg = x^T . dlogits,
  * dbias = sum_t dlogits[t] (bias of the logits).
  *   x [B][d] x_dtype; Wg [d][E]; dlogits [B][E]; dx_acc [B][d] float or
  *   NULL; dx [B][d] x_dtype out; dWg [d][E] float out; dbias [E] float out
@@ -672,7 +690,9 @@ typedef struct {
   float* dw;      /* [B][k]              */
 } moe_grads_t;
 
-/* The whole backward on one stream: combine, route, expert FFN, dispatch
+/* "Expert Parallelism", narrativegoldmine.com, "About" (the layer trained
+ * by backpropagation with an auxiliary load-balancing loss).
+ * The whole backward on one stream: combine, route, expert FFN, dispatch
  * and gate backward, in that order (the forward's steps reversed).
  *   ws >= moe_workspace_bytes(p, MOE_OP_BACKWARD), 16-byte aligned. */
 moe_status_t moe_backward(const moe_problem_t* p, const void* x, const float* Wg,
