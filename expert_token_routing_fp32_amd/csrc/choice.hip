@@ -280,11 +280,12 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(
       for (int u = 0; u < 8; ++u) acc[u] += xr[u];
     }
     if (XBF16) {
-      *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
+      // non-temporal, as in the token-choice combine: nothing reads y again
+      __builtin_nontemporal_store(pack8(acc), (u32x4*)((uint16_t*)y + t * d + c * 8));
     } else {
       float* yf = (float*)y + t * d + c * 8;
-      *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)yf);
+      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, (f32x4*)(yf + 4));
     }
   }
 }

@@ -78,12 +78,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc[u] += xr[u];
     }
+    // y is stored non-temporally: nothing in the layer reads it again, and
+    // normal stores let it displace the expert rows still to be read (EP
+    // share: combine 760 -> 711 us; the drop-heavy shape 14.5 -> 13.4 us;
+    // the others unchanged)
     if (XBF16) {
-      *(u32x4*)((uint16_t*)y + t * d + c * 8) = pack8(acc);
+      __builtin_nontemporal_store(pack8(acc), (u32x4*)((uint16_t*)y + t * d + c * 8));
     } else {
       float* yf = (float*)y + t * d + c * 8;
-      *(f32x4*)yf = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(yf + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)yf);
+      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, (f32x4*)(yf + 4));
     }
   }
 }
