@@ -792,6 +792,15 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if ffn_bound == "mfma":
+        # the attainable ceiling measured live, after the timed steps: the same
+        # MFMA instruction mix with random bf16 operands and no memory traffic
+        probe = mfma_probe(torch)["mfma_probe"]["random_bf16"]
+        roof["attainable"] = {"achieved_frac": round(ffn_tflops / probe["tflops"], 4),
+                              "ceiling_tflops": probe["tflops"],
+                              "ceiling": "the expert GEMM's MFMA mix (libmoe_probe.so) with "
+                                         "random bf16 operands and no memory traffic, one "
+                                         "workgroup per CU, timed in this run"}
     roof["traffic"] = measured_traffic(w.name) if shared is None and not ec else None
     roof["kernel"] = "expert FFN: grouped_gemm_kernel GEMM1 (act) + GEMM2, one moe_expert_ffn call"
     roof["algorithmic_bytes"] = alg["ffn_bytes"]
